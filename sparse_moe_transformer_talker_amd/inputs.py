@@ -1,0 +1,166 @@
+"""Seeded synthetic inputs for the Talker MoE feed-forward layer.
+
+This module is shared by the CPU oracle tests and the HIP path. It holds none of
+the layer's arithmetic: only seeded random draws, the per-expert bias recipe for
+the skewed-routing workload, and the fp32 <-> bf16 storage conversion (round to
+nearest even), so that both sides see bit-identical inputs.
+
+Shapes follow "3C · Talker MoE (20 lớp, 128 Experts Top-6)" (openarchlab), §1:
+hidden 1024, 128 routed experts with intermediate 384, Top-6 renormalised, one
+shared expert with intermediate 768, 20 layers, codec_head 1024 -> 3072.  The
+lab-scale shape (hidden 6, 6 experts, Top-2) is the size of the NumPy lab on
+"Bài Lab tổng hợp — Qwen3-Omni & Qwen3-TTS-12Hz Architecture" (openarchlab).
+
+Draw recipe (ours; the pages fix no seeds beyond the lab's seed 30):
+  * weights of a layer with seed ``s``: ``numpy.random.default_rng(s)``, drawn in the
+    order router [E,H], gate [E,I,H], up [E,I,H], down [E,H,I], shared gate [Is,H],
+    shared up [Is,H], shared down [H,Is], each ``standard_normal(float32) * sigma``;
+  * activations: ``default_rng(s + 10000)``, ``standard_normal(float32)`` of [T,H];
+  * bf16 tensors are the fp32 draw rounded to nearest even.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Dict, Optional
+
+import numpy as np
+
+__all__ = [
+    "LayerShape", "WORKLOADS", "f32_to_bf16_bits", "bf16_bits_to_f32",
+    "layer_weights", "activations", "zipf_router_bias", "stack_weights",
+    "bf16_round", "to_f64", "workload_inputs",
+]
+
+
+@dataclasses.dataclass(frozen=True)
+class LayerShape:
+    """Sizes of one MoE layer (names as in the pages' configuration fields)."""
+    hidden_size: int
+    num_experts: int
+    num_experts_per_tok: int
+    moe_intermediate_size: int
+    shared_expert_intermediate_size: int
+    norm_topk_prob: bool = True
+
+    @property
+    def H(self) -> int:
+        return self.hidden_size
+
+    @property
+    def E(self) -> int:
+        return self.num_experts
+
+    @property
+    def k(self) -> int:
+        return self.num_experts_per_tok
+
+    @property
+    def I(self) -> int:  # noqa: E743
+        return self.moe_intermediate_size
+
+    @property
+    def Is(self) -> int:
+        return self.shared_expert_intermediate_size
+
+
+TALKER = LayerShape(1024, 128, 6, 384, 768)
+LAB = LayerShape(6, 6, 2, 12, 12)
+
+# The workloads: sizes, distributions and seeds.
+WORKLOADS: Dict[str, dict] = {
+    "lab_f32": dict(shape=LAB, T=4, sigma=0.5, seed=30, dtype="f32"),
+    "decode_t64": dict(shape=TALKER, T=64, sigma=0.02, seed=30, dtype="bf16"),
+    "prefill_t4096": dict(shape=TALKER, T=4096, sigma=0.02, seed=30, dtype="bf16"),
+    "skew_t8192": dict(shape=TALKER, T=8192, sigma=0.02, seed=30, dtype="bf16",
+                       zipf_s=1.2, zipf_seed=20030),
+    "stack20_t1024": dict(shape=TALKER, T=1024, sigma=0.02, seed=30, dtype="bf16",
+                          layers=20, vocab=3072, head_seed=50, eps=1e-6),
+}
+
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 bit pattern (uint16), round to nearest, ties to even."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    rounding = ((u >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
+    return ((u + rounding) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """bf16 bit pattern (uint16) -> exactly equal fp32."""
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def bf16_round(a: np.ndarray) -> np.ndarray:
+    """Value of ``a`` after storage in bf16, as fp32."""
+    return bf16_bits_to_f32(f32_to_bf16_bits(a))
+
+
+def to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact fp64 value of a stored tensor (bf16 bits or fp32)."""
+    if dtype == "bf16":
+        return bf16_bits_to_f32(a).astype(np.float64)
+    return np.asarray(a, dtype=np.float32).astype(np.float64)
+
+
+def _store(a32: np.ndarray, dtype: str) -> np.ndarray:
+    return f32_to_bf16_bits(a32) if dtype == "bf16" else np.ascontiguousarray(a32, dtype=np.float32)
+
+
+def _normal(rng: np.random.Generator, shape, sigma: float) -> np.ndarray:
+    a = rng.standard_normal(size=shape, dtype=np.float32)
+    if sigma != 1.0:
+        a *= np.float32(sigma)
+    return a
+
+
+def layer_weights(shape: LayerShape, seed: int, sigma: float, dtype: str) -> Dict[str, np.ndarray]:
+    """Weights of one layer in nn.Linear layout [out, in]; bf16 as uint16 bits, else fp32."""
+    rng = np.random.default_rng(seed)
+    H, E, I, Is = shape.H, shape.E, shape.I, shape.Is
+    out = {}
+    for name, shp in (("router", (E, H)), ("gate", (E, I, H)), ("up", (E, I, H)),
+                      ("down", (E, H, I)), ("shared_gate", (Is, H)),
+                      ("shared_up", (Is, H)), ("shared_down", (H, Is))):
+        if name.startswith("shared") and Is == 0:
+            out[name] = None
+            continue
+        out[name] = _store(_normal(rng, shp, sigma), dtype)
+    return out
+
+
+def activations(T: int, H: int, seed: int, dtype: str) -> np.ndarray:
+    """Token hidden states [T, H] ~ N(0, 1)."""
+    rng = np.random.default_rng(seed + 10000)
+    return _store(_normal(rng, (T, H), 1.0), dtype)
+
+
+def zipf_router_bias(E: int, s: float, seed: int) -> np.ndarray:
+    """Per-expert logit bias b_e = -s * ln(rank_e) with ranks a seeded permutation of 1..E.
+
+    Adding it to the router logits multiplies each expert's softmax prior by rank^-s,
+    i.e. a Zipf(s) popularity over the experts (fp32, length E).
+    """
+    ranks = np.random.default_rng(seed).permutation(E) + 1
+    return (-s * np.log(ranks.astype(np.float64))).astype(np.float32)
+
+
+def stack_weights(shape: LayerShape, layers: int, seed: int, sigma: float, dtype: str,
+                  vocab: int, head_seed: int) -> dict:
+    """Weights of an L-layer stack: layer l uses seed+l; codec_head [V,H] uses head_seed."""
+    ws = [layer_weights(shape, seed + l, sigma, dtype) for l in range(layers)]
+    head = _store(_normal(np.random.default_rng(head_seed), (vocab, shape.H), sigma), dtype)
+    return {"layers": ws, "codec_head": head,
+            "norm_gain": np.ones(shape.H, dtype=np.float32)}
+
+
+def workload_inputs(name: str, T: Optional[int] = None) -> dict:
+    """Inputs of one named workload (single-layer ones): weights, x and optional bias."""
+    cfg = WORKLOADS[name]
+    shape: LayerShape = cfg["shape"]
+    T = cfg["T"] if T is None else T
+    w = layer_weights(shape, cfg["seed"], cfg["sigma"], cfg["dtype"])
+    x = activations(T, shape.H, cfg["seed"], cfg["dtype"])
+    bias = None
+    if "zipf_s" in cfg:
+        bias = zipf_router_bias(shape.E, cfg["zipf_s"], cfg["zipf_seed"])
+    return {"shape": shape, "dtype": cfg["dtype"], "T": T, "weights": w, "x": x, "bias": bias}
