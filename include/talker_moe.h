@@ -1,0 +1,213 @@
+/*
+ * talker_moe.h — C ABI of libtalker_moe.so: the Talker mixture-of-experts
+ * feed-forward layer on AMD Instinct MI355X (gfx950), hand-written HIP.
+ *
+ * What it computes ("3C · Talker MoE (20 lớp, 128 Experts Top-6) & Đầu ra mã
+ * ngữ nghĩa c_0", openarchlab, §1 Định nghĩa and §3 Giải pháp):
+ *   p   = softmax(W_r x)                       router over E experts
+ *   S   = the k experts with the largest p    (Top-6 of 128 in the Talker)
+ *   w_i = p_i / sum_{j in S} p_j               (norm_topk_prob = True)
+ *   y   = SharedMLP(x) + sum_{i in S} w_i * Expert_i(x)
+ * Each expert and the shared expert is a SwiGLU MLP, down(SiLU(gate x) * up x)
+ * ("用 print(model) 认识 Qwen3-TTS", horus-space, MLP section); routed experts
+ * are 1024 -> 384 -> 1024 and the shared one 1024 -> 768 -> 1024 in the Talker.
+ *
+ * Conventions for every entry point
+ *   - Pointers marked [dev] are device memory owned by the caller; the library
+ *     never allocates, frees, retains or synchronises.  Host-side structs
+ *     (moe_config, moe_weights) are read during the call only.
+ *   - Matrices are row-major with the last index contiguous.  Weights use the
+ *     nn.Linear layout [out_features, in_features].
+ *   - Element type of activations and weights is cfg->dtype: MOE_BF16 (bf16 bit
+ *     patterns, 2 bytes) or MOE_F32.  Indices are int32, gate weights, router
+ *     bias and probabilities fp32.  MOE_BF16 accumulates in fp32 and rounds
+ *     stored results to bf16 (nearest even).
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *     is asynchronous; kernel faults surface at the caller's next synchronisation.
+ *   - Scratch comes from the caller's workspace `ws` of `ws_bytes` bytes,
+ *     256-byte aligned; moe_workspace_size() gives a size that suffices for every
+ *     entry point at that T.  Calls that share one workspace must not overlap.
+ *   - Every argument is checked on the host before anything is enqueued.  The
+ *     return value is MOE_OK or a negative status (moe_status_string() names
+ *     it); on a negative status nothing was enqueued, except MOE_ERR_HIP,
+ *     which reports a failed launch.  T == 0 is a successful no-op.
+ *   - Device pointers must be 16-byte aligned; inputs must be finite (no NaN,
+ *     Inf or subnormal values).
+ *   - Expert selection is exact: the library's Top-k equals the Top-k of the
+ *     exactly computed scores W_r x (+ bias), ties going to the lower expert
+ *     index, listed by descending weight.  It scores in fp32 and recomputes in
+ *     fp64 every token whose fp32 order is not certain under a rigorous
+ *     rounding-error bound.
+ *
+ * Supported shapes: 1 <= k <= 32, k <= E <= 1024, 1 <= H, I <= 16384,
+ * 0 <= Is <= 16384, T * k <= 2^22.  The bf16 matrix-core paths are taken when
+ * H % 128 == 0 and I % 64 == 0, Is % 64 == 0 (expert products) and
+ * E % 16 == 0, E <= 128 (fused router); other shapes and MOE_F32 run portable
+ * kernels of the same library.
+ */
+#ifndef TALKER_MOE_H
+#define TALKER_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define MOE_OK 0
+#define MOE_ERR_INVALID (-1)     /* bad argument: NULL required pointer, T < 0, k > E, misaligned pointer, ... */
+#define MOE_ERR_UNSUPPORTED (-2) /* valid but outside the supported shapes / dtypes */
+#define MOE_ERR_WORKSPACE (-3)   /* ws_bytes below what the call needs */
+#define MOE_ERR_HIP (-4)         /* a HIP launch failed */
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Layer configuration, named after the model's configuration fields
+ * (openarchlab Talker MoE page, §1). */
+typedef struct moe_config {
+    int32_t hidden_size;                     /* H (1024) */
+    int32_t num_experts;                     /* E (128) */
+    int32_t num_experts_per_tok;             /* k (6) */
+    int32_t moe_intermediate_size;           /* I (384) */
+    int32_t shared_expert_intermediate_size; /* Is (768); 0 = no shared expert */
+    int32_t norm_topk_prob;                  /* 1: w_i = p_i / sum_S p; 0: w_i = p_i */
+    int32_t dtype;                           /* moe_dtype */
+} moe_config;
+
+/* Weights of one layer; every pointer [dev]. */
+typedef struct moe_weights {
+    const void* router;       /* [E, H] */
+    const float* router_bias; /* [E] fp32 added to the router scores, or NULL */
+    const void* gate;         /* [E, I, H] */
+    const void* up;           /* [E, I, H] */
+    const void* down;         /* [E, H, I] */
+    const void* shared_gate;  /* [Is, H]  (NULL when Is == 0) */
+    const void* shared_up;    /* [Is, H]  (NULL when Is == 0) */
+    const void* shared_down;  /* [H, Is]  (NULL when Is == 0) */
+} moe_weights;
+
+/* Text for a status code (static storage). */
+const char* moe_status_string(int status);
+
+/* MOE_OK if cfg is a valid, supported configuration, else the status a call
+ * with it would return.  Host only. */
+int moe_check_config(const moe_config* cfg);
+
+/* Workspace bytes that suffice for any entry point below at T tokens
+ * (0 on an invalid configuration).  Host only. */
+size_t moe_workspace_size(const moe_config* cfg, int64_t T);
+
+/*
+ * moe_route — router, softmax, Top-k and renormalisation (Talker MoE page §3).
+ *   x        [dev] [T, H] token hidden states
+ *   router   [dev] [E, H] router weight W_r
+ *   bias     [dev] [E] fp32 score bias, or NULL
+ *   topk_idx [dev] [T, k] int32 out: selected experts, largest weight first,
+ *                  equal scores in ascending expert index
+ *   topk_w   [dev] [T, k] fp32 out: w_i (renormalised when cfg->norm_topk_prob)
+ *   probs    [dev] [T, E] fp32 out: the full softmax p, or NULL to skip
+ */
+int moe_route(const moe_config* cfg, const void* x, const void* router, const float* bias,
+              int64_t T, int32_t* topk_idx, float* topk_w, float* probs,
+              void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_permute — group the T*k (token, slot) pairs by expert (a stable counting
+ * sort; the data layout that lets each expert run as one matrix product).
+ *   topk_idx  [dev] [T, k] int32, every entry in [0, E)
+ *   counts    [dev] [E] int32 out: pairs per expert
+ *   offsets   [dev] [E+1] int32 out: exclusive prefix sum of counts
+ *   row_token [dev] [T*k] int32 out: token of grouped row r; rows of one expert
+ *                   are consecutive and in ascending (token, slot) order
+ *   row_of    [dev] [T, k] int32 out: grouped row of pair (t, j)
+ *   x, x_perm [dev] optional gather: when both are non-NULL,
+ *                   x_perm[r, :] = x[row_token[r], :]  ([T*k, H])
+ */
+int moe_permute(const moe_config* cfg, const int32_t* topk_idx, int64_t T,
+                int32_t* counts, int32_t* offsets, int32_t* row_token, int32_t* row_of,
+                const void* x, void* x_perm, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_grouped_swiglu — every routed expert applied to its grouped rows
+ * (Talker MoE page §1: each expert is a SwiGLU 1024 -> 384 -> 1024).
+ *   x         [dev] [T, H] hidden states, or [T*k, H] already grouped when
+ *                   row_token is NULL
+ *   row_token [dev] [T*k] from moe_permute, or NULL (x already grouped)
+ *   offsets   [dev] [E+1] from moe_permute
+ *   gate, up  [dev] [E, I, H];  down [dev] [E, H, I]
+ *   y_perm    [dev] [T*k, H] out: y_perm[r] = Expert_e(x_r) for grouped row r
+ *                   of expert e (unweighted)
+ */
+int moe_grouped_swiglu(const moe_config* cfg, const void* x, const int32_t* row_token,
+                       const int32_t* offsets, int64_t T, const void* gate, const void* up,
+                       const void* down, void* y_perm, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_shared_swiglu — the always-on shared expert (Talker MoE page §1, §3:
+ * SharedMLP(x), intermediate 768).
+ *   x [dev] [T, H];  sg, su [dev] [Is, H];  sd [dev] [H, Is]
+ *   y_shared [dev] [T, H] out
+ * Returns MOE_ERR_INVALID when cfg has Is == 0.
+ */
+int moe_shared_swiglu(const moe_config* cfg, const void* x, int64_t T, const void* sg,
+                      const void* su, const void* sd, void* y_shared,
+                      void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_combine — weighted sum of the expert outputs (Talker MoE page §3):
+ *   y[t] = y_shared[t] + sum_{j<k} topk_w[t,j] * y_perm[row_of[t,j]] + residual[t]
+ * accumulated in fp32 in that order (shared, slots 0..k-1, residual).
+ *   y_perm [dev] [T*k, H];  row_of [dev] [T, k];  topk_w [dev] [T, k] fp32
+ *   y_shared, residual [dev] [T, H] or NULL (term omitted)
+ *   y [dev] [T, H] out (may alias residual)
+ */
+int moe_combine(const moe_config* cfg, const void* y_perm, const int32_t* row_of,
+                const float* topk_w, const void* y_shared, const void* residual,
+                int64_t T, void* y, void* stream);
+
+/*
+ * moe_layer_forward — the whole layer: route, group, routed and shared SwiGLU
+ * experts, combine (Talker MoE page §3 equation), plus an optional residual
+ * add (the [3C] step of the lab on "Bài Lab tổng hợp — Qwen3-Omni &
+ * Qwen3-TTS-12Hz Architecture" adds the layer input back).
+ *   w        host struct of [dev] weight pointers
+ *   x        [dev] [T, H];  residual [dev] [T, H] or NULL
+ *   y        [dev] [T, H] out (must not alias x; may alias residual)
+ *   topk_idx_out [dev] [T, k] int32, topk_w_out [dev] [T, k] fp32,
+ *   counts_out   [dev] [E] int32: optional copies of the routing, or NULL
+ */
+int moe_layer_forward(const moe_config* cfg, const moe_weights* w, const void* x,
+                      const void* residual, int64_t T, void* y, int32_t* topk_idx_out,
+                      float* topk_w_out, int32_t* counts_out,
+                      void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_rmsnorm — out = x / sqrt(mean(x^2) + eps) * gain over each row of H
+ * (the pre-norm of the lab's [3C] step; eps 1e-6 and the final norm before
+ * codec_head from the Qwen3-TTS module print on the horus-space page).
+ *   x [dev] [T, H] (cfg->dtype);  gain [dev] [H] fp32;  out [dev] [T, H] (may alias x)
+ */
+int moe_rmsnorm(const moe_config* cfg, const void* x, const float* gain, float eps,
+                int64_t T, void* out, void* stream);
+
+/*
+ * moe_codec_head_argmax — c_0 = argmax_v (W_c x)_v, the first codec code
+ * (Talker MoE page §1: codec_head Linear 1024 -> 3072 after the last layer;
+ * the lab picks the argmax).  Exact like the routing: ties go to the lowest v.
+ *   x [dev] [T, H];  w_head [dev] [V, H] (cfg->dtype, bias-free)
+ *   logits [dev] [T, V] fp32 out, or NULL;  c0 [dev] [T] int32 out
+ */
+int moe_codec_head_argmax(const moe_config* cfg, const void* x, const void* w_head, int32_t V,
+                          int64_t T, float* logits, int32_t* c0,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes for moe_codec_head_argmax at (V, T). Host only. */
+size_t moe_codec_head_workspace_size(const moe_config* cfg, int32_t V, int64_t T);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TALKER_MOE_H */

@@ -1,0 +1,275 @@
+"""Python binding of libtalker_moe.so (ctypes): argument marshalling only.
+
+Every function has the name of the C entry point it calls and takes torch
+tensors that live on the GPU; torch supplies device memory and the current HIP
+stream, all arithmetic runs in the library's kernels.  Outputs not passed in
+are allocated with ``torch.empty``.  A nonzero status raises :class:`MoeError`.
+
+Loading fails loudly when the library has not been built; there is no CPU or
+PyTorch fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Dict, Optional
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtalker_moe.so")
+
+MOE_F32, MOE_BF16 = 0, 1
+STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID", -2: "MOE_ERR_UNSUPPORTED", -3: "MOE_ERR_WORKSPACE", -4: "MOE_ERR_HIP"}
+
+EXPORTS = ("moe_status_string", "moe_check_config", "moe_workspace_size", "moe_route", "moe_permute",
+           "moe_grouped_swiglu", "moe_shared_swiglu", "moe_combine", "moe_layer_forward", "moe_rmsnorm",
+           "moe_codec_head_argmax", "moe_codec_head_workspace_size")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, status: int, text: str):
+        super().__init__("%s failed: %s (%s)" % (fn, STATUS.get(status, status), text))
+        self.status = status
+
+
+class moe_config(ctypes.Structure):
+    _fields_ = [("hidden_size", ctypes.c_int32), ("num_experts", ctypes.c_int32),
+                ("num_experts_per_tok", ctypes.c_int32), ("moe_intermediate_size", ctypes.c_int32),
+                ("shared_expert_intermediate_size", ctypes.c_int32), ("norm_topk_prob", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
+
+
+class moe_weights(ctypes.Structure):
+    _fields_ = [("router", ctypes.c_void_p), ("router_bias", ctypes.c_void_p), ("gate", ctypes.c_void_p),
+                ("up", ctypes.c_void_p), ("down", ctypes.c_void_p), ("shared_gate", ctypes.c_void_p),
+                ("shared_up", ctypes.c_void_p), ("shared_down", ctypes.c_void_p)]
+
+
+@dataclasses.dataclass(frozen=True)
+class Config:
+    """Layer configuration (field names as in the model configuration)."""
+    hidden_size: int
+    num_experts: int
+    num_experts_per_tok: int
+    moe_intermediate_size: int
+    shared_expert_intermediate_size: int
+    norm_topk_prob: bool = True
+    dtype: torch.dtype = torch.bfloat16
+
+    def c(self) -> moe_config:
+        if self.dtype not in (torch.bfloat16, torch.float32):
+            raise TypeError("dtype must be torch.bfloat16 or torch.float32")
+        return moe_config(self.hidden_size, self.num_experts, self.num_experts_per_tok,
+                          self.moe_intermediate_size, self.shared_expert_intermediate_size,
+                          1 if self.norm_topk_prob else 0,
+                          MOE_BF16 if self.dtype == torch.bfloat16 else MOE_F32)
+
+
+_lib = None
+
+
+def load_library(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load the HIP library (once).  Raises if it is missing: build it first."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError("libtalker_moe.so not found at %s; build it with "
+                           "`python -m sparse_moe_transformer_talker_amd.build`" % p)
+    lib = ctypes.CDLL(p)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    cfgp = ctypes.POINTER(moe_config)
+    sig = {
+        "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "moe_check_config": (ctypes.c_int, [cfgp]),
+        "moe_workspace_size": (sz, [cfgp, i64]),
+        "moe_route": (ctypes.c_int, [cfgp, vp, vp, vp, i64, vp, vp, vp, vp, sz, vp]),
+        "moe_permute": (ctypes.c_int, [cfgp, vp, i64, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "moe_grouped_swiglu": (ctypes.c_int, [cfgp, vp, vp, vp, i64, vp, vp, vp, vp, vp, sz, vp]),
+        "moe_shared_swiglu": (ctypes.c_int, [cfgp, vp, i64, vp, vp, vp, vp, vp, sz, vp]),
+        "moe_combine": (ctypes.c_int, [cfgp, vp, vp, vp, vp, vp, i64, vp, vp]),
+        "moe_layer_forward": (ctypes.c_int, [cfgp, ctypes.POINTER(moe_weights), vp, vp, i64, vp, vp, vp, vp,
+                                             vp, sz, vp]),
+        "moe_rmsnorm": (ctypes.c_int, [cfgp, vp, vp, ctypes.c_float, i64, vp, vp]),
+        "moe_codec_head_argmax": (ctypes.c_int, [cfgp, vp, vp, i32, i64, vp, vp, vp, sz, vp]),
+        "moe_codec_head_workspace_size": (sz, [cfgp, i32, i64]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().moe_status_string(status).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise MoeError(fn, status, status_string(status))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+_ws_cache: Dict[int, torch.Tensor] = {}
+
+
+def workspace(nbytes: int, device: torch.device) -> torch.Tensor:
+    """A cached device workspace of at least nbytes (one per device, stream-ordered use)."""
+    dev = torch.device(device).index or 0
+    buf = _ws_cache.get(dev)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=torch.device("cuda", dev))
+        _ws_cache[dev] = buf
+    return buf
+
+
+def moe_check_config(cfg: Config) -> int:
+    return load_library().moe_check_config(ctypes.byref(cfg.c()))
+
+
+def moe_workspace_size(cfg: Config, T: int) -> int:
+    return int(load_library().moe_workspace_size(ctypes.byref(cfg.c()), T))
+
+
+def _ws(cfg: Config, T: int, device, ws: Optional[torch.Tensor]):
+    n = moe_workspace_size(cfg, T)
+    buf = ws if ws is not None else workspace(n, device)
+    return buf, n if ws is None else buf.numel()
+
+
+def moe_route(cfg: Config, x: torch.Tensor, router: torch.Tensor, bias: Optional[torch.Tensor] = None,
+              want_probs: bool = False, topk_idx=None, topk_w=None, probs=None, ws=None):
+    """Router + softmax + exact Top-k + renormalisation.  Returns (idx, w, probs or None)."""
+    T = x.shape[0]
+    k, E = cfg.num_experts_per_tok, cfg.num_experts
+    dev = x.device
+    topk_idx = topk_idx if topk_idx is not None else torch.empty((T, k), dtype=torch.int32, device=dev)
+    topk_w = topk_w if topk_w is not None else torch.empty((T, k), dtype=torch.float32, device=dev)
+    if want_probs and probs is None:
+        probs = torch.empty((T, E), dtype=torch.float32, device=dev)
+    buf, n = _ws(cfg, T, dev, ws)
+    _check("moe_route", load_library().moe_route(
+        ctypes.byref(cfg.c()), _ptr(x), _ptr(router), _ptr(bias), T, _ptr(topk_idx), _ptr(topk_w), _ptr(probs),
+        _ptr(buf), n, _stream(dev)))
+    return topk_idx, topk_w, probs
+
+
+def moe_permute(cfg: Config, topk_idx: torch.Tensor, x: Optional[torch.Tensor] = None, ws=None):
+    """Stable grouping by expert.  Returns dict(counts, offsets, row_token, row_of[, x_perm])."""
+    T, k = topk_idx.shape
+    E, dev = cfg.num_experts, topk_idx.device
+    out = {"counts": torch.empty(E, dtype=torch.int32, device=dev),
+           "offsets": torch.empty(E + 1, dtype=torch.int32, device=dev),
+           "row_token": torch.empty(T * k, dtype=torch.int32, device=dev),
+           "row_of": torch.empty((T, k), dtype=torch.int32, device=dev)}
+    if x is not None:
+        out["x_perm"] = torch.empty((T * k, x.shape[1]), dtype=x.dtype, device=dev)
+    buf, n = _ws(cfg, T, dev, ws)
+    _check("moe_permute", load_library().moe_permute(
+        ctypes.byref(cfg.c()), _ptr(topk_idx), T, _ptr(out["counts"]), _ptr(out["offsets"]),
+        _ptr(out["row_token"]), _ptr(out["row_of"]), _ptr(x), _ptr(out.get("x_perm")), _ptr(buf), n,
+        _stream(dev)))
+    return out
+
+
+def moe_grouped_swiglu(cfg: Config, x: torch.Tensor, row_token: Optional[torch.Tensor], offsets: torch.Tensor,
+                       T: int, gate: torch.Tensor, up: torch.Tensor, down: torch.Tensor, y_perm=None, ws=None):
+    """Routed experts on their grouped rows (unweighted).  Returns y_perm [T*k, H]."""
+    dev = x.device
+    y_perm = y_perm if y_perm is not None else torch.empty((T * cfg.num_experts_per_tok, cfg.hidden_size),
+                                                           dtype=x.dtype, device=dev)
+    buf, n = _ws(cfg, T, dev, ws)
+    _check("moe_grouped_swiglu", load_library().moe_grouped_swiglu(
+        ctypes.byref(cfg.c()), _ptr(x), _ptr(row_token), _ptr(offsets), T, _ptr(gate), _ptr(up), _ptr(down),
+        _ptr(y_perm), _ptr(buf), n, _stream(dev)))
+    return y_perm
+
+
+def moe_shared_swiglu(cfg: Config, x: torch.Tensor, sg: torch.Tensor, su: torch.Tensor, sd: torch.Tensor,
+                      y_shared=None, ws=None):
+    """The shared expert on every token.  Returns y_shared [T, H]."""
+    T, dev = x.shape[0], x.device
+    y_shared = y_shared if y_shared is not None else torch.empty_like(x)
+    buf, n = _ws(cfg, T, dev, ws)
+    _check("moe_shared_swiglu", load_library().moe_shared_swiglu(
+        ctypes.byref(cfg.c()), _ptr(x), T, _ptr(sg), _ptr(su), _ptr(sd), _ptr(y_shared), _ptr(buf), n,
+        _stream(dev)))
+    return y_shared
+
+
+def moe_combine(cfg: Config, y_perm: torch.Tensor, row_of: torch.Tensor, topk_w: torch.Tensor,
+                y_shared: Optional[torch.Tensor] = None, residual: Optional[torch.Tensor] = None, y=None):
+    """Weighted combine of expert outputs (+ shared, + residual).  Returns y [T, H]."""
+    T = row_of.shape[0]
+    dev = y_perm.device
+    y = y if y is not None else torch.empty((T, cfg.hidden_size), dtype=y_perm.dtype, device=dev)
+    _check("moe_combine", load_library().moe_combine(
+        ctypes.byref(cfg.c()), _ptr(y_perm), _ptr(row_of), _ptr(topk_w), _ptr(y_shared), _ptr(residual), T,
+        _ptr(y), _stream(dev)))
+    return y
+
+
+def weights_struct(w: Dict[str, Optional[torch.Tensor]]) -> moe_weights:
+    """moe_weights from a dict of device tensors (keys as in the C struct)."""
+    p = lambda name: (None if w.get(name) is None else _ptr(w[name]))
+    return moe_weights(p("router"), p("router_bias"), p("gate"), p("up"), p("down"), p("shared_gate"),
+                       p("shared_up"), p("shared_down"))
+
+
+def moe_layer_forward(cfg: Config, weights, x: torch.Tensor, residual: Optional[torch.Tensor] = None,
+                      y=None, topk_idx=None, topk_w=None, counts=None, ws=None, stream=None):
+    """The whole MoE layer.  ``weights``: dict of device tensors or a prebuilt moe_weights.
+    Returns y [T, H] (routing copies are written to the optional tensors)."""
+    T, dev = x.shape[0], x.device
+    y = y if y is not None else torch.empty_like(x)
+    ws_struct = weights if isinstance(weights, moe_weights) else weights_struct(weights)
+    buf, n = _ws(cfg, T, dev, ws)
+    st = stream if stream is not None else _stream(dev)
+    _check("moe_layer_forward", load_library().moe_layer_forward(
+        ctypes.byref(cfg.c()), ctypes.byref(ws_struct), _ptr(x), _ptr(residual), T, _ptr(y), _ptr(topk_idx),
+        _ptr(topk_w), _ptr(counts), _ptr(buf), n, st))
+    return y
+
+
+def moe_rmsnorm(cfg: Config, x: torch.Tensor, gain: torch.Tensor, eps: float = 1e-6, out=None):
+    """Row RMSNorm.  Returns out [T, H]."""
+    T, dev = x.shape[0], x.device
+    out = out if out is not None else torch.empty_like(x)
+    _check("moe_rmsnorm", load_library().moe_rmsnorm(
+        ctypes.byref(cfg.c()), _ptr(x), _ptr(gain), eps, T, _ptr(out), _stream(dev)))
+    return out
+
+
+def moe_codec_head_argmax(cfg: Config, x: torch.Tensor, w_head: torch.Tensor, want_logits: bool = False,
+                          c0=None, logits=None, ws=None):
+    """codec_head + exact argmax.  Returns (c0 [T] int32, logits [T, V] fp32 or None)."""
+    T, dev = x.shape[0], x.device
+    V = w_head.shape[0]
+    c0 = c0 if c0 is not None else torch.empty(T, dtype=torch.int32, device=dev)
+    if want_logits and logits is None:
+        logits = torch.empty((T, V), dtype=torch.float32, device=dev)
+    lib = load_library()
+    need = int(lib.moe_codec_head_workspace_size(ctypes.byref(cfg.c()), V, T))
+    buf = ws if ws is not None else workspace(need, dev)
+    _check("moe_codec_head_argmax", lib.moe_codec_head_argmax(
+        ctypes.byref(cfg.c()), _ptr(x), _ptr(w_head), V, T, _ptr(logits), _ptr(c0), _ptr(buf), buf.numel(),
+        _stream(dev)))
+    return c0, logits

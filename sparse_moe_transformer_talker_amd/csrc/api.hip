@@ -1,0 +1,451 @@
+// C ABI of libtalker_moe.so (declared in include/talker_moe.h): argument
+// checks, workspace carving and the launch sequence of each entry point.
+// Every check runs on the host before anything is enqueued; the library never
+// allocates or synchronises.
+#include "talker_moe.h"
+
+#include <stdint.h>
+
+#include "kernels.hpp"
+
+using namespace tmoe;
+
+namespace {
+
+constexpr int64_t kMaxPairs = int64_t(1) << 22;
+constexpr int kMaxDim = 16384;
+
+// Carves 256-byte aligned regions out of the caller's workspace; with a null
+// base it only measures.
+struct Carver {
+    char* base;
+    size_t off = 0;
+    explicit Carver(void* b) : base(static_cast<char*>(b)) {}
+    template <class T>
+    T* take(int64_t n) {
+        off = (off + 255) & ~size_t(255);
+        T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+        off += size_t(n > 0 ? n : 0) * sizeof(T);
+        return p;
+    }
+    size_t size() const { return (off + 255) & ~size_t(255); }
+};
+
+size_t esize(int dtype) { return dtype == MOE_BF16 ? 2 : 4; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+bool ok_ptr(const void* p) { return p != nullptr && aligned16(p); }
+bool ok_opt(const void* p) { return p == nullptr || aligned16(p); }
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+int check_cfg(const moe_config* c) {
+    if (!c) return MOE_ERR_INVALID;
+    if (c->dtype != MOE_F32 && c->dtype != MOE_BF16) return MOE_ERR_INVALID;
+    if (c->hidden_size < 1 || c->num_experts < 1 || c->num_experts_per_tok < 1 || c->moe_intermediate_size < 1 ||
+        c->shared_expert_intermediate_size < 0)
+        return MOE_ERR_INVALID;
+    if (c->num_experts_per_tok > c->num_experts) return MOE_ERR_INVALID;
+    if (c->norm_topk_prob != 0 && c->norm_topk_prob != 1) return MOE_ERR_INVALID;
+    if (c->num_experts > kMaxExperts || c->num_experts_per_tok > kMaxTopK || c->hidden_size > kMaxDim ||
+        c->moe_intermediate_size > kMaxDim || c->shared_expert_intermediate_size > kMaxDim)
+        return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+int check_T(const moe_config* c, int64_t T) {
+    if (T < 0) return MOE_ERR_INVALID;
+    if (T * c->num_experts_per_tok > kMaxPairs) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+// --- workspace plans ---------------------------------------------------------
+struct RoutePlan {
+    float* sc = nullptr;
+    float* bd = nullptr;
+};
+void plan_route(const moe_config* c, int64_t T, Carver& cv, RoutePlan& p) {
+    if (!route_fused_ok(c->dtype, c->hidden_size, c->num_experts)) {
+        p.sc = cv.take<float>(T * c->num_experts);
+        p.bd = cv.take<float>(T * c->num_experts);
+    }
+}
+
+struct GemmPlan {
+    bool mfma = false;
+    int variant = kGemmSmallM;
+    TileSpec t[2]{};
+    int64_t max_items[2]{0, 0};
+};
+// Tile lists for the two passes when the matrix-core path applies.
+void plan_gemm(const moe_config* c, int64_t T, bool routed, bool shared, Carver& cv, GemmPlan& g) {
+    const int H = c->hidden_size, E = c->num_experts, k = c->num_experts_per_tok;
+    const int I = c->moe_intermediate_size, Is = shared ? c->shared_expert_intermediate_size : 0;
+    g.mfma = gemm_mfma_ok(c->dtype, H, I, Is);
+    if (!g.mfma) return;
+    const int64_t pairs = routed ? T * k : 0;
+    const int64_t rows_per_expert = routed ? pairs / E : T;
+    g.variant = rows_per_expert >= 32 ? kGemmLargeM : kGemmSmallM;
+    int* counters = cv.take<int>(4);
+    for (int pass = 0; pass < 2; ++pass) {
+        int mt, nt;
+        gemm_tiles(g.variant, pass, &mt, &nt);
+        const int n_routed = pass == 0 ? I : H;
+        const int n_shared = Is > 0 ? (pass == 0 ? Is : H) : 0;
+        g.max_items[pass] = tile_max_items(pairs, routed ? E : 0, T, mt, nt, n_routed, n_shared);
+        TileSpec& ts = g.t[pass];
+        ts.mt = mt;
+        ts.nt = nt;
+        ts.n_routed = n_routed;
+        ts.n_shared = n_shared;
+        ts.items = cv.take<int4>(g.max_items[pass]);
+        ts.count = counters ? counters + pass : nullptr;
+        ts.max_items = (int)g.max_items[pass];
+    }
+}
+
+struct LayerPlan {
+    int32_t* idx;
+    float* w;
+    RoutePlan route;
+    int32_t *counts, *offsets, *hist, *row_token, *row_of, *row_dst;
+    float* row_scale;
+    GemmPlan gemm;
+    void *hr, *hs, *ybuf;
+};
+void plan_layer(const moe_config* c, int64_t T, Carver& cv, LayerPlan& p) {
+    const int E = c->num_experts, k = c->num_experts_per_tok, H = c->hidden_size;
+    const int I = c->moe_intermediate_size, Is = c->shared_expert_intermediate_size;
+    const int64_t N = T * k;
+    const int64_t nb = (N + kPermChunk - 1) / kPermChunk;
+    const size_t es = esize(c->dtype);
+    p.idx = cv.take<int32_t>(N);
+    p.w = cv.take<float>(N);
+    plan_route(c, T, cv, p.route);
+    p.counts = cv.take<int32_t>(E);
+    p.offsets = cv.take<int32_t>(E + 1);
+    p.hist = cv.take<int32_t>(nb * E);
+    p.row_token = cv.take<int32_t>(N);
+    p.row_of = cv.take<int32_t>(N);
+    p.row_dst = cv.take<int32_t>(N);
+    p.row_scale = cv.take<float>(N);
+    plan_gemm(c, T, true, Is > 0, cv, p.gemm);
+    p.hr = cv.take<char>(N * I * (int64_t)es);
+    p.hs = cv.take<char>(T * Is * (int64_t)es);
+    p.ybuf = cv.take<char>(T * (k + 1) * (int64_t)H * (int64_t)es);
+}
+
+size_t route_ws(const moe_config* c, int64_t T) {
+    Carver cv(nullptr);
+    RoutePlan p;
+    plan_route(c, T, cv, p);
+    return cv.size();
+}
+size_t permute_ws(const moe_config* c, int64_t T) {
+    Carver cv(nullptr);
+    cv.take<int32_t>(((T * c->num_experts_per_tok + kPermChunk - 1) / kPermChunk) * c->num_experts);
+    return cv.size();
+}
+size_t grouped_ws(const moe_config* c, int64_t T, void* base, GemmPlan* g, void** hr) {
+    Carver cv(base);
+    GemmPlan tmp;
+    plan_gemm(c, T, true, false, cv, g ? *g : tmp);
+    void* h = cv.take<char>(T * c->num_experts_per_tok * (int64_t)c->moe_intermediate_size * (int64_t)esize(c->dtype));
+    if (hr) *hr = h;
+    return cv.size();
+}
+size_t shared_ws(const moe_config* c, int64_t T, void* base, GemmPlan* g, void** hs) {
+    Carver cv(base);
+    GemmPlan tmp;
+    plan_gemm(c, T, false, true, cv, g ? *g : tmp);
+    void* h = cv.take<char>(T * (int64_t)c->shared_expert_intermediate_size * (int64_t)esize(c->dtype));
+    if (hs) *hs = h;
+    return cv.size();
+}
+size_t layer_ws(const moe_config* c, int64_t T) {
+    Carver cv(nullptr);
+    LayerPlan p;
+    plan_layer(c, T, cv, p);
+    return cv.size();
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+#define TMOE_TRY(expr)                                \
+    do {                                              \
+        hipError_t _e = (expr);                       \
+        if (_e != hipSuccess) return MOE_ERR_HIP;     \
+    } while (0)
+
+// The two passes of the grouped SwiGLU experts over a plan's tile lists, or the
+// portable kernels.  g0 / g1 describe routed / shared work (g1.N == 0: none).
+int run_gemm_pass(const moe_config* c, const GemmPlan& plan, int pass, const GemmGroup& g0, const GemmGroup& g1,
+                  const int32_t* offsets, int64_t routed_rows, int64_t T, hipStream_t st) {
+    if (plan.mfma) {
+        GemmArgs a{};
+        a.g[0] = g0;
+        a.g[1] = g1;
+        a.items = plan.t[pass].items;
+        a.count = plan.t[pass].count;
+        a.E = routed_rows > 0 ? c->num_experts : 0;
+        TMOE_TRY(launch_grouped_gemm(c->dtype, plan.variant, pass, a, plan.max_items[pass], st));
+        return MOE_OK;
+    }
+    if (routed_rows > 0) TMOE_TRY(launch_gemm_generic(c->dtype, pass, g0, offsets, 0, c->num_experts, routed_rows, st));
+    if (g1.N > 0 && T > 0) TMOE_TRY(launch_gemm_generic(c->dtype, pass, g1, nullptr, 0, 1, T, st));
+    return MOE_OK;
+}
+
+GemmGroup group(const void* wa, const void* wb, int64_t estride, int N, int K, const void* a, int64_t a_ld,
+                const int32_t* a_rows, void* out, int64_t out_ld, const int32_t* out_rows, int mul, int add,
+                const float* scale) {
+    GemmGroup g;
+    g.wa = wa;
+    g.wb = wb;
+    g.w_estride = estride;
+    g.N = N;
+    g.K = K;
+    g.a = a;
+    g.a_ld = a_ld;
+    g.a_rows = a_rows;
+    g.out = out;
+    g.out_ld = out_ld;
+    g.out_rows = out_rows;
+    g.out_mul = mul;
+    g.out_add = add;
+    g.out_scale = scale;
+    return g;
+}
+
+GemmGroup no_group() {
+    GemmGroup g{};
+    g.N = 0;
+    return g;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int status) {
+    switch (status) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_INVALID: return "invalid argument";
+        case MOE_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+        case MOE_ERR_WORKSPACE: return "workspace too small";
+        case MOE_ERR_HIP: return "HIP launch failed";
+        default: return "unknown status";
+    }
+}
+
+int moe_check_config(const moe_config* cfg) { return check_cfg(cfg); }
+
+size_t moe_workspace_size(const moe_config* cfg, int64_t T) {
+    if (check_cfg(cfg) != MOE_OK || check_T(cfg, T) != MOE_OK) return 0;
+    size_t s = layer_ws(cfg, T);
+    s = s > route_ws(cfg, T) ? s : route_ws(cfg, T);
+    s = s > permute_ws(cfg, T) ? s : permute_ws(cfg, T);
+    size_t g = grouped_ws(cfg, T, nullptr, nullptr, nullptr);
+    s = s > g ? s : g;
+    if (cfg->shared_expert_intermediate_size > 0) {
+        size_t h = shared_ws(cfg, T, nullptr, nullptr, nullptr);
+        s = s > h ? s : h;
+    }
+    return s < 256 ? 256 : s;
+}
+
+int moe_route(const moe_config* cfg, const void* x, const void* router, const float* bias, int64_t T,
+              int32_t* topk_idx, float* topk_w, float* probs, void* ws, size_t ws_bytes, void* stream) {
+    int st = check_cfg(cfg);
+    if (st != MOE_OK) return st;
+    if ((st = check_T(cfg, T)) != MOE_OK) return st;
+    if (T == 0) return MOE_OK;
+    if (!ok_ptr(x) || !ok_ptr(router) || !ok_ptr(topk_idx) || !ok_ptr(topk_w) || !ok_opt(bias) || !ok_opt(probs) ||
+        !ok_opt(ws))
+        return MOE_ERR_INVALID;
+    if (ws_bytes < route_ws(cfg, T) || (route_ws(cfg, T) > 0 && !ws)) return MOE_ERR_WORKSPACE;
+    Carver cv(ws);
+    RoutePlan p;
+    plan_route(cfg, T, cv, p);
+    return hip_status(launch_route(cfg->dtype, x, router, bias, T, cfg->hidden_size, cfg->num_experts,
+                                   cfg->num_experts_per_tok, cfg->norm_topk_prob, topk_idx, topk_w, probs, p.sc, p.bd,
+                                   as_stream(stream)));
+}
+
+int moe_permute(const moe_config* cfg, const int32_t* topk_idx, int64_t T, int32_t* counts, int32_t* offsets,
+                int32_t* row_token, int32_t* row_of, const void* x, void* x_perm, void* ws, size_t ws_bytes,
+                void* stream) {
+    int st = check_cfg(cfg);
+    if (st != MOE_OK) return st;
+    if ((st = check_T(cfg, T)) != MOE_OK) return st;
+    const int E = cfg->num_experts, k = cfg->num_experts_per_tok;
+    hipStream_t s = as_stream(stream);
+    if (!ok_ptr(counts) || !ok_ptr(offsets)) return MOE_ERR_INVALID;
+    if (T == 0) {
+        // an empty routing still has well-defined counts and offsets
+        TMOE_TRY(launch_fill_i32(counts, 0, E, s));
+        TMOE_TRY(launch_fill_i32(offsets, 0, E + 1, s));
+        return MOE_OK;
+    }
+    if (!ok_ptr(topk_idx) || !ok_ptr(row_token) || !ok_ptr(row_of) || !ok_opt(x) || !ok_opt(x_perm) || !ok_ptr(ws))
+        return MOE_ERR_INVALID;
+    if ((x == nullptr) != (x_perm == nullptr)) return MOE_ERR_INVALID;
+    if (ws_bytes < permute_ws(cfg, T)) return MOE_ERR_WORKSPACE;
+    Carver cv(ws);
+    int32_t* hist = cv.take<int32_t>(((T * k + kPermChunk - 1) / kPermChunk) * E);
+    TMOE_TRY(launch_permute(topk_idx, T, k, E, hist, counts, offsets, row_token, row_of, nullptr, nullptr, nullptr, 0,
+                            nullptr, nullptr, s));
+    if (x) TMOE_TRY(launch_gather_rows(cfg->dtype, x, row_token, T * k, cfg->hidden_size, x_perm, s));
+    return MOE_OK;
+}
+
+int moe_grouped_swiglu(const moe_config* cfg, const void* x, const int32_t* row_token, const int32_t* offsets,
+                       int64_t T, const void* gate, const void* up, const void* down, void* y_perm, void* ws,
+                       size_t ws_bytes, void* stream) {
+    int st = check_cfg(cfg);
+    if (st != MOE_OK) return st;
+    if ((st = check_T(cfg, T)) != MOE_OK) return st;
+    if (T == 0) return MOE_OK;
+    if (!ok_ptr(x) || !ok_opt(row_token) || !ok_ptr(offsets) || !ok_ptr(gate) || !ok_ptr(up) || !ok_ptr(down) ||
+        !ok_ptr(y_perm) || !ok_ptr(ws))
+        return MOE_ERR_INVALID;
+    if (ws_bytes < grouped_ws(cfg, T, nullptr, nullptr, nullptr)) return MOE_ERR_WORKSPACE;
+    const int H = cfg->hidden_size, I = cfg->moe_intermediate_size, E = cfg->num_experts;
+    const int64_t N = T * cfg->num_experts_per_tok;
+    GemmPlan plan;
+    void* hr = nullptr;
+    grouped_ws(cfg, T, ws, &plan, &hr);
+    hipStream_t s = as_stream(stream);
+    if (plan.mfma) TMOE_TRY(launch_build_items(offsets, E, T, &plan.t[0], &plan.t[1], s));
+    GemmGroup gu = group(gate, up, (int64_t)I * H, I, H, x, H, row_token, hr, I, nullptr, 1, 0, nullptr);
+    int r = run_gemm_pass(cfg, plan, 0, gu, no_group(), offsets, N, 0, s);
+    if (r != MOE_OK) return r;
+    GemmGroup dn = group(down, nullptr, (int64_t)H * I, H, I, hr, I, nullptr, y_perm, H, nullptr, 1, 0, nullptr);
+    return run_gemm_pass(cfg, plan, 1, dn, no_group(), offsets, N, 0, s);
+}
+
+int moe_shared_swiglu(const moe_config* cfg, const void* x, int64_t T, const void* sg, const void* su,
+                      const void* sd, void* y_shared, void* ws, size_t ws_bytes, void* stream) {
+    int st = check_cfg(cfg);
+    if (st != MOE_OK) return st;
+    if ((st = check_T(cfg, T)) != MOE_OK) return st;
+    const int Is = cfg->shared_expert_intermediate_size;
+    if (Is == 0) return MOE_ERR_INVALID;
+    if (T == 0) return MOE_OK;
+    if (!ok_ptr(x) || !ok_ptr(sg) || !ok_ptr(su) || !ok_ptr(sd) || !ok_ptr(y_shared) || !ok_ptr(ws))
+        return MOE_ERR_INVALID;
+    if (ws_bytes < shared_ws(cfg, T, nullptr, nullptr, nullptr)) return MOE_ERR_WORKSPACE;
+    const int H = cfg->hidden_size;
+    GemmPlan plan;
+    void* hs = nullptr;
+    shared_ws(cfg, T, ws, &plan, &hs);
+    hipStream_t s = as_stream(stream);
+    if (plan.mfma) TMOE_TRY(launch_build_items(nullptr, 0, T, &plan.t[0], &plan.t[1], s));
+    GemmGroup gu = group(sg, su, 0, Is, H, x, H, nullptr, hs, Is, nullptr, 1, 0, nullptr);
+    int r = run_gemm_pass(cfg, plan, 0, no_group(), gu, nullptr, 0, T, s);
+    if (r != MOE_OK) return r;
+    GemmGroup dn = group(sd, nullptr, 0, H, Is, hs, Is, nullptr, y_shared, H, nullptr, 1, 0, nullptr);
+    return run_gemm_pass(cfg, plan, 1, no_group(), dn, nullptr, 0, T, s);
+}
+
+int moe_combine(const moe_config* cfg, const void* y_perm, const int32_t* row_of, const float* topk_w,
+                const void* y_shared, const void* residual, int64_t T, void* y, void* stream) {
+    int st = check_cfg(cfg);
+    if (st != MOE_OK) return st;
+    if ((st = check_T(cfg, T)) != MOE_OK) return st;
+    if (T == 0) return MOE_OK;
+    if (!ok_ptr(y_perm) || !ok_ptr(row_of) || !ok_ptr(topk_w) || !ok_opt(y_shared) || !ok_opt(residual) ||
+        !ok_ptr(y))
+        return MOE_ERR_INVALID;
+    return hip_status(launch_combine(cfg->dtype, y_perm, row_of, topk_w, cfg->num_experts_per_tok, 0, y_shared,
+                                     cfg->hidden_size, residual, y, T, cfg->hidden_size, as_stream(stream)));
+}
+
+int moe_layer_forward(const moe_config* cfg, const moe_weights* w, const void* x, const void* residual, int64_t T,
+                      void* y, int32_t* topk_idx_out, float* topk_w_out, int32_t* counts_out, void* ws,
+                      size_t ws_bytes, void* stream) {
+    int st = check_cfg(cfg);
+    if (st != MOE_OK) return st;
+    if ((st = check_T(cfg, T)) != MOE_OK) return st;
+    if (T == 0) return MOE_OK;
+    if (!w) return MOE_ERR_INVALID;
+    const int Is = cfg->shared_expert_intermediate_size;
+    if (!ok_ptr(x) || !ok_ptr(y) || !ok_opt(residual) || !ok_ptr(w->router) || !ok_opt(w->router_bias) ||
+        !ok_ptr(w->gate) || !ok_ptr(w->up) || !ok_ptr(w->down) || !ok_opt(topk_idx_out) || !ok_opt(topk_w_out) ||
+        !ok_opt(counts_out) || !ok_ptr(ws))
+        return MOE_ERR_INVALID;
+    if (Is > 0 && (!ok_ptr(w->shared_gate) || !ok_ptr(w->shared_up) || !ok_ptr(w->shared_down)))
+        return MOE_ERR_INVALID;
+    if (x == y) return MOE_ERR_INVALID;
+    if (ws_bytes < layer_ws(cfg, T)) return MOE_ERR_WORKSPACE;
+
+    const int H = cfg->hidden_size, E = cfg->num_experts, k = cfg->num_experts_per_tok;
+    const int I = cfg->moe_intermediate_size;
+    const int64_t N = T * k;
+    hipStream_t s = as_stream(stream);
+    Carver cv(ws);
+    LayerPlan p;
+    plan_layer(cfg, T, cv, p);
+    int32_t* idx = topk_idx_out ? topk_idx_out : p.idx;
+    float* wt = topk_w_out ? topk_w_out : p.w;
+    int32_t* counts = counts_out ? counts_out : p.counts;
+
+    TMOE_TRY(launch_route(cfg->dtype, x, w->router, w->router_bias, T, H, E, k, cfg->norm_topk_prob, idx, wt, nullptr,
+                          p.route.sc, p.route.bd, s));
+    const int slots = k + 1;  // per token: k weighted expert rows, then the shared row
+    TMOE_TRY(launch_permute(idx, T, k, E, p.hist, counts, p.offsets, p.row_token, p.row_of, wt, p.row_dst,
+                            p.row_scale, slots, p.gemm.mfma ? &p.gemm.t[0] : nullptr,
+                            p.gemm.mfma ? &p.gemm.t[1] : nullptr, s));
+
+    GemmGroup gu_r = group(w->gate, w->up, (int64_t)I * H, I, H, x, H, p.row_token, p.hr, I, nullptr, 1, 0, nullptr);
+    GemmGroup gu_s = Is > 0 ? group(w->shared_gate, w->shared_up, 0, Is, H, x, H, nullptr, p.hs, Is, nullptr, 1, 0,
+                                    nullptr)
+                            : no_group();
+    int r = run_gemm_pass(cfg, p.gemm, 0, gu_r, gu_s, p.offsets, N, T, s);
+    if (r != MOE_OK) return r;
+    GemmGroup dn_r = group(w->down, nullptr, (int64_t)H * I, H, I, p.hr, I, nullptr, p.ybuf, H, p.row_dst, 1, 0,
+                           p.row_scale);
+    GemmGroup dn_s = Is > 0 ? group(w->shared_down, nullptr, 0, H, Is, p.hs, Is, nullptr, p.ybuf, H, nullptr, slots,
+                                    k, nullptr)
+                            : no_group();
+    r = run_gemm_pass(cfg, p.gemm, 1, dn_r, dn_s, p.offsets, N, T, s);
+    if (r != MOE_OK) return r;
+    const char* shared_base = Is > 0 ? static_cast<const char*>(p.ybuf) + (int64_t)k * H * esize(cfg->dtype) : nullptr;
+    return hip_status(launch_combine(cfg->dtype, p.ybuf, nullptr, nullptr, k, slots, shared_base,
+                                     (int64_t)slots * H, residual, y, T, H, s));
+}
+
+int moe_rmsnorm(const moe_config* cfg, const void* x, const float* gain, float eps, int64_t T, void* out,
+                void* stream) {
+    int st = check_cfg(cfg);
+    if (st != MOE_OK) return st;
+    if (T < 0 || !(eps >= 0.0f)) return MOE_ERR_INVALID;
+    if (T == 0) return MOE_OK;
+    if (!ok_ptr(x) || !ok_ptr(gain) || !ok_ptr(out)) return MOE_ERR_INVALID;
+    return hip_status(launch_rmsnorm(cfg->dtype, x, gain, eps, T, cfg->hidden_size, out, as_stream(stream)));
+}
+
+size_t moe_codec_head_workspace_size(const moe_config* cfg, int32_t V, int64_t T) {
+    if (check_cfg(cfg) != MOE_OK || V < 1 || T < 0) return 0;
+    Carver cv(nullptr);
+    cv.take<float>(T * V);
+    cv.take<float>(T * V);
+    return cv.size();
+}
+
+int moe_codec_head_argmax(const moe_config* cfg, const void* x, const void* w_head, int32_t V, int64_t T,
+                          float* logits, int32_t* c0, void* ws, size_t ws_bytes, void* stream) {
+    int st = check_cfg(cfg);
+    if (st != MOE_OK) return st;
+    if (T < 0 || V < 1) return MOE_ERR_INVALID;
+    if (V > (1 << 20) || T > (int64_t(1) << 22)) return MOE_ERR_UNSUPPORTED;
+    if (T == 0) return MOE_OK;
+    if (!ok_ptr(x) || !ok_ptr(w_head) || !ok_opt(logits) || !ok_ptr(c0) || !ok_ptr(ws)) return MOE_ERR_INVALID;
+    if (ws_bytes < moe_codec_head_workspace_size(cfg, V, T)) return MOE_ERR_WORKSPACE;
+    Carver cv(ws);
+    float* sc = cv.take<float>(T * V);
+    float* bd = cv.take<float>(T * V);
+    if (logits) sc = logits;
+    hipStream_t s = as_stream(stream);
+    TMOE_TRY(launch_scores(cfg->dtype, x, w_head, nullptr, T, cfg->hidden_size, V, sc, bd, s));
+    return hip_status(launch_argmax(cfg->dtype, sc, bd, x, w_head, T, cfg->hidden_size, V, c0, s));
+}
+
+}  // extern "C"

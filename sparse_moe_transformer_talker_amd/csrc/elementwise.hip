@@ -1,0 +1,179 @@
+// Combine of expert outputs, RMSNorm and row gather: HBM-bound, one block per
+// token row, 16-byte accesses where the row length allows.
+//
+// combine ("3C · Talker MoE (20 lớp, 128 Experts Top-6)", openarchlab, §3):
+//   y_t = SharedMLP(x_t) + sum_{i in S_t} w_{t,i} Expert_i(x_t)  (+ residual_t)
+// summed in fp32 in a fixed order (shared, slots 0..k-1, residual), so results
+// are bitwise reproducible.
+// RMSNorm (lab helper on "Bài Lab tổng hợp — Qwen3-Omni & Qwen3-TTS-12Hz
+// Architecture"; eps 1e-6 in the Qwen3-TTS module print on the horus-space page):
+//   out = x / sqrt(mean(x^2) + eps) * gain
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace tmoe {
+
+// Source row of term j of token t.  Slot mode (rows == nullptr): expert
+// outputs are stored per token in `slots` consecutive rows with the weights
+// already applied.  The shared-expert term of token t is shared + t * sstride
+// (nullptr: no shared term).
+template <typename T>
+__global__ __launch_bounds__(128) void combine_kernel(const T* __restrict__ ysrc, const int32_t* __restrict__ rows,
+                                                      const float* __restrict__ w, int k, int slots,
+                                                      const T* __restrict__ shared, int64_t sstride,
+                                                      const T* residual, T* y, int64_t Ttok, int H) {
+    const int64_t t = blockIdx.x;
+    if (t >= Ttok) return;
+    const T* shared_row = shared ? shared + t * sstride : nullptr;
+    for (int h = threadIdx.x; h < H; h += blockDim.x) {
+        float acc = shared_row ? Elem<T>::load(shared_row, h) : 0.f;
+        for (int j = 0; j < k; ++j) {
+            if (rows) {
+                const int64_t r = rows[t * k + j];
+                acc += w[t * k + j] * Elem<T>::load(ysrc, r * H + h);
+            } else {
+                acc += Elem<T>::load(ysrc, (t * slots + j) * (int64_t)H + h);
+            }
+        }
+        if (residual) acc += Elem<T>::load(residual, t * H + h);
+        Elem<T>::store(y, t * H + h, acc);
+    }
+}
+
+// bf16, H % 8 == 0: eight elements per thread with 16-byte loads.
+__global__ __launch_bounds__(128) void combine_bf16x8_kernel(const bf16_t* __restrict__ ysrc,
+                                                             const int32_t* __restrict__ rows,
+                                                             const float* __restrict__ w, int k, int slots,
+                                                             const bf16_t* __restrict__ shared, int64_t sstride,
+                                                             const bf16_t* residual, bf16_t* y, int64_t Ttok, int H) {
+    const int64_t t = blockIdx.x;
+    if (t >= Ttok) return;
+    const bf16_t* shared_row = shared ? shared + t * sstride : nullptr;
+    for (int h = threadIdx.x * 8; h < H; h += blockDim.x * 8) {
+        float acc[8];
+        if (shared_row) {
+            u32x4 v = *reinterpret_cast<const u32x4*>(shared_row + h);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                acc[2 * q] = __uint_as_float(v[q] << 16);
+                acc[2 * q + 1] = __uint_as_float(v[q] & 0xFFFF0000u);
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < 8; ++q) acc[q] = 0.f;
+        }
+        for (int j = 0; j < k; ++j) {
+            const bf16_t* src;
+            float wj = 1.0f;
+            if (rows) {
+                src = ysrc + (int64_t)rows[t * k + j] * H;
+                wj = w[t * k + j];
+            } else {
+                src = ysrc + (t * slots + j) * (int64_t)H;
+            }
+            u32x4 v = *reinterpret_cast<const u32x4*>(src + h);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                acc[2 * q] += wj * __uint_as_float(v[q] << 16);
+                acc[2 * q + 1] += wj * __uint_as_float(v[q] & 0xFFFF0000u);
+            }
+        }
+        if (residual) {
+            u32x4 v = *reinterpret_cast<const u32x4*>(residual + t * H + h);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                acc[2 * q] += __uint_as_float(v[q] << 16);
+                acc[2 * q + 1] += __uint_as_float(v[q] & 0xFFFF0000u);
+            }
+        }
+        u32x4 o;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            o[q] = (uint32_t)f32_to_bf16(acc[2 * q]) | ((uint32_t)f32_to_bf16(acc[2 * q + 1]) << 16);
+        *reinterpret_cast<u32x4*>(y + t * H + h) = o;
+    }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const T* x, const float* __restrict__ gain, float eps,
+                                                      int64_t Ttok, int H, T* out) {
+    __shared__ float part[4];
+    const int64_t t = blockIdx.x;
+    if (t >= Ttok) return;
+    const T* xr = x + t * H;
+    float ss = 0.f;
+    for (int h = threadIdx.x; h < H; h += blockDim.x) {
+        float v = Elem<T>::load(xr, h);
+        ss = fmaf(v, v, ss);
+    }
+    ss = wave_sum(ss);
+    if (lane_id() == 0) part[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    const float ms = (part[0] + part[1] + part[2] + part[3]) / (float)H;
+    const float inv = 1.0f / sqrtf(ms + eps);
+    for (int h = threadIdx.x; h < H; h += blockDim.x) {
+        float v = Elem<T>::load(xr, h);
+        Elem<T>::store(out, t * H + h, v * inv * gain[h]);
+    }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void gather_rows_kernel(const T* __restrict__ x, const int32_t* __restrict__ rows,
+                                                          int64_t n, int H, T* __restrict__ out) {
+    const int64_t r = blockIdx.x;
+    if (r >= n) return;
+    const T* src = x + (int64_t)rows[r] * H;
+    for (int h = threadIdx.x; h < H; h += blockDim.x) out[r * H + h] = src[h];
+}
+
+hipError_t launch_combine(int dtype, const void* ysrc, const int32_t* rows, const float* w, int k, int slots,
+                          const void* shared, int64_t sstride, const void* residual, void* y, int64_t Ttok, int H,
+                          hipStream_t st) {
+    if (Ttok <= 0) return hipSuccess;
+    if (dtype == kBF16 && H % 8 == 0)
+        combine_bf16x8_kernel<<<(unsigned)Ttok, 128, 0, st>>>((const bf16_t*)ysrc, rows, w, k, slots,
+                                                               (const bf16_t*)shared, sstride,
+                                                               (const bf16_t*)residual, (bf16_t*)y, Ttok, H);
+    else if (dtype == kBF16)
+        combine_kernel<bf16_t><<<(unsigned)Ttok, 128, 0, st>>>((const bf16_t*)ysrc, rows, w, k, slots,
+                                                                (const bf16_t*)shared, sstride,
+                                                                (const bf16_t*)residual, (bf16_t*)y, Ttok, H);
+    else
+        combine_kernel<float><<<(unsigned)Ttok, 128, 0, st>>>((const float*)ysrc, rows, w, k, slots,
+                                                               (const float*)shared, sstride,
+                                                               (const float*)residual, (float*)y, Ttok, H);
+    return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void fill_i32_kernel(int32_t* __restrict__ p, int32_t v, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = v;
+}
+
+hipError_t launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    fill_i32_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(p, v, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm(int dtype, const void* x, const float* gain, float eps, int64_t Ttok, int H, void* out,
+                          hipStream_t st) {
+    if (Ttok <= 0) return hipSuccess;
+    if (dtype == kBF16)
+        rmsnorm_kernel<bf16_t><<<(unsigned)Ttok, 256, 0, st>>>((const bf16_t*)x, gain, eps, Ttok, H, (bf16_t*)out);
+    else
+        rmsnorm_kernel<float><<<(unsigned)Ttok, 256, 0, st>>>((const float*)x, gain, eps, Ttok, H, (float*)out);
+    return hipGetLastError();
+}
+
+hipError_t launch_gather_rows(int dtype, const void* x, const int32_t* rows, int64_t n, int H, void* out,
+                              hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    if (dtype == kBF16)
+        gather_rows_kernel<bf16_t><<<(unsigned)n, 256, 0, st>>>((const bf16_t*)x, rows, n, H, (bf16_t*)out);
+    else
+        gather_rows_kernel<float><<<(unsigned)n, 256, 0, st>>>((const float*)x, rows, n, H, (float*)out);
+    return hipGetLastError();
+}
+
+}  // namespace tmoe

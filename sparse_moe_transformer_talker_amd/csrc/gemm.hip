@@ -1,0 +1,247 @@
+// Grouped SwiGLU matrix products of the routed experts and the shared expert
+// ("3C · Talker MoE (20 lớp, 128 Experts Top-6)", openarchlab, §1: each expert
+// is a SwiGLU 1024 -> 384 -> 1024, the shared one 1024 -> 768 -> 1024; the
+// SwiGLU form down(SiLU(gate x) * up x) is from "用 print(model) 认识 Qwen3-TTS",
+// horus-space, MLP section).
+//
+// pass 0 (gate/up):  h[r, n] = SiLU(x_r . gate[e, n]) * (x_r . up[e, n])
+// pass 1 (down):     y[dst(r), n] = scale(r) * (h_r . down[e, n])
+//
+// Work arrives as a device-built list of tiles (expert, n0, m0, rows); the
+// launch is sized for the worst case and surplus workgroups exit at once.
+// Consecutive tiles share a weight block; workgroup p runs on XCD p % 8, so the
+// logical order is dealt out in 8 contiguous runs, one per XCD, which keeps
+// tiles that reuse a weight block in the same L2.
+//
+// bf16 x bf16 -> fp32 on the matrix cores (v_mfma_f32_16x16x32_bf16); A and B
+// tiles are staged through LDS (rows padded by 16 bytes against bank
+// conflicts) with a register prefetch of the next K block.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace tmoe {
+
+template <int PASS, int BM, int BN, int BK, int WM, int WN>
+__global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs args) {
+    constexpr int BROWS = (PASS == 0) ? 2 * BN : BN;
+    constexpr int LDK = BK + 8;
+    constexpr int KC = BK / 8;                 // 16-byte chunks per tile row
+    constexpr int NA = BM * KC, NB = BROWS * KC;
+    constexpr int CA = (NA + 255) / 256, CB = (NB + 255) / 256;
+    constexpr int TM = BM / WM, TN = BN / WN;
+    constexpr int MS = TM / 16, NS = TN / 16;
+    static_assert(WM * WN == 4, "four waves");
+    static_assert(TM % 16 == 0 && TN % 16 == 0 && BK % 32 == 0, "tile shape");
+    static_assert(NB % 256 == 0, "B tile loads cover the block");
+
+    __shared__ __attribute__((aligned(16))) bf16_t As[BM * LDK];
+    __shared__ __attribute__((aligned(16))) bf16_t Bs[BROWS * LDK];
+
+    const int n_items = *args.count;
+    const int p = blockIdx.x;
+    const int chunk = (n_items + 7) >> 3;
+    const int slot = p >> 3;
+    if (slot >= chunk) return;
+    const int q = (p & 7) * chunk + slot;
+    if (q >= n_items) return;
+    const int4 it = args.items[q];
+    const int gi = it.x < args.E ? 0 : 1;
+    const GemmGroup& g = args.g[gi];
+    const int e = gi == 0 ? it.x : 0;
+    const int n0 = it.y, m0 = it.z, mrows = it.w;
+    const int K = g.K;
+    const int tid = threadIdx.x;
+
+    // Per-thread global source pointers (fixed over K).
+    const bf16_t* pa[CA];
+    const bf16_t* pb[CB];
+#pragma unroll
+    for (int i = 0; i < CA; ++i) {
+        int c = tid + 256 * i;
+        if (c >= NA) c = 0;
+        int row = c / KC, kc = c % KC;
+        int m = row < mrows ? row : 0;
+        int64_t grow = g.a_rows ? (int64_t)g.a_rows[m0 + m] : (int64_t)(m0 + m);
+        pa[i] = (const bf16_t*)g.a + grow * g.a_ld + kc * 8;
+    }
+#pragma unroll
+    for (int i = 0; i < CB; ++i) {
+        int c = tid + 256 * i;
+        int row = c / KC, kc = c % KC;
+        const bf16_t* w = (const bf16_t*)((PASS == 0 && row >= BN) ? g.wb : g.wa);
+        int wrow = n0 + (row % BN);
+        pb[i] = w + (int64_t)e * g.w_estride + (int64_t)wrow * K + kc * 8;
+    }
+
+    u32x4 ra[CA], rb[CB];
+    auto load = [&](int k0) {
+#pragma unroll
+        for (int i = 0; i < CA; ++i)
+            if (tid + 256 * i < NA) ra[i] = *reinterpret_cast<const u32x4*>(pa[i] + k0);
+#pragma unroll
+        for (int i = 0; i < CB; ++i) rb[i] = *reinterpret_cast<const u32x4*>(pb[i] + k0);
+    };
+    auto stash = [&]() {
+#pragma unroll
+        for (int i = 0; i < CA; ++i) {
+            int c = tid + 256 * i;
+            if (c < NA) *reinterpret_cast<u32x4*>(&As[(c / KC) * LDK + (c % KC) * 8]) = ra[i];
+        }
+#pragma unroll
+        for (int i = 0; i < CB; ++i) {
+            int c = tid + 256 * i;
+            *reinterpret_cast<u32x4*>(&Bs[(c / KC) * LDK + (c % KC) * 8]) = rb[i];
+        }
+    };
+
+    const int wave = tid >> 6, lane = tid & 63;
+    const int wm = wave / WN, wn = wave % WN;
+    const int li = lane & 15, lk = (lane >> 4) * 8;
+
+    f32x4 acc[MS][NS], accu[MS][NS];
+#pragma unroll
+    for (int a = 0; a < MS; ++a)
+#pragma unroll
+        for (int b = 0; b < NS; ++b) { acc[a][b] = f32x4{0, 0, 0, 0}; accu[a][b] = f32x4{0, 0, 0, 0}; }
+
+    load(0);
+    for (int k0 = 0; k0 < K; k0 += BK) {
+        __syncthreads();
+        stash();
+        __syncthreads();
+        if (k0 + BK < K) load(k0 + BK);
+#pragma unroll
+        for (int ks = 0; ks < BK; ks += 32) {
+            bf16x8 af[MS], bg[NS], bu[NS];
+#pragma unroll
+            for (int a = 0; a < MS; ++a)
+                af[a] = *reinterpret_cast<const bf16x8*>(&As[(wm * TM + a * 16 + li) * LDK + ks + lk]);
+#pragma unroll
+            for (int b = 0; b < NS; ++b) {
+                bg[b] = *reinterpret_cast<const bf16x8*>(&Bs[(wn * TN + b * 16 + li) * LDK + ks + lk]);
+                if (PASS == 0)
+                    bu[b] = *reinterpret_cast<const bf16x8*>(&Bs[(BN + wn * TN + b * 16 + li) * LDK + ks + lk]);
+            }
+#pragma unroll
+            for (int a = 0; a < MS; ++a)
+#pragma unroll
+                for (int b = 0; b < NS; ++b) {
+                    acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[a], bg[b], acc[a][b], 0, 0, 0);
+                    if (PASS == 0)
+                        accu[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[a], bu[b], accu[a][b], 0, 0, 0);
+                }
+        }
+    }
+
+    // Epilogue: lane holds D[4*(lane/16) + r][lane % 16] of every 16x16 block.
+    bf16_t* out = (bf16_t*)g.out;
+#pragma unroll
+    for (int a = 0; a < MS; ++a)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = wm * TM + a * 16 + (lane >> 4) * 4 + r;
+            if (row >= mrows) continue;
+            const int64_t src = (int64_t)m0 + row;
+            const int64_t dst = (g.out_rows ? (int64_t)g.out_rows[src] : src) * g.out_mul + g.out_add;
+            const float sc = (PASS == 1 && g.out_scale) ? g.out_scale[src] : 1.0f;
+#pragma unroll
+            for (int b = 0; b < NS; ++b) {
+                const int col = n0 + wn * TN + b * 16 + li;
+                float v;
+                if (PASS == 0) {
+                    float gv = acc[a][b][r];
+                    v = gv / (1.0f + __expf(-gv)) * accu[a][b][r];
+                } else {
+                    v = acc[a][b][r] * sc;
+                }
+                out[dst * g.out_ld + col] = f32_to_bf16(v);
+            }
+        }
+}
+
+// ---------------------------------------------------------------------------
+// Portable path (fp32 and shapes the matrix-core tiles do not cover): one
+// thread per output element, fp32 accumulation.
+template <typename T, int PASS>
+__global__ __launch_bounds__(256) void gemm_generic_kernel(GemmGroup g, const int32_t* __restrict__ offsets, int E,
+                                                           int64_t rows) {
+    const int64_t r = blockIdx.x;
+    const int n = blockIdx.y * blockDim.x + threadIdx.x;
+    if (r >= rows || n >= g.N) return;
+    int e = 0;
+    if (offsets) {  // expert of grouped row r: last e with offsets[e] <= r
+        int lo = 0, hi = E - 1;
+        while (lo < hi) {
+            int mid = (lo + hi + 1) >> 1;
+            if (offsets[mid] <= r) lo = mid; else hi = mid - 1;
+        }
+        e = lo;
+    }
+    const int64_t arow = g.a_rows ? (int64_t)g.a_rows[r] : r;
+    const T* a = (const T*)g.a + arow * g.a_ld;
+    const T* wa = (const T*)g.wa + (int64_t)e * g.w_estride + (int64_t)n * g.K;
+    float s0 = 0.f, s1 = 0.f;
+    if (PASS == 0) {
+        const T* wb = (const T*)g.wb + (int64_t)e * g.w_estride + (int64_t)n * g.K;
+        for (int kk = 0; kk < g.K; ++kk) {
+            float av = Elem<T>::load(a, kk);
+            s0 = fmaf(av, Elem<T>::load(wa, kk), s0);
+            s1 = fmaf(av, Elem<T>::load(wb, kk), s1);
+        }
+        s0 = s0 / (1.0f + __expf(-s0)) * s1;
+    } else {
+        for (int kk = 0; kk < g.K; ++kk) s0 = fmaf(Elem<T>::load(a, kk), Elem<T>::load(wa, kk), s0);
+        if (g.out_scale) s0 *= g.out_scale[r];
+    }
+    const int64_t dst = (g.out_rows ? (int64_t)g.out_rows[r] : r) * g.out_mul + g.out_add;
+    Elem<T>::store((T*)g.out, dst * g.out_ld + n, s0);
+}
+
+// ---------------------------------------------------------------------------
+// Tilings: small-M (few rows per expert: weight streaming) and large-M.
+//                         BM   BN   BK  WM WN
+#define TMOE_SMALL_GU 0,   16,  64, 128, 1, 4
+#define TMOE_SMALL_DN 1,   16, 128,  64, 1, 4
+#define TMOE_LARGE_GU 0,  128,  64,  64, 2, 2
+#define TMOE_LARGE_DN 1,  128, 128,  64, 2, 2
+
+void gemm_tiles(int variant, int pass, int* mt, int* nt) {
+    if (variant == kGemmSmallM) { *mt = 16; *nt = pass == 0 ? 64 : 128; }
+    else { *mt = 128; *nt = pass == 0 ? 64 : 128; }
+}
+
+bool gemm_mfma_ok(int dtype, int H, int I, int Is) {
+    return dtype == kBF16 && H % 128 == 0 && I % 64 == 0 && Is % 64 == 0;
+}
+
+hipError_t launch_grouped_gemm(int dtype, int variant, int pass, const GemmArgs& args, int64_t max_items,
+                               hipStream_t st) {
+    (void)dtype;
+    const unsigned grid = (unsigned)(((max_items + 7) / 8) * 8);
+    if (grid == 0) return hipSuccess;
+    if (variant == kGemmSmallM) {
+        if (pass == 0) grouped_gemm_kernel<TMOE_SMALL_GU><<<grid, 256, 0, st>>>(args);
+        else grouped_gemm_kernel<TMOE_SMALL_DN><<<grid, 256, 0, st>>>(args);
+    } else {
+        if (pass == 0) grouped_gemm_kernel<TMOE_LARGE_GU><<<grid, 256, 0, st>>>(args);
+        else grouped_gemm_kernel<TMOE_LARGE_DN><<<grid, 256, 0, st>>>(args);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_generic(int dtype, int pass, const GemmGroup& g, const int32_t* offsets, int n_groups_rows,
+                               int E, int64_t rows, hipStream_t st) {
+    (void)n_groups_rows;
+    if (rows <= 0) return hipSuccess;
+    dim3 grid((unsigned)rows, (unsigned)((g.N + 255) / 256));
+    if (dtype == kBF16) {
+        if (pass == 0) gemm_generic_kernel<bf16_t, 0><<<grid, 256, 0, st>>>(g, offsets, E, rows);
+        else gemm_generic_kernel<bf16_t, 1><<<grid, 256, 0, st>>>(g, offsets, E, rows);
+    } else {
+        if (pass == 0) gemm_generic_kernel<float, 0><<<grid, 256, 0, st>>>(g, offsets, E, rows);
+        else gemm_generic_kernel<float, 1><<<grid, 256, 0, st>>>(g, offsets, E, rows);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace tmoe

@@ -1,0 +1,84 @@
+// Host-side launchers of the Talker MoE kernels (one HIP translation unit each).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tmoe {
+
+constexpr int kF32 = 0;
+constexpr int kBF16 = 1;
+constexpr int kMaxTopK = 32;
+constexpr int kMaxExperts = 1024;
+constexpr int kPermChunk = 512;  // (token, slot) pairs per permutation block
+
+// --- routing (route.hip) ---
+bool route_fused_ok(int dtype, int H, int E);
+hipError_t launch_route(int dtype, const void* x, const void* W, const float* bias, int64_t T, int H, int E, int k,
+                        int norm, int32_t* idx, float* w, float* probs, float* scratch_sc, float* scratch_bd,
+                        hipStream_t st);
+hipError_t launch_scores(int dtype, const void* x, const void* W, const float* bias, int64_t T, int H, int n,
+                         float* sc, float* bd, hipStream_t st);
+hipError_t launch_argmax(int dtype, const float* sc, const float* bd, const void* x, const void* W, int64_t T, int H,
+                         int n, int32_t* out, hipStream_t st);
+
+// --- grouping (permute.hip) ---
+// Tiling of one grouped GEMM: items are (expert, n0, m0, rows) tiles of at most
+// mt rows and nt columns of an output of width n_routed (routed experts) or
+// n_shared (the shared expert, taken as expert index E, rows = tokens).
+struct TileSpec {
+    int mt, nt;
+    int n_routed, n_shared;
+    int4* items;
+    int* count;
+    int max_items;
+};
+int64_t tile_max_items(int64_t pairs, int E, int64_t T, int mt, int nt, int n_routed, int n_shared);
+hipError_t launch_permute(const int32_t* idx, int64_t T, int k, int E, int32_t* hist, int32_t* counts,
+                          int32_t* offsets, int32_t* row_token, int32_t* row_of, const float* w,
+                          int32_t* row_dst, float* row_scale, int slots, const TileSpec* t1, const TileSpec* t2,
+                          hipStream_t st);
+hipError_t launch_build_items(const int32_t* offsets, int E, int64_t T, const TileSpec* t1, const TileSpec* t2,
+                              hipStream_t st);
+
+// --- grouped SwiGLU matrix products (gemm.hip) ---
+struct GemmGroup {
+    const void* wa;        // gate (gate/up pass) or down (down pass): [n_experts, N, K]
+    const void* wb;        // up (gate/up pass); unused in the down pass
+    int64_t w_estride;     // elements between experts
+    int N, K;              // output width, reduction length
+    const void* a;         // A rows
+    int64_t a_ld;          // elements between A rows
+    const int32_t* a_rows; // item row -> A row, or nullptr (identity)
+    void* out;
+    int64_t out_ld;
+    const int32_t* out_rows;  // item row -> destination row, or nullptr (identity)
+    int out_mul, out_add;     // destination row = map(row) * out_mul + out_add
+    const float* out_scale;   // per item-row scale, or nullptr
+};
+struct GemmArgs {
+    GemmGroup g[2];  // [0] routed experts, [1] shared expert (expert index == E)
+    const int4* items;
+    const int* count;
+    int E;
+};
+enum GemmVariant { kGemmSmallM = 0, kGemmLargeM = 1 };
+void gemm_tiles(int variant, int pass, int* mt, int* nt);
+bool gemm_mfma_ok(int dtype, int H, int I, int Is);
+hipError_t launch_grouped_gemm(int dtype, int variant, int pass, const GemmArgs& args, int64_t max_items,
+                               hipStream_t st);
+// Portable path: one thread per output; rows of group 0 find their expert in offsets.
+hipError_t launch_gemm_generic(int dtype, int pass, const GemmGroup& g, const int32_t* offsets, int n_groups_rows,
+                               int E, int64_t rows, hipStream_t st);
+
+// --- element-wise (elementwise.hip) ---
+hipError_t launch_combine(int dtype, const void* ysrc, const int32_t* rows, const float* w, int k, int slots,
+                          const void* shared, int64_t sstride, const void* residual, void* y, int64_t T, int H,
+                          hipStream_t st);
+hipError_t launch_rmsnorm(int dtype, const void* x, const float* gain, float eps, int64_t T, int H, void* out,
+                          hipStream_t st);
+hipError_t launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t st);
+hipError_t launch_gather_rows(int dtype, const void* x, const int32_t* rows, int64_t n, int H, void* out,
+                              hipStream_t st);
+
+}  // namespace tmoe

@@ -1,0 +1,136 @@
+"""The C ABI on the host (no GPU): the library loads, exports every function the
+header declares, and validates arguments before anything reaches HIP."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_moe_transformer_talker_amd import api
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "talker_moe.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(api.LIB_PATH), reason="library not built")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(moe_\w+)\s*\(", text, flags=re.M)))
+
+
+def _cfg(**kw):
+    base = dict(hidden_size=1024, num_experts=128, num_experts_per_tok=6, moe_intermediate_size=384,
+                shared_expert_intermediate_size=768, norm_topk_prob=1, dtype=api.MOE_BF16)
+    base.update(kw)
+    return api.moe_config(**base)
+
+
+def test_header_declares_the_six_layer_entry_points():
+    names = _declared_functions()
+    for n in ("moe_route", "moe_permute", "moe_grouped_swiglu", "moe_shared_swiglu", "moe_combine",
+              "moe_layer_forward"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(api.LIB_PATH)
+    names = _declared_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(api.EXPORTS)
+    api.load_library()
+
+
+def test_status_strings():
+    assert api.status_string(0) == "ok"
+    assert api.status_string(-1) == "invalid argument"
+    assert api.status_string(-3) == "workspace too small"
+    assert api.status_string(99) == "unknown status"
+
+
+@pytest.mark.parametrize("kw,expect", [
+    ({}, 0),
+    ({"num_experts_per_tok": 129}, -1),          # k > E
+    ({"num_experts_per_tok": 0}, -1),
+    ({"hidden_size": 0}, -1),
+    ({"shared_expert_intermediate_size": -1}, -1),
+    ({"norm_topk_prob": 2}, -1),
+    ({"dtype": 7}, -1),
+    ({"num_experts": 2048, "num_experts_per_tok": 6}, -2),   # beyond the supported sizes
+    ({"num_experts_per_tok": 33}, -2),
+    ({"shared_expert_intermediate_size": 0}, 0),
+    ({"dtype": api.MOE_F32, "hidden_size": 6, "num_experts": 6, "num_experts_per_tok": 2,
+      "moe_intermediate_size": 12, "shared_expert_intermediate_size": 12}, 0),
+])
+def test_check_config(kw, expect):
+    lib = api.load_library()
+    assert lib.moe_check_config(ctypes.byref(_cfg(**kw))) == expect
+
+
+def test_workspace_size_grows_with_T_and_is_zero_on_bad_config():
+    lib = api.load_library()
+    c = _cfg()
+    s64 = lib.moe_workspace_size(ctypes.byref(c), 64)
+    s4096 = lib.moe_workspace_size(ctypes.byref(c), 4096)
+    assert 0 < s64 < s4096
+    assert s64 % 256 == 0
+    # the layer needs at least its expert-output slots: T * (k + 1) * H bf16
+    assert s4096 >= 4096 * 7 * 1024 * 2
+    assert lib.moe_workspace_size(ctypes.byref(_cfg(num_experts_per_tok=200)), 64) == 0
+    assert lib.moe_workspace_size(ctypes.byref(c), -1) == 0
+
+
+FAKE = 0x7F0000000000  # never dereferenced: every call below fails its checks first
+
+
+def _p(off=0):
+    return ctypes.c_void_p(FAKE + off)
+
+
+def test_route_argument_errors():
+    lib = api.load_library()
+    c = _cfg()
+    ws = lib.moe_workspace_size(ctypes.byref(c), 16)
+    ok = lambda **kw: lib.moe_route(ctypes.byref(kw.get("cfg", c)), kw.get("x", _p()), kw.get("r", _p()), None,
+                                     kw.get("T", 16), kw.get("idx", _p()), kw.get("w", _p()), None, _p(), ws, None)
+    assert ok(x=None) == -1
+    assert ok(idx=None) == -1
+    assert ok(w=None) == -1
+    assert ok(x=_p(2)) == -1            # not 16-byte aligned
+    assert ok(T=-3) == -1
+    assert ok(T=0) == 0                 # empty batch: nothing to do
+    assert ok(T=1 << 22) == -2          # T * k beyond 2^22
+    assert ok(cfg=_cfg(num_experts_per_tok=130)) == -1
+    # the portable router needs score scratch: a too-small workspace is reported
+    f32 = _cfg(dtype=api.MOE_F32, hidden_size=6, num_experts=6, num_experts_per_tok=2, moe_intermediate_size=12,
+               shared_expert_intermediate_size=12)
+    assert lib.moe_route(ctypes.byref(f32), _p(), _p(), None, 4, _p(), _p(), None, _p(), 0, None) == -3
+
+
+def test_layer_and_helper_argument_errors():
+    lib = api.load_library()
+    c = _cfg()
+    w = api.moe_weights(FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    need = lib.moe_workspace_size(ctypes.byref(c), 64)
+    call = lambda **kw: lib.moe_layer_forward(
+        ctypes.byref(c), kw.get("w", ctypes.byref(w)), kw.get("x", _p()), None, 64, kw.get("y", _p(4096)), None,
+        None, None, _p(), kw.get("ws", need), None)
+    assert call(x=None) == -1
+    assert call(y=_p()) == -1          # y may not alias x
+    assert call(w=None) == -1
+    assert call(ws=need - 256) == -3
+    w_noshared = api.moe_weights(FAKE, None, FAKE, FAKE, FAKE, None, None, None)
+    assert call(w=ctypes.byref(w_noshared)) == -1   # Is > 0 needs the shared expert
+    assert lib.moe_shared_swiglu(ctypes.byref(_cfg(shared_expert_intermediate_size=0)), _p(), 8, _p(), _p(), _p(),
+                                 _p(), _p(), 1 << 20, None) == -1
+    assert lib.moe_combine(ctypes.byref(c), _p(), None, _p(), None, None, 8, _p(), None) == -1
+    assert lib.moe_rmsnorm(ctypes.byref(c), _p(), _p(), ctypes.c_float(-1.0), 8, _p(), None) == -1
+    assert lib.moe_codec_head_argmax(ctypes.byref(c), _p(), _p(), 0, 8, None, _p(), _p(), 1 << 30, None) == -1
+    assert lib.moe_codec_head_workspace_size(ctypes.byref(c), 3072, 1024) >= 2 * 3072 * 1024 * 4
+    assert lib.moe_permute(ctypes.byref(c), _p(), 8, _p(), _p(), _p(), _p(), _p(), None, _p(), 1 << 20,
+                           None) == -1          # x without x_perm
+    assert lib.moe_grouped_swiglu(ctypes.byref(c), _p(), None, None, 8, _p(), _p(), _p(), _p(), _p(), 1 << 30,
+                                  None) == -1   # offsets required
