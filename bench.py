@@ -1,0 +1,245 @@
+#!/usr/bin/env python3
+"""Benchmark of the Talker MoE feed-forward layer on one MI355X.
+
+One step = one whole layer (route, group, routed + shared SwiGLU experts,
+combine) over one batch of synthetic tokens already resident in HBM.  The
+headline line is the decode workload (T=64 tokens: 64 streams x one 80 ms
+frame); the prefill workload (T=4096) is reported alongside.  Weights rotate
+over several independently seeded layers so that timed reads come from HBM and
+not from the 256 MB Infinity Cache.
+
+    python bench.py [--steps K] [--warmup W] [--rotate R] [--no-cpu-baseline]
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores
+METRIC = "Talker MoE layer tokens/s (T=64 decode, T=4096 prefill); % HBM/MFMA peak"
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def layer_costs(shape, T, touched):
+    """Algorithmic bytes and flops of one layer step and of its gate/up pass.
+
+    Weight bytes count each touched expert once (bf16); activations count the
+    token rows read and written once; routing outputs 8 bytes per (token, slot).
+    """
+    H, E, k, I, Is = shape.H, shape.E, shape.k, shape.I, shape.Is
+    expert_b = 3 * I * H * 2
+    shared_b = 3 * Is * H * 2
+    router_b = E * H * 2
+    layer_bytes = touched * expert_b + shared_b + router_b + 2 * T * H * 2 + T * k * 8
+    layer_flops = T * (2 * H * E + 6 * H * I * k + 6 * H * Is)
+    gu_bytes = touched * 2 * I * H * 2 + 2 * Is * H * 2 + T * H * 2 + (T * k * I + T * Is) * 2
+    gu_flops = T * (4 * H * I * k + 4 * H * Is)
+    return layer_bytes, layer_flops, gu_bytes, gu_flops
+
+
+def pct(a, q):
+    return float(np.percentile(np.asarray(a), q)) if len(a) else None
+
+
+def measure(api, torch, INP, shape, T, weight_sets, steps, warmup):
+    cfg = api.Config(shape.H, shape.E, shape.k, shape.I, shape.Is, True, torch.bfloat16)
+    dev = torch.device("cuda", 0)
+    to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    xs = [to_dev(INP.activations(T, shape.H, 30 + i, "bf16")) for i in range(len(weight_sets))]
+    ys = [torch.empty_like(x) for x in xs]
+    ws = api.workspace(api.moe_workspace_size(cfg, T), dev)
+    structs = [api.weights_struct(w) for w in weight_sets]
+    R = len(weight_sets)
+
+    # routing of each weight set: number of experts that receive tokens
+    touched = []
+    counts = torch.empty(shape.E, dtype=torch.int32, device=dev)
+    for i in range(R):
+        api.moe_layer_forward(cfg, structs[i], xs[i], y=ys[i], counts=counts, ws=ws)
+        touched.append(int((counts > 0).sum().item()))
+    torch.cuda.synchronize()
+
+    for i in range(warmup):
+        api.moe_layer_forward(cfg, structs[i % R], xs[i % R], y=ys[i % R], ws=ws)
+    torch.cuda.synchronize()
+
+    # one HIP graph per weight set: the layer's launches replayed as one unit
+    graphs = []
+    for i in range(R):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            api.moe_layer_forward(cfg, structs[i], xs[i], y=ys[i], ws=ws)
+        graphs.append(g)
+    for i in range(warmup):
+        graphs[i % R].replay()
+    torch.cuda.synchronize()
+
+    def timed(fn):
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        start.record()
+        for i in range(steps):
+            fn(i)
+        stop.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(stop), time.perf_counter() - t0
+
+    # timed region: exactly `steps` layer steps (graph replay), then the same eagerly
+    gpu_ms, wall = timed(lambda i: graphs[i % R].replay())
+    eager_ms, _ = timed(lambda i: api.moe_layer_forward(cfg, structs[i % R], xs[i % R], y=ys[i % R], ws=ws))
+
+    # the same steps with HIP events at every stage boundary, on the library's stream
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
+    for row in evs:  # torch creates the HIP event on first record; the library re-records it
+        for e in row:
+            e.record()
+    torch.cuda.synchronize()
+    for i in range(steps):
+        api.moe_layer_forward(cfg, structs[i % R], xs[i % R], y=ys[i % R], ws=ws, stage_events=evs[i])
+    torch.cuda.synchronize()
+    names = ["route", "permute", "gate_up", "down", "combine"]
+    stages = {n: [evs[i][j].elapsed_time(evs[i][j + 1]) * 1e3 for i in range(steps)] for j, n in enumerate(names)}
+    step_us = [evs[i][0].elapsed_time(evs[i][5]) * 1e3 for i in range(steps)]
+
+    mean_touched = float(np.mean([touched[i % R] for i in range(steps)]))
+    lb, lf, gb, gf = layer_costs(shape, T, mean_touched)
+    s = gpu_ms / 1e3 / steps
+    gu_s = float(np.mean(stages["gate_up"])) * 1e-6
+    return {
+        "T": T, "steps": steps, "warmup": warmup, "weight_sets": R,
+        "ms_per_step": gpu_ms / steps, "wall_ms_per_step": wall * 1e3 / steps,
+        "eager_ms_per_step": eager_ms / steps,
+        "tokens_per_s": T / s, "touched_experts": touched,
+        "layer_bytes": lb, "layer_flops": lf, "layer_hbm_frac": lb / s / (HBM_PEAK_GBS * 1e9),
+        "layer_mfma_frac": lf / s / (MFMA_BF16_PEAK_TFLOPS * 1e12),
+        "step_us": {"p50": pct(step_us, 50), "p95": pct(step_us, 95), "p99": pct(step_us, 99)},
+        "stages_us_mean": {n: float(np.mean(v)) for n, v in stages.items()},
+        "gate_up": {"bytes": gb, "flops": gf, "mean_us": gu_s * 1e6,
+                    "p50_us": pct(stages["gate_up"], 50), "p99_us": pct(stages["gate_up"], 99),
+                    "gbs": gb / gu_s / 1e9, "tflops": gf / gu_s / 1e12},
+    }
+
+
+def cpu_baseline(INP, shape, T, seconds):
+    from oracle import moe_ref as R
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    except Exception:  # noqa: BLE001
+        threads = 1
+    w = INP.layer_weights(shape, 30, 0.02, "bf16")
+    w64 = {k: INP.to_f64(v, "bf16") for k, v in w.items()}
+    x64 = INP.to_f64(INP.activations(T, shape.H, 30, "bf16"), "bf16")
+    R.moe_layer(x64, w64, shape.k)  # first call outside the clock
+    n, t0 = 0, time.perf_counter()
+    while True:
+        R.moe_layer(x64, w64, shape.k)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": T * n / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "fp64 numpy oracle, one Talker MoE layer at T=%d (seed 30), %d calls in %.1f s" % (T, n, el)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--rotate", type=int, default=4, help="independently seeded weight sets cycled per step")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the layer is built and timed on a single MI355X; "
+              "--gpus %d is not supported" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from sparse_moe_transformer_talker_amd import api
+    from sparse_moe_transformer_talker_amd import inputs as INP
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    api.load_library()
+    shape = INP.TALKER
+    dev = torch.device("cuda", 0)
+    log("generating %d seeded weight sets" % args.rotate)
+    sets = []
+    for i in range(args.rotate):
+        w = INP.layer_weights(shape, 30 + i, 0.02, "bf16")
+        sets.append({k: torch.from_numpy(np.ascontiguousarray(v).view(np.int16)).view(torch.bfloat16).to(dev)
+                     for k, v in w.items()})
+        sets[-1]["router_bias"] = None
+    log("decode T=64")
+    dec = measure(api, torch, INP, shape, 64, sets, args.steps, args.warmup)
+    log("decode: %.2f us/step, %.3f M tok/s, gate/up %.1f us" % (dec["ms_per_step"] * 1e3,
+                                                                  dec["tokens_per_s"] / 1e6, dec["gate_up"]["mean_us"]))
+    pre = None
+    if not args.no_prefill:
+        log("prefill T=4096")
+        pre = measure(api, torch, INP, shape, 4096, sets, args.steps, args.warmup)
+        log("prefill: %.2f us/step, %.2f M tok/s" % (pre["ms_per_step"] * 1e3, pre["tokens_per_s"] / 1e6))
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle, ~%.0f s)" % args.cpu_seconds)
+        cpu = cpu_baseline(INP, shape, 64, args.cpu_seconds)
+
+    g = dec["gate_up"]
+    line = {
+        "metric": METRIC,
+        "value": dec["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": dec["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "talker_moe_layer_decode_T64", "tokens": 64, "hidden": shape.H,
+                   "experts": shape.E, "top_k": shape.k, "expert_intermediate": shape.I,
+                   "shared_intermediate": shape.Is, "weight_sets_rotated": args.rotate},
+        "roofline": {"bound": "hbm", "kernel": "grouped gate/up SwiGLU pass (routed + shared)",
+                     "achieved": g["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": g["gbs"] / HBM_PEAK_GBS, "traffic": None,
+                     "bytes_per_launch": g["bytes"], "mean_us": g["mean_us"]},
+        "layer": {"hbm_frac": dec["layer_hbm_frac"], "bytes_per_step": dec["layer_bytes"],
+                  "timing": "HIP graph replay per step; eager_ms_per_step without graphs",
+                  "eager_ms_per_step": dec["eager_ms_per_step"],
+                  "step_us": dec["step_us"], "stages_us_mean": dec["stages_us_mean"],
+                  "touched_experts": dec["touched_experts"]},
+        "cpu_baseline": cpu,
+    }
+    if pre is not None:
+        gp = pre["gate_up"]
+        line["prefill"] = {"workload": "talker_moe_layer_prefill_T4096", "tokens_per_s": pre["tokens_per_s"],
+                           "ms_per_step": pre["ms_per_step"], "eager_ms_per_step": pre["eager_ms_per_step"],
+                           "mfma_frac": pre["layer_mfma_frac"],
+                           "hbm_frac": pre["layer_hbm_frac"], "step_us": pre["step_us"],
+                           "stages_us_mean": pre["stages_us_mean"],
+                           "gate_up": {"mean_us": gp["mean_us"], "tflops": gp["tflops"],
+                                       "mfma_frac": gp["tflops"] / MFMA_BF16_PEAK_TFLOPS, "gbs": gp["gbs"]}}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -184,6 +184,21 @@ int moe_layer_forward(const moe_config* cfg, const moe_weights* w, const void* x
                       void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * moe_layer_forward_timed — moe_layer_forward that also records HIP events at
+ * its stage boundaries, for per-stage timing on the caller's stream (the
+ * Talker MoE page's §4 profiling advice: pin numbers on the real workload and
+ * keep percentiles).  stage_events is NULL or an array of 6 hipEvent_t, each
+ * NULL or created by the caller; event i is recorded on `stream`:
+ *   0 before routing, 1 after routing, 2 after grouping, 3 after the gate/up
+ *   pass of all experts, 4 after the down pass, 5 after the combine.
+ * Other arguments, results and errors are those of moe_layer_forward.
+ */
+int moe_layer_forward_timed(const moe_config* cfg, const moe_weights* w, const void* x,
+                            const void* residual, int64_t T, void* y, int32_t* topk_idx_out,
+                            float* topk_w_out, int32_t* counts_out, void* ws, size_t ws_bytes,
+                            void* stream, void* const* stage_events);
+
+/*
  * moe_rmsnorm — out = x / sqrt(mean(x^2) + eps) * gain over each row of H
  * (the pre-norm of the lab's [3C] step; eps 1e-6 and the final norm before
  * codec_head from the Qwen3-TTS module print on the horus-space page).

@@ -23,7 +23,8 @@ MOE_F32, MOE_BF16 = 0, 1
 STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID", -2: "MOE_ERR_UNSUPPORTED", -3: "MOE_ERR_WORKSPACE", -4: "MOE_ERR_HIP"}
 
 EXPORTS = ("moe_status_string", "moe_check_config", "moe_workspace_size", "moe_route", "moe_permute",
-           "moe_grouped_swiglu", "moe_shared_swiglu", "moe_combine", "moe_layer_forward", "moe_rmsnorm",
+           "moe_grouped_swiglu", "moe_shared_swiglu", "moe_combine", "moe_layer_forward",
+           "moe_layer_forward_timed", "moe_rmsnorm",
            "moe_codec_head_argmax", "moe_codec_head_workspace_size")
 
 
@@ -92,6 +93,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         "moe_combine": (ctypes.c_int, [cfgp, vp, vp, vp, vp, vp, i64, vp, vp]),
         "moe_layer_forward": (ctypes.c_int, [cfgp, ctypes.POINTER(moe_weights), vp, vp, i64, vp, vp, vp, vp,
                                              vp, sz, vp]),
+        "moe_layer_forward_timed": (ctypes.c_int, [cfgp, ctypes.POINTER(moe_weights), vp, vp, i64, vp, vp, vp,
+                                                   vp, vp, sz, vp, ctypes.POINTER(vp)]),
         "moe_rmsnorm": (ctypes.c_int, [cfgp, vp, vp, ctypes.c_float, i64, vp, vp]),
         "moe_codec_head_argmax": (ctypes.c_int, [cfgp, vp, vp, i32, i64, vp, vp, vp, sz, vp]),
         "moe_codec_head_workspace_size": (sz, [cfgp, i32, i64]),
@@ -235,17 +238,23 @@ def weights_struct(w: Dict[str, Optional[torch.Tensor]]) -> moe_weights:
 
 
 def moe_layer_forward(cfg: Config, weights, x: torch.Tensor, residual: Optional[torch.Tensor] = None,
-                      y=None, topk_idx=None, topk_w=None, counts=None, ws=None, stream=None):
+                      y=None, topk_idx=None, topk_w=None, counts=None, ws=None, stream=None, stage_events=None):
     """The whole MoE layer.  ``weights``: dict of device tensors or a prebuilt moe_weights.
-    Returns y [T, H] (routing copies are written to the optional tensors)."""
+    Returns y [T, H] (routing copies are written to the optional tensors).  With
+    ``stage_events`` (6 torch.cuda.Event or None) it calls moe_layer_forward_timed."""
     T, dev = x.shape[0], x.device
     y = y if y is not None else torch.empty_like(x)
     ws_struct = weights if isinstance(weights, moe_weights) else weights_struct(weights)
     buf, n = _ws(cfg, T, dev, ws)
     st = stream if stream is not None else _stream(dev)
-    _check("moe_layer_forward", load_library().moe_layer_forward(
-        ctypes.byref(cfg.c()), ctypes.byref(ws_struct), _ptr(x), _ptr(residual), T, _ptr(y), _ptr(topk_idx),
-        _ptr(topk_w), _ptr(counts), _ptr(buf), n, st))
+    lib = load_library()
+    args = (ctypes.byref(cfg.c()), ctypes.byref(ws_struct), _ptr(x), _ptr(residual), T, _ptr(y), _ptr(topk_idx),
+            _ptr(topk_w), _ptr(counts), _ptr(buf), n, st)
+    if stage_events is None:
+        _check("moe_layer_forward", lib.moe_layer_forward(*args))
+    else:
+        evs = (ctypes.c_void_p * 6)(*[None if e is None else e.cuda_event for e in stage_events])
+        _check("moe_layer_forward_timed", lib.moe_layer_forward_timed(*args, evs))
     return y
 
 

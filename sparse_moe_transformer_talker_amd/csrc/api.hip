@@ -106,7 +106,8 @@ struct LayerPlan {
     int32_t* idx;
     float* w;
     RoutePlan route;
-    int32_t *counts, *offsets, *hist, *row_token, *row_of, *row_dst;
+    uint16_t* masks;
+    int32_t *prefix, *counts, *offsets, *row_token, *row_of, *row_dst;
     float* row_scale;
     GemmPlan gemm;
     void *hr, *hs, *ybuf;
@@ -115,14 +116,14 @@ void plan_layer(const moe_config* c, int64_t T, Carver& cv, LayerPlan& p) {
     const int E = c->num_experts, k = c->num_experts_per_tok, H = c->hidden_size;
     const int I = c->moe_intermediate_size, Is = c->shared_expert_intermediate_size;
     const int64_t N = T * k;
-    const int64_t nb = (N + kPermChunk - 1) / kPermChunk;
     const size_t es = esize(c->dtype);
     p.idx = cv.take<int32_t>(N);
     p.w = cv.take<float>(N);
     plan_route(c, T, cv, p.route);
     p.counts = cv.take<int32_t>(E);
     p.offsets = cv.take<int32_t>(E + 1);
-    p.hist = cv.take<int32_t>(nb * E);
+    p.masks = cv.take<uint16_t>((int64_t)E * mask_stride(T));
+    p.prefix = cv.take<int32_t>((int64_t)E * mask_stride(T));
     p.row_token = cv.take<int32_t>(N);
     p.row_of = cv.take<int32_t>(N);
     p.row_dst = cv.take<int32_t>(N);
@@ -141,7 +142,8 @@ size_t route_ws(const moe_config* c, int64_t T) {
 }
 size_t permute_ws(const moe_config* c, int64_t T) {
     Carver cv(nullptr);
-    cv.take<int32_t>(((T * c->num_experts_per_tok + kPermChunk - 1) / kPermChunk) * c->num_experts);
+    cv.take<uint16_t>((int64_t)c->num_experts * mask_stride(T));
+    cv.take<int32_t>((int64_t)c->num_experts * mask_stride(T));
     return cv.size();
 }
 size_t grouped_ws(const moe_config* c, int64_t T, void* base, GemmPlan* g, void** hr) {
@@ -266,7 +268,7 @@ int moe_route(const moe_config* cfg, const void* x, const void* router, const fl
     plan_route(cfg, T, cv, p);
     return hip_status(launch_route(cfg->dtype, x, router, bias, T, cfg->hidden_size, cfg->num_experts,
                                    cfg->num_experts_per_tok, cfg->norm_topk_prob, topk_idx, topk_w, probs, p.sc, p.bd,
-                                   as_stream(stream)));
+                                   nullptr, as_stream(stream)));
 }
 
 int moe_permute(const moe_config* cfg, const int32_t* topk_idx, int64_t T, int32_t* counts, int32_t* offsets,
@@ -289,9 +291,11 @@ int moe_permute(const moe_config* cfg, const int32_t* topk_idx, int64_t T, int32
     if ((x == nullptr) != (x_perm == nullptr)) return MOE_ERR_INVALID;
     if (ws_bytes < permute_ws(cfg, T)) return MOE_ERR_WORKSPACE;
     Carver cv(ws);
-    int32_t* hist = cv.take<int32_t>(((T * k + kPermChunk - 1) / kPermChunk) * E);
-    TMOE_TRY(launch_permute(topk_idx, T, k, E, hist, counts, offsets, row_token, row_of, nullptr, nullptr, nullptr, 0,
-                            nullptr, nullptr, s));
+    uint16_t* masks = cv.take<uint16_t>((int64_t)E * mask_stride(T));
+    int32_t* prefix = cv.take<int32_t>((int64_t)E * mask_stride(T));
+    TMOE_TRY(launch_masks(topk_idx, T, k, E, masks, s));
+    TMOE_TRY(launch_permute(topk_idx, T, k, E, masks, prefix, counts, offsets, row_token, row_of, nullptr, nullptr,
+                            nullptr, 0, nullptr, nullptr, s));
     if (x) TMOE_TRY(launch_gather_rows(cfg->dtype, x, row_token, T * k, cfg->hidden_size, x_perm, s));
     return MOE_OK;
 }
@@ -361,6 +365,13 @@ int moe_combine(const moe_config* cfg, const void* y_perm, const int32_t* row_of
 int moe_layer_forward(const moe_config* cfg, const moe_weights* w, const void* x, const void* residual, int64_t T,
                       void* y, int32_t* topk_idx_out, float* topk_w_out, int32_t* counts_out, void* ws,
                       size_t ws_bytes, void* stream) {
+    return moe_layer_forward_timed(cfg, w, x, residual, T, y, topk_idx_out, topk_w_out, counts_out, ws, ws_bytes,
+                                   stream, nullptr);
+}
+
+int moe_layer_forward_timed(const moe_config* cfg, const moe_weights* w, const void* x, const void* residual,
+                            int64_t T, void* y, int32_t* topk_idx_out, float* topk_w_out, int32_t* counts_out,
+                            void* ws, size_t ws_bytes, void* stream, void* const* stage_events) {
     int st = check_cfg(cfg);
     if (st != MOE_OK) return st;
     if ((st = check_T(cfg, T)) != MOE_OK) return st;
@@ -386,13 +397,20 @@ int moe_layer_forward(const moe_config* cfg, const moe_weights* w, const void* x
     int32_t* idx = topk_idx_out ? topk_idx_out : p.idx;
     float* wt = topk_w_out ? topk_w_out : p.w;
     int32_t* counts = counts_out ? counts_out : p.counts;
+    auto mark = [&](int i) -> hipError_t {
+        return (stage_events && stage_events[i]) ? hipEventRecord(static_cast<hipEvent_t>(stage_events[i]), s)
+                                                 : hipSuccess;
+    };
 
+    TMOE_TRY(mark(0));
     TMOE_TRY(launch_route(cfg->dtype, x, w->router, w->router_bias, T, H, E, k, cfg->norm_topk_prob, idx, wt, nullptr,
-                          p.route.sc, p.route.bd, s));
+                          p.route.sc, p.route.bd, p.masks, s));
+    TMOE_TRY(mark(1));
     const int slots = k + 1;  // per token: k weighted expert rows, then the shared row
-    TMOE_TRY(launch_permute(idx, T, k, E, p.hist, counts, p.offsets, p.row_token, p.row_of, wt, p.row_dst,
+    TMOE_TRY(launch_permute(idx, T, k, E, p.masks, p.prefix, counts, p.offsets, p.row_token, p.row_of, wt, p.row_dst,
                             p.row_scale, slots, p.gemm.mfma ? &p.gemm.t[0] : nullptr,
                             p.gemm.mfma ? &p.gemm.t[1] : nullptr, s));
+    TMOE_TRY(mark(2));
 
     GemmGroup gu_r = group(w->gate, w->up, (int64_t)I * H, I, H, x, H, p.row_token, p.hr, I, nullptr, 1, 0, nullptr);
     GemmGroup gu_s = Is > 0 ? group(w->shared_gate, w->shared_up, 0, Is, H, x, H, nullptr, p.hs, Is, nullptr, 1, 0,
@@ -400,6 +418,7 @@ int moe_layer_forward(const moe_config* cfg, const moe_weights* w, const void* x
                             : no_group();
     int r = run_gemm_pass(cfg, p.gemm, 0, gu_r, gu_s, p.offsets, N, T, s);
     if (r != MOE_OK) return r;
+    TMOE_TRY(mark(3));
     GemmGroup dn_r = group(w->down, nullptr, (int64_t)H * I, H, I, p.hr, I, nullptr, p.ybuf, H, p.row_dst, 1, 0,
                            p.row_scale);
     GemmGroup dn_s = Is > 0 ? group(w->shared_down, nullptr, 0, H, Is, p.hs, Is, nullptr, p.ybuf, H, nullptr, slots,
@@ -407,9 +426,12 @@ int moe_layer_forward(const moe_config* cfg, const moe_weights* w, const void* x
                             : no_group();
     r = run_gemm_pass(cfg, p.gemm, 1, dn_r, dn_s, p.offsets, N, T, s);
     if (r != MOE_OK) return r;
+    TMOE_TRY(mark(4));
     const char* shared_base = Is > 0 ? static_cast<const char*>(p.ybuf) + (int64_t)k * H * esize(cfg->dtype) : nullptr;
-    return hip_status(launch_combine(cfg->dtype, p.ybuf, nullptr, nullptr, k, slots, shared_base,
-                                     (int64_t)slots * H, residual, y, T, H, s));
+    TMOE_TRY(launch_combine(cfg->dtype, p.ybuf, nullptr, nullptr, k, slots, shared_base, (int64_t)slots * H,
+                            residual, y, T, H, s));
+    TMOE_TRY(mark(5));
+    return MOE_OK;
 }
 
 int moe_rmsnorm(const moe_config* cfg, const void* x, const float* gain, float eps, int64_t T, void* out,

@@ -70,6 +70,86 @@ __device__ __forceinline__ void wave_best(V& v, int& i) {
     }
 }
 
+// --- DPP wave primitives (row_shr within 16-lane rows, then row_bcast15 /
+// row_bcast31 across rows).  Disabled or out-of-row source lanes contribute the
+// `old` operand, which is the identity of the operation.
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114, kDppRowShr8 = 0x118;
+constexpr int kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
+
+// Inclusive prefix sum over the 64 lanes.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, kDppRowShr1, 0xf, 0xf, false);
+    x += __builtin_amdgcn_update_dpp(0, x, kDppRowShr2, 0xf, 0xf, false);
+    x += __builtin_amdgcn_update_dpp(0, x, kDppRowShr4, 0xf, 0xf, false);
+    x += __builtin_amdgcn_update_dpp(0, x, kDppRowShr8, 0xf, 0xf, false);
+    x += __builtin_amdgcn_update_dpp(0, x, kDppRowBcast15, 0xa, 0xf, false);
+    x += __builtin_amdgcn_update_dpp(0, x, kDppRowBcast31, 0xc, 0xf, false);
+    return x;
+}
+
+// Maximum of a 64-bit key over the wave, returned to every lane (0 is the identity).
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t key) {
+#define TMOE_MAX_STEP(CTRL, ROWS)                                                                    \
+    {                                                                                                \
+        uint32_t lo = __builtin_amdgcn_update_dpp(0u, (uint32_t)key, CTRL, ROWS, 0xf, false);        \
+        uint32_t hi = __builtin_amdgcn_update_dpp(0u, (uint32_t)(key >> 32), CTRL, ROWS, 0xf, false); \
+        uint64_t o = ((uint64_t)hi << 32) | lo;                                                      \
+        key = o > key ? o : key;                                                                     \
+    }
+    TMOE_MAX_STEP(kDppRowShr1, 0xf)
+    TMOE_MAX_STEP(kDppRowShr2, 0xf)
+    TMOE_MAX_STEP(kDppRowShr4, 0xf)
+    TMOE_MAX_STEP(kDppRowShr8, 0xf)
+    TMOE_MAX_STEP(kDppRowBcast15, 0xa)
+    TMOE_MAX_STEP(kDppRowBcast31, 0xc)
+#undef TMOE_MAX_STEP
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)key, 63);
+    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(key >> 32), 63);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Sum / maximum over the wave, returned to every lane (fixed order: deterministic).
+__device__ __forceinline__ float wave_sum_dpp(float x) {
+#define TMOE_SUM_STEP(CTRL, ROWS) \
+    x += __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(x), CTRL, ROWS, 0xf, false));
+    TMOE_SUM_STEP(kDppRowShr1, 0xf)
+    TMOE_SUM_STEP(kDppRowShr2, 0xf)
+    TMOE_SUM_STEP(kDppRowShr4, 0xf)
+    TMOE_SUM_STEP(kDppRowShr8, 0xf)
+    TMOE_SUM_STEP(kDppRowBcast15, 0xa)
+    TMOE_SUM_STEP(kDppRowBcast31, 0xc)
+#undef TMOE_SUM_STEP
+    return __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(x), 63));
+}
+__device__ __forceinline__ float wave_max_dpp(float x) {
+    const uint32_t ninf = 0xFF800000u;
+#define TMOE_FMAX_STEP(CTRL, ROWS) \
+    x = fmaxf(x, __uint_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_uint(x), CTRL, ROWS, 0xf, false)));
+    TMOE_FMAX_STEP(kDppRowShr1, 0xf)
+    TMOE_FMAX_STEP(kDppRowShr2, 0xf)
+    TMOE_FMAX_STEP(kDppRowShr4, 0xf)
+    TMOE_FMAX_STEP(kDppRowShr8, 0xf)
+    TMOE_FMAX_STEP(kDppRowBcast15, 0xa)
+    TMOE_FMAX_STEP(kDppRowBcast31, 0xc)
+#undef TMOE_FMAX_STEP
+    return __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(x), 63));
+}
+
+// Order-preserving map of a finite float to uint32 (larger float -> larger key);
+// -0 and +0 map to the same key.
+__device__ __forceinline__ uint32_t float_order_key(float f) {
+    const uint32_t u = __float_as_uint(f + 0.0f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float float_from_order_key(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+// Key ranking larger values first and, among equal values, lower indices first.
+__device__ __forceinline__ uint64_t rank_key(float v, int idx) {
+    return ((uint64_t)float_order_key(v) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)idx);
+}
+__device__ __forceinline__ int rank_key_index(uint64_t k) { return (int)(0xFFFFFFFFu - (uint32_t)k); }
+
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
 __device__ __forceinline__ uint64_t lanemask_lt() {
     int l = lane_id();

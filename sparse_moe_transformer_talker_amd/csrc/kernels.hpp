@@ -10,13 +10,13 @@ constexpr int kF32 = 0;
 constexpr int kBF16 = 1;
 constexpr int kMaxTopK = 32;
 constexpr int kMaxExperts = 1024;
-constexpr int kPermChunk = 512;  // (token, slot) pairs per permutation block
 
 // --- routing (route.hip) ---
 bool route_fused_ok(int dtype, int H, int E);
+// masks (nullable): [E][mask_stride(T)] uint16, bit t % 16 of word t / 16 set when token t routes to e
 hipError_t launch_route(int dtype, const void* x, const void* W, const float* bias, int64_t T, int H, int E, int k,
                         int norm, int32_t* idx, float* w, float* probs, float* scratch_sc, float* scratch_bd,
-                        hipStream_t st);
+                        uint16_t* masks, hipStream_t st);
 hipError_t launch_scores(int dtype, const void* x, const void* W, const float* bias, int64_t T, int H, int n,
                          float* sc, float* bd, hipStream_t st);
 hipError_t launch_argmax(int dtype, const float* sc, const float* bd, const void* x, const void* W, int64_t T, int H,
@@ -34,8 +34,12 @@ struct TileSpec {
     int max_items;
 };
 int64_t tile_max_items(int64_t pairs, int E, int64_t T, int mt, int nt, int n_routed, int n_shared);
-hipError_t launch_permute(const int32_t* idx, int64_t T, int k, int E, int32_t* hist, int32_t* counts,
-                          int32_t* offsets, int32_t* row_token, int32_t* row_of, const float* w,
+int mask_words(int64_t T);
+int mask_stride(int64_t T);
+hipError_t launch_masks(const int32_t* idx, int64_t T, int k, int E, uint16_t* masks, hipStream_t st);
+// prefix: [E][mask_stride(T)] int32 scratch
+hipError_t launch_permute(const int32_t* idx, int64_t T, int k, int E, const uint16_t* masks, int32_t* prefix,
+                          int32_t* counts, int32_t* offsets, int32_t* row_token, int32_t* row_of, const float* w,
                           int32_t* row_dst, float* row_scale, int slots, const TileSpec* t1, const TileSpec* t2,
                           hipStream_t st);
 hipError_t launch_build_items(const int32_t* offsets, int E, int64_t T, const TileSpec* t1, const TileSpec* t2,
