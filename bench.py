@@ -164,6 +164,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-calibration-mb", type=int, default=0,
+                    help="after timing, copy a buffer of this many MiB once (a plain copy kernel of known size, "
+                         "for scaling hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the layer is built and timed on a single MI355X; "
@@ -187,15 +191,28 @@ def main():
         sets.append({k: torch.from_numpy(np.ascontiguousarray(v).view(np.int16)).view(torch.bfloat16).to(dev)
                      for k, v in w.items()})
         sets[-1]["router_bias"] = None
-    log("decode T=64")
-    dec = measure(api, torch, INP, shape, 64, sets, args.steps, args.warmup)
-    log("decode: %.2f us/step, %.3f M tok/s, gate/up %.1f us" % (dec["ms_per_step"] * 1e3,
-                                                                  dec["tokens_per_s"] / 1e6, dec["gate_up"]["mean_us"]))
+    dec = None
+    if not args.no_decode:
+        log("decode T=64")
+        dec = measure(api, torch, INP, shape, 64, sets, args.steps, args.warmup)
+        log("decode: %.2f us/step, %.3f M tok/s, gate/up %.1f us" % (
+            dec["ms_per_step"] * 1e3, dec["tokens_per_s"] / 1e6, dec["gate_up"]["mean_us"]))
     pre = None
     if not args.no_prefill:
         log("prefill T=4096")
         pre = measure(api, torch, INP, shape, 4096, sets, args.steps, args.warmup)
         log("prefill: %.2f us/step, %.2f M tok/s" % (pre["ms_per_step"] * 1e3, pre["tokens_per_s"] / 1e6))
+    if args.copy_calibration_mb:
+        n = args.copy_calibration_mb << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("calibration copy of %d MiB done" % args.copy_calibration_mb)
+    if dec is None:
+        print(json.dumps({"prefill": pre}), flush=True)
+        return
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle, ~%.0f s)" % args.cpu_seconds)

@@ -63,10 +63,8 @@ struct RoutePlan {
     float* bd = nullptr;
 };
 void plan_route(const moe_config* c, int64_t T, Carver& cv, RoutePlan& p) {
-    if (!route_fused_ok(c->dtype, c->hidden_size, c->num_experts)) {
-        p.sc = cv.take<float>(T * c->num_experts);
-        p.bd = cv.take<float>(T * c->num_experts);
-    }
+    p.sc = cv.take<float>(T * c->num_experts);
+    p.bd = cv.take<float>(T * c->num_experts);
 }
 
 struct GemmPlan {
@@ -83,7 +81,9 @@ void plan_gemm(const moe_config* c, int64_t T, bool routed, bool shared, Carver&
     if (!g.mfma) return;
     const int64_t pairs = routed ? T * k : 0;
     const int64_t rows_per_expert = routed ? pairs / E : T;
-    g.variant = rows_per_expert >= 32 ? kGemmLargeM : kGemmSmallM;
+    if (rows_per_expert < 32) g.variant = kGemmSmallM;
+    else if (!gemm_lds_ok(H, I, Is)) g.variant = kGemmLargeM;
+    else g.variant = rows_per_expert >= 160 ? kGemmHugeLds : kGemmLargeLds;
     int* counters = cv.take<int>(4);
     for (int pass = 0; pass < 2; ++pass) {
         int mt, nt;
@@ -402,14 +402,19 @@ int moe_layer_forward_timed(const moe_config* cfg, const moe_weights* w, const v
                                                  : hipSuccess;
     };
 
+    const int slots = k + 1;  // per token: k weighted expert rows, then the shared row
+    const TileSpec* t1 = p.gemm.mfma ? &p.gemm.t[0] : nullptr;
+    const TileSpec* t2 = p.gemm.mfma ? &p.gemm.t[1] : nullptr;
     TMOE_TRY(mark(0));
     TMOE_TRY(launch_route(cfg->dtype, x, w->router, w->router_bias, T, H, E, k, cfg->norm_topk_prob, idx, wt, nullptr,
                           p.route.sc, p.route.bd, p.masks, s));
     TMOE_TRY(mark(1));
-    const int slots = k + 1;  // per token: k weighted expert rows, then the shared row
-    TMOE_TRY(launch_permute(idx, T, k, E, p.masks, p.prefix, counts, p.offsets, p.row_token, p.row_of, wt, p.row_dst,
-                            p.row_scale, slots, p.gemm.mfma ? &p.gemm.t[0] : nullptr,
-                            p.gemm.mfma ? &p.gemm.t[1] : nullptr, s));
+    if (group_small_ok(T, E))
+        TMOE_TRY(launch_group_small(idx, wt, p.masks, T, E, k, counts, p.offsets, p.row_token, p.row_of, p.row_dst,
+                                    p.row_scale, slots, t1, t2, s));
+    else
+        TMOE_TRY(launch_permute(idx, T, k, E, p.masks, p.prefix, counts, p.offsets, p.row_token, p.row_of, wt,
+                                p.row_dst, p.row_scale, slots, t1, t2, s));
     TMOE_TRY(mark(2));
 
     GemmGroup gu_r = group(w->gate, w->up, (int64_t)I * H, I, H, x, H, p.row_token, p.hr, I, nullptr, 1, 0, nullptr);

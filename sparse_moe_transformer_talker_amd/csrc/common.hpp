@@ -135,6 +135,51 @@ __device__ __forceinline__ float wave_max_dpp(float x) {
     return __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(x), 63));
 }
 
+// --- all-reduce inside each 16-lane row (DPP row_ror by 8, 4, 2, 1): every
+// lane of a row gets the row's result.  Sums associate differently per lane
+// (each lane's value is deterministic).
+#define TMOE_ROR(V, N) __builtin_amdgcn_update_dpp(0u, (V), 0x120 + (N), 0xf, 0xf, false)
+__device__ __forceinline__ uint64_t row_max_key(uint64_t key) {
+#define TMOE_RMAX(N)                                                          \
+    {                                                                         \
+        const uint32_t lo = TMOE_ROR((uint32_t)key, N);                       \
+        const uint32_t hi = TMOE_ROR((uint32_t)(key >> 32), N);               \
+        const uint64_t o = ((uint64_t)hi << 32) | lo;                         \
+        key = o > key ? o : key;                                              \
+    }
+    TMOE_RMAX(8)
+    TMOE_RMAX(4)
+    TMOE_RMAX(2)
+    TMOE_RMAX(1)
+#undef TMOE_RMAX
+    return key;
+}
+__device__ __forceinline__ float row_sum(float x) {
+    x += __uint_as_float(TMOE_ROR(__float_as_uint(x), 8));
+    x += __uint_as_float(TMOE_ROR(__float_as_uint(x), 4));
+    x += __uint_as_float(TMOE_ROR(__float_as_uint(x), 2));
+    x += __uint_as_float(TMOE_ROR(__float_as_uint(x), 1));
+    return x;
+}
+__device__ __forceinline__ float row_max(float x) {
+    x = fmaxf(x, __uint_as_float(TMOE_ROR(__float_as_uint(x), 8)));
+    x = fmaxf(x, __uint_as_float(TMOE_ROR(__float_as_uint(x), 4)));
+    x = fmaxf(x, __uint_as_float(TMOE_ROR(__float_as_uint(x), 2)));
+    x = fmaxf(x, __uint_as_float(TMOE_ROR(__float_as_uint(x), 1)));
+    return x;
+}
+// Order-preserving map of a double to uint64, and the row minimum built on it.
+__device__ __forceinline__ uint64_t double_order_key(double d) {
+    const uint64_t u = __double_as_longlong(d + 0.0);
+    return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
+}
+__device__ __forceinline__ double double_from_order_key(uint64_t k) {
+    return __longlong_as_double((long long)((k >> 63) ? (k & 0x7FFFFFFFFFFFFFFFull) : ~k));
+}
+__device__ __forceinline__ double row_min(double x) {
+    return double_from_order_key(~row_max_key(~double_order_key(x)));
+}
+
 // Order-preserving map of a finite float to uint32 (larger float -> larger key);
 // -0 and +0 map to the same key.
 __device__ __forceinline__ uint32_t float_order_key(float f) {

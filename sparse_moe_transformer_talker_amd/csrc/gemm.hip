@@ -160,6 +160,193 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs args) {
 }
 
 // ---------------------------------------------------------------------------
+// Many rows per expert: BM x 256 tiles, BM = 128 or 256 (gate/up: 128 gate +
+// 128 up columns; down: 256 output columns) on v_mfma_f32_32x32x16_bf16, four
+// waves of (BM / 2) x 128.
+// K advances in stages of 32; every stage is copied global -> LDS by the
+// direct-to-LDS loads (no VGPR staging) into a ring of 4 buffers with 3 stages
+// in flight, waited for with vmcnt and a raw s_barrier.  In LDS a tile row is
+// 64 bytes (four 16-byte chunks); chunk c of row r is stored at position
+// (c + r / 4) % 4, which spreads the 32 rows one fragment read touches over
+// all banks.  The rotation is realised by choosing which global chunk each
+// lane fetches, since lane i of a direct-to-LDS load writes bytes
+// [16 i, 16 i + 16) of its 1 KB destination.
+namespace lds_gemm {
+constexpr int BNR = 256, BK = 32;
+constexpr int NSTAGE = 4, INFLIGHT = NSTAGE - 1;
+constexpr int B_BYTES = BNR * BK * 2;
+constexpr int B_CALLS = B_BYTES / 1024 / 4;  // per wave, per stage
+template <int BM> struct Tile {
+    static constexpr int A_BYTES = BM * BK * 2;
+    static constexpr int STAGE = A_BYTES + B_BYTES;
+    static constexpr int A_CALLS = A_BYTES / 1024 / 4;
+    static constexpr int CALLS = A_CALLS + B_CALLS;
+    static constexpr int MI = BM / 64;  // 32-row blocks per wave (2 x 2 waves)
+};
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ int lds_chunk(int row, int c) { return (c + (row >> 2)) & 3; }
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    // vmcnt <= N (N < 64); expcnt and lgkmcnt left at their maxima
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+}  // namespace lds_gemm
+
+template <int PASS, int BM>
+__global__ __launch_bounds__(256) void grouped_gemm_lds_kernel(GemmArgs args) {
+    using namespace lds_gemm;
+    constexpr int A_BYTES = Tile<BM>::A_BYTES, STAGE = Tile<BM>::STAGE, A_CALLS = Tile<BM>::A_CALLS;
+    constexpr int CALLS = Tile<BM>::CALLS, MI = Tile<BM>::MI;
+    // one array per ring stage, so the compiler can tell which direct-to-LDS
+    // load writes which buffer and waits only for the right one
+    __shared__ __attribute__((aligned(1024))) char buf0[STAGE];
+    __shared__ __attribute__((aligned(1024))) char buf1[STAGE];
+    __shared__ __attribute__((aligned(1024))) char buf2[STAGE];
+    __shared__ __attribute__((aligned(1024))) char buf3[STAGE];
+
+    const int n_items = *args.count;
+    const int p = blockIdx.x;
+    const int chunk = (n_items + 7) >> 3;
+    const int slot = p >> 3;
+    if (slot >= chunk) return;
+    const int q = (p & 7) * chunk + slot;
+    if (q >= n_items) return;
+    const int4 it = args.items[q];
+    const int gi = it.x < args.E ? 0 : 1;
+    const GemmGroup& g = args.g[gi];
+    const int e = gi == 0 ? it.x : 0;
+    const int n0 = it.y, m0 = it.z, mrows = it.w;
+    const int K = g.K;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+
+    // Global sources of this lane's direct-to-LDS chunks (fixed over K).
+    const bf16_t* pa[A_CALLS];
+    const bf16_t* pb[B_CALLS];
+#pragma unroll
+    for (int j = 0; j < A_CALLS; ++j) {
+        const int r = (wave * A_CALLS + j) * 16 + (lane >> 2);
+        const int c = ((lane & 3) - (r >> 2)) & 3;  // global chunk landing at position lane & 3
+        const int m = r < mrows ? r : 0;
+        const int64_t grow = g.a_rows ? (int64_t)g.a_rows[m0 + m] : (int64_t)(m0 + m);
+        pa[j] = (const bf16_t*)g.a + grow * g.a_ld + c * 8;
+    }
+#pragma unroll
+    for (int j = 0; j < B_CALLS; ++j) {
+        const int r = (wave * B_CALLS + j) * 16 + (lane >> 2);
+        const int c = ((lane & 3) - (r >> 2)) & 3;
+        const bf16_t* w;
+        int wrow;
+        if (PASS == 0) {
+            w = (const bf16_t*)(r < BNR / 2 ? g.wa : g.wb);
+            wrow = n0 + (r & (BNR / 2 - 1));
+        } else {
+            w = (const bf16_t*)g.wa;
+            wrow = n0 + r;
+        }
+        pb[j] = w + (int64_t)e * g.w_estride + (int64_t)wrow * K + c * 8;
+    }
+    typedef __attribute__((address_space(3))) void lds_void;
+    auto issue = [&](int stage, char* base) {
+        const int k0 = stage * BK;
+#pragma unroll
+        for (int j = 0; j < A_CALLS; ++j)
+            __builtin_amdgcn_global_load_lds((const void*)(pa[j] + k0),
+                                             (lds_void*)(base + (wave * A_CALLS + j) * 1024), 16, 0, 0);
+#pragma unroll
+        for (int j = 0; j < B_CALLS; ++j)
+            __builtin_amdgcn_global_load_lds((const void*)(pb[j] + k0),
+                                             (lds_void*)(base + A_BYTES + (wave * B_CALLS + j) * 1024), 16, 0, 0);
+    };
+
+    const int wm = wave >> 1, wn = wave & 1;
+    const int lr = lane & 31, lh = lane >> 5;
+    f32x16 acc[MI][4];
+#pragma unroll
+    for (int a = 0; a < MI; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
+    // B-tile row of fragment column block b (32 columns)
+    auto brow0 = [&](int b) {
+        if (PASS == 0) return (b < 2 ? 0 : BNR / 2) + wn * 64 + (b & 1) * 32;
+        return wn * 128 + b * 32;
+    };
+    auto compute = [&](const char* base) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const int c = 2 * ks + lh;
+            bf16x8 af[MI], bfr[4];
+#pragma unroll
+            for (int a = 0; a < MI; ++a) {
+                const int r = wm * (BM / 2) + a * 32 + lr;
+                af[a] = *reinterpret_cast<const bf16x8*>(base + r * 64 + lds_chunk(r, c) * 16);
+            }
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const int r = brow0(b) + lr;
+                bfr[b] = *reinterpret_cast<const bf16x8*>(base + A_BYTES + r * 64 + lds_chunk(r, c) * 16);
+            }
+#pragma unroll
+            for (int a = 0; a < MI; ++a)
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bfr[b], acc[a][b], 0, 0, 0);
+        }
+    };
+    // stage s: wait until its loads (all waves') have landed, refill the buffer
+    // freed by stage s - 1 with stage s + 3, compute stage s
+    const int nst = K / BK;  // a multiple of 4
+    auto step = [&](int s, const char* cur, char* refill) {
+        const int newer = min(INFLIGHT - 1, nst - 1 - s);
+        if (newer >= 2) wait_vm<2 * CALLS>();
+        else if (newer == 1) wait_vm<CALLS>();
+        else wait_vm<0>();
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (s + INFLIGHT < nst) issue(s + INFLIGHT, refill);
+        compute(cur);
+    };
+    issue(0, buf0);
+    issue(1, buf1);
+    issue(2, buf2);
+    for (int s = 0; s < nst; s += 4) {
+        step(s, buf0, buf3);
+        step(s + 1, buf1, buf0);
+        step(s + 2, buf2, buf1);
+        step(s + 3, buf3, buf2);
+    }
+
+    // Epilogue: lane holds D[8 * (i / 4) + 4 * (lane / 32) + i % 4][lane % 32] of each 32 x 32 block.
+    bf16_t* out = (bf16_t*)g.out;
+#pragma unroll
+    for (int a = 0; a < MI; ++a)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int row = wm * (BM / 2) + a * 32 + 8 * (i >> 2) + 4 * lh + (i & 3);
+            if (row >= mrows) continue;
+            const int64_t src = (int64_t)m0 + row;
+            const int64_t dst = (g.out_rows ? (int64_t)g.out_rows[src] : src) * g.out_mul + g.out_add;
+            if (PASS == 0) {
+#pragma unroll
+                for (int b = 0; b < 2; ++b) {
+                    const float gv = acc[a][b][i];
+                    const float v = gv / (1.0f + __expf(-gv)) * acc[a][b + 2][i];
+                    out[dst * g.out_ld + n0 + wn * 64 + b * 32 + lr] = f32_to_bf16(v);
+                }
+            } else {
+                const float sc = g.out_scale ? g.out_scale[src] : 1.0f;
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+                    out[dst * g.out_ld + n0 + wn * 128 + b * 32 + lr] = f32_to_bf16(acc[a][b][i] * sc);
+            }
+        }
+}
+
+// ---------------------------------------------------------------------------
 // Portable path (fp32 and shapes the matrix-core tiles do not cover): one
 // thread per output element, fp32 accumulation.
 template <typename T, int PASS>
@@ -207,7 +394,14 @@ __global__ __launch_bounds__(256) void gemm_generic_kernel(GemmGroup g, const in
 
 void gemm_tiles(int variant, int pass, int* mt, int* nt) {
     if (variant == kGemmSmallM) { *mt = 16; *nt = pass == 0 ? 64 : 128; }
+    else if (variant == kGemmLargeLds) { *mt = 128; *nt = pass == 0 ? lds_gemm::BNR / 2 : lds_gemm::BNR; }
+    else if (variant == kGemmHugeLds) { *mt = 256; *nt = pass == 0 ? lds_gemm::BNR / 2 : lds_gemm::BNR; }
     else { *mt = 128; *nt = pass == 0 ? 64 : 128; }
+}
+
+bool gemm_lds_ok(int H, int I, int Is) {
+    // K stages of 32 in groups of 4 (K % 128) and whole 128 x 256 tiles
+    return H % 256 == 0 && I % 128 == 0 && Is % 128 == 0;
 }
 
 bool gemm_mfma_ok(int dtype, int H, int I, int Is) {
@@ -222,6 +416,12 @@ hipError_t launch_grouped_gemm(int dtype, int variant, int pass, const GemmArgs&
     if (variant == kGemmSmallM) {
         if (pass == 0) grouped_gemm_kernel<TMOE_SMALL_GU><<<grid, 256, 0, st>>>(args);
         else grouped_gemm_kernel<TMOE_SMALL_DN><<<grid, 256, 0, st>>>(args);
+    } else if (variant == kGemmLargeLds) {
+        if (pass == 0) grouped_gemm_lds_kernel<0, 128><<<grid, 256, 0, st>>>(args);
+        else grouped_gemm_lds_kernel<1, 128><<<grid, 256, 0, st>>>(args);
+    } else if (variant == kGemmHugeLds) {
+        if (pass == 0) grouped_gemm_lds_kernel<0, 256><<<grid, 256, 0, st>>>(args);
+        else grouped_gemm_lds_kernel<1, 256><<<grid, 256, 0, st>>>(args);
     } else {
         if (pass == 0) grouped_gemm_kernel<TMOE_LARGE_GU><<<grid, 256, 0, st>>>(args);
         else grouped_gemm_kernel<TMOE_LARGE_DN><<<grid, 256, 0, st>>>(args);

@@ -12,7 +12,14 @@ constexpr int kMaxTopK = 32;
 constexpr int kMaxExperts = 1024;
 
 // --- routing (route.hip) ---
-bool route_fused_ok(int dtype, int H, int E);
+struct TileSpec;
+// Small batches: one block groups the routing from the router's masks (counts,
+// offsets, tile lists, row_token / row_of / row_dst / row_scale).
+bool group_small_ok(int64_t T, int E);
+hipError_t launch_group_small(const int32_t* idx, const float* w, const uint16_t* masks, int64_t T, int E, int k,
+                              int32_t* counts, int32_t* offsets, int32_t* row_token, int32_t* row_of,
+                              int32_t* row_dst, float* row_scale, int slots, const TileSpec* t1, const TileSpec* t2,
+                              hipStream_t st);
 // masks (nullable): [E][mask_stride(T)] uint16, bit t % 16 of word t / 16 set when token t routes to e
 hipError_t launch_route(int dtype, const void* x, const void* W, const float* bias, int64_t T, int H, int E, int k,
                         int norm, int32_t* idx, float* w, float* probs, float* scratch_sc, float* scratch_bd,
@@ -66,9 +73,10 @@ struct GemmArgs {
     const int* count;
     int E;
 };
-enum GemmVariant { kGemmSmallM = 0, kGemmLargeM = 1 };
+enum GemmVariant { kGemmSmallM = 0, kGemmLargeM = 1, kGemmLargeLds = 2, kGemmHugeLds = 3 };
 void gemm_tiles(int variant, int pass, int* mt, int* nt);
 bool gemm_mfma_ok(int dtype, int H, int I, int Is);
+bool gemm_lds_ok(int H, int I, int Is);  // shapes of the 128 x 256 direct-to-LDS tiles
 hipError_t launch_grouped_gemm(int dtype, int variant, int pass, const GemmArgs& args, int64_t max_items,
                                hipStream_t st);
 // Portable path: one thread per output; rows of group 0 find their expert in offsets.

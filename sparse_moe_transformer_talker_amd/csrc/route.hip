@@ -16,11 +16,10 @@
 // products are exact in fp64) and selected again.  The result is the Top-k of
 // the exact scores with ties to the lower index.
 //
-// The router also writes, per block of 16 tokens, a 16-bit mask per expert of
-// which tokens chose it; the grouping kernels derive the stable per-expert
-// order from these masks.
-#include "common.hpp"
-#include "kernels.hpp"
+// Selection also records, per expert and block of 16 tokens, a 16-bit mask of
+// the tokens that chose the expert; grouping derives the stable per-expert
+// row order from these masks.
+#include "grouping.hpp"
 
 namespace tmoe {
 
@@ -30,22 +29,24 @@ __device__ __forceinline__ double partial_error_scale() { return 33.0 * 1.192092
 __device__ __forceinline__ double fp64_error_scale(int H) { return (double)(H / 32 + 8) * 2.220446049250313e-16; }
 
 // ---------------------------------------------------------------------------
-// fp64 rescoring of up to 4 candidates at once: dot(x_row, W[e_i]) over H,
-// wave-cooperative, 16-byte loads issued for all candidates before use.
-template <typename T>
-__device__ void wave_dot64_x4(const T* __restrict__ xr, const T* __restrict__ W, int H, const int* e, int n,
-                              double* out) {
-    double acc[4] = {0.0, 0.0, 0.0, 0.0};
+// fp64 rescoring of up to N candidates at once: dot(x_row, W[e_i]) over H,
+// wave-cooperative, all 16-byte loads of a chunk issued before use.
+template <typename T, int N>
+__device__ void wave_dot64(const T* __restrict__ xr, const T* __restrict__ W, int H, const int* e, int n,
+                           double* out) {
+    double acc[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) acc[i] = 0.0;
     constexpr int V = 16 / sizeof(T);  // elements per 16-byte chunk
     if (H % V == 0) {
         for (int c = lane_id(); c < H / V; c += kWave) {
             const u32x4 xv = *reinterpret_cast<const u32x4*>(xr + c * V);
-            u32x4 wv[4];
+            u32x4 wv[N];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < N; ++i)
                 if (i < n) wv[i] = *reinterpret_cast<const u32x4*>(W + (int64_t)e[i] * H + c * V);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < N; ++i) {
                 if (i >= n) continue;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
@@ -64,12 +65,12 @@ __device__ void wave_dot64_x4(const T* __restrict__ xr, const T* __restrict__ W,
         for (int h = lane_id(); h < H; h += kWave) {
             const double xv = Elem<T>::load64(xr, h);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < N; ++i)
                 if (i < n) acc[i] = fma(xv, Elem<T>::load64(W + (int64_t)e[i] * H, h), acc[i]);
         }
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) out[i] = wave_sum(acc[i]);
+    for (int i = 0; i < N; ++i) out[i] = wave_sum(acc[i]);
 }
 
 // Per-wave selection state in LDS.
@@ -78,14 +79,13 @@ struct SelScratch {
     double score[kMaxTopK];
 };
 
-// Exact Top-k of one row of scores s[0..n) (fp32 or fp64) with error bounds
-// d[0..n); writes idx / weights / probs and, when mask != nullptr, ORs bit
-// `bit` into mask[e] for every selected e (LDS).  Called by one full wave;
-// lanes own entries e = lane + 64 j.
+// Exact Top-k of one row of scores s[0..n) with error bounds d[0..n); writes
+// idx / weights / probs and ORs bit `bit` into mask[e * mstride] for every
+// selected e (LDS).  Called by one full wave; lanes own entries e = lane + 64 j.
 template <typename T, int MAXJ, typename S>
-__device__ void exact_select_row(const S* s, const float* d, int n, int k, const T* xrow, const T* W, int H,
+__device__ __noinline__ void exact_select_row(const S* s, const float* d, int n, int k, const T* xrow, const T* W, int H,
                                  const float* bias, SelScratch* sc, int norm, int32_t* out_idx, float* out_w,
-                                 float* out_probs, uint32_t* mask, int bit) {
+                                 float* out_probs, uint32_t* mask, int mstride, int bit) {
     const int lane = lane_id();
     float v[MAXJ];
     double dv[MAXJ];
@@ -130,7 +130,8 @@ __device__ void exact_select_row(const S* s, const float* d, int n, int k, const
     if (__ballot(threat) != 0ull) certain = false;
 
     if (!certain) {
-        // Candidates: the selected ones and every other one that may reach them.
+        // Candidates: the selected ones and every other one that may reach them,
+        // rescored eight at a time.
         bool cand[MAXJ];
         double v64[MAXJ];
 #pragma unroll
@@ -143,35 +144,44 @@ __device__ void exact_select_row(const S* s, const float* d, int n, int k, const
         for (int j = 0; j < MAXJ; ++j) {
             uint64_t m = __ballot(cand[j]);
             while (m) {
-                int ids[4], cnt = 0;
-                while (m && cnt < 4) {
+                int ids[8], cnt = 0;
+                while (m && cnt < 8) {
                     ids[cnt++] = (__ffsll((unsigned long long)m) - 1) + kWave * j;
                     m &= m - 1;
                 }
-                double r4[4];
-                wave_dot64_x4(xrow, W, H, ids, cnt, r4);
+                double r8[8];
+                wave_dot64<T, 8>(xrow, W, H, ids, cnt, r8);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    if (i < cnt) {
-                        const double sc64 = r4[i] + (bias ? (double)bias[ids[i]] : 0.0);
-                        if (lane == ids[i] - kWave * j) v64[j] = sc64;
-                    }
+                for (int i = 0; i < 8; ++i) {
+                    if (i < cnt && lane == ids[i] - kWave * j)
+                        v64[j] = r8[i] + (bias ? (double)bias[ids[i]] : 0.0);
                 }
             }
         }
+        // fp64 selection among the candidates: largest value, then lowest index
         for (int r = 0; r < k; ++r) {
-            double bv = 0.0;
-            int bi = -1;
+            uint64_t key = 0;
 #pragma unroll
             for (int j = 0; j < MAXJ; ++j) {
-                const int e = lane + kWave * j;
-                if (cand[j] && (bi < 0 || ranks_before(v64[j], e, bv, bi))) { bv = v64[j]; bi = e; }
+                if (!cand[j]) continue;
+                const uint64_t kk = double_order_key(v64[j]);
+                key = kk > key ? kk : key;
             }
-            wave_best(bv, bi);
+            const uint64_t kmax = wave_max_key(key);
+            uint64_t ik = 0;
+#pragma unroll
+            for (int j = 0; j < MAXJ; ++j) {
+                if (cand[j] && double_order_key(v64[j]) == kmax) {
+                    const uint64_t c = 0xFFFFFFFFull - (uint64_t)(lane + kWave * j);
+                    ik = c > ik ? c : ik;
+                }
+            }
+            ik = wave_max_key(ik);
+            const int bi = (int)(0xFFFFFFFFull - ik);
 #pragma unroll
             for (int j = 0; j < MAXJ; ++j)
                 if (lane + kWave * j == bi) cand[j] = false;
-            if (lane == 0) { sc->idx[r] = bi; sc->score[r] = bv; }
+            if (lane == 0) { sc->idx[r] = bi; sc->score[r] = double_from_order_key(kmax); }
         }
     }
     __builtin_amdgcn_wave_barrier();
@@ -210,122 +220,322 @@ __device__ void exact_select_row(const S* s, const float* d, int n, int k, const
     if (lane < k) {
         out_idx[lane] = my_e;
         out_w[lane] = ex / den;
-        if (mask) atomicOr(&mask[my_e], 1u << bit);
+        if (mask) atomicOr(&mask[my_e * mstride], 1u << bit);
     }
 }
 
 // ---------------------------------------------------------------------------
-// Matrix-core scores for 16 tokens x (NS*16) weight rows.  The NW waves of the
-// block take the 32-wide K steps round robin (any H % 32 == 0); each step is
-// a fresh fp32 partial added into fp64.  Partials of the waves are reduced into
-// LDS in fixed wave order (deterministic).  Rows/tokens beyond the limits are
-// clamped on load and their outputs are never read.
-template <int NS, int NW>
-__device__ void mfma_scores_tile(const bf16_t* __restrict__ x, int64_t T, int H, int64_t tok0,
-                                 const bf16_t* __restrict__ W, int nrows, int e0, double* lg, float* ab, int ld) {
+// Row-group selection for n <= 16 * J <= 128 and k <= 16: each 16-lane row of
+// a wave selects for its own token (lane ri holds entries ri + 16 j), with DPP
+// rotations as the row all-reductions, so the four tokens of a wave advance
+// together.  Rows whose fp32 selection is not certain are redone afterwards by
+// the whole wave (exact_select_row).  The mask of expert e for token t is
+// mask[e * mstride + word], bit t % 16.  t < 0 marks an empty row.
+struct RowPicks {
+    float v[4][16];
+    double d[4][16];
+    int idx[4][16];
+};
+
+// Scores of token t are sc[(t - tbase) * n + e] (fp32 in global memory or fp64 in LDS).
+template <typename T, int J, typename S>
+__device__ __forceinline__ void select_rows_wave(const S* __restrict__ sc, const float* __restrict__ bd, int64_t tbase, int64_t t, int n, int k,
+                                 const T* __restrict__ x, const T* __restrict__ W, int H, const float* bias, int norm,
+                                 int32_t* out_idx, float* out_w, float* out_probs, uint32_t* mask, int mstride,
+                                 int word_of_row0, RowPicks& pk, SelScratch* scr) {
+    const int lane = lane_id();
+    const int row = lane >> 4, ri = lane & 15;
+    const bool valid = t >= 0;
+    float v[J];
+    double dv[J];
+    uint64_t key[J];  // rank keys (unique: they carry the index); 0 once picked or absent
+    int pick[J];      // round in which the entry was picked, -1 if not
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        const int e = ri + 16 * j;
+        const bool ok = valid && e < n;
+        v[j] = ok ? (float)sc[(t - tbase) * n + e] + 0.0f : 0.0f;
+        dv[j] = ok ? (double)bd[(t - tbase) * n + e] + 1.1920928955078125e-07 * fabs((double)v[j]) : 0.0;
+        key[j] = ok ? rank_key(v[j], e) : 0ull;
+        pick[j] = -1;
+    }
+    for (int r = 0; r < k; ++r) {
+        uint64_t m = 0;
+#pragma unroll
+        for (int j = 0; j < J; ++j) m = key[j] > m ? key[j] : m;
+        m = row_max_key(m);
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const bool hit = key[j] == m && m != 0;
+            pick[j] = hit ? r : pick[j];
+            key[j] = hit ? 0ull : key[j];
+        }
+    }
+    bool taken[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        taken[j] = !(valid && ri + 16 * j < n) || pick[j] >= 0;
+        if (pick[j] >= 0) {
+            pk.v[row][pick[j]] = v[j];
+            pk.d[row][pick[j]] = dv[j];
+            pk.idx[row][pick[j]] = ri + 16 * j;
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+    // certain: consecutive picks strictly separated, and nothing else can reach the lowest pick
+    bool bad = false;
+    double lo = 1.0e300;
+    if (valid && ri < k) {
+        lo = (double)pk.v[row][ri] - pk.d[row][ri];
+        if (ri > 0) {
+            const double prev_lo = (double)pk.v[row][ri - 1] - pk.d[row][ri - 1];
+            bad = !(prev_lo > (double)pk.v[row][ri] + pk.d[row][ri]);
+        }
+    }
+    const double low = row_min(lo);
+#pragma unroll
+    for (int j = 0; j < J; ++j)
+        if (!taken[j] && (double)v[j] + dv[j] >= low) bad = true;
+    const uint64_t badmask = __ballot(valid && bad);
+    const bool certain = ((badmask >> (16 * row)) & 0xFFFFull) == 0;
+    if (valid && certain) {
+        float mx = -3.0e38f;
+#pragma unroll
+        for (int j = 0; j < J; ++j)
+            if (ri + 16 * j < n) mx = fmaxf(mx, v[j]);
+        mx = row_max(mx);
+        float z = 0.f;
+        if (out_probs || !norm) {
+#pragma unroll
+            for (int j = 0; j < J; ++j)
+                if (ri + 16 * j < n) z += __expf(v[j] - mx);
+            z = row_sum(z);
+        }
+        if (out_probs) {
+            const float inv = 1.0f / z;
+#pragma unroll
+            for (int j = 0; j < J; ++j)
+                if (ri + 16 * j < n) out_probs[t * n + ri + 16 * j] = __expf(v[j] - mx) * inv;
+        }
+        float ex = 0.f;
+        if (ri < k) ex = norm ? __expf(pk.v[row][ri] - pk.v[row][0]) : __expf(pk.v[row][ri] - mx);
+        const float den = norm ? row_sum(ex) : z;
+        if (ri < k) {
+            const int e = pk.idx[row][ri];
+            out_idx[t * k + ri] = e;
+            out_w[t * k + ri] = ex / den;
+            atomicOr(&mask[e * mstride + word_of_row0], 1u << (t & 15));
+        }
+    }
+    // rows left uncertain: the whole wave redoes them with fp64 rescoring
+    uint64_t redo = __ballot(valid && !certain && ri == 0);
+    while (redo) {
+        const int g = (__ffsll((unsigned long long)redo) - 1) >> 4;
+        redo &= redo - 1;
+        const int64_t tg = __shfl(t, g * 16, kWave);
+        exact_select_row<T, (16 * J + 63) / 64, S>(sc + (tg - tbase) * n, bd + (tg - tbase) * n, n, k, x + tg * H, W, H, bias, scr, norm,
+                                                out_idx + tg * k, out_w + tg * k,
+                                                out_probs ? out_probs + tg * n : nullptr, mask + word_of_row0,
+                                                mstride, (int)(tg & 15));
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Matrix-core scores to global [T, n] (bf16, H % 32 == 0): a block computes
+// 16 tokens x 32 weight rows.  Its 8 waves take the 32-wide K steps round
+// robin, with the loads of up to 4 steps issued together; every step is a
+// fresh fp32 partial added into fp64.  Partials of the waves are reduced in
+// LDS in fixed wave order (deterministic).  Splitting the rows over blocks
+// spreads the router's bytes over many CUs even for a few tokens.
+constexpr int kScoreWaves = 8;
+constexpr int kScoreRows = 32;
+
+__global__ __launch_bounds__(64 * kScoreWaves) void scores_kernel(const bf16_t* __restrict__ x,
+                                                                  const bf16_t* __restrict__ W,
+                                                                  const float* __restrict__ bias, int64_t T, int H,
+                                                                  int n, float* __restrict__ sc,
+                                                                  float* __restrict__ bd) {
+    __shared__ double lg[16 * kScoreRows];
+    __shared__ float ab[16 * kScoreRows];
     const int wave = threadIdx.x >> 6;
     const int lane = lane_id();
     const int i = lane & 15;
     const int kq = (lane >> 4) * 8;
-    double acc[NS][4];
-    f32x4 aacc[NS];
+    const int64_t tok0 = (int64_t)blockIdx.x * 16;
+    const int e0 = blockIdx.y * kScoreRows;
+    int64_t tok = tok0 + i;
+    if (tok >= T) tok = T - 1;
+    int r0 = e0 + i, r1 = e0 + 16 + i;
+    if (r0 >= n) r0 = n - 1;
+    if (r1 >= n) r1 = n - 1;
+    const bf16_t* xp = x + tok * (int64_t)H + kq;
+    const bf16_t* w0 = W + (int64_t)r0 * H + kq;
+    const bf16_t* w1 = W + (int64_t)r1 * H + kq;
+    const u32x4 absmask = {0x7FFF7FFFu, 0x7FFF7FFFu, 0x7FFF7FFFu, 0x7FFF7FFFu};
+    const f32x4 zero = {0, 0, 0, 0};
+    double acc0[4] = {0, 0, 0, 0}, acc1[4] = {0, 0, 0, 0};
+    f32x4 aa0 = zero, aa1 = zero;
+    const int nsteps = H / 32;
+    for (int c0 = wave; c0 < nsteps; c0 += 4 * kScoreWaves) {
+        u32x4 a[4], b0[4], b1[4];
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-        aacc[s] = f32x4{0, 0, 0, 0};
+        for (int u = 0; u < 4; ++u) {
+            const int st = c0 + u * kScoreWaves;
+            if (st < nsteps) {
+                a[u] = *reinterpret_cast<const u32x4*>(xp + st * 32);
+                b0[u] = *reinterpret_cast<const u32x4*>(w0 + st * 32);
+                b1[u] = *reinterpret_cast<const u32x4*>(w1 + st * 32);
+            }
+        }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[s][r] = 0.0;
+        for (int u = 0; u < 4; ++u) {
+            if (c0 + u * kScoreWaves >= nsteps) continue;
+            const bf16x8 av = __builtin_bit_cast(bf16x8, a[u]);
+            const bf16x8 aav = __builtin_bit_cast(bf16x8, a[u] & absmask);
+            const f32x4 p0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, b0[u]), zero, 0, 0, 0);
+            const f32x4 p1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, b1[u]), zero, 0, 0, 0);
+            aa0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aav, __builtin_bit_cast(bf16x8, b0[u] & absmask), aa0, 0, 0, 0);
+            aa1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aav, __builtin_bit_cast(bf16x8, b1[u] & absmask), aa1, 0, 0, 0);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                acc0[r] += (double)p0[r];
+                acc1[r] += (double)p1[r];
+            }
+        }
     }
+    // D[row = 4*(lane/16) + r][col = lane%16] per 16x16 block
+    for (int w = 0; w < kScoreWaves; ++w) {
+        if (wave == w) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int q = ((lane >> 4) * 4 + r) * kScoreRows + i;
+                if (w == 0) {
+                    lg[q] = acc0[r]; ab[q] = aa0[r];
+                    lg[q + 16] = acc1[r]; ab[q + 16] = aa1[r];
+                } else {
+                    lg[q] += acc0[r]; ab[q] += aa0[r];
+                    lg[q + 16] += acc1[r]; ab[q + 16] += aa1[r];
+                }
+            }
+        }
+        __syncthreads();
+    }
+    const double es = partial_error_scale(), fs = fp64_error_scale(H);
+    for (int q = threadIdx.x; q < 16 * kScoreRows; q += blockDim.x) {
+        const int row = q / kScoreRows, col = q % kScoreRows;
+        const int64_t t = tok0 + row;
+        const int e = e0 + col;
+        if (t >= T || e >= n) continue;
+        const float b = bias ? bias[e] : 0.f;
+        const double sv = lg[q] + (double)b;
+        const double a = (double)ab[q];
+        sc[t * n + e] = (float)sv;
+        bd[t * n + e] = (float)(es * a + fs * (a + fabs((double)b)) + 0.5 * 1.1920928955078125e-07 * fabs(sv)) *
+                        (1.0f + kTwoM23);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Fused router for bf16, E = NS * 16 in {16, 32, 64, 128}, H % 32 == 0: one block of 16
+// waves per 16 tokens scores all experts and selects, so the scores never
+// leave LDS.  Waves are split into KG K-groups x EG expert groups (each wave
+// two 16-expert subtiles when NS >= 2); a wave issues the loads of up to 4 of
+// its 32-wide K steps at once and adds every step's fp32 partial into fp64.
+// K-groups are reduced in LDS in fixed order.  Waves 0..3 then select four
+// tokens each (row groups) and the block writes its mask word of every expert.
+constexpr int kFusedWaves = 16;
+
+template <int NS>
+__global__ __launch_bounds__(64 * kFusedWaves) void route_fused_kernel(
+    const bf16_t* __restrict__ x, const bf16_t* __restrict__ W, const float* __restrict__ bias, int64_t T, int H,
+    int E, int k, int norm, int32_t* __restrict__ out_idx, float* __restrict__ out_w, float* __restrict__ out_probs,
+    uint16_t* __restrict__ masks, int mstride) {
+    constexpr int LD = NS * 16;
+    constexpr int SPW = NS >= 2 ? 2 : 1;  // 16-expert subtiles per wave
+    constexpr int EG = NS / SPW;          // expert groups
+    constexpr int KG = kFusedWaves / EG;  // K groups
+    __shared__ double lg[16 * LD];
+    __shared__ float ab[16 * LD];
+    __shared__ RowPicks picks[4];
+    __shared__ SelScratch scr[4];
+    __shared__ uint32_t msk[LD];
+    const int wave = threadIdx.x >> 6, lane = lane_id();
+    const int kg = wave % KG, eg = wave / KG;
+    const int i = lane & 15, kq = (lane >> 4) * 8;
+    const int64_t tok0 = (int64_t)blockIdx.x * 16;
+    for (int q = threadIdx.x; q < LD; q += blockDim.x) msk[q] = 0;
     int64_t tok = tok0 + i;
     if (tok >= T) tok = T - 1;
     const bf16_t* xp = x + tok * (int64_t)H + kq;
-    const bf16_t* wp[NS];
+    const bf16_t* wp[SPW];
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-        int r = e0 + s * 16 + i;
-        if (r >= nrows) r = nrows - 1;
-        wp[s] = W + (int64_t)r * H + kq;
-    }
-    const int nsteps = H / 32;
+    for (int s = 0; s < SPW; ++s) wp[s] = W + (int64_t)((eg * SPW + s) * 16 + i) * H + kq;
     const u32x4 absmask = {0x7FFF7FFFu, 0x7FFF7FFFu, 0x7FFF7FFFu, 0x7FFF7FFFu};
     const f32x4 zero = {0, 0, 0, 0};
-    if (wave < nsteps) {
-        // software pipeline: the next step's operands load while this step computes
-        u32x4 a = *reinterpret_cast<const u32x4*>(xp + wave * 32);
-        u32x4 b[NS];
+    double acc[SPW][4];
+    f32x4 aacc[SPW];
 #pragma unroll
-        for (int s = 0; s < NS; ++s) b[s] = *reinterpret_cast<const u32x4*>(wp[s] + wave * 32);
-        for (int st = wave; st < nsteps; st += NW) {
-            const int kn = (st + NW < nsteps ? st + NW : st) * 32;
-            const u32x4 an = *reinterpret_cast<const u32x4*>(xp + kn);
-            u32x4 bn[NS];
+    for (int s = 0; s < SPW; ++s) {
+        aacc[s] = zero;
 #pragma unroll
-            for (int s = 0; s < NS; ++s) bn[s] = *reinterpret_cast<const u32x4*>(wp[s] + kn);
-            const u32x4 aa = a & absmask;
+        for (int r = 0; r < 4; ++r) acc[s][r] = 0.0;
+    }
+    const int nsteps = H / 32;
+    for (int c0 = kg; c0 < nsteps; c0 += 4 * KG) {
+        u32x4 a[4], b[4][SPW];
 #pragma unroll
-            for (int s = 0; s < NS; ++s) {
-                const f32x4 p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b[s]), zero, 0, 0, 0);
-                aacc[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, aa),
-                                                                  __builtin_bit_cast(bf16x8, b[s] & absmask),
+        for (int u = 0; u < 4; ++u) {
+            const int st = c0 + u * KG;
+            if (st < nsteps) {
+                a[u] = *reinterpret_cast<const u32x4*>(xp + st * 32);
+#pragma unroll
+                for (int s = 0; s < SPW; ++s) b[u][s] = *reinterpret_cast<const u32x4*>(wp[s] + st * 32);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if (c0 + u * KG >= nsteps) continue;
+            const bf16x8 av = __builtin_bit_cast(bf16x8, a[u]);
+            const bf16x8 aav = __builtin_bit_cast(bf16x8, a[u] & absmask);
+#pragma unroll
+            for (int s = 0; s < SPW; ++s) {
+                const f32x4 p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, b[u][s]), zero,
+                                                                        0, 0, 0);
+                aacc[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aav, __builtin_bit_cast(bf16x8, b[u][s] & absmask),
                                                                   aacc[s], 0, 0, 0);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) acc[s][r] += (double)p[r];
             }
-            a = an;
-#pragma unroll
-            for (int s = 0; s < NS; ++s) b[s] = bn[s];
         }
     }
-    // D[row = 4*(lane/16) + r][col = lane%16] per 16x16 block
-    for (int w = 0; w < NW; ++w) {
-        if (wave == w) {
+    // D[row = 4*(lane/16) + r][col = lane%16] per 16x16 block; K-groups in order
+    for (int g = 0; g < KG; ++g) {
+        if (kg == g) {
 #pragma unroll
-            for (int s = 0; s < NS; ++s)
+            for (int s = 0; s < SPW; ++s)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int q = ((lane >> 4) * 4 + r) * ld + s * 16 + i;
-                    if (w == 0) { lg[q] = acc[s][r]; ab[q] = aacc[s][r]; }
+                    const int q = ((lane >> 4) * 4 + r) * LD + (eg * SPW + s) * 16 + i;
+                    if (g == 0) { lg[q] = acc[s][r]; ab[q] = aacc[s][r]; }
                     else { lg[q] += acc[s][r]; ab[q] += aacc[s][r]; }
                 }
         }
         __syncthreads();
     }
-}
-
-constexpr int kRouteWaves = 8;
-
-// Fused route for bf16, E <= NS*16 <= 128, H % 32 == 0: 16 tokens per block.
-// masks (nullable): [E][mstride] uint16, word = blockIdx.x, bit = token % 16.
-template <int NS>
-__global__ __launch_bounds__(64 * kRouteWaves) void route_mfma_kernel(
-    const bf16_t* __restrict__ x, const bf16_t* __restrict__ W, const float* __restrict__ bias, int64_t T, int H,
-    int E, int k, int norm, int32_t* __restrict__ out_idx, float* __restrict__ out_w, float* __restrict__ out_probs,
-    uint16_t* __restrict__ masks, int mstride) {
-    constexpr int LD = NS * 16;
-    __shared__ double lg[16 * LD];
-    __shared__ float ab[16 * LD];
-    __shared__ SelScratch sc[kRouteWaves];
-    __shared__ uint32_t msk[LD];
-    const int64_t tok0 = (int64_t)blockIdx.x * 16;
-    for (int q = threadIdx.x; q < LD; q += blockDim.x) msk[q] = 0;
-    mfma_scores_tile<NS, kRouteWaves>(x, T, H, tok0, W, E, 0, lg, ab, LD);
     const double es = partial_error_scale(), fs = fp64_error_scale(H);
     for (int q = threadIdx.x; q < 16 * LD; q += blockDim.x) {
         const int e = q % LD;
-        const float b = (bias && e < E) ? bias[e] : 0.f;
+        const float b = bias ? bias[e] : 0.f;
         const double sv = lg[q] + (double)b;
         lg[q] = sv;
         const double a = (double)ab[q];
         ab[q] = (float)(es * a + fs * (a + fabs((double)b))) * (1.0f + kTwoM23);
     }
     __syncthreads();
-    const int wave = threadIdx.x >> 6;
-    for (int tt = wave; tt < 16; tt += kRouteWaves) {
-        const int64_t t = tok0 + tt;
-        if (t >= T) break;
-        exact_select_row<bf16_t, (LD + 63) / 64, double>(lg + tt * LD, ab + tt * LD, E, k, x + t * H, W, H, bias,
-                                                         &sc[wave], norm, out_idx + t * k, out_w + t * k,
-                                                         out_probs ? out_probs + t * E : nullptr, msk, tt);
+    if (wave < 4) {
+        const int64_t t = tok0 + wave * 4 + (lane >> 4);
+        select_rows_wave<bf16_t, NS, double>(lg, ab, tok0, t < T ? t : -1, E, k, x, W, H, bias, norm, out_idx, out_w,
+                                              out_probs, msk, 1, 0, picks[wave], &scr[wave]);
     }
     if (masks) {
         __syncthreads();
@@ -333,7 +543,6 @@ __global__ __launch_bounds__(64 * kRouteWaves) void route_mfma_kernel(
     }
 }
 
-// ---------------------------------------------------------------------------
 // Portable scores: one lane per weight row, 32-term fp32 partials added in
 // fp64; writes fp32 scores and bounds (including the final rounding to fp32)
 // to global [T, n].  Any H, any element type.
@@ -371,32 +580,32 @@ __global__ __launch_bounds__(256) void scores_generic_kernel(const T* __restrict
     bd[t * n + e] = (float)bound * (1.0f + kTwoM23);
 }
 
-// Matrix-core scores to global [T, n] (bf16, H % 32 == 0): 16 tokens x 128 rows per block.
-__global__ __launch_bounds__(64 * kRouteWaves) void scores_mfma_kernel(
-    const bf16_t* __restrict__ x, const bf16_t* __restrict__ W, const float* __restrict__ bias, int64_t T, int H,
-    int n, float* __restrict__ sc, float* __restrict__ bd) {
-    constexpr int NS = 8, LD = NS * 16;
-    __shared__ double lg[16 * LD];
-    __shared__ float ab[16 * LD];
-    const int64_t tok0 = (int64_t)blockIdx.y * 16;
-    const int e0 = blockIdx.x * LD;
-    mfma_scores_tile<NS, kRouteWaves>(x, T, H, tok0, W, n, e0, lg, ab, LD);
-    const double es = partial_error_scale(), fs = fp64_error_scale(H);
-    for (int q = threadIdx.x; q < 16 * LD; q += blockDim.x) {
-        const int row = q / LD, col = q % LD;
-        const int64_t t = tok0 + row;
-        const int e = e0 + col;
-        if (t >= T || e >= n) continue;
-        const float b = bias ? bias[e] : 0.f;
-        const double sv = lg[q] + (double)b;
-        const double a = (double)ab[q];
-        sc[t * n + e] = (float)sv;
-        bd[t * n + e] = (float)(es * a + fs * (a + fabs((double)b)) + 0.5 * 1.1920928955078125e-07 * fabs(sv)) *
-                        (1.0f + kTwoM23);
+// ---------------------------------------------------------------------------
+// Selection from global scores, 16 tokens per block (one mask word), with
+// masks [E][mstride] uint16 written when non-null.
+template <typename T, int J>
+__global__ __launch_bounds__(256) void select_rows_kernel(const float* __restrict__ sc, const float* __restrict__ bd,
+                                                          const T* __restrict__ x, const T* __restrict__ W,
+                                                          const float* __restrict__ bias, int64_t Ttok, int H,
+                                                          int n, int k, int norm, int32_t* __restrict__ out_idx,
+                                                          float* __restrict__ out_w, float* __restrict__ out_probs,
+                                                          uint16_t* __restrict__ masks, int mstride) {
+    __shared__ RowPicks picks[4];
+    __shared__ SelScratch scr[4];
+    __shared__ uint32_t msk[16 * J];
+    for (int q = threadIdx.x; q < 16 * J; q += blockDim.x) msk[q] = 0;
+    __syncthreads();
+    const int wave = threadIdx.x >> 6;
+    const int64_t t = (int64_t)blockIdx.x * 16 + wave * 4 + (lane_id() >> 4);
+    select_rows_wave<T, J, float>(sc, bd, 0, t < Ttok ? t : -1, n, k, x, W, H, bias, norm, out_idx, out_w, out_probs, msk, 1, 0,
+                           picks[wave], &scr[wave]);
+    if (masks) {
+        __syncthreads();
+        for (int e = threadIdx.x; e < n; e += blockDim.x) masks[(int64_t)e * mstride + blockIdx.x] = (uint16_t)msk[e];
     }
 }
 
-// Exact Top-k from global fp32 scores: 16 tokens per block, 4 per wave (n <= 1024).
+// Whole-wave selection (any n <= 1024, k <= 32): 16 tokens per block, 4 per wave.
 template <typename T, int MAXJ>
 __global__ __launch_bounds__(256) void select_topk_kernel(const float* __restrict__ sc, const float* __restrict__ bd,
                                                           const T* __restrict__ x, const T* __restrict__ W,
@@ -414,12 +623,71 @@ __global__ __launch_bounds__(256) void select_topk_kernel(const float* __restric
         const int64_t t = tok0 + tt;
         if (t >= Ttok) break;
         exact_select_row<T, MAXJ, float>(sc + t * n, bd + t * n, n, k, x + t * H, W, H, bias, &scr[wave], norm,
-                                         out_idx + t * k, out_w + t * k, out_probs ? out_probs + t * n : nullptr,
-                                         msk, tt);
+                                  out_idx + t * k, out_w + t * k, out_probs ? out_probs + t * n : nullptr, msk, 1, tt);
     }
     if (masks) {
         __syncthreads();
         for (int e = threadIdx.x; e < n; e += blockDim.x) masks[(int64_t)e * mstride + blockIdx.x] = (uint16_t)msk[e];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Small batches (T <= 256, E <= 128): one block groups the routing — per-expert
+// counts / offsets / prefixes of the token masks, GEMM tile lists, and the
+// scatter of (token, slot) pairs — with the masks and prefixes in LDS.
+constexpr int kSmallMaxT = 256;
+constexpr int kSmallWords = kSmallMaxT / 16;
+
+__global__ __launch_bounds__(1024) void group_small_kernel(const int32_t* __restrict__ idx,
+                                                           const float* __restrict__ wts,
+                                                           const uint16_t* __restrict__ masks, int mstride, int Ttok,
+                                                           int E, int k, int32_t* __restrict__ counts,
+                                                           int32_t* __restrict__ offsets,
+                                                           int32_t* __restrict__ row_token,
+                                                           int32_t* __restrict__ row_of, int32_t* __restrict__ row_dst,
+                                                           float* __restrict__ row_scale, int slots, TileSpecs specs) {
+    __shared__ uint32_t msk[128 * kSmallWords];
+    __shared__ int pre[128 * kSmallWords];
+    __shared__ int offs[128];
+    __shared__ int lds[17];
+    const int nw = (Ttok + 15) / 16;
+    for (int q = threadIdx.x; q < E * nw; q += blockDim.x) {
+        const int e = q / nw, w = q % nw;
+        msk[e * kSmallWords + w] = masks[(int64_t)e * mstride + w];
+    }
+    __syncthreads();
+    const int e = threadIdx.x;
+    int c = 0;
+    if (e < E) {
+        for (int w = 0; w < nw; ++w) {
+            pre[e * kSmallWords + w] = c;
+            c += __popc(msk[e * kSmallWords + w]);
+        }
+    }
+    int total;
+    const int excl = block_exclusive_scan(e < E ? c : 0, lds, &total);
+    if (e < E) {
+        offs[e] = excl;
+        counts[e] = c;
+        offsets[e] = excl;
+    }
+    if (e == 0) offsets[E] = total;
+    for (int s = 0; s < specs.n; ++s) block_build_items(c, excl, E, Ttok, specs.t[s], lds);
+    __syncthreads();
+    const int N = Ttok * k;
+    for (int i = threadIdx.x; i < N; i += blockDim.x) {
+        const int ee = idx[i];
+        if (ee < 0 || ee >= E) continue;
+        const int t = i / k, j = i % k;
+        const int m = ee * kSmallWords + (t >> 4);
+        const int dst = offs[ee] + pre[m] + __popc(msk[m] & ((1u << (t & 15)) - 1u));
+        if (dst < 0 || dst >= N) continue;
+        row_token[dst] = t;
+        row_of[i] = dst;
+        if (row_dst) {
+            row_dst[dst] = t * slots + j;
+            row_scale[dst] = wts[i];
+        }
     }
 }
 
@@ -444,7 +712,7 @@ __global__ __launch_bounds__(256) void argmax_exact_kernel(const float* __restri
     }
     key = wave_max_key(key);
     int bi = rank_key_index(key);
-    for (int o = 32; o > 0; o >>= 1) low = fmax(low, __shfl_xor(low, o, kWave));
+    low = double_from_order_key(wave_max_key(double_order_key(low)));
     int ncand = 0;
     for (int e = lane; e < n; e += kWave) ncand += ((double)s[e] + (double)d[e] >= low) ? 1 : 0;
     ncand = __builtin_amdgcn_readlane(wave_incl_scan(ncand), 63);
@@ -457,15 +725,15 @@ __global__ __launch_bounds__(256) void argmax_exact_kernel(const float* __restri
             const bool c = e < n && (double)s[e] + (double)d[e] >= low;
             uint64_t m = __ballot(c);
             while (m) {
-                int ids[4], cnt = 0;
-                while (m && cnt < 4) {
+                int ids[8], cnt = 0;
+                while (m && cnt < 8) {
                     ids[cnt++] = base + __ffsll((unsigned long long)m) - 1;
                     m &= m - 1;
                 }
-                double r4[4];
-                wave_dot64_x4(xr, W, H, ids, cnt, r4);
+                double r8[8];
+                wave_dot64<T, 8>(xr, W, H, ids, cnt, r8);
                 for (int i = 0; i < cnt; ++i)
-                    if (besti < 0 || ranks_before(r4[i], ids[i], best, besti)) { best = r4[i]; besti = ids[i]; }
+                    if (besti < 0 || ranks_before(r8[i], ids[i], best, besti)) { best = r8[i]; besti = ids[i]; }
             }
         }
         bi = besti;
@@ -480,6 +748,17 @@ static hipError_t launch_select(const float* sc, const float* bd, const T* x, co
                                 int64_t Ttok, int H, int n, int k, int norm, int32_t* idx, float* w, float* probs,
                                 uint16_t* masks, int mstride, hipStream_t st) {
     dim3 grid((unsigned)((Ttok + 15) / 16));
+    if (n <= 128 && k <= 16) {
+#define TMOE_ROWS(J)                                                                                     \
+    select_rows_kernel<T, J><<<grid, 256, 0, st>>>(sc, bd, x, W, bias, Ttok, H, n, k, norm, idx, w, probs, \
+                                                   masks, mstride)
+        if (n <= 16) TMOE_ROWS(1);
+        else if (n <= 32) TMOE_ROWS(2);
+        else if (n <= 64) TMOE_ROWS(4);
+        else TMOE_ROWS(8);
+#undef TMOE_ROWS
+        return hipGetLastError();
+    }
 #define TMOE_SEL(J)                                                                                      \
     select_topk_kernel<T, J><<<grid, 256, 0, st>>>(sc, bd, x, W, bias, Ttok, H, n, k, norm, idx, w, probs, \
                                                    masks, mstride)
@@ -492,14 +771,12 @@ static hipError_t launch_select(const float* sc, const float* bd, const T* x, co
     return hipGetLastError();
 }
 
-static bool mfma_scores_ok(int dtype, int H) { return dtype == kBF16 && H % 32 == 0; }
-
 hipError_t launch_scores(int dtype, const void* x, const void* W, const float* bias, int64_t Ttok, int H, int n,
                          float* sc, float* bd, hipStream_t st) {
-    if (mfma_scores_ok(dtype, H)) {
-        dim3 grid((unsigned)((n + 127) / 128), (unsigned)((Ttok + 15) / 16));
-        scores_mfma_kernel<<<grid, 64 * kRouteWaves, 0, st>>>((const bf16_t*)x, (const bf16_t*)W, bias, Ttok, H, n,
-                                                              sc, bd);
+    if (dtype == kBF16 && H % 32 == 0) {
+        dim3 grid((unsigned)((Ttok + 15) / 16), (unsigned)((n + kScoreRows - 1) / kScoreRows));
+        scores_kernel<<<grid, 64 * kScoreWaves, 0, st>>>((const bf16_t*)x, (const bf16_t*)W, bias, Ttok, H, n, sc,
+                                                         bd);
     } else {
         dim3 grid((unsigned)((n + 255) / 256), (unsigned)Ttok);
         if (dtype == kBF16)
@@ -512,25 +789,27 @@ hipError_t launch_scores(int dtype, const void* x, const void* W, const float* b
     return hipGetLastError();
 }
 
-bool route_fused_ok(int dtype, int H, int E) { return mfma_scores_ok(dtype, H) && E % 16 == 0 && E <= 128; }
+bool route_fused_ok(int dtype, int H, int E, int k) {
+    return dtype == kBF16 && H % 32 == 0 && (E == 16 || E == 32 || E == 64 || E == 128) && k <= 16;
+}
+bool group_small_ok(int64_t T, int E) { return T <= kSmallMaxT && E <= 128; }
 
 hipError_t launch_route(int dtype, const void* x, const void* W, const float* bias, int64_t Ttok, int H, int E,
                         int k, int norm, int32_t* idx, float* w, float* probs, float* scratch_sc,
                         float* scratch_bd, uint16_t* masks, hipStream_t st) {
     // one block per 16 tokens (one mask word); mask rows are mask_stride(T) words apart
     const int nwords = mask_words(Ttok), mstride = mask_stride(Ttok);
-    if (route_fused_ok(dtype, H, E)) {
-        dim3 grid((unsigned)nwords);
+    if (route_fused_ok(dtype, H, E, k)) {
         const bf16_t* xb = (const bf16_t*)x;
         const bf16_t* wb = (const bf16_t*)W;
-#define TMOE_ROUTE(NS)                                                                                       \
-    route_mfma_kernel<NS><<<grid, 64 * kRouteWaves, 0, st>>>(xb, wb, bias, Ttok, H, E, k, norm, idx, w, probs, \
-                                                             masks, mstride)
-        if (E <= 16) TMOE_ROUTE(1);
-        else if (E <= 32) TMOE_ROUTE(2);
-        else if (E <= 64) TMOE_ROUTE(4);
-        else TMOE_ROUTE(8);
-#undef TMOE_ROUTE
+#define TMOE_FUSED(NS)                                                                                          \
+    route_fused_kernel<NS><<<nwords, 64 * kFusedWaves, 0, st>>>(xb, wb, bias, Ttok, H, E, k, norm, idx, w, probs, \
+                                                                masks, mstride)
+        if (E == 16) TMOE_FUSED(1);
+        else if (E == 32) TMOE_FUSED(2);
+        else if (E == 64) TMOE_FUSED(4);
+        else TMOE_FUSED(8);
+#undef TMOE_FUSED
         return hipGetLastError();
     }
     hipError_t err = launch_scores(dtype, x, W, bias, Ttok, H, E, scratch_sc, scratch_bd, st);
@@ -540,6 +819,15 @@ hipError_t launch_route(int dtype, const void* x, const void* W, const float* bi
                                      norm, idx, w, probs, masks, mstride, st);
     return launch_select<float>(scratch_sc, scratch_bd, (const float*)x, (const float*)W, bias, Ttok, H, E, k, norm,
                                 idx, w, probs, masks, mstride, st);
+}
+
+hipError_t launch_group_small(const int32_t* idx, const float* w, const uint16_t* masks, int64_t Ttok, int E, int k,
+                              int32_t* counts, int32_t* offsets, int32_t* row_token, int32_t* row_of,
+                              int32_t* row_dst, float* row_scale, int slots, const TileSpec* t1, const TileSpec* t2,
+                              hipStream_t st) {
+    group_small_kernel<<<1, 1024, 0, st>>>(idx, w, masks, mask_stride(Ttok), (int)Ttok, E, k, counts, offsets,
+                                           row_token, row_of, row_dst, row_scale, slots, make_specs(t1, t2));
+    return hipGetLastError();
 }
 
 hipError_t launch_argmax(int dtype, const float* sc, const float* bd, const void* x, const void* W, int64_t Ttok,
