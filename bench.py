@@ -49,6 +49,27 @@ def layer_costs(shape, T, touched):
     return layer_bytes, layer_flops, gu_bytes, gu_flops
 
 
+def measured_traffic():
+    """HBM bytes per launch of the decode gate/up kernel, from the rocprofv3
+    FETCH_SIZE / WRITE_SIZE summary in profiles/, scaled by the copy-kernel
+    calibration stated there; None when that summary is missing or the kernel
+    source has changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "hbm_bytes_pmc.md")
+    try:
+        text = open(path).read()
+        rec = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
+    except (OSError, IndexError, ValueError):
+        return None
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "common.hpp"):
+        with open(os.path.join(ROOT, "sparse_moe_transformer_talker_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest() != rec.get("source_sha256"):
+        return None
+    return float(rec["traffic_bytes_per_launch"])
+
+
 def pct(a, q):
     return float(np.percentile(np.asarray(a), q)) if len(a) else None
 
@@ -102,7 +123,8 @@ def measure(api, torch, INP, shape, T, weight_sets, steps, warmup):
     eager_ms, _ = timed(lambda i: api.moe_layer_forward(cfg, structs[i % R], xs[i % R], y=ys[i % R], ws=ws))
 
     # the same steps with HIP events at every stage boundary, on the library's stream
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
+    # (events 6 and 7 are timestamped by the gate/up kernel's own launch)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(steps)]
     for row in evs:  # torch creates the HIP event on first record; the library re-records it
         for e in row:
             e.record()
@@ -113,11 +135,12 @@ def measure(api, torch, INP, shape, T, weight_sets, steps, warmup):
     names = ["route", "permute", "gate_up", "down", "combine"]
     stages = {n: [evs[i][j].elapsed_time(evs[i][j + 1]) * 1e3 for i in range(steps)] for j, n in enumerate(names)}
     step_us = [evs[i][0].elapsed_time(evs[i][5]) * 1e3 for i in range(steps)]
+    gu_kernel_us = [evs[i][6].elapsed_time(evs[i][7]) * 1e3 for i in range(steps)]
 
     mean_touched = float(np.mean([touched[i % R] for i in range(steps)]))
     lb, lf, gb, gf = layer_costs(shape, T, mean_touched)
     s = gpu_ms / 1e3 / steps
-    gu_s = float(np.mean(stages["gate_up"])) * 1e-6
+    gu_s = float(np.mean(gu_kernel_us)) * 1e-6
     return {
         "T": T, "steps": steps, "warmup": warmup, "weight_sets": R,
         "ms_per_step": gpu_ms / steps, "wall_ms_per_step": wall * 1e3 / steps,
@@ -128,7 +151,8 @@ def measure(api, torch, INP, shape, T, weight_sets, steps, warmup):
         "step_us": {"p50": pct(step_us, 50), "p95": pct(step_us, 95), "p99": pct(step_us, 99)},
         "stages_us_mean": {n: float(np.mean(v)) for n, v in stages.items()},
         "gate_up": {"bytes": gb, "flops": gf, "mean_us": gu_s * 1e6,
-                    "p50_us": pct(stages["gate_up"], 50), "p99_us": pct(stages["gate_up"], 99),
+                    "p50_us": pct(gu_kernel_us, 50), "p99_us": pct(gu_kernel_us, 99),
+                    "timing": "kernel start/end timestamps of its own launch (hipExtLaunchKernel events)",
                     "gbs": gb / gu_s / 1e9, "tflops": gf / gu_s / 1e12},
     }
 
@@ -203,10 +227,16 @@ def main():
         pre = measure(api, torch, INP, shape, 4096, sets, args.steps, args.warmup)
         log("prefill: %.2f us/step, %.2f M tok/s" % (pre["ms_per_step"] * 1e3, pre["tokens_per_s"] / 1e6))
     if args.copy_calibration_mb:
+        # one device-to-device copy of n bytes from a source evicted from the
+        # caches (a 2 GiB sweep after it was written), so the counters of that
+        # dispatch read n bytes from HBM and write n bytes
         n = args.copy_calibration_mb << 20
         src = torch.ones(n // 4, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
+        sweep = torch.empty(2 << 30, dtype=torch.uint8, device=dev)
+        sweep.fill_(1)
         torch.cuda.synchronize()
+        del sweep
         dst.copy_(src)
         torch.cuda.synchronize()
         log("calibration copy of %d MiB done" % args.copy_calibration_mb)
@@ -237,7 +267,7 @@ def main():
                    "shared_intermediate": shape.Is, "weight_sets_rotated": args.rotate},
         "roofline": {"bound": "hbm", "kernel": "grouped gate/up SwiGLU pass (routed + shared)",
                      "achieved": g["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": g["gbs"] / HBM_PEAK_GBS, "traffic": None,
+                     "frac": g["gbs"] / HBM_PEAK_GBS, "traffic": measured_traffic(),
                      "bytes_per_launch": g["bytes"], "mean_us": g["mean_us"]},
         "layer": {"hbm_frac": dec["layer_hbm_frac"], "bytes_per_step": dec["layer_bytes"],
                   "timing": "HIP graph replay per step; eager_ms_per_step without graphs",

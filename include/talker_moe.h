@@ -187,10 +187,12 @@ int moe_layer_forward(const moe_config* cfg, const moe_weights* w, const void* x
  * moe_layer_forward_timed — moe_layer_forward that also records HIP events at
  * its stage boundaries, for per-stage timing on the caller's stream (the
  * Talker MoE page's §4 profiling advice: pin numbers on the real workload and
- * keep percentiles).  stage_events is NULL or an array of 6 hipEvent_t, each
- * NULL or created by the caller; event i is recorded on `stream`:
+ * keep percentiles).  stage_events is NULL or an array of 8 hipEvent_t, each
+ * NULL or created by the caller; events 0-5 are recorded on `stream`:
  *   0 before routing, 1 after routing, 2 after grouping, 3 after the gate/up
- *   pass of all experts, 4 after the down pass, 5 after the combine.
+ *   pass of all experts, 4 after the down pass, 5 after the combine;
+ * events 6 and 7 are timestamped by the gate/up kernel's own launch at its
+ * start and end (hipExtLaunchKernel), so 6 -> 7 excludes dispatch latency.
  * Other arguments, results and errors are those of moe_layer_forward.
  */
 int moe_layer_forward_timed(const moe_config* cfg, const moe_weights* w, const void* x,

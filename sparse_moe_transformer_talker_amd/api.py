@@ -241,7 +241,8 @@ def moe_layer_forward(cfg: Config, weights, x: torch.Tensor, residual: Optional[
                       y=None, topk_idx=None, topk_w=None, counts=None, ws=None, stream=None, stage_events=None):
     """The whole MoE layer.  ``weights``: dict of device tensors or a prebuilt moe_weights.
     Returns y [T, H] (routing copies are written to the optional tensors).  With
-    ``stage_events`` (6 torch.cuda.Event or None) it calls moe_layer_forward_timed."""
+    ``stage_events`` (up to 8 torch.cuda.Event or None: six stage boundaries, then
+    the gate/up kernel's own start and end) it calls moe_layer_forward_timed."""
     T, dev = x.shape[0], x.device
     y = y if y is not None else torch.empty_like(x)
     ws_struct = weights if isinstance(weights, moe_weights) else weights_struct(weights)
@@ -253,7 +254,9 @@ def moe_layer_forward(cfg: Config, weights, x: torch.Tensor, residual: Optional[
     if stage_events is None:
         _check("moe_layer_forward", lib.moe_layer_forward(*args))
     else:
-        evs = (ctypes.c_void_p * 6)(*[None if e is None else e.cuda_event for e in stage_events])
+        if len(stage_events) > 8:
+            raise ValueError("at most 8 stage events")
+        evs = (ctypes.c_void_p * 8)(*[None if e is None else e.cuda_event for e in stage_events])
         _check("moe_layer_forward_timed", lib.moe_layer_forward_timed(*args, evs))
     return y
 

@@ -179,7 +179,8 @@ int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 // The two passes of the grouped SwiGLU experts over a plan's tile lists, or the
 // portable kernels.  g0 / g1 describe routed / shared work (g1.N == 0: none).
 int run_gemm_pass(const moe_config* c, const GemmPlan& plan, int pass, const GemmGroup& g0, const GemmGroup& g1,
-                  const int32_t* offsets, int64_t routed_rows, int64_t T, hipStream_t st) {
+                  const int32_t* offsets, int64_t routed_rows, int64_t T, hipStream_t st,
+                  hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr) {
     if (plan.mfma) {
         GemmArgs a{};
         a.g[0] = g0;
@@ -187,11 +188,13 @@ int run_gemm_pass(const moe_config* c, const GemmPlan& plan, int pass, const Gem
         a.items = plan.t[pass].items;
         a.count = plan.t[pass].count;
         a.E = routed_rows > 0 ? c->num_experts : 0;
-        TMOE_TRY(launch_grouped_gemm(c->dtype, plan.variant, pass, a, plan.max_items[pass], st));
+        TMOE_TRY(launch_grouped_gemm(c->dtype, plan.variant, pass, a, plan.max_items[pass], st, ev_start, ev_stop));
         return MOE_OK;
     }
+    if (ev_start) TMOE_TRY(hipEventRecord(ev_start, st));
     if (routed_rows > 0) TMOE_TRY(launch_gemm_generic(c->dtype, pass, g0, offsets, 0, c->num_experts, routed_rows, st));
     if (g1.N > 0 && T > 0) TMOE_TRY(launch_gemm_generic(c->dtype, pass, g1, nullptr, 0, 1, T, st));
+    if (ev_stop) TMOE_TRY(hipEventRecord(ev_stop, st));
     return MOE_OK;
 }
 
@@ -421,7 +424,8 @@ int moe_layer_forward_timed(const moe_config* cfg, const moe_weights* w, const v
     GemmGroup gu_s = Is > 0 ? group(w->shared_gate, w->shared_up, 0, Is, H, x, H, nullptr, p.hs, Is, nullptr, 1, 0,
                                     nullptr)
                             : no_group();
-    int r = run_gemm_pass(cfg, p.gemm, 0, gu_r, gu_s, p.offsets, N, T, s);
+    auto ev = [&](int i) { return stage_events ? static_cast<hipEvent_t>(stage_events[i]) : nullptr; };
+    int r = run_gemm_pass(cfg, p.gemm, 0, gu_r, gu_s, p.offsets, N, T, s, ev(6), ev(7));
     if (r != MOE_OK) return r;
     TMOE_TRY(mark(3));
     GemmGroup dn_r = group(w->down, nullptr, (int64_t)H * I, H, I, p.hr, I, nullptr, p.ybuf, H, p.row_dst, 1, 0,

@@ -19,6 +19,8 @@
 #include "common.hpp"
 #include "kernels.hpp"
 
+#include <hip/hip_ext.h>
+
 namespace tmoe {
 
 template <int PASS, int BM, int BN, int BK, int WM, int WN>
@@ -189,8 +191,10 @@ __device__ __forceinline__ int lds_chunk(int row, int c) { return (c + (row >> 2
 
 template <int N>
 __device__ __forceinline__ void wait_vm() {
-    // vmcnt <= N (N < 64); expcnt and lgkmcnt left at their maxima
-    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+    // vmcnt <= N (N < 64) and lgkmcnt == 0: this wave's loads of stage s have
+    // landed and its own LDS reads of earlier stages are done, so after the
+    // barrier that follows no wave still reads the buffer about to be refilled
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4));
 }
 }  // namespace lds_gemm
 
@@ -247,6 +251,17 @@ __global__ __launch_bounds__(256) void grouped_gemm_lds_kernel(GemmArgs args) {
         }
         pb[j] = w + (int64_t)e * g.w_estride + (int64_t)wrow * K + c * 8;
     }
+    // Destination row and scale of this lane's token in each of its MI token
+    // blocks, fetched now so the loads overlap the main loop.
+    int32_t dst_row[MI];
+    float row_sc[MI];
+#pragma unroll
+    for (int a = 0; a < MI; ++a) {
+        const int r = (wave >> 1) * (BM / 2) + a * 32 + (lane & 31);
+        const int64_t src = (int64_t)m0 + (r < mrows ? r : 0);
+        dst_row[a] = r < mrows ? (g.out_rows ? g.out_rows[src] : (int32_t)src) * g.out_mul + g.out_add : -1;
+        row_sc[a] = (PASS == 1 && g.out_scale) ? g.out_scale[src] : 1.0f;
+    }
     typedef __attribute__((address_space(3))) void lds_void;
     auto issue = [&](int stage, char* base) {
         const int k0 = stage * BK;
@@ -293,57 +308,69 @@ __global__ __launch_bounds__(256) void grouped_gemm_lds_kernel(GemmArgs args) {
             for (int a = 0; a < MI; ++a)
 #pragma unroll
                 for (int b = 0; b < 4; ++b)
-                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bfr[b], acc[a][b], 0, 0, 0);
+                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[b], af[a], acc[a][b], 0, 0, 0);
         }
     };
     // stage s: wait until its loads (all waves') have landed, refill the buffer
     // freed by stage s - 1 with stage s + 3, compute stage s
-    const int nst = K / BK;  // a multiple of 4
-    auto step = [&](int s, const char* cur, char* refill) {
-        const int newer = min(INFLIGHT - 1, nst - 1 - s);
-        if (newer >= 2) wait_vm<2 * CALLS>();
-        else if (newer == 1) wait_vm<CALLS>();
-        else wait_vm<0>();
+    // Every branch below is resolved at compile time, so the wait counts are
+    // the only synchronisation on the ring and the compiler adds none of its own.
+    const int nst = K / BK;  // a multiple of 4, at least 4
+    auto sync = [&]() {
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        if (s + INFLIGHT < nst) issue(s + INFLIGHT, refill);
-        compute(cur);
     };
+    // keep each refill ahead of the stage's matrix work
+    auto fence = [&]() { __builtin_amdgcn_sched_barrier(0); };
     issue(0, buf0);
     issue(1, buf1);
     issue(2, buf2);
-    for (int s = 0; s < nst; s += 4) {
-        step(s, buf0, buf3);
-        step(s + 1, buf1, buf0);
-        step(s + 2, buf2, buf1);
-        step(s + 3, buf3, buf2);
+    // steady state: stage s waits for itself with two newer stages in flight,
+    // then refills the buffer stage s - 1 used with stage s + 3
+    for (int s = 0; s + 4 < nst; s += 4) {
+        wait_vm<2 * CALLS>(); sync(); issue(s + 3, buf3); fence(); compute(buf0);
+        wait_vm<2 * CALLS>(); sync(); issue(s + 4, buf0); fence(); compute(buf1);
+        wait_vm<2 * CALLS>(); sync(); issue(s + 5, buf1); fence(); compute(buf2);
+        wait_vm<2 * CALLS>(); sync(); issue(s + 6, buf2); fence(); compute(buf3);
     }
+    // last four stages: nst - 4 .. nst - 1 in buf0 .. buf3
+    wait_vm<2 * CALLS>(); sync(); issue(nst - 1, buf3); fence(); compute(buf0);
+    wait_vm<2 * CALLS>(); sync(); compute(buf1);
+    wait_vm<CALLS>(); sync(); compute(buf2);
+    wait_vm<0>(); sync(); compute(buf3);
 
-    // Epilogue: lane holds D[8 * (i / 4) + 4 * (lane / 32) + i % 4][lane % 32] of each 32 x 32 block.
+    // Epilogue.  The weight tile is the MFMA's first operand, so block (a, b)
+    // holds output features x tokens: lane l, entry i has feature
+    // 8 * (i / 4) + 4 * (l / 32) + i % 4 of the block's 32 and token l % 32,
+    // i.e. four consecutive features of one token per group of four entries,
+    // written as one 8-byte store.
     bf16_t* out = (bf16_t*)g.out;
 #pragma unroll
-    for (int a = 0; a < MI; ++a)
+    for (int a = 0; a < MI; ++a) {
+        if (dst_row[a] < 0) continue;
+        bf16_t* orow = out + (int64_t)dst_row[a] * g.out_ld + n0 + 4 * lh;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int row = wm * (BM / 2) + a * 32 + 8 * (i >> 2) + 4 * lh + (i & 3);
-            if (row >= mrows) continue;
-            const int64_t src = (int64_t)m0 + row;
-            const int64_t dst = (g.out_rows ? (int64_t)g.out_rows[src] : src) * g.out_mul + g.out_add;
-            if (PASS == 0) {
+        for (int b = 0; b < (PASS == 0 ? 2 : 4); ++b)
 #pragma unroll
-                for (int b = 0; b < 2; ++b) {
-                    const float gv = acc[a][b][i];
-                    const float v = gv / (1.0f + __expf(-gv)) * acc[a][b + 2][i];
-                    out[dst * g.out_ld + n0 + wn * 64 + b * 32 + lr] = f32_to_bf16(v);
+            for (int j = 0; j < 4; ++j) {
+                float v[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    if (PASS == 0) {
+                        const float gv = acc[a][b][4 * j + q];
+                        v[q] = gv / (1.0f + __expf(-gv)) * acc[a][b + 2][4 * j + q];
+                    } else {
+                        v[q] = acc[a][b][4 * j + q] * row_sc[a];
+                    }
                 }
-            } else {
-                const float sc = g.out_scale ? g.out_scale[src] : 1.0f;
-#pragma unroll
-                for (int b = 0; b < 4; ++b)
-                    out[dst * g.out_ld + n0 + wn * 128 + b * 32 + lr] = f32_to_bf16(acc[a][b][i] * sc);
+                uint2 pk;
+                pk.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+                pk.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+                const int f = (PASS == 0 ? wn * 64 : wn * 128) + b * 32 + 8 * j;
+                *reinterpret_cast<uint2*>(orow + f) = pk;
             }
-        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -408,25 +435,40 @@ bool gemm_mfma_ok(int dtype, int H, int I, int Is) {
     return dtype == kBF16 && H % 128 == 0 && I % 64 == 0 && Is % 64 == 0;
 }
 
+namespace {
+// With events, the launch itself timestamps the kernel's start and end.
+template <typename Kernel>
+hipError_t launch_gemm(Kernel kernel, unsigned grid, hipStream_t st, hipEvent_t e0, hipEvent_t e1,
+                       const GemmArgs& args) {
+    if (!e0 && !e1) {
+        kernel<<<grid, 256, 0, st>>>(args);
+        return hipGetLastError();
+    }
+    GemmArgs copy = args;
+    void* argv[] = {&copy};
+    return hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), dim3(grid), dim3(256), argv, 0, st, e0, e1, 0);
+}
+}  // namespace
+
 hipError_t launch_grouped_gemm(int dtype, int variant, int pass, const GemmArgs& args, int64_t max_items,
-                               hipStream_t st) {
+                               hipStream_t st, hipEvent_t ev_start, hipEvent_t ev_stop) {
     (void)dtype;
     const unsigned grid = (unsigned)(((max_items + 7) / 8) * 8);
     if (grid == 0) return hipSuccess;
     if (variant == kGemmSmallM) {
-        if (pass == 0) grouped_gemm_kernel<TMOE_SMALL_GU><<<grid, 256, 0, st>>>(args);
-        else grouped_gemm_kernel<TMOE_SMALL_DN><<<grid, 256, 0, st>>>(args);
-    } else if (variant == kGemmLargeLds) {
-        if (pass == 0) grouped_gemm_lds_kernel<0, 128><<<grid, 256, 0, st>>>(args);
-        else grouped_gemm_lds_kernel<1, 128><<<grid, 256, 0, st>>>(args);
-    } else if (variant == kGemmHugeLds) {
-        if (pass == 0) grouped_gemm_lds_kernel<0, 256><<<grid, 256, 0, st>>>(args);
-        else grouped_gemm_lds_kernel<1, 256><<<grid, 256, 0, st>>>(args);
-    } else {
-        if (pass == 0) grouped_gemm_kernel<TMOE_LARGE_GU><<<grid, 256, 0, st>>>(args);
-        else grouped_gemm_kernel<TMOE_LARGE_DN><<<grid, 256, 0, st>>>(args);
+        if (pass == 0) return launch_gemm(grouped_gemm_kernel<TMOE_SMALL_GU>, grid, st, ev_start, ev_stop, args);
+        return launch_gemm(grouped_gemm_kernel<TMOE_SMALL_DN>, grid, st, ev_start, ev_stop, args);
     }
-    return hipGetLastError();
+    if (variant == kGemmLargeLds) {
+        if (pass == 0) return launch_gemm(grouped_gemm_lds_kernel<0, 128>, grid, st, ev_start, ev_stop, args);
+        return launch_gemm(grouped_gemm_lds_kernel<1, 128>, grid, st, ev_start, ev_stop, args);
+    }
+    if (variant == kGemmHugeLds) {
+        if (pass == 0) return launch_gemm(grouped_gemm_lds_kernel<0, 256>, grid, st, ev_start, ev_stop, args);
+        return launch_gemm(grouped_gemm_lds_kernel<1, 256>, grid, st, ev_start, ev_stop, args);
+    }
+    if (pass == 0) return launch_gemm(grouped_gemm_kernel<TMOE_LARGE_GU>, grid, st, ev_start, ev_stop, args);
+    return launch_gemm(grouped_gemm_kernel<TMOE_LARGE_DN>, grid, st, ev_start, ev_stop, args);
 }
 
 hipError_t launch_gemm_generic(int dtype, int pass, const GemmGroup& g, const int32_t* offsets, int n_groups_rows,

@@ -77,8 +77,9 @@ enum GemmVariant { kGemmSmallM = 0, kGemmLargeM = 1, kGemmLargeLds = 2, kGemmHug
 void gemm_tiles(int variant, int pass, int* mt, int* nt);
 bool gemm_mfma_ok(int dtype, int H, int I, int Is);
 bool gemm_lds_ok(int H, int I, int Is);  // shapes of the 128 x 256 direct-to-LDS tiles
+// ev_start / ev_stop (nullable): timestamped by the launch at the kernel's start and end
 hipError_t launch_grouped_gemm(int dtype, int variant, int pass, const GemmArgs& args, int64_t max_items,
-                               hipStream_t st);
+                               hipStream_t st, hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 // Portable path: one thread per output; rows of group 0 find their expert in offsets.
 hipError_t launch_gemm_generic(int dtype, int pass, const GemmGroup& g, const int32_t* offsets, int n_groups_rows,
                                int E, int64_t rows, hipStream_t st);
