@@ -111,7 +111,19 @@ struct LayerPlan {
     float* row_scale;
     GemmPlan gemm;
     void *hr, *hs, *ybuf;
+    // direct decode path: per-expert pair lists and h rows at e * T + slot
+    bool direct;
+    int32_t* list;
+    void* hd;
 };
+// Small batches on the matrix-core path: routing writes per-expert lists and
+// the expert products tile themselves from them (no grouping launch).
+bool direct_ok(const moe_config* c, int64_t T, const GemmPlan& g) {
+    const int E = c->num_experts, I = c->moe_intermediate_size;
+    return g.mfma && g.variant == kGemmSmallM && c->dtype == kBF16 && c->hidden_size % 32 == 0 &&
+           route_lists_ok(c->dtype, T, E, c->num_experts_per_tok) &&
+           (int64_t)E * T * I * (int64_t)esize(c->dtype) <= (64ll << 20);
+}
 void plan_layer(const moe_config* c, int64_t T, Carver& cv, LayerPlan& p) {
     const int E = c->num_experts, k = c->num_experts_per_tok, H = c->hidden_size;
     const int I = c->moe_intermediate_size, Is = c->shared_expert_intermediate_size;
@@ -132,6 +144,9 @@ void plan_layer(const moe_config* c, int64_t T, Carver& cv, LayerPlan& p) {
     p.hr = cv.take<char>(N * I * (int64_t)es);
     p.hs = cv.take<char>(T * Is * (int64_t)es);
     p.ybuf = cv.take<char>(T * (k + 1) * (int64_t)H * (int64_t)es);
+    p.direct = direct_ok(c, T, p.gemm);
+    p.list = p.direct ? cv.take<int32_t>((int64_t)E * T) : nullptr;
+    p.hd = p.direct ? cv.take<char>((int64_t)E * T * I * (int64_t)es) : nullptr;
 }
 
 size_t route_ws(const moe_config* c, int64_t T) {
@@ -201,7 +216,7 @@ int run_gemm_pass(const moe_config* c, const GemmPlan& plan, int pass, const Gem
 GemmGroup group(const void* wa, const void* wb, int64_t estride, int N, int K, const void* a, int64_t a_ld,
                 const int32_t* a_rows, void* out, int64_t out_ld, const int32_t* out_rows, int mul, int add,
                 const float* scale) {
-    GemmGroup g;
+    GemmGroup g{};
     g.wa = wa;
     g.wb = wb;
     g.w_estride = estride;
@@ -210,6 +225,7 @@ GemmGroup group(const void* wa, const void* wb, int64_t estride, int N, int K, c
     g.a = a;
     g.a_ld = a_ld;
     g.a_rows = a_rows;
+    g.a_div = 1;
     g.out = out;
     g.out_ld = out_ld;
     g.out_rows = out_rows;
@@ -409,22 +425,70 @@ int moe_layer_forward_timed(const moe_config* cfg, const moe_weights* w, const v
     const TileSpec* t1 = p.gemm.mfma ? &p.gemm.t[0] : nullptr;
     const TileSpec* t2 = p.gemm.mfma ? &p.gemm.t[1] : nullptr;
     TMOE_TRY(mark(0));
-    TMOE_TRY(launch_route(cfg->dtype, x, w->router, w->router_bias, T, H, E, k, cfg->norm_topk_prob, idx, wt, nullptr,
-                          p.route.sc, p.route.bd, p.masks, s));
-    TMOE_TRY(mark(1));
-    if (group_small_ok(T, E))
-        TMOE_TRY(launch_group_small(idx, wt, p.masks, T, E, k, counts, p.offsets, p.row_token, p.row_of, p.row_dst,
-                                    p.row_scale, slots, t1, t2, s));
-    else
-        TMOE_TRY(launch_permute(idx, T, k, E, p.masks, p.prefix, counts, p.offsets, p.row_token, p.row_of, wt,
-                                p.row_dst, p.row_scale, slots, t1, t2, s));
+    auto ev = [&](int i) { return stage_events ? static_cast<hipEvent_t>(stage_events[i]) : nullptr; };
+    if (p.direct) {
+        TMOE_TRY(launch_scores(cfg->dtype, x, w->router, w->router_bias, T, H, E, p.route.sc, p.route.bd, s, counts,
+                               E));
+        TMOE_TRY(mark(1));
+        TMOE_TRY(launch_select_lists(cfg->dtype, p.route.sc, p.route.bd, x, w->router, w->router_bias, T, H, E, k,
+                                     cfg->norm_topk_prob, idx, wt, counts, p.list, s));
+        TMOE_TRY(mark(2));
+        int bm;
+        GemmArgs a{};
+        a.E = E;
+        a.direct_cnt = counts;
+        a.direct_T = (int)T;
+        a.g[0] = group(w->gate, w->up, (int64_t)I * H, I, H, x, H, p.list, p.hd, I, nullptr, 1, 0, nullptr);
+        a.g[0].a_div = k;
+        a.g[1] = Is > 0 ? group(w->shared_gate, w->shared_up, 0, Is, H, x, H, nullptr, p.hs, Is, nullptr, 1, 0, nullptr)
+                        : no_group();
+        int bn = gemm_direct_tile(0, &bm);
+        a.direct_nt[0] = I / bn;
+        a.direct_nt[1] = Is / bn;
+        a.direct_mt1 = (int)((T + bm - 1) / bm);
+        TMOE_TRY(launch_grouped_gemm_direct(0, a, s, ev(6), ev(7)));
+        TMOE_TRY(mark(3));
+        a.g[0] = group(w->down, nullptr, (int64_t)H * I, H, I, p.hd, I, nullptr, p.ybuf, H, p.list, 1, 0, wt);
+        a.g[0].out_div = k;
+        a.g[0].scale_by_map = 1;
+        a.g[1] = Is > 0 ? group(w->shared_down, nullptr, 0, H, Is, p.hs, Is, nullptr, p.ybuf, H, nullptr, slots, k,
+                                nullptr)
+                        : no_group();
+        bn = gemm_direct_tile(1, &bm);
+        a.direct_nt[0] = H / bn;
+        a.direct_nt[1] = Is > 0 ? H / bn : 0;
+        TMOE_TRY(launch_grouped_gemm_direct(1, a, s));
+        TMOE_TRY(mark(4));
+        const char* sb = Is > 0 ? static_cast<const char*>(p.ybuf) + (int64_t)k * H * esize(cfg->dtype) : nullptr;
+        TMOE_TRY(launch_combine(cfg->dtype, p.ybuf, nullptr, nullptr, k, slots, sb, (int64_t)slots * H, residual, y,
+                                T, H, s));
+        TMOE_TRY(mark(5));
+        return MOE_OK;
+    }
+    if (route_group_small_ok(cfg->dtype, T, H, E, k)) {
+        // scores over many CUs, then selection and grouping in one block
+        TMOE_TRY(launch_scores(cfg->dtype, x, w->router, w->router_bias, T, H, E, p.route.sc, p.route.bd, s));
+        TMOE_TRY(mark(1));
+        TMOE_TRY(launch_select_group_small(p.route.sc, p.route.bd, x, w->router, w->router_bias, T, H, E, k,
+                                           cfg->norm_topk_prob, idx, wt, counts, p.offsets, p.row_token, p.row_of,
+                                           p.row_dst, p.row_scale, slots, t1, t2, s));
+    } else {
+        TMOE_TRY(launch_route(cfg->dtype, x, w->router, w->router_bias, T, H, E, k, cfg->norm_topk_prob, idx, wt,
+                              nullptr, p.route.sc, p.route.bd, p.masks, s));
+        TMOE_TRY(mark(1));
+        if (group_small_ok(T, E))
+            TMOE_TRY(launch_group_small(idx, wt, p.masks, T, E, k, counts, p.offsets, p.row_token, p.row_of,
+                                        p.row_dst, p.row_scale, slots, t1, t2, s));
+        else
+            TMOE_TRY(launch_permute(idx, T, k, E, p.masks, p.prefix, counts, p.offsets, p.row_token, p.row_of, wt,
+                                    p.row_dst, p.row_scale, slots, t1, t2, s));
+    }
     TMOE_TRY(mark(2));
 
     GemmGroup gu_r = group(w->gate, w->up, (int64_t)I * H, I, H, x, H, p.row_token, p.hr, I, nullptr, 1, 0, nullptr);
     GemmGroup gu_s = Is > 0 ? group(w->shared_gate, w->shared_up, 0, Is, H, x, H, nullptr, p.hs, Is, nullptr, 1, 0,
                                     nullptr)
                             : no_group();
-    auto ev = [&](int i) { return stage_events ? static_cast<hipEvent_t>(stage_events[i]) : nullptr; };
     int r = run_gemm_pass(cfg, p.gemm, 0, gu_r, gu_s, p.offsets, N, T, s, ev(6), ev(7));
     if (r != MOE_OK) return r;
     TMOE_TRY(mark(3));

@@ -39,18 +39,9 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs args) {
     __shared__ __attribute__((aligned(16))) bf16_t As[BM * LDK];
     __shared__ __attribute__((aligned(16))) bf16_t Bs[BROWS * LDK];
 
-    const int n_items = *args.count;
-    const int p = blockIdx.x;
-    const int chunk = (n_items + 7) >> 3;
-    const int slot = p >> 3;
-    if (slot >= chunk) return;
-    const int q = (p & 7) * chunk + slot;
-    if (q >= n_items) return;
-    const int4 it = args.items[q];
-    const int gi = it.x < args.E ? 0 : 1;
+  // one tile: rows m0 .. m0 + mrows - 1 of group gi, columns n0 .. n0 + BN - 1
+  auto tile = [&](const int gi, const int e, const int n0, const int m0, const int mrows) {
     const GemmGroup& g = args.g[gi];
-    const int e = gi == 0 ? it.x : 0;
-    const int n0 = it.y, m0 = it.z, mrows = it.w;
     const int K = g.K;
     const int tid = threadIdx.x;
 
@@ -63,7 +54,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs args) {
         if (c >= NA) c = 0;
         int row = c / KC, kc = c % KC;
         int m = row < mrows ? row : 0;
-        int64_t grow = g.a_rows ? (int64_t)g.a_rows[m0 + m] : (int64_t)(m0 + m);
+        int64_t grow = g.a_rows ? (int64_t)(g.a_rows[m0 + m] / g.a_div) : (int64_t)(m0 + m);
         pa[i] = (const bf16_t*)g.a + grow * g.a_ld + kc * 8;
     }
 #pragma unroll
@@ -108,7 +99,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs args) {
 
     load(0);
     for (int k0 = 0; k0 < K; k0 += BK) {
-        __syncthreads();
+        __syncthreads();  // (also: the previous tile's last LDS reads are done)
         stash();
         __syncthreads();
         if (k0 + BK < K) load(k0 + BK);
@@ -144,21 +135,55 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs args) {
             const int row = wm * TM + a * 16 + (lane >> 4) * 4 + r;
             if (row >= mrows) continue;
             const int64_t src = (int64_t)m0 + row;
-            const int64_t dst = (g.out_rows ? (int64_t)g.out_rows[src] : src) * g.out_mul + g.out_add;
-            const float sc = (PASS == 1 && g.out_scale) ? g.out_scale[src] : 1.0f;
+            const int64_t v = g.out_rows ? (int64_t)g.out_rows[src] : src;
+            const int64_t dst = v * g.out_mul + g.out_add + (g.out_div > 0 ? v / g.out_div : 0);
+            const float sc = (PASS == 1 && g.out_scale) ? g.out_scale[g.scale_by_map ? v : src] : 1.0f;
 #pragma unroll
             for (int b = 0; b < NS; ++b) {
                 const int col = n0 + wn * TN + b * 16 + li;
-                float v;
+                float val;
                 if (PASS == 0) {
                     float gv = acc[a][b][r];
-                    v = gv / (1.0f + __expf(-gv)) * accu[a][b][r];
+                    val = gv / (1.0f + __expf(-gv)) * accu[a][b][r];
                 } else {
-                    v = acc[a][b][r] * sc;
+                    val = acc[a][b][r] * sc;
                 }
-                out[dst * g.out_ld + col] = f32_to_bf16(v);
+                out[dst * g.out_ld + col] = f32_to_bf16(val);
             }
         }
+  };
+
+    const int p = blockIdx.x;
+    if (args.direct_cnt) {
+        const int nt0 = args.direct_nt[0];
+        const int n_routed = args.E * nt0;
+        const int n_all = n_routed + args.direct_nt[1] * args.direct_mt1;
+        const int chunk = (n_all + 7) >> 3;
+        const int slot = p >> 3;
+        if (slot >= chunk) return;
+        int q = (p & 7) * chunk + slot;
+        if (q >= n_all) return;
+        if (q < n_routed) {
+            const int e = q / nt0, n0 = (q % nt0) * BN;
+            const int m = args.direct_cnt[e];
+            const int base = e * args.direct_T;
+            for (int m0 = 0; m0 < m; m0 += BM) tile(0, e, n0, base + m0, min(BM, m - m0));
+        } else {
+            q -= n_routed;
+            const int n0 = (q / args.direct_mt1) * BN, m0 = (q % args.direct_mt1) * BM;
+            tile(1, 0, n0, m0, min(BM, args.direct_T - m0));
+        }
+        return;
+    }
+    const int n_items = *args.count;
+    const int chunk = (n_items + 7) >> 3;
+    const int slot = p >> 3;
+    if (slot >= chunk) return;
+    const int q = (p & 7) * chunk + slot;
+    if (q >= n_items) return;
+    const int4 it = args.items[q];
+    const int gi = it.x < args.E ? 0 : 1;
+    tile(gi, gi == 0 ? it.x : 0, it.y, it.z, it.w);
 }
 
 // ---------------------------------------------------------------------------
@@ -233,7 +258,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_lds_kernel(GemmArgs args) {
         const int r = (wave * A_CALLS + j) * 16 + (lane >> 2);
         const int c = ((lane & 3) - (r >> 2)) & 3;  // global chunk landing at position lane & 3
         const int m = r < mrows ? r : 0;
-        const int64_t grow = g.a_rows ? (int64_t)g.a_rows[m0 + m] : (int64_t)(m0 + m);
+        const int64_t grow = g.a_rows ? (int64_t)(g.a_rows[m0 + m] / g.a_div) : (int64_t)(m0 + m);
         pa[j] = (const bf16_t*)g.a + grow * g.a_ld + c * 8;
     }
 #pragma unroll
@@ -259,8 +284,9 @@ __global__ __launch_bounds__(256) void grouped_gemm_lds_kernel(GemmArgs args) {
     for (int a = 0; a < MI; ++a) {
         const int r = (wave >> 1) * (BM / 2) + a * 32 + (lane & 31);
         const int64_t src = (int64_t)m0 + (r < mrows ? r : 0);
-        dst_row[a] = r < mrows ? (g.out_rows ? g.out_rows[src] : (int32_t)src) * g.out_mul + g.out_add : -1;
-        row_sc[a] = (PASS == 1 && g.out_scale) ? g.out_scale[src] : 1.0f;
+        const int32_t v = g.out_rows ? g.out_rows[src] : (int32_t)src;
+        dst_row[a] = r < mrows ? v * g.out_mul + g.out_add + (g.out_div > 0 ? v / g.out_div : 0) : -1;
+        row_sc[a] = (PASS == 1 && g.out_scale) ? g.out_scale[g.scale_by_map ? v : src] : 1.0f;
     }
     typedef __attribute__((address_space(3))) void lds_void;
     auto issue = [&](int stage, char* base) {
@@ -469,6 +495,20 @@ hipError_t launch_grouped_gemm(int dtype, int variant, int pass, const GemmArgs&
     }
     if (pass == 0) return launch_gemm(grouped_gemm_kernel<TMOE_LARGE_GU>, grid, st, ev_start, ev_stop, args);
     return launch_gemm(grouped_gemm_kernel<TMOE_LARGE_DN>, grid, st, ev_start, ev_stop, args);
+}
+
+int gemm_direct_tile(int pass, int* bm) {
+    *bm = 16;
+    return pass == 0 ? 64 : 128;
+}
+
+hipError_t launch_grouped_gemm_direct(int pass, const GemmArgs& args, hipStream_t st, hipEvent_t ev_start,
+                                      hipEvent_t ev_stop) {
+    const int64_t n_all = (int64_t)args.E * args.direct_nt[0] + (int64_t)args.direct_nt[1] * args.direct_mt1;
+    const unsigned grid = (unsigned)(((n_all + 7) / 8) * 8);
+    if (grid == 0) return hipSuccess;
+    if (pass == 0) return launch_gemm(grouped_gemm_kernel<TMOE_SMALL_GU>, grid, st, ev_start, ev_stop, args);
+    return launch_gemm(grouped_gemm_kernel<TMOE_SMALL_DN>, grid, st, ev_start, ev_stop, args);
 }
 
 hipError_t launch_gemm_generic(int dtype, int pass, const GemmGroup& g, const int32_t* offsets, int n_groups_rows,

@@ -24,8 +24,24 @@ hipError_t launch_group_small(const int32_t* idx, const float* w, const uint16_t
 hipError_t launch_route(int dtype, const void* x, const void* W, const float* bias, int64_t T, int H, int E, int k,
                         int norm, int32_t* idx, float* w, float* probs, float* scratch_sc, float* scratch_bd,
                         uint16_t* masks, hipStream_t st);
+// Small batches, bf16: after launch_scores, one block selects every token and
+// groups the routing (same outputs as launch_route + launch_group_small).
+bool route_group_small_ok(int dtype, int64_t T, int H, int E, int k);
+hipError_t launch_select_group_small(const float* sc, const float* bd, const void* x, const void* W,
+                                     const float* bias, int64_t T, int H, int E, int k, int norm, int32_t* idx,
+                                     float* w, int32_t* counts, int32_t* offsets, int32_t* row_token,
+                                     int32_t* row_of, int32_t* row_dst, float* row_scale, int slots,
+                                     const TileSpec* t1, const TileSpec* t2, hipStream_t st);
+// zero (nullable): n_zero ints cleared before any later launch on the stream
 hipError_t launch_scores(int dtype, const void* x, const void* W, const float* bias, int64_t T, int H, int n,
-                         float* sc, float* bd, hipStream_t st);
+                         float* sc, float* bd, hipStream_t st, int* zero = nullptr, int n_zero = 0);
+// Small batches (T <= 256, E <= 128, k <= 16): selection from launch_scores'
+// output, appending pair t * k + j to list[e * T + slot] with slot from cnt[e]
+// (cnt cleared by launch_scores).  Row order within a list is arbitrary.
+bool route_lists_ok(int dtype, int64_t T, int E, int k);
+hipError_t launch_select_lists(int dtype, const float* sc, const float* bd, const void* x, const void* W,
+                               const float* bias, int64_t T, int H, int E, int k, int norm, int32_t* idx, float* w,
+                               int* cnt, int* list, hipStream_t st);
 hipError_t launch_argmax(int dtype, const float* sc, const float* bd, const void* x, const void* W, int64_t T, int H,
                          int n, int32_t* out, hipStream_t st);
 
@@ -60,18 +76,29 @@ struct GemmGroup {
     int N, K;              // output width, reduction length
     const void* a;         // A rows
     int64_t a_ld;          // elements between A rows
-    const int32_t* a_rows; // item row -> A row, or nullptr (identity)
+    const int32_t* a_rows; // row r -> A row a_rows[r] / a_div, or nullptr (A row r)
+    int a_div;
     void* out;
     int64_t out_ld;
-    const int32_t* out_rows;  // item row -> destination row, or nullptr (identity)
-    int out_mul, out_add;     // destination row = map(row) * out_mul + out_add
-    const float* out_scale;   // per item-row scale, or nullptr
+    const int32_t* out_rows;  // row r -> v = out_rows[r], or nullptr (v = r)
+    int out_mul, out_add;     // destination row = v * out_mul + out_add (+ v / out_div if out_div > 0)
+    int out_div;
+    const float* out_scale;   // scale out_scale[r] (out_scale[v] if scale_by_map), or nullptr
+    int scale_by_map;
 };
 struct GemmArgs {
     GemmGroup g[2];  // [0] routed experts, [1] shared expert (expert index == E)
     const int4* items;
     const int* count;
     int E;
+    // Direct tiling (when direct_cnt is not null; small-M kernel only): the grid
+    // is E * direct_nt[0] routed tiles, expert-major, then direct_nt[1] x
+    // direct_mt1 shared tiles.  A routed tile covers rows e * direct_T ..
+    // e * direct_T + direct_cnt[e] - 1 of group 0 in chunks of the tile height.
+    const int* direct_cnt;
+    int direct_T;
+    int direct_nt[2];
+    int direct_mt1;
 };
 enum GemmVariant { kGemmSmallM = 0, kGemmLargeM = 1, kGemmLargeLds = 2, kGemmHugeLds = 3 };
 void gemm_tiles(int variant, int pass, int* mt, int* nt);
@@ -80,6 +107,10 @@ bool gemm_lds_ok(int H, int I, int Is);  // shapes of the 128 x 256 direct-to-LD
 // ev_start / ev_stop (nullable): timestamped by the launch at the kernel's start and end
 hipError_t launch_grouped_gemm(int dtype, int variant, int pass, const GemmArgs& args, int64_t max_items,
                                hipStream_t st, hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
+// Direct tiling of the small-M kernel: tile width of a pass, and the launch.
+int gemm_direct_tile(int pass, int* bm);
+hipError_t launch_grouped_gemm_direct(int pass, const GemmArgs& args, hipStream_t st, hipEvent_t ev_start = nullptr,
+                                      hipEvent_t ev_stop = nullptr);
 // Portable path: one thread per output; rows of group 0 find their expert in offsets.
 hipError_t launch_gemm_generic(int dtype, int pass, const GemmGroup& g, const int32_t* offsets, int n_groups_rows,
                                int E, int64_t rows, hipStream_t st);

@@ -79,13 +79,23 @@ struct SelScratch {
     double score[kMaxTopK];
 };
 
+// Where a token's selection is recorded besides idx / weights: per-expert
+// lists (list[e * lstride + slot] = pair index t * k + j, slot from cnt[e]),
+// when cnt is not null.
+struct ListSink {
+    int* cnt;
+    int* list;
+    int lstride;
+};
+
 // Exact Top-k of one row of scores s[0..n) with error bounds d[0..n); writes
-// idx / weights / probs and ORs bit `bit` into mask[e * mstride] for every
-// selected e (LDS).  Called by one full wave; lanes own entries e = lane + 64 j.
+// idx / weights / probs, ORs bit `bit` into mask[e * mstride] (when mask is not
+// null) and appends pair `pair0 + rank` to the list of every selected e.
+// Called by one full wave; lanes own entries e = lane + 64 j.
 template <typename T, int MAXJ, typename S>
 __device__ __noinline__ void exact_select_row(const S* s, const float* d, int n, int k, const T* xrow, const T* W, int H,
                                  const float* bias, SelScratch* sc, int norm, int32_t* out_idx, float* out_w,
-                                 float* out_probs, uint32_t* mask, int mstride, int bit) {
+                                 float* out_probs, uint32_t* mask, int mstride, int bit, ListSink ls, int pair0) {
     const int lane = lane_id();
     float v[MAXJ];
     double dv[MAXJ];
@@ -221,6 +231,7 @@ __device__ __noinline__ void exact_select_row(const S* s, const float* d, int n,
         out_idx[lane] = my_e;
         out_w[lane] = ex / den;
         if (mask) atomicOr(&mask[my_e * mstride], 1u << bit);
+        if (ls.cnt) ls.list[my_e * ls.lstride + atomicAdd(&ls.cnt[my_e], 1)] = pair0 + lane;
     }
 }
 
@@ -242,7 +253,7 @@ template <typename T, int J, typename S>
 __device__ __forceinline__ void select_rows_wave(const S* __restrict__ sc, const float* __restrict__ bd, int64_t tbase, int64_t t, int n, int k,
                                  const T* __restrict__ x, const T* __restrict__ W, int H, const float* bias, int norm,
                                  int32_t* out_idx, float* out_w, float* out_probs, uint32_t* mask, int mstride,
-                                 int word_of_row0, RowPicks& pk, SelScratch* scr) {
+                                 int word_of_row0, RowPicks& pk, SelScratch* scr, ListSink ls = ListSink{}) {
     const int lane = lane_id();
     const int row = lane >> 4, ri = lane & 15;
     const bool valid = t >= 0;
@@ -324,7 +335,8 @@ __device__ __forceinline__ void select_rows_wave(const S* __restrict__ sc, const
             const int e = pk.idx[row][ri];
             out_idx[t * k + ri] = e;
             out_w[t * k + ri] = ex / den;
-            atomicOr(&mask[e * mstride + word_of_row0], 1u << (t & 15));
+            if (mask) atomicOr(&mask[e * mstride + word_of_row0], 1u << (t & 15));
+            if (ls.cnt) ls.list[e * ls.lstride + atomicAdd(&ls.cnt[e], 1)] = (int)(t * k + ri);
         }
     }
     // rows left uncertain: the whole wave redoes them with fp64 rescoring
@@ -335,8 +347,9 @@ __device__ __forceinline__ void select_rows_wave(const S* __restrict__ sc, const
         const int64_t tg = __shfl(t, g * 16, kWave);
         exact_select_row<T, (16 * J + 63) / 64, S>(sc + (tg - tbase) * n, bd + (tg - tbase) * n, n, k, x + tg * H, W, H, bias, scr, norm,
                                                 out_idx + tg * k, out_w + tg * k,
-                                                out_probs ? out_probs + tg * n : nullptr, mask + word_of_row0,
-                                                mstride, (int)(tg & 15));
+                                                out_probs ? out_probs + tg * n : nullptr,
+                                                mask ? mask + word_of_row0 : nullptr, mstride, (int)(tg & 15), ls,
+                                                (int)(tg * k));
     }
 }
 
@@ -348,13 +361,18 @@ __device__ __forceinline__ void select_rows_wave(const S* __restrict__ sc, const
 // LDS in fixed wave order (deterministic).  Splitting the rows over blocks
 // spreads the router's bytes over many CUs even for a few tokens.
 constexpr int kScoreWaves = 8;
-constexpr int kScoreRows = 32;
 
+template <int kScoreRows>  // 16 or 32 weight rows per block
 __global__ __launch_bounds__(64 * kScoreWaves) void scores_kernel(const bf16_t* __restrict__ x,
                                                                   const bf16_t* __restrict__ W,
                                                                   const float* __restrict__ bias, int64_t T, int H,
                                                                   int n, float* __restrict__ sc,
-                                                                  float* __restrict__ bd) {
+                                                                  float* __restrict__ bd, int* __restrict__ clear,
+                                                                  int n_clear) {
+    constexpr bool two = kScoreRows == 32;
+    // clear the per-expert list counters that the selection after this launch fills
+    if (clear && blockIdx.x == 0 && blockIdx.y == 0)
+        for (int q = threadIdx.x; q < n_clear; q += blockDim.x) clear[q] = 0;
     __shared__ double lg[16 * kScoreRows];
     __shared__ float ab[16 * kScoreRows];
     const int wave = threadIdx.x >> 6;
@@ -365,7 +383,7 @@ __global__ __launch_bounds__(64 * kScoreWaves) void scores_kernel(const bf16_t* 
     const int e0 = blockIdx.y * kScoreRows;
     int64_t tok = tok0 + i;
     if (tok >= T) tok = T - 1;
-    int r0 = e0 + i, r1 = e0 + 16 + i;
+    int r0 = e0 + i, r1 = two ? e0 + 16 + i : r0;
     if (r0 >= n) r0 = n - 1;
     if (r1 >= n) r1 = n - 1;
     const bf16_t* xp = x + tok * (int64_t)H + kq;
@@ -384,7 +402,7 @@ __global__ __launch_bounds__(64 * kScoreWaves) void scores_kernel(const bf16_t* 
             if (st < nsteps) {
                 a[u] = *reinterpret_cast<const u32x4*>(xp + st * 32);
                 b0[u] = *reinterpret_cast<const u32x4*>(w0 + st * 32);
-                b1[u] = *reinterpret_cast<const u32x4*>(w1 + st * 32);
+                if (two) b1[u] = *reinterpret_cast<const u32x4*>(w1 + st * 32);
             }
         }
 #pragma unroll
@@ -393,13 +411,16 @@ __global__ __launch_bounds__(64 * kScoreWaves) void scores_kernel(const bf16_t* 
             const bf16x8 av = __builtin_bit_cast(bf16x8, a[u]);
             const bf16x8 aav = __builtin_bit_cast(bf16x8, a[u] & absmask);
             const f32x4 p0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, b0[u]), zero, 0, 0, 0);
-            const f32x4 p1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, b1[u]), zero, 0, 0, 0);
             aa0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aav, __builtin_bit_cast(bf16x8, b0[u] & absmask), aa0, 0, 0, 0);
-            aa1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aav, __builtin_bit_cast(bf16x8, b1[u] & absmask), aa1, 0, 0, 0);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                acc0[r] += (double)p0[r];
-                acc1[r] += (double)p1[r];
+            for (int r = 0; r < 4; ++r) acc0[r] += (double)p0[r];
+            if (two) {
+                const f32x4 p1 =
+                    __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, b1[u]), zero, 0, 0, 0);
+                aa1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aav, __builtin_bit_cast(bf16x8, b1[u] & absmask), aa1,
+                                                              0, 0, 0);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc1[r] += (double)p1[r];
             }
         }
     }
@@ -411,10 +432,10 @@ __global__ __launch_bounds__(64 * kScoreWaves) void scores_kernel(const bf16_t* 
                 const int q = ((lane >> 4) * 4 + r) * kScoreRows + i;
                 if (w == 0) {
                     lg[q] = acc0[r]; ab[q] = aa0[r];
-                    lg[q + 16] = acc1[r]; ab[q + 16] = aa1[r];
+                    if (two) { lg[q + 16] = acc1[r]; ab[q + 16] = aa1[r]; }
                 } else {
                     lg[q] += acc0[r]; ab[q] += aa0[r];
-                    lg[q + 16] += acc1[r]; ab[q + 16] += aa1[r];
+                    if (two) { lg[q + 16] += acc1[r]; ab[q + 16] += aa1[r]; }
                 }
             }
         }
@@ -623,7 +644,8 @@ __global__ __launch_bounds__(256) void select_topk_kernel(const float* __restric
         const int64_t t = tok0 + tt;
         if (t >= Ttok) break;
         exact_select_row<T, MAXJ, float>(sc + t * n, bd + t * n, n, k, x + t * H, W, H, bias, &scr[wave], norm,
-                                  out_idx + t * k, out_w + t * k, out_probs ? out_probs + t * n : nullptr, msk, 1, tt);
+                                  out_idx + t * k, out_w + t * k, out_probs ? out_probs + t * n : nullptr, msk, 1, tt,
+                                  ListSink{}, 0);
     }
     if (masks) {
         __syncthreads();
@@ -687,6 +709,72 @@ __global__ __launch_bounds__(1024) void group_small_kernel(const int32_t* __rest
         if (row_dst) {
             row_dst[dst] = t * slots + j;
             row_scale[dst] = wts[i];
+        }
+    }
+}
+
+// Small batches, routing finished in the grouping block: each of the 8
+// waves selects four tokens at a time from the global scores (certified, with
+// fp64 rescoring of uncertain tokens) and records the token masks in LDS; the
+// block then derives counts, offsets, stable row order, row maps and GEMM tile
+// lists from those masks, as group_small_kernel does from global ones.
+constexpr int kSelectGroupThreads = 512;
+
+template <int J>
+__global__ __launch_bounds__(kSelectGroupThreads) void select_group_small_kernel(
+    const float* __restrict__ sc, const float* __restrict__ bd, const bf16_t* __restrict__ x,
+    const bf16_t* __restrict__ W, const float* __restrict__ bias, int Ttok, int H, int E, int k, int norm,
+    int32_t* __restrict__ out_idx, float* __restrict__ out_w, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ row_token, int32_t* __restrict__ row_of,
+    int32_t* __restrict__ row_dst, float* __restrict__ row_scale, int slots, TileSpecs specs) {
+    __shared__ uint32_t msk[128 * kSmallWords];
+    __shared__ int pre[128 * kSmallWords];
+    __shared__ int offs[128];
+    __shared__ int lds[17];
+    constexpr int kWaves = kSelectGroupThreads / 64;
+    __shared__ RowPicks picks[kWaves];
+    __shared__ SelScratch scr[kWaves];
+    for (int q = threadIdx.x; q < 128 * kSmallWords; q += blockDim.x) msk[q] = 0;
+    __syncthreads();
+    const int wave = threadIdx.x >> 6;
+    for (int t0 = wave * 4; t0 < Ttok; t0 += 4 * kWaves) {
+        const int t = t0 + (lane_id() >> 4);
+        select_rows_wave<bf16_t, J, float>(sc, bd, 0, t < Ttok ? t : -1, E, k, x, W, H, bias, norm, out_idx, out_w,
+                                           nullptr, msk, kSmallWords, t0 >> 4, picks[wave], &scr[wave]);
+    }
+    __syncthreads();
+    const int nw = (Ttok + 15) / 16;
+    const int e = threadIdx.x;
+    int c = 0;
+    if (e < E) {
+        for (int w = 0; w < nw; ++w) {
+            pre[e * kSmallWords + w] = c;
+            c += __popc(msk[e * kSmallWords + w]);
+        }
+    }
+    int total;
+    const int excl = block_exclusive_scan(e < E ? c : 0, lds, &total);
+    if (e < E) {
+        offs[e] = excl;
+        counts[e] = c;
+        offsets[e] = excl;
+    }
+    if (e == 0) offsets[E] = total;
+    for (int s = 0; s < specs.n; ++s) block_build_items(c, excl, E, Ttok, specs.t[s], lds);
+    __syncthreads();
+    const int N = Ttok * k;
+    for (int i = threadIdx.x; i < N; i += blockDim.x) {
+        const int ee = out_idx[i];
+        if (ee < 0 || ee >= E) continue;
+        const int t = i / k, j = i % k;
+        const int m = ee * kSmallWords + (t >> 4);
+        const int dst = offs[ee] + pre[m] + __popc(msk[m] & ((1u << (t & 15)) - 1u));
+        if (dst < 0 || dst >= N) continue;
+        row_token[dst] = t;
+        row_of[i] = dst;
+        if (row_dst) {
+            row_dst[dst] = t * slots + j;
+            row_scale[dst] = out_w[i];
         }
     }
 }
@@ -772,12 +860,23 @@ static hipError_t launch_select(const float* sc, const float* bd, const T* x, co
 }
 
 hipError_t launch_scores(int dtype, const void* x, const void* W, const float* bias, int64_t Ttok, int H, int n,
-                         float* sc, float* bd, hipStream_t st) {
+                         float* sc, float* bd, hipStream_t st, int* zero, int n_zero) {
     if (dtype == kBF16 && H % 32 == 0) {
-        dim3 grid((unsigned)((Ttok + 15) / 16), (unsigned)((n + kScoreRows - 1) / kScoreRows));
-        scores_kernel<<<grid, 64 * kScoreWaves, 0, st>>>((const bf16_t*)x, (const bf16_t*)W, bias, Ttok, H, n, sc,
-                                                         bd);
+        // few tokens: 16 weight rows per block, so the router spreads over more CUs
+        if (Ttok <= 256) {
+            dim3 grid((unsigned)((Ttok + 15) / 16), (unsigned)((n + 15) / 16));
+            scores_kernel<16><<<grid, 64 * kScoreWaves, 0, st>>>((const bf16_t*)x, (const bf16_t*)W, bias, Ttok, H,
+                                                                 n, sc, bd, zero, n_zero);
+        } else {
+            dim3 grid((unsigned)((Ttok + 15) / 16), (unsigned)((n + 31) / 32));
+            scores_kernel<32><<<grid, 64 * kScoreWaves, 0, st>>>((const bf16_t*)x, (const bf16_t*)W, bias, Ttok, H,
+                                                                 n, sc, bd, zero, n_zero);
+        }
     } else {
+        if (zero) {
+            hipError_t e = launch_fill_i32(zero, 0, n_zero, st);
+            if (e != hipSuccess) return e;
+        }
         dim3 grid((unsigned)((n + 255) / 256), (unsigned)Ttok);
         if (dtype == kBF16)
             scores_generic_kernel<bf16_t><<<grid, 256, 0, st>>>((const bf16_t*)x, (const bf16_t*)W, bias, Ttok, H, n,
@@ -812,7 +911,7 @@ hipError_t launch_route(int dtype, const void* x, const void* W, const float* bi
 #undef TMOE_FUSED
         return hipGetLastError();
     }
-    hipError_t err = launch_scores(dtype, x, W, bias, Ttok, H, E, scratch_sc, scratch_bd, st);
+    hipError_t err = launch_scores(dtype, x, W, bias, Ttok, H, E, scratch_sc, scratch_bd, st, nullptr, 0);
     if (err != hipSuccess) return err;
     if (dtype == kBF16)
         return launch_select<bf16_t>(scratch_sc, scratch_bd, (const bf16_t*)x, (const bf16_t*)W, bias, Ttok, H, E, k,
@@ -827,6 +926,71 @@ hipError_t launch_group_small(const int32_t* idx, const float* w, const uint16_t
                               hipStream_t st) {
     group_small_kernel<<<1, 1024, 0, st>>>(idx, w, masks, mask_stride(Ttok), (int)Ttok, E, k, counts, offsets,
                                            row_token, row_of, row_dst, row_scale, slots, make_specs(t1, t2));
+    return hipGetLastError();
+}
+
+bool route_group_small_ok(int dtype, int64_t T, int H, int E, int k) {
+    return dtype == kBF16 && H % 32 == 0 && group_small_ok(T, E) && k <= 16;
+}
+
+hipError_t launch_select_group_small(const float* scratch_sc, const float* scratch_bd, const void* x, const void* W,
+                                     const float* bias, int64_t Ttok, int H, int E, int k, int norm, int32_t* idx,
+                                     float* w, int32_t* counts, int32_t* offsets, int32_t* row_token,
+                                     int32_t* row_of, int32_t* row_dst, float* row_scale, int slots,
+                                     const TileSpec* t1, const TileSpec* t2, hipStream_t st) {
+    const bf16_t* xb = (const bf16_t*)x;
+    const bf16_t* wb = (const bf16_t*)W;
+    const TileSpecs specs = make_specs(t1, t2);
+#define TMOE_SG(J)                                                                                          \
+    select_group_small_kernel<J><<<1, kSelectGroupThreads, 0, st>>>(scratch_sc, scratch_bd, xb, wb, bias, (int)Ttok, H, E, k, \
+                                                     norm, idx, w, counts, offsets, row_token, row_of, row_dst, \
+                                                     row_scale, slots, specs)
+    if (E <= 16) TMOE_SG(1);
+    else if (E <= 32) TMOE_SG(2);
+    else if (E <= 64) TMOE_SG(4);
+    else TMOE_SG(8);
+#undef TMOE_SG
+    return hipGetLastError();
+}
+
+// Small batches: selection spread over T / 4 one-wave blocks, each token's
+// pairs appended to per-expert lists (counters cleared by the scores launch).
+template <typename T, int J>
+__global__ __launch_bounds__(64) void select_lists_kernel(const float* __restrict__ sc, const float* __restrict__ bd,
+                                                          const T* __restrict__ x, const T* __restrict__ W,
+                                                          const float* __restrict__ bias, int64_t Ttok, int H, int n,
+                                                          int k, int norm, int32_t* __restrict__ out_idx,
+                                                          float* __restrict__ out_w, int* __restrict__ cnt,
+                                                          int* __restrict__ list, int lstride) {
+    __shared__ RowPicks picks;
+    __shared__ SelScratch scr;
+    const int64_t t = (int64_t)blockIdx.x * 4 + (lane_id() >> 4);
+    select_rows_wave<T, J, float>(sc, bd, 0, t < Ttok ? t : -1, n, k, x, W, H, bias, norm, out_idx, out_w, nullptr,
+                                  nullptr, 0, 0, picks, &scr, ListSink{cnt, list, lstride});
+}
+
+bool route_lists_ok(int dtype, int64_t T, int E, int k) { return T <= kSmallMaxT && E <= 128 && k <= 16; }
+
+hipError_t launch_select_lists(int dtype, const float* sc, const float* bd, const void* x, const void* W,
+                               const float* bias, int64_t Ttok, int H, int E, int k, int norm, int32_t* idx, float* w,
+                               int* cnt, int* list, hipStream_t st) {
+    const dim3 grid((unsigned)((Ttok + 3) / 4));
+    const int ls = (int)Ttok;
+#define TMOE_SL(TT, J)                                                                                          \
+    select_lists_kernel<TT, J><<<grid, 64, 0, st>>>(sc, bd, (const TT*)x, (const TT*)W, bias, Ttok, H, E, k, norm, \
+                                                    idx, w, cnt, list, ls)
+    if (dtype == kBF16) {
+        if (E <= 16) TMOE_SL(bf16_t, 1);
+        else if (E <= 32) TMOE_SL(bf16_t, 2);
+        else if (E <= 64) TMOE_SL(bf16_t, 4);
+        else TMOE_SL(bf16_t, 8);
+    } else {
+        if (E <= 16) TMOE_SL(float, 1);
+        else if (E <= 32) TMOE_SL(float, 2);
+        else if (E <= 64) TMOE_SL(float, 4);
+        else TMOE_SL(float, 8);
+    }
+#undef TMOE_SL
     return hipGetLastError();
 }
 
