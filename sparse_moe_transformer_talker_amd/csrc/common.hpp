@@ -154,6 +154,14 @@ __device__ __forceinline__ uint64_t row_max_key(uint64_t key) {
 #undef TMOE_RMAX
     return key;
 }
+__device__ __forceinline__ uint32_t umax32(uint32_t a, uint32_t b) { return a > b ? a : b; }
+__device__ __forceinline__ uint32_t row_max_u32(uint32_t x) {
+    x = umax32(x, (uint32_t)TMOE_ROR(x, 8));
+    x = umax32(x, (uint32_t)TMOE_ROR(x, 4));
+    x = umax32(x, (uint32_t)TMOE_ROR(x, 2));
+    x = umax32(x, (uint32_t)TMOE_ROR(x, 1));
+    return x;
+}
 __device__ __forceinline__ float row_sum(float x) {
     x += __uint_as_float(TMOE_ROR(__float_as_uint(x), 8));
     x += __uint_as_float(TMOE_ROR(__float_as_uint(x), 4));

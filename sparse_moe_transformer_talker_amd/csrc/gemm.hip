@@ -39,119 +39,119 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs args) {
     __shared__ __attribute__((aligned(16))) bf16_t As[BM * LDK];
     __shared__ __attribute__((aligned(16))) bf16_t Bs[BROWS * LDK];
 
-  // one tile: rows m0 .. m0 + mrows - 1 of group gi, columns n0 .. n0 + BN - 1
-  auto tile = [&](const int gi, const int e, const int n0, const int m0, const int mrows) {
-    const GemmGroup& g = args.g[gi];
-    const int K = g.K;
-    const int tid = threadIdx.x;
+    // one tile: rows m0 .. m0 + mrows - 1 of group gi, columns n0 .. n0 + BN - 1
+    auto tile = [&](const int gi, const int e, const int n0, const int m0, const int mrows) {
+        const GemmGroup& g = args.g[gi];
+        const int K = g.K;
+        const int tid = threadIdx.x;
 
-    // Per-thread global source pointers (fixed over K).
-    const bf16_t* pa[CA];
-    const bf16_t* pb[CB];
-#pragma unroll
-    for (int i = 0; i < CA; ++i) {
-        int c = tid + 256 * i;
-        if (c >= NA) c = 0;
-        int row = c / KC, kc = c % KC;
-        int m = row < mrows ? row : 0;
-        int64_t grow = g.a_rows ? (int64_t)(g.a_rows[m0 + m] / g.a_div) : (int64_t)(m0 + m);
-        pa[i] = (const bf16_t*)g.a + grow * g.a_ld + kc * 8;
-    }
-#pragma unroll
-    for (int i = 0; i < CB; ++i) {
-        int c = tid + 256 * i;
-        int row = c / KC, kc = c % KC;
-        const bf16_t* w = (const bf16_t*)((PASS == 0 && row >= BN) ? g.wb : g.wa);
-        int wrow = n0 + (row % BN);
-        pb[i] = w + (int64_t)e * g.w_estride + (int64_t)wrow * K + kc * 8;
-    }
-
-    u32x4 ra[CA], rb[CB];
-    auto load = [&](int k0) {
-#pragma unroll
-        for (int i = 0; i < CA; ++i)
-            if (tid + 256 * i < NA) ra[i] = *reinterpret_cast<const u32x4*>(pa[i] + k0);
-#pragma unroll
-        for (int i = 0; i < CB; ++i) rb[i] = *reinterpret_cast<const u32x4*>(pb[i] + k0);
-    };
-    auto stash = [&]() {
+        // Per-thread global source pointers (fixed over K).
+        const bf16_t* pa[CA];
+        const bf16_t* pb[CB];
 #pragma unroll
         for (int i = 0; i < CA; ++i) {
             int c = tid + 256 * i;
-            if (c < NA) *reinterpret_cast<u32x4*>(&As[(c / KC) * LDK + (c % KC) * 8]) = ra[i];
+            if (c >= NA) c = 0;
+            int row = c / KC, kc = c % KC;
+            int m = row < mrows ? row : 0;
+            int64_t grow = g.a_rows ? (int64_t)(g.a_rows[m0 + m] / g.a_div) : (int64_t)(m0 + m);
+            pa[i] = (const bf16_t*)g.a + grow * g.a_ld + kc * 8;
         }
 #pragma unroll
         for (int i = 0; i < CB; ++i) {
             int c = tid + 256 * i;
-            *reinterpret_cast<u32x4*>(&Bs[(c / KC) * LDK + (c % KC) * 8]) = rb[i];
+            int row = c / KC, kc = c % KC;
+            const bf16_t* w = (const bf16_t*)((PASS == 0 && row >= BN) ? g.wb : g.wa);
+            int wrow = n0 + (row % BN);
+            pb[i] = w + (int64_t)e * g.w_estride + (int64_t)wrow * K + kc * 8;
         }
-    };
 
-    const int wave = tid >> 6, lane = tid & 63;
-    const int wm = wave / WN, wn = wave % WN;
-    const int li = lane & 15, lk = (lane >> 4) * 8;
-
-    f32x4 acc[MS][NS], accu[MS][NS];
+        u32x4 ra[CA], rb[CB];
+        auto load = [&](int k0) {
 #pragma unroll
-    for (int a = 0; a < MS; ++a)
+            for (int i = 0; i < CA; ++i)
+                if (tid + 256 * i < NA) ra[i] = *reinterpret_cast<const u32x4*>(pa[i] + k0);
 #pragma unroll
-        for (int b = 0; b < NS; ++b) { acc[a][b] = f32x4{0, 0, 0, 0}; accu[a][b] = f32x4{0, 0, 0, 0}; }
-
-    load(0);
-    for (int k0 = 0; k0 < K; k0 += BK) {
-        __syncthreads();  // (also: the previous tile's last LDS reads are done)
-        stash();
-        __syncthreads();
-        if (k0 + BK < K) load(k0 + BK);
+            for (int i = 0; i < CB; ++i) rb[i] = *reinterpret_cast<const u32x4*>(pb[i] + k0);
+        };
+        auto stash = [&]() {
 #pragma unroll
-        for (int ks = 0; ks < BK; ks += 32) {
-            bf16x8 af[MS], bg[NS], bu[NS];
-#pragma unroll
-            for (int a = 0; a < MS; ++a)
-                af[a] = *reinterpret_cast<const bf16x8*>(&As[(wm * TM + a * 16 + li) * LDK + ks + lk]);
-#pragma unroll
-            for (int b = 0; b < NS; ++b) {
-                bg[b] = *reinterpret_cast<const bf16x8*>(&Bs[(wn * TN + b * 16 + li) * LDK + ks + lk]);
-                if (PASS == 0)
-                    bu[b] = *reinterpret_cast<const bf16x8*>(&Bs[(BN + wn * TN + b * 16 + li) * LDK + ks + lk]);
+            for (int i = 0; i < CA; ++i) {
+                int c = tid + 256 * i;
+                if (c < NA) *reinterpret_cast<u32x4*>(&As[(c / KC) * LDK + (c % KC) * 8]) = ra[i];
             }
 #pragma unroll
-            for (int a = 0; a < MS; ++a)
+            for (int i = 0; i < CB; ++i) {
+                int c = tid + 256 * i;
+                *reinterpret_cast<u32x4*>(&Bs[(c / KC) * LDK + (c % KC) * 8]) = rb[i];
+            }
+        };
+
+        const int wave = tid >> 6, lane = tid & 63;
+        const int wm = wave / WN, wn = wave % WN;
+        const int li = lane & 15, lk = (lane >> 4) * 8;
+
+        f32x4 acc[MS][NS], accu[MS][NS];
+#pragma unroll
+        for (int a = 0; a < MS; ++a)
+#pragma unroll
+            for (int b = 0; b < NS; ++b) { acc[a][b] = f32x4{0, 0, 0, 0}; accu[a][b] = f32x4{0, 0, 0, 0}; }
+
+        load(0);
+        for (int k0 = 0; k0 < K; k0 += BK) {
+            __syncthreads();  // (also: the previous tile's last LDS reads are done)
+            stash();
+            __syncthreads();
+            if (k0 + BK < K) load(k0 + BK);
+#pragma unroll
+            for (int ks = 0; ks < BK; ks += 32) {
+                bf16x8 af[MS], bg[NS], bu[NS];
+#pragma unroll
+                for (int a = 0; a < MS; ++a)
+                    af[a] = *reinterpret_cast<const bf16x8*>(&As[(wm * TM + a * 16 + li) * LDK + ks + lk]);
 #pragma unroll
                 for (int b = 0; b < NS; ++b) {
-                    acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[a], bg[b], acc[a][b], 0, 0, 0);
+                    bg[b] = *reinterpret_cast<const bf16x8*>(&Bs[(wn * TN + b * 16 + li) * LDK + ks + lk]);
                     if (PASS == 0)
-                        accu[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[a], bu[b], accu[a][b], 0, 0, 0);
+                        bu[b] = *reinterpret_cast<const bf16x8*>(&Bs[(BN + wn * TN + b * 16 + li) * LDK + ks + lk]);
                 }
-        }
-    }
-
-    // Epilogue: lane holds D[4*(lane/16) + r][lane % 16] of every 16x16 block.
-    bf16_t* out = (bf16_t*)g.out;
 #pragma unroll
-    for (int a = 0; a < MS; ++a)
+                for (int a = 0; a < MS; ++a)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int row = wm * TM + a * 16 + (lane >> 4) * 4 + r;
-            if (row >= mrows) continue;
-            const int64_t src = (int64_t)m0 + row;
-            const int64_t v = g.out_rows ? (int64_t)g.out_rows[src] : src;
-            const int64_t dst = v * g.out_mul + g.out_add + (g.out_div > 0 ? v / g.out_div : 0);
-            const float sc = (PASS == 1 && g.out_scale) ? g.out_scale[g.scale_by_map ? v : src] : 1.0f;
-#pragma unroll
-            for (int b = 0; b < NS; ++b) {
-                const int col = n0 + wn * TN + b * 16 + li;
-                float val;
-                if (PASS == 0) {
-                    float gv = acc[a][b][r];
-                    val = gv / (1.0f + __expf(-gv)) * accu[a][b][r];
-                } else {
-                    val = acc[a][b][r] * sc;
-                }
-                out[dst * g.out_ld + col] = f32_to_bf16(val);
+                    for (int b = 0; b < NS; ++b) {
+                        acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[a], bg[b], acc[a][b], 0, 0, 0);
+                        if (PASS == 0)
+                            accu[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[a], bu[b], accu[a][b], 0, 0, 0);
+                    }
             }
         }
-  };
+
+        // Epilogue: lane holds D[4*(lane/16) + r][lane % 16] of every 16x16 block.
+        bf16_t* out = (bf16_t*)g.out;
+#pragma unroll
+        for (int a = 0; a < MS; ++a)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = wm * TM + a * 16 + (lane >> 4) * 4 + r;
+                if (row >= mrows) continue;
+                const int64_t src = (int64_t)m0 + row;
+                const int64_t v = g.out_rows ? (int64_t)g.out_rows[src] : src;
+                const int64_t dst = v * g.out_mul + g.out_add + (g.out_div > 0 ? v / g.out_div : 0);
+                const float sc = (PASS == 1 && g.out_scale) ? g.out_scale[g.scale_by_map ? v : src] : 1.0f;
+#pragma unroll
+                for (int b = 0; b < NS; ++b) {
+                    const int col = n0 + wn * TN + b * 16 + li;
+                    float val;
+                    if (PASS == 0) {
+                        float gv = acc[a][b][r];
+                        val = gv / (1.0f + __expf(-gv)) * accu[a][b][r];
+                    } else {
+                        val = acc[a][b][r] * sc;
+                    }
+                    out[dst * g.out_ld + col] = f32_to_bf16(val);
+                }
+            }
+    };
 
     const int p = blockIdx.x;
     if (args.direct_cnt) {
@@ -440,13 +440,15 @@ __global__ __launch_bounds__(256) void gemm_generic_kernel(GemmGroup g, const in
 // ---------------------------------------------------------------------------
 // Tilings: small-M (few rows per expert: weight streaming) and large-M.
 //                         BM   BN   BK  WM WN
-#define TMOE_SMALL_GU 0,   16,  64, 128, 1, 4
-#define TMOE_SMALL_DN 1,   16, 128,  64, 1, 4
+constexpr int kSmallBM = 16, kSmallBN0 = 64, kSmallBN1 = 64;
+#define TMOE_SMALL_GU 0, kSmallBM, kSmallBN0, 128, 1, 4
+#define TMOE_SMALL_DN 1, kSmallBM, kSmallBN1, 128, 1, 4
+#define TMOE_SMALL_DN64 1, kSmallBM, kSmallBN1, 64, 1, 4  // reductions of 64 * odd length
 #define TMOE_LARGE_GU 0,  128,  64,  64, 2, 2
 #define TMOE_LARGE_DN 1,  128, 128,  64, 2, 2
 
 void gemm_tiles(int variant, int pass, int* mt, int* nt) {
-    if (variant == kGemmSmallM) { *mt = 16; *nt = pass == 0 ? 64 : 128; }
+    if (variant == kGemmSmallM) { *mt = kSmallBM; *nt = pass == 0 ? kSmallBN0 : kSmallBN1; }
     else if (variant == kGemmLargeLds) { *mt = 128; *nt = pass == 0 ? lds_gemm::BNR / 2 : lds_gemm::BNR; }
     else if (variant == kGemmHugeLds) { *mt = 256; *nt = pass == 0 ? lds_gemm::BNR / 2 : lds_gemm::BNR; }
     else { *mt = 128; *nt = pass == 0 ? 64 : 128; }
@@ -462,6 +464,11 @@ bool gemm_mfma_ok(int dtype, int H, int I, int Is) {
 }
 
 namespace {
+// reduction lengths of both groups are multiples of m (absent groups pass)
+bool k_multiple(const GemmArgs& a, int m) {
+    return a.g[0].K % m == 0 && (a.g[1].N == 0 || a.g[1].K % m == 0);
+}
+
 // With events, the launch itself timestamps the kernel's start and end.
 template <typename Kernel>
 hipError_t launch_gemm(Kernel kernel, unsigned grid, hipStream_t st, hipEvent_t e0, hipEvent_t e1,
@@ -483,6 +490,8 @@ hipError_t launch_grouped_gemm(int dtype, int variant, int pass, const GemmArgs&
     if (grid == 0) return hipSuccess;
     if (variant == kGemmSmallM) {
         if (pass == 0) return launch_gemm(grouped_gemm_kernel<TMOE_SMALL_GU>, grid, st, ev_start, ev_stop, args);
+        if (!k_multiple(args, 128))
+            return launch_gemm(grouped_gemm_kernel<TMOE_SMALL_DN64>, grid, st, ev_start, ev_stop, args);
         return launch_gemm(grouped_gemm_kernel<TMOE_SMALL_DN>, grid, st, ev_start, ev_stop, args);
     }
     if (variant == kGemmLargeLds) {
@@ -498,8 +507,8 @@ hipError_t launch_grouped_gemm(int dtype, int variant, int pass, const GemmArgs&
 }
 
 int gemm_direct_tile(int pass, int* bm) {
-    *bm = 16;
-    return pass == 0 ? 64 : 128;
+    *bm = kSmallBM;
+    return pass == 0 ? kSmallBN0 : kSmallBN1;
 }
 
 hipError_t launch_grouped_gemm_direct(int pass, const GemmArgs& args, hipStream_t st, hipEvent_t ev_start,
@@ -508,6 +517,8 @@ hipError_t launch_grouped_gemm_direct(int pass, const GemmArgs& args, hipStream_
     const unsigned grid = (unsigned)(((n_all + 7) / 8) * 8);
     if (grid == 0) return hipSuccess;
     if (pass == 0) return launch_gemm(grouped_gemm_kernel<TMOE_SMALL_GU>, grid, st, ev_start, ev_stop, args);
+    if (!k_multiple(args, 128))
+        return launch_gemm(grouped_gemm_kernel<TMOE_SMALL_DN64>, grid, st, ev_start, ev_stop, args);
     return launch_gemm(grouped_gemm_kernel<TMOE_SMALL_DN>, grid, st, ev_start, ev_stop, args);
 }
 

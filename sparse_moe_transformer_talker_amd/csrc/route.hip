@@ -259,27 +259,31 @@ __device__ __forceinline__ void select_rows_wave(const S* __restrict__ sc, const
     const bool valid = t >= 0;
     float v[J];
     double dv[J];
-    uint64_t key[J];  // rank keys (unique: they carry the index); 0 once picked or absent
-    int pick[J];      // round in which the entry was picked, -1 if not
+    // Ranking keys: the score's order key with its low byte replaced by 255 - e
+    // (n <= 128), unique and never 0; 0 once picked or absent.  Scores that
+    // differ only in that byte may come out misordered, which the certificate
+    // below (on the exact fp32 values) always rejects.
+    uint32_t key[J];
+    int pick[J];  // round in which the entry was picked, -1 if not
 #pragma unroll
     for (int j = 0; j < J; ++j) {
         const int e = ri + 16 * j;
         const bool ok = valid && e < n;
         v[j] = ok ? (float)sc[(t - tbase) * n + e] + 0.0f : 0.0f;
         dv[j] = ok ? (double)bd[(t - tbase) * n + e] + 1.1920928955078125e-07 * fabs((double)v[j]) : 0.0;
-        key[j] = ok ? rank_key(v[j], e) : 0ull;
+        key[j] = ok ? ((float_order_key(v[j]) & 0xFFFFFF00u) | (uint32_t)(255 - e)) : 0u;
         pick[j] = -1;
     }
     for (int r = 0; r < k; ++r) {
-        uint64_t m = 0;
+        uint32_t m = 0;
 #pragma unroll
-        for (int j = 0; j < J; ++j) m = key[j] > m ? key[j] : m;
-        m = row_max_key(m);
+        for (int j = 0; j < J; ++j) m = umax32(m, key[j]);
+        m = row_max_u32(m);
 #pragma unroll
         for (int j = 0; j < J; ++j) {
             const bool hit = key[j] == m && m != 0;
             pick[j] = hit ? r : pick[j];
-            key[j] = hit ? 0ull : key[j];
+            key[j] = hit ? 0u : key[j];
         }
     }
     bool taken[J];
@@ -452,6 +456,95 @@ __global__ __launch_bounds__(64 * kScoreWaves) void scores_kernel(const bf16_t* 
         const double a = (double)ab[q];
         sc[t * n + e] = (float)sv;
         bd[t * n + e] = (float)(es * a + fs * (a + fabs((double)b)) + 0.5 * 1.1920928955078125e-07 * fabs(sv)) *
+                        (1.0f + kTwoM23);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Few tokens (bf16, H % 256 == 0): scores from exact products.  A bf16 x bf16
+// product is exact in fp64, so on the fp64 matrix cores (v_mfma_f64_16x16x4_f64)
+// only the fp64 additions round: each instruction adds four products to the
+// running sum, so |s - exact| <= (H / 8 + 16) 2^-53 sum_h |x_h W_eh|, far below
+// any gap that can separate two fp32 scores; the selection after it almost
+// never needs its fp64 rescoring.  The abs-sum bound comes from one bf16
+// matrix-core step per eight products (relative error below 2^-17).
+// A block computes 16 tokens x 16 weight rows; wave w takes the w-th eighth of
+// K, and the four lane groups of a wave contiguous quarters of it (the K order
+// inside a product is immaterial as long as both operands use it).  Wave
+// partials are added in LDS in wave order.
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+constexpr int kS64Waves = 8;
+
+__global__ __launch_bounds__(64 * kS64Waves) void scores64_kernel(const bf16_t* __restrict__ x,
+                                                                  const bf16_t* __restrict__ W,
+                                                                  const float* __restrict__ bias, int64_t T, int H,
+                                                                  int n, float* __restrict__ sc,
+                                                                  float* __restrict__ bd, int* __restrict__ clear,
+                                                                  int n_clear) {
+    __shared__ double part[kS64Waves][256];
+    __shared__ float apart[kS64Waves][256];
+    if (clear && blockIdx.x == 0 && blockIdx.y == 0)
+        for (int q = threadIdx.x; q < n_clear; q += blockDim.x) clear[q] = 0;
+    const int wave = threadIdx.x >> 6, lane = lane_id();
+    const int i = lane & 15, grp = lane >> 4;
+    const int64_t tok0 = (int64_t)blockIdx.x * 16;
+    const int e0 = blockIdx.y * 16;
+    const int64_t tok = tok0 + i < T ? tok0 + i : T - 1;
+    const int row = min(e0 + i, n - 1);
+    const int kw = H / kS64Waves, kq = kw / 4;
+    const bf16_t* xp = x + tok * (int64_t)H + wave * kw + grp * kq;
+    const bf16_t* wp = W + (int64_t)row * H + wave * kw + grp * kq;
+    const u32x4 absmask = {0x7FFF7FFFu, 0x7FFF7FFFu, 0x7FFF7FFFu, 0x7FFF7FFFu};
+    f64x4 acc = {0, 0, 0, 0};
+    f32x4 aacc = {0, 0, 0, 0};
+    for (int c = 0; c < kq; c += 32) {  // kq % 8 == 0; up to four 8-element chunks in flight
+        u32x4 xa[4], wa[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if (c + 8 * u < kq) {
+                xa[u] = *reinterpret_cast<const u32x4*>(xp + c + 8 * u);
+                wa[u] = *reinterpret_cast<const u32x4*>(wp + c + 8 * u);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if (c + 8 * u >= kq) continue;
+            aacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa[u] & absmask),
+                                                           __builtin_bit_cast(bf16x8, wa[u] & absmask), aacc, 0, 0, 0);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)__uint_as_float(xa[u][q] << 16),
+                                                           (double)__uint_as_float(wa[u][q] << 16), acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)__uint_as_float(xa[u][q] & 0xFFFF0000u),
+                                                           (double)__uint_as_float(wa[u][q] & 0xFFFF0000u), acc, 0, 0,
+                                                           0);
+            }
+        }
+    }
+    // token row x weight row: the fp64 product leaves D[lane / 16 + 4 r][lane % 16]
+    // in register r, the bf16 one D[4 (lane / 16) + r][lane % 16]
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        part[wave][(grp + 4 * r) * 16 + i] = acc[r];
+        apart[wave][(grp * 4 + r) * 16 + i] = aacc[r];
+    }
+    __syncthreads();
+    const double es = (double)(H / 8 + 16) * 1.1102230246251565e-16;  // (H / 8 + 16) 2^-53
+    for (int q = threadIdx.x; q < 256; q += blockDim.x) {
+        const int64_t t = tok0 + q / 16;
+        const int e = e0 + q % 16;
+        if (t >= T || e >= n) continue;
+        double s = 0.0;
+        float a32 = 0.f;
+        for (int w = 0; w < kS64Waves; ++w) {
+            s += part[w][q];
+            a32 += apart[w][q];
+        }
+        const float b = bias ? bias[e] : 0.f;
+        const double sv = s + (double)b;
+        const double a = (double)a32 * (1.0 + 1.0 / 65536);
+        sc[t * n + e] = (float)sv;
+        bd[t * n + e] = (float)(es * (a + fabs((double)b)) + 0.5 * 1.1920928955078125e-07 * fabs(sv)) *
                         (1.0f + kTwoM23);
     }
 }
@@ -862,8 +955,12 @@ static hipError_t launch_select(const float* sc, const float* bd, const T* x, co
 hipError_t launch_scores(int dtype, const void* x, const void* W, const float* bias, int64_t Ttok, int H, int n,
                          float* sc, float* bd, hipStream_t st, int* zero, int n_zero) {
     if (dtype == kBF16 && H % 32 == 0) {
-        // few tokens: 16 weight rows per block, so the router spreads over more CUs
-        if (Ttok <= 256) {
+        // few tokens: exact-product scores, 16 weight rows per block
+        if (Ttok <= 256 && H % 256 == 0) {
+            dim3 grid((unsigned)((Ttok + 15) / 16), (unsigned)((n + 15) / 16));
+            scores64_kernel<<<grid, 64 * kS64Waves, 0, st>>>((const bf16_t*)x, (const bf16_t*)W, bias, Ttok, H, n,
+                                                             sc, bd, zero, n_zero);
+        } else if (Ttok <= 256) {
             dim3 grid((unsigned)((Ttok + 15) / 16), (unsigned)((n + 15) / 16));
             scores_kernel<16><<<grid, 64 * kScoreWaves, 0, st>>>((const bf16_t*)x, (const bf16_t*)W, bias, Ttok, H,
                                                                  n, sc, bd, zero, n_zero);
