@@ -36,6 +36,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 
 bool ok_ptr(const void* p) { return p != nullptr && aligned16(p); }
 bool ok_opt(const void* p) { return p == nullptr || aligned16(p); }
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+int64_t nb_of(int64_t T) { return mask_words(T); }  // 16-token router blocks
 
 int check_cfg(const moe_config* c) {
     if (!c) return MOE_ERR_INVALID;
@@ -111,17 +112,18 @@ struct LayerPlan {
     float* row_scale;
     GemmPlan gemm;
     void *hr, *hs, *ybuf;
-    // direct decode path: per-expert pair lists and h rows at e * T + slot
+    // direct decode path: the router's per-block pair lists, h rows at e * T + i
     bool direct;
-    int32_t* list;
+    int32_t *bcnt, *blist;
     void* hd;
 };
-// Small batches on the matrix-core path: routing writes per-expert lists and
-// the expert products tile themselves from them (no grouping launch).
+// Small batches on the matrix-core path: the router writes per-block pair
+// lists and the expert products tile themselves from them (no grouping launch).
+constexpr int64_t kDirectMaxT = 256;
 bool direct_ok(const moe_config* c, int64_t T, const GemmPlan& g) {
     const int E = c->num_experts, I = c->moe_intermediate_size;
-    return g.mfma && g.variant == kGemmSmallM && c->dtype == kBF16 && c->hidden_size % 32 == 0 &&
-           route_lists_ok(c->dtype, T, E, c->num_experts_per_tok) &&
+    return g.mfma && g.variant == kGemmSmallM && T <= kDirectMaxT &&
+           route_block_ok(c->dtype, c->hidden_size, E, c->num_experts_per_tok) &&
            (int64_t)E * T * I * (int64_t)esize(c->dtype) <= (64ll << 20);
 }
 void plan_layer(const moe_config* c, int64_t T, Carver& cv, LayerPlan& p) {
@@ -145,7 +147,9 @@ void plan_layer(const moe_config* c, int64_t T, Carver& cv, LayerPlan& p) {
     p.hs = cv.take<char>(T * Is * (int64_t)es);
     p.ybuf = cv.take<char>(T * (k + 1) * (int64_t)H * (int64_t)es);
     p.direct = direct_ok(c, T, p.gemm);
-    p.list = p.direct ? cv.take<int32_t>((int64_t)E * T) : nullptr;
+    const int64_t nb = mask_words(T);
+    p.bcnt = p.direct ? cv.take<int32_t>(nb * E) : nullptr;
+    p.blist = p.direct ? cv.take<int32_t>(nb * E * 16) : nullptr;
     p.hd = p.direct ? cv.take<char>((int64_t)E * T * I * (int64_t)es) : nullptr;
 }
 
@@ -427,18 +431,19 @@ int moe_layer_forward_timed(const moe_config* cfg, const moe_weights* w, const v
     TMOE_TRY(mark(0));
     auto ev = [&](int i) { return stage_events ? static_cast<hipEvent_t>(stage_events[i]) : nullptr; };
     if (p.direct) {
-        TMOE_TRY(launch_scores(cfg->dtype, x, w->router, w->router_bias, T, H, E, p.route.sc, p.route.bd, s, counts,
-                               E));
+        TMOE_TRY(launch_route_block(x, w->router, w->router_bias, T, H, E, k, cfg->norm_topk_prob, idx, wt, nullptr,
+                                    nullptr, p.bcnt, p.blist, s));
         TMOE_TRY(mark(1));
-        TMOE_TRY(launch_select_lists(cfg->dtype, p.route.sc, p.route.bd, x, w->router, w->router_bias, T, H, E, k,
-                                     cfg->norm_topk_prob, idx, wt, counts, p.list, s));
         TMOE_TRY(mark(2));
         int bm;
         GemmArgs a{};
         a.E = E;
-        a.direct_cnt = counts;
+        a.direct_bcnt = p.bcnt;
+        a.direct_blist = p.blist;
+        a.direct_nb = (int)nb_of(T);
+        a.direct_counts = counts;
         a.direct_T = (int)T;
-        a.g[0] = group(w->gate, w->up, (int64_t)I * H, I, H, x, H, p.list, p.hd, I, nullptr, 1, 0, nullptr);
+        a.g[0] = group(w->gate, w->up, (int64_t)I * H, I, H, x, H, nullptr, p.hd, I, nullptr, 1, 0, nullptr);
         a.g[0].a_div = k;
         a.g[1] = Is > 0 ? group(w->shared_gate, w->shared_up, 0, Is, H, x, H, nullptr, p.hs, Is, nullptr, 1, 0, nullptr)
                         : no_group();
@@ -448,7 +453,8 @@ int moe_layer_forward_timed(const moe_config* cfg, const moe_weights* w, const v
         a.direct_mt1 = (int)((T + bm - 1) / bm);
         TMOE_TRY(launch_grouped_gemm_direct(0, a, s, ev(6), ev(7)));
         TMOE_TRY(mark(3));
-        a.g[0] = group(w->down, nullptr, (int64_t)H * I, H, I, p.hd, I, nullptr, p.ybuf, H, p.list, 1, 0, wt);
+        a.direct_counts = nullptr;  // written by the gate/up pass
+        a.g[0] = group(w->down, nullptr, (int64_t)H * I, H, I, p.hd, I, nullptr, p.ybuf, H, nullptr, 1, 0, wt);
         a.g[0].out_div = k;
         a.g[0].scale_by_map = 1;
         a.g[1] = Is > 0 ? group(w->shared_down, nullptr, 0, H, Is, p.hs, Is, nullptr, p.ybuf, H, nullptr, slots, k,
@@ -465,7 +471,7 @@ int moe_layer_forward_timed(const moe_config* cfg, const moe_weights* w, const v
         TMOE_TRY(mark(5));
         return MOE_OK;
     }
-    if (route_group_small_ok(cfg->dtype, T, H, E, k)) {
+    if (!route_block_ok(cfg->dtype, H, E, k) && route_group_small_ok(cfg->dtype, T, H, E, k)) {
         // scores over many CUs, then selection and grouping in one block
         TMOE_TRY(launch_scores(cfg->dtype, x, w->router, w->router_bias, T, H, E, p.route.sc, p.route.bd, s));
         TMOE_TRY(mark(1));

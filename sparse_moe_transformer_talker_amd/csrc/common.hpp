@@ -121,6 +121,27 @@ __device__ __forceinline__ float wave_sum_dpp(float x) {
 #undef TMOE_SUM_STEP
     return __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(x), 63));
 }
+// fp64 sum over the wave (DPP on the two halves), returned to every lane.
+__device__ __forceinline__ double wave_sum_dpp_f64(double x) {
+#define TMOE_SUM64_STEP(CTRL, ROWS)                                                         \
+    {                                                                                       \
+        const uint64_t u = (uint64_t)__double_as_longlong(x);                               \
+        const uint32_t lo = __builtin_amdgcn_update_dpp(0u, (uint32_t)u, CTRL, ROWS, 0xf, false);         \
+        const uint32_t hi = __builtin_amdgcn_update_dpp(0u, (uint32_t)(u >> 32), CTRL, ROWS, 0xf, false); \
+        x += __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));                   \
+    }
+    TMOE_SUM64_STEP(kDppRowShr1, 0xf)
+    TMOE_SUM64_STEP(kDppRowShr2, 0xf)
+    TMOE_SUM64_STEP(kDppRowShr4, 0xf)
+    TMOE_SUM64_STEP(kDppRowShr8, 0xf)
+    TMOE_SUM64_STEP(kDppRowBcast15, 0xa)
+    TMOE_SUM64_STEP(kDppRowBcast31, 0xc)
+#undef TMOE_SUM64_STEP
+    const uint64_t u = (uint64_t)__double_as_longlong(x);
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)u, 63);
+    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(u >> 32), 63);
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
 __device__ __forceinline__ float wave_max_dpp(float x) {
     const uint32_t ninf = 0xFF800000u;
 #define TMOE_FMAX_STEP(CTRL, ROWS) \

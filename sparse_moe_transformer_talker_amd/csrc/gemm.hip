@@ -23,6 +23,10 @@
 
 namespace tmoe {
 
+// direct tiling: at most this many tokens (16-token router blocks)
+constexpr int kDirectMaxT = 256;
+constexpr int kDirectMaxBlocks = kDirectMaxT / 16;
+
 template <int PASS, int BM, int BN, int BK, int WM, int WN>
 __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs args) {
     constexpr int BROWS = (PASS == 0) ? 2 * BN : BN;
@@ -39,8 +43,11 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs args) {
     __shared__ __attribute__((aligned(16))) bf16_t As[BM * LDK];
     __shared__ __attribute__((aligned(16))) bf16_t Bs[BROWS * LDK];
 
-    // one tile: rows m0 .. m0 + mrows - 1 of group gi, columns n0 .. n0 + BN - 1
-    auto tile = [&](const int gi, const int e, const int n0, const int m0, const int mrows) {
+    // one tile: rows m0 .. m0 + mrows - 1 of group gi, columns n0 .. n0 + BN - 1;
+    // amap / omap (nullable) replace the group's A / output row maps, indexed
+    // by the row within the tile
+    auto tile = [&](const int gi, const int e, const int n0, const int m0, const int mrows, const int* amap,
+                    const int* omap) {
         const GemmGroup& g = args.g[gi];
         const int K = g.K;
         const int tid = threadIdx.x;
@@ -54,7 +61,8 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs args) {
             if (c >= NA) c = 0;
             int row = c / KC, kc = c % KC;
             int m = row < mrows ? row : 0;
-            int64_t grow = g.a_rows ? (int64_t)(g.a_rows[m0 + m] / g.a_div) : (int64_t)(m0 + m);
+            int64_t grow = amap ? (int64_t)(amap[m] / g.a_div)
+                                : (g.a_rows ? (int64_t)(g.a_rows[m0 + m] / g.a_div) : (int64_t)(m0 + m));
             pa[i] = (const bf16_t*)g.a + grow * g.a_ld + kc * 8;
         }
 #pragma unroll
@@ -135,7 +143,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs args) {
                 const int row = wm * TM + a * 16 + (lane >> 4) * 4 + r;
                 if (row >= mrows) continue;
                 const int64_t src = (int64_t)m0 + row;
-                const int64_t v = g.out_rows ? (int64_t)g.out_rows[src] : src;
+                const int64_t v = omap ? (int64_t)omap[row] : (g.out_rows ? (int64_t)g.out_rows[src] : src);
                 const int64_t dst = v * g.out_mul + g.out_add + (g.out_div > 0 ? v / g.out_div : 0);
                 const float sc = (PASS == 1 && g.out_scale) ? g.out_scale[g.scale_by_map ? v : src] : 1.0f;
 #pragma unroll
@@ -154,7 +162,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs args) {
     };
 
     const int p = blockIdx.x;
-    if (args.direct_cnt) {
+    if (args.direct_bcnt) {
         const int nt0 = args.direct_nt[0];
         const int n_routed = args.E * nt0;
         const int n_all = n_routed + args.direct_nt[1] * args.direct_mt1;
@@ -164,14 +172,33 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs args) {
         int q = (p & 7) * chunk + slot;
         if (q >= n_all) return;
         if (q < n_routed) {
+            // this expert's pairs: the per-block lists concatenated in block order
+            __shared__ int rl[kDirectMaxT];
+            __shared__ int boff[kDirectMaxBlocks + 1], bc[kDirectMaxBlocks];
             const int e = q / nt0, n0 = (q % nt0) * BN;
-            const int m = args.direct_cnt[e];
+            const int nb = args.direct_nb;
+            if (threadIdx.x < kWave) {
+                const int lane = threadIdx.x;
+                const int c = lane < nb ? args.direct_bcnt[lane * args.E + e] : 0;
+                const int incl = wave_incl_scan(c);
+                if (lane < nb) { boff[lane] = incl - c; bc[lane] = c; }
+                if (lane == kWave - 1) boff[kDirectMaxBlocks] = incl;
+            }
+            __syncthreads();
+            for (int i = threadIdx.x; i < nb * 16; i += blockDim.x) {
+                const int b = i >> 4, s = i & 15;
+                if (s < bc[b]) rl[boff[b] + s] = args.direct_blist[((int64_t)b * args.E + e) * 16 + s];
+            }
+            __syncthreads();
+            const int m = boff[kDirectMaxBlocks];
+            if (n0 == 0 && threadIdx.x == 0 && args.direct_counts) args.direct_counts[e] = m;
             const int base = e * args.direct_T;
-            for (int m0 = 0; m0 < m; m0 += BM) tile(0, e, n0, base + m0, min(BM, m - m0));
+            for (int m0 = 0; m0 < m; m0 += BM)
+                tile(0, e, n0, base + m0, min(BM, m - m0), PASS == 0 ? rl + m0 : nullptr, PASS == 1 ? rl + m0 : nullptr);
         } else {
             q -= n_routed;
             const int n0 = (q / args.direct_mt1) * BN, m0 = (q % args.direct_mt1) * BM;
-            tile(1, 0, n0, m0, min(BM, args.direct_T - m0));
+            tile(1, 0, n0, m0, min(BM, args.direct_T - m0), nullptr, nullptr);
         }
         return;
     }
@@ -183,7 +210,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs args) {
     if (q >= n_items) return;
     const int4 it = args.items[q];
     const int gi = it.x < args.E ? 0 : 1;
-    tile(gi, gi == 0 ? it.x : 0, it.y, it.z, it.w);
+    tile(gi, gi == 0 ? it.x : 0, it.y, it.z, it.w, nullptr, nullptr);
 }
 
 // ---------------------------------------------------------------------------

@@ -32,16 +32,17 @@ hipError_t launch_select_group_small(const float* sc, const float* bd, const voi
                                      float* w, int32_t* counts, int32_t* offsets, int32_t* row_token,
                                      int32_t* row_of, int32_t* row_dst, float* row_scale, int slots,
                                      const TileSpec* t1, const TileSpec* t2, hipStream_t st);
-// zero (nullable): n_zero ints cleared before any later launch on the stream
 hipError_t launch_scores(int dtype, const void* x, const void* W, const float* bias, int64_t T, int H, int n,
-                         float* sc, float* bd, hipStream_t st, int* zero = nullptr, int n_zero = 0);
-// Small batches (T <= 256, E <= 128, k <= 16): selection from launch_scores'
-// output, appending pair t * k + j to list[e * T + slot] with slot from cnt[e]
-// (cnt cleared by launch_scores).  Row order within a list is arbitrary.
-bool route_lists_ok(int dtype, int64_t T, int E, int k);
-hipError_t launch_select_lists(int dtype, const float* sc, const float* bd, const void* x, const void* W,
-                               const float* bias, int64_t T, int H, int E, int k, int norm, int32_t* idx, float* w,
-                               int* cnt, int* list, hipStream_t st);
+                         float* sc, float* bd, hipStream_t st);
+// bf16, E in {16, 32, 64, 128}, H <= 1024 a multiple of 128 (8 / (E / 16)), k <= 16: scores and
+// selection in one launch (one block per 16 tokens).  Writes masks (nullable,
+// as launch_route), or per block b of 16 tokens and expert e the count
+// bcnt[b * E + e] and the pairs t * k + j in blist[(b * E + e) * 16 + i]
+// (bcnt / blist nullable; order inside a block's list is arbitrary).
+bool route_block_ok(int dtype, int H, int E, int k);
+hipError_t launch_route_block(const void* x, const void* W, const float* bias, int64_t T, int H, int E, int k,
+                              int norm, int32_t* idx, float* w, float* probs, uint16_t* masks, int32_t* bcnt,
+                              int32_t* blist, hipStream_t st);
 hipError_t launch_argmax(int dtype, const float* sc, const float* bd, const void* x, const void* W, int64_t T, int H,
                          int n, int32_t* out, hipStream_t st);
 
@@ -91,11 +92,18 @@ struct GemmArgs {
     const int4* items;
     const int* count;
     int E;
-    // Direct tiling (when direct_cnt is not null; small-M kernel only): the grid
+    // Direct tiling (when direct_bcnt is not null; small-M kernel only): the grid
     // is E * direct_nt[0] routed tiles, expert-major, then direct_nt[1] x
-    // direct_mt1 shared tiles.  A routed tile covers rows e * direct_T ..
-    // e * direct_T + direct_cnt[e] - 1 of group 0 in chunks of the tile height.
-    const int* direct_cnt;
+    // direct_mt1 shared tiles.  A routed tile of expert e concatenates the
+    // router's per-block pair lists (direct_bcnt / direct_blist of
+    // launch_route_block, direct_nb blocks) into its m rows, which are rows
+    // e * direct_T .. e * direct_T + m - 1 of its h buffer; in the gate/up pass
+    // the pair p gives A row p / a_div, in the down pass output row p (with the
+    // scale of p).  Tiles of column 0 write m to direct_counts[e] (nullable).
+    const int* direct_bcnt;
+    const int* direct_blist;
+    int direct_nb;
+    int* direct_counts;
     int direct_T;
     int direct_nt[2];
     int direct_mt1;

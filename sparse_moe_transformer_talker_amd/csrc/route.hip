@@ -29,8 +29,27 @@ __device__ __forceinline__ double partial_error_scale() { return 33.0 * 1.192092
 __device__ __forceinline__ double fp64_error_scale(int H) { return (double)(H / 32 + 8) * 2.220446049250313e-16; }
 
 // ---------------------------------------------------------------------------
+// The next (up to) eight set bits of a wave-uniform mask m (m != 0), as
+// indices base + bit in ids[0..8); slots past the count repeat the last index.
+// Returns the count.  Static indexing keeps ids in registers.
+__device__ __forceinline__ int take8(uint64_t& m, int base, int* ids) {
+    int cnt = 0;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        if (m) {
+            ids[q] = base + (__ffsll((unsigned long long)m) - 1);
+            m &= m - 1;
+            cnt = q + 1;
+        } else {
+            ids[q] = ids[q > 0 ? q - 1 : 0];
+        }
+    }
+    return cnt;
+}
+
 // fp64 rescoring of up to N candidates at once: dot(x_row, W[e_i]) over H,
-// wave-cooperative, all 16-byte loads of a chunk issued before use.
+// wave-cooperative, all 16-byte loads of a chunk issued before use.  Every
+// e[0..N) is a valid row (entries past n are loaded and ignored).
 template <typename T, int N>
 __device__ void wave_dot64(const T* __restrict__ xr, const T* __restrict__ W, int H, const int* e, int n,
                            double* out) {
@@ -43,8 +62,7 @@ __device__ void wave_dot64(const T* __restrict__ xr, const T* __restrict__ W, in
             const u32x4 xv = *reinterpret_cast<const u32x4*>(xr + c * V);
             u32x4 wv[N];
 #pragma unroll
-            for (int i = 0; i < N; ++i)
-                if (i < n) wv[i] = *reinterpret_cast<const u32x4*>(W + (int64_t)e[i] * H + c * V);
+            for (int i = 0; i < N; ++i) wv[i] = *reinterpret_cast<const u32x4*>(W + (int64_t)e[i] * H + c * V);
 #pragma unroll
             for (int i = 0; i < N; ++i) {
                 if (i >= n) continue;
@@ -70,7 +88,7 @@ __device__ void wave_dot64(const T* __restrict__ xr, const T* __restrict__ W, in
         }
     }
 #pragma unroll
-    for (int i = 0; i < N; ++i) out[i] = wave_sum(acc[i]);
+    for (int i = 0; i < N; ++i) out[i] = wave_sum_dpp_f64(acc[i]);
 }
 
 // Per-wave selection state in LDS.
@@ -154,11 +172,8 @@ __device__ __noinline__ void exact_select_row(const S* s, const float* d, int n,
         for (int j = 0; j < MAXJ; ++j) {
             uint64_t m = __ballot(cand[j]);
             while (m) {
-                int ids[8], cnt = 0;
-                while (m && cnt < 8) {
-                    ids[cnt++] = (__ffsll((unsigned long long)m) - 1) + kWave * j;
-                    m &= m - 1;
-                }
+                int ids[8];
+                const int cnt = take8(m, kWave * j, ids);
                 double r8[8];
                 wave_dot64<T, 8>(xrow, W, H, ids, cnt, r8);
 #pragma unroll
@@ -248,12 +263,23 @@ struct RowPicks {
     int idx[4][16];
 };
 
+// Tokens of a block whose fp32 selection was not certain, left for a later
+// exact pass: token within the block and the lowest bound of its fp32 picks.
+struct Deferred {
+    int n;
+    int tok[16];
+    double low[16];
+};
+
 // Scores of token t are sc[(t - tbase) * n + e] (fp32 in global memory or fp64 in LDS).
-template <typename T, int J, typename S>
+// DEFER: uncertain rows are appended to *dfr (nothing recorded for them) instead
+// of being redone here.
+template <typename T, int J, typename S, bool DEFER = false>
 __device__ __forceinline__ void select_rows_wave(const S* __restrict__ sc, const float* __restrict__ bd, int64_t tbase, int64_t t, int n, int k,
                                  const T* __restrict__ x, const T* __restrict__ W, int H, const float* bias, int norm,
                                  int32_t* out_idx, float* out_w, float* out_probs, uint32_t* mask, int mstride,
-                                 int word_of_row0, RowPicks& pk, SelScratch* scr, ListSink ls = ListSink{}) {
+                                 int word_of_row0, RowPicks& pk, SelScratch* scr, ListSink ls = ListSink{},
+                                 Deferred* dfr = nullptr) {
     const int lane = lane_id();
     const int row = lane >> 4, ri = lane & 15;
     const bool valid = t >= 0;
@@ -343,6 +369,14 @@ __device__ __forceinline__ void select_rows_wave(const S* __restrict__ sc, const
             if (ls.cnt) ls.list[e * ls.lstride + atomicAdd(&ls.cnt[e], 1)] = (int)(t * k + ri);
         }
     }
+    if (DEFER) {
+        if (valid && !certain && ri == 0) {
+            const int u = atomicAdd(&dfr->n, 1);
+            dfr->tok[u] = (int)(t - tbase);
+            dfr->low[u] = low;
+        }
+        return;
+    }
     // rows left uncertain: the whole wave redoes them with fp64 rescoring
     uint64_t redo = __ballot(valid && !certain && ri == 0);
     while (redo) {
@@ -371,12 +405,8 @@ __global__ __launch_bounds__(64 * kScoreWaves) void scores_kernel(const bf16_t* 
                                                                   const bf16_t* __restrict__ W,
                                                                   const float* __restrict__ bias, int64_t T, int H,
                                                                   int n, float* __restrict__ sc,
-                                                                  float* __restrict__ bd, int* __restrict__ clear,
-                                                                  int n_clear) {
+                                                                  float* __restrict__ bd) {
     constexpr bool two = kScoreRows == 32;
-    // clear the per-expert list counters that the selection after this launch fills
-    if (clear && blockIdx.x == 0 && blockIdx.y == 0)
-        for (int q = threadIdx.x; q < n_clear; q += blockDim.x) clear[q] = 0;
     __shared__ double lg[16 * kScoreRows];
     __shared__ float ab[16 * kScoreRows];
     const int wave = threadIdx.x >> 6;
@@ -400,14 +430,13 @@ __global__ __launch_bounds__(64 * kScoreWaves) void scores_kernel(const bf16_t* 
     const int nsteps = H / 32;
     for (int c0 = wave; c0 < nsteps; c0 += 4 * kScoreWaves) {
         u32x4 a[4], b0[4], b1[4];
+        // branch-free loads (steps past the end repeat the last one, unused)
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const int st = c0 + u * kScoreWaves;
-            if (st < nsteps) {
-                a[u] = *reinterpret_cast<const u32x4*>(xp + st * 32);
-                b0[u] = *reinterpret_cast<const u32x4*>(w0 + st * 32);
-                if (two) b1[u] = *reinterpret_cast<const u32x4*>(w1 + st * 32);
-            }
+            const int st = min(c0 + u * kScoreWaves, nsteps - 1);
+            a[u] = *reinterpret_cast<const u32x4*>(xp + st * 32);
+            b0[u] = *reinterpret_cast<const u32x4*>(w0 + st * 32);
+            if (two) b1[u] = *reinterpret_cast<const u32x4*>(w1 + st * 32);
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
@@ -479,12 +508,9 @@ __global__ __launch_bounds__(64 * kS64Waves) void scores64_kernel(const bf16_t* 
                                                                   const bf16_t* __restrict__ W,
                                                                   const float* __restrict__ bias, int64_t T, int H,
                                                                   int n, float* __restrict__ sc,
-                                                                  float* __restrict__ bd, int* __restrict__ clear,
-                                                                  int n_clear) {
+                                                                  float* __restrict__ bd) {
     __shared__ double part[kS64Waves][256];
     __shared__ float apart[kS64Waves][256];
-    if (clear && blockIdx.x == 0 && blockIdx.y == 0)
-        for (int q = threadIdx.x; q < n_clear; q += blockDim.x) clear[q] = 0;
     const int wave = threadIdx.x >> 6, lane = lane_id();
     const int i = lane & 15, grp = lane >> 4;
     const int64_t tok0 = (int64_t)blockIdx.x * 16;
@@ -500,11 +526,10 @@ __global__ __launch_bounds__(64 * kS64Waves) void scores64_kernel(const bf16_t* 
     for (int c = 0; c < kq; c += 32) {  // kq % 8 == 0; up to four 8-element chunks in flight
         u32x4 xa[4], wa[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            if (c + 8 * u < kq) {
-                xa[u] = *reinterpret_cast<const u32x4*>(xp + c + 8 * u);
-                wa[u] = *reinterpret_cast<const u32x4*>(wp + c + 8 * u);
-            }
+        for (int u = 0; u < 4; ++u) {  // branch-free: chunks past the end repeat the last one, unused
+            const int cu = min(c + 8 * u, kq - 8);
+            xa[u] = *reinterpret_cast<const u32x4*>(xp + cu);
+            wa[u] = *reinterpret_cast<const u32x4*>(wp + cu);
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
@@ -550,110 +575,273 @@ __global__ __launch_bounds__(64 * kS64Waves) void scores64_kernel(const bf16_t* 
 }
 
 // ---------------------------------------------------------------------------
-// Fused router for bf16, E = NS * 16 in {16, 32, 64, 128}, H % 32 == 0: one block of 16
-// waves per 16 tokens scores all experts and selects, so the scores never
-// leave LDS.  Waves are split into KG K-groups x EG expert groups (each wave
-// two 16-expert subtiles when NS >= 2); a wave issues the loads of up to 4 of
-// its 32-wide K steps at once and adds every step's fp32 partial into fp64.
-// K-groups are reduced in LDS in fixed order.  Waves 0..3 then select four
-// tokens each (row groups) and the block writes its mask word of every expert.
-constexpr int kFusedWaves = 16;
+// Router for bf16 with E = 16 NS experts (NS in {1, 2, 4, 8}), H a multiple of
+// 128 (8 / NS), H <= 1024, k <= 16: one block of 8 waves per 16 tokens; scores never
+// leave LDS.
+//   scores: the block stages its 16 token rows in LDS.  Wave w scores expert
+//     tile w % NS over the stages s (128 K-elements each) with s % (8 / NS) ==
+//     w / NS, streaming its own 16 W_r rows through a private LDS slice: lanes
+//     load whole 256-byte row slices (four rows per instruction; reading the
+//     matrix-core fragment shape, 16 rows x 64 bytes per instruction, straight
+//     from memory streams several times slower), DEPTH stages in flight in
+//     registers, and no block barrier in the loop.  Staged rows are padded by
+//     16 bytes, so fragment reads are free of bank conflicts.  Every bf16
+//     matrix-core step (32 exact products summed in fp32) is a fresh partial
+//     added into fp64, beside the abs-sum that bounds the error; the K groups
+//     are added in LDS in a fixed order (deterministic).
+//   selection: waves 0..3 select four tokens each, one per 16-lane row
+//     (select_rows_wave: certified fp32 ranking); tokens left uncertain are
+//     then taken by the eight waves in parallel, one each, with fp64
+//     rescoring of their candidates (route_exact_token).
+//   outputs: idx / weights (/ probs); per (expert, 16-token block) a token mask
+//     (masks != null), or per block and expert the count and list of its pairs
+//     t * k + j (bcnt != null; list order within a block is arbitrary).
+constexpr int kRouteWaves = 8;
+constexpr int kRouteThreads = 64 * kRouteWaves;
+constexpr int kRouteMaxH = 1024;
+constexpr int kRouteStageK = 128;  // K-elements per W_r stage
 
-template <int NS>
-__global__ __launch_bounds__(64 * kFusedWaves) void route_fused_kernel(
+// Exact Top-k of one token whose fp32 selection was not certain.  Every score
+// that may reach the fp32 picks (s + d >= low, the picks included) is rescored
+// in fp64 (bf16 products are exact there), and the k best are taken by value,
+// ties to the lower index: every expert of the exact Top-k is among these
+// candidates, because the k picks all have exact scores >= low.  One full wave;
+// lane r < k writes pick r.  Lists: lcnt (nullable) / llist as in the router.
+template <int J>
+__device__ void route_exact_token(const double* s, const float* d, int E, int k, int norm, double low,
+                                  const bf16_t* xrow, const bf16_t* W, int H, const float* bias, int32_t* oidx,
+                                  float* ow, float* oprob, uint32_t* msk, int bit, int* lcnt, int* llist, int pair0) {
+    const int lane = lane_id();
+    float v[J];
+    bool cand[J];
+    double v64[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        const int e = lane + kWave * j;
+        const bool ok = e < E;
+        v[j] = ok ? (float)s[e] + 0.0f : 0.0f;
+        const double dv = ok ? (double)d[e] + 1.1920928955078125e-07 * fabs((double)v[j]) : 0.0;
+        cand[j] = ok && (double)v[j] + dv >= low;
+        v64[j] = 0.0;
+    }
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        uint64_t cm = __ballot(cand[j]);
+        while (cm) {
+            int ids[8];
+            const int cnt = take8(cm, kWave * j, ids);
+            double r8[8];
+            wave_dot64<bf16_t, 8>(xrow, W, H, ids, cnt, r8);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                if (i < cnt && lane + kWave * j == ids[i]) v64[j] = r8[i] + (bias ? (double)bias[ids[i]] : 0.0);
+        }
+    }
+    int my_e = 0;
+    double my_s = 0.0;
+    for (int r = 0; r < k; ++r) {
+        uint64_t m = 0;
+#pragma unroll
+        for (int j = 0; j < J; ++j)
+            if (cand[j]) {
+                const uint64_t kk = double_order_key(v64[j]);
+                m = kk > m ? kk : m;
+            }
+        m = wave_max_key(m);
+        uint64_t ik = 0;
+#pragma unroll
+        for (int j = 0; j < J; ++j)
+            if (cand[j] && double_order_key(v64[j]) == m) {
+                const uint64_t c = 0xFFFFFFFFull - (uint64_t)(lane + kWave * j);
+                ik = c > ik ? c : ik;
+            }
+        ik = wave_max_key(ik);
+        const int bi = (int)(0xFFFFFFFFull - ik);
+#pragma unroll
+        for (int j = 0; j < J; ++j)
+            if (lane + kWave * j == bi) cand[j] = false;
+        if (lane == r) {
+            my_e = bi;
+            my_s = double_from_order_key(m);
+        }
+    }
+    // softmax statistics over all E in fp32 (probs, and the plain weights)
+    float mx = 0.f, z = 1.f;
+    if (oprob || !norm) {
+        mx = -3.0e38f;
+#pragma unroll
+        for (int j = 0; j < J; ++j)
+            if (lane + kWave * j < E) mx = fmaxf(mx, v[j]);
+        mx = wave_max_dpp(mx);
+        z = 0.f;
+#pragma unroll
+        for (int j = 0; j < J; ++j)
+            if (lane + kWave * j < E) z += __expf(v[j] - mx);
+        z = wave_sum_dpp(z);
+        if (oprob) {
+            const float inv = 1.0f / z;
+#pragma unroll
+            for (int j = 0; j < J; ++j)
+                if (lane + kWave * j < E) oprob[lane + kWave * j] = __expf(v[j] - mx) * inv;
+        }
+    }
+    const double s0 = __shfl(my_s, 0, kWave);
+    const float ex = lane < k ? (norm ? (float)exp(my_s - s0) : __expf((float)my_s - mx)) : 0.f;
+    const float den = norm ? wave_sum_dpp(ex) : z;
+    if (lane < k) {
+        oidx[lane] = my_e;
+        ow[lane] = ex / den;
+        atomicOr(&msk[my_e], 1u << bit);
+        if (lcnt) llist[my_e * 16 + atomicAdd(&lcnt[my_e], 1)] = pair0 + lane;
+    }
+}
+
+template <int NS, int DEPTH>
+__global__ __launch_bounds__(kRouteThreads) void route_block_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ W, const float* __restrict__ bias, int64_t T, int H,
-    int E, int k, int norm, int32_t* __restrict__ out_idx, float* __restrict__ out_w, float* __restrict__ out_probs,
-    uint16_t* __restrict__ masks, int mstride) {
-    constexpr int LD = NS * 16;
-    constexpr int SPW = NS >= 2 ? 2 : 1;  // 16-expert subtiles per wave
-    constexpr int EG = NS / SPW;          // expert groups
-    constexpr int KG = kFusedWaves / EG;  // K groups
-    __shared__ double lg[16 * LD];
-    __shared__ float ab[16 * LD];
+    int k, int norm, int32_t* __restrict__ out_idx, float* __restrict__ out_w, float* __restrict__ out_probs,
+    uint16_t* __restrict__ masks, int mstride, int32_t* __restrict__ bcnt, int32_t* __restrict__ blist) {
+    constexpr int E = NS * 16;
+    constexpr int KG = kRouteWaves / NS;                        // K groups per expert tile
+    constexpr int XCH = 16 * (kRouteMaxH / 8) / kRouteThreads;  // staged x chunks per thread (max)
+    constexpr int SLD = kRouteStageK + 8;                       // bf16 per staged W_r row (272 bytes)
+    constexpr int WI = 16 * kRouteStageK / 8 / kWave;           // load instructions per stage and wave (4)
+    __shared__ __attribute__((aligned(16))) bf16_t xs[16 * (kRouteMaxH + 8)];
+    __shared__ __attribute__((aligned(16))) bf16_t wsb[kRouteWaves][16 * SLD];
+    __shared__ double lg[16 * E];
+    __shared__ float ab[16 * E];
+    __shared__ uint32_t msk[E];
+    __shared__ int lcnt[E];
+    __shared__ int llist[E * 16];
     __shared__ RowPicks picks[4];
     __shared__ SelScratch scr[4];
-    __shared__ uint32_t msk[LD];
-    const int wave = threadIdx.x >> 6, lane = lane_id();
-    const int kg = wave % KG, eg = wave / KG;
-    const int i = lane & 15, kq = (lane >> 4) * 8;
+    __shared__ Deferred dfr;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int64_t tok0 = (int64_t)blockIdx.x * 16;
-    for (int q = threadIdx.x; q < LD; q += blockDim.x) msk[q] = 0;
-    int64_t tok = tok0 + i;
-    if (tok >= T) tok = T - 1;
-    const bf16_t* xp = x + tok * (int64_t)H + kq;
-    const bf16_t* wp[SPW];
+    const int XLD = H + 8;
+    const int tile = wave % NS, g = wave / NS;
+    const int nmine = H / (kRouteStageK * KG);  // this wave's stages g, g + KG, ...; a multiple of DEPTH
+
+    // stage m of this wave: lane l loads row 4 j + l / 16, 16-byte chunk l % 16
+    // of K-slice st = g + m KG of rows tile * 16 .. + 15
+    const bf16_t* wsrc = W + (int64_t)(tile * 16 + (lane >> 4)) * H + (lane & 15) * 8;
+    auto wload = [&](int m, u32x4* r) {
+        const int st = g + m * KG;
 #pragma unroll
-    for (int s = 0; s < SPW; ++s) wp[s] = W + (int64_t)((eg * SPW + s) * 16 + i) * H + kq;
+        for (int j = 0; j < WI; ++j)
+            r[j] = *reinterpret_cast<const u32x4*>(wsrc + (int64_t)(4 * j) * H + st * kRouteStageK);
+    };
+    u32x4 wr[DEPTH][WI];
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) wload(d, wr[d]);
+
+    if (tid == 0) dfr.n = 0;
+    for (int q = tid; q < E; q += blockDim.x) {
+        msk[q] = 0;
+        lcnt[q] = 0;
+    }
+    // stage the block's token rows (rows past T repeat row T - 1; never used):
+    // every load first, then the LDS stores
+    {
+        const int cpr = H / 8, n = 16 * cpr;
+        u32x4 v[XCH];
+#pragma unroll
+        for (int j = 0; j < XCH; ++j) {
+            const int c = min(tid + j * kRouteThreads, n - 1);
+            const int r = c / cpr, q = c % cpr;
+            const int64_t t = tok0 + r < T ? tok0 + r : T - 1;
+            v[j] = *reinterpret_cast<const u32x4*>(x + t * H + q * 8);
+        }
+#pragma unroll
+        for (int j = 0; j < XCH; ++j) {
+            const int c = tid + j * kRouteThreads;
+            if (c < n) *reinterpret_cast<u32x4*>(&xs[(c / cpr) * XLD + (c % cpr) * 8]) = v[j];
+        }
+    }
+    __syncthreads();
+
+    const int i = lane & 15, kq = (lane >> 4) * 8;
+    const bf16_t* xr = &xs[i * XLD + kq];
+    bf16_t* wb = wsb[wave];
+    const int wst = (lane >> 4) * SLD + (lane & 15) * 8;  // this lane's store slot (row 4 j + lane / 16)
+    const bf16_t* wfr = &wb[i * SLD + kq];               // fragment: row i, k offset kq
     const u32x4 absmask = {0x7FFF7FFFu, 0x7FFF7FFFu, 0x7FFF7FFFu, 0x7FFF7FFFu};
     const f32x4 zero = {0, 0, 0, 0};
-    double acc[SPW][4];
-    f32x4 aacc[SPW];
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};
+    f32x4 aacc = zero;
+    for (int m0 = 0; m0 < nmine; m0 += DEPTH) {
 #pragma unroll
-    for (int s = 0; s < SPW; ++s) {
-        aacc[s] = zero;
+        for (int d = 0; d < DEPTH; ++d) {
+            const int m = m0 + d;
+            // the wave's own LDS slice: its earlier fragment reads are ordered
+            // before these stores
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[s][r] = 0.0;
-    }
-    const int nsteps = H / 32;
-    for (int c0 = kg; c0 < nsteps; c0 += 4 * KG) {
-        u32x4 a[4], b[4][SPW];
+            for (int j = 0; j < WI; ++j) *reinterpret_cast<u32x4*>(&wb[wst + 4 * j * SLD]) = wr[d][j];
+            wload(min(m + DEPTH, nmine - 1), wr[d]);  // past the end: the last stage again, unused
+            const int k0 = (g + m * KG) * kRouteStageK;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int st = c0 + u * KG;
-            if (st < nsteps) {
-                a[u] = *reinterpret_cast<const u32x4*>(xp + st * 32);
+            for (int ks = 0; ks < kRouteStageK; ks += 32) {
+                const u32x4 a = *reinterpret_cast<const u32x4*>(xr + k0 + ks);
+                const u32x4 b = *reinterpret_cast<const u32x4*>(wfr + ks);
+                const f32x4 p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), zero, 0, 0, 0);
+                aacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a & absmask),
+                                                               __builtin_bit_cast(bf16x8, b & absmask), aacc, 0, 0,
+                                                               0);
 #pragma unroll
-                for (int s = 0; s < SPW; ++s) b[u][s] = *reinterpret_cast<const u32x4*>(wp[s] + st * 32);
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            if (c0 + u * KG >= nsteps) continue;
-            const bf16x8 av = __builtin_bit_cast(bf16x8, a[u]);
-            const bf16x8 aav = __builtin_bit_cast(bf16x8, a[u] & absmask);
-#pragma unroll
-            for (int s = 0; s < SPW; ++s) {
-                const f32x4 p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, b[u][s]), zero,
-                                                                        0, 0, 0);
-                aacc[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aav, __builtin_bit_cast(bf16x8, b[u][s] & absmask),
-                                                                  aacc[s], 0, 0, 0);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) acc[s][r] += (double)p[r];
+                for (int r = 0; r < 4; ++r) acc[r] += (double)p[r];
             }
         }
     }
-    // D[row = 4*(lane/16) + r][col = lane%16] per 16x16 block; K-groups in order
-    for (int g = 0; g < KG; ++g) {
-        if (kg == g) {
+    // D[token 4 (lane / 16) + r][expert lane % 16] per tile; K groups added in order
 #pragma unroll
-            for (int s = 0; s < SPW; ++s)
+    for (int gg = 0; gg < KG; ++gg) {
+        if (g == gg) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int q = ((lane >> 4) * 4 + r) * LD + (eg * SPW + s) * 16 + i;
-                    if (g == 0) { lg[q] = acc[s][r]; ab[q] = aacc[s][r]; }
-                    else { lg[q] += acc[s][r]; ab[q] += aacc[s][r]; }
-                }
+            for (int r = 0; r < 4; ++r) {
+                const int q = ((lane >> 4) * 4 + r) * E + tile * 16 + i;
+                if (gg == 0) { lg[q] = acc[r]; ab[q] = aacc[r]; }
+                else { lg[q] += acc[r]; ab[q] += aacc[r]; }
+            }
         }
         __syncthreads();
     }
     const double es = partial_error_scale(), fs = fp64_error_scale(H);
-    for (int q = threadIdx.x; q < 16 * LD; q += blockDim.x) {
-        const int e = q % LD;
-        const float b = bias ? bias[e] : 0.f;
-        const double sv = lg[q] + (double)b;
+    for (int q = tid; q < 16 * E; q += blockDim.x) {
+        const int e = q % E;
+        const float bb = bias ? bias[e] : 0.f;
+        const double sv = lg[q] + (double)bb;
         lg[q] = sv;
         const double a = (double)ab[q];
-        ab[q] = (float)(es * a + fs * (a + fabs((double)b))) * (1.0f + kTwoM23);
+        ab[q] = (float)(es * a + fs * (a + fabs((double)bb))) * (1.0f + kTwoM23);
     }
     __syncthreads();
+
     if (wave < 4) {
         const int64_t t = tok0 + wave * 4 + (lane >> 4);
-        select_rows_wave<bf16_t, NS, double>(lg, ab, tok0, t < T ? t : -1, E, k, x, W, H, bias, norm, out_idx, out_w,
-                                              out_probs, msk, 1, 0, picks[wave], &scr[wave]);
+        select_rows_wave<bf16_t, NS, double, true>(lg, ab, tok0, t < T ? t : -1, E, k, x, W, H, bias, norm, out_idx,
+                                                   out_w, out_probs, msk, 1, 0, picks[wave], &scr[wave],
+                                                   bcnt ? ListSink{lcnt, llist, 16} : ListSink{}, &dfr);
     }
-    if (masks) {
-        __syncthreads();
-        for (int e = threadIdx.x; e < E; e += blockDim.x) masks[(int64_t)e * mstride + blockIdx.x] = (uint16_t)msk[e];
+    __syncthreads();
+    // uncertain tokens: one wave each
+    for (int u = wave; u < dfr.n; u += kRouteWaves) {
+        const int tt = dfr.tok[u];
+        const int64_t t = tok0 + tt;
+        route_exact_token<(E + kWave - 1) / kWave>(&lg[tt * E], &ab[tt * E], E, k, norm, dfr.low[u], x + t * H, W, H,
+                                                   bias, out_idx + t * k, out_w + t * k,
+                                                   out_probs ? out_probs + t * E : nullptr, msk, tt,
+                                                   bcnt ? lcnt : nullptr, llist, (int)(t * k));
+    }
+    __syncthreads();
+    if (masks)
+        for (int e = tid; e < E; e += blockDim.x) masks[(int64_t)e * mstride + blockIdx.x] = (uint16_t)msk[e];
+    if (bcnt) {
+        int32_t* cnt_b = bcnt + (int64_t)blockIdx.x * E;
+        int32_t* list_b = blist + (int64_t)blockIdx.x * E * 16;
+        for (int e = tid; e < E; e += blockDim.x) cnt_b[e] = lcnt[e];
+        for (int q = tid; q < E * 16; q += blockDim.x)
+            if ((q & 15) < lcnt[q >> 4]) list_b[q] = llist[q];
     }
 }
 
@@ -906,11 +1094,8 @@ __global__ __launch_bounds__(256) void argmax_exact_kernel(const float* __restri
             const bool c = e < n && (double)s[e] + (double)d[e] >= low;
             uint64_t m = __ballot(c);
             while (m) {
-                int ids[8], cnt = 0;
-                while (m && cnt < 8) {
-                    ids[cnt++] = base + __ffsll((unsigned long long)m) - 1;
-                    m &= m - 1;
-                }
+                int ids[8];
+                const int cnt = take8(m, base, ids);
                 double r8[8];
                 wave_dot64<T, 8>(xr, W, H, ids, cnt, r8);
                 for (int i = 0; i < cnt; ++i)
@@ -953,27 +1138,23 @@ static hipError_t launch_select(const float* sc, const float* bd, const T* x, co
 }
 
 hipError_t launch_scores(int dtype, const void* x, const void* W, const float* bias, int64_t Ttok, int H, int n,
-                         float* sc, float* bd, hipStream_t st, int* zero, int n_zero) {
+                         float* sc, float* bd, hipStream_t st) {
     if (dtype == kBF16 && H % 32 == 0) {
         // few tokens: exact-product scores, 16 weight rows per block
         if (Ttok <= 256 && H % 256 == 0) {
             dim3 grid((unsigned)((Ttok + 15) / 16), (unsigned)((n + 15) / 16));
             scores64_kernel<<<grid, 64 * kS64Waves, 0, st>>>((const bf16_t*)x, (const bf16_t*)W, bias, Ttok, H, n,
-                                                             sc, bd, zero, n_zero);
+                                                             sc, bd);
         } else if (Ttok <= 256) {
             dim3 grid((unsigned)((Ttok + 15) / 16), (unsigned)((n + 15) / 16));
             scores_kernel<16><<<grid, 64 * kScoreWaves, 0, st>>>((const bf16_t*)x, (const bf16_t*)W, bias, Ttok, H,
-                                                                 n, sc, bd, zero, n_zero);
+                                                                 n, sc, bd);
         } else {
             dim3 grid((unsigned)((Ttok + 15) / 16), (unsigned)((n + 31) / 32));
             scores_kernel<32><<<grid, 64 * kScoreWaves, 0, st>>>((const bf16_t*)x, (const bf16_t*)W, bias, Ttok, H,
-                                                                 n, sc, bd, zero, n_zero);
+                                                                 n, sc, bd);
         }
     } else {
-        if (zero) {
-            hipError_t e = launch_fill_i32(zero, 0, n_zero, st);
-            if (e != hipSuccess) return e;
-        }
         dim3 grid((unsigned)((n + 255) / 256), (unsigned)Ttok);
         if (dtype == kBF16)
             scores_generic_kernel<bf16_t><<<grid, 256, 0, st>>>((const bf16_t*)x, (const bf16_t*)W, bias, Ttok, H, n,
@@ -985,30 +1166,45 @@ hipError_t launch_scores(int dtype, const void* x, const void* W, const float* b
     return hipGetLastError();
 }
 
-bool route_fused_ok(int dtype, int H, int E, int k) {
-    return dtype == kBF16 && H % 32 == 0 && (E == 16 || E == 32 || E == 64 || E == 128) && k <= 16;
+bool route_block_ok(int dtype, int H, int E, int k) {
+    if (dtype != kBF16 || H > kRouteMaxH || k > 16 || !(E == 16 || E == 32 || E == 64 || E == 128)) return false;
+    const int kg = kRouteWaves / (E / 16);
+    return H % (kRouteStageK * kg) == 0;  // every wave streams at least one whole stage
 }
 bool group_small_ok(int64_t T, int E) { return T <= kSmallMaxT && E <= 128; }
+
+hipError_t launch_route_block(const void* x, const void* W, const float* bias, int64_t Ttok, int H, int E, int k,
+                              int norm, int32_t* idx, float* w, float* probs, uint16_t* masks, int32_t* bcnt,
+                              int32_t* blist, hipStream_t st) {
+    const unsigned grid = (unsigned)mask_words(Ttok);
+    const int mstride = mask_stride(Ttok);
+    const bf16_t* xb = (const bf16_t*)x;
+    const bf16_t* wb = (const bf16_t*)W;
+    const int nmine = H / (kRouteStageK * (kRouteWaves / (E / 16)));  // stages per wave
+#define TMOE_RB(NS, D)                                                                                   \
+    route_block_kernel<NS, D><<<grid, kRouteThreads, 0, st>>>(xb, wb, bias, Ttok, H, k, norm, idx, w, probs, \
+                                                              masks, mstride, bcnt, blist)
+#define TMOE_RB_E(D)                 \
+    if (E == 16) TMOE_RB(1, D);      \
+    else if (E == 32) TMOE_RB(2, D); \
+    else if (E == 64) TMOE_RB(4, D); \
+    else TMOE_RB(8, D);
+    if (nmine % 4 == 0) { TMOE_RB_E(4) }
+    else if (nmine % 2 == 0) { TMOE_RB_E(2) }
+    else { TMOE_RB_E(1) }
+#undef TMOE_RB_E
+#undef TMOE_RB
+    return hipGetLastError();
+}
 
 hipError_t launch_route(int dtype, const void* x, const void* W, const float* bias, int64_t Ttok, int H, int E,
                         int k, int norm, int32_t* idx, float* w, float* probs, float* scratch_sc,
                         float* scratch_bd, uint16_t* masks, hipStream_t st) {
     // one block per 16 tokens (one mask word); mask rows are mask_stride(T) words apart
     const int nwords = mask_words(Ttok), mstride = mask_stride(Ttok);
-    if (route_fused_ok(dtype, H, E, k)) {
-        const bf16_t* xb = (const bf16_t*)x;
-        const bf16_t* wb = (const bf16_t*)W;
-#define TMOE_FUSED(NS)                                                                                          \
-    route_fused_kernel<NS><<<nwords, 64 * kFusedWaves, 0, st>>>(xb, wb, bias, Ttok, H, E, k, norm, idx, w, probs, \
-                                                                masks, mstride)
-        if (E == 16) TMOE_FUSED(1);
-        else if (E == 32) TMOE_FUSED(2);
-        else if (E == 64) TMOE_FUSED(4);
-        else TMOE_FUSED(8);
-#undef TMOE_FUSED
-        return hipGetLastError();
-    }
-    hipError_t err = launch_scores(dtype, x, W, bias, Ttok, H, E, scratch_sc, scratch_bd, st, nullptr, 0);
+    if (route_block_ok(dtype, H, E, k))
+        return launch_route_block(x, W, bias, Ttok, H, E, k, norm, idx, w, probs, masks, nullptr, nullptr, st);
+    hipError_t err = launch_scores(dtype, x, W, bias, Ttok, H, E, scratch_sc, scratch_bd, st);
     if (err != hipSuccess) return err;
     if (dtype == kBF16)
         return launch_select<bf16_t>(scratch_sc, scratch_bd, (const bf16_t*)x, (const bf16_t*)W, bias, Ttok, H, E, k,
@@ -1047,47 +1243,6 @@ hipError_t launch_select_group_small(const float* scratch_sc, const float* scrat
     else if (E <= 64) TMOE_SG(4);
     else TMOE_SG(8);
 #undef TMOE_SG
-    return hipGetLastError();
-}
-
-// Small batches: selection spread over T / 4 one-wave blocks, each token's
-// pairs appended to per-expert lists (counters cleared by the scores launch).
-template <typename T, int J>
-__global__ __launch_bounds__(64) void select_lists_kernel(const float* __restrict__ sc, const float* __restrict__ bd,
-                                                          const T* __restrict__ x, const T* __restrict__ W,
-                                                          const float* __restrict__ bias, int64_t Ttok, int H, int n,
-                                                          int k, int norm, int32_t* __restrict__ out_idx,
-                                                          float* __restrict__ out_w, int* __restrict__ cnt,
-                                                          int* __restrict__ list, int lstride) {
-    __shared__ RowPicks picks;
-    __shared__ SelScratch scr;
-    const int64_t t = (int64_t)blockIdx.x * 4 + (lane_id() >> 4);
-    select_rows_wave<T, J, float>(sc, bd, 0, t < Ttok ? t : -1, n, k, x, W, H, bias, norm, out_idx, out_w, nullptr,
-                                  nullptr, 0, 0, picks, &scr, ListSink{cnt, list, lstride});
-}
-
-bool route_lists_ok(int dtype, int64_t T, int E, int k) { return T <= kSmallMaxT && E <= 128 && k <= 16; }
-
-hipError_t launch_select_lists(int dtype, const float* sc, const float* bd, const void* x, const void* W,
-                               const float* bias, int64_t Ttok, int H, int E, int k, int norm, int32_t* idx, float* w,
-                               int* cnt, int* list, hipStream_t st) {
-    const dim3 grid((unsigned)((Ttok + 3) / 4));
-    const int ls = (int)Ttok;
-#define TMOE_SL(TT, J)                                                                                          \
-    select_lists_kernel<TT, J><<<grid, 64, 0, st>>>(sc, bd, (const TT*)x, (const TT*)W, bias, Ttok, H, E, k, norm, \
-                                                    idx, w, cnt, list, ls)
-    if (dtype == kBF16) {
-        if (E <= 16) TMOE_SL(bf16_t, 1);
-        else if (E <= 32) TMOE_SL(bf16_t, 2);
-        else if (E <= 64) TMOE_SL(bf16_t, 4);
-        else TMOE_SL(bf16_t, 8);
-    } else {
-        if (E <= 16) TMOE_SL(float, 1);
-        else if (E <= 32) TMOE_SL(float, 2);
-        else if (E <= 64) TMOE_SL(float, 4);
-        else TMOE_SL(float, 8);
-    }
-#undef TMOE_SL
     return hipGetLastError();
 }
 
