@@ -108,8 +108,8 @@ struct LayerPlan {
     float* w;
     RoutePlan route;
     uint16_t* masks;
-    int32_t *prefix, *counts, *offsets, *row_token, *row_of, *row_dst;
-    float* row_scale;
+    uint64_t* jmask;
+    int32_t *prefix, *counts, *offsets, *row_token, *row_of, *row_pair;
     GemmPlan gemm;
     void *hr, *hs, *ybuf;
     // direct decode path: the router's per-block pair lists, h rows at e * T + i
@@ -137,11 +137,11 @@ void plan_layer(const moe_config* c, int64_t T, Carver& cv, LayerPlan& p) {
     p.counts = cv.take<int32_t>(E);
     p.offsets = cv.take<int32_t>(E + 1);
     p.masks = cv.take<uint16_t>((int64_t)E * mask_stride(T));
+    p.jmask = cv.take<uint64_t>((int64_t)E * mask_stride(T));
     p.prefix = cv.take<int32_t>((int64_t)E * mask_stride(T));
     p.row_token = cv.take<int32_t>(N);
     p.row_of = cv.take<int32_t>(N);
-    p.row_dst = cv.take<int32_t>(N);
-    p.row_scale = cv.take<float>(N);
+    p.row_pair = cv.take<int32_t>(N);
     plan_gemm(c, T, true, Is > 0, cv, p.gemm);
     p.hr = cv.take<char>(N * I * (int64_t)es);
     p.hs = cv.take<char>(T * Is * (int64_t)es);
@@ -162,6 +162,7 @@ size_t route_ws(const moe_config* c, int64_t T) {
 size_t permute_ws(const moe_config* c, int64_t T) {
     Carver cv(nullptr);
     cv.take<uint16_t>((int64_t)c->num_experts * mask_stride(T));
+    cv.take<uint64_t>((int64_t)c->num_experts * mask_stride(T));
     cv.take<int32_t>((int64_t)c->num_experts * mask_stride(T));
     return cv.size();
 }
@@ -291,7 +292,7 @@ int moe_route(const moe_config* cfg, const void* x, const void* router, const fl
     plan_route(cfg, T, cv, p);
     return hip_status(launch_route(cfg->dtype, x, router, bias, T, cfg->hidden_size, cfg->num_experts,
                                    cfg->num_experts_per_tok, cfg->norm_topk_prob, topk_idx, topk_w, probs, p.sc, p.bd,
-                                   nullptr, as_stream(stream)));
+                                   nullptr, nullptr, as_stream(stream)));
 }
 
 int moe_permute(const moe_config* cfg, const int32_t* topk_idx, int64_t T, int32_t* counts, int32_t* offsets,
@@ -315,10 +316,11 @@ int moe_permute(const moe_config* cfg, const int32_t* topk_idx, int64_t T, int32
     if (ws_bytes < permute_ws(cfg, T)) return MOE_ERR_WORKSPACE;
     Carver cv(ws);
     uint16_t* masks = cv.take<uint16_t>((int64_t)E * mask_stride(T));
+    uint64_t* jmask = cv.take<uint64_t>((int64_t)E * mask_stride(T));
     int32_t* prefix = cv.take<int32_t>((int64_t)E * mask_stride(T));
-    TMOE_TRY(launch_masks(topk_idx, T, k, E, masks, s));
-    TMOE_TRY(launch_permute(topk_idx, T, k, E, masks, prefix, counts, offsets, row_token, row_of, nullptr, nullptr,
-                            nullptr, 0, nullptr, nullptr, s));
+    TMOE_TRY(launch_masks(topk_idx, T, k, E, masks, jmask, s));
+    TMOE_TRY(launch_permute(topk_idx, T, k, E, masks, jmask, prefix, counts, offsets, row_token, row_of, nullptr,
+                            nullptr, nullptr, s));
     if (x) TMOE_TRY(launch_gather_rows(cfg->dtype, x, row_token, T * k, cfg->hidden_size, x_perm, s));
     return MOE_OK;
 }
@@ -432,7 +434,7 @@ int moe_layer_forward_timed(const moe_config* cfg, const moe_weights* w, const v
     auto ev = [&](int i) { return stage_events ? static_cast<hipEvent_t>(stage_events[i]) : nullptr; };
     if (p.direct) {
         TMOE_TRY(launch_route_block(x, w->router, w->router_bias, T, H, E, k, cfg->norm_topk_prob, idx, wt, nullptr,
-                                    nullptr, p.bcnt, p.blist, s));
+                                    nullptr, nullptr, p.bcnt, p.blist, s));
         TMOE_TRY(mark(1));
         TMOE_TRY(mark(2));
         int bm;
@@ -477,17 +479,19 @@ int moe_layer_forward_timed(const moe_config* cfg, const moe_weights* w, const v
         TMOE_TRY(mark(1));
         TMOE_TRY(launch_select_group_small(p.route.sc, p.route.bd, x, w->router, w->router_bias, T, H, E, k,
                                            cfg->norm_topk_prob, idx, wt, counts, p.offsets, p.row_token, p.row_of,
-                                           p.row_dst, p.row_scale, slots, t1, t2, s));
+                                           p.row_pair, t1, t2, s));
     } else {
+        // choice slots come with the masks only from the one-launch router
+        uint64_t* jm = route_block_ok(cfg->dtype, H, E, k) ? p.jmask : nullptr;
         TMOE_TRY(launch_route(cfg->dtype, x, w->router, w->router_bias, T, H, E, k, cfg->norm_topk_prob, idx, wt,
-                              nullptr, p.route.sc, p.route.bd, p.masks, s));
+                              nullptr, p.route.sc, p.route.bd, p.masks, jm, s));
         TMOE_TRY(mark(1));
         if (group_small_ok(T, E))
-            TMOE_TRY(launch_group_small(idx, wt, p.masks, T, E, k, counts, p.offsets, p.row_token, p.row_of,
-                                        p.row_dst, p.row_scale, slots, t1, t2, s));
+            TMOE_TRY(launch_group_small(idx, p.masks, T, E, k, counts, p.offsets, p.row_token, p.row_of, p.row_pair,
+                                        t1, t2, s));
         else
-            TMOE_TRY(launch_permute(idx, T, k, E, p.masks, p.prefix, counts, p.offsets, p.row_token, p.row_of, wt,
-                                    p.row_dst, p.row_scale, slots, t1, t2, s));
+            TMOE_TRY(launch_permute(idx, T, k, E, p.masks, jm, p.prefix, counts, p.offsets, p.row_token,
+                                    p.row_of, p.row_pair, t1, t2, s));
     }
     TMOE_TRY(mark(2));
 
@@ -498,8 +502,10 @@ int moe_layer_forward_timed(const moe_config* cfg, const moe_weights* w, const v
     int r = run_gemm_pass(cfg, p.gemm, 0, gu_r, gu_s, p.offsets, N, T, s, ev(6), ev(7));
     if (r != MOE_OK) return r;
     TMOE_TRY(mark(3));
-    GemmGroup dn_r = group(w->down, nullptr, (int64_t)H * I, H, I, p.hr, I, nullptr, p.ybuf, H, p.row_dst, 1, 0,
-                           p.row_scale);
+    // row_pair v = t * k + j goes to slot j of token t: row v + v / k of [T, k + 1, H], scaled by w[v]
+    GemmGroup dn_r = group(w->down, nullptr, (int64_t)H * I, H, I, p.hr, I, nullptr, p.ybuf, H, p.row_pair, 1, 0, wt);
+    dn_r.out_div = k;
+    dn_r.scale_by_map = 1;
     GemmGroup dn_s = Is > 0 ? group(w->shared_down, nullptr, 0, H, Is, p.hs, Is, nullptr, p.ybuf, H, nullptr, slots,
                                     k, nullptr)
                             : no_group();

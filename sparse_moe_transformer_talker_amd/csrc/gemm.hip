@@ -303,16 +303,22 @@ __global__ __launch_bounds__(256) void grouped_gemm_lds_kernel(GemmArgs args) {
         }
         pb[j] = w + (int64_t)e * g.w_estride + (int64_t)wrow * K + c * 8;
     }
-    // Destination row and scale of this lane's token in each of its MI token
-    // blocks, fetched now so the loads overlap the main loop.
-    int32_t dst_row[MI];
+    // Destination row of every tile row (LDS, for the epilogue's row stores) and
+    // the scale of this lane's token in each of its MI token blocks, fetched now
+    // so the loads overlap the main loop.
+    __shared__ int32_t dst_rows[BM];
+    if (tid < BM) {
+        const int r = tid;
+        const int64_t src = (int64_t)m0 + (r < mrows ? r : 0);
+        const int32_t v = g.out_rows ? g.out_rows[src] : (int32_t)src;
+        dst_rows[r] = r < mrows ? v * g.out_mul + g.out_add + (g.out_div > 0 ? v / g.out_div : 0) : -1;
+    }
     float row_sc[MI];
 #pragma unroll
     for (int a = 0; a < MI; ++a) {
         const int r = (wave >> 1) * (BM / 2) + a * 32 + (lane & 31);
         const int64_t src = (int64_t)m0 + (r < mrows ? r : 0);
         const int32_t v = g.out_rows ? g.out_rows[src] : (int32_t)src;
-        dst_row[a] = r < mrows ? v * g.out_mul + g.out_add + (g.out_div > 0 ? v / g.out_div : 0) : -1;
         row_sc[a] = (PASS == 1 && g.out_scale) ? g.out_scale[g.scale_by_map ? v : src] : 1.0f;
     }
     typedef __attribute__((address_space(3))) void lds_void;
@@ -396,13 +402,26 @@ __global__ __launch_bounds__(256) void grouped_gemm_lds_kernel(GemmArgs args) {
     // Epilogue.  The weight tile is the MFMA's first operand, so block (a, b)
     // holds output features x tokens: lane l, entry i has feature
     // 8 * (i / 4) + 4 * (l / 32) + i % 4 of the block's 32 and token l % 32,
-    // i.e. four consecutive features of one token per group of four entries,
-    // written as one 8-byte store.
-    bf16_t* out = (bf16_t*)g.out;
+    // i.e. four consecutive features of one token per group of four entries.
+    // They are rounded to bf16 and placed in the idle ring as a row-major
+    // tile (16-byte chunks swizzled by row against bank conflicts); then whole
+    // output rows are written, 16 bytes per lane (stores straight from the
+    // fragment layout would touch 32 rows per instruction).
+    constexpr int NOUT = PASS == 0 ? BNR / 2 : BNR;  // output columns of the tile
+    constexpr int ROWB = NOUT * 2;                    // bytes per output row
+    constexpr int CPR = ROWB / 16;                    // 16-byte chunks per row
+    constexpr int RPB = STAGE / ROWB;                 // rows per ring buffer
+    static_assert(4 * RPB >= BM, "the output tile fits in the ring");
+    auto row_at = [&](int r) -> char* {
+        const int bsel = r / RPB;
+        char* base = bsel == 0 ? buf0 : (bsel == 1 ? buf1 : (bsel == 2 ? buf2 : buf3));
+        return base + (r % RPB) * ROWB;
+    };
+    sync();  // every wave is done with the ring
 #pragma unroll
     for (int a = 0; a < MI; ++a) {
-        if (dst_row[a] < 0) continue;
-        bf16_t* orow = out + (int64_t)dst_row[a] * g.out_ld + n0 + 4 * lh;
+        const int r = wm * (BM / 2) + a * 32 + lr;
+        char* rp = row_at(r);
 #pragma unroll
         for (int b = 0; b < (PASS == 0 ? 2 : 4); ++b)
 #pragma unroll
@@ -420,9 +439,17 @@ __global__ __launch_bounds__(256) void grouped_gemm_lds_kernel(GemmArgs args) {
                 uint2 pk;
                 pk.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
                 pk.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
-                const int f = (PASS == 0 ? wn * 64 : wn * 128) + b * 32 + 8 * j;
-                *reinterpret_cast<uint2*>(orow + f) = pk;
+                const int c = ((PASS == 0 ? wn * 64 : wn * 128) + b * 32 + 8 * j) / 8;  // 16-byte chunk
+                *reinterpret_cast<uint2*>(rp + ((c ^ (r % CPR)) * 16) + lh * 8) = pk;
             }
+    }
+    sync();
+    bf16_t* out = (bf16_t*)g.out;
+    for (int q = tid; q < BM * CPR; q += 256) {
+        const int r = q / CPR, c = q % CPR;
+        if (r >= mrows) break;  // rows ascend with q
+        const u32x4 v = *reinterpret_cast<const u32x4*>(row_at(r) + ((c ^ (r % CPR)) * 16));
+        *reinterpret_cast<u32x4*>(out + (int64_t)dst_rows[r] * g.out_ld + n0 + c * 8) = v;
     }
 }
 
@@ -458,9 +485,10 @@ __global__ __launch_bounds__(256) void gemm_generic_kernel(GemmGroup g, const in
         s0 = s0 / (1.0f + __expf(-s0)) * s1;
     } else {
         for (int kk = 0; kk < g.K; ++kk) s0 = fmaf(Elem<T>::load(a, kk), Elem<T>::load(wa, kk), s0);
-        if (g.out_scale) s0 *= g.out_scale[r];
     }
-    const int64_t dst = (g.out_rows ? (int64_t)g.out_rows[r] : r) * g.out_mul + g.out_add;
+    const int64_t v = g.out_rows ? (int64_t)g.out_rows[r] : r;
+    if (PASS == 1 && g.out_scale) s0 *= g.out_scale[g.scale_by_map ? v : r];
+    const int64_t dst = v * g.out_mul + g.out_add + (g.out_div > 0 ? v / g.out_div : 0);
     Elem<T>::store((T*)g.out, dst * g.out_ld + n, s0);
 }
 

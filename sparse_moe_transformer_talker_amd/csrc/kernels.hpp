@@ -12,26 +12,30 @@ constexpr int kMaxTopK = 32;
 constexpr int kMaxExperts = 1024;
 
 // --- routing (route.hip) ---
+// Row maps of a grouping: row_token[r] = token of grouped row r; row_of[t * k + j]
+// = grouped row of pair (t, j); row_pair[r] = t * k + j (nullable).
 struct TileSpec;
 // Small batches: one block groups the routing from the router's masks (counts,
-// offsets, tile lists, row_token / row_of / row_dst / row_scale).
+// offsets, tile lists and row maps).
 bool group_small_ok(int64_t T, int E);
-hipError_t launch_group_small(const int32_t* idx, const float* w, const uint16_t* masks, int64_t T, int E, int k,
-                              int32_t* counts, int32_t* offsets, int32_t* row_token, int32_t* row_of,
-                              int32_t* row_dst, float* row_scale, int slots, const TileSpec* t1, const TileSpec* t2,
-                              hipStream_t st);
-// masks (nullable): [E][mask_stride(T)] uint16, bit t % 16 of word t / 16 set when token t routes to e
+hipError_t launch_group_small(const int32_t* idx, const uint16_t* masks, int64_t T, int E, int k, int32_t* counts,
+                              int32_t* offsets, int32_t* row_token, int32_t* row_of, int32_t* row_pair,
+                              const TileSpec* t1, const TileSpec* t2, hipStream_t st);
+// masks (nullable): [E][mask_stride(T)] uint16, bit t % 16 of word t / 16 set when
+// token t routes to e; jmask (nullable, k <= 16): [E][mask_stride(T)] uint64 with
+// the slot j of that choice in bits 4 (t % 16) .. + 3, written only when
+// route_block_ok (the other selection kernels write masks alone)
 hipError_t launch_route(int dtype, const void* x, const void* W, const float* bias, int64_t T, int H, int E, int k,
                         int norm, int32_t* idx, float* w, float* probs, float* scratch_sc, float* scratch_bd,
-                        uint16_t* masks, hipStream_t st);
+                        uint16_t* masks, uint64_t* jmask, hipStream_t st);
 // Small batches, bf16: after launch_scores, one block selects every token and
 // groups the routing (same outputs as launch_route + launch_group_small).
 bool route_group_small_ok(int dtype, int64_t T, int H, int E, int k);
 hipError_t launch_select_group_small(const float* sc, const float* bd, const void* x, const void* W,
                                      const float* bias, int64_t T, int H, int E, int k, int norm, int32_t* idx,
                                      float* w, int32_t* counts, int32_t* offsets, int32_t* row_token,
-                                     int32_t* row_of, int32_t* row_dst, float* row_scale, int slots,
-                                     const TileSpec* t1, const TileSpec* t2, hipStream_t st);
+                                     int32_t* row_of, int32_t* row_pair, const TileSpec* t1, const TileSpec* t2,
+                                     hipStream_t st);
 hipError_t launch_scores(int dtype, const void* x, const void* W, const float* bias, int64_t T, int H, int n,
                          float* sc, float* bd, hipStream_t st);
 // bf16, E in {16, 32, 64, 128}, H <= 1024 a multiple of 128 (8 / (E / 16)), k <= 16: scores and
@@ -41,8 +45,8 @@ hipError_t launch_scores(int dtype, const void* x, const void* W, const float* b
 // (bcnt / blist nullable; order inside a block's list is arbitrary).
 bool route_block_ok(int dtype, int H, int E, int k);
 hipError_t launch_route_block(const void* x, const void* W, const float* bias, int64_t T, int H, int E, int k,
-                              int norm, int32_t* idx, float* w, float* probs, uint16_t* masks, int32_t* bcnt,
-                              int32_t* blist, hipStream_t st);
+                              int norm, int32_t* idx, float* w, float* probs, uint16_t* masks, uint64_t* jmask,
+                              int32_t* bcnt, int32_t* blist, hipStream_t st);
 hipError_t launch_argmax(int dtype, const float* sc, const float* bd, const void* x, const void* W, int64_t T, int H,
                          int n, int32_t* out, hipStream_t st);
 
@@ -60,12 +64,12 @@ struct TileSpec {
 int64_t tile_max_items(int64_t pairs, int E, int64_t T, int mt, int nt, int n_routed, int n_shared);
 int mask_words(int64_t T);
 int mask_stride(int64_t T);
-hipError_t launch_masks(const int32_t* idx, int64_t T, int k, int E, uint16_t* masks, hipStream_t st);
-// prefix: [E][mask_stride(T)] int32 scratch
-hipError_t launch_permute(const int32_t* idx, int64_t T, int k, int E, const uint16_t* masks, int32_t* prefix,
-                          int32_t* counts, int32_t* offsets, int32_t* row_token, int32_t* row_of, const float* w,
-                          int32_t* row_dst, float* row_scale, int slots, const TileSpec* t1, const TileSpec* t2,
-                          hipStream_t st);
+hipError_t launch_masks(const int32_t* idx, int64_t T, int k, int E, uint16_t* masks, uint64_t* jmask,
+                        hipStream_t st);
+// prefix: [E][mask_stride(T)] int32 scratch (E > 128 only); jmask nullable
+hipError_t launch_permute(const int32_t* idx, int64_t T, int k, int E, const uint16_t* masks, const uint64_t* jmask,
+                          int32_t* prefix, int32_t* counts, int32_t* offsets, int32_t* row_token, int32_t* row_of,
+                          int32_t* row_pair, const TileSpec* t1, const TileSpec* t2, hipStream_t st);
 hipError_t launch_build_items(const int32_t* offsets, int E, int64_t T, const TileSpec* t1, const TileSpec* t2,
                               hipStream_t st);
 

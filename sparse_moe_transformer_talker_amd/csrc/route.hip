@@ -700,7 +700,8 @@ template <int NS, int DEPTH>
 __global__ __launch_bounds__(kRouteThreads) void route_block_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ W, const float* __restrict__ bias, int64_t T, int H,
     int k, int norm, int32_t* __restrict__ out_idx, float* __restrict__ out_w, float* __restrict__ out_probs,
-    uint16_t* __restrict__ masks, int mstride, int32_t* __restrict__ bcnt, int32_t* __restrict__ blist) {
+    uint16_t* __restrict__ masks, uint64_t* __restrict__ jmask, int mstride, int32_t* __restrict__ bcnt,
+    int32_t* __restrict__ blist) {
     constexpr int E = NS * 16;
     constexpr int KG = kRouteWaves / NS;                        // K groups per expert tile
     constexpr int XCH = 16 * (kRouteMaxH / 8) / kRouteThreads;  // staged x chunks per thread (max)
@@ -711,6 +712,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_block_kernel(
     __shared__ double lg[16 * E];
     __shared__ float ab[16 * E];
     __shared__ uint32_t msk[E];
+    __shared__ uint64_t jm[E];
     __shared__ int lcnt[E];
     __shared__ int llist[E * 16];
     __shared__ RowPicks picks[4];
@@ -738,6 +740,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_block_kernel(
     if (tid == 0) dfr.n = 0;
     for (int q = tid; q < E; q += blockDim.x) {
         msk[q] = 0;
+        jm[q] = 0;
         lcnt[q] = 0;
     }
     // stage the block's token rows (rows past T repeat row T - 1; never used):
@@ -834,6 +837,16 @@ __global__ __launch_bounds__(kRouteThreads) void route_block_kernel(
                                                    bcnt ? lcnt : nullptr, llist, (int)(t * k));
     }
     __syncthreads();
+    if (jmask) {
+        // slot of every choice, 4 bits per token, from this block's routing outputs
+        for (int q = tid; q < 16 * k; q += blockDim.x) {
+            const int tt = q / k, j = q % k;
+            if (tok0 + tt < T)
+                atomicOr((unsigned long long*)&jm[out_idx[(tok0 + tt) * k + j]], (unsigned long long)j << (4 * tt));
+        }
+        __syncthreads();
+        for (int e = tid; e < E; e += blockDim.x) jmask[(int64_t)e * mstride + blockIdx.x] = jm[e];
+    }
     if (masks)
         for (int e = tid; e < E; e += blockDim.x) masks[(int64_t)e * mstride + blockIdx.x] = (uint16_t)msk[e];
     if (bcnt) {
@@ -942,13 +955,12 @@ constexpr int kSmallMaxT = 256;
 constexpr int kSmallWords = kSmallMaxT / 16;
 
 __global__ __launch_bounds__(1024) void group_small_kernel(const int32_t* __restrict__ idx,
-                                                           const float* __restrict__ wts,
                                                            const uint16_t* __restrict__ masks, int mstride, int Ttok,
                                                            int E, int k, int32_t* __restrict__ counts,
                                                            int32_t* __restrict__ offsets,
                                                            int32_t* __restrict__ row_token,
-                                                           int32_t* __restrict__ row_of, int32_t* __restrict__ row_dst,
-                                                           float* __restrict__ row_scale, int slots, TileSpecs specs) {
+                                                           int32_t* __restrict__ row_of,
+                                                           int32_t* __restrict__ row_pair, TileSpecs specs) {
     __shared__ uint32_t msk[128 * kSmallWords];
     __shared__ int pre[128 * kSmallWords];
     __shared__ int offs[128];
@@ -987,10 +999,7 @@ __global__ __launch_bounds__(1024) void group_small_kernel(const int32_t* __rest
         if (dst < 0 || dst >= N) continue;
         row_token[dst] = t;
         row_of[i] = dst;
-        if (row_dst) {
-            row_dst[dst] = t * slots + j;
-            row_scale[dst] = wts[i];
-        }
+        if (row_pair) row_pair[dst] = i;
     }
 }
 
@@ -1007,7 +1016,7 @@ __global__ __launch_bounds__(kSelectGroupThreads) void select_group_small_kernel
     const bf16_t* __restrict__ W, const float* __restrict__ bias, int Ttok, int H, int E, int k, int norm,
     int32_t* __restrict__ out_idx, float* __restrict__ out_w, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ row_token, int32_t* __restrict__ row_of,
-    int32_t* __restrict__ row_dst, float* __restrict__ row_scale, int slots, TileSpecs specs) {
+    int32_t* __restrict__ row_pair, TileSpecs specs) {
     __shared__ uint32_t msk[128 * kSmallWords];
     __shared__ int pre[128 * kSmallWords];
     __shared__ int offs[128];
@@ -1053,10 +1062,7 @@ __global__ __launch_bounds__(kSelectGroupThreads) void select_group_small_kernel
         if (dst < 0 || dst >= N) continue;
         row_token[dst] = t;
         row_of[i] = dst;
-        if (row_dst) {
-            row_dst[dst] = t * slots + j;
-            row_scale[dst] = out_w[i];
-        }
+        if (row_pair) row_pair[dst] = i;
     }
 }
 
@@ -1174,8 +1180,8 @@ bool route_block_ok(int dtype, int H, int E, int k) {
 bool group_small_ok(int64_t T, int E) { return T <= kSmallMaxT && E <= 128; }
 
 hipError_t launch_route_block(const void* x, const void* W, const float* bias, int64_t Ttok, int H, int E, int k,
-                              int norm, int32_t* idx, float* w, float* probs, uint16_t* masks, int32_t* bcnt,
-                              int32_t* blist, hipStream_t st) {
+                              int norm, int32_t* idx, float* w, float* probs, uint16_t* masks, uint64_t* jmask,
+                              int32_t* bcnt, int32_t* blist, hipStream_t st) {
     const unsigned grid = (unsigned)mask_words(Ttok);
     const int mstride = mask_stride(Ttok);
     const bf16_t* xb = (const bf16_t*)x;
@@ -1183,7 +1189,7 @@ hipError_t launch_route_block(const void* x, const void* W, const float* bias, i
     const int nmine = H / (kRouteStageK * (kRouteWaves / (E / 16)));  // stages per wave
 #define TMOE_RB(NS, D)                                                                                   \
     route_block_kernel<NS, D><<<grid, kRouteThreads, 0, st>>>(xb, wb, bias, Ttok, H, k, norm, idx, w, probs, \
-                                                              masks, mstride, bcnt, blist)
+                                                              masks, jmask, mstride, bcnt, blist)
 #define TMOE_RB_E(D)                 \
     if (E == 16) TMOE_RB(1, D);      \
     else if (E == 32) TMOE_RB(2, D); \
@@ -1199,11 +1205,12 @@ hipError_t launch_route_block(const void* x, const void* W, const float* bias, i
 
 hipError_t launch_route(int dtype, const void* x, const void* W, const float* bias, int64_t Ttok, int H, int E,
                         int k, int norm, int32_t* idx, float* w, float* probs, float* scratch_sc,
-                        float* scratch_bd, uint16_t* masks, hipStream_t st) {
+                        float* scratch_bd, uint16_t* masks, uint64_t* jmask, hipStream_t st) {
     // one block per 16 tokens (one mask word); mask rows are mask_stride(T) words apart
     const int nwords = mask_words(Ttok), mstride = mask_stride(Ttok);
     if (route_block_ok(dtype, H, E, k))
-        return launch_route_block(x, W, bias, Ttok, H, E, k, norm, idx, w, probs, masks, nullptr, nullptr, st);
+        return launch_route_block(x, W, bias, Ttok, H, E, k, norm, idx, w, probs, masks, masks ? jmask : nullptr,
+                                  nullptr, nullptr, st);
     hipError_t err = launch_scores(dtype, x, W, bias, Ttok, H, E, scratch_sc, scratch_bd, st);
     if (err != hipSuccess) return err;
     if (dtype == kBF16)
@@ -1213,12 +1220,11 @@ hipError_t launch_route(int dtype, const void* x, const void* W, const float* bi
                                 idx, w, probs, masks, mstride, st);
 }
 
-hipError_t launch_group_small(const int32_t* idx, const float* w, const uint16_t* masks, int64_t Ttok, int E, int k,
-                              int32_t* counts, int32_t* offsets, int32_t* row_token, int32_t* row_of,
-                              int32_t* row_dst, float* row_scale, int slots, const TileSpec* t1, const TileSpec* t2,
-                              hipStream_t st) {
-    group_small_kernel<<<1, 1024, 0, st>>>(idx, w, masks, mask_stride(Ttok), (int)Ttok, E, k, counts, offsets,
-                                           row_token, row_of, row_dst, row_scale, slots, make_specs(t1, t2));
+hipError_t launch_group_small(const int32_t* idx, const uint16_t* masks, int64_t Ttok, int E, int k, int32_t* counts,
+                              int32_t* offsets, int32_t* row_token, int32_t* row_of, int32_t* row_pair,
+                              const TileSpec* t1, const TileSpec* t2, hipStream_t st) {
+    group_small_kernel<<<1, 1024, 0, st>>>(idx, masks, mask_stride(Ttok), (int)Ttok, E, k, counts, offsets,
+                                           row_token, row_of, row_pair, make_specs(t1, t2));
     return hipGetLastError();
 }
 
@@ -1229,15 +1235,15 @@ bool route_group_small_ok(int dtype, int64_t T, int H, int E, int k) {
 hipError_t launch_select_group_small(const float* scratch_sc, const float* scratch_bd, const void* x, const void* W,
                                      const float* bias, int64_t Ttok, int H, int E, int k, int norm, int32_t* idx,
                                      float* w, int32_t* counts, int32_t* offsets, int32_t* row_token,
-                                     int32_t* row_of, int32_t* row_dst, float* row_scale, int slots,
-                                     const TileSpec* t1, const TileSpec* t2, hipStream_t st) {
+                                     int32_t* row_of, int32_t* row_pair, const TileSpec* t1, const TileSpec* t2,
+                                     hipStream_t st) {
     const bf16_t* xb = (const bf16_t*)x;
     const bf16_t* wb = (const bf16_t*)W;
     const TileSpecs specs = make_specs(t1, t2);
 #define TMOE_SG(J)                                                                                          \
     select_group_small_kernel<J><<<1, kSelectGroupThreads, 0, st>>>(scratch_sc, scratch_bd, xb, wb, bias, (int)Ttok, H, E, k, \
-                                                     norm, idx, w, counts, offsets, row_token, row_of, row_dst, \
-                                                     row_scale, slots, specs)
+                                                     norm, idx, w, counts, offsets, row_token, row_of, row_pair, \
+                                                     specs)
     if (E <= 16) TMOE_SG(1);
     else if (E <= 32) TMOE_SG(2);
     else if (E <= 64) TMOE_SG(4);
