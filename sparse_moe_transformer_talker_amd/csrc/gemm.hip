@@ -163,13 +163,19 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs args) {
 
     const int p = blockIdx.x;
     if (args.direct_bcnt) {
+        // Workgroup p runs on XCD p % 8.  Each XCD takes a contiguous run of the
+        // routed tiles first and then an equal share of the shared-expert tiles,
+        // whose weights are re-read from L2 by their M-tiles, so the tiles
+        // dispatched last on every XCD are the cheap ones.
         const int nt0 = args.direct_nt[0];
         const int n_routed = args.E * nt0;
-        const int n_all = n_routed + args.direct_nt[1] * args.direct_mt1;
-        const int chunk = (n_all + 7) >> 3;
-        const int slot = p >> 3;
-        if (slot >= chunk) return;
-        int q = (p & 7) * chunk + slot;
+        const int n_shared = args.direct_nt[1] * args.direct_mt1;
+        const int n_all = n_routed + n_shared;
+        const int cr = (n_routed + 7) >> 3, cs = (n_shared + 7) >> 3;
+        const int slot = p >> 3, x = p & 7;
+        int q;
+        if (slot < cr) q = x * cr + slot < n_routed ? x * cr + slot : n_all;
+        else q = x * cs + (slot - cr) < n_shared ? n_routed + x * cs + (slot - cr) : n_all;
         if (q >= n_all) return;
         if (q < n_routed) {
             // this expert's pairs: the per-block lists concatenated in block order
@@ -568,8 +574,9 @@ int gemm_direct_tile(int pass, int* bm) {
 
 hipError_t launch_grouped_gemm_direct(int pass, const GemmArgs& args, hipStream_t st, hipEvent_t ev_start,
                                       hipEvent_t ev_stop) {
-    const int64_t n_all = (int64_t)args.E * args.direct_nt[0] + (int64_t)args.direct_nt[1] * args.direct_mt1;
-    const unsigned grid = (unsigned)(((n_all + 7) / 8) * 8);
+    const int64_t cr = ((int64_t)args.E * args.direct_nt[0] + 7) / 8;
+    const int64_t cs = ((int64_t)args.direct_nt[1] * args.direct_mt1 + 7) / 8;
+    const unsigned grid = (unsigned)(8 * (cr + cs));
     if (grid == 0) return hipSuccess;
     if (pass == 0) return launch_gemm(grouped_gemm_kernel<TMOE_SMALL_GU>, grid, st, ev_start, ev_stop, args);
     if (!k_multiple(args, 128))
