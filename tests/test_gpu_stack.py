@@ -1,0 +1,105 @@
+"""Parity of the stacked layer and of the graph-replayed layer (through the C ABI).
+
+* The 20-layer stack with pre-RMSNorm and residual adds, then the final RMSNorm,
+  codec_head and argmax to c_0 (T=1024, bf16, seeds 30+l, head seed 50).  Each
+  layer is checked on the GPU's own bf16 input (teacher forcing): the RMSNorm
+  output and the layer output within the bf16 bars, routing indices bit-exact;
+  c_0 bit-exact against the oracle's argmax of the GPU's final normalised state.
+  The free-running fp64 stack is run beside it; its c_0 agreement and final
+  relative L2 are reported, not asserted (bf16 rounding differences compound
+  over 20 layers).
+* The layer captured in a HIP graph, replayed several times with other eager
+  layer calls in between (the launch configuration the benchmark times): every
+  replay equals the eager result bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_ref as R
+from sparse_moe_transformer_talker_amd import api
+from sparse_moe_transformer_talker_amd import inputs as INP
+from tests import gpu_helpers as G
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    api.load_library()  # fails loudly when the HIP library is missing
+
+
+@pytest.mark.timeout(900)
+def test_stack20_teacher_forced():
+    c = INP.WORKLOADS["stack20_t1024"]
+    shape, T, L = c["shape"], c["T"], c["layers"]
+    cfg = G.config(shape, "bf16")
+    eps = c["eps"]
+    ones = np.ones(shape.H)
+    gain = torch.ones(shape.H, dtype=torch.float32, device="cuda")
+    x_np = INP.activations(T, shape.H, c["seed"], "bf16")
+    h = G.dev(x_np, "bf16")
+    h_free = INP.to_f64(x_np, "bf16")  # free-running fp64 stack
+    idx = torch.empty((T, shape.k), dtype=torch.int32, device="cuda")
+    worst = 0.0
+    for layer in range(L):
+        w = INP.layer_weights(shape, c["seed"] + layer, c["sigma"], "bf16")
+        wd = G.weights_dev(w, "bf16")
+        xn = api.moe_rmsnorm(cfg, h, gain, eps)
+        y = api.moe_layer_forward(cfg, wd, xn, h, topk_idx=idx)
+        torch.cuda.synchronize()
+        h64, xn64 = G.host64(h), G.host64(xn)
+        w64 = G.weights_f64(w, "bf16")
+        G.assert_close(xn64, R.rmsnorm(h64, ones, eps), "bf16", "stack layer %d rmsnorm" % layer)
+        ref = R.moe_layer(xn64, w64, shape.k, residual=h64)
+        np.testing.assert_array_equal(idx.cpu().numpy(), ref["idx"], err_msg="layer %d routing" % layer)
+        got = G.host64(y)
+        G.assert_close(got, ref["y"], "bf16", "stack layer %d" % layer)
+        worst = max(worst, float(np.abs(got - ref["y"]).max()))
+        h_free = h_free + R.moe_layer(R.rmsnorm(h_free, ones, eps), w64, shape.k)["y"]
+        h = y
+        del wd, w, w64
+    head_np = INP.stack_weights(shape, 0, c["seed"], c["sigma"], "bf16", c["vocab"], c["head_seed"])["codec_head"]
+    head = G.dev(head_np, "bf16")
+    xf = api.moe_rmsnorm(cfg, h, gain, eps)
+    c0, _ = api.moe_codec_head_argmax(cfg, xf, head)
+    torch.cuda.synchronize()
+    head64 = INP.to_f64(head_np, "bf16")
+    xf64 = G.host64(xf)
+    G.assert_close(xf64, R.rmsnorm(G.host64(h), ones, eps), "bf16", "stack final rmsnorm")
+    np.testing.assert_array_equal(c0.cpu().numpy(), R.argmax_first(R.codec_head_logits(xf64, head64)))
+    c0_free = R.argmax_first(R.codec_head_logits(R.rmsnorm(h_free, ones, eps), head64))
+    agree = float(np.mean(c0.cpu().numpy() == c0_free))
+    rel = float(np.linalg.norm(G.host64(h) - h_free) / np.linalg.norm(h_free))
+    print("stack: %d layers, T=%d; worst per-layer max_abs %.3e; free-running c0 agreement %.3f, "
+          "final hidden rel_l2 %.3e" % (L, T, worst, agree, rel), flush=True)
+
+
+@pytest.mark.parametrize("T", [64, 4096])
+def test_layer_graph_replay(T):
+    shape = INP.TALKER
+    cfg = G.config(shape, "bf16")
+    wd = G.weights_dev(INP.layer_weights(shape, 30, 0.02, "bf16"), "bf16")
+    other = G.weights_dev(INP.layer_weights(shape, 31, 0.02, "bf16"), "bf16")
+    x = G.dev(INP.activations(T, shape.H, 30, "bf16"), "bf16")
+    x2 = G.dev(INP.activations(T, shape.H, 31, "bf16"), "bf16")
+    dev = torch.device("cuda", 0)
+    ws = api.workspace(api.moe_workspace_size(cfg, T), dev)
+    ws2 = api.workspace(api.moe_workspace_size(cfg, T), dev)
+    y_eager = api.moe_layer_forward(cfg, wd, x, ws=ws)
+    torch.cuda.synchronize()
+    y_g = torch.empty_like(x)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        api.moe_layer_forward(cfg, wd, x, y=y_g, ws=ws)
+    for rep in range(3):
+        y_other = api.moe_layer_forward(cfg, other, x2, ws=ws2)  # eager work between replays
+        torch.cuda.synchronize()
+        y_g.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y_g.view(torch.int16), y_eager.view(torch.int16)), "replay %d differs" % rep
+        assert not torch.equal(y_other.view(torch.int16), y_eager.view(torch.int16))
+    print("graph replay T=%d: 3 replays equal to eager" % T, flush=True)
