@@ -28,7 +28,7 @@ constexpr int kDirectMaxT = 256;
 constexpr int kDirectMaxBlocks = kDirectMaxT / 16;
 
 template <int PASS, int BM, int BN, int BK, int WM, int WN>
-__global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs args) {
+__global__ __launch_bounds__(256, PASS == 1 ? 6 : 1) void grouped_gemm_kernel(GemmArgs args) {
     constexpr int BROWS = (PASS == 0) ? 2 * BN : BN;
     constexpr int LDK = BK + 8;
     constexpr int KC = BK / 8;                 // 16-byte chunks per tile row
@@ -42,59 +42,72 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs args) {
 
     __shared__ __attribute__((aligned(16))) bf16_t As[BM * LDK];
     __shared__ __attribute__((aligned(16))) bf16_t Bs[BROWS * LDK];
+    const int tid = threadIdx.x;
 
-    // one tile: rows m0 .. m0 + mrows - 1 of group gi, columns n0 .. n0 + BN - 1;
-    // amap / omap (nullable) replace the group's A / output row maps, indexed
-    // by the row within the tile
-    auto tile = [&](const int gi, const int e, const int n0, const int m0, const int mrows, const int* amap,
-                    const int* omap) {
-        const GemmGroup& g = args.g[gi];
-        const int K = g.K;
-        const int tid = threadIdx.x;
-
-        // Per-thread global source pointers (fixed over K).
-        const bf16_t* pa[CA];
-        const bf16_t* pb[CB];
+    // Global sources of this thread's A and B chunks (fixed over K), and the
+    // register copy of the next K block.  A tile is run in phases so that its
+    // weight loads can be issued before its token rows are known.  Weight
+    // chunk i of a thread is tile row tid / KC + RPI i, so its address is a
+    // block base (uniform: gate or up rows of the tile) plus one per-thread
+    // 32-bit offset.
+    constexpr int RPI = 256 / KC;  // tile rows per chunk index
+    static_assert(256 % KC == 0 && BN % RPI == 0, "weight chunks map to rows");
+    const bf16_t* pa[CA];
+    const bf16_t* bbase[2];
+    int bK = 0;
+    uint32_t blane = 0;
+    u32x4 ra[CA], rb[CB];
+    // weight rows n0 .. n0 + BN - 1 of expert e (gate rows, then up rows)
+    auto set_b = [&](const GemmGroup& g, const int e, const int n0) {
+        bK = g.K;
+        bbase[0] = (const bf16_t*)g.wa + (int64_t)e * g.w_estride + (int64_t)n0 * g.K;
+        bbase[1] = PASS == 0 ? (const bf16_t*)g.wb + (int64_t)e * g.w_estride + (int64_t)n0 * g.K : bbase[0];
+        blane = (uint32_t)((tid / KC) * g.K + (tid % KC) * 8) * (uint32_t)sizeof(bf16_t);  // bytes
+    };
+    // tile row r < mrows reads A row amap[r] / a_div (amap not null), else
+    // a_rows[m0 + r] / a_div (a_rows not null), else m0 + r; rows past mrows
+    // repeat row 0 and are never stored
+    auto set_a = [&](const GemmGroup& g, const int m0, const int mrows, const int* amap) {
+#pragma unroll
+        for (int i = 0; i < CA; ++i) {
+            const int c = tid + 256 * i < NA ? tid + 256 * i : 0;
+            const int row = c / KC, kc = c % KC;
+            const int m = row < mrows ? row : 0;
+            const int64_t grow = amap ? (int64_t)(amap[m] / g.a_div)
+                                      : (g.a_rows ? (int64_t)(g.a_rows[m0 + m] / g.a_div) : (int64_t)(m0 + m));
+            pa[i] = (const bf16_t*)g.a + grow * g.a_ld + kc * 8;
+        }
+    };
+    auto load_a = [&](int k0) {
+#pragma unroll
+        for (int i = 0; i < CA; ++i) ra[i] = *reinterpret_cast<const u32x4*>(pa[i] + k0);
+    };
+    auto load_b = [&](int k0) {
+#pragma unroll
+        for (int i = 0; i < CB; ++i) {
+            const int sel = (PASS == 0 && i * RPI >= BN) ? 1 : 0;
+            const char* b = reinterpret_cast<const char*>(bbase[sel] + (int64_t)((i * RPI) % BN) * bK + k0);
+            rb[i] = *reinterpret_cast<const u32x4*>(b + blane);
+        }
+    };
+    auto stash = [&]() {
 #pragma unroll
         for (int i = 0; i < CA; ++i) {
             int c = tid + 256 * i;
-            if (c >= NA) c = 0;
-            int row = c / KC, kc = c % KC;
-            int m = row < mrows ? row : 0;
-            int64_t grow = amap ? (int64_t)(amap[m] / g.a_div)
-                                : (g.a_rows ? (int64_t)(g.a_rows[m0 + m] / g.a_div) : (int64_t)(m0 + m));
-            pa[i] = (const bf16_t*)g.a + grow * g.a_ld + kc * 8;
+            if (c < NA) *reinterpret_cast<u32x4*>(&As[(c / KC) * LDK + (c % KC) * 8]) = ra[i];
         }
 #pragma unroll
         for (int i = 0; i < CB; ++i) {
             int c = tid + 256 * i;
-            int row = c / KC, kc = c % KC;
-            const bf16_t* w = (const bf16_t*)((PASS == 0 && row >= BN) ? g.wb : g.wa);
-            int wrow = n0 + (row % BN);
-            pb[i] = w + (int64_t)e * g.w_estride + (int64_t)wrow * K + kc * 8;
+            *reinterpret_cast<u32x4*>(&Bs[(c / KC) * LDK + (c % KC) * 8]) = rb[i];
         }
+    };
 
-        u32x4 ra[CA], rb[CB];
-        auto load = [&](int k0) {
-#pragma unroll
-            for (int i = 0; i < CA; ++i)
-                if (tid + 256 * i < NA) ra[i] = *reinterpret_cast<const u32x4*>(pa[i] + k0);
-#pragma unroll
-            for (int i = 0; i < CB; ++i) rb[i] = *reinterpret_cast<const u32x4*>(pb[i] + k0);
-        };
-        auto stash = [&]() {
-#pragma unroll
-            for (int i = 0; i < CA; ++i) {
-                int c = tid + 256 * i;
-                if (c < NA) *reinterpret_cast<u32x4*>(&As[(c / KC) * LDK + (c % KC) * 8]) = ra[i];
-            }
-#pragma unroll
-            for (int i = 0; i < CB; ++i) {
-                int c = tid + 256 * i;
-                *reinterpret_cast<u32x4*>(&Bs[(c / KC) * LDK + (c % KC) * 8]) = rb[i];
-            }
-        };
-
+    // The K loop and epilogue of one tile whose first K block is in flight:
+    // output rows m0 .. m0 + mrows - 1 of group g (omap, nullable, replaces the
+    // group's output row map, indexed by the row within the tile).
+    auto run = [&](const GemmGroup& g, const int n0, const int m0, const int mrows, const int* omap) {
+        const int K = g.K;
         const int wave = tid >> 6, lane = tid & 63;
         const int wm = wave / WN, wn = wave % WN;
         const int li = lane & 15, lk = (lane >> 4) * 8;
@@ -105,12 +118,14 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs args) {
 #pragma unroll
             for (int b = 0; b < NS; ++b) { acc[a][b] = f32x4{0, 0, 0, 0}; accu[a][b] = f32x4{0, 0, 0, 0}; }
 
-        load(0);
         for (int k0 = 0; k0 < K; k0 += BK) {
             __syncthreads();  // (also: the previous tile's last LDS reads are done)
             stash();
             __syncthreads();
-            if (k0 + BK < K) load(k0 + BK);
+            if (k0 + BK < K) {
+                load_b(k0 + BK);
+                load_a(k0 + BK);
+            }
 #pragma unroll
             for (int ks = 0; ks < BK; ks += 32) {
                 bf16x8 af[MS], bg[NS], bu[NS];
@@ -178,33 +193,69 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs args) {
         else q = x * cs + (slot - cr) < n_shared ? n_routed + x * cs + (slot - cr) : n_all;
         if (q >= n_all) return;
         if (q < n_routed) {
-            // this expert's pairs: the per-block lists concatenated in block order
+            const GemmGroup& g = args.g[0];
+            const int e = q / nt0, n0 = (q % nt0) * BN;
+            const int T = args.direct_T, base = e * T;
+            // In the down pass neither operand depends on the routing (the A
+            // rows of expert e are rows base .. base + T - 1 in order; rows the
+            // expert does not use are loaded and never stored), so the first K
+            // block goes out before the pair lists.  In the gate/up pass the
+            // lists come first: weight loads issued ahead of them by every
+            // workgroup would queue the lists (and then the token rows) behind
+            // a whole round of weight traffic.
+            if (PASS == 1) {
+                set_b(g, e, n0);
+                load_b(0);
+                set_a(g, base, min(BM, T), nullptr);
+                load_a(0);
+            }
+            // This expert's pairs: the per-block lists concatenated in block
+            // order.  Counts and list entries are fetched together (entries
+            // past a block's count are read and dropped).
             __shared__ int rl[kDirectMaxT];
             __shared__ int boff[kDirectMaxBlocks + 1], bc[kDirectMaxBlocks];
-            const int e = q / nt0, n0 = (q % nt0) * BN;
             const int nb = args.direct_nb;
-            if (threadIdx.x < kWave) {
-                const int lane = threadIdx.x;
-                const int c = lane < nb ? args.direct_bcnt[lane * args.E + e] : 0;
+            const int lv = tid < nb * 16 ? args.direct_blist[((int64_t)(tid >> 4) * args.E + e) * 16 + (tid & 15)] : 0;
+            if (tid < kWave) {
+                const int c = tid < nb ? args.direct_bcnt[tid * args.E + e] : 0;
                 const int incl = wave_incl_scan(c);
-                if (lane < nb) { boff[lane] = incl - c; bc[lane] = c; }
-                if (lane == kWave - 1) boff[kDirectMaxBlocks] = incl;
+                if (tid < nb) { boff[tid] = incl - c; bc[tid] = c; }
+                if (tid == kWave - 1) boff[kDirectMaxBlocks] = incl;
             }
             __syncthreads();
-            for (int i = threadIdx.x; i < nb * 16; i += blockDim.x) {
-                const int b = i >> 4, s = i & 15;
-                if (s < bc[b]) rl[boff[b] + s] = args.direct_blist[((int64_t)b * args.E + e) * 16 + s];
-            }
+            if (tid < nb * 16 && (tid & 15) < bc[tid >> 4]) rl[boff[tid >> 4] + (tid & 15)] = lv;
             __syncthreads();
             const int m = boff[kDirectMaxBlocks];
-            if (n0 == 0 && threadIdx.x == 0 && args.direct_counts) args.direct_counts[e] = m;
-            const int base = e * args.direct_T;
-            for (int m0 = 0; m0 < m; m0 += BM)
-                tile(0, e, n0, base + m0, min(BM, m - m0), PASS == 0 ? rl + m0 : nullptr, PASS == 1 ? rl + m0 : nullptr);
+            if (n0 == 0 && tid == 0 && args.direct_counts) args.direct_counts[e] = m;
+            if (m == 0) {
+                if (PASS == 1) __builtin_amdgcn_s_waitcnt(0);  // nothing to compute: drain the early loads
+                return;
+            }
+            for (int m0 = 0; m0 < m; m0 += BM) {
+                const int mr = min(BM, m - m0);
+                if (PASS == 1 && m0 > 0) {
+                    load_b(0);
+                    set_a(g, base + m0, mr, nullptr);
+                    load_a(0);
+                }
+                if (PASS == 0) {
+                    if (m0 == 0) set_b(g, e, n0);
+                    set_a(g, 0, mr, rl + m0);
+                    load_b(0);
+                    load_a(0);
+                }
+                run(g, n0, base + m0, mr, PASS == 1 ? rl + m0 : nullptr);
+            }
         } else {
             q -= n_routed;
+            const GemmGroup& g = args.g[1];
             const int n0 = (q / args.direct_mt1) * BN, m0 = (q % args.direct_mt1) * BM;
-            tile(1, 0, n0, m0, min(BM, args.direct_T - m0), nullptr, nullptr);
+            const int mr = min(BM, args.direct_T - m0);
+            set_b(g, 0, n0);
+            set_a(g, m0, mr, nullptr);
+            load_b(0);
+            load_a(0);
+            run(g, n0, m0, mr, nullptr);
         }
         return;
     }
@@ -216,7 +267,12 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs args) {
     if (q >= n_items) return;
     const int4 it = args.items[q];
     const int gi = it.x < args.E ? 0 : 1;
-    tile(gi, gi == 0 ? it.x : 0, it.y, it.z, it.w, nullptr, nullptr);
+    const GemmGroup& g = args.g[gi];
+    set_b(g, gi == 0 ? it.x : 0, it.y);
+    set_a(g, it.z, it.w, nullptr);
+    load_b(0);
+    load_a(0);
+    run(g, it.y, it.z, it.w, nullptr);
 }
 
 // ---------------------------------------------------------------------------

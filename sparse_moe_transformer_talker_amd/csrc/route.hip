@@ -578,10 +578,11 @@ __global__ __launch_bounds__(64 * kS64Waves) void scores64_kernel(const bf16_t* 
 // Router for bf16 with E = 16 NS experts (NS in {1, 2, 4, 8}), H a multiple of
 // 128 (8 / NS), H <= 1024, k <= 16: one block of 8 waves per 16 tokens; scores never
 // leave LDS.
-//   scores: the block stages its 16 token rows in LDS.  Wave w scores expert
-//     tile w % NS over the stages s (128 K-elements each) with s % (8 / NS) ==
-//     w / NS, streaming its own 16 W_r rows through a private LDS slice: lanes
-//     load whole 256-byte row slices (four rows per instruction; reading the
+//   scores: the block stages its 16 token rows in LDS (their loads go out
+//     first, ahead of the weight stream).  Wave w scores expert tile w % NS
+//     over the stages s (128 K-elements each) with s % (8 / NS) == w / NS,
+//     streaming its own 16 W_r rows through a private LDS slice: lanes load
+//     whole 256-byte row slices (four rows per instruction; reading the
 //     matrix-core fragment shape, 16 rows x 64 bytes per instruction, straight
 //     from memory streams several times slower), DEPTH stages in flight in
 //     registers, and no block barrier in the loop.  Staged rows are padded by
@@ -589,10 +590,11 @@ __global__ __launch_bounds__(64 * kS64Waves) void scores64_kernel(const bf16_t* 
 //     matrix-core step (32 exact products summed in fp32) is a fresh partial
 //     added into fp64, beside the abs-sum that bounds the error; the K groups
 //     are added in LDS in a fixed order (deterministic).
-//   selection: waves 0..3 select four tokens each, one per 16-lane row
-//     (select_rows_wave: certified fp32 ranking); tokens left uncertain are
-//     then taken by the eight waves in parallel, one each, with fp64
-//     rescoring of their candidates (route_exact_token).
+//   selection: one token per 32-lane half-wave (route_select_half: certified
+//     fp32 ranking; lane ri holds experts ri + 32 j).  Tokens left uncertain
+//     are redone exactly by the whole block: candidate lists, then the fp64
+//     rescoring of every (token, candidate) pair spread over the eight waves,
+//     then a rank count per token (route_exact_picks).
 //   outputs: idx / weights (/ probs); per (expert, 16-token block) a token mask
 //     (masks != null), or per block and expert the count and list of its pairs
 //     t * k + j (bcnt != null; list order within a block is arbitrary).
@@ -601,71 +603,189 @@ constexpr int kRouteThreads = 64 * kRouteWaves;
 constexpr int kRouteMaxH = 1024;
 constexpr int kRouteStageK = 128;  // K-elements per W_r stage
 
-// Exact Top-k of one token whose fp32 selection was not certain.  Every score
-// that may reach the fp32 picks (s + d >= low, the picks included) is rescored
-// in fp64 (bf16 products are exact there), and the k best are taken by value,
-// ties to the lower index: every expert of the exact Top-k is among these
-// candidates, because the k picks all have exact scores >= low.  One full wave;
-// lane r < k writes pick r.  Lists: lcnt (nullable) / llist as in the router.
+// All-reductions over a 32-lane half-wave: the 16-lane row step, then the
+// partner row (lane ^ 16) through a swizzle.
+__device__ __forceinline__ uint32_t swz_xor16(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F);  // bit mode: and 31, xor 16
+}
+__device__ __forceinline__ uint32_t half_max_u32(uint32_t x) {
+    x = row_max_u32(x);
+    return umax32(x, swz_xor16(x));
+}
+__device__ __forceinline__ float half_max(float x) {
+    x = row_max(x);
+    return fmaxf(x, __uint_as_float(swz_xor16(__float_as_uint(x))));
+}
+__device__ __forceinline__ float half_sum(float x) {
+    x = row_sum(x);
+    return x + __uint_as_float(swz_xor16(__float_as_uint(x)));
+}
+__device__ __forceinline__ double half_min(double x) {
+    uint64_t kk = row_max_key(~double_order_key(x));
+    const uint64_t o = ((uint64_t)swz_xor16((uint32_t)(kk >> 32)) << 32) | swz_xor16((uint32_t)kk);
+    kk = o > kk ? o : kk;
+    return double_from_order_key(~kk);
+}
+
+// The picks of the block's tokens, by rank: fp32 value, its bound, expert.
+struct BlockPicks {
+    float v[16][16];
+    double d[16][16];
+    int e[16][16];
+};
+
+// Certified fp32 Top-k of token tt of the block on one 32-lane half-wave
+// (lane ri holds experts ri + 32 j).  s / a: the token's fp64 score sums and
+// fp32 abs-sums; on return s holds the biased score and a its error bound
+// (for the exact pass).  A certain token's outputs are written here; an
+// uncertain one is appended to dfr with the lowest bound of its picks.
 template <int J>
-__device__ void route_exact_token(const double* s, const float* d, int E, int k, int norm, double low,
-                                  const bf16_t* xrow, const bf16_t* W, int H, const float* bias, int32_t* oidx,
-                                  float* ow, float* oprob, uint32_t* msk, int bit, int* lcnt, int* llist, int pair0) {
-    const int lane = lane_id();
+__device__ __forceinline__ void route_select_half(double* __restrict__ s, float* __restrict__ a,
+                                                  const float* __restrict__ bsh, int E, int H, int k, int norm,
+                                                  bool valid, int tt, int64_t t, int32_t* __restrict__ out_idx,
+                                                  float* __restrict__ out_w, float* __restrict__ out_probs,
+                                                  uint32_t* msk, int* lcnt, int* llist, BlockPicks& pk,
+                                                  Deferred* dfr) {
+    const int lane = lane_id(), ri = lane & 31;
+    const double es = partial_error_scale(), fs = fp64_error_scale(H);
     float v[J];
-    bool cand[J];
-    double v64[J];
+    double dv[J];
+    // ranking keys: the order key of the value with its low byte replaced by
+    // 255 - e (E <= 128), unique and never 0; 0 once picked or absent.  Values
+    // that differ only in that byte may come out misordered, which the
+    // certificate below (on the exact fp32 values) always rejects.
+    uint32_t key[J];
+    int pick[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        const int e = ri + 32 * j;
+        const bool ok = valid && e < E;
+        const int ec = ok ? e : 0;
+        const float bb = bsh ? bsh[ec] : 0.f;
+        const double sv = s[ec] + (double)bb;
+        const double ab = (double)a[ec];
+        const float dd = (float)(es * ab + fs * (ab + fabs((double)bb))) * (1.0f + kTwoM23);
+        if (ok) {
+            s[e] = sv;
+            a[e] = dd;
+        }
+        v[j] = ok ? (float)sv + 0.0f : 0.0f;
+        dv[j] = ok ? (double)dd + 1.1920928955078125e-07 * fabs((double)v[j]) : 0.0;
+        key[j] = ok ? ((float_order_key(v[j]) & 0xFFFFFF00u) | (uint32_t)(255 - e)) : 0u;
+        pick[j] = -1;
+    }
+    for (int r = 0; r < k; ++r) {
+        uint32_t m = 0;
+#pragma unroll
+        for (int j = 0; j < J; ++j) m = umax32(m, key[j]);
+        m = half_max_u32(m);
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const bool hit = key[j] == m && m != 0;
+            pick[j] = hit ? r : pick[j];
+            key[j] = hit ? 0u : key[j];
+        }
+    }
+    bool taken[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        taken[j] = !(valid && ri + 32 * j < E) || pick[j] >= 0;
+        if (pick[j] >= 0) {
+            pk.v[tt][pick[j]] = v[j];
+            pk.d[tt][pick[j]] = dv[j];
+            pk.e[tt][pick[j]] = ri + 32 * j;
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+    // certain: consecutive picks strictly separated, and nothing else can reach the lowest pick
+    bool bad = false;
+    double lo = 1.0e300;
+    if (valid && ri < k) {
+        lo = (double)pk.v[tt][ri] - pk.d[tt][ri];
+        if (ri > 0) bad = !((double)pk.v[tt][ri - 1] - pk.d[tt][ri - 1] > (double)pk.v[tt][ri] + pk.d[tt][ri]);
+    }
+    const double low = half_min(lo);
+#pragma unroll
+    for (int j = 0; j < J; ++j)
+        if (!taken[j] && (double)v[j] + dv[j] >= low) bad = true;
+    const uint64_t badmask = __ballot(valid && bad);
+    const bool certain = ((badmask >> (lane & 32)) & 0xFFFFFFFFull) == 0;
+    if (valid && certain) {
+        float mx = 0.f, z = 1.f;
+        if (out_probs || !norm) {
+            mx = -3.0e38f;
+#pragma unroll
+            for (int j = 0; j < J; ++j)
+                if (ri + 32 * j < E) mx = fmaxf(mx, v[j]);
+            mx = half_max(mx);
+            z = 0.f;
+#pragma unroll
+            for (int j = 0; j < J; ++j)
+                if (ri + 32 * j < E) z += __expf(v[j] - mx);
+            z = half_sum(z);
+            if (out_probs) {
+                const float inv = 1.0f / z;
+#pragma unroll
+                for (int j = 0; j < J; ++j)
+                    if (ri + 32 * j < E) out_probs[t * E + ri + 32 * j] = __expf(v[j] - mx) * inv;
+            }
+        }
+        float ex = 0.f;
+        if (ri < k) ex = norm ? __expf(pk.v[tt][ri] - pk.v[tt][0]) : __expf(pk.v[tt][ri] - mx);
+        const float den = norm ? half_sum(ex) : z;
+        if (ri < k) {
+            const int e = pk.e[tt][ri];
+            out_idx[t * k + ri] = e;
+            out_w[t * k + ri] = ex / den;
+            atomicOr(&msk[e], 1u << tt);
+            if (lcnt) llist[e * 16 + atomicAdd(&lcnt[e], 1)] = (int)(t * k + ri);
+        }
+    }
+    if (valid && !certain && ri == 0) {
+        const int u = atomicAdd(&dfr->n, 1);
+        dfr->tok[u] = tt;
+        dfr->low[u] = low;
+    }
+}
+
+// Exact Top-k of an uncertain token from its rescored candidates (one full
+// wave): every score that may reach the fp32 picks (value + bound >= low, the
+// picks included) has been rescored in fp64 (bf16 products are exact there),
+// and the k best are taken by value, ties to the lower index.  Every expert of
+// the exact Top-k is among the candidates, because the k picks all have exact
+// scores >= low.  cs / ce: the candidates' exact scores and experts, in
+// expert order; s: the token's biased scores (fp32 softmax statistics).
+template <int J>
+__device__ void route_exact_picks(const double* s, const double* cs, const int* ce, int nc, int E, int k, int norm,
+                                  int tt, int64_t t, int32_t* oidx, float* ow, float* oprob, uint32_t* msk,
+                                  int* lcnt, int* llist, BlockPicks& pk) {
+    const int lane = lane_id();
+    // rank of candidate l: how many candidates come before it
+#pragma unroll
+    for (int h = 0; h < J; ++h) {
+        const int l = lane + 64 * h;
+        const bool ok = l < nc;
+        const double sl = ok ? cs[l] : 0.0;
+        const int el = ok ? ce[l] : 0;
+        int rank = 0;
+        for (int m = 0; m < nc; ++m) {
+            const double sm = cs[m];
+            const int em = ce[m];
+            rank += (sm > sl || (sm == sl && em < el)) ? 1 : 0;
+        }
+        if (ok && rank < k) {
+            pk.d[tt][rank] = sl;  // here: the exact score
+            pk.e[tt][rank] = el;
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+    // softmax statistics over all E in fp32 (probs, and the plain weights)
+    float v[J];
 #pragma unroll
     for (int j = 0; j < J; ++j) {
         const int e = lane + kWave * j;
-        const bool ok = e < E;
-        v[j] = ok ? (float)s[e] + 0.0f : 0.0f;
-        const double dv = ok ? (double)d[e] + 1.1920928955078125e-07 * fabs((double)v[j]) : 0.0;
-        cand[j] = ok && (double)v[j] + dv >= low;
-        v64[j] = 0.0;
+        v[j] = e < E ? (float)s[e] + 0.0f : 0.0f;
     }
-#pragma unroll
-    for (int j = 0; j < J; ++j) {
-        uint64_t cm = __ballot(cand[j]);
-        while (cm) {
-            int ids[8];
-            const int cnt = take8(cm, kWave * j, ids);
-            double r8[8];
-            wave_dot64<bf16_t, 8>(xrow, W, H, ids, cnt, r8);
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                if (i < cnt && lane + kWave * j == ids[i]) v64[j] = r8[i] + (bias ? (double)bias[ids[i]] : 0.0);
-        }
-    }
-    int my_e = 0;
-    double my_s = 0.0;
-    for (int r = 0; r < k; ++r) {
-        uint64_t m = 0;
-#pragma unroll
-        for (int j = 0; j < J; ++j)
-            if (cand[j]) {
-                const uint64_t kk = double_order_key(v64[j]);
-                m = kk > m ? kk : m;
-            }
-        m = wave_max_key(m);
-        uint64_t ik = 0;
-#pragma unroll
-        for (int j = 0; j < J; ++j)
-            if (cand[j] && double_order_key(v64[j]) == m) {
-                const uint64_t c = 0xFFFFFFFFull - (uint64_t)(lane + kWave * j);
-                ik = c > ik ? c : ik;
-            }
-        ik = wave_max_key(ik);
-        const int bi = (int)(0xFFFFFFFFull - ik);
-#pragma unroll
-        for (int j = 0; j < J; ++j)
-            if (lane + kWave * j == bi) cand[j] = false;
-        if (lane == r) {
-            my_e = bi;
-            my_s = double_from_order_key(m);
-        }
-    }
-    // softmax statistics over all E in fp32 (probs, and the plain weights)
     float mx = 0.f, z = 1.f;
     if (oprob || !norm) {
         mx = -3.0e38f;
@@ -682,17 +802,19 @@ __device__ void route_exact_token(const double* s, const float* d, int E, int k,
             const float inv = 1.0f / z;
 #pragma unroll
             for (int j = 0; j < J; ++j)
-                if (lane + kWave * j < E) oprob[lane + kWave * j] = __expf(v[j] - mx) * inv;
+                if (lane + kWave * j < E) oprob[t * E + lane + kWave * j] = __expf(v[j] - mx) * inv;
         }
     }
-    const double s0 = __shfl(my_s, 0, kWave);
+    const int r = lane < k ? lane : 0;
+    const double my_s = pk.d[tt][r], s0 = pk.d[tt][0];
+    const int my_e = pk.e[tt][r];
     const float ex = lane < k ? (norm ? (float)exp(my_s - s0) : __expf((float)my_s - mx)) : 0.f;
     const float den = norm ? wave_sum_dpp(ex) : z;
     if (lane < k) {
-        oidx[lane] = my_e;
-        ow[lane] = ex / den;
-        atomicOr(&msk[my_e], 1u << bit);
-        if (lcnt) llist[my_e * 16 + atomicAdd(&lcnt[my_e], 1)] = pair0 + lane;
+        oidx[t * k + lane] = my_e;
+        ow[t * k + lane] = ex / den;
+        atomicOr(&msk[my_e], 1u << tt);
+        if (lcnt) llist[my_e * 16 + atomicAdd(&lcnt[my_e], 1)] = (int)(t * k + lane);
     }
 }
 
@@ -707,23 +829,36 @@ __global__ __launch_bounds__(kRouteThreads) void route_block_kernel(
     constexpr int XCH = 16 * (kRouteMaxH / 8) / kRouteThreads;  // staged x chunks per thread (max)
     constexpr int SLD = kRouteStageK + 8;                       // bf16 per staged W_r row (272 bytes)
     constexpr int WI = 16 * kRouteStageK / 8 / kWave;           // load instructions per stage and wave (4)
+    constexpr int CPL = kRouteMaxH / 8 / kWave;                 // 16-byte chunks per lane of one row (exact pass)
     __shared__ __attribute__((aligned(16))) bf16_t xs[16 * (kRouteMaxH + 8)];
     __shared__ __attribute__((aligned(16))) bf16_t wsb[kRouteWaves][16 * SLD];
     __shared__ double lg[16 * E];
     __shared__ float ab[16 * E];
+    __shared__ float bsh[E];
     __shared__ uint32_t msk[E];
     __shared__ uint64_t jm[E];
     __shared__ int lcnt[E];
     __shared__ int llist[E * 16];
-    __shared__ RowPicks picks[4];
-    __shared__ SelScratch scr[4];
+    __shared__ BlockPicks picks;
     __shared__ Deferred dfr;
+    __shared__ int cnc[16];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int64_t tok0 = (int64_t)blockIdx.x * 16;
     const int XLD = H + 8;
     const int tile = wave % NS, g = wave / NS;
     const int nmine = H / (kRouteStageK * KG);  // this wave's stages g, g + KG, ...; a multiple of DEPTH
 
+    // the block's token rows (rows past T repeat row T - 1; never used): their
+    // loads go out first, the weight stream behind them
+    const int cpr = H / 8, nxc = 16 * cpr;
+    u32x4 xv[XCH];
+#pragma unroll
+    for (int j = 0; j < XCH; ++j) {
+        const int c = min(tid + j * kRouteThreads, nxc - 1);
+        const int r = c / cpr, q = c % cpr;
+        const int64_t t = tok0 + r < T ? tok0 + r : T - 1;
+        xv[j] = *reinterpret_cast<const u32x4*>(x + t * H + q * 8);
+    }
     // stage m of this wave: lane l loads row 4 j + l / 16, 16-byte chunk l % 16
     // of K-slice st = g + m KG of rows tile * 16 .. + 15
     const bf16_t* wsrc = W + (int64_t)(tile * 16 + (lane >> 4)) * H + (lane & 15) * 8;
@@ -739,27 +874,15 @@ __global__ __launch_bounds__(kRouteThreads) void route_block_kernel(
 
     if (tid == 0) dfr.n = 0;
     for (int q = tid; q < E; q += blockDim.x) {
+        bsh[q] = bias ? bias[q] : 0.f;
         msk[q] = 0;
         jm[q] = 0;
         lcnt[q] = 0;
     }
-    // stage the block's token rows (rows past T repeat row T - 1; never used):
-    // every load first, then the LDS stores
-    {
-        const int cpr = H / 8, n = 16 * cpr;
-        u32x4 v[XCH];
 #pragma unroll
-        for (int j = 0; j < XCH; ++j) {
-            const int c = min(tid + j * kRouteThreads, n - 1);
-            const int r = c / cpr, q = c % cpr;
-            const int64_t t = tok0 + r < T ? tok0 + r : T - 1;
-            v[j] = *reinterpret_cast<const u32x4*>(x + t * H + q * 8);
-        }
-#pragma unroll
-        for (int j = 0; j < XCH; ++j) {
-            const int c = tid + j * kRouteThreads;
-            if (c < n) *reinterpret_cast<u32x4*>(&xs[(c / cpr) * XLD + (c % cpr) * 8]) = v[j];
-        }
+    for (int j = 0; j < XCH; ++j) {
+        const int c = tid + j * kRouteThreads;
+        if (c < nxc) *reinterpret_cast<u32x4*>(&xs[(c / cpr) * XLD + (c % cpr) * 8]) = xv[j];
     }
     __syncthreads();
 
@@ -809,40 +932,112 @@ __global__ __launch_bounds__(kRouteThreads) void route_block_kernel(
         }
         __syncthreads();
     }
-    const double es = partial_error_scale(), fs = fp64_error_scale(H);
-    for (int q = tid; q < 16 * E; q += blockDim.x) {
-        const int e = q % E;
-        const float bb = bias ? bias[e] : 0.f;
-        const double sv = lg[q] + (double)bb;
-        lg[q] = sv;
-        const double a = (double)ab[q];
-        ab[q] = (float)(es * a + fs * (a + fabs((double)bb))) * (1.0f + kTwoM23);
-    }
-    __syncthreads();
 
-    if (wave < 4) {
-        const int64_t t = tok0 + wave * 4 + (lane >> 4);
-        select_rows_wave<bf16_t, NS, double, true>(lg, ab, tok0, t < T ? t : -1, E, k, x, W, H, bias, norm, out_idx,
-                                                   out_w, out_probs, msk, 1, 0, picks[wave], &scr[wave],
-                                                   bcnt ? ListSink{lcnt, llist, 16} : ListSink{}, &dfr);
-    }
-    __syncthreads();
-    // uncertain tokens: one wave each
-    for (int u = wave; u < dfr.n; u += kRouteWaves) {
-        const int tt = dfr.tok[u];
+    // certified selection, one token per half-wave
+    {
+        const int tt = 2 * wave + (lane >> 5);
         const int64_t t = tok0 + tt;
-        route_exact_token<(E + kWave - 1) / kWave>(&lg[tt * E], &ab[tt * E], E, k, norm, dfr.low[u], x + t * H, W, H,
-                                                   bias, out_idx + t * k, out_w + t * k,
-                                                   out_probs ? out_probs + t * E : nullptr, msk, tt,
-                                                   bcnt ? lcnt : nullptr, llist, (int)(t * k));
+        route_select_half<(E + 31) / 32>(&lg[tt * E], &ab[tt * E], bias ? bsh : nullptr, E, H, k, norm, t < T,
+                                         tt, t, out_idx, out_w, out_probs, msk, bcnt ? lcnt : nullptr, llist, picks,
+                                         &dfr);
     }
     __syncthreads();
+    const int nd = dfr.n;
+    if (nd > 0) {
+        // exact pass over the uncertain tokens (LDS of the weight slices reused:
+        // candidate scores [16][E] fp64, then candidate experts [16][E])
+        double* cs = reinterpret_cast<double*>(&wsb[0][0]);
+        int* ce = reinterpret_cast<int*>(cs + 16 * E);
+        static_assert(sizeof(wsb) >= 16 * E * (sizeof(double) + sizeof(int)), "exact-pass scratch fits");
+        // 1. candidate lists, in expert order, one wave per token
+        for (int u = wave; u < nd; u += kRouteWaves) {
+            const int tt = dfr.tok[u];
+            const double low = dfr.low[u];
+            int nc = 0;
+#pragma unroll
+            for (int j = 0; j < (E + 63) / 64; ++j) {
+                const int e = lane + 64 * j;
+                const bool ok = e < E;
+                const float v = ok ? (float)lg[tt * E + e] + 0.0f : 0.0f;
+                const double dv = ok ? (double)ab[tt * E + e] + 1.1920928955078125e-07 * fabs((double)v) : 0.0;
+                const bool c = ok && (double)v + dv >= low;
+                const uint64_t m = __ballot(c);
+                if (c) ce[u * E + nc + __popcll(m & lanemask_lt())] = e;
+                nc += __popcll(m);
+            }
+            if (lane == 0) cnc[u] = nc;
+        }
+        __syncthreads();
+        // 2. fp64 rescoring of every (token, candidate) pair: pairs p and p + 8
+        // of every round of 16 go to wave p % 8, all loads of both issued first
+        int np = 0, cnt_u = 0, off_u = 0;  // lane u < nd: token u's count and first pair
+        if (lane < nd) cnt_u = cnc[lane];
+        {
+            const int incl = wave_incl_scan(cnt_u);
+            off_u = incl - cnt_u;
+            np = __builtin_amdgcn_readlane(incl, 15);  // nd <= 16
+        }
+        for (int p0 = wave; p0 < np; p0 += 2 * kRouteWaves) {
+            int pu[2], pi[2], pe[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int p = min(p0 + h * kRouteWaves, np - 1);
+                // token of pair p: the last u with off_u <= p
+                const uint64_t le = __ballot(lane < nd && off_u <= p);
+                const int u = 63 - __builtin_clzll(le);
+                pu[h] = u;
+                pi[h] = p - __builtin_amdgcn_readlane(off_u, u);
+                pe[h] = ce[u * E + pi[h]];
+            }
+            u32x4 wv[2][CPL], xw[2][CPL];
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) {
+                    const int ch = c * kWave + lane < cpr ? c * kWave + lane : 0;
+                    wv[h][c] = *reinterpret_cast<const u32x4*>(W + (int64_t)pe[h] * H + ch * 8);
+                }
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) {
+                    const int ch = c * kWave + lane < cpr ? c * kWave + lane : 0;
+                    xw[h][c] = *reinterpret_cast<const u32x4*>(&xs[dfr.tok[pu[h]] * XLD + ch * 8]);
+                }
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                double d = 0.0;
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) {
+                    if (c * kWave + lane >= cpr) continue;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        d = fma((double)__uint_as_float(xw[h][c][q] << 16), (double)__uint_as_float(wv[h][c][q] << 16), d);
+                        d = fma((double)__uint_as_float(xw[h][c][q] & 0xFFFF0000u),
+                                (double)__uint_as_float(wv[h][c][q] & 0xFFFF0000u), d);
+                    }
+                }
+                d = wave_sum_dpp_f64(d);
+                const int p = p0 + h * kRouteWaves;
+                if (lane == 0 && p < np) cs[pu[h] * E + pi[h]] = d + (double)bsh[pe[h]];
+            }
+        }
+        __syncthreads();
+        // 3. exact picks and outputs, one wave per token
+        for (int u = wave; u < nd; u += kRouteWaves) {
+            const int tt = dfr.tok[u];
+            const int64_t t = tok0 + tt;
+            route_exact_picks<(E + kWave - 1) / kWave>(&lg[tt * E], &cs[u * E], &ce[u * E], cnc[u], E, k, norm, tt,
+                                                       t, out_idx, out_w, out_probs, msk, bcnt ? lcnt : nullptr,
+                                                       llist, picks);
+        }
+        __syncthreads();
+    }
     if (jmask) {
-        // slot of every choice, 4 bits per token, from this block's routing outputs
+        // slot of every choice, 4 bits per token, from the block's picks
         for (int q = tid; q < 16 * k; q += blockDim.x) {
             const int tt = q / k, j = q % k;
-            if (tok0 + tt < T)
-                atomicOr((unsigned long long*)&jm[out_idx[(tok0 + tt) * k + j]], (unsigned long long)j << (4 * tt));
+            if (tok0 + tt < T) atomicOr((unsigned long long*)&jm[picks.e[tt][j]], (unsigned long long)j << (4 * tt));
         }
         __syncthreads();
         for (int e = tid; e < E; e += blockDim.x) jmask[(int64_t)e * mstride + blockIdx.x] = jm[e];
@@ -858,6 +1053,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_block_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
 // Portable scores: one lane per weight row, 32-term fp32 partials added in
 // fp64; writes fp32 scores and bounds (including the final rounding to fp32)
 // to global [T, n].  Any H, any element type.
