@@ -603,27 +603,37 @@ constexpr int kRouteThreads = 64 * kRouteWaves;
 constexpr int kRouteMaxH = 1024;
 constexpr int kRouteStageK = 128;  // K-elements per W_r stage
 
-// All-reductions over a 32-lane half-wave: the 16-lane row step, then the
-// partner row (lane ^ 16) through a swizzle.
-__device__ __forceinline__ uint32_t swz_xor16(uint32_t v) {
-    return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F);  // bit mode: and 31, xor 16
+// All-reductions over a 32-lane half-wave: the 16-lane row step, then row
+// 2h + 1 takes in lane 15 of row 2h (DPP row broadcast), and every lane of
+// half h reads lane 32 h + 31.  No LDS round trip; one value per half.
+template <typename F>
+__device__ __forceinline__ uint32_t half_bcast(uint32_t x, F op) {
+    const uint32_t y = op(x, (uint32_t)__builtin_amdgcn_update_dpp(0u, x, kDppRowBcast15, 0xa, 0xf, false));
+    const uint32_t h0 = __builtin_amdgcn_readlane(y, 31), h1 = __builtin_amdgcn_readlane(y, 63);
+    return lane_id() < 32 ? h0 : h1;
 }
 __device__ __forceinline__ uint32_t half_max_u32(uint32_t x) {
-    x = row_max_u32(x);
-    return umax32(x, swz_xor16(x));
+    return half_bcast(row_max_u32(x), [](uint32_t a, uint32_t b) { return umax32(a, b); });
 }
 __device__ __forceinline__ float half_max(float x) {
-    x = row_max(x);
-    return fmaxf(x, __uint_as_float(swz_xor16(__float_as_uint(x))));
+    return __uint_as_float(half_bcast(__float_as_uint(row_max(x)), [](uint32_t a, uint32_t b) {
+        return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b)));
+    }));
 }
 __device__ __forceinline__ float half_sum(float x) {
-    x = row_sum(x);
-    return x + __uint_as_float(swz_xor16(__float_as_uint(x)));
+    return __uint_as_float(half_bcast(__float_as_uint(row_sum(x)), [](uint32_t a, uint32_t b) {
+        return __float_as_uint(__uint_as_float(a) + __uint_as_float(b));
+    }));
 }
 __device__ __forceinline__ double half_min(double x) {
     uint64_t kk = row_max_key(~double_order_key(x));
-    const uint64_t o = ((uint64_t)swz_xor16((uint32_t)(kk >> 32)) << 32) | swz_xor16((uint32_t)kk);
+    const uint32_t lo = __builtin_amdgcn_update_dpp(0u, (uint32_t)kk, kDppRowBcast15, 0xa, 0xf, false);
+    const uint32_t hi = __builtin_amdgcn_update_dpp(0u, (uint32_t)(kk >> 32), kDppRowBcast15, 0xa, 0xf, false);
+    const uint64_t o = ((uint64_t)hi << 32) | lo;
     kk = o > kk ? o : kk;
+    const uint32_t l0 = __builtin_amdgcn_readlane((uint32_t)kk, 31), h0 = __builtin_amdgcn_readlane((uint32_t)(kk >> 32), 31);
+    const uint32_t l1 = __builtin_amdgcn_readlane((uint32_t)kk, 63), h1 = __builtin_amdgcn_readlane((uint32_t)(kk >> 32), 63);
+    kk = lane_id() < 32 ? (((uint64_t)h0 << 32) | l0) : (((uint64_t)h1 << 32) | l1);
     return double_from_order_key(~kk);
 }
 
@@ -656,14 +666,23 @@ __device__ __forceinline__ void route_select_half(double* __restrict__ s, float*
     // certificate below (on the exact fp32 values) always rejects.
     uint32_t key[J];
     int pick[J];
+    // all reads first (the write-backs below go to the same rows)
+    double s0[J];
+    float a0[J], b0[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        const int ec = ri + 32 * j < E ? ri + 32 * j : 0;
+        s0[j] = s[ec];
+        a0[j] = a[ec];
+        b0[j] = bsh ? bsh[ec] : 0.f;
+    }
 #pragma unroll
     for (int j = 0; j < J; ++j) {
         const int e = ri + 32 * j;
         const bool ok = valid && e < E;
-        const int ec = ok ? e : 0;
-        const float bb = bsh ? bsh[ec] : 0.f;
-        const double sv = s[ec] + (double)bb;
-        const double ab = (double)a[ec];
+        const float bb = b0[j];
+        const double sv = s0[j] + (double)bb;
+        const double ab = (double)a0[j];
         const float dd = (float)(es * ab + fs * (ab + fabs((double)bb))) * (1.0f + kTwoM23);
         if (ok) {
             s[e] = sv;
@@ -760,24 +779,36 @@ __device__ void route_exact_picks(const double* s, const double* cs, const int* 
                                   int tt, int64_t t, int32_t* oidx, float* ow, float* oprob, uint32_t* msk,
                                   int* lcnt, int* llist, BlockPicks& pk) {
     const int lane = lane_id();
-    // rank of candidate l: how many candidates come before it
+    // rank of candidate l: how many candidates come before it (lane l holds
+    // candidates l + 64 h; the others are broadcast with readlane)
+    double sl[J];
+    int el[J], rank[J];
 #pragma unroll
     for (int h = 0; h < J; ++h) {
         const int l = lane + 64 * h;
-        const bool ok = l < nc;
-        const double sl = ok ? cs[l] : 0.0;
-        const int el = ok ? ce[l] : 0;
-        int rank = 0;
-        for (int m = 0; m < nc; ++m) {
-            const double sm = cs[m];
-            const int em = ce[m];
-            rank += (sm > sl || (sm == sl && em < el)) ? 1 : 0;
-        }
-        if (ok && rank < k) {
-            pk.d[tt][rank] = sl;  // here: the exact score
-            pk.e[tt][rank] = el;
+        sl[h] = l < nc ? cs[l] : 0.0;
+        el[h] = l < nc ? ce[l] : 0;
+        rank[h] = 0;
+    }
+#pragma unroll
+    for (int hm = 0; hm < J; ++hm) {
+        const int n = min(nc - 64 * hm, 64);
+        const uint64_t u = (uint64_t)__double_as_longlong(sl[hm]);
+        for (int m = 0; m < n; ++m) {
+            const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)u, m);
+            const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(u >> 32), m);
+            const double sm = __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+            const int em = __builtin_amdgcn_readlane(el[hm], m);
+#pragma unroll
+            for (int h = 0; h < J; ++h) rank[h] += (sm > sl[h] || (sm == sl[h] && em < el[h])) ? 1 : 0;
         }
     }
+#pragma unroll
+    for (int h = 0; h < J; ++h)
+        if (lane + 64 * h < nc && rank[h] < k) {
+            pk.d[tt][rank[h]] = sl[h];  // here: the exact score
+            pk.e[tt][rank[h]] = el[h];
+        }
     __builtin_amdgcn_wave_barrier();
     // softmax statistics over all E in fp32 (probs, and the plain weights)
     float v[J];
@@ -808,7 +839,8 @@ __device__ void route_exact_picks(const double* s, const double* cs, const int* 
     const int r = lane < k ? lane : 0;
     const double my_s = pk.d[tt][r], s0 = pk.d[tt][0];
     const int my_e = pk.e[tt][r];
-    const float ex = lane < k ? (norm ? (float)exp(my_s - s0) : __expf((float)my_s - mx)) : 0.f;
+    // renormalised weights from the exact score differences (<= 0)
+    const float ex = lane < k ? (norm ? __expf((float)(my_s - s0)) : __expf((float)my_s - mx)) : 0.f;
     const float den = norm ? wave_sum_dpp(ex) : z;
     if (lane < k) {
         oidx[t * k + lane] = my_e;
@@ -838,7 +870,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_block_kernel(
     __shared__ uint32_t msk[E];
     __shared__ uint64_t jm[E];
     __shared__ int lcnt[E];
-    __shared__ int llist[E * 16];
+    __shared__ __attribute__((aligned(16))) int llist[E * 16];
     __shared__ BlockPicks picks;
     __shared__ Deferred dfr;
     __shared__ int cnc[16];
@@ -859,6 +891,11 @@ __global__ __launch_bounds__(kRouteThreads) void route_block_kernel(
         const int64_t t = tok0 + r < T ? tok0 + r : T - 1;
         xv[j] = *reinterpret_cast<const u32x4*>(x + t * H + q * 8);
     }
+    float bias_v = 0.f;  // E <= 128 < block size: one entry per thread
+    if (bias != nullptr && tid < E) bias_v = bias[tid];
+    // every wave's token-row loads enter the CU's load pipeline before any
+    // weight load (which it serves in order): a barrier on issue, not on data
+    __builtin_amdgcn_s_barrier();
     // stage m of this wave: lane l loads row 4 j + l / 16, 16-byte chunk l % 16
     // of K-slice st = g + m KG of rows tile * 16 .. + 15
     const bf16_t* wsrc = W + (int64_t)(tile * 16 + (lane >> 4)) * H + (lane & 15) * 8;
@@ -873,17 +910,17 @@ __global__ __launch_bounds__(kRouteThreads) void route_block_kernel(
     for (int d = 0; d < DEPTH; ++d) wload(d, wr[d]);
 
     if (tid == 0) dfr.n = 0;
-    for (int q = tid; q < E; q += blockDim.x) {
-        bsh[q] = bias ? bias[q] : 0.f;
-        msk[q] = 0;
-        jm[q] = 0;
-        lcnt[q] = 0;
+    if (tid < E) {
+        msk[tid] = 0;
+        jm[tid] = 0;
+        lcnt[tid] = 0;
     }
 #pragma unroll
     for (int j = 0; j < XCH; ++j) {
         const int c = tid + j * kRouteThreads;
         if (c < nxc) *reinterpret_cast<u32x4*>(&xs[(c / cpr) * XLD + (c % cpr) * 8]) = xv[j];
     }
+    if (tid < E) bsh[tid] = bias_v;
     __syncthreads();
 
     const int i = lane & 15, kq = (lane >> 4) * 8;
@@ -895,30 +932,34 @@ __global__ __launch_bounds__(kRouteThreads) void route_block_kernel(
     const f32x4 zero = {0, 0, 0, 0};
     double acc[4] = {0.0, 0.0, 0.0, 0.0};
     f32x4 aacc = zero;
-    for (int m0 = 0; m0 < nmine; m0 += DEPTH) {
+    // stage m: its registers go to the wave's own LDS slice (its earlier
+    // fragment reads are ordered before these stores), the registers are
+    // refilled with stage m + DEPTH (refill false: none left), then the
+    // stage's matrix work
+    auto stage = [&](const int m, u32x4* r, const bool refill) {
 #pragma unroll
-        for (int d = 0; d < DEPTH; ++d) {
-            const int m = m0 + d;
-            // the wave's own LDS slice: its earlier fragment reads are ordered
-            // before these stores
+        for (int j = 0; j < WI; ++j) *reinterpret_cast<u32x4*>(&wb[wst + 4 * j * SLD]) = r[j];
+        if (refill) wload(m + DEPTH, r);
+        const int k0 = (g + m * KG) * kRouteStageK;
 #pragma unroll
-            for (int j = 0; j < WI; ++j) *reinterpret_cast<u32x4*>(&wb[wst + 4 * j * SLD]) = wr[d][j];
-            wload(min(m + DEPTH, nmine - 1), wr[d]);  // past the end: the last stage again, unused
-            const int k0 = (g + m * KG) * kRouteStageK;
+        for (int ks = 0; ks < kRouteStageK; ks += 32) {
+            const u32x4 a = *reinterpret_cast<const u32x4*>(xr + k0 + ks);
+            const u32x4 b = *reinterpret_cast<const u32x4*>(wfr + ks);
+            const f32x4 p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), zero, 0, 0, 0);
+            aacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a & absmask),
+                                                           __builtin_bit_cast(bf16x8, b & absmask), aacc, 0, 0, 0);
 #pragma unroll
-            for (int ks = 0; ks < kRouteStageK; ks += 32) {
-                const u32x4 a = *reinterpret_cast<const u32x4*>(xr + k0 + ks);
-                const u32x4 b = *reinterpret_cast<const u32x4*>(wfr + ks);
-                const f32x4 p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), zero, 0, 0, 0);
-                aacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a & absmask),
-                                                               __builtin_bit_cast(bf16x8, b & absmask), aacc, 0, 0,
-                                                               0);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) acc[r] += (double)p[r];
-            }
+            for (int r = 0; r < 4; ++r) acc[r] += (double)p[r];
         }
+    };
+    // the last DEPTH stages issue no loads (nothing left in flight to wait for later)
+    for (int m0 = 0; m0 + DEPTH < nmine; m0 += DEPTH) {
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d) stage(m0 + d, wr[d], true);
     }
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) stage(nmine - DEPTH + d, wr[d], false);
     // D[token 4 (lane / 16) + r][expert lane % 16] per tile; K groups added in order
 #pragma unroll
     for (int gg = 0; gg < KG; ++gg) {
@@ -1045,11 +1086,12 @@ __global__ __launch_bounds__(kRouteThreads) void route_block_kernel(
     if (masks)
         for (int e = tid; e < E; e += blockDim.x) masks[(int64_t)e * mstride + blockIdx.x] = (uint16_t)msk[e];
     if (bcnt) {
+        // whole list rows: entries past an expert's count are copied too, and
+        // readers drop them
         int32_t* cnt_b = bcnt + (int64_t)blockIdx.x * E;
-        int32_t* list_b = blist + (int64_t)blockIdx.x * E * 16;
+        int4* list_b = reinterpret_cast<int4*>(blist + (int64_t)blockIdx.x * E * 16);
         for (int e = tid; e < E; e += blockDim.x) cnt_b[e] = lcnt[e];
-        for (int q = tid; q < E * 16; q += blockDim.x)
-            if ((q & 15) < lcnt[q >> 4]) list_b[q] = llist[q];
+        for (int q = tid; q < E * 4; q += blockDim.x) list_b[q] = reinterpret_cast<const int4*>(llist)[q];
     }
 }
 
