@@ -89,7 +89,7 @@ __global__ __launch_bounds__(128) void combine_bf16x8_kernel(const bf16_t* __res
         u32x4 o;
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-            o[q] = (uint32_t)f32_to_bf16(acc[2 * q]) | ((uint32_t)f32_to_bf16(acc[2 * q + 1]) << 16);
+            o[q] = pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
         *reinterpret_cast<u32x4*>(y + t * H + h) = o;
     }
 }

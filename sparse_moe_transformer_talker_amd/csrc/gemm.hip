@@ -166,8 +166,7 @@ __global__ __launch_bounds__(256, PASS == 1 ? 6 : 1) void grouped_gemm_kernel(Ge
                     const int col = n0 + wn * TN + b * 16 + li;
                     float val;
                     if (PASS == 0) {
-                        float gv = acc[a][b][r];
-                        val = gv / (1.0f + __expf(-gv)) * accu[a][b][r];
+                        val = silu(acc[a][b][r]) * accu[a][b][r];
                     } else {
                         val = acc[a][b][r] * sc;
                     }
@@ -492,15 +491,14 @@ __global__ __launch_bounds__(256) void grouped_gemm_lds_kernel(GemmArgs args) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     if (PASS == 0) {
-                        const float gv = acc[a][b][4 * j + q];
-                        v[q] = gv / (1.0f + __expf(-gv)) * acc[a][b + 2][4 * j + q];
+                        v[q] = silu(acc[a][b][4 * j + q]) * acc[a][b + 2][4 * j + q];
                     } else {
                         v[q] = acc[a][b][4 * j + q] * row_sc[a];
                     }
                 }
                 uint2 pk;
-                pk.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-                pk.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+                pk.x = pack_bf16x2(v[0], v[1]);
+                pk.y = pack_bf16x2(v[2], v[3]);
                 const int c = ((PASS == 0 ? wn * 64 : wn * 128) + b * 32 + 8 * j) / 8;  // 16-byte chunk
                 *reinterpret_cast<uint2*>(rp + ((c ^ (r % CPR)) * 16) + lh * 8) = pk;
             }
@@ -544,7 +542,7 @@ __global__ __launch_bounds__(256) void gemm_generic_kernel(GemmGroup g, const in
             s0 = fmaf(av, Elem<T>::load(wa, kk), s0);
             s1 = fmaf(av, Elem<T>::load(wb, kk), s1);
         }
-        s0 = s0 / (1.0f + __expf(-s0)) * s1;
+        s0 = silu(s0) * s1;
     } else {
         for (int kk = 0; kk < g.K; ++kk) s0 = fmaf(Elem<T>::load(a, kk), Elem<T>::load(wa, kk), s0);
     }
