@@ -205,9 +205,12 @@ int run_gemm_pass(const moe_config* c, const GemmPlan& plan, int pass, const Gem
         GemmArgs a{};
         a.g[0] = g0;
         a.g[1] = g1;
-        a.items = plan.t[pass].items;
-        a.count = plan.t[pass].count;
+        const TileSpec& ts = plan.t[pass];
+        a.items = ts.items;
+        a.count = ts.count;
         a.E = routed_rows > 0 ? c->num_experts : 0;
+        a.n_shared_items = (g1.N > 0 && T > 0) ? (int)(((T + ts.mt - 1) / ts.mt) * (g1.N / ts.nt)) : 0;
+        a.shared_first = (g1.N > 0 && routed_rows > 0 && g1.K > g0.K) ? 1 : 0;
         TMOE_TRY(launch_grouped_gemm(c->dtype, plan.variant, pass, a, plan.max_items[pass], st, ev_start, ev_stop));
         return MOE_OK;
     }

@@ -27,6 +27,29 @@ namespace tmoe {
 constexpr int kDirectMaxT = 256;
 constexpr int kDirectMaxBlocks = kDirectMaxT / 16;
 
+// Item of workgroup p in a device-built tile list, or -1.  Workgroup p runs on
+// XCD p % 8; each XCD takes a contiguous run of the routed items (tiles that
+// share a weight block or token rows are adjacent) and an equal share of the
+// shared-expert items, before or after its routed run.  The grid has at least
+// 8 (ceil(n / 8) + 1) workgroups for a list of n items.
+__device__ __forceinline__ int list_item(const GemmArgs& args, int p) {
+    const int n = *args.count;
+    const int ns = min(args.n_shared_items, n), nr = n - ns;
+    const int cr = (nr + 7) >> 3, cs = (ns + 7) >> 3;
+    const int slot = p >> 3, x = p & 7;
+    const int first = args.shared_first ? cs : cr;  // slots of the kind taken first
+    if (slot < first) {
+        const int i = x * first + slot;
+        if (args.shared_first) return i < ns ? nr + i : -1;
+        return i < nr ? i : -1;
+    }
+    const int second = args.shared_first ? cr : cs;
+    const int i = x * second + (slot - first);
+    if (slot - first >= second) return -1;
+    if (args.shared_first) return i < nr ? i : -1;
+    return i < ns ? nr + i : -1;
+}
+
 template <int PASS, int BM, int BN, int BK, int WM, int WN>
 __global__ __launch_bounds__(256, PASS == 1 ? 6 : 1) void grouped_gemm_kernel(GemmArgs args) {
     constexpr int BROWS = (PASS == 0) ? 2 * BN : BN;
@@ -258,12 +281,8 @@ __global__ __launch_bounds__(256, PASS == 1 ? 6 : 1) void grouped_gemm_kernel(Ge
         }
         return;
     }
-    const int n_items = *args.count;
-    const int chunk = (n_items + 7) >> 3;
-    const int slot = p >> 3;
-    if (slot >= chunk) return;
-    const int q = (p & 7) * chunk + slot;
-    if (q >= n_items) return;
+    const int q = list_item(args, p);
+    if (q < 0) return;
     const int4 it = args.items[q];
     const int gi = it.x < args.E ? 0 : 1;
     const GemmGroup& g = args.g[gi];
@@ -323,13 +342,8 @@ __global__ __launch_bounds__(256) void grouped_gemm_lds_kernel(GemmArgs args) {
     __shared__ __attribute__((aligned(1024))) char buf2[STAGE];
     __shared__ __attribute__((aligned(1024))) char buf3[STAGE];
 
-    const int n_items = *args.count;
-    const int p = blockIdx.x;
-    const int chunk = (n_items + 7) >> 3;
-    const int slot = p >> 3;
-    if (slot >= chunk) return;
-    const int q = (p & 7) * chunk + slot;
-    if (q >= n_items) return;
+    const int q = list_item(args, blockIdx.x);
+    if (q < 0) return;
     const int4 it = args.items[q];
     const int gi = it.x < args.E ? 0 : 1;
     const GemmGroup& g = args.g[gi];
@@ -601,8 +615,8 @@ hipError_t launch_gemm(Kernel kernel, unsigned grid, hipStream_t st, hipEvent_t 
 hipError_t launch_grouped_gemm(int dtype, int variant, int pass, const GemmArgs& args, int64_t max_items,
                                hipStream_t st, hipEvent_t ev_start, hipEvent_t ev_stop) {
     (void)dtype;
-    const unsigned grid = (unsigned)(((max_items + 7) / 8) * 8);
-    if (grid == 0) return hipSuccess;
+    if (max_items <= 0) return hipSuccess;
+    const unsigned grid = (unsigned)(((max_items + 7) / 8 + 1) * 8);  // one more slot per XCD: see list_item
     if (variant == kGemmSmallM) {
         if (pass == 0) return launch_gemm(grouped_gemm_kernel<TMOE_SMALL_GU>, grid, st, ev_start, ev_stop, args);
         if (!k_multiple(args, 128))

@@ -96,6 +96,11 @@ struct GemmArgs {
     const int4* items;
     const int* count;
     int E;
+    // The list holds the routed tiles, then n_shared_items shared-expert tiles.
+    // Each XCD takes an equal share of both kinds, the shared ones first when
+    // shared_first (their reduction is longer), else last.
+    int n_shared_items;
+    int shared_first;
     // Direct tiling (when direct_bcnt is not null; small-M kernel only): the grid
     // is E * direct_nt[0] routed tiles, expert-major, then direct_nt[1] x
     // direct_mt1 shared tiles.  A routed tile of expert e concatenates the
