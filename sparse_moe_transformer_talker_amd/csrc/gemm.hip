@@ -308,14 +308,18 @@ __global__ __launch_bounds__(256, PASS == 1 ? 6 : 1) void grouped_gemm_kernel(Ge
 namespace lds_gemm {
 constexpr int BNR = 256, BK = 32;
 constexpr int NSTAGE = 4, INFLIGHT = NSTAGE - 1;
+// Eight waves, two per SIMD (so one wave's matrix work covers the other's LDS
+// reads and waits), as 4 token rows x 2 feature halves of 128.
+constexpr int NWAVE = 8;
 constexpr int B_BYTES = BNR * BK * 2;
-constexpr int B_CALLS = B_BYTES / 1024 / 4;  // per wave, per stage
+constexpr int B_CALLS = B_BYTES / 1024 / NWAVE;  // per wave, per stage
 template <int BM> struct Tile {
     static constexpr int A_BYTES = BM * BK * 2;
     static constexpr int STAGE = A_BYTES + B_BYTES;
-    static constexpr int A_CALLS = A_BYTES / 1024 / 4;
+    static constexpr int A_CALLS = A_BYTES / 1024 / NWAVE;
     static constexpr int CALLS = A_CALLS + B_CALLS;
-    static constexpr int MI = BM / 64;  // 32-row blocks per wave (2 x 2 waves)
+    static constexpr int WROWS = BM / (NWAVE / 2);  // token rows per wave
+    static constexpr int MI = WROWS / 32;           // 32-row blocks per wave
 };
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
@@ -331,10 +335,10 @@ __device__ __forceinline__ void wait_vm() {
 }  // namespace lds_gemm
 
 template <int PASS, int BM>
-__global__ __launch_bounds__(256) void grouped_gemm_lds_kernel(GemmArgs args) {
+__global__ __launch_bounds__(64 * lds_gemm::NWAVE) void grouped_gemm_lds_kernel(GemmArgs args) {
     using namespace lds_gemm;
     constexpr int A_BYTES = Tile<BM>::A_BYTES, STAGE = Tile<BM>::STAGE, A_CALLS = Tile<BM>::A_CALLS;
-    constexpr int CALLS = Tile<BM>::CALLS, MI = Tile<BM>::MI;
+    constexpr int CALLS = Tile<BM>::CALLS, MI = Tile<BM>::MI, WROWS = Tile<BM>::WROWS;
     // one array per ring stage, so the compiler can tell which direct-to-LDS
     // load writes which buffer and waits only for the right one
     __shared__ __attribute__((aligned(1024))) char buf0[STAGE];
@@ -391,7 +395,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_lds_kernel(GemmArgs args) {
     float row_sc[MI];
 #pragma unroll
     for (int a = 0; a < MI; ++a) {
-        const int r = (wave >> 1) * (BM / 2) + a * 32 + (lane & 31);
+        const int r = (wave >> 1) * WROWS + a * 32 + (lane & 31);
         const int64_t src = (int64_t)m0 + (r < mrows ? r : 0);
         const int32_t v = g.out_rows ? g.out_rows[src] : (int32_t)src;
         row_sc[a] = (PASS == 1 && g.out_scale) ? g.out_scale[g.scale_by_map ? v : src] : 1.0f;
@@ -430,7 +434,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_lds_kernel(GemmArgs args) {
             bf16x8 af[MI], bfr[4];
 #pragma unroll
             for (int a = 0; a < MI; ++a) {
-                const int r = wm * (BM / 2) + a * 32 + lr;
+                const int r = wm * WROWS + a * 32 + lr;
                 af[a] = *reinterpret_cast<const bf16x8*>(base + r * 64 + lds_chunk(r, c) * 16);
             }
 #pragma unroll
@@ -495,7 +499,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_lds_kernel(GemmArgs args) {
     sync();  // every wave is done with the ring
 #pragma unroll
     for (int a = 0; a < MI; ++a) {
-        const int r = wm * (BM / 2) + a * 32 + lr;
+        const int r = wm * WROWS + a * 32 + lr;
         char* rp = row_at(r);
 #pragma unroll
         for (int b = 0; b < (PASS == 0 ? 2 : 4); ++b)
@@ -516,10 +520,11 @@ __global__ __launch_bounds__(256) void grouped_gemm_lds_kernel(GemmArgs args) {
                 const int c = ((PASS == 0 ? wn * 64 : wn * 128) + b * 32 + 8 * j) / 8;  // 16-byte chunk
                 *reinterpret_cast<uint2*>(rp + ((c ^ (r % CPR)) * 16) + lh * 8) = pk;
             }
+        __builtin_amdgcn_sched_barrier(0);  // one token block at a time: bounds the live accumulator copies
     }
     sync();
     bf16_t* out = (bf16_t*)g.out;
-    for (int q = tid; q < BM * CPR; q += 256) {
+    for (int q = tid; q < BM * CPR; q += 64 * NWAVE) {
         const int r = q / CPR, c = q % CPR;
         if (r >= mrows) break;  // rows ascend with q
         const u32x4 v = *reinterpret_cast<const u32x4*>(row_at(r) + ((c ^ (r % CPR)) * 16));
@@ -601,14 +606,14 @@ bool k_multiple(const GemmArgs& a, int m) {
 // With events, the launch itself timestamps the kernel's start and end.
 template <typename Kernel>
 hipError_t launch_gemm(Kernel kernel, unsigned grid, hipStream_t st, hipEvent_t e0, hipEvent_t e1,
-                       const GemmArgs& args) {
+                       const GemmArgs& args, unsigned block = 256) {
     if (!e0 && !e1) {
-        kernel<<<grid, 256, 0, st>>>(args);
+        kernel<<<grid, block, 0, st>>>(args);
         return hipGetLastError();
     }
     GemmArgs copy = args;
     void* argv[] = {&copy};
-    return hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), dim3(grid), dim3(256), argv, 0, st, e0, e1, 0);
+    return hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), dim3(grid), dim3(block), argv, 0, st, e0, e1, 0);
 }
 }  // namespace
 
@@ -624,12 +629,12 @@ hipError_t launch_grouped_gemm(int dtype, int variant, int pass, const GemmArgs&
         return launch_gemm(grouped_gemm_kernel<TMOE_SMALL_DN>, grid, st, ev_start, ev_stop, args);
     }
     if (variant == kGemmLargeLds) {
-        if (pass == 0) return launch_gemm(grouped_gemm_lds_kernel<0, 128>, grid, st, ev_start, ev_stop, args);
-        return launch_gemm(grouped_gemm_lds_kernel<1, 128>, grid, st, ev_start, ev_stop, args);
+        if (pass == 0) return launch_gemm(grouped_gemm_lds_kernel<0, 128>, grid, st, ev_start, ev_stop, args, 64 * lds_gemm::NWAVE);
+        return launch_gemm(grouped_gemm_lds_kernel<1, 128>, grid, st, ev_start, ev_stop, args, 64 * lds_gemm::NWAVE);
     }
     if (variant == kGemmHugeLds) {
-        if (pass == 0) return launch_gemm(grouped_gemm_lds_kernel<0, 256>, grid, st, ev_start, ev_stop, args);
-        return launch_gemm(grouped_gemm_lds_kernel<1, 256>, grid, st, ev_start, ev_stop, args);
+        if (pass == 0) return launch_gemm(grouped_gemm_lds_kernel<0, 256>, grid, st, ev_start, ev_stop, args, 64 * lds_gemm::NWAVE);
+        return launch_gemm(grouped_gemm_lds_kernel<1, 256>, grid, st, ev_start, ev_stop, args, 64 * lds_gemm::NWAVE);
     }
     if (pass == 0) return launch_gemm(grouped_gemm_kernel<TMOE_LARGE_GU>, grid, st, ev_start, ev_stop, args);
     return launch_gemm(grouped_gemm_kernel<TMOE_LARGE_DN>, grid, st, ev_start, ev_stop, args);
