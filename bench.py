@@ -175,6 +175,49 @@ def measure(api, torch, INP, shape, T, weight_sets, steps, warmup):
     }
 
 
+def measure_stack(api, torch, INP, shape, T, weight_sets, L, frames, vocab=3072):
+    """The L-layer stack and the codec head (moe_stack_forward) as one HIP graph:
+    layer l uses weight set l % len(weight_sets); per frame, T tokens through all
+    L layers, the final RMSNorm and the c_0 argmax."""
+    cfg = api.Config(shape.H, shape.E, shape.k, shape.I, shape.Is, True, torch.bfloat16)
+    dev = torch.device("cuda", 0)
+    to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    structs = [api.weights_struct(weight_sets[l % len(weight_sets)]) for l in range(L)]
+    head = to_dev(INP.stack_weights(shape, 0, 30, 0.02, "bf16", vocab, 50)["codec_head"])
+    gains = torch.ones((L + 1, shape.H), dtype=torch.float32, device=dev)
+    x = to_dev(INP.activations(T, shape.H, 30, "bf16"))
+    h = torch.empty_like(x)
+    c0 = torch.empty(T, dtype=torch.int32, device=dev)
+    ws = api.workspace(api.moe_stack_workspace_size(cfg, T, vocab), dev)
+    run = lambda: api.moe_stack_forward(cfg, structs, x, gains, 1e-6, head, h_out=h, c0=c0, ws=ws)
+    run()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    g.replay()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(frames):
+        g.replay()
+    stop.record()
+    torch.cuda.synchronize()
+    frame_ms = start.elapsed_time(stop) / frames
+    start.record()
+    for _ in range(frames):
+        run()
+    stop.record()
+    torch.cuda.synchronize()
+    eager_ms = start.elapsed_time(stop) / frames
+    return {"workload": "talker_moe_stack%d_codec_head_T%d" % (L, T), "layers": L, "tokens": T, "vocab": vocab,
+            "weight_sets_rotated": len(weight_sets), "frames": frames,
+            "frame_us": frame_ms * 1e3, "per_layer_us": frame_ms * 1e3 / L, "eager_frame_us": eager_ms * 1e3,
+            "tokens_per_s": T / (frame_ms / 1e3),
+            "timing": "one HIP graph per frame: RMSNorm, L layers (combine + residual + next RMSNorm fused), "
+                      "codec_head argmax"}
+
+
 def cpu_baseline(INP, shape, T, seconds):
     from oracle import moe_ref as R
     try:
@@ -207,6 +250,9 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-stack", action="store_true")
+    ap.add_argument("--stack-layers", type=int, default=20)
+    ap.add_argument("--stack-frames", type=int, default=20)
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="after timing, copy a buffer of this many MiB once (a plain copy kernel of known size, "
                          "for scaling hardware byte counters)")
@@ -244,6 +290,11 @@ def main():
         log("prefill T=4096")
         pre = measure(api, torch, INP, shape, 4096, sets, args.steps, args.warmup)
         log("prefill: %.2f us/step, %.2f M tok/s" % (pre["ms_per_step"] * 1e3, pre["tokens_per_s"] / 1e6))
+    stack = None
+    if not args.no_stack and not args.no_decode:
+        log("stack: %d layers + codec head, T=64" % args.stack_layers)
+        stack = measure_stack(api, torch, INP, shape, 64, sets, args.stack_layers, args.stack_frames)
+        log("stack: %.1f us/frame, %.2f us/layer" % (stack["frame_us"], stack["per_layer_us"]))
     if args.copy_calibration_mb:
         # one device-to-device copy of n bytes from a source evicted from the
         # caches (a 2 GiB sweep after it was written), so the counters of that
@@ -295,6 +346,8 @@ def main():
                   "touched_experts": dec["touched_experts"]},
         "cpu_baseline": cpu,
     }
+    if stack is not None:
+        line["stack"] = stack
     if pre is not None:
         gp = pre["gate_up"]
         line["prefill"] = {"workload": "talker_moe_layer_prefill_T4096", "tokens_per_s": pre["tokens_per_s"],

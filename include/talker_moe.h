@@ -223,6 +223,35 @@ int moe_codec_head_argmax(const moe_config* cfg, const void* x, const void* w_he
 /* Workspace bytes for moe_codec_head_argmax at (V, T). Host only. */
 size_t moe_codec_head_workspace_size(const moe_config* cfg, int32_t V, int64_t T);
 
+/*
+ * moe_stack_forward — L stacked layers and the codec head, the lab's [3C]
+ * step layer by layer ("Bài Lab tổng hợp — Qwen3-Omni & Qwen3-TTS-12Hz
+ * Architecture"; 20 layers and codec_head 1024 -> 3072 on the Talker MoE page,
+ * §1; the norm before codec_head from the Qwen3-TTS module print):
+ *   h_0 = x;  h_{l+1} = h_l + MoE_l(RMSNorm_l(h_l));  xn = RMSNorm_L(h_L);
+ *   c_0 = argmax_v (W_c xn)_v  (ties to the lowest v).
+ * Each layer's combine, residual add and the next RMSNorm run as one launch;
+ * results equal those of moe_rmsnorm and moe_layer_forward (residual = h_l)
+ * called layer by layer.
+ *   layers     host array of L weight structs (L >= 1)
+ *   x          [dev] [T, H] stack input;  h_out [dev] [T, H] out: h_L (may alias x)
+ *   gains      [dev] [L + 1, H] fp32 (norm l before layer l; norm L before
+ *              the head), or NULL for gains of 1.0;  eps >= 0
+ *   codec_head [dev] [V, H] or NULL;  c0 [dev] [T] int32 out or NULL (needs
+ *              codec_head and V >= 1)
+ *   xn_out     [dev] [T, H] out: the final normalised state, or NULL (must not
+ *              alias x or h_out)
+ * All layer pointers are checked before anything is enqueued.  Workspace:
+ * moe_stack_workspace_size(cfg, T, V) (V = 0 without the head).
+ */
+int moe_stack_forward(const moe_config* cfg, const moe_weights* layers, int32_t L, const void* x,
+                      int64_t T, const float* gains, float eps, const void* codec_head, int32_t V,
+                      void* h_out, void* xn_out, int32_t* c0, void* ws, size_t ws_bytes,
+                      void* stream);
+
+/* Workspace bytes for moe_stack_forward at (T, V); V = 0 when no c0 is asked for. Host only. */
+size_t moe_stack_workspace_size(const moe_config* cfg, int64_t T, int32_t V);
+
 #ifdef __cplusplus
 }
 #endif

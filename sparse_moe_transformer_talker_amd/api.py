@@ -25,7 +25,8 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID", -2: "MOE_ERR_UNSUPPORTED", -3: "MO
 EXPORTS = ("moe_status_string", "moe_check_config", "moe_workspace_size", "moe_route", "moe_permute",
            "moe_grouped_swiglu", "moe_shared_swiglu", "moe_combine", "moe_layer_forward",
            "moe_layer_forward_timed", "moe_rmsnorm",
-           "moe_codec_head_argmax", "moe_codec_head_workspace_size")
+           "moe_codec_head_argmax", "moe_codec_head_workspace_size", "moe_stack_forward",
+           "moe_stack_workspace_size")
 
 
 class MoeError(RuntimeError):
@@ -98,6 +99,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         "moe_rmsnorm": (ctypes.c_int, [cfgp, vp, vp, ctypes.c_float, i64, vp, vp]),
         "moe_codec_head_argmax": (ctypes.c_int, [cfgp, vp, vp, i32, i64, vp, vp, vp, sz, vp]),
         "moe_codec_head_workspace_size": (sz, [cfgp, i32, i64]),
+        "moe_stack_forward": (ctypes.c_int, [cfgp, ctypes.POINTER(moe_weights), i32, vp, i64, vp, ctypes.c_float,
+                                             vp, i32, vp, vp, vp, vp, sz, vp]),
+        "moe_stack_workspace_size": (sz, [cfgp, i64, i32]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -285,3 +289,30 @@ def moe_codec_head_argmax(cfg: Config, x: torch.Tensor, w_head: torch.Tensor, wa
         ctypes.byref(cfg.c()), _ptr(x), _ptr(w_head), V, T, _ptr(logits), _ptr(c0), _ptr(buf), buf.numel(),
         _stream(dev)))
     return c0, logits
+
+
+def moe_stack_workspace_size(cfg: Config, T: int, V: int = 0) -> int:
+    return int(load_library().moe_stack_workspace_size(ctypes.byref(cfg.c()), T, V))
+
+
+def moe_stack_forward(cfg: Config, layers, x: torch.Tensor, gains: Optional[torch.Tensor] = None,
+                      eps: float = 1e-6, codec_head: Optional[torch.Tensor] = None, h_out=None, xn_out=None,
+                      c0=None, want_c0: bool = True, ws=None, stream=None):
+    """L stacked layers, then the final RMSNorm and (with ``codec_head``) the head
+    argmax.  ``layers``: list of weight dicts or moe_weights; ``gains`` [L + 1, H]
+    fp32.  Returns (h_out [T, H], xn_out [T, H] or None, c0 [T] int32 or None)."""
+    T, dev = x.shape[0], x.device
+    L = len(layers)
+    arr = (moe_weights * max(L, 1))(*[w if isinstance(w, moe_weights) else weights_struct(w) for w in layers])
+    h_out = h_out if h_out is not None else torch.empty_like(x)
+    V = 0 if codec_head is None else codec_head.shape[0]
+    if c0 is None and want_c0 and codec_head is not None:
+        c0 = torch.empty(T, dtype=torch.int32, device=dev)
+    lib = load_library()
+    need = int(lib.moe_stack_workspace_size(ctypes.byref(cfg.c()), T, V if c0 is not None else 0))
+    buf = ws if ws is not None else workspace(need, dev)
+    st = stream if stream is not None else _stream(dev)
+    _check("moe_stack_forward", lib.moe_stack_forward(
+        ctypes.byref(cfg.c()), arr, L, _ptr(x), T, _ptr(gains), eps, _ptr(codec_head), V, _ptr(h_out),
+        _ptr(xn_out), _ptr(c0), _ptr(buf), buf.numel(), st))
+    return h_out, xn_out, c0

@@ -14,6 +14,7 @@ namespace {
 
 constexpr int64_t kMaxPairs = int64_t(1) << 22;
 constexpr int kMaxDim = 16384;
+constexpr int kMaxStackLayers = 1024;
 
 // Carves 256-byte aligned regions out of the caller's workspace; with a null
 // base it only measures.
@@ -249,6 +250,143 @@ GemmGroup no_group() {
     return g;
 }
 
+// Optional end of a stacked layer: the next pre-norm of y, fused into the combine.
+struct LayerEnd {
+    const float* gain = nullptr;  // nullable: 1.0
+    float eps = 0.f;
+    void* norm_out = nullptr;     // null: plain combine
+};
+
+hipError_t finish_layer(int dtype, const void* ybuf, int k, int slots, const void* shared, int64_t sstride,
+                        const void* residual, void* y, int64_t T, int H, const LayerEnd& end, hipStream_t s) {
+    if (end.norm_out)
+        return launch_combine_norm(dtype, ybuf, k, slots, shared, sstride, residual, y, T, H, end.gain, end.eps,
+                                   end.norm_out, s);
+    return launch_combine(dtype, ybuf, nullptr, nullptr, k, slots, shared, sstride, residual, y, T, H, s);
+}
+
+int check_layer_args(const moe_config* cfg, const moe_weights* w, const void* x, const void* residual,
+                     const void* y, const void* ws) {
+    if (!w) return MOE_ERR_INVALID;
+    const int Is = cfg->shared_expert_intermediate_size;
+    if (!ok_ptr(x) || !ok_ptr(y) || !ok_opt(residual) || !ok_ptr(w->router) || !ok_opt(w->router_bias) ||
+        !ok_ptr(w->gate) || !ok_ptr(w->up) || !ok_ptr(w->down) || !ok_ptr(ws))
+        return MOE_ERR_INVALID;
+    if (Is > 0 && (!ok_ptr(w->shared_gate) || !ok_ptr(w->shared_up) || !ok_ptr(w->shared_down)))
+        return MOE_ERR_INVALID;
+    if (x == y) return MOE_ERR_INVALID;
+    return MOE_OK;
+}
+
+// One layer on stream s (arguments already checked).
+int layer_run(const moe_config* cfg, const moe_weights* w, const void* x, const void* residual, int64_t T, void* y,
+              int32_t* topk_idx_out, float* topk_w_out, int32_t* counts_out, void* ws, hipStream_t s,
+              void* const* stage_events, const LayerEnd& end) {
+    const int H = cfg->hidden_size, E = cfg->num_experts, k = cfg->num_experts_per_tok;
+    const int I = cfg->moe_intermediate_size, Is = cfg->shared_expert_intermediate_size;
+    const int64_t N = T * k;
+    Carver cv(ws);
+    LayerPlan p;
+    plan_layer(cfg, T, cv, p);
+    int32_t* idx = topk_idx_out ? topk_idx_out : p.idx;
+    float* wt = topk_w_out ? topk_w_out : p.w;
+    int32_t* counts = counts_out ? counts_out : p.counts;
+    auto mark = [&](int i) -> hipError_t {
+        return (stage_events && stage_events[i]) ? hipEventRecord(static_cast<hipEvent_t>(stage_events[i]), s)
+                                                 : hipSuccess;
+    };
+
+    const int slots = k + 1;  // per token: k weighted expert rows, then the shared row
+    const TileSpec* t1 = p.gemm.mfma ? &p.gemm.t[0] : nullptr;
+    const TileSpec* t2 = p.gemm.mfma ? &p.gemm.t[1] : nullptr;
+    TMOE_TRY(mark(0));
+    auto ev = [&](int i) { return stage_events ? static_cast<hipEvent_t>(stage_events[i]) : nullptr; };
+    if (p.direct) {
+        TMOE_TRY(launch_route_block(x, w->router, w->router_bias, T, H, E, k, cfg->norm_topk_prob, idx, wt, nullptr,
+                                    nullptr, nullptr, p.bcnt, p.blist, s));
+        TMOE_TRY(mark(1));
+        TMOE_TRY(mark(2));
+        int bm;
+        GemmArgs a{};
+        a.E = E;
+        a.direct_bcnt = p.bcnt;
+        a.direct_blist = p.blist;
+        a.direct_nb = (int)nb_of(T);
+        a.direct_counts = counts;
+        a.direct_T = (int)T;
+        a.g[0] = group(w->gate, w->up, (int64_t)I * H, I, H, x, H, nullptr, p.hd, I, nullptr, 1, 0, nullptr);
+        a.g[0].a_div = k;
+        a.g[1] = Is > 0 ? group(w->shared_gate, w->shared_up, 0, Is, H, x, H, nullptr, p.hs, Is, nullptr, 1, 0, nullptr)
+                        : no_group();
+        int bn = gemm_direct_tile(0, &bm);
+        a.direct_nt[0] = I / bn;
+        a.direct_nt[1] = Is / bn;
+        a.direct_mt1 = (int)((T + bm - 1) / bm);
+        TMOE_TRY(launch_grouped_gemm_direct(0, a, s, ev(6), ev(7)));
+        TMOE_TRY(mark(3));
+        a.direct_counts = nullptr;  // written by the gate/up pass
+        a.g[0] = group(w->down, nullptr, (int64_t)H * I, H, I, p.hd, I, nullptr, p.ybuf, H, nullptr, 1, 0, wt);
+        a.g[0].out_div = k;
+        a.g[0].scale_by_map = 1;
+        a.g[1] = Is > 0 ? group(w->shared_down, nullptr, 0, H, Is, p.hs, Is, nullptr, p.ybuf, H, nullptr, slots, k,
+                                nullptr)
+                        : no_group();
+        bn = gemm_direct_tile(1, &bm);
+        a.direct_nt[0] = H / bn;
+        a.direct_nt[1] = Is > 0 ? H / bn : 0;
+        TMOE_TRY(launch_grouped_gemm_direct(1, a, s));
+        TMOE_TRY(mark(4));
+        const char* sb = Is > 0 ? static_cast<const char*>(p.ybuf) + (int64_t)k * H * esize(cfg->dtype) : nullptr;
+        TMOE_TRY(finish_layer(cfg->dtype, p.ybuf, k, slots, sb, (int64_t)slots * H, residual, y, T, H, end, s));
+        TMOE_TRY(mark(5));
+        return MOE_OK;
+    }
+    if (!route_block_ok(cfg->dtype, H, E, k) && route_group_small_ok(cfg->dtype, T, H, E, k)) {
+        // scores over many CUs, then selection and grouping in one block
+        TMOE_TRY(launch_scores(cfg->dtype, x, w->router, w->router_bias, T, H, E, p.route.sc, p.route.bd, s));
+        TMOE_TRY(mark(1));
+        TMOE_TRY(launch_select_group_small(p.route.sc, p.route.bd, x, w->router, w->router_bias, T, H, E, k,
+                                           cfg->norm_topk_prob, idx, wt, counts, p.offsets, p.row_token, p.row_of,
+                                           p.row_pair, t1, t2, s));
+    } else {
+        // choice slots come with the masks only from the one-launch router
+        uint64_t* jm = route_block_ok(cfg->dtype, H, E, k) ? p.jmask : nullptr;
+        TMOE_TRY(launch_route(cfg->dtype, x, w->router, w->router_bias, T, H, E, k, cfg->norm_topk_prob, idx, wt,
+                              nullptr, p.route.sc, p.route.bd, p.masks, jm, s));
+        TMOE_TRY(mark(1));
+        if (group_small_ok(T, E))
+            TMOE_TRY(launch_group_small(idx, p.masks, T, E, k, counts, p.offsets, p.row_token, p.row_of, p.row_pair,
+                                        t1, t2, s));
+        else
+            TMOE_TRY(launch_permute(idx, T, k, E, p.masks, jm, p.prefix, counts, p.offsets, p.row_token,
+                                    p.row_of, p.row_pair, t1, t2, s));
+    }
+    TMOE_TRY(mark(2));
+
+    GemmGroup gu_r = group(w->gate, w->up, (int64_t)I * H, I, H, x, H, p.row_token, p.hr, I, nullptr, 1, 0, nullptr);
+    GemmGroup gu_s = Is > 0 ? group(w->shared_gate, w->shared_up, 0, Is, H, x, H, nullptr, p.hs, Is, nullptr, 1, 0,
+                                    nullptr)
+                            : no_group();
+    int r = run_gemm_pass(cfg, p.gemm, 0, gu_r, gu_s, p.offsets, N, T, s, ev(6), ev(7));
+    if (r != MOE_OK) return r;
+    TMOE_TRY(mark(3));
+    // row_pair v = t * k + j goes to slot j of token t: row v + v / k of [T, k + 1, H], scaled by w[v]
+    GemmGroup dn_r = group(w->down, nullptr, (int64_t)H * I, H, I, p.hr, I, nullptr, p.ybuf, H, p.row_pair, 1, 0, wt);
+    dn_r.out_div = k;
+    dn_r.scale_by_map = 1;
+    GemmGroup dn_s = Is > 0 ? group(w->shared_down, nullptr, 0, H, Is, p.hs, Is, nullptr, p.ybuf, H, nullptr, slots,
+                                    k, nullptr)
+                            : no_group();
+    r = run_gemm_pass(cfg, p.gemm, 1, dn_r, dn_s, p.offsets, N, T, s);
+    if (r != MOE_OK) return r;
+    TMOE_TRY(mark(4));
+    const char* shared_base = Is > 0 ? static_cast<const char*>(p.ybuf) + (int64_t)k * H * esize(cfg->dtype) : nullptr;
+    TMOE_TRY(finish_layer(cfg->dtype, p.ybuf, k, slots, shared_base, (int64_t)slots * H, residual, y, T, H, end,
+                          s));
+    TMOE_TRY(mark(5));
+    return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -404,122 +542,60 @@ int moe_layer_forward_timed(const moe_config* cfg, const moe_weights* w, const v
     if (st != MOE_OK) return st;
     if ((st = check_T(cfg, T)) != MOE_OK) return st;
     if (T == 0) return MOE_OK;
-    if (!w) return MOE_ERR_INVALID;
-    const int Is = cfg->shared_expert_intermediate_size;
-    if (!ok_ptr(x) || !ok_ptr(y) || !ok_opt(residual) || !ok_ptr(w->router) || !ok_opt(w->router_bias) ||
-        !ok_ptr(w->gate) || !ok_ptr(w->up) || !ok_ptr(w->down) || !ok_opt(topk_idx_out) || !ok_opt(topk_w_out) ||
-        !ok_opt(counts_out) || !ok_ptr(ws))
-        return MOE_ERR_INVALID;
-    if (Is > 0 && (!ok_ptr(w->shared_gate) || !ok_ptr(w->shared_up) || !ok_ptr(w->shared_down)))
-        return MOE_ERR_INVALID;
-    if (x == y) return MOE_ERR_INVALID;
+    if ((st = check_layer_args(cfg, w, x, residual, y, ws)) != MOE_OK) return st;
+    if (!ok_opt(topk_idx_out) || !ok_opt(topk_w_out) || !ok_opt(counts_out)) return MOE_ERR_INVALID;
     if (ws_bytes < layer_ws(cfg, T)) return MOE_ERR_WORKSPACE;
+    return layer_run(cfg, w, x, residual, T, y, topk_idx_out, topk_w_out, counts_out, ws, as_stream(stream),
+                     stage_events, LayerEnd{});
+}
 
-    const int H = cfg->hidden_size, E = cfg->num_experts, k = cfg->num_experts_per_tok;
-    const int I = cfg->moe_intermediate_size;
-    const int64_t N = T * k;
-    hipStream_t s = as_stream(stream);
+size_t moe_stack_workspace_size(const moe_config* cfg, int64_t T, int32_t V) {
+    if (check_cfg(cfg) != MOE_OK || check_T(cfg, T) != MOE_OK || V < 0) return 0;
+    Carver cv(nullptr);
+    cv.take<char>(T * cfg->hidden_size * (int64_t)esize(cfg->dtype));  // the normalised layer input
+    cv.take<char>(layer_ws(cfg, T));
+    if (V > 0) cv.take<char>(moe_codec_head_workspace_size(cfg, V, T));
+    return cv.size();
+}
+
+int moe_stack_forward(const moe_config* cfg, const moe_weights* layers, int32_t L, const void* x, int64_t T,
+                      const float* gains, float eps, const void* codec_head, int32_t V, void* h_out, void* xn_out,
+                      int32_t* c0, void* ws, size_t ws_bytes, void* stream) {
+    int st = check_cfg(cfg);
+    if (st != MOE_OK) return st;
+    if ((st = check_T(cfg, T)) != MOE_OK) return st;
+    if (L < 1 || L > kMaxStackLayers || !layers || !(eps >= 0.0f) || V < 0) return MOE_ERR_INVALID;
+    if (T == 0) return MOE_OK;
+    if (!ok_ptr(x) || !ok_ptr(h_out) || !ok_opt(xn_out) || !ok_opt(gains) || !ok_opt(codec_head) || !ok_opt(c0) ||
+        !ok_ptr(ws))
+        return MOE_ERR_INVALID;
+    if (c0 && (!codec_head || V < 1)) return MOE_ERR_INVALID;
+    if (V > (1 << 20)) return MOE_ERR_UNSUPPORTED;
+    if (xn_out && (xn_out == x || xn_out == h_out)) return MOE_ERR_INVALID;
+    if (ws_bytes < moe_stack_workspace_size(cfg, T, c0 ? V : 0)) return MOE_ERR_WORKSPACE;
+    const int H = cfg->hidden_size;
     Carver cv(ws);
-    LayerPlan p;
-    plan_layer(cfg, T, cv, p);
-    int32_t* idx = topk_idx_out ? topk_idx_out : p.idx;
-    float* wt = topk_w_out ? topk_w_out : p.w;
-    int32_t* counts = counts_out ? counts_out : p.counts;
-    auto mark = [&](int i) -> hipError_t {
-        return (stage_events && stage_events[i]) ? hipEventRecord(static_cast<hipEvent_t>(stage_events[i]), s)
-                                                 : hipSuccess;
-    };
+    void* xn_ws = cv.take<char>(T * H * (int64_t)esize(cfg->dtype));
+    void* lws = cv.take<char>(layer_ws(cfg, T));
+    void* hws = c0 ? cv.take<char>(moe_codec_head_workspace_size(cfg, V, T)) : nullptr;
+    void* xn = xn_out ? xn_out : xn_ws;
+    for (int l = 0; l < L; ++l)
+        if ((st = check_layer_args(cfg, &layers[l], xn, l == 0 ? x : h_out, h_out, lws)) != MOE_OK) return st;
 
-    const int slots = k + 1;  // per token: k weighted expert rows, then the shared row
-    const TileSpec* t1 = p.gemm.mfma ? &p.gemm.t[0] : nullptr;
-    const TileSpec* t2 = p.gemm.mfma ? &p.gemm.t[1] : nullptr;
-    TMOE_TRY(mark(0));
-    auto ev = [&](int i) { return stage_events ? static_cast<hipEvent_t>(stage_events[i]) : nullptr; };
-    if (p.direct) {
-        TMOE_TRY(launch_route_block(x, w->router, w->router_bias, T, H, E, k, cfg->norm_topk_prob, idx, wt, nullptr,
-                                    nullptr, nullptr, p.bcnt, p.blist, s));
-        TMOE_TRY(mark(1));
-        TMOE_TRY(mark(2));
-        int bm;
-        GemmArgs a{};
-        a.E = E;
-        a.direct_bcnt = p.bcnt;
-        a.direct_blist = p.blist;
-        a.direct_nb = (int)nb_of(T);
-        a.direct_counts = counts;
-        a.direct_T = (int)T;
-        a.g[0] = group(w->gate, w->up, (int64_t)I * H, I, H, x, H, nullptr, p.hd, I, nullptr, 1, 0, nullptr);
-        a.g[0].a_div = k;
-        a.g[1] = Is > 0 ? group(w->shared_gate, w->shared_up, 0, Is, H, x, H, nullptr, p.hs, Is, nullptr, 1, 0, nullptr)
-                        : no_group();
-        int bn = gemm_direct_tile(0, &bm);
-        a.direct_nt[0] = I / bn;
-        a.direct_nt[1] = Is / bn;
-        a.direct_mt1 = (int)((T + bm - 1) / bm);
-        TMOE_TRY(launch_grouped_gemm_direct(0, a, s, ev(6), ev(7)));
-        TMOE_TRY(mark(3));
-        a.direct_counts = nullptr;  // written by the gate/up pass
-        a.g[0] = group(w->down, nullptr, (int64_t)H * I, H, I, p.hd, I, nullptr, p.ybuf, H, nullptr, 1, 0, wt);
-        a.g[0].out_div = k;
-        a.g[0].scale_by_map = 1;
-        a.g[1] = Is > 0 ? group(w->shared_down, nullptr, 0, H, Is, p.hs, Is, nullptr, p.ybuf, H, nullptr, slots, k,
-                                nullptr)
-                        : no_group();
-        bn = gemm_direct_tile(1, &bm);
-        a.direct_nt[0] = H / bn;
-        a.direct_nt[1] = Is > 0 ? H / bn : 0;
-        TMOE_TRY(launch_grouped_gemm_direct(1, a, s));
-        TMOE_TRY(mark(4));
-        const char* sb = Is > 0 ? static_cast<const char*>(p.ybuf) + (int64_t)k * H * esize(cfg->dtype) : nullptr;
-        TMOE_TRY(launch_combine(cfg->dtype, p.ybuf, nullptr, nullptr, k, slots, sb, (int64_t)slots * H, residual, y,
-                                T, H, s));
-        TMOE_TRY(mark(5));
-        return MOE_OK;
+    hipStream_t s = as_stream(stream);
+    TMOE_TRY(launch_rmsnorm(cfg->dtype, x, gains, eps, T, H, xn, s));
+    for (int l = 0; l < L; ++l) {
+        LayerEnd end;
+        end.gain = gains ? gains + (int64_t)(l + 1) * H : nullptr;
+        end.eps = eps;
+        end.norm_out = xn;
+        const int r = layer_run(cfg, &layers[l], xn, l == 0 ? x : h_out, T, h_out, nullptr, nullptr, nullptr, lws,
+                                s, nullptr, end);
+        if (r != MOE_OK) return r;
     }
-    if (!route_block_ok(cfg->dtype, H, E, k) && route_group_small_ok(cfg->dtype, T, H, E, k)) {
-        // scores over many CUs, then selection and grouping in one block
-        TMOE_TRY(launch_scores(cfg->dtype, x, w->router, w->router_bias, T, H, E, p.route.sc, p.route.bd, s));
-        TMOE_TRY(mark(1));
-        TMOE_TRY(launch_select_group_small(p.route.sc, p.route.bd, x, w->router, w->router_bias, T, H, E, k,
-                                           cfg->norm_topk_prob, idx, wt, counts, p.offsets, p.row_token, p.row_of,
-                                           p.row_pair, t1, t2, s));
-    } else {
-        // choice slots come with the masks only from the one-launch router
-        uint64_t* jm = route_block_ok(cfg->dtype, H, E, k) ? p.jmask : nullptr;
-        TMOE_TRY(launch_route(cfg->dtype, x, w->router, w->router_bias, T, H, E, k, cfg->norm_topk_prob, idx, wt,
-                              nullptr, p.route.sc, p.route.bd, p.masks, jm, s));
-        TMOE_TRY(mark(1));
-        if (group_small_ok(T, E))
-            TMOE_TRY(launch_group_small(idx, p.masks, T, E, k, counts, p.offsets, p.row_token, p.row_of, p.row_pair,
-                                        t1, t2, s));
-        else
-            TMOE_TRY(launch_permute(idx, T, k, E, p.masks, jm, p.prefix, counts, p.offsets, p.row_token,
-                                    p.row_of, p.row_pair, t1, t2, s));
-    }
-    TMOE_TRY(mark(2));
-
-    GemmGroup gu_r = group(w->gate, w->up, (int64_t)I * H, I, H, x, H, p.row_token, p.hr, I, nullptr, 1, 0, nullptr);
-    GemmGroup gu_s = Is > 0 ? group(w->shared_gate, w->shared_up, 0, Is, H, x, H, nullptr, p.hs, Is, nullptr, 1, 0,
-                                    nullptr)
-                            : no_group();
-    int r = run_gemm_pass(cfg, p.gemm, 0, gu_r, gu_s, p.offsets, N, T, s, ev(6), ev(7));
-    if (r != MOE_OK) return r;
-    TMOE_TRY(mark(3));
-    // row_pair v = t * k + j goes to slot j of token t: row v + v / k of [T, k + 1, H], scaled by w[v]
-    GemmGroup dn_r = group(w->down, nullptr, (int64_t)H * I, H, I, p.hr, I, nullptr, p.ybuf, H, p.row_pair, 1, 0, wt);
-    dn_r.out_div = k;
-    dn_r.scale_by_map = 1;
-    GemmGroup dn_s = Is > 0 ? group(w->shared_down, nullptr, 0, H, Is, p.hs, Is, nullptr, p.ybuf, H, nullptr, slots,
-                                    k, nullptr)
-                            : no_group();
-    r = run_gemm_pass(cfg, p.gemm, 1, dn_r, dn_s, p.offsets, N, T, s);
-    if (r != MOE_OK) return r;
-    TMOE_TRY(mark(4));
-    const char* shared_base = Is > 0 ? static_cast<const char*>(p.ybuf) + (int64_t)k * H * esize(cfg->dtype) : nullptr;
-    TMOE_TRY(launch_combine(cfg->dtype, p.ybuf, nullptr, nullptr, k, slots, shared_base, (int64_t)slots * H,
-                            residual, y, T, H, s));
-    TMOE_TRY(mark(5));
-    return MOE_OK;
+    if (!c0) return MOE_OK;
+    return moe_codec_head_argmax(cfg, xn, codec_head, V, T, nullptr, c0, hws,
+                                 moe_codec_head_workspace_size(cfg, V, T), stream);
 }
 
 int moe_rmsnorm(const moe_config* cfg, const void* x, const float* gain, float eps, int64_t T, void* out,

@@ -94,6 +94,122 @@ __global__ __launch_bounds__(128) void combine_bf16x8_kernel(const bf16_t* __res
     }
 }
 
+// RMSNorm of bf16 rows (H % 8 == 0, H <= 1024 NCH): 128 threads, thread i
+// holds elements 8 (i + 128 c) .. + 7 of chunk c.  Each thread sums its squares
+// in element order, the two waves reduce by DPP and the block adds wave 0's
+// total and wave 1's: one fixed order, shared with the fused combine below, so
+// the stack's fused layer end and a separate moe_rmsnorm call give the same
+// bits.  gain may be null (1.0).
+template <int NCH>
+__device__ __forceinline__ float rms_inv_bf16x8(const u32x4 (&v)[NCH], bool (&ok)[NCH], int H, float eps) {
+    __shared__ float part[2];
+    float ss = 0.f;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+        if (ok[c])
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float lo = __uint_as_float(v[c][q] << 16), hi = __uint_as_float(v[c][q] & 0xFFFF0000u);
+                ss = fmaf(lo, lo, ss);
+                ss = fmaf(hi, hi, ss);
+            }
+    ss = wave_sum_dpp(ss);
+    if (lane_id() == 0) part[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    const float ms = (part[0] + part[1]) / (float)H;
+    return 1.0f / sqrtf(ms + eps);
+}
+template <int NCH>
+__device__ __forceinline__ void rms_store_bf16x8(const u32x4 (&v)[NCH], bool (&ok)[NCH], float inv,
+                                                 const float* __restrict__ gain, bf16_t* out_row) {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        if (!ok[c]) continue;
+        const int h = (threadIdx.x + 128 * c) * 8;
+        u32x4 o;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float g0 = gain ? gain[h + 2 * q] : 1.0f, g1 = gain ? gain[h + 2 * q + 1] : 1.0f;
+            o[q] = pack_bf16x2(__uint_as_float(v[c][q] << 16) * inv * g0,
+                               __uint_as_float(v[c][q] & 0xFFFF0000u) * inv * g1);
+        }
+        *reinterpret_cast<u32x4*>(out_row + h) = o;
+    }
+}
+template <int NCH>
+__global__ __launch_bounds__(128) void rmsnorm_bf16x8_kernel(const bf16_t* x, const float* __restrict__ gain,
+                                                             float eps, int64_t Ttok, int H, bf16_t* out) {
+    const int64_t t = blockIdx.x;
+    if (t >= Ttok) return;
+    u32x4 v[NCH];
+    bool ok[NCH];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int h = (threadIdx.x + 128 * c) * 8;
+        ok[c] = h < H;
+        v[c] = ok[c] ? *reinterpret_cast<const u32x4*>(x + t * H + h) : u32x4{0, 0, 0, 0};
+    }
+    const float inv = rms_inv_bf16x8<NCH>(v, ok, H, eps);
+    rms_store_bf16x8<NCH>(v, ok, inv, gain, out + t * H);
+}
+
+// The end of a stacked layer: the combine above (shared, slots 0..k-1,
+// residual, rounded to bf16 and stored as y), then the next layer's pre-norm of
+// that stored row (the lab's [3C] step normalises the layer input; the final
+// norm before codec_head likewise), written to norm_out.
+template <int NCH>
+__global__ __launch_bounds__(128) void combine_norm_bf16x8_kernel(const bf16_t* __restrict__ ysrc, int k, int slots,
+                                                                  const bf16_t* __restrict__ shared, int64_t sstride,
+                                                                  const bf16_t* residual, bf16_t* y, int64_t Ttok,
+                                                                  int H, const float* __restrict__ gain, float eps,
+                                                                  bf16_t* norm_out) {
+    const int64_t t = blockIdx.x;
+    if (t >= Ttok) return;
+    const bf16_t* shared_row = shared ? shared + t * sstride : nullptr;
+    u32x4 yv[NCH];
+    bool ok[NCH];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int h = (threadIdx.x + 128 * c) * 8;
+        ok[c] = h < H;
+        yv[c] = u32x4{0, 0, 0, 0};
+        if (!ok[c]) continue;
+        float acc[8];
+        if (shared_row) {
+            const u32x4 v = *reinterpret_cast<const u32x4*>(shared_row + h);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                acc[2 * q] = __uint_as_float(v[q] << 16);
+                acc[2 * q + 1] = __uint_as_float(v[q] & 0xFFFF0000u);
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < 8; ++q) acc[q] = 0.f;
+        }
+        for (int j = 0; j < k; ++j) {
+            const u32x4 v = *reinterpret_cast<const u32x4*>(ysrc + (t * slots + j) * (int64_t)H + h);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                acc[2 * q] += 1.0f * __uint_as_float(v[q] << 16);
+                acc[2 * q + 1] += 1.0f * __uint_as_float(v[q] & 0xFFFF0000u);
+            }
+        }
+        if (residual) {
+            const u32x4 v = *reinterpret_cast<const u32x4*>(residual + t * H + h);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                acc[2 * q] += __uint_as_float(v[q] << 16);
+                acc[2 * q + 1] += __uint_as_float(v[q] & 0xFFFF0000u);
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) yv[c][q] = pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
+        *reinterpret_cast<u32x4*>(y + t * H + h) = yv[c];
+    }
+    const float inv = rms_inv_bf16x8<NCH>(yv, ok, H, eps);
+    rms_store_bf16x8<NCH>(yv, ok, inv, gain, norm_out + t * H);
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const T* x, const float* __restrict__ gain, float eps,
                                                       int64_t Ttok, int H, T* out) {
@@ -113,7 +229,7 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const T* x, const float* _
     const float inv = 1.0f / sqrtf(ms + eps);
     for (int h = threadIdx.x; h < H; h += blockDim.x) {
         float v = Elem<T>::load(xr, h);
-        Elem<T>::store(out, t * H + h, v * inv * gain[h]);
+        Elem<T>::store(out, t * H + h, v * inv * (gain ? gain[h] : 1.0f));
     }
 }
 
@@ -156,13 +272,50 @@ hipError_t launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t st) {
     return hipGetLastError();
 }
 
+// Chunks of 1024 elements per row for the bf16 row kernels (0: they do not apply).
+static int bf16x8_chunks(int dtype, int H) {
+    if (dtype != kBF16 || H % 8 != 0 || H > 4 * 1024) return 0;
+    return (H + 1023) / 1024;
+}
+
 hipError_t launch_rmsnorm(int dtype, const void* x, const float* gain, float eps, int64_t Ttok, int H, void* out,
                           hipStream_t st) {
     if (Ttok <= 0) return hipSuccess;
-    if (dtype == kBF16)
+    const int nch = bf16x8_chunks(dtype, H);
+#define TMOE_RMS(N) \
+    rmsnorm_bf16x8_kernel<N><<<(unsigned)Ttok, 128, 0, st>>>((const bf16_t*)x, gain, eps, Ttok, H, (bf16_t*)out)
+    if (nch == 1) TMOE_RMS(1);
+    else if (nch == 2) TMOE_RMS(2);
+    else if (nch == 3) TMOE_RMS(3);
+    else if (nch == 4) TMOE_RMS(4);
+#undef TMOE_RMS
+    else if (dtype == kBF16)
         rmsnorm_kernel<bf16_t><<<(unsigned)Ttok, 256, 0, st>>>((const bf16_t*)x, gain, eps, Ttok, H, (bf16_t*)out);
     else
         rmsnorm_kernel<float><<<(unsigned)Ttok, 256, 0, st>>>((const float*)x, gain, eps, Ttok, H, (float*)out);
+    return hipGetLastError();
+}
+
+hipError_t launch_combine_norm(int dtype, const void* ysrc, int k, int slots, const void* shared, int64_t sstride,
+                               const void* residual, void* y, int64_t Ttok, int H, const float* gain, float eps,
+                               void* norm_out, hipStream_t st) {
+    if (Ttok <= 0) return hipSuccess;
+    const int nch = bf16x8_chunks(dtype, H);
+    if (nch == 0) {  // the two steps apart, with the same kernels as the separate calls
+        hipError_t e = launch_combine(dtype, ysrc, nullptr, nullptr, k, slots, shared, sstride, residual, y, Ttok, H, st);
+        if (e != hipSuccess) return e;
+        return launch_rmsnorm(dtype, y, gain, eps, Ttok, H, norm_out, st);
+    }
+#define TMOE_CN(N)                                                                                              \
+    combine_norm_bf16x8_kernel<N><<<(unsigned)Ttok, 128, 0, st>>>((const bf16_t*)ysrc, k, slots,               \
+                                                                 (const bf16_t*)shared, sstride,               \
+                                                                 (const bf16_t*)residual, (bf16_t*)y, Ttok, H, \
+                                                                 gain, eps, (bf16_t*)norm_out)
+    if (nch == 1) TMOE_CN(1);
+    else if (nch == 2) TMOE_CN(2);
+    else if (nch == 3) TMOE_CN(3);
+    else TMOE_CN(4);
+#undef TMOE_CN
     return hipGetLastError();
 }
 

@@ -136,8 +136,15 @@ hipError_t launch_gemm_generic(int dtype, int pass, const GemmGroup& g, const in
 hipError_t launch_combine(int dtype, const void* ysrc, const int32_t* rows, const float* w, int k, int slots,
                           const void* shared, int64_t sstride, const void* residual, void* y, int64_t T, int H,
                           hipStream_t st);
+// gain nullable (1.0)
 hipError_t launch_rmsnorm(int dtype, const void* x, const float* gain, float eps, int64_t T, int H, void* out,
                           hipStream_t st);
+// Slot-mode combine (as launch_combine with rows == nullptr) followed by the
+// RMSNorm of the stored y into norm_out, fused for bf16 rows; same results as
+// the two launches.
+hipError_t launch_combine_norm(int dtype, const void* ysrc, int k, int slots, const void* shared, int64_t sstride,
+                               const void* residual, void* y, int64_t T, int H, const float* gain, float eps,
+                               void* norm_out, hipStream_t st);
 hipError_t launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t st);
 hipError_t launch_gather_rows(int dtype, const void* x, const int32_t* rows, int64_t n, int H, void* out,
                               hipStream_t st);

@@ -134,3 +134,38 @@ def test_layer_and_helper_argument_errors():
                            None) == -1          # x without x_perm
     assert lib.moe_grouped_swiglu(ctypes.byref(c), _p(), None, None, 8, _p(), _p(), _p(), _p(), _p(), 1 << 30,
                                   None) == -1   # offsets required
+
+
+def test_stack_argument_errors():
+    lib = api.load_library()
+    c = _cfg()
+    w = api.moe_weights(FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    arr = (api.moe_weights * 3)(w, w, w)
+    T, V = 64, 3072
+    need = lib.moe_stack_workspace_size(ctypes.byref(c), T, V)
+    need0 = lib.moe_stack_workspace_size(ctypes.byref(c), T, 0)
+    # the stack needs one layer's workspace, the normalised input and the head's scores
+    assert need0 >= lib.moe_workspace_size(ctypes.byref(c), T) + T * 1024 * 2
+    assert need >= need0 + lib.moe_codec_head_workspace_size(ctypes.byref(c), V, T)
+    assert lib.moe_stack_workspace_size(ctypes.byref(c), T, -1) == 0
+
+    def call(**kw):
+        return lib.moe_stack_forward(
+            ctypes.byref(c), kw.get("layers", arr), kw.get("L", 3), kw.get("x", _p()), kw.get("T", T),
+            kw.get("gains", None), ctypes.c_float(kw.get("eps", 1e-6)), kw.get("head", _p(1 << 24)),
+            kw.get("V", V), kw.get("h", _p(1 << 26)), kw.get("xn", None), kw.get("c0", _p(1 << 28)), _p(1 << 30),
+            kw.get("ws", need), None)
+
+    assert call(L=0) == -1
+    assert call(layers=None) == -1
+    assert call(eps=-1.0) == -1
+    assert call(x=None) == -1
+    assert call(h=None) == -1
+    assert call(head=None) == -1                 # c0 needs the head
+    assert call(V=0) == -1
+    assert call(xn=_p()) == -1                   # xn_out may not alias x
+    assert call(xn=_p(1 << 26)) == -1            # ... nor h_out
+    assert call(ws=need - 256) == -3
+    assert call(T=0) == 0
+    w_bad = api.moe_weights(FAKE, None, FAKE, FAKE, None, FAKE, FAKE, FAKE)
+    assert call(layers=(api.moe_weights * 3)(w, w, w_bad)) == -1   # every layer checked before launching

@@ -11,6 +11,11 @@
 * The layer captured in a HIP graph, replayed several times with other eager
   layer calls in between (the launch configuration the benchmark times): every
   replay equals the eager result bit for bit.
+* The stack entry point (each layer's combine, residual add and the next
+  RMSNorm in one launch; T = 64, 333 and 4096, three layers, non-unit gains)
+  against moe_rmsnorm + moe_layer_forward called layer by layer: bit for bit,
+  in place too; c_0 exact against the oracle's argmax of its final state; and
+  the whole stack with its head captured in one graph and replayed.
 """
 import numpy as np
 import pytest
@@ -103,3 +108,87 @@ def test_layer_graph_replay(T):
         assert torch.equal(y_g.view(torch.int16), y_eager.view(torch.int16)), "replay %d differs" % rep
         assert not torch.equal(y_other.view(torch.int16), y_eager.view(torch.int16))
     print("graph replay T=%d: 3 replays equal to eager" % T, flush=True)
+
+
+def _stack_inputs(T, L, dev):
+    shape = INP.TALKER
+    layers_np = [INP.layer_weights(shape, 30 + l, 0.02, "bf16") for l in range(L)]
+    layers = [G.weights_dev(w, "bf16") for w in layers_np]
+    head_np = INP.stack_weights(shape, 0, 30, 0.02, "bf16", 3072, 50)["codec_head"]
+    rng = np.random.default_rng(70)
+    gains = torch.from_numpy((1.0 + 0.1 * rng.standard_normal((L + 1, shape.H))).astype(np.float32)).to(dev)
+    x = G.dev(INP.activations(T, shape.H, 30, "bf16"), "bf16")
+    return shape, layers, G.dev(head_np, "bf16"), head_np, gains, x
+
+
+def _layer_by_layer(cfg, layers, x, gains, eps, head):
+    h = x
+    for l, wd in enumerate(layers):
+        xn = api.moe_rmsnorm(cfg, h, gains[l], eps)
+        h = api.moe_layer_forward(cfg, wd, xn, h)
+    xf = api.moe_rmsnorm(cfg, h, gains[len(layers)], eps)
+    c0, _ = api.moe_codec_head_argmax(cfg, xf, head)
+    return h, xf, c0
+
+
+@pytest.mark.parametrize("T", [64, 333, 4096])
+def test_stack_entry_point_matches_layer_by_layer(T):
+    """moe_stack_forward (combine, residual and the next RMSNorm fused) equals
+    moe_rmsnorm + moe_layer_forward called layer by layer, bit for bit; its c_0 is
+    the exact argmax of the oracle's codec_head logits of its own final state."""
+    dev = torch.device("cuda", 0)
+    L, eps = 3, 1e-6
+    shape, layers, head, head_np, gains, x = _stack_inputs(T, L, dev)
+    cfg = G.config(shape, "bf16")
+    h_ref, xf_ref, c0_ref = _layer_by_layer(cfg, layers, x, gains, eps, head)
+    xn = torch.empty_like(x)
+    h, _, c0 = api.moe_stack_forward(cfg, layers, x, gains, eps, head, xn_out=xn)
+    torch.cuda.synchronize()
+    assert torch.equal(h.view(torch.int16), h_ref.view(torch.int16))
+    assert torch.equal(xn.view(torch.int16), xf_ref.view(torch.int16))
+    assert torch.equal(c0, c0_ref)
+    want = R.argmax_first(R.codec_head_logits(G.host64(xn), INP.to_f64(head_np, "bf16")))
+    np.testing.assert_array_equal(c0.cpu().numpy(), want)
+    # h_out may alias x (the stack updates the hidden state in place)
+    h_in = x.clone()
+    api.moe_stack_forward(cfg, layers, h_in, gains, eps, head, h_out=h_in, want_c0=False)
+    torch.cuda.synchronize()
+    assert torch.equal(h_in.view(torch.int16), h_ref.view(torch.int16))
+    # no gains (all 1.0), no head
+    ones = torch.ones((L + 1, shape.H), dtype=torch.float32, device=dev)
+    h1_ref, xf1_ref, _ = _layer_by_layer(cfg, layers, x, ones, eps, head)
+    xn1 = torch.empty_like(x)
+    h1, _, none = api.moe_stack_forward(cfg, layers, x, None, eps, None, xn_out=xn1)
+    torch.cuda.synchronize()
+    assert none is None
+    assert torch.equal(h1.view(torch.int16), h1_ref.view(torch.int16))
+    assert torch.equal(xn1.view(torch.int16), xf1_ref.view(torch.int16))
+    print("stack entry point T=%d L=%d: equal to layer-by-layer; c0 exact" % (T, L), flush=True)
+
+
+def test_stack_graph_replay():
+    """The stack with its head captured in one HIP graph: every replay, with other
+    eager stack calls in between, equals the eager result."""
+    dev = torch.device("cuda", 0)
+    T, L, eps = 64, 4, 1e-6
+    shape, layers, head, _, gains, x = _stack_inputs(T, L, dev)
+    cfg = G.config(shape, "bf16")
+    ws = api.workspace(api.moe_stack_workspace_size(cfg, T, 3072), dev)
+    h_e, _, c0_e = api.moe_stack_forward(cfg, layers, x, gains, eps, head, ws=ws)
+    torch.cuda.synchronize()
+    h_g, c0_g = torch.empty_like(x), torch.empty(T, dtype=torch.int32, device=dev)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        api.moe_stack_forward(cfg, layers, x, gains, eps, head, h_out=h_g, c0=c0_g, ws=ws)
+    x2 = G.dev(INP.activations(T, shape.H, 31, "bf16"), "bf16")
+    for rep in range(3):
+        h_o, _, _ = api.moe_stack_forward(cfg, layers[::-1], x2, gains, eps, head)
+        torch.cuda.synchronize()
+        h_g.zero_()
+        c0_g.fill_(-1)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(h_g.view(torch.int16), h_e.view(torch.int16)), "replay %d differs" % rep
+        assert torch.equal(c0_g, c0_e), "replay %d c0 differs" % rep
+        assert not torch.equal(h_o.view(torch.int16), h_e.view(torch.int16))
+    print("stack graph replay T=%d L=%d: 3 replays equal to eager" % (T, L), flush=True)
