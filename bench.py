@@ -74,9 +74,12 @@ def pct(a, q):
     return float(np.percentile(np.asarray(a), q)) if len(a) else None
 
 
-def measure(api, torch, INP, shape, T, weight_sets, steps, warmup):
+def measure(api, torch, INP, shape, T, weight_sets, steps, warmup, bias=None):
     cfg = api.Config(shape.H, shape.E, shape.k, shape.I, shape.Is, True, torch.bfloat16)
     dev = torch.device("cuda", 0)
+    if bias is not None:
+        b = torch.from_numpy(np.asarray(bias, np.float32)).to(dev)
+        weight_sets = [dict(w, router_bias=b) for w in weight_sets]
     to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
     xs = [to_dev(INP.activations(T, shape.H, 30 + i, "bf16")) for i in range(len(weight_sets))]
     ys = [torch.empty_like(x) for x in xs]
@@ -85,11 +88,12 @@ def measure(api, torch, INP, shape, T, weight_sets, steps, warmup):
     R = len(weight_sets)
 
     # routing of each weight set: number of experts that receive tokens
-    touched = []
+    touched, max_rows = [], []
     counts = torch.empty(shape.E, dtype=torch.int32, device=dev)
     for i in range(R):
         api.moe_layer_forward(cfg, structs[i], xs[i], y=ys[i], counts=counts, ws=ws)
         touched.append(int((counts > 0).sum().item()))
+        max_rows.append(int(counts.max().item()))
     torch.cuda.synchronize()
 
     for i in range(warmup):
@@ -163,7 +167,7 @@ def measure(api, torch, INP, shape, T, weight_sets, steps, warmup):
         "T": T, "steps": steps, "warmup": warmup, "weight_sets": R,
         "ms_per_step": gpu_ms / steps, "wall_ms_per_step": wall * 1e3 / steps,
         "eager_ms_per_step": eager_ms / steps,
-        "tokens_per_s": T / s, "touched_experts": touched,
+        "tokens_per_s": T / s, "touched_experts": touched, "max_rows_per_expert": max_rows,
         "layer_bytes": lb, "layer_flops": lf, "layer_hbm_frac": lb / s / (HBM_PEAK_GBS * 1e9),
         "layer_mfma_frac": lf / s / (MFMA_BF16_PEAK_TFLOPS * 1e12),
         "step_us": {"p50": pct(step_us, 50), "p95": pct(step_us, 95), "p99": pct(step_us, 99)},
@@ -253,6 +257,8 @@ def main():
     ap.add_argument("--no-stack", action="store_true")
     ap.add_argument("--stack-layers", type=int, default=20)
     ap.add_argument("--stack-frames", type=int, default=20)
+    ap.add_argument("--no-reports", action="store_true",
+                    help="skip the report-only workloads (Zipf-skewed T=8192 layer, 20-layer stack at T=1024)")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="after timing, copy a buffer of this many MiB once (a plain copy kernel of known size, "
                          "for scaling hardware byte counters)")
@@ -295,6 +301,22 @@ def main():
         log("stack: %d layers + codec head, T=64" % args.stack_layers)
         stack = measure_stack(api, torch, INP, shape, 64, sets, args.stack_layers, args.stack_frames)
         log("stack: %.1f us/frame, %.2f us/layer" % (stack["frame_us"], stack["per_layer_us"]))
+    reports = None
+    if not args.no_reports and not args.no_decode and not args.no_prefill:
+        c = INP.WORKLOADS["skew_t8192"]
+        log("report: Zipf-skewed layer T=8192")
+        sk = measure(api, torch, INP, shape, 8192, sets, max(10, args.steps // 4), max(2, args.warmup // 4),
+                     bias=INP.zipf_router_bias(shape.E, c["zipf_s"], c["zipf_seed"]))
+        log("report: stack of 20 layers + codec head, T=1024")
+        st1k = measure_stack(api, torch, INP, shape, 1024, sets, 20, max(5, args.stack_frames // 4))
+        reports = {
+            "skew": {"workload": "talker_moe_layer_zipf%.1f_T8192" % c["zipf_s"], "tokens_per_s": sk["tokens_per_s"],
+                     "ms_per_step": sk["ms_per_step"], "mfma_frac": sk["layer_mfma_frac"],
+                     "hbm_frac": sk["layer_hbm_frac"], "touched_experts": sk["touched_experts"],
+                     "max_rows_per_expert": sk["max_rows_per_expert"], "stages_us_mean": sk["stages_us_mean"]},
+            "stack_T1024": st1k,
+        }
+        log("skew: %.1f us/step; stack T=1024: %.1f us/frame" % (sk["ms_per_step"] * 1e3, st1k["frame_us"]))
     if args.copy_calibration_mb:
         # one device-to-device copy of n bytes from a source evicted from the
         # caches (a 2 GiB sweep after it was written), so the counters of that
@@ -338,7 +360,8 @@ def main():
                      "achieved": g["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": g["gbs"] / HBM_PEAK_GBS, "traffic": measured_traffic(),
                      "bytes_per_launch": g["bytes"], "mean_us": g["mean_us"]},
-        "layer": {"hbm_frac": dec["layer_hbm_frac"], "bytes_per_step": dec["layer_bytes"],
+        "layer": {"hbm_frac": dec["layer_hbm_frac"], "mfma_frac": dec["layer_mfma_frac"],
+                  "bytes_per_step": dec["layer_bytes"],
                   "timing": "HIP graph replay (the rotated layers back to back in one graph); "
                             "eager_ms_per_step without graphs",
                   "eager_ms_per_step": dec["eager_ms_per_step"],
@@ -348,6 +371,8 @@ def main():
     }
     if stack is not None:
         line["stack"] = stack
+    if reports is not None:
+        line["reports"] = reports
     if pre is not None:
         gp = pre["gate_up"]
         line["prefill"] = {"workload": "talker_moe_layer_prefill_T4096", "tokens_per_s": pre["tokens_per_s"],
