@@ -25,7 +25,8 @@ Readings where the pages leave a step open (each listed in the design notes):
   * the shared expert is added ungated;
   * Top-k is taken on the logits (softmax is strictly increasing), ties go to the
     lower expert index, and the k outputs are listed in descending weight;
-  * c_0 is the argmax of the codec_head logits, ties to the lowest code.
+  * c_0 is the argmax of the codec_head logits, ties to the lowest code; the
+    sampled variant draws by inverse transform from one given uniform per token.
 
 All floating-point work is float64; weights are taken in nn.Linear layout
 [out_features, in_features], so a projection is ``x @ W.T``.
@@ -41,7 +42,7 @@ import numpy as np
 
 __all__ = [
     "silu", "softmax", "router_logits", "topk_select", "topk_weights", "route",
-    "swiglu", "moe_layer", "permute", "rmsnorm", "codec_head_logits", "argmax_first",
+    "swiglu", "moe_layer", "permute", "rmsnorm", "codec_head_logits", "argmax_first", "sample_inverse_cdf",
     "stack_forward", "active_ffn_width",
 ]
 
@@ -187,6 +188,27 @@ def codec_head_logits(xf: np.ndarray, w_head: np.ndarray) -> np.ndarray:
 def argmax_first(logits: np.ndarray) -> np.ndarray:
     """Index of the largest value per row; the lowest index among equal maxima ([P1] lab c_0)."""
     return np.argmax(np.asarray(logits, np.float64), axis=-1).astype(np.int64)
+
+
+def sample_inverse_cdf(logits: np.ndarray, u: np.ndarray, temperature: float = 1.0) -> np.ndarray:
+    """c_0 drawn from softmax(logits / temperature), one uniform u per row.
+
+    [P5] "Codec Head" says the 3072 logits go through a softmax and the next
+    semantic code is sampled from it (the lab [P1] takes the argmax instead).
+    The draw here is inverse transform sampling: the first code v whose
+    cumulative probability exceeds u, i.e. sum_{i<=v} e_i > u * sum_i e_i with
+    e_i = exp((l_i - max l) / temperature).  u outside [0, 1) clamps to the first
+    or the last code.  The pages name no temperature; 1.0 is the plain softmax.
+    """
+    t = float(temperature)
+    if not t > 0:
+        raise ValueError("temperature must be positive")
+    lg = np.asarray(logits, np.float64)
+    e = np.exp((lg - lg.max(axis=-1, keepdims=True)) / t)
+    c = np.cumsum(e, axis=-1)
+    thr = np.asarray(u, np.float64) * c[..., -1]
+    idx = np.sum(c <= thr[..., None], axis=-1)
+    return np.minimum(idx, lg.shape[-1] - 1).astype(np.int64)
 
 
 def stack_forward(x: np.ndarray, layers: Sequence[Dict[str, np.ndarray]], k: int,

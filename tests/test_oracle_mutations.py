@@ -12,7 +12,8 @@ from oracle import moe_ref as R
 import tests.test_oracle_pins as P
 
 _orig = {n: getattr(R, n) for n in ("silu", "swiglu", "topk_select", "topk_weights", "rmsnorm",
-                                     "permute", "router_logits", "moe_layer", "softmax")}
+                                     "permute", "router_logits", "moe_layer", "softmax",
+                                     "sample_inverse_cdf")}
 
 
 def _swapped_gate_up(x, wg, wu, wd):
@@ -62,6 +63,21 @@ def _drop_shared(x, weights, k, bias=None, norm_topk_prob=True, residual=None):
     return _orig["moe_layer"](x, w, k, bias, norm_topk_prob, residual)
 
 
+def _sample_at_or_above(lg, u, temperature=1.0):  # >= instead of > at a boundary
+    e = np.exp((lg - lg.max(axis=-1, keepdims=True)) / temperature)
+    c = np.cumsum(e, axis=-1)
+    return np.minimum(np.sum(c < (u * c[..., -1])[..., None], axis=-1), lg.shape[-1] - 1)
+
+
+def _sample_times_temperature(lg, u, temperature=1.0):
+    return _orig["sample_inverse_cdf"](np.asarray(lg) * temperature * temperature, u, temperature)
+
+
+def _sample_reversed(lg, u, temperature=1.0):  # cumulated from the last code
+    lg = np.asarray(lg)
+    return lg.shape[-1] - 1 - _orig["sample_inverse_cdf"](lg[..., ::-1], u, temperature)
+
+
 MUTATIONS = [
     ("swiglu", _swapped_gate_up),
     ("topk_select", _ties_to_higher),
@@ -71,6 +87,9 @@ MUTATIONS = [
     ("permute", _unstable_permute),
     ("router_logits", _transposed_router),
     ("moe_layer", _drop_shared),
+    ("sample_inverse_cdf", _sample_at_or_above),
+    ("sample_inverse_cdf", _sample_times_temperature),
+    ("sample_inverse_cdf", _sample_reversed),
 ]
 
 PINS = [n for n in dir(P) if n.startswith("test_") and not n.startswith("test_bruteforce")

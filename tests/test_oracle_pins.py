@@ -329,3 +329,44 @@ def test_bf16_rounding_is_nearest_even():
     got = INP.bf16_round(vals)
     ref = torch.from_numpy(vals).to(torch.bfloat16).to(torch.float32).numpy()
     np.testing.assert_array_equal(got, ref)
+
+
+# --- c_0 sampling ([P5] "Codec Head": softmax over the logits, then a draw) ---
+
+def test_sample_boundaries_uniform_closed_form():
+    # four equal logits: cumulative probabilities are exactly 1/4, 1/2, 3/4, 1, and
+    # a draw exactly on a boundary belongs to the next code (strictly greater)
+    lg = np.zeros((1, 4))
+    for u, want in [(0.0, 0), (0.2499, 0), (0.25, 1), (0.5, 2), (0.7499, 2), (0.75, 3), (0.9999, 3),
+                    (1.0, 3), (1.5, 3), (-0.5, 0)]:
+        assert int(R.sample_inverse_cdf(lg, np.array([u]))[0]) == want, u
+    # a shift of every logit changes nothing
+    assert int(R.sample_inverse_cdf(lg + 123.25, np.array([0.5]))[0]) == 2
+
+
+def test_sample_frequencies_match_softmax():
+    # inverse transform sampling reproduces softmax(l / t) (chi-square over 400k draws)
+    from scipy.stats import chisquare
+    rng = np.random.default_rng(71)
+    lg = rng.normal(0.0, 1.0, 6)
+    n = 400_000
+    u = rng.random(n)
+    for t in (1.0, 0.5, 2.5):
+        got = R.sample_inverse_cdf(np.broadcast_to(lg, (n, 6)), u, t)
+        freq = np.bincount(got, minlength=6)
+        want = sp_softmax(lg / t) * n
+        assert chisquare(freq, want).pvalue > 1e-4, t
+
+
+def test_sample_cold_temperature_is_argmax_and_order_is_by_index():
+    rng = np.random.default_rng(72)
+    lg = rng.normal(0.0, 1.0, (32, 3072))
+    u = rng.random(32) * 0.999
+    gap = np.sort(lg, axis=1)[:, -1] - np.sort(lg, axis=1)[:, -2]
+    t = float(gap.min()) / 60.0   # the best code holds all but < 3072 e^-60 of the mass
+    np.testing.assert_array_equal(R.sample_inverse_cdf(lg, u, t), R.argmax_first(lg))
+    # two codes, the first with probability p: u < p draws code 0, else code 1
+    p = 1.0 / (1.0 + math.exp(-0.75))
+    two = np.array([[0.75, 0.0]])
+    assert int(R.sample_inverse_cdf(two, np.array([p - 1e-9]))[0]) == 0
+    assert int(R.sample_inverse_cdf(two, np.array([p + 1e-9]))[0]) == 1
