@@ -214,9 +214,33 @@ def measure_stack(api, torch, INP, shape, T, weight_sets, L, frames, vocab=3072)
     stop.record()
     torch.cuda.synchronize()
     eager_ms = start.elapsed_time(stop) / frames
+    # the head alone on the final state: exact argmax against the sampled draw
+    xn = torch.empty_like(x)
+    api.moe_stack_forward(cfg, structs[:1], x, gains[:2], 1e-6, None, xn_out=xn, ws=ws)
+    u = torch.rand(T, dtype=torch.float64, device=dev)
+    c0s = torch.empty_like(c0)
+    hws = api.workspace(api.moe_stack_workspace_size(cfg, T, vocab), dev)
+    head_us = {}
+    for name, fn in (("argmax", lambda: api.moe_codec_head_argmax(cfg, xn, head, c0=c0s, ws=hws)),
+                     ("sample", lambda: api.moe_codec_head_sample(cfg, xn, head, u, 1.0, c0=c0s, ws=hws))):
+        fn()
+        torch.cuda.synchronize()
+        hg = torch.cuda.CUDAGraph()  # 20 calls in one graph: device time, not launch overhead
+        with torch.cuda.graph(hg):
+            for _ in range(20):
+                fn()
+        hg.replay()
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(5):
+            hg.replay()
+        stop.record()
+        torch.cuda.synchronize()
+        head_us[name] = start.elapsed_time(stop) * 1e3 / 100
     return {"workload": "talker_moe_stack%d_codec_head_T%d" % (L, T), "layers": L, "tokens": T, "vocab": vocab,
             "weight_sets_rotated": len(weight_sets), "frames": frames,
             "frame_us": frame_ms * 1e3, "per_layer_us": frame_ms * 1e3 / L, "eager_frame_us": eager_ms * 1e3,
+            "codec_head_us": head_us,
             "tokens_per_s": T / (frame_ms / 1e3),
             "timing": "one HIP graph per frame: RMSNorm, L layers (combine + residual + next RMSNorm fused), "
                       "codec_head argmax"}

@@ -224,6 +224,26 @@ int moe_codec_head_argmax(const moe_config* cfg, const void* x, const void* w_he
 size_t moe_codec_head_workspace_size(const moe_config* cfg, int32_t V, int64_t T);
 
 /*
+ * moe_codec_head_sample — c_0 drawn from the softmax of the codec head's logits
+ * ("用 print(model) 认识 Qwen3-TTS", "Codec Head：语义码预测": the 3072 logits go
+ * through a softmax and the next semantic code is sampled).  Inverse transform
+ * with one caller-supplied uniform per token:
+ *   e_v = exp(logit_v / temperature) (up to a common factor),
+ *   c0[t] = the first v with  sum_{i<=v} e_i > u[t] * sum_i e_i.
+ * The decision is exact up to fp64 rounding: it is certified from the fp32
+ * logits and their error bounds, and tokens whose u falls within that error of
+ * a boundary are decided on logits recomputed in fp64.  The random numbers are
+ * inputs, so a draw is reproducible.
+ *   x [dev] [T, H]; w_head [dev] [V, H]; 1 <= V <= 8192; temperature > 0 (finite)
+ *   u      [dev] [T] fp64 uniforms; u < 0 or NaN gives code 0, u >= 1 code V - 1
+ *   logits [dev] [T, V] fp32 out, or NULL;  c0 [dev] [T] int32 out
+ * Workspace: moe_codec_head_workspace_size(cfg, V, T).
+ */
+int moe_codec_head_sample(const moe_config* cfg, const void* x, const void* w_head, int32_t V, int64_t T,
+                          float temperature, const double* u, float* logits, int32_t* c0, void* ws,
+                          size_t ws_bytes, void* stream);
+
+/*
  * moe_stack_forward — L stacked layers and the codec head, the lab's [3C]
  * step layer by layer ("Bài Lab tổng hợp — Qwen3-Omni & Qwen3-TTS-12Hz
  * Architecture"; 20 layers and codec_head 1024 -> 3072 on the Talker MoE page,

@@ -26,7 +26,7 @@ EXPORTS = ("moe_status_string", "moe_check_config", "moe_workspace_size", "moe_r
            "moe_grouped_swiglu", "moe_shared_swiglu", "moe_combine", "moe_layer_forward",
            "moe_layer_forward_timed", "moe_rmsnorm",
            "moe_codec_head_argmax", "moe_codec_head_workspace_size", "moe_stack_forward",
-           "moe_stack_workspace_size")
+           "moe_stack_workspace_size", "moe_codec_head_sample")
 
 
 class MoeError(RuntimeError):
@@ -102,6 +102,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         "moe_stack_forward": (ctypes.c_int, [cfgp, ctypes.POINTER(moe_weights), i32, vp, i64, vp, ctypes.c_float,
                                              vp, i32, vp, vp, vp, vp, sz, vp]),
         "moe_stack_workspace_size": (sz, [cfgp, i64, i32]),
+        "moe_codec_head_sample": (ctypes.c_int, [cfgp, vp, vp, i32, i64, ctypes.c_float, vp, vp, vp, vp, sz, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -288,6 +289,26 @@ def moe_codec_head_argmax(cfg: Config, x: torch.Tensor, w_head: torch.Tensor, wa
     _check("moe_codec_head_argmax", lib.moe_codec_head_argmax(
         ctypes.byref(cfg.c()), _ptr(x), _ptr(w_head), V, T, _ptr(logits), _ptr(c0), _ptr(buf), buf.numel(),
         _stream(dev)))
+    return c0, logits
+
+
+def moe_codec_head_sample(cfg: Config, x: torch.Tensor, w_head: torch.Tensor, u: torch.Tensor,
+                          temperature: float = 1.0, want_logits: bool = False, c0=None, logits=None, ws=None):
+    """c_0 drawn from softmax(logits / temperature) with the uniforms u [T] (fp64).
+    Returns (c0 [T] int32, logits [T, V] fp32 or None)."""
+    T, dev = x.shape[0], x.device
+    V = w_head.shape[0]
+    if u.dtype != torch.float64 or u.numel() < T:
+        raise ValueError("u must hold T float64 values")
+    c0 = c0 if c0 is not None else torch.empty(T, dtype=torch.int32, device=dev)
+    if want_logits and logits is None:
+        logits = torch.empty((T, V), dtype=torch.float32, device=dev)
+    lib = load_library()
+    need = int(lib.moe_codec_head_workspace_size(ctypes.byref(cfg.c()), V, T))
+    buf = ws if ws is not None else workspace(need, dev)
+    _check("moe_codec_head_sample", lib.moe_codec_head_sample(
+        ctypes.byref(cfg.c()), _ptr(x), _ptr(w_head), V, T, temperature, _ptr(u), _ptr(logits), _ptr(c0),
+        _ptr(buf), buf.numel(), _stream(dev)))
     return c0, logits
 
 

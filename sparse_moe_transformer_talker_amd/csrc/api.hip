@@ -634,4 +634,25 @@ int moe_codec_head_argmax(const moe_config* cfg, const void* x, const void* w_he
     return hip_status(launch_argmax(cfg->dtype, sc, bd, x, w_head, T, cfg->hidden_size, V, c0, s));
 }
 
+int moe_codec_head_sample(const moe_config* cfg, const void* x, const void* w_head, int32_t V, int64_t T,
+                          float temperature, const double* u, float* logits, int32_t* c0, void* ws, size_t ws_bytes,
+                          void* stream) {
+    int st = check_cfg(cfg);
+    if (st != MOE_OK) return st;
+    if (T < 0 || V < 1 || !(temperature > 0.0f) || !(temperature < INFINITY)) return MOE_ERR_INVALID;
+    if (!sample_ok(V) || T > (int64_t(1) << 22)) return MOE_ERR_UNSUPPORTED;
+    if (T == 0) return MOE_OK;
+    if (!ok_ptr(x) || !ok_ptr(w_head) || !ok_ptr(u) || !ok_opt(logits) || !ok_ptr(c0) || !ok_ptr(ws))
+        return MOE_ERR_INVALID;
+    if (ws_bytes < moe_codec_head_workspace_size(cfg, V, T)) return MOE_ERR_WORKSPACE;
+    Carver cv(ws);
+    float* sc = cv.take<float>(T * V);
+    float* bd = cv.take<float>(T * V);
+    if (logits) sc = logits;
+    hipStream_t s = as_stream(stream);
+    TMOE_TRY(launch_scores_exact(cfg->dtype, x, w_head, T, cfg->hidden_size, V, sc, bd, s));
+    return hip_status(launch_sample(cfg->dtype, sc, bd, x, w_head, T, cfg->hidden_size, V, (double)temperature, u,
+                                    c0, s));
+}
+
 }  // extern "C"

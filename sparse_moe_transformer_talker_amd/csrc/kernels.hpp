@@ -49,6 +49,17 @@ hipError_t launch_route_block(const void* x, const void* W, const float* bias, i
                               int32_t* bcnt, int32_t* blist, hipStream_t st);
 hipError_t launch_argmax(int dtype, const float* sc, const float* bd, const void* x, const void* W, int64_t T, int H,
                          int n, int32_t* out, hipStream_t st);
+// Draw per token from softmax(scores / tau) by inverse transform with the given
+// uniform u[t] (fp64), exact up to fp64 rounding: certified from sc / bd, else
+// from fp64 logits recomputed from x and W.  n <= kSampleMaxN.
+constexpr int kSampleMaxN = 8192;
+bool sample_ok(int n);
+// Scores with the tightest bounds available (fp64 sums of exact products for bf16
+// with H % 256 == 0, at any T; else launch_scores).
+hipError_t launch_scores_exact(int dtype, const void* x, const void* W, int64_t T, int H, int n, float* sc, float* bd,
+                               hipStream_t st);
+hipError_t launch_sample(int dtype, const float* sc, const float* bd, const void* x, const void* W, int64_t T, int H,
+                         int n, double tau, const double* u, int32_t* out, hipStream_t st);
 
 // --- grouping (permute.hip) ---
 // Tiling of one grouped GEMM: items are (expert, n0, m0, rows) tiles of at most

@@ -1304,36 +1304,85 @@ __global__ __launch_bounds__(kSelectGroupThreads) void select_group_small_kernel
     }
 }
 
-// Exact argmax over n scores of any length: one wave per token.
+// Exact argmax over n scores of any length (ties to the lower index): one block
+// of four waves per token, thread j taking entries j + 256 i.  From the fp32
+// scores s and their bounds d: the fp32 argmax, and low = max (s - d), a lower
+// bound of the exact maximum; entries with s + d >= low are the candidates.  With
+// more than one, each wave rescores the candidates among its own entries in
+// fp64 from x and W, and the four winners are ranked.
+constexpr int kArgmaxThreads = 256;
+constexpr int kArgmaxWaves = kArgmaxThreads / kWave;
+
 template <typename T>
-__global__ __launch_bounds__(256) void argmax_exact_kernel(const float* __restrict__ sc, const float* __restrict__ bd,
-                                                           const T* __restrict__ x, const T* __restrict__ W,
-                                                           int64_t Ttok, int H, int n, int32_t* __restrict__ out) {
-    const int wave = threadIdx.x >> 6;
-    const int lane = lane_id();
-    const int64_t t = (int64_t)blockIdx.x * 4 + wave;
-    if (t >= Ttok) return;
+__global__ __launch_bounds__(kArgmaxThreads) void argmax_exact_kernel(const float* __restrict__ sc,
+                                                                      const float* __restrict__ bd,
+                                                                      const T* __restrict__ x,
+                                                                      const T* __restrict__ W, int H, int n,
+                                                                      int32_t* __restrict__ out) {
+    __shared__ uint64_t kx[kArgmaxWaves];
+    __shared__ double lx[kArgmaxWaves], bx[kArgmaxWaves];
+    __shared__ int nx[kArgmaxWaves], ix[kArgmaxWaves];
+    const int wave = (int)(threadIdx.x >> 6), lane = lane_id();
+    const int64_t t = blockIdx.x;
     const float* s = sc + t * n;
     const float* d = bd + t * n;
-    // fp32 argmax and a lower bound of the maximum (interval ends in fp64)
+    constexpr int U = 4;  // entries per thread with loads in flight together
     uint64_t key = 0;
     double low = -1.0e300;
-    for (int e = lane; e < n; e += kWave) {
-        const uint64_t kk = rank_key(s[e], e);
-        key = kk > key ? kk : key;
-        low = fmax(low, (double)s[e] - (double)d[e]);
+    for (int e0 = (int)threadIdx.x; e0 < n; e0 += U * kArgmaxThreads) {
+        float sv[U], dv[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {  // branch-free: entries past the end repeat the last one, unused
+            const int e = min(e0 + u * kArgmaxThreads, n - 1);
+            sv[u] = s[e];
+            dv[u] = d[e];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int e = e0 + u * kArgmaxThreads;
+            if (e >= n) continue;
+            const uint64_t kk = rank_key(sv[u], e);
+            key = kk > key ? kk : key;
+            low = fmax(low, (double)sv[u] - (double)dv[u]);
+        }
     }
     key = wave_max_key(key);
-    int bi = rank_key_index(key);
     low = double_from_order_key(wave_max_key(double_order_key(low)));
-    int ncand = 0;
-    for (int e = lane; e < n; e += kWave) ncand += ((double)s[e] + (double)d[e] >= low) ? 1 : 0;
-    ncand = __builtin_amdgcn_readlane(wave_incl_scan(ncand), 63);
-    if (ncand > 1) {
+    if (lane == 0) {
+        kx[wave] = key;
+        lx[wave] = low;
+    }
+    __syncthreads();
+    key = kx[0];
+    low = lx[0];
+    for (int w = 1; w < kArgmaxWaves; ++w) {
+        key = kx[w] > key ? kx[w] : key;
+        low = fmax(low, lx[w]);
+    }
+    int bi = rank_key_index(key);
+    int nc = 0;
+    for (int e0 = (int)threadIdx.x; e0 < n; e0 += U * kArgmaxThreads) {
+        float sv[U], dv[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int e = min(e0 + u * kArgmaxThreads, n - 1);
+            sv[u] = s[e];
+            dv[u] = d[e];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (e0 + u * kArgmaxThreads < n) nc += ((double)sv[u] + (double)dv[u] >= low) ? 1 : 0;
+    }
+    nc = __builtin_amdgcn_readlane(wave_incl_scan(nc), 63);
+    if (lane == 0) nx[wave] = nc;
+    __syncthreads();
+    nc = 0;
+    for (int w = 0; w < kArgmaxWaves; ++w) nc += nx[w];
+    if (nc > 1) {  // block-uniform
         double best = 0.0;
         int besti = -1;
         const T* xr = x + t * H;
-        for (int base = 0; base < n; base += kWave) {
+        for (int base = wave * kWave; base < n; base += kArgmaxThreads) {
             const int e = base + lane;
             const bool c = e < n && (double)s[e] + (double)d[e] >= low;
             uint64_t m = __ballot(c);
@@ -1343,12 +1392,207 @@ __global__ __launch_bounds__(256) void argmax_exact_kernel(const float* __restri
                 double r8[8];
                 wave_dot64<T, 8>(xr, W, H, ids, cnt, r8);
                 for (int i = 0; i < cnt; ++i)
-                    if (besti < 0 || ranks_before(r8[i], ids[i], best, besti)) { best = r8[i]; besti = ids[i]; }
+                    if (besti < 0 || ranks_before(r8[i], ids[i], best, besti)) {
+                        best = r8[i];
+                        besti = ids[i];
+                    }
             }
         }
-        bi = besti;
+        if (lane == 0) {
+            bx[wave] = best;
+            ix[wave] = besti;
+        }
+        __syncthreads();
+        bi = -1;
+        double bv = 0.0;
+        for (int w = 0; w < kArgmaxWaves; ++w)
+            if (ix[w] >= 0 && (bi < 0 || ranks_before(bx[w], ix[w], bv, bi))) {
+                bv = bx[w];
+                bi = ix[w];
+            }
     }
-    if (lane == 0) out[t] = bi;
+    if (threadIdx.x == 0) out[t] = bi;
+}
+
+// ---------------------------------------------------------------------------
+// c_0 drawn from softmax(logits / tau) by inverse transform: the first code v
+// with sum_{i<=v} e_i > u * sum_i e_i, e_i = exp(l_i / tau) up to a common
+// factor (the Qwen3-TTS module walkthrough, "Codec Head": a softmax over the
+// codec head's logits, then a draw).  u outside [0, 1) clamps to the first or
+// the last code.  One block of 16 waves per token; thread j owns the
+// contiguous codes [j s, j s + s), s = ceil(n / 1024).
+//  * Certified pass.  A score s_i with |s_i - l_i| <= d_i gives
+//    e_i = exp((l_i - M) / tau) within exp(+-w_i) of c_i = exp((s_i - M) / tau)
+//    (w_i = d_i / tau plus the argument's and exp's own rounding; the shift
+//    M = max (s + d) bounds every exact logit from above), so e_i lies in
+//    [lo_i, hi_i] = c_i [1 - w_i, 1 + w_i + w_i^2] for w_i <= 1 (exps otherwise).
+//    Prefix sums of both bounds, with a bound gam on their own rounding, decide
+//    for each v whether the exact prefix C_v certainly exceeds u Z, written
+//    C_v (1 - u) > u R_v with R_v = Z - C_v ("above"), or certainly does not
+//    ("below").  The draw is settled when the first v not below is also the
+//    first v above.
+//  * Exact pass, otherwise (u within the scores' error of a boundary): the
+//    token's n logits are recomputed in fp64 from x and W into LDS (products
+//    of the inputs are exact; only the fp64 additions round) and the
+//    definition is applied to them.
+constexpr int kSampleThreads = 1024;
+constexpr int kSampleWaves = kSampleThreads / kWave;
+
+struct ScanF64 {
+    double excl, total;
+};
+// Exclusive prefix sum of one value per thread in thread order, and the total
+// (fixed association: deterministic).  tmp: kSampleThreads + 1 doubles.
+__device__ ScanF64 block_scan_f64(double v, double* tmp) {
+    constexpr int PER = kSampleThreads / kWave;  // consecutive threads per lane of wave 0
+    __syncthreads();
+    tmp[threadIdx.x] = v;
+    __syncthreads();
+    if (threadIdx.x < kWave) {
+        const int l = (int)threadIdx.x;
+        double r[PER];
+        double acc = 0.0;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            r[i] = acc;  // exclusive within the lane's run
+            acc += tmp[PER * l + i];
+        }
+        double sum = acc;
+        for (int off = 1; off < kWave; off <<= 1) {
+            const double o = __shfl_up(sum, off);
+            if (l >= off) sum += o;
+        }
+        const double up = __shfl_up(sum, 1);
+        const double ex = l == 0 ? 0.0 : up;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) tmp[PER * l + i] = ex + r[i];
+        if (l == kWave - 1) tmp[kSampleThreads] = sum;
+    }
+    __syncthreads();
+    return {tmp[threadIdx.x], tmp[kSampleThreads]};
+}
+__device__ double block_max_f64(double v, double* tmp) {
+    for (int off = 1; off < kWave; off <<= 1) v = fmax(v, __shfl_xor(v, off));
+    __syncthreads();
+    if (lane_id() == 0) tmp[threadIdx.x >> 6] = v;
+    __syncthreads();
+    double m = tmp[0];
+    for (int w = 1; w < kSampleWaves; ++w) m = fmax(m, tmp[w]);
+    return m;
+}
+__device__ int block_min_i32(int v, int* tmp) {
+    for (int off = 1; off < kWave; off <<= 1) v = min(v, __shfl_xor(v, off));
+    __syncthreads();
+    if (lane_id() == 0) tmp[threadIdx.x >> 6] = v;
+    __syncthreads();
+    int m = tmp[0];
+    for (int w = 1; w < kSampleWaves; ++w) m = min(m, tmp[w]);
+    return m;
+}
+
+// Half-width w (in the exponent) of the interval of e_i around c = exp(a),
+// a = (s - M) * itau: the score's bound d, the rounding of a (three operations
+// and 1 / tau) and exp's own error.
+__device__ __forceinline__ double exp_halfwidth(float s, float d, double M, double itau) {
+    return ((double)d * (1.0 + 0x1p-50) + ((double)fabsf(s) + fabs(M)) * 0x1p-50) * itau + 0x1p-50;
+}
+__device__ __forceinline__ void exp_interval(double c, double a, double w, double& lo, double& hi) {
+    if (w <= 1.0) {  // exp(w) <= 1 + w + w^2 and exp(-w) >= 1 - w for 0 <= w <= 1
+        hi = c * (1.0 + w + w * w) * (1.0 + 0x1p-50);
+        lo = c * (1.0 - w) * (1.0 - 0x1p-50);
+    } else {  // the sum a +- w rounds by up to (|a| + w) 2^-53 in the exponent
+        const double r = (fabs(a) + w + 2.0) * 0x1p-50;
+        hi = exp(a + w) * (1.0 + r);
+        lo = exp(a - w) * (1.0 - r);
+    }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kSampleThreads) void sample_exact_kernel(const float* __restrict__ sc,
+                                                                      const float* __restrict__ bd,
+                                                                      const T* __restrict__ x,
+                                                                      const T* __restrict__ W, int H, int n,
+                                                                      double tau, const double* __restrict__ uin,
+                                                                      int32_t* __restrict__ out) {
+    extern __shared__ double lex[];  // c_i of the certified pass, then the exact logits
+    __shared__ double tmp[kSampleThreads + 1];
+    __shared__ int itmp[kSampleWaves];
+    const int64_t t = blockIdx.x;
+    const double u = uin[t];
+    if (!(u >= 0.0) || u >= 1.0) {  // clamp (NaN to the first code)
+        if (threadIdx.x == 0) out[t] = u >= 1.0 ? n - 1 : 0;
+        return;
+    }
+    const int seg = (n + kSampleThreads - 1) / kSampleThreads;
+    const int v0 = min((int)threadIdx.x * seg, n), v1 = min(v0 + seg, n);
+    const float* s = sc + t * n;
+    const float* d = bd + t * n;
+    const double itau = 1.0 / tau;
+
+    double ml = -INFINITY;
+    for (int v = v0; v < v1; ++v) ml = fmax(ml, (double)s[v] + (double)d[v]);
+    const double M = block_max_f64(ml, tmp);
+    double sl = 0.0, sh = 0.0;
+    for (int v = v0; v < v1; ++v) {
+        const double a = ((double)s[v] - M) * itau;
+        const double c = exp(a);
+        lex[v] = c;
+        double lo, hi;
+        exp_interval(c, a, exp_halfwidth(s[v], d[v], M, itau), lo, hi);
+        sl += lo;
+        sh += hi;
+    }
+    const ScanF64 pl = block_scan_f64(sl, tmp);
+    const ScanF64 ph = block_scan_f64(sh, tmp);
+    const double ZL = pl.total, ZH = ph.total;
+    // every computed prefix or total lies within gam of the exact sum of its terms
+    const double gam = (double)(n + 2 * kSampleThreads) * 0x1p-52 * ZH;
+    int first_above = n, first_open = n;
+    double L = pl.excl, Hs = ph.excl;
+    for (int v = v0; v < v1; ++v) {
+        const double a = ((double)s[v] - M) * itau;
+        double lo, hi;
+        exp_interval(lex[v], a, exp_halfwidth(s[v], d[v], M, itau), lo, hi);
+        L += lo;
+        Hs += hi;
+        const bool above = (L - gam) * (1.0 - u) > u * (ZH - Hs + 2.0 * gam) * (1.0 + 0x1p-50);
+        const bool below = (Hs + gam) * (1.0 - u) * (1.0 + 0x1p-50) <= u * (ZL - L - 2.0 * gam);
+        if (above && first_above == n) first_above = v;
+        if (!below && first_open == n) first_open = v;
+    }
+    int fo = block_min_i32(first_open, itmp);
+    const int fa = block_min_i32(first_above, itmp);
+    if (fo != fa) {  // block-uniform: the exact pass
+        const int wave = (int)(threadIdx.x >> 6), lane = lane_id();
+        const T* xr = x + t * H;
+        __syncthreads();  // every thread is done with the c_i in lex
+        for (int base = wave * 8; base < n; base += kSampleWaves * 8) {
+            int ids[8];
+            const int cnt = min(8, n - base);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) ids[i] = min(base + i, n - 1);
+            double r8[8];
+            wave_dot64<T, 8>(xr, W, H, ids, cnt, r8);
+            if (lane == 0)
+                for (int i = 0; i < cnt; ++i) lex[base + i] = r8[i];
+        }
+        __syncthreads();
+        double mx = -INFINITY;
+        for (int v = v0; v < v1; ++v) mx = fmax(mx, lex[v]);
+        mx = block_max_f64(mx, tmp);
+        double se = 0.0;
+        for (int v = v0; v < v1; ++v) se += exp((lex[v] - mx) / tau);
+        const ScanF64 pe = block_scan_f64(se, tmp);
+        const double thr = u * pe.total;
+        int first = n;
+        double c = pe.excl;
+        for (int v = v0; v < v1; ++v) {
+            c += exp((lex[v] - mx) / tau);
+            if (c > thr && first == n) first = v;
+        }
+        fo = block_min_i32(first, itmp);
+    }
+    if (threadIdx.x == 0) out[t] = min(fo, n - 1);
 }
 
 // ---------------------------------------------------------------------------
@@ -1492,11 +1736,40 @@ hipError_t launch_select_group_small(const float* scratch_sc, const float* scrat
 
 hipError_t launch_argmax(int dtype, const float* sc, const float* bd, const void* x, const void* W, int64_t Ttok,
                          int H, int n, int32_t* out, hipStream_t st) {
-    dim3 grid((unsigned)((Ttok + 3) / 4));
+    if (Ttok < 1) return hipSuccess;
     if (dtype == kBF16)
-        argmax_exact_kernel<bf16_t><<<grid, 256, 0, st>>>(sc, bd, (const bf16_t*)x, (const bf16_t*)W, Ttok, H, n, out);
+        argmax_exact_kernel<bf16_t><<<(unsigned)Ttok, kArgmaxThreads, 0, st>>>(sc, bd, (const bf16_t*)x,
+                                                                              (const bf16_t*)W, H, n, out);
     else
-        argmax_exact_kernel<float><<<grid, 256, 0, st>>>(sc, bd, (const float*)x, (const float*)W, Ttok, H, n, out);
+        argmax_exact_kernel<float><<<(unsigned)Ttok, kArgmaxThreads, 0, st>>>(sc, bd, (const float*)x,
+                                                                             (const float*)W, H, n, out);
+    return hipGetLastError();
+}
+
+bool sample_ok(int n) { return n >= 1 && n <= kSampleMaxN; }
+
+hipError_t launch_scores_exact(int dtype, const void* x, const void* W, int64_t Ttok, int H, int n, float* sc,
+                               float* bd, hipStream_t st) {
+    if (dtype == kBF16 && H % 256 == 0) {
+        dim3 grid((unsigned)((Ttok + 15) / 16), (unsigned)((n + 15) / 16));
+        scores64_kernel<<<grid, 64 * kS64Waves, 0, st>>>((const bf16_t*)x, (const bf16_t*)W, nullptr, Ttok, H, n, sc,
+                                                         bd);
+        return hipGetLastError();
+    }
+    return launch_scores(dtype, x, W, nullptr, Ttok, H, n, sc, bd, st);
+}
+
+hipError_t launch_sample(int dtype, const float* sc, const float* bd, const void* x, const void* W, int64_t Ttok,
+                         int H, int n, double tau, const double* u, int32_t* out, hipStream_t st) {
+    if (!sample_ok(n)) return hipErrorInvalidValue;
+    const size_t lds = (size_t)n * sizeof(double);
+    if (dtype == kBF16)
+        sample_exact_kernel<bf16_t><<<(unsigned)Ttok, kSampleThreads, lds, st>>>(sc, bd, (const bf16_t*)x,
+                                                                                  (const bf16_t*)W, H, n, tau, u,
+                                                                                  out);
+    else
+        sample_exact_kernel<float><<<(unsigned)Ttok, kSampleThreads, lds, st>>>(sc, bd, (const float*)x,
+                                                                                 (const float*)W, H, n, tau, u, out);
     return hipGetLastError();
 }
 

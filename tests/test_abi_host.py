@@ -169,3 +169,24 @@ def test_stack_argument_errors():
     assert call(T=0) == 0
     w_bad = api.moe_weights(FAKE, None, FAKE, FAKE, None, FAKE, FAKE, FAKE)
     assert call(layers=(api.moe_weights * 3)(w, w, w_bad)) == -1   # every layer checked before launching
+
+
+def test_codec_head_sample_argument_errors():
+    lib = api.load_library()
+    c = _cfg()
+    need = lib.moe_codec_head_workspace_size(ctypes.byref(c), 3072, 64)
+
+    def call(**kw):
+        return lib.moe_codec_head_sample(ctypes.byref(c), _p(), _p(1 << 24), kw.get("V", 3072), kw.get("T", 64),
+                                         ctypes.c_float(kw.get("temp", 1.0)), kw.get("u", _p(1 << 26)), None,
+                                         _p(1 << 27), _p(1 << 28), kw.get("ws", need), None)
+
+    assert call(temp=0.0) == -1
+    assert call(temp=-1.0) == -1
+    assert call(temp=float("nan")) == -1
+    assert call(temp=float("inf")) == -1
+    assert call(u=None) == -1
+    assert call(V=0) == -1
+    assert call(V=8193) == -2          # the exact pass keeps one token's logits in LDS
+    assert call(ws=need - 256) == -3
+    assert call(T=0) == 0

@@ -198,6 +198,13 @@ def test_layer_residual_and_determinism(talker):
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
 
 
+@pytest.mark.parametrize("T", [64, 300, 4096])
+def test_layer_without_renormalisation(talker, T):
+    # norm_topk_prob = False: the k softmax probabilities weight the experts as they
+    # are (decode path with the router's pair lists, the mid-size grouping, prefill)
+    _layer_check(talker, talker.x(T, seed=7), what="norm_topk_prob=0", norm=False)
+
+
 def test_layer_lab_scale_f32():
     c = INP.WORKLOADS["lab_f32"]
     L = Layer(c["shape"], c["seed"], c["sigma"], "f32")
@@ -243,6 +250,12 @@ def test_rmsnorm_and_codec_head(talker):
     c0b, _ = api.moe_codec_head_argmax(cfg, xn, G.dev(hd, "bf16"))
     torch.cuda.synchronize()
     assert int(c0b[0]) == 0
+    # decode-sized batch (exact-product scores): the same tie, and parity
+    c0c, _ = api.moe_codec_head_argmax(cfg, xn[:64].contiguous(), G.dev(hd, "bf16"))
+    c0d, _ = api.moe_codec_head_argmax(cfg, xn[:64].contiguous(), head)
+    torch.cuda.synchronize()
+    assert int(c0c[0]) == 0
+    np.testing.assert_array_equal(c0d.cpu().numpy(), R.argmax_first(ref_logits[:64]))
 
 
 def test_empty_batch(talker):
