@@ -27,7 +27,8 @@ import numpy as np
 
 __all__ = [
     "LayerShape", "WORKLOADS", "f32_to_bf16_bits", "bf16_bits_to_f32",
-    "layer_weights", "activations", "zipf_router_bias", "stack_weights",
+    "layer_weights", "activations", "zipf_router_bias", "stack_weights", "AttnShape", "TALKER_ATTN",
+    "attention_weights", "kv_cache", "cache_lengths", "speech_positions",
     "bf16_round", "to_f64", "workload_inputs",
 ]
 
@@ -151,6 +152,51 @@ def stack_weights(shape: LayerShape, layers: int, seed: int, sigma: float, dtype
     head = _store(_normal(np.random.default_rng(head_seed), (vocab, shape.H), sigma), dtype)
     return {"layers": ws, "codec_head": head,
             "norm_gain": np.ones(shape.H, dtype=np.float32)}
+
+
+@dataclasses.dataclass(frozen=True)
+class AttnShape:
+    """The Talker's attention: hidden size, query heads, key/value heads, head width."""
+    H: int = 1024
+    n_heads: int = 16
+    n_kv_heads: int = 2
+    head_dim: int = 128
+
+
+TALKER_ATTN = AttnShape()
+
+
+def attention_weights(shape: AttnShape, seed: int, sigma: float = 0.02) -> Dict[str, np.ndarray]:
+    """w_qkv [(nq + 2 nkv) d, H] and w_o [H, nq d] (bf16 bits), q_norm / k_norm gains [d] (fp32,
+    1 + N(0, 0.1))."""
+    rng = np.random.default_rng(seed + 20000)
+    d, nq, nkv = shape.head_dim, shape.n_heads, shape.n_kv_heads
+    w = {"w_qkv": _store(_normal(rng, ((nq + 2 * nkv) * d, shape.H), sigma), "bf16"),
+         "w_o": _store(_normal(rng, (shape.H, nq * d), sigma), "bf16")}
+    w["q_norm"] = (1.0 + 0.1 * rng.standard_normal(d)).astype(np.float32)
+    w["k_norm"] = (1.0 + 0.1 * rng.standard_normal(d)).astype(np.float32)
+    return w
+
+
+def kv_cache(T: int, shape: AttnShape, max_len: int, seed: int, v_sigma: float = 0.64) -> Dict[str, np.ndarray]:
+    """Random caches [T, nkv, max_len, d] (bf16 bits): keys N(0, 1), values N(0, v_sigma)."""
+    rng = np.random.default_rng(seed + 30000)
+    shp = (T, shape.n_kv_heads, max_len, shape.head_dim)
+    return {"k": _store(_normal(rng, shp, 1.0), "bf16"), "v": _store(_normal(rng, shp, v_sigma), "bf16")}
+
+
+def cache_lengths(T: int, max_len: int, seed: int, fixed: Optional[int] = None) -> np.ndarray:
+    """Cached positions per stream (int32, < max_len): all equal to `fixed`, or uniform over [0, max_len)."""
+    if fixed is not None:
+        return np.full(T, fixed, dtype=np.int32)
+    return np.random.default_rng(seed + 40000).integers(0, max_len, T).astype(np.int32)
+
+
+def speech_positions(lengths: np.ndarray) -> np.ndarray:
+    """(T, H, W) indices [T, 3] int32 of each stream's new token: speech gives all three axes its
+    sequence index."""
+    p = np.asarray(lengths, np.int32)
+    return np.stack([p, p, p], axis=1).astype(np.int32)
 
 
 def workload_inputs(name: str, T: Optional[int] = None) -> dict:
