@@ -224,6 +224,58 @@ int moe_codec_head_argmax(const moe_config* cfg, const void* x, const void* w_he
 size_t moe_codec_head_workspace_size(const moe_config* cfg, int32_t V, int64_t T);
 
 /*
+ * Decode-time attention of the Talker ("3C · Talker MoE (20 lớp, 128 Experts
+ * Top-6) & Đầu ra mã ngữ nghĩa c_0" §1: grouped-query attention, 16 query heads
+ * over 2 key/value heads of 128; "1B · Interleaved TM-RoPE 3D (24, 20, 20)" §3:
+ * the rotation of adjacent pairs, T/H/W interleaved, rope_theta 1e6;
+ * "用 print(model) 认识 Qwen3-TTS": bias-free q/k/v/o projections and an RMSNorm
+ * over each query and key head).
+ */
+typedef struct {
+    int32_t hidden_size;       /* 1024 */
+    int32_t num_heads;         /* 16 query heads */
+    int32_t num_kv_heads;      /* 2; num_heads / num_kv_heads in {1, 2, 4, 8} */
+    int32_t head_dim;          /* 128 (the only width supported) */
+    int32_t rope_sections[3];  /* pairs on the T, H, W axes, sum head_dim / 2: {24, 20, 20} */
+    float rope_theta;          /* 1e6; pair k turns by index * rope_theta^(-2k / head_dim) */
+    float eps;                 /* q_norm / k_norm epsilon, 1e-6 */
+    int32_t max_len;           /* cache capacity per stream (positions) */
+    int32_t dtype;             /* MOE_BF16 */
+} moe_attn_config;
+
+typedef struct {
+    const void* w_qkv;   /* [(num_heads + 2 num_kv_heads) head_dim, hidden]: query, key, value rows */
+    const float* q_norm; /* [head_dim] gain */
+    const float* k_norm; /* [head_dim] gain */
+    const void* w_o;     /* [hidden, num_heads head_dim] */
+} moe_attn_weights;
+
+/*
+ * moe_attention_decode — one decode step for T streams, each with its own cache.
+ *   x          [dev] [T, hidden] the normalised layer input of each stream's new token
+ *   pos        [dev] [T, 3] int32: its (T, H, W) indices (speech: three equal values)
+ *   cache_len  [dev] [T] int32: positions already cached for stream t; the new key
+ *              and value go to position cache_len[t] and the query attends to
+ *              positions 0 .. cache_len[t].  The library does not advance it.  A
+ *              value outside [0, max_len) writes no cache row and gives that
+ *              stream a zero attention output.
+ *   k_cache, v_cache [dev] [T, num_kv_heads, max_len, head_dim] bf16, in/out
+ *              (keys stored after q/k norm and rotation)
+ *   y          [dev] [T, hidden] out: o_proj(attention) (+ residual, nullable);
+ *              may alias residual or x
+ *   norm_out   [dev] [T, hidden] out or NULL: RMSNorm(y) with norm_gain (nullable,
+ *              1.0) and norm_eps, the next sub-layer's input, from the same pass
+ * Workspace: moe_attention_workspace_size(cfg, T).  T <= 65535.
+ */
+int moe_attention_decode(const moe_attn_config* cfg, const moe_attn_weights* w, const void* x, int64_t T,
+                         const int32_t* pos, const int32_t* cache_len, void* k_cache, void* v_cache,
+                         const void* residual, void* y, const float* norm_gain, float norm_eps,
+                         void* norm_out, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes for moe_attention_decode at T (0 for an invalid config). Host only. */
+size_t moe_attention_workspace_size(const moe_attn_config* cfg, int64_t T);
+
+/*
  * moe_codec_head_sample — c_0 drawn from the softmax of the codec head's logits
  * ("用 print(model) 认识 Qwen3-TTS", "Codec Head：语义码预测": the 3072 logits go
  * through a softmax and the next semantic code is sampled).  Inverse transform

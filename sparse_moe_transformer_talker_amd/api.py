@@ -26,7 +26,8 @@ EXPORTS = ("moe_status_string", "moe_check_config", "moe_workspace_size", "moe_r
            "moe_grouped_swiglu", "moe_shared_swiglu", "moe_combine", "moe_layer_forward",
            "moe_layer_forward_timed", "moe_rmsnorm",
            "moe_codec_head_argmax", "moe_codec_head_workspace_size", "moe_stack_forward",
-           "moe_stack_workspace_size", "moe_codec_head_sample")
+           "moe_stack_workspace_size", "moe_codec_head_sample", "moe_attention_decode",
+           "moe_attention_workspace_size")
 
 
 class MoeError(RuntimeError):
@@ -40,6 +41,35 @@ class moe_config(ctypes.Structure):
                 ("num_experts_per_tok", ctypes.c_int32), ("moe_intermediate_size", ctypes.c_int32),
                 ("shared_expert_intermediate_size", ctypes.c_int32), ("norm_topk_prob", ctypes.c_int32),
                 ("dtype", ctypes.c_int32)]
+
+
+class moe_attn_config(ctypes.Structure):
+    _fields_ = [("hidden_size", ctypes.c_int32), ("num_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("rope_sections", ctypes.c_int32 * 3), ("rope_theta", ctypes.c_float),
+                ("eps", ctypes.c_float), ("max_len", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class moe_attn_weights(ctypes.Structure):
+    _fields_ = [("w_qkv", ctypes.c_void_p), ("q_norm", ctypes.c_void_p), ("k_norm", ctypes.c_void_p),
+                ("w_o", ctypes.c_void_p)]
+
+
+@dataclasses.dataclass
+class AttnConfig:
+    """The attention shape (defaults: the Talker's 16 query / 2 KV heads of 128, TM-RoPE 24/20/20)."""
+    max_len: int
+    hidden_size: int = 1024
+    num_heads: int = 16
+    num_kv_heads: int = 2
+    head_dim: int = 128
+    rope_sections: tuple = (24, 20, 20)
+    rope_theta: float = 1.0e6
+    eps: float = 1e-6
+
+    def c(self) -> moe_attn_config:
+        return moe_attn_config(self.hidden_size, self.num_heads, self.num_kv_heads, self.head_dim,
+                               (ctypes.c_int32 * 3)(*self.rope_sections), self.rope_theta, self.eps, self.max_len,
+                               MOE_BF16)
 
 
 class moe_weights(ctypes.Structure):
@@ -103,6 +133,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
                                              vp, i32, vp, vp, vp, vp, sz, vp]),
         "moe_stack_workspace_size": (sz, [cfgp, i64, i32]),
         "moe_codec_head_sample": (ctypes.c_int, [cfgp, vp, vp, i32, i64, ctypes.c_float, vp, vp, vp, vp, sz, vp]),
+        "moe_attention_decode": (ctypes.c_int, [ctypes.POINTER(moe_attn_config), ctypes.POINTER(moe_attn_weights),
+                                                vp, i64, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, sz, vp]),
+        "moe_attention_workspace_size": (sz, [ctypes.POINTER(moe_attn_config), i64]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -337,3 +370,29 @@ def moe_stack_forward(cfg: Config, layers, x: torch.Tensor, gains: Optional[torc
         ctypes.byref(cfg.c()), arr, L, _ptr(x), T, _ptr(gains), eps, _ptr(codec_head), V, _ptr(h_out),
         _ptr(xn_out), _ptr(c0), _ptr(buf), buf.numel(), st))
     return h_out, xn_out, c0
+
+
+def moe_attention_workspace_size(acfg: AttnConfig, T: int) -> int:
+    return int(load_library().moe_attention_workspace_size(ctypes.byref(acfg.c()), T))
+
+
+def attn_weights_struct(w: Dict[str, torch.Tensor]) -> moe_attn_weights:
+    return moe_attn_weights(_ptr(w["w_qkv"]), _ptr(w["q_norm"]), _ptr(w["k_norm"]), _ptr(w["w_o"]))
+
+
+def moe_attention_decode(acfg: AttnConfig, weights, x: torch.Tensor, pos: torch.Tensor, cache_len: torch.Tensor,
+                         k_cache: torch.Tensor, v_cache: torch.Tensor, residual: Optional[torch.Tensor] = None,
+                         y=None, norm_gain: Optional[torch.Tensor] = None, norm_eps: float = 1e-6, norm_out=None,
+                         ws=None, stream=None):
+    """One decode step of the attention block (caches updated in place).  Returns y [T, H]."""
+    T, dev = x.shape[0], x.device
+    y = y if y is not None else torch.empty_like(x)
+    w = weights if isinstance(weights, moe_attn_weights) else attn_weights_struct(weights)
+    lib = load_library()
+    c = acfg.c()
+    buf = ws if ws is not None else workspace(int(lib.moe_attention_workspace_size(ctypes.byref(c), T)), dev)
+    st = stream if stream is not None else _stream(dev)
+    _check("moe_attention_decode", lib.moe_attention_decode(
+        ctypes.byref(c), ctypes.byref(w), _ptr(x), T, _ptr(pos), _ptr(cache_len), _ptr(k_cache), _ptr(v_cache),
+        _ptr(residual), _ptr(y), _ptr(norm_gain), norm_eps, _ptr(norm_out), _ptr(buf), buf.numel(), st))
+    return y

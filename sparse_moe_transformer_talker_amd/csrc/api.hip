@@ -76,14 +76,15 @@ struct GemmPlan {
     int64_t max_items[2]{0, 0};
 };
 // Tile lists for the two passes when the matrix-core path applies.
-void plan_gemm(const moe_config* c, int64_t T, bool routed, bool shared, Carver& cv, GemmPlan& g) {
+void plan_gemm(const moe_config* c, int64_t T, bool routed, bool shared, Carver& cv, GemmPlan& g,
+               int64_t small_rows = 32) {
     const int H = c->hidden_size, E = c->num_experts, k = c->num_experts_per_tok;
     const int I = c->moe_intermediate_size, Is = shared ? c->shared_expert_intermediate_size : 0;
     g.mfma = gemm_mfma_ok(c->dtype, H, I, Is);
     if (!g.mfma) return;
     const int64_t pairs = routed ? T * k : 0;
     const int64_t rows_per_expert = routed ? pairs / E : T;
-    if (rows_per_expert < 32) g.variant = kGemmSmallM;
+    if (rows_per_expert < small_rows) g.variant = kGemmSmallM;
     else if (!gemm_lds_ok(H, I, Is)) g.variant = kGemmLargeM;
     else g.variant = rows_per_expert >= 160 ? kGemmHugeLds : kGemmLargeLds;
     int* counters = cv.take<int>(4);
@@ -248,6 +249,64 @@ GemmGroup no_group() {
     GemmGroup g{};
     g.N = 0;
     return g;
+}
+
+// A plain product C [T, N] = A [T, K] W^T (W [N, K]) is the shared-expert tile
+// list of the down pass alone: a layer shape whose hidden size is N and whose
+// shared expert is K wide.  Up to 256 rows take the 16-row tiles.
+moe_config dense_cfg(int dtype, int N, int K) {
+    moe_config c{};
+    c.hidden_size = N;
+    c.num_experts = 1;
+    c.num_experts_per_tok = 1;
+    c.moe_intermediate_size = 64;
+    c.shared_expert_intermediate_size = K;
+    c.norm_topk_prob = 1;
+    c.dtype = dtype;
+    return c;
+}
+void plan_dense(const moe_config* c, int64_t T, Carver& cv, GemmPlan& g) { plan_gemm(c, T, false, true, cv, g, 257); }
+int run_dense(const moe_config* c, GemmPlan& plan, const void* A, const void* W, void* C, int64_t T, hipStream_t s) {
+    const int N = c->hidden_size, K = c->shared_expert_intermediate_size;
+    if (plan.mfma) TMOE_TRY(launch_build_items(nullptr, 0, T, &plan.t[0], &plan.t[1], s));
+    const GemmGroup dn = group(W, nullptr, 0, N, K, A, K, nullptr, C, N, nullptr, 1, 0, nullptr);
+    return run_gemm_pass(c, plan, 1, no_group(), dn, nullptr, 0, T, s);
+}
+
+// --- decode-time attention ---
+struct AttnPlan {
+    moe_config cq, co;  // the two projections as plain products
+    GemmPlan gq, go;
+    void *qkv, *q, *o, *ao;
+    float *pm, *pl, *pacc;
+};
+void plan_attn(const moe_attn_config* a, int64_t T, Carver& cv, AttnPlan& p) {
+    const int H = a->hidden_size, nq = a->num_heads, nkv = a->num_kv_heads, d = a->head_dim;
+    const int64_t parts = T * nkv * (int64_t)attn_chunks(a->max_len) * (nq / nkv);
+    p.cq = dense_cfg(a->dtype, (nq + 2 * nkv) * d, H);
+    p.co = dense_cfg(a->dtype, H, nq * d);
+    plan_dense(&p.cq, T, cv, p.gq);
+    plan_dense(&p.co, T, cv, p.go);
+    p.qkv = cv.take<char>(T * (int64_t)(nq + 2 * nkv) * d * 2);
+    p.q = cv.take<char>(T * (int64_t)nq * d * 2);
+    p.o = cv.take<char>(T * (int64_t)nq * d * 2);
+    p.ao = cv.take<char>(T * (int64_t)H * 2);
+    p.pm = cv.take<float>(parts);
+    p.pl = cv.take<float>(parts);
+    p.pacc = cv.take<float>(parts * d);
+}
+int check_attn_cfg(const moe_attn_config* a) {
+    if (!a) return MOE_ERR_INVALID;
+    if (a->hidden_size < 1 || a->num_heads < 1 || a->num_kv_heads < 1 || a->head_dim < 2 || a->head_dim % 2 ||
+        a->max_len < 1 || !(a->eps >= 0.0f) || !(a->rope_theta > 1.0f) || !(a->rope_theta < INFINITY))
+        return MOE_ERR_INVALID;
+    const int* sec = a->rope_sections;
+    if (sec[0] < 0 || sec[1] < 0 || sec[2] < 0 || sec[0] + sec[1] + sec[2] != a->head_dim / 2) return MOE_ERR_INVALID;
+    if (a->num_heads % a->num_kv_heads) return MOE_ERR_INVALID;
+    if (a->dtype != MOE_BF16 || !attn_decode_ok(a->head_dim, a->num_heads, a->num_kv_heads) ||
+        a->hidden_size % 128 || a->hidden_size > 16384 || a->max_len > (1 << 24))
+        return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
 }
 
 // Optional end of a stacked layer: the next pre-norm of y, fused into the combine.
@@ -632,6 +691,50 @@ int moe_codec_head_argmax(const moe_config* cfg, const void* x, const void* w_he
     hipStream_t s = as_stream(stream);
     TMOE_TRY(launch_scores(cfg->dtype, x, w_head, nullptr, T, cfg->hidden_size, V, sc, bd, s));
     return hip_status(launch_argmax(cfg->dtype, sc, bd, x, w_head, T, cfg->hidden_size, V, c0, s));
+}
+
+size_t moe_attention_workspace_size(const moe_attn_config* cfg, int64_t T) {
+    if (check_attn_cfg(cfg) != MOE_OK || T < 0 || T > 65535) return 0;
+    Carver cv(nullptr);
+    AttnPlan p;
+    plan_attn(cfg, T, cv, p);
+    return cv.size();
+}
+
+int moe_attention_decode(const moe_attn_config* cfg, const moe_attn_weights* w, const void* x, int64_t T,
+                         const int32_t* pos, const int32_t* cache_len, void* k_cache, void* v_cache,
+                         const void* residual, void* y, const float* norm_gain, float norm_eps, void* norm_out,
+                         void* ws, size_t ws_bytes, void* stream) {
+    int st = check_attn_cfg(cfg);
+    if (st != MOE_OK) return st;
+    if (T < 0) return MOE_ERR_INVALID;
+    if (T > 65535) return MOE_ERR_UNSUPPORTED;
+    if (T == 0) return MOE_OK;
+    if (!w || !ok_ptr(w->w_qkv) || !ok_ptr(w->q_norm) || !ok_ptr(w->k_norm) || !ok_ptr(w->w_o) || !ok_ptr(x) ||
+        !ok_ptr(pos) || !ok_ptr(cache_len) || !ok_ptr(k_cache) || !ok_ptr(v_cache) || !ok_opt(residual) ||
+        !ok_ptr(y) || !ok_opt(norm_gain) || !ok_opt(norm_out) || !ok_ptr(ws))
+        return MOE_ERR_INVALID;
+    if (norm_out && (!(norm_eps >= 0.0f) || norm_out == y)) return MOE_ERR_INVALID;
+    if (ws_bytes < moe_attention_workspace_size(cfg, T)) return MOE_ERR_WORKSPACE;
+    const int H = cfg->hidden_size, nq = cfg->num_heads, nkv = cfg->num_kv_heads;
+    Carver cv(ws);
+    AttnPlan p;
+    plan_attn(cfg, T, cv, p);
+    hipStream_t s = as_stream(stream);
+    int r = run_dense(&p.cq, p.gq, x, w->w_qkv, p.qkv, T, s);
+    if (r != MOE_OK) return r;
+    TMOE_TRY(launch_qk_rope_append(p.qkv, T, nq, nkv, w->q_norm, w->k_norm, cfg->eps, pos, cache_len, cfg->max_len,
+                                   cfg->rope_sections[1], cfg->rope_sections[2], (double)cfg->rope_theta, p.q,
+                                   k_cache, v_cache, s));
+    TMOE_TRY(launch_attn_decode(p.q, k_cache, v_cache, cache_len, T, nq, nkv, cfg->max_len, p.pm, p.pl, p.pacc,
+                                p.o, s));
+    if (!residual && !norm_out) return run_dense(&p.co, p.go, p.o, w->w_o, y, T, s);
+    r = run_dense(&p.co, p.go, p.o, w->w_o, p.ao, T, s);
+    if (r != MOE_OK) return r;
+    if (norm_out)
+        return hip_status(launch_combine_norm(cfg->dtype, nullptr, 0, 0, p.ao, H, residual, y, T, H, norm_gain,
+                                              norm_eps, norm_out, s));
+    return hip_status(launch_combine(cfg->dtype, nullptr, nullptr, nullptr, 0, 0, p.ao, H, residual, y, T, H, s));
 }
 
 int moe_codec_head_sample(const moe_config* cfg, const void* x, const void* w_head, int32_t V, int64_t T,

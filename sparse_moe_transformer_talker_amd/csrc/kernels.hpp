@@ -160,4 +160,19 @@ hipError_t launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t st);
 hipError_t launch_gather_rows(int dtype, const void* x, const int32_t* rows, int64_t n, int H, void* out,
                               hipStream_t st);
 
+// --- decode-time attention (attention.hip) ---
+// head_dim 128 and nq / nkv in {1, 2, 4, 8}
+bool attn_decode_ok(int head_dim, int nq, int nkv);
+int attn_chunks(int max_len);  // partials per (stream, KV head): 128 positions each
+// qkv [T, (nq + 2 nkv) 128] -> q_out [T, nq, 128] (normalised, rotated) and the
+// new key / value rows at position len[t] of kc / vc [T, nkv, max_len, 128]
+hipError_t launch_qk_rope_append(const void* qkv, int64_t T, int nq, int nkv, const float* q_gain,
+                                 const float* k_gain, float eps, const int32_t* pos, const int32_t* len,
+                                 int max_len, int sec_h, int sec_w, double theta, void* q_out, void* kc, void* vc,
+                                 hipStream_t st);
+// o [T, nq, 128] = attention of q over positions 0..len[t] of each stream's
+// cache; pm / pl [T nkv chunks (nq / nkv)], pacc [.. x 128] fp32 scratch
+hipError_t launch_attn_decode(const void* q, const void* kc, const void* vc, const int32_t* len, int64_t T, int nq,
+                              int nkv, int max_len, float* pm, float* pl, float* pacc, void* o, hipStream_t st);
+
 }  // namespace tmoe

@@ -190,3 +190,33 @@ def test_codec_head_sample_argument_errors():
     assert call(V=8193) == -2          # the exact pass keeps one token's logits in LDS
     assert call(ws=need - 256) == -3
     assert call(T=0) == 0
+
+
+def test_attention_config_and_argument_errors():
+    lib = api.load_library()
+    good = api.AttnConfig(max_len=1024)
+    c = good.c()
+    n = lib.moe_attention_workspace_size(ctypes.byref(c), 64)
+    assert n > 64 * 1024 * 2 * 3
+    bad = [dict(num_kv_heads=3), dict(rope_sections=(24, 20, 21)), dict(rope_theta=0.5), dict(max_len=0),
+           dict(eps=-1.0)]
+    for kw in bad:
+        assert lib.moe_attention_workspace_size(ctypes.byref(api.AttnConfig(**dict(dict(max_len=1024), **kw)).c()),
+                                                64) == 0, kw
+    w = api.moe_attn_weights(FAKE, FAKE, FAKE, FAKE)
+
+    def call(cfg=c, **kw):
+        return lib.moe_attention_decode(ctypes.byref(cfg), kw.get("w", ctypes.byref(w)), kw.get("x", _p()),
+                                        kw.get("T", 64), _p(1 << 20), _p(1 << 21), _p(1 << 24), _p(1 << 26), None,
+                                        kw.get("y", _p(1 << 28)), None, ctypes.c_float(1e-6), kw.get("no", None),
+                                        _p(1 << 30), kw.get("ws", n), None)
+
+    assert call(w=None) == -1
+    assert call(x=None) == -1
+    assert call(ws=n - 256) == -3
+    assert call(T=0) == 0
+    assert call(T=70000) == -2
+    assert call(no=_p(1 << 28)) == -1            # norm_out may not alias y
+    for kw, want in ((dict(head_dim=64, rope_sections=(12, 10, 10)), -2), (dict(num_heads=48, num_kv_heads=2), -2),
+                     (dict(num_heads=16, num_kv_heads=3), -1)):
+        assert call(cfg=api.AttnConfig(**dict(dict(max_len=1024), **kw)).c()) == want, kw
