@@ -246,6 +246,59 @@ def measure_stack(api, torch, INP, shape, T, weight_sets, L, frames, vocab=3072)
                       "codec_head argmax"}
 
 
+def measure_attention(api, torch, INP, T, L, steps, R=4):
+    """One decode step of the attention block for T streams with L cached positions
+    each (the new token makes L + 1), R layers' weights and caches rotated in one
+    graph so that reads come from HBM."""
+    shape = INP.TALKER_ATTN
+    dev = torch.device("cuda", 0)
+    to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    acfg = api.AttnConfig(max_len=L + 1)
+    layers = []
+    for r in range(R):
+        w = INP.attention_weights(shape, 60 + r)
+        wd = {"w_qkv": to_dev(w["w_qkv"]), "w_o": to_dev(w["w_o"]),
+              "q_norm": torch.from_numpy(w["q_norm"]).to(dev), "k_norm": torch.from_numpy(w["k_norm"]).to(dev)}
+        kv = INP.kv_cache(T, shape, L + 1, 61 + r)
+        layers.append((api.attn_weights_struct(wd), wd, to_dev(kv["k"]),
+                       to_dev(np.ascontiguousarray(np.swapaxes(kv["v"], 2, 3)))))
+    lens = torch.full((T,), L, dtype=torch.int32, device=dev)
+    pos = torch.from_numpy(INP.speech_positions(np.full(T, L, np.int32))).to(dev)
+    x = to_dev(INP.activations(T, shape.H, 62, "bf16"))
+    res = to_dev(INP.activations(T, shape.H, 63, "bf16"))
+    y = torch.empty_like(x)
+    ws = api.workspace(api.moe_attention_workspace_size(acfg, T), dev)
+    run = lambda i: api.moe_attention_decode(acfg, layers[i][0], x, pos, lens, layers[i][2], layers[i][3],
+                                             residual=res, y=y, ws=ws)
+    for i in range(R):
+        run(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(R):
+            run(i)
+    g.replay()
+    torch.cuda.synchronize()
+    reps = max(1, steps // R)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(reps):
+        g.replay()
+    stop.record()
+    torch.cuda.synchronize()
+    us = start.elapsed_time(stop) * 1e3 / (reps * R)
+    d, nq, nkv, H = shape.head_dim, shape.n_heads, shape.n_kv_heads, shape.H
+    kv_bytes = T * nkv * (L + 1) * d * 2 * 2
+    w_bytes = ((nq + 2 * nkv) * d * H + H * nq * d) * 2
+    act_bytes = T * H * 2 * 3 + T * (nq + 2 * nkv) * d * 2 * 2 + T * nq * d * 2 * 2
+    total = kv_bytes + w_bytes + act_bytes
+    return {"workload": "talker_attention_decode_T%d_ctx%d" % (T, L + 1), "streams": T, "positions": L + 1,
+            "layers_rotated": R, "us_per_step": us, "tokens_per_s": T / (us * 1e-6),
+            "bytes_per_step": total, "kv_bytes": kv_bytes, "weight_bytes": w_bytes,
+            "hbm_frac": total / (us * 1e-6) / (HBM_PEAK_GBS * 1e9),
+            "timing": "HIP graph of %d layers' attention steps back to back" % R}
+
+
 def cpu_baseline(INP, shape, T, seconds):
     from oracle import moe_ref as R
     try:
@@ -281,6 +334,7 @@ def main():
     ap.add_argument("--no-stack", action="store_true")
     ap.add_argument("--stack-layers", type=int, default=20)
     ap.add_argument("--stack-frames", type=int, default=20)
+    ap.add_argument("--no-attention", action="store_true")
     ap.add_argument("--no-reports", action="store_true",
                     help="skip the report-only workloads (Zipf-skewed T=8192 layer, 20-layer stack at T=1024)")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
@@ -325,6 +379,11 @@ def main():
         log("stack: %d layers + codec head, T=64" % args.stack_layers)
         stack = measure_stack(api, torch, INP, shape, 64, sets, args.stack_layers, args.stack_frames)
         log("stack: %.1f us/frame, %.2f us/layer" % (stack["frame_us"], stack["per_layer_us"]))
+    attn = None
+    if not args.no_attention and not args.no_decode:
+        log("attention decode: 64 streams x 1024 cached positions")
+        attn = measure_attention(api, torch, INP, 64, 1023, args.steps)
+        log("attention: %.2f us/step, %.1f%% of HBM peak" % (attn["us_per_step"], 100 * attn["hbm_frac"]))
     reports = None
     if not args.no_reports and not args.no_decode and not args.no_prefill:
         c = INP.WORKLOADS["skew_t8192"]
@@ -397,6 +456,8 @@ def main():
         line["stack"] = stack
     if reports is not None:
         line["reports"] = reports
+    if attn is not None:
+        line["attention"] = attn
     if pre is not None:
         gp = pre["gate_up"]
         line["prefill"] = {"workload": "talker_moe_layer_prefill_T4096", "tokens_per_s": pre["tokens_per_s"],

@@ -239,7 +239,7 @@ typedef struct {
     int32_t rope_sections[3];  /* pairs on the T, H, W axes, sum head_dim / 2: {24, 20, 20} */
     float rope_theta;          /* 1e6; pair k turns by index * rope_theta^(-2k / head_dim) */
     float eps;                 /* q_norm / k_norm epsilon, 1e-6 */
-    int32_t max_len;           /* cache capacity per stream (positions) */
+    int32_t max_len;           /* cache capacity per stream (positions), a multiple of 32 */
     int32_t dtype;             /* MOE_BF16 */
 } moe_attn_config;
 
@@ -259,8 +259,10 @@ typedef struct {
  *              positions 0 .. cache_len[t].  The library does not advance it.  A
  *              value outside [0, max_len) writes no cache row and gives that
  *              stream a zero attention output.
- *   k_cache, v_cache [dev] [T, num_kv_heads, max_len, head_dim] bf16, in/out
- *              (keys stored after q/k norm and rotation)
+ *   k_cache    [dev] [T, num_kv_heads, max_len, head_dim] bf16, in/out: keys after
+ *              q/k norm and rotation, one row per position
+ *   v_cache    [dev] [T, num_kv_heads, head_dim, max_len] bf16, in/out: values,
+ *              transposed (one row per dimension, positions contiguous)
  *   y          [dev] [T, hidden] out: o_proj(attention) (+ residual, nullable);
  *              may alias residual or x
  *   norm_out   [dev] [T, hidden] out or NULL: RMSNorm(y) with norm_gain (nullable,

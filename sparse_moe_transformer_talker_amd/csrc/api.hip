@@ -277,20 +277,31 @@ int run_dense(const moe_config* c, GemmPlan& plan, const void* A, const void* W,
 struct AttnPlan {
     moe_config cq, co;  // the two projections as plain products
     GemmPlan gq, go;
-    void *qkv, *q, *o, *ao;
+    int ksq = 0, kso = 0;  // split-K runs of the skinny products (0: the grouped GEMM path)
+    float *pq = nullptr, *po = nullptr;
+    void *qkv = nullptr, *q, *o, *ao = nullptr;
     float *pm, *pl, *pacc;
 };
 void plan_attn(const moe_attn_config* a, int64_t T, Carver& cv, AttnPlan& p) {
     const int H = a->hidden_size, nq = a->num_heads, nkv = a->num_kv_heads, d = a->head_dim;
+    const int nqkv = (nq + 2 * nkv) * d;
     const int64_t parts = T * nkv * (int64_t)attn_chunks(a->max_len) * (nq / nkv);
-    p.cq = dense_cfg(a->dtype, (nq + 2 * nkv) * d, H);
+    p.cq = dense_cfg(a->dtype, nqkv, H);
     p.co = dense_cfg(a->dtype, H, nq * d);
-    plan_dense(&p.cq, T, cv, p.gq);
-    plan_dense(&p.co, T, cv, p.go);
-    p.qkv = cv.take<char>(T * (int64_t)(nq + 2 * nkv) * d * 2);
+    p.ksq = skinny_gemm_runs(T, nqkv, H);
+    p.kso = skinny_gemm_runs(T, H, nq * d);
+    if (p.ksq && p.kso) {
+        p.pq = cv.take<float>(p.ksq * T * (int64_t)nqkv);
+        p.po = cv.take<float>(p.kso * T * (int64_t)H);
+    } else {
+        p.ksq = p.kso = 0;
+        plan_dense(&p.cq, T, cv, p.gq);
+        plan_dense(&p.co, T, cv, p.go);
+        p.qkv = cv.take<char>(T * (int64_t)nqkv * 2);
+        p.ao = cv.take<char>(T * (int64_t)H * 2);
+    }
     p.q = cv.take<char>(T * (int64_t)nq * d * 2);
     p.o = cv.take<char>(T * (int64_t)nq * d * 2);
-    p.ao = cv.take<char>(T * (int64_t)H * 2);
     p.pm = cv.take<float>(parts);
     p.pl = cv.take<float>(parts);
     p.pacc = cv.take<float>(parts * d);
@@ -303,7 +314,7 @@ int check_attn_cfg(const moe_attn_config* a) {
     const int* sec = a->rope_sections;
     if (sec[0] < 0 || sec[1] < 0 || sec[2] < 0 || sec[0] + sec[1] + sec[2] != a->head_dim / 2) return MOE_ERR_INVALID;
     if (a->num_heads % a->num_kv_heads) return MOE_ERR_INVALID;
-    if (a->dtype != MOE_BF16 || !attn_decode_ok(a->head_dim, a->num_heads, a->num_kv_heads) ||
+    if (a->dtype != MOE_BF16 || !attn_decode_ok(a->head_dim, a->num_heads, a->num_kv_heads, a->max_len) ||
         a->hidden_size % 128 || a->hidden_size > 16384 || a->max_len > (1 << 24))
         return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
@@ -721,15 +732,25 @@ int moe_attention_decode(const moe_attn_config* cfg, const moe_attn_weights* w, 
     AttnPlan p;
     plan_attn(cfg, T, cv, p);
     hipStream_t s = as_stream(stream);
-    int r = run_dense(&p.cq, p.gq, x, w->w_qkv, p.qkv, T, s);
-    if (r != MOE_OK) return r;
-    TMOE_TRY(launch_qk_rope_append(p.qkv, T, nq, nkv, w->q_norm, w->k_norm, cfg->eps, pos, cache_len, cfg->max_len,
+    const int d = cfg->head_dim, nqkv = (nq + 2 * nkv) * d;
+    if (p.ksq) {
+        TMOE_TRY(launch_skinny_gemm(x, w->w_qkv, p.pq, T, nqkv, H, p.ksq, s));
+    } else {
+        const int r = run_dense(&p.cq, p.gq, x, w->w_qkv, p.qkv, T, s);
+        if (r != MOE_OK) return r;
+    }
+    TMOE_TRY(launch_qk_rope_append(p.ksq ? p.pq : reinterpret_cast<const float*>(p.qkv), p.ksq, T, nq, nkv,
+                                   w->q_norm, w->k_norm, cfg->eps, pos, cache_len, cfg->max_len,
                                    cfg->rope_sections[1], cfg->rope_sections[2], (double)cfg->rope_theta, p.q,
                                    k_cache, v_cache, s));
     TMOE_TRY(launch_attn_decode(p.q, k_cache, v_cache, cache_len, T, nq, nkv, cfg->max_len, p.pm, p.pl, p.pacc,
                                 p.o, s));
+    if (p.kso) {
+        TMOE_TRY(launch_skinny_gemm(p.o, w->w_o, p.po, T, H, nq * d, p.kso, s));
+        return hip_status(launch_attn_out(p.po, p.kso, residual, y, T, H, norm_gain, norm_eps, norm_out, s));
+    }
     if (!residual && !norm_out) return run_dense(&p.co, p.go, p.o, w->w_o, y, T, s);
-    r = run_dense(&p.co, p.go, p.o, w->w_o, p.ao, T, s);
+    const int r = run_dense(&p.co, p.go, p.o, w->w_o, p.ao, T, s);
     if (r != MOE_OK) return r;
     if (norm_out)
         return hip_status(launch_combine_norm(cfg->dtype, nullptr, 0, 0, p.ao, H, residual, y, T, H, norm_gain,

@@ -8,8 +8,8 @@
 //     rope_theta 1e6.
 //   "用 print(model) 认识 Qwen3-TTS", the attention module print: q_norm / k_norm,
 //     an RMSNorm over each 128-wide head.
-// The projections run on the grouped GEMM kernels (a plain product is the
-// shared-expert tile list of the down pass); these kernels do the rest.
+// The projections run on the split-K skinny product kernel (or, above 64
+// tokens, the grouped GEMM's shared tile list); these kernels do the rest.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -20,43 +20,56 @@ constexpr int kHead = 128;                       // head width (64 pairs, one pe
 constexpr int kChunk = 128;                      // cached positions per partial
 constexpr int kAttnWaves = 4;
 constexpr int kKeysPerWave = kChunk / kAttnWaves;
-constexpr int kSteps = kKeysPerWave / 4;         // a wave reads 4 positions per load (16 lanes each)
 
-__device__ __forceinline__ void unpack8(const u32x4 v, float* f) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        f[2 * q] = __uint_as_float(v[q] << 16);
-        f[2 * q + 1] = __uint_as_float(v[q] & 0xFFFF0000u);
-    }
-}
-
-// One wave per (token, head of the fused q / k / v row); lane l owns pair l.
-// Query and key heads: RMSNorm over the head (fp32), times the gain, then the
-// rotation of pair l by pos[axis(l)] * theta^(-2 l / 128) (angle and its sine
-// and cosine in fp64).  Queries go to q_out [T, nq, 128]; keys and values to
-// position len[t] of the stream's cache [T, nkv, max_len, 128] (values
-// unchanged).  A stream whose len is outside [0, max_len) writes no cache row.
-__global__ __launch_bounds__(64) void qk_rope_append_kernel(const bf16_t* __restrict__ qkv, int nq, int nkv,
-                                                            const float* __restrict__ q_gain,
-                                                            const float* __restrict__ k_gain, float eps,
-                                                            const int32_t* __restrict__ pos,
-                                                            const int32_t* __restrict__ len, int max_len,
-                                                            int sec_h, int sec_w, double log_theta,
-                                                            bf16_t* __restrict__ q_out, bf16_t* __restrict__ kc,
-                                                            bf16_t* __restrict__ vc) {
+// One wave per (token, head of the fused q / k / v row), four heads per
+// workgroup; lane l owns pair l.  The row comes as KS fp32 partial products
+// (summed in order) or, with KS == 0, as bf16.  Query and key heads: RMSNorm
+// over the head (fp32), times the gain, then the rotation of pair l by
+// pos[axis(l)] * theta^(-2 l / 128) (the angle in fp64, reduced to [-pi, pi]
+// before its sine and cosine).  Queries go to q_out [T, nq, 128]; keys to
+// position len[t] of the key cache [T, nkv, max_len, 128], values (unchanged,
+// rounded to bf16) to column len[t] of the transposed value cache
+// [T, nkv, 128, max_len].  A stream whose len is outside [0, max_len) writes no
+// cache entry.
+constexpr int kRopeWaves = 4;
+__global__ __launch_bounds__(64 * kRopeWaves) void qk_rope_append_kernel(
+    const void* __restrict__ qkv, int KS, int64_t T, int nq, int nkv, const float* __restrict__ q_gain,
+    const float* __restrict__ k_gain, float eps, const int32_t* __restrict__ pos, const int32_t* __restrict__ len,
+    int max_len, int sec_h, int sec_w, double log_theta, bf16_t* __restrict__ q_out, bf16_t* __restrict__ kc,
+    bf16_t* __restrict__ vc) {
     const int64_t t = blockIdx.x;
-    const int y = blockIdx.y;
-    const int l = threadIdx.x;
+    const int y = blockIdx.y * kRopeWaves + (int)(threadIdx.x >> 6);
+    const int l = lane_id();
+    if (y >= nq + 2 * nkv) return;  // wave-uniform
     const int64_t ld = (int64_t)(nq + 2 * nkv) * kHead;
-    const uint32_t raw = *reinterpret_cast<const uint32_t*>(qkv + t * ld + (int64_t)y * kHead + 2 * l);
+    const int64_t e = t * ld + (int64_t)y * kHead + 2 * l;
+    float x0, x1;
+    if (KS > 0) {
+        const float* p = reinterpret_cast<const float*>(qkv);
+        x0 = 0.f;
+        x1 = 0.f;
+        for (int s = 0; s < KS; ++s) {
+            const f32x2_t v = *reinterpret_cast<const f32x2_t*>(p + s * T * ld + e);
+            x0 += v[0];
+            x1 += v[1];
+        }
+    } else {
+        const uint32_t raw = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const bf16_t*>(qkv) + e);
+        x0 = __uint_as_float(raw << 16);
+        x1 = __uint_as_float(raw & 0xFFFF0000u);
+    }
     const int n = len[t];
     const bool ok = n >= 0 && n < max_len;
-    if (y >= nq + nkv) {
+    if (y >= nq + nkv) {  // values: dims are rows of the transposed cache
         const int g = y - nq - nkv;
-        if (ok) *reinterpret_cast<uint32_t*>(vc + (((t * nkv + g) * (int64_t)max_len + n) * kHead + 2 * l)) = raw;
+        if (ok) {
+            const uint32_t packed = pack_bf16x2(x0, x1);
+            bf16_t* col = vc + ((t * nkv + g) * (int64_t)kHead + 2 * l) * max_len + n;
+            col[0] = (bf16_t)(packed & 0xFFFFu);
+            col[max_len] = (bf16_t)(packed >> 16);
+        }
         return;
     }
-    float x0 = __uint_as_float(raw << 16), x1 = __uint_as_float(raw & 0xFFFF0000u);
     const float ss = wave_sum_dpp(fmaf(x0, x0, x1 * x1));
     const float inv = 1.0f / sqrtf(ss * (1.0f / kHead) + eps);
     const float* gain = y < nq ? q_gain : k_gain;
@@ -64,9 +77,10 @@ __global__ __launch_bounds__(64) void qk_rope_append_kernel(const bf16_t* __rest
     x1 = x1 * inv * gain[2 * l + 1];
     const int axis = (l % 3 == 1 && l < 3 * sec_h) ? 1 : ((l % 3 == 2 && l < 3 * sec_w) ? 2 : 0);
     const double ang = (double)pos[t * 3 + axis] * exp(-2.0 * l / kHead * log_theta);
-    double sd, cd;
-    sincos(ang, &sd, &cd);
-    const float c = (float)cd, s = (float)sd;
+    const double two_pi = 6.283185307179586;
+    const float red = (float)(ang - two_pi * rint(ang / two_pi));
+    float s, c;
+    sincosf(red, &s, &c);
     const uint32_t packed = pack_bf16x2(x0 * c - x1 * s, x0 * s + x1 * c);
     if (y < nq) {
         *reinterpret_cast<uint32_t*>(q_out + (t * nq + y) * kHead + 2 * l) = packed;
@@ -76,27 +90,95 @@ __global__ __launch_bounds__(64) void qk_rope_append_kernel(const bf16_t* __rest
     }
 }
 
+// y = sum of KS fp32 partial rows (in order) + residual, stored bf16; with
+// norm_out, also RMSNorm of the stored y times the gain.  One workgroup per
+// row, 8 contiguous features per thread per pass.
+__global__ __launch_bounds__(128) void attn_out_kernel(const float* __restrict__ part, int KS, int64_t T, int H,
+                                                       const bf16_t* residual, bf16_t* y,
+                                                       const float* __restrict__ gain, float eps,
+                                                       bf16_t* __restrict__ norm_out) {
+    __shared__ float wsum[2];
+    const int64_t t = blockIdx.x;
+    float ss = 0.f;
+    for (int h = threadIdx.x * 8; h < H; h += 128 * 8) {
+        float v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = 0.f;
+        for (int s = 0; s < KS; ++s) {
+            const float* p = part + (s * T + t) * (int64_t)H + h;
+            const f32x4 a = *reinterpret_cast<const f32x4*>(p), b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                v[i] += a[i];
+                v[4 + i] += b[i];
+            }
+        }
+        if (residual) {
+            const u32x4 r = *reinterpret_cast<const u32x4*>(residual + t * H + h);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                v[2 * q] += __uint_as_float(r[q] << 16);
+                v[2 * q + 1] += __uint_as_float(r[q] & 0xFFFF0000u);
+            }
+        }
+        u32x4 o;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            o[q] = pack_bf16x2(v[2 * q], v[2 * q + 1]);
+            const float a = __uint_as_float(o[q] << 16), b = __uint_as_float(o[q] & 0xFFFF0000u);
+            ss = fmaf(a, a, ss);
+            ss = fmaf(b, b, ss);
+        }
+        *reinterpret_cast<u32x4*>(y + t * H + h) = o;
+    }
+    if (!norm_out) return;  // block-uniform
+    ss = wave_sum_dpp(ss);
+    if (lane_id() == 0) wsum[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    const float inv = 1.0f / sqrtf((wsum[0] + wsum[1]) / (float)H + eps);
+    for (int h = threadIdx.x * 8; h < H; h += 128 * 8) {
+        const u32x4 yv = *reinterpret_cast<const u32x4*>(y + t * H + h);
+        u32x4 o;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float g0 = gain ? gain[h + 2 * q] : 1.f, g1 = gain ? gain[h + 2 * q + 1] : 1.f;
+            o[q] = pack_bf16x2(__uint_as_float(yv[q] << 16) * inv * g0,
+                               __uint_as_float(yv[q] & 0xFFFF0000u) * inv * g1);
+        }
+        *reinterpret_cast<u32x4*>(norm_out + t * H + h) = o;
+    }
+}
+
 // Partial attention of the G query heads of KV head g over positions
 // [c * 128, c * 128 + 128) of stream t (the stream attends to len[t] + 1
-// positions, the new one included).  Wave w takes 32 positions, four per load
-// (16 lanes x 16 bytes per 256-byte row), all its key and value rows in flight
-// at once; an online softmax per head, then the lanes' and waves' partials
-// merge.  Writes the chunk's max m, sum l and unnormalised output per head; an
-// empty chunk writes m = -inf, l = 0 and no output.
+// positions, the new one included), on the matrix cores.  Wave w takes 32
+// positions with all its key and value fragments in flight at once:
+//   S = Q K^T: the G query heads (zero rows up to 16) against two 16-position
+//     tiles, four 32-wide K steps each (v_mfma_f32_16x16x32_bf16; the operand
+//     fragment of a lane is 8 consecutive dimensions of one row);
+//   per head the maximum and the sum of exp over the wave's positions (16-lane
+//   reductions), positions past the stream's end masked to -inf;
+//   P (bf16) turns from the product layout to the operand layout through 1 KB of
+//   LDS, and O = P V over eight 16-dimension tiles reads the transposed value
+//   cache (8 consecutive positions of one dimension per lane; positions past
+//   the end are zeroed, so stale cache contents never reach the sum).
+// The waves' (max, sum, output) merge in LDS.  Writes the chunk's max m, sum l
+// and unnormalised output per head; an empty chunk writes m = -inf, l = 0.
 template <int G>
 __global__ __launch_bounds__(64 * kAttnWaves) void attn_partial_kernel(const bf16_t* __restrict__ q,
                                                                        const bf16_t* __restrict__ kc,
-                                                                       const bf16_t* __restrict__ vc,
+                                                                       const bf16_t* __restrict__ vt,
                                                                        const int32_t* __restrict__ len, int nkv,
                                                                        int max_len, int nch, float* __restrict__ pm,
                                                                        float* __restrict__ pl,
                                                                        float* __restrict__ pacc) {
-    __shared__ float red_m[kAttnWaves][G], red_l[kAttnWaves][G];
+    __shared__ float red_m[kAttnWaves][16], red_l[kAttnWaves][16];
     __shared__ float red_acc[kAttnWaves][G][kHead];
+    __shared__ __attribute__((aligned(16))) bf16_t pbuf[kAttnWaves][16][40];  // rows padded to 80 bytes
     const int c = blockIdx.x, g = blockIdx.y;
     const int64_t t = blockIdx.z;
     const int wave = (int)(threadIdx.x >> 6), lane = lane_id();
-    const int sub = lane >> 4, part = lane & 15;
+    const int col = lane & 15, grp = lane >> 4;
     const int nraw = len[t];
     const int n = (nraw >= 0 && nraw < max_len) ? nraw + 1 : 0;
     const int64_t pidx = (t * nkv + g) * nch + c;
@@ -109,85 +191,107 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_partial_kernel(const bf1
         return;
     }
     const int nq = nkv * G;
-    u32x4 qv[G];
+    const int key0 = k0 + wave * kKeysPerWave;
+    const f32x4 zero = {0, 0, 0, 0};
+    float m_r[4], l_r[4];
+    f32x4 o[8];
 #pragma unroll
-    for (int j = 0; j < G; ++j)
-        qv[j] = *reinterpret_cast<const u32x4*>(q + ((t * nq + g * G + j) * kHead + part * 8));
-    const int64_t base = (t * nkv + g) * (int64_t)max_len * kHead + part * 8;
-    u32x4 kr[kSteps], vr[kSteps];
-#pragma unroll
-    for (int s = 0; s < kSteps; ++s) {  // branch-free: positions past the end repeat the last one, unused
-        const int p = min(k0 + wave * kKeysPerWave + 4 * s + sub, n - 1);
-        kr[s] = *reinterpret_cast<const u32x4*>(kc + base + (int64_t)p * kHead);
-        vr[s] = *reinterpret_cast<const u32x4*>(vc + base + (int64_t)p * kHead);
-    }
-    const float scale = 0.08838834764831845f;  // 1 / sqrt(128)
-    float m[G], l[G], acc[G][8];
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-        m[j] = -INFINITY;
-        l[j] = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[j][i] = 0.f;
+    for (int i = 0; i < 4; ++i) {
+        m_r[i] = -INFINITY;
+        l_r[i] = 0.f;
     }
 #pragma unroll
-    for (int s = 0; s < kSteps; ++s) {
-        const bool valid = k0 + wave * kKeysPerWave + 4 * s + sub < n;
-        float kf[8], vf[8];
-        unpack8(kr[s], kf);
-        unpack8(vr[s], vf);
-        float dot[G];
+    for (int dt = 0; dt < 8; ++dt) o[dt] = zero;
+    if (key0 < n) {  // wave-uniform
+        const u32x4 z4 = {0, 0, 0, 0};
+        u32x4 qa[4], kb[2][4], vb[8];
+        const bf16_t* qp = q + ((t * nq + g * G + min(col, G - 1)) * kHead + grp * 8);
 #pragma unroll
-        for (int j = 0; j < G; ++j) {
-            float qf[8];
-            unpack8(qv[j], qf);
-            float a = 0.f;
+        for (int s = 0; s < 4; ++s) qa[s] = col < G ? *reinterpret_cast<const u32x4*>(qp + s * 32) : z4;
+        const int64_t kvrow = (t * nkv + g) * (int64_t)max_len;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) a = fmaf(qf[i], kf[i], a);
-            dot[j] = a;
+        for (int nt = 0; nt < 2; ++nt) {  // positions past the end load the last one (masked below)
+            const int key = min(key0 + nt * 16 + col, n - 1);
+            const bf16_t* kp = kc + (kvrow + key) * kHead + grp * 8;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) kb[nt][s] = *reinterpret_cast<const u32x4*>(kp + s * 32);
+        }
+        // key0 + 32 <= max_len (max_len % 32 == 0), so the value rows stay in bounds
+        const bf16_t* vp = vt + ((t * nkv + g) * (int64_t)kHead + col) * max_len + key0 + grp * 8;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) vb[dt] = *reinterpret_cast<const u32x4*>(vp + (int64_t)dt * 16 * max_len);
+        f32x4 sacc[2] = {zero, zero};
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                sacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa[s]),
+                                                                   __builtin_bit_cast(bf16x8, kb[nt][s]), sacc[nt],
+                                                                   0, 0, 0);
+        // sacc[nt][i] = S[head 4 grp + i][position key0 + 16 nt + col]
+        const float scale = 0.08838834764831845f;  // 1 / sqrt(128)
+        float sv[2][4];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sv[nt][i] = key0 + nt * 16 + col < n ? sacc[nt][i] * scale : -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float mx = fmaxf(sv[0][i], sv[1][i]);
+#pragma unroll
+            for (int off = 1; off < 16; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+            m_r[i] = mx;
+        }
+        float pv[2][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) pv[nt][i] = __expf(sv[nt][i] - m_r[i]);
+            float sm = pv[0][i] + pv[1][i];
+#pragma unroll
+            for (int off = 1; off < 16; off <<= 1) sm += __shfl_xor(sm, off);
+            l_r[i] = sm;
+        }
+        // P to the operand layout: row = head, 8 consecutive positions per lane
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pbuf[wave][4 * grp + i][nt * 16 + col] = f32_to_bf16(pv[nt][i]);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const u32x4 pa = *reinterpret_cast<const u32x4*>(&pbuf[wave][col][grp * 8]);
+        // zero the value entries of positions past the end
+        const int valid = n - (key0 + grp * 8);  // positions of this lane's 8 that are in range
+        if (valid < 8) {
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    uint32_t w2 = vb[dt][e];
+                    if (2 * e >= valid) w2 &= 0xFFFF0000u;
+                    if (2 * e + 1 >= valid) w2 &= 0x0000FFFFu;
+                    vb[dt][e] = w2;
+                }
         }
 #pragma unroll
-        for (int off = 1; off < 16; off <<= 1)
-#pragma unroll
-            for (int j = 0; j < G; ++j) dot[j] += __shfl_xor(dot[j], off);
-#pragma unroll
-        for (int j = 0; j < G; ++j) {
-            const float sc = valid ? dot[j] * scale : -INFINITY;
-            const float mn = fmaxf(m[j], sc);
-            const float alpha = m[j] == -INFINITY ? 0.f : __expf(m[j] - mn);
-            const float p = valid ? __expf(sc - mn) : 0.f;
-            l[j] = fmaf(l[j], alpha, p);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) acc[j][i] = fmaf(acc[j][i], alpha, p * vf[i]);
-            m[j] = mn;
-        }
+        for (int dt = 0; dt < 8; ++dt)
+            o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pa),
+                                                            __builtin_bit_cast(bf16x8, vb[dt]), o[dt], 0, 0, 0);
     }
-    // merge the four position groups of the wave (lanes 16 apart)
+    // o[dt][i] = O[head 4 grp + i][dim 16 dt + col]
+    if (col == 0)
 #pragma unroll
-    for (int off = 16; off < 64; off <<= 1) {
-#pragma unroll
-        for (int j = 0; j < G; ++j) {
-            const float om = __shfl_xor(m[j], off), ol = __shfl_xor(l[j], off);
-            const float mn = fmaxf(m[j], om);
-            const float a = m[j] == -INFINITY ? 0.f : __expf(m[j] - mn);
-            const float b = om == -INFINITY ? 0.f : __expf(om - mn);
-            l[j] = l[j] * a + ol * b;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) acc[j][i] = acc[j][i] * a + __shfl_xor(acc[j][i], off) * b;
-            m[j] = mn;
+        for (int i = 0; i < 4; ++i) {
+            red_m[wave][4 * grp + i] = m_r[i];
+            red_l[wave][4 * grp + i] = l_r[i];
         }
-    }
-    if (sub == 0) {
 #pragma unroll
-        for (int j = 0; j < G; ++j)
+    for (int i = 0; i < 4; ++i) {
+        const int h = 4 * grp + i;
+        if (h < G)
 #pragma unroll
-            for (int i = 0; i < 8; ++i) red_acc[wave][j][part * 8 + i] = acc[j][i];
-        if (part == 0)
-#pragma unroll
-            for (int j = 0; j < G; ++j) {
-                red_m[wave][j] = m[j];
-                red_l[wave][j] = l[j];
-            }
+            for (int dt = 0; dt < 8; ++dt) red_acc[wave][h][dt * 16 + col] = o[dt][i];
     }
     __syncthreads();
     for (int idx = threadIdx.x; idx < G * kHead; idx += 64 * kAttnWaves) {
@@ -240,22 +344,31 @@ __global__ __launch_bounds__(kHead) void attn_combine_kernel(const float* __rest
 
 }  // namespace
 
-bool attn_decode_ok(int head_dim, int nq, int nkv) {
-    if (head_dim != kHead || nkv < 1 || nq % nkv != 0) return false;
+bool attn_decode_ok(int head_dim, int nq, int nkv, int max_len) {
+    if (head_dim != kHead || nkv < 1 || nq % nkv != 0 || max_len % kKeysPerWave != 0) return false;
     const int G = nq / nkv;
     return G == 1 || G == 2 || G == 4 || G == 8;
 }
 
 int attn_chunks(int max_len) { return (max_len + kChunk - 1) / kChunk; }
 
-hipError_t launch_qk_rope_append(const void* qkv, int64_t T, int nq, int nkv, const float* q_gain,
+hipError_t launch_qk_rope_append(const float* qkv, int KS, int64_t T, int nq, int nkv, const float* q_gain,
                                  const float* k_gain, float eps, const int32_t* pos, const int32_t* len,
                                  int max_len, int sec_h, int sec_w, double theta, void* q_out, void* kc, void* vc,
                                  hipStream_t st) {
     if (T <= 0) return hipSuccess;
-    dim3 grid((unsigned)T, (unsigned)(nq + 2 * nkv));
-    qk_rope_append_kernel<<<grid, 64, 0, st>>>((const bf16_t*)qkv, nq, nkv, q_gain, k_gain, eps, pos, len, max_len,
-                                               sec_h, sec_w, log(theta), (bf16_t*)q_out, (bf16_t*)kc, (bf16_t*)vc);
+    dim3 grid((unsigned)T, (unsigned)((nq + 2 * nkv + kRopeWaves - 1) / kRopeWaves));
+    qk_rope_append_kernel<<<grid, 64 * kRopeWaves, 0, st>>>(qkv, KS, T, nq, nkv, q_gain, k_gain, eps, pos, len,
+                                                             max_len, sec_h, sec_w, log(theta), (bf16_t*)q_out,
+                                                             (bf16_t*)kc, (bf16_t*)vc);
+    return hipGetLastError();
+}
+
+hipError_t launch_attn_out(const float* part, int KS, const void* residual, void* y, int64_t T, int H,
+                           const float* gain, float eps, void* norm_out, hipStream_t st) {
+    if (T <= 0) return hipSuccess;
+    attn_out_kernel<<<(unsigned)T, 128, 0, st>>>(part, KS, T, H, (const bf16_t*)residual, (bf16_t*)y, gain, eps,
+                                                (bf16_t*)norm_out);
     return hipGetLastError();
 }
 

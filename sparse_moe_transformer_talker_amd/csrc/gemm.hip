@@ -657,6 +657,84 @@ hipError_t launch_grouped_gemm_direct(int pass, const GemmArgs& args, hipStream_
     return launch_gemm(grouped_gemm_kernel<TMOE_SMALL_DN>, grid, st, ev_start, ev_stop, args);
 }
 
+// ---------------------------------------------------------------------------
+// Skinny products for M <= 64 rows (a decode batch), split over K:
+// P[s] [M, N] = A [M, K_s] W_s^T in fp32, where K_s is the s-th of KS equal runs
+// of K.  One workgroup per (16 output columns, run) reads its 16 x K_s weight
+// block once; its four waves split the run again, each covering all 64 rows as
+// four 16-row matrix-core tiles (v_mfma_f32_16x16x32_bf16, four 32-wide K steps
+// with their loads in flight together).  The waves' partials are added in LDS
+// in wave order; the consumer adds the KS runs in run order (deterministic).
+namespace {
+constexpr int kSkinnyRows = 64;
+constexpr int kSkinnyWaves = 4;
+__global__ __launch_bounds__(64 * kSkinnyWaves) void skinny_gemm_kernel(const bf16_t* __restrict__ A,
+                                                                        const bf16_t* __restrict__ W,
+                                                                        float* __restrict__ P, int M, int N, int K,
+                                                                        int KS) {
+    constexpr int U = 4;
+    __shared__ float part[kSkinnyWaves][kSkinnyRows][17];
+    const int wave = (int)(threadIdx.x >> 6), lane = lane_id();
+    const int n0 = blockIdx.x * 16, run = blockIdx.y;
+    const int r = lane & 15, kg = (lane >> 4) * 8;
+    const int kw = K / KS / kSkinnyWaves, kb = run * (K / KS) + wave * kw;
+    const bf16_t* wp = W + (int64_t)(n0 + r) * K + kb + kg;
+    const bf16_t* ap[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) ap[mt] = A + (int64_t)min(mt * 16 + r, M - 1) * K + kb + kg;
+    const f32x4 zero = {0, 0, 0, 0};
+    f32x4 acc[4] = {zero, zero, zero, zero};
+    for (int kk = 0; kk < kw; kk += 32 * U) {
+        u32x4 b[U], a[4][U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {  // branch-free: steps past the end repeat the last one, unused
+            const int k = min(kk + 32 * u, kw - 32);
+            b[u] = *reinterpret_cast<const u32x4*>(wp + k);
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) a[mt][u] = *reinterpret_cast<const u32x4*>(ap[mt] + k);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (kk + 32 * u >= kw) continue;
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+                acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[mt][u]),
+                                                                  __builtin_bit_cast(bf16x8, b[u]), acc[mt], 0, 0, 0);
+        }
+    }
+    // D[row = 4 (lane / 16) + i][col = lane % 16] of each 16-row tile
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) part[wave][mt * 16 + 4 * (lane >> 4) + i][r] = acc[mt][i];
+    __syncthreads();
+    float* out = P + (int64_t)run * M * N;
+    for (int idx = threadIdx.x; idx < kSkinnyRows * 16; idx += 64 * kSkinnyWaves) {
+        const int row = idx >> 4, col = idx & 15;
+        if (row >= M) continue;
+        float v = part[0][row][col];
+#pragma unroll
+        for (int w = 1; w < kSkinnyWaves; ++w) v += part[w][row][col];
+        out[(int64_t)row * N + n0 + col] = v;
+    }
+}
+}  // namespace
+
+int skinny_gemm_runs(int64_t M, int N, int K) {
+    if (M < 1 || M > kSkinnyRows || N < 16 || N % 16 || K % (32 * kSkinnyWaves)) return 0;
+    // enough workgroups to fill the chip, each run at least 512 long
+    int ks = 1;
+    while (ks * 2 * 512 <= K && K % (ks * 2 * 32 * kSkinnyWaves) == 0 && (N / 16) * ks < 256) ks *= 2;
+    return ks;
+}
+
+hipError_t launch_skinny_gemm(const void* A, const void* W, float* P, int64_t M, int N, int K, int KS,
+                              hipStream_t st) {
+    dim3 grid((unsigned)(N / 16), (unsigned)KS);
+    skinny_gemm_kernel<<<grid, 64 * kSkinnyWaves, 0, st>>>((const bf16_t*)A, (const bf16_t*)W, P, (int)M, N, K, KS);
+    return hipGetLastError();
+}
+
 hipError_t launch_gemm_generic(int dtype, int pass, const GemmGroup& g, const int32_t* offsets, int n_groups_rows,
                                int E, int64_t rows, hipStream_t st) {
     (void)n_groups_rows;

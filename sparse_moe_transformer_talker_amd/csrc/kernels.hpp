@@ -139,6 +139,12 @@ hipError_t launch_grouped_gemm(int dtype, int variant, int pass, const GemmArgs&
 int gemm_direct_tile(int pass, int* bm);
 hipError_t launch_grouped_gemm_direct(int pass, const GemmArgs& args, hipStream_t st, hipEvent_t ev_start = nullptr,
                                       hipEvent_t ev_stop = nullptr);
+// Split-K skinny product: P[s] [M, N] (fp32, s < KS) = A [M, K_s] W_s^T over the
+// s-th of KS equal runs of K; bf16 inputs, M <= 64, N % 16 == 0.  KS from
+// skinny_gemm_runs (0: the shape does not fit).
+int skinny_gemm_runs(int64_t M, int N, int K);
+hipError_t launch_skinny_gemm(const void* A, const void* W, float* P, int64_t M, int N, int K, int KS,
+                              hipStream_t st);
 // Portable path: one thread per output; rows of group 0 find their expert in offsets.
 hipError_t launch_gemm_generic(int dtype, int pass, const GemmGroup& g, const int32_t* offsets, int n_groups_rows,
                                int E, int64_t rows, hipStream_t st);
@@ -161,12 +167,14 @@ hipError_t launch_gather_rows(int dtype, const void* x, const int32_t* rows, int
                               hipStream_t st);
 
 // --- decode-time attention (attention.hip) ---
-// head_dim 128 and nq / nkv in {1, 2, 4, 8}
-bool attn_decode_ok(int head_dim, int nq, int nkv);
+// head_dim 128, nq / nkv in {1, 2, 4, 8}, max_len a multiple of 32
+bool attn_decode_ok(int head_dim, int nq, int nkv, int max_len);
 int attn_chunks(int max_len);  // partials per (stream, KV head): 128 positions each
-// qkv [T, (nq + 2 nkv) 128] -> q_out [T, nq, 128] (normalised, rotated) and the
-// new key / value rows at position len[t] of kc / vc [T, nkv, max_len, 128]
-hipError_t launch_qk_rope_append(const void* qkv, int64_t T, int nq, int nkv, const float* q_gain,
+// qkv: KS fp32 partials [KS][T][(nq + 2 nkv) 128] of the projection (summed in
+// order) -> q_out [T, nq, 128] (normalised, rotated), the new
+// key row at position len[t] of kc [T, nkv, max_len, 128] and the new value
+// column at len[t] of the transposed vc [T, nkv, 128, max_len]
+hipError_t launch_qk_rope_append(const float* qkv, int KS, int64_t T, int nq, int nkv, const float* q_gain,
                                  const float* k_gain, float eps, const int32_t* pos, const int32_t* len,
                                  int max_len, int sec_h, int sec_w, double theta, void* q_out, void* kc, void* vc,
                                  hipStream_t st);
@@ -174,5 +182,9 @@ hipError_t launch_qk_rope_append(const void* qkv, int64_t T, int nq, int nkv, co
 // cache; pm / pl [T nkv chunks (nq / nkv)], pacc [.. x 128] fp32 scratch
 hipError_t launch_attn_decode(const void* q, const void* kc, const void* vc, const int32_t* len, int64_t T, int nq,
                               int nkv, int max_len, float* pm, float* pl, float* pacc, void* o, hipStream_t st);
+// y [T, H] = sum of the KS fp32 partials [KS][T][H] (in order) + residual
+// (nullable), stored bf16; norm_out (nullable) = RMSNorm(y) * gain (nullable)
+hipError_t launch_attn_out(const float* part, int KS, const void* residual, void* y, int64_t T, int H,
+                           const float* gain, float eps, void* norm_out, hipStream_t st);
 
 }  // namespace tmoe

@@ -4,10 +4,12 @@ One step of the Talker's attention block for T streams with their own caches
 (16 query heads over 2 KV heads of 128, q/k RMSNorm, interleaved TM-RoPE 24/20/20,
 rope_theta 1e6): the output y = residual + o_proj(attention) and the cache rows
 written at each stream's length are compared with the float64 oracle under the
-bf16 bars; every other cache row must be unchanged bit for bit.  Cases: random
+bf16 bars; every other cache entry must be unchanged bit for bit.  The value
+cache is transposed in the library ([T, nkv, head_dim, max_len]).  Cases: random
 lengths up to 1024 (T = 64), ragged chunks and lengths 0 / 1 / 127 / 128 / 129 /
-max_len - 1 (T = 37, max_len = 300), 3D positions with distinct T/H/W indices,
-long caches (max_len 4096), the 16/8 head split, the fused RMSNorm of y, streams
+max_len - 1 (T = 37, max_len = 320), 3D positions with distinct T/H/W indices,
+long caches (max_len 4096), the 16/8 head split, the fused RMSNorm of y, a batch of 96
+streams (the grouped GEMM path for the projections), streams
 whose length is out of range, and a captured graph replayed.
 """
 import numpy as np
@@ -30,6 +32,11 @@ def _gpu():
     api.load_library()
 
 
+def _vt(v):
+    """The value cache in the library's layout: [T, nkv, head_dim, max_len]."""
+    return np.ascontiguousarray(np.swapaxes(v, 2, 3))
+
+
 def _case(T, max_len, lens, pos=None, shape=INP.TALKER_ATTN, seed=60):
     w = INP.attention_weights(shape, seed)
     kv = INP.kv_cache(T, shape, max_len, seed + 1)
@@ -45,7 +52,7 @@ def _run(shape, max_len, w, kv, x, res, lens, pos, norm=False):
                           num_kv_heads=shape.n_kv_heads, head_dim=shape.head_dim)
     wd = {"w_qkv": G.dev(w["w_qkv"], "bf16"), "w_o": G.dev(w["w_o"], "bf16"),
           "q_norm": torch.from_numpy(w["q_norm"]).cuda(), "k_norm": torch.from_numpy(w["k_norm"]).cuda()}
-    kc, vc = G.dev(kv["k"], "bf16"), G.dev(kv["v"], "bf16")
+    kc, vc = G.dev(kv["k"], "bf16"), G.dev(_vt(kv["v"]), "bf16")
     xd, rd = G.dev(x, "bf16"), G.dev(res, "bf16")
     ld = torch.from_numpy(lens).cuda()
     pd = torch.from_numpy(np.ascontiguousarray(pos)).cuda()
@@ -65,7 +72,7 @@ def _check(shape, max_len, w, kv, x, res, lens, pos, what, norm=False):
                              residual=INP.to_f64(res, "bf16"))
     G.assert_close(G.host64(y), ref["y"], "bf16", what + " y")
     kg = kc.view(torch.int16).cpu().numpy().view(np.uint16)
-    vg = vc.view(torch.int16).cpu().numpy().view(np.uint16)
+    vg = np.swapaxes(vc.view(torch.int16).cpu().numpy().view(np.uint16), 2, 3)
     tt = np.arange(T)
     knew = INP.to_f64(kg[tt, :, lens], "bf16")   # [T, nkv, d]
     vnew = INP.to_f64(vg[tt, :, lens], "bf16")
@@ -87,7 +94,7 @@ def test_attention_decode_random_lengths():
 
 
 def test_attention_decode_ragged_chunks_and_edges():
-    T, L = 37, 300
+    T, L = 37, 320
     lens = INP.cache_lengths(T, L, 65)
     lens[:8] = [0, 1, 127, 128, 129, 255, 256, L - 1]
     w, kv, x, res, lens, pos = _case(T, L, lens)
@@ -133,7 +140,7 @@ def test_attention_decode_graph_replay():
     acfg = api.AttnConfig(max_len=L)
     wd = {"w_qkv": G.dev(w["w_qkv"], "bf16"), "w_o": G.dev(w["w_o"], "bf16"),
           "q_norm": torch.from_numpy(w["q_norm"]).cuda(), "k_norm": torch.from_numpy(w["k_norm"]).cuda()}
-    kc, vc = G.dev(kv["k"], "bf16"), G.dev(kv["v"], "bf16")
+    kc, vc = G.dev(kv["k"], "bf16"), G.dev(_vt(kv["v"]), "bf16")
     xd, rd = G.dev(x, "bf16"), G.dev(res, "bf16")
     ld, pd = torch.from_numpy(lens).cuda(), torch.from_numpy(pos).cuda()
     dev = torch.device("cuda", 0)
@@ -153,3 +160,10 @@ def test_attention_decode_graph_replay():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(y_g.view(torch.int16), y_e.view(torch.int16)), "replay %d differs" % rep
+
+
+def test_attention_decode_batch_above_64():
+    # more streams than the skinny products take: the grouped GEMM tile path
+    T, L = 96, 256
+    w, kv, x, res, lens, pos = _case(T, L, INP.cache_lengths(T, L, 69))
+    _check(INP.TALKER_ATTN, L, w, kv, x, res, lens, pos, "T=96", norm=True)
