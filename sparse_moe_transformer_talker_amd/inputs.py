@@ -28,7 +28,8 @@ import numpy as np
 __all__ = [
     "LayerShape", "WORKLOADS", "f32_to_bf16_bits", "bf16_bits_to_f32",
     "layer_weights", "activations", "zipf_router_bias", "stack_weights", "AttnShape", "TALKER_ATTN",
-    "attention_weights", "kv_cache", "cache_lengths", "speech_positions",
+    "attention_weights", "kv_cache", "cache_lengths", "speech_positions", "PredictorShape", "PREDICTOR",
+    "predictor_weights",
     "bf16_round", "to_f64", "workload_inputs",
 ]
 
@@ -197,6 +198,41 @@ def speech_positions(lengths: np.ndarray) -> np.ndarray:
     sequence index."""
     p = np.asarray(lengths, np.int32)
     return np.stack([p, p, p], axis=1).astype(np.int32)
+
+
+@dataclasses.dataclass(frozen=True)
+class PredictorShape:
+    """The depth code predictor: layers, hidden, heads, MLP width, codes per frame, codebook, c_0 vocabulary."""
+    layers: int = 5
+    H: int = 1024
+    n_heads: int = 16
+    n_kv_heads: int = 8
+    I: int = 3072  # noqa: E741
+    num_codes: int = 16
+    codebook: int = 2048
+    c0_vocab: int = 3072
+
+
+PREDICTOR = PredictorShape()
+
+
+def predictor_weights(shape: PredictorShape, seed: int, sigma: float = 0.02) -> Dict:
+    """Weights of the predictor (bf16 bits; gains fp32 1 + N(0, 0.1)); embedding tables N(0, 1)."""
+    rng = np.random.default_rng(seed + 50000)
+    H, d = shape.H, 128
+    gain = lambda n: (1.0 + 0.1 * rng.standard_normal(n)).astype(np.float32)
+    bf = lambda shp, sg: _store(_normal(rng, shp, sg), "bf16")
+    layers = []
+    for _ in range(shape.layers):
+        layers.append({"in_norm": gain(H), "post_norm": gain(H),
+                       "w_qkv": bf(((shape.n_heads + 2 * shape.n_kv_heads) * d, H), sigma),
+                       "w_o": bf((H, shape.n_heads * d), sigma), "q_norm": gain(d), "k_norm": gain(d),
+                       "gate": bf((shape.I, H), sigma), "up": bf((shape.I, H), sigma),
+                       "down": bf((H, shape.I), sigma)})
+    return {"layers": layers, "final_norm": gain(H),
+            "c0_embedding": bf((shape.c0_vocab, H), 1.0),
+            "codec_embedding": bf((shape.num_codes - 1, shape.codebook, H), 1.0),
+            "lm_head": bf((shape.num_codes - 1, shape.codebook, H), sigma)}
 
 
 def workload_inputs(name: str, T: Optional[int] = None) -> dict:
