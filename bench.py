@@ -299,6 +299,42 @@ def measure_attention(api, torch, INP, T, L, steps, R=4):
             "timing": "HIP graph of %d layers' attention steps back to back" % R}
 
 
+def measure_predictor(api, torch, INP, T, frames):
+    """One frame of the depth code predictor (16 positions x 5 layers + 15 heads) for T streams, as one graph."""
+    shape = INP.PREDICTOR
+    dev = torch.device("cuda", 0)
+    w = INP.predictor_weights(shape, 80)
+    todev = lambda a: (torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+                       if a.dtype == np.uint16 else torch.from_numpy(a).to(dev))
+    wd = {k: todev(v) for k, v in w.items() if k != "layers"}
+    wd["layers"] = [{k: todev(v) for k, v in lw.items()} for lw in w["layers"]]
+    pc = api.PredictorConfig()
+    wst = api.predictor_weights_struct(wd)
+    h = todev(INP.activations(T, shape.H, 81, "bf16"))
+    c0 = torch.from_numpy(np.random.default_rng(81).integers(0, shape.c0_vocab, T).astype(np.int32)).to(dev)
+    codes = torch.empty((shape.num_codes, T), dtype=torch.int32, device=dev)
+    ws = api.workspace(api.moe_predictor_workspace_size(pc, T), dev)
+    api.moe_predictor_frame(pc, wst, h, c0, codes=codes, ws=ws)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        api.moe_predictor_frame(pc, wst, h, c0, codes=codes, ws=ws)
+    g.replay()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(frames):
+        g.replay()
+    stop.record()
+    torch.cuda.synchronize()
+    us = start.elapsed_time(stop) * 1e3 / frames
+    layer_bytes = sum(v.numel() * v.element_size() for lw in wd["layers"] for v in lw.values())
+    return {"workload": "depth_code_predictor_frame_T%d" % T, "streams": T, "positions": shape.num_codes,
+            "layers": shape.layers, "frame_us": us, "position_us": us / shape.num_codes,
+            "codes_per_s": T * (shape.num_codes - 1) / (us * 1e-6), "layer_weight_bytes": layer_bytes,
+            "timing": "one HIP graph per frame: 16 positions x 5 layers (attention + SwiGLU) and 15 heads"}
+
+
 def cpu_baseline(INP, shape, T, seconds):
     from oracle import moe_ref as R
     try:
@@ -335,6 +371,7 @@ def main():
     ap.add_argument("--stack-layers", type=int, default=20)
     ap.add_argument("--stack-frames", type=int, default=20)
     ap.add_argument("--no-attention", action="store_true")
+    ap.add_argument("--no-predictor", action="store_true")
     ap.add_argument("--no-reports", action="store_true",
                     help="skip the report-only workloads (Zipf-skewed T=8192 layer, 20-layer stack at T=1024)")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
@@ -384,6 +421,11 @@ def main():
         log("attention decode: 64 streams x 1024 cached positions")
         attn = measure_attention(api, torch, INP, 64, 1023, args.steps)
         log("attention: %.2f us/step, %.1f%% of HBM peak" % (attn["us_per_step"], 100 * attn["hbm_frac"]))
+    pred = None
+    if not args.no_predictor and not args.no_decode:
+        log("depth code predictor frame: 64 streams")
+        pred = measure_predictor(api, torch, INP, 64, max(5, args.stack_frames // 2))
+        log("predictor: %.1f us/frame, %.1f us/position" % (pred["frame_us"], pred["position_us"]))
     reports = None
     if not args.no_reports and not args.no_decode and not args.no_prefill:
         c = INP.WORKLOADS["skew_t8192"]
@@ -458,6 +500,8 @@ def main():
         line["reports"] = reports
     if attn is not None:
         line["attention"] = attn
+    if pred is not None:
+        line["predictor"] = pred
     if pre is not None:
         gp = pre["gate_up"]
         line["prefill"] = {"workload": "talker_moe_layer_prefill_T4096", "tokens_per_s": pre["tokens_per_s"],

@@ -278,6 +278,62 @@ int moe_attention_decode(const moe_attn_config* cfg, const moe_attn_weights* w, 
 size_t moe_attention_workspace_size(const moe_attn_config* cfg, int64_t T);
 
 /*
+ * Depth code predictor ("Bài Lab tổng hợp — Qwen3-Omni & Qwen3-TTS-12Hz
+ * Architecture", step [4A]: the predictor is prefilled with [h_talker, embed(c_0)]
+ * and produces c_1 .. c_15 in 15 autoregressive steps, one head per code;
+ * "用 print(model) 认识 Qwen3-TTS", the code_predictor print: 5 decoder layers
+ * with the Talker's attention (q/k norms), a SwiGLU MLP, input / post-attention
+ * RMSNorms, a final norm, 15 codec_embedding tables and 15 lm_heads).
+ */
+typedef struct {
+    moe_attn_config attn;       /* the layers' attention; max_len is ignored (the frame's positions) */
+    int32_t num_layers;         /* 5 */
+    int32_t intermediate_size;  /* 3072 */
+    int32_t num_codes;          /* 16: c_0 .. c_15 */
+    int32_t codebook_size;      /* 2048 */
+    int32_t c0_vocab;           /* 3072: rows of the c_0 embedding table */
+    float eps;                  /* RMSNorm eps, 1e-6 */
+} moe_predictor_config;
+
+typedef struct {
+    moe_attn_weights attn;
+    const float* in_norm;    /* [hidden] input_layernorm gain */
+    const float* post_norm;  /* [hidden] post_attention_layernorm gain */
+    const void* gate;        /* [intermediate, hidden] */
+    const void* up;          /* [intermediate, hidden] */
+    const void* down;        /* [hidden, intermediate] */
+} moe_predictor_layer;
+
+typedef struct {
+    const moe_predictor_layer* layers;  /* host array [num_layers] */
+    const float* final_norm;            /* [hidden] */
+    const void* c0_embedding;           /* [c0_vocab, hidden] (the Talker's codec embedding) */
+    const void* codec_embedding;        /* [num_codes - 1, codebook_size, hidden]: table j - 1 embeds c_j */
+    const void* lm_head;                /* [num_codes - 1, codebook_size, hidden]: head j - 1 gives c_j */
+} moe_predictor_weights;
+
+/*
+ * moe_predictor_frame — one frame for T streams (1 <= T <= 64):
+ *   position 0 is h_talker, position 1 the embedding of c_0, position j + 1 that
+ *   of c_j from table j - 1; each position passes the layers (pre-norm attention
+ *   over the frame's own positions, residual, pre-norm SwiGLU, residual); from
+ *   position 1 on, code j = argmax (exact, ties to the lowest code) of head j - 1
+ *   on the final norm of position j's output.
+ *   h_talker [dev] [T, hidden] bf16;  c0 [dev] [T] int32 (outside [0, c0_vocab):
+ *   a zero embedding);  codes [dev] [num_codes, T] int32 out (row 0 = c0)
+ *   xn_out   [dev] [num_codes, T, hidden] bf16 out or NULL: the final-normed state
+ *            at every position (the heads' input)
+ * The frame's key / value caches live in the workspace:
+ * moe_predictor_workspace_size(cfg, T).
+ */
+int moe_predictor_frame(const moe_predictor_config* cfg, const moe_predictor_weights* w, const void* h_talker,
+                        const int32_t* c0, int64_t T, int32_t* codes, void* xn_out, void* ws, size_t ws_bytes,
+                        void* stream);
+
+/* Workspace bytes for moe_predictor_frame at T (0 for an invalid or unsupported case). Host only. */
+size_t moe_predictor_workspace_size(const moe_predictor_config* cfg, int64_t T);
+
+/*
  * moe_codec_head_sample — c_0 drawn from the softmax of the codec head's logits
  * ("用 print(model) 认识 Qwen3-TTS", "Codec Head：语义码预测": the 3072 logits go
  * through a softmax and the next semantic code is sampled).  Inverse transform

@@ -57,12 +57,14 @@ def decoder_layer(x: np.ndarray, lw: Dict[str, np.ndarray], pos: np.ndarray, k_c
 
 def predictor_frame(h_talker: np.ndarray, c0: np.ndarray, w: Dict, n_heads: int = 16, n_kv_heads: int = 8,
                     num_codes: int = 16, eps: float = 1e-6, theta: float = 1.0e6,
-                    sections: Sequence[int] = (24, 20, 20)) -> Dict[str, np.ndarray]:
+                    sections: Sequence[int] = (24, 20, 20), forced=None) -> Dict[str, np.ndarray]:
     """Codes c_0 .. c_{num_codes - 1} [num_codes, T] of one frame for T streams.
 
     w: "layers" (list of dicts: in_norm, post_norm, w_qkv, q_norm, k_norm, w_o, gate,
     up, down), "final_norm", "c0_embedding" [V0, H], "codec_embedding"
-    [num_codes - 1, K, H], "lm_head" [num_codes - 1, K, H].
+    [num_codes - 1, K, H], "lm_head" [num_codes - 1, K, H].  With ``forced`` [num_codes, T]
+    (teacher forcing), position j + 1 embeds forced[j] instead of the code drawn at j;
+    the drawn codes are still returned.
     """
     h_talker = np.asarray(h_talker, np.float64)
     T, H = h_talker.shape
@@ -79,7 +81,8 @@ def predictor_frame(h_talker: np.ndarray, c0: np.ndarray, w: Dict, n_heads: int 
         elif p == 1:
             x = np.asarray(w["c0_embedding"], np.float64)[codes[0]]
         else:
-            x = np.asarray(w["codec_embedding"][p - 2], np.float64)[codes[p - 1]]
+            prev = codes[p - 1] if forced is None else np.asarray(forced[p - 1])
+            x = np.asarray(w["codec_embedding"][p - 2], np.float64)[prev]
         pos = np.full((T, 3), p)
         lens = np.full(T, p)
         for li, lw in enumerate(w["layers"]):

@@ -27,7 +27,7 @@ EXPORTS = ("moe_status_string", "moe_check_config", "moe_workspace_size", "moe_r
            "moe_layer_forward_timed", "moe_rmsnorm",
            "moe_codec_head_argmax", "moe_codec_head_workspace_size", "moe_stack_forward",
            "moe_stack_workspace_size", "moe_codec_head_sample", "moe_attention_decode",
-           "moe_attention_workspace_size")
+           "moe_attention_workspace_size", "moe_predictor_frame", "moe_predictor_workspace_size")
 
 
 class MoeError(RuntimeError):
@@ -70,6 +70,46 @@ class AttnConfig:
         return moe_attn_config(self.hidden_size, self.num_heads, self.num_kv_heads, self.head_dim,
                                (ctypes.c_int32 * 3)(*self.rope_sections), self.rope_theta, self.eps, self.max_len,
                                MOE_BF16)
+
+
+class moe_predictor_config(ctypes.Structure):
+    _fields_ = [("attn", moe_attn_config), ("num_layers", ctypes.c_int32), ("intermediate_size", ctypes.c_int32),
+                ("num_codes", ctypes.c_int32), ("codebook_size", ctypes.c_int32), ("c0_vocab", ctypes.c_int32),
+                ("eps", ctypes.c_float)]
+
+
+class moe_predictor_layer(ctypes.Structure):
+    _fields_ = [("attn", moe_attn_weights), ("in_norm", ctypes.c_void_p), ("post_norm", ctypes.c_void_p),
+                ("gate", ctypes.c_void_p), ("up", ctypes.c_void_p), ("down", ctypes.c_void_p)]
+
+
+class moe_predictor_weights(ctypes.Structure):
+    _fields_ = [("layers", ctypes.POINTER(moe_predictor_layer)), ("final_norm", ctypes.c_void_p),
+                ("c0_embedding", ctypes.c_void_p), ("codec_embedding", ctypes.c_void_p), ("lm_head", ctypes.c_void_p)]
+
+
+@dataclasses.dataclass
+class PredictorConfig:
+    """The depth code predictor (defaults: 5 layers, 16 query / 8 KV heads, MLP 3072, 16 codes of 2048, c_0
+    vocabulary 3072)."""
+    num_layers: int = 5
+    hidden_size: int = 1024
+    num_heads: int = 16
+    num_kv_heads: int = 8
+    intermediate_size: int = 3072
+    num_codes: int = 16
+    codebook_size: int = 2048
+    c0_vocab: int = 3072
+    eps: float = 1e-6
+    rope_sections: tuple = (24, 20, 20)
+    rope_theta: float = 1.0e6
+
+    def c(self) -> moe_predictor_config:
+        a = AttnConfig(max_len=32, hidden_size=self.hidden_size, num_heads=self.num_heads,
+                       num_kv_heads=self.num_kv_heads, rope_sections=self.rope_sections, rope_theta=self.rope_theta,
+                       eps=self.eps)
+        return moe_predictor_config(a.c(), self.num_layers, self.intermediate_size, self.num_codes,
+                                    self.codebook_size, self.c0_vocab, self.eps)
 
 
 class moe_weights(ctypes.Structure):
@@ -136,6 +176,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         "moe_attention_decode": (ctypes.c_int, [ctypes.POINTER(moe_attn_config), ctypes.POINTER(moe_attn_weights),
                                                 vp, i64, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, sz, vp]),
         "moe_attention_workspace_size": (sz, [ctypes.POINTER(moe_attn_config), i64]),
+        "moe_predictor_frame": (ctypes.c_int, [ctypes.POINTER(moe_predictor_config),
+                                               ctypes.POINTER(moe_predictor_weights), vp, vp, i64, vp, vp, vp, sz,
+                                               vp]),
+        "moe_predictor_workspace_size": (sz, [ctypes.POINTER(moe_predictor_config), i64]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -396,3 +440,35 @@ def moe_attention_decode(acfg: AttnConfig, weights, x: torch.Tensor, pos: torch.
         ctypes.byref(c), ctypes.byref(w), _ptr(x), T, _ptr(pos), _ptr(cache_len), _ptr(k_cache), _ptr(v_cache),
         _ptr(residual), _ptr(y), _ptr(norm_gain), norm_eps, _ptr(norm_out), _ptr(buf), buf.numel(), st))
     return y
+
+
+def moe_predictor_workspace_size(pcfg: PredictorConfig, T: int) -> int:
+    return int(load_library().moe_predictor_workspace_size(ctypes.byref(pcfg.c()), T))
+
+
+def predictor_weights_struct(w: Dict) -> moe_predictor_weights:
+    """moe_predictor_weights from device tensors: "layers" (dicts with w_qkv, q_norm, k_norm, w_o, in_norm,
+    post_norm, gate, up, down), final_norm, c0_embedding, codec_embedding, lm_head.  The layer array is kept
+    alive on the returned struct."""
+    arr = (moe_predictor_layer * len(w["layers"]))(*[
+        moe_predictor_layer(attn_weights_struct(l), _ptr(l["in_norm"]), _ptr(l["post_norm"]), _ptr(l["gate"]),
+                            _ptr(l["up"]), _ptr(l["down"])) for l in w["layers"]])
+    st = moe_predictor_weights(ctypes.cast(arr, ctypes.POINTER(moe_predictor_layer)), _ptr(w["final_norm"]),
+                               _ptr(w["c0_embedding"]), _ptr(w["codec_embedding"]), _ptr(w["lm_head"]))
+    st._layers = arr
+    return st
+
+
+def moe_predictor_frame(pcfg: PredictorConfig, weights, h_talker: torch.Tensor, c0: torch.Tensor, codes=None,
+                        xn_out=None, ws=None, stream=None):
+    """One frame of the depth code predictor.  Returns codes [num_codes, T] int32 (row 0 = c0)."""
+    T, dev = h_talker.shape[0], h_talker.device
+    codes = codes if codes is not None else torch.empty((pcfg.num_codes, T), dtype=torch.int32, device=dev)
+    w = weights if isinstance(weights, moe_predictor_weights) else predictor_weights_struct(weights)
+    lib = load_library()
+    c = pcfg.c()
+    buf = ws if ws is not None else workspace(int(lib.moe_predictor_workspace_size(ctypes.byref(c), T)), dev)
+    st = stream if stream is not None else _stream(dev)
+    _check("moe_predictor_frame", lib.moe_predictor_frame(ctypes.byref(c), ctypes.byref(w), _ptr(h_talker), _ptr(c0),
+                                                          T, _ptr(codes), _ptr(xn_out), _ptr(buf), buf.numel(), st))
+    return codes

@@ -266,7 +266,7 @@ moe_config dense_cfg(int dtype, int N, int K) {
     return c;
 }
 void plan_dense(const moe_config* c, int64_t T, Carver& cv, GemmPlan& g) { plan_gemm(c, T, false, true, cv, g, 257); }
-int run_dense(const moe_config* c, GemmPlan& plan, const void* A, const void* W, void* C, int64_t T, hipStream_t s) {
+int run_dense(const moe_config* c, const GemmPlan& plan, const void* A, const void* W, void* C, int64_t T, hipStream_t s) {
     const int N = c->hidden_size, K = c->shared_expert_intermediate_size;
     if (plan.mfma) TMOE_TRY(launch_build_items(nullptr, 0, T, &plan.t[0], &plan.t[1], s));
     const GemmGroup dn = group(W, nullptr, 0, N, K, A, K, nullptr, C, N, nullptr, 1, 0, nullptr);
@@ -319,6 +319,92 @@ int check_attn_cfg(const moe_attn_config* a) {
         return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
 }
+
+// --- depth code predictor ---
+struct PredPlan {
+    moe_attn_config acfg;  // the layers' attention over the frame's positions
+    AttnPlan ap;
+    int ksgu = 0, ksd = 0;
+    float *pgu, *pd, *sc, *bd;
+    void *h, *X, *Hh, *XN, *HN;
+    char *kc, *vc;
+    size_t cache_bytes;  // per layer, each of K and V
+    int32_t *pos, *len;
+};
+moe_attn_config pred_attn_cfg(const moe_predictor_config* c) {
+    moe_attn_config a = c->attn;
+    a.max_len = (c->num_codes + 31) / 32 * 32;
+    return a;
+}
+int check_pred_cfg(const moe_predictor_config* c, int64_t T) {
+    if (!c) return MOE_ERR_INVALID;
+    const moe_attn_config a = pred_attn_cfg(c);
+    if (c->num_layers < 1 || c->num_codes < 2 || c->codebook_size < 1 || c->c0_vocab < 1 || c->intermediate_size < 1 ||
+        !(c->eps >= 0.0f))
+        return MOE_ERR_INVALID;
+    int st = check_attn_cfg(&a);
+    if (st != MOE_OK) return st;
+    const int H = a.hidden_size, I = c->intermediate_size;
+    if (c->num_layers > 256 || c->num_codes > 256 || c->codebook_size > (1 << 20) || I % 16) return MOE_ERR_UNSUPPORTED;
+    if (T < 1 || T > 64 || !skinny_gemm_runs(T, 2 * I, H) || !skinny_gemm_runs(T, H, I) ||
+        !skinny_gemm_runs(T, (a.num_heads + 2 * a.num_kv_heads) * a.head_dim, H) ||
+        !skinny_gemm_runs(T, H, a.num_heads * a.head_dim))
+        return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+void plan_pred(const moe_predictor_config* c, int64_t T, Carver& cv, PredPlan& p) {
+    p.acfg = pred_attn_cfg(c);
+    const int H = p.acfg.hidden_size, I = c->intermediate_size, K = c->codebook_size, P = c->num_codes;
+    plan_attn(&p.acfg, T, cv, p.ap);
+    p.ksgu = skinny_gemm_runs(T, 2 * I, H);
+    p.ksd = skinny_gemm_runs(T, H, I);
+    p.pgu = cv.take<float>((int64_t)p.ksgu * T * 2 * I);
+    p.pd = cv.take<float>((int64_t)p.ksd * T * H);
+    p.h = cv.take<char>(T * (int64_t)I * 2);
+    p.X = cv.take<char>(T * (int64_t)H * 2);
+    p.Hh = cv.take<char>(T * (int64_t)H * 2);
+    p.XN = cv.take<char>(T * (int64_t)H * 2);
+    p.HN = cv.take<char>(T * (int64_t)H * 2);
+    p.cache_bytes = (size_t)T * p.acfg.num_kv_heads * p.acfg.max_len * p.acfg.head_dim * 2;
+    p.kc = cv.take<char>((int64_t)p.cache_bytes * c->num_layers);
+    p.vc = cv.take<char>((int64_t)p.cache_bytes * c->num_layers);
+    p.pos = cv.take<int32_t>((int64_t)P * T * 3);
+    p.len = cv.take<int32_t>((int64_t)P * T);
+    p.sc = cv.take<float>(T * (int64_t)K);
+    p.bd = cv.take<float>(T * (int64_t)K);
+}
+
+// One attention step with a prepared plan (arguments already checked).
+int attn_run(const moe_attn_config* cfg, const moe_attn_weights* w, const AttnPlan& p, const void* x, int64_t T,
+             const int32_t* pos, const int32_t* cache_len, void* k_cache, void* v_cache, const void* residual,
+             void* y, const float* norm_gain, float norm_eps, void* norm_out, hipStream_t s) {
+    const int H = cfg->hidden_size, nq = cfg->num_heads, nkv = cfg->num_kv_heads;
+    const int d = cfg->head_dim, nqkv = (nq + 2 * nkv) * d;
+    if (p.ksq) {
+        TMOE_TRY(launch_skinny_gemm(x, w->w_qkv, p.pq, T, nqkv, H, p.ksq, s));
+    } else {
+        const int r = run_dense(&p.cq, p.gq, x, w->w_qkv, p.qkv, T, s);
+        if (r != MOE_OK) return r;
+    }
+    TMOE_TRY(launch_qk_rope_append(p.ksq ? p.pq : reinterpret_cast<const float*>(p.qkv), p.ksq, T, nq, nkv,
+                                   w->q_norm, w->k_norm, cfg->eps, pos, cache_len, cfg->max_len,
+                                   cfg->rope_sections[1], cfg->rope_sections[2], (double)cfg->rope_theta, p.q,
+                                   k_cache, v_cache, s));
+    TMOE_TRY(launch_attn_decode(p.q, k_cache, v_cache, cache_len, T, nq, nkv, cfg->max_len, p.pm, p.pl, p.pacc,
+                                p.o, s));
+    if (p.kso) {
+        TMOE_TRY(launch_skinny_gemm(p.o, w->w_o, p.po, T, H, nq * d, p.kso, s));
+        return hip_status(launch_attn_out(p.po, p.kso, residual, y, T, H, norm_gain, norm_eps, norm_out, s));
+    }
+    if (!residual && !norm_out) return run_dense(&p.co, p.go, p.o, w->w_o, y, T, s);
+    const int r = run_dense(&p.co, p.go, p.o, w->w_o, p.ao, T, s);
+    if (r != MOE_OK) return r;
+    if (norm_out)
+        return hip_status(launch_combine_norm(cfg->dtype, nullptr, 0, 0, p.ao, H, residual, y, T, H, norm_gain,
+                                              norm_eps, norm_out, s));
+    return hip_status(launch_combine(cfg->dtype, nullptr, nullptr, nullptr, 0, 0, p.ao, H, residual, y, T, H, s));
+}
+
 
 // Optional end of a stacked layer: the next pre-norm of y, fused into the combine.
 struct LayerEnd {
@@ -727,35 +813,80 @@ int moe_attention_decode(const moe_attn_config* cfg, const moe_attn_weights* w, 
         return MOE_ERR_INVALID;
     if (norm_out && (!(norm_eps >= 0.0f) || norm_out == y)) return MOE_ERR_INVALID;
     if (ws_bytes < moe_attention_workspace_size(cfg, T)) return MOE_ERR_WORKSPACE;
-    const int H = cfg->hidden_size, nq = cfg->num_heads, nkv = cfg->num_kv_heads;
     Carver cv(ws);
     AttnPlan p;
     plan_attn(cfg, T, cv, p);
+    return attn_run(cfg, w, p, x, T, pos, cache_len, k_cache, v_cache, residual, y, norm_gain, norm_eps, norm_out,
+                    as_stream(stream));
+}
+
+size_t moe_predictor_workspace_size(const moe_predictor_config* cfg, int64_t T) {
+    if (check_pred_cfg(cfg, T) != MOE_OK) return 0;
+    Carver cv(nullptr);
+    PredPlan p;
+    plan_pred(cfg, T, cv, p);
+    return cv.size();
+}
+
+int moe_predictor_frame(const moe_predictor_config* cfg, const moe_predictor_weights* w, const void* h_talker,
+                        const int32_t* c0, int64_t T, int32_t* codes, void* xn_out, void* ws, size_t ws_bytes,
+                        void* stream) {
+    if (T == 0 && cfg) return MOE_OK;
+    int st = check_pred_cfg(cfg, T);
+    if (st != MOE_OK) return st;
+    if (!w || !w->layers || !ok_ptr(w->final_norm) || !ok_ptr(w->c0_embedding) || !ok_ptr(w->codec_embedding) ||
+        !ok_ptr(w->lm_head) || !ok_ptr(h_talker) || !ok_ptr(c0) || !ok_ptr(codes) || !ok_opt(xn_out) ||
+        !ok_ptr(ws))
+        return MOE_ERR_INVALID;
+    for (int l = 0; l < cfg->num_layers; ++l) {
+        const moe_predictor_layer& L = w->layers[l];
+        if (!ok_ptr(L.attn.w_qkv) || !ok_ptr(L.attn.q_norm) || !ok_ptr(L.attn.k_norm) || !ok_ptr(L.attn.w_o) ||
+            !ok_ptr(L.in_norm) || !ok_ptr(L.post_norm) || !ok_ptr(L.gate) || !ok_ptr(L.up) || !ok_ptr(L.down))
+            return MOE_ERR_INVALID;
+    }
+    if (ws_bytes < moe_predictor_workspace_size(cfg, T)) return MOE_ERR_WORKSPACE;
+    Carver cv(ws);
+    PredPlan p;
+    plan_pred(cfg, T, cv, p);
     hipStream_t s = as_stream(stream);
-    const int d = cfg->head_dim, nqkv = (nq + 2 * nkv) * d;
-    if (p.ksq) {
-        TMOE_TRY(launch_skinny_gemm(x, w->w_qkv, p.pq, T, nqkv, H, p.ksq, s));
-    } else {
-        const int r = run_dense(&p.cq, p.gq, x, w->w_qkv, p.qkv, T, s);
-        if (r != MOE_OK) return r;
+    const int H = p.acfg.hidden_size, I = cfg->intermediate_size, K = cfg->codebook_size;
+    const int P = cfg->num_codes, L = cfg->num_layers;
+    const float eps = cfg->eps;
+    const int64_t table = (int64_t)K * H * 2;  // bytes per embedding table / head
+    TMOE_TRY(launch_frame_setup(p.pos, p.len, P, T, c0, codes, s));
+    for (int q = 0; q < P; ++q) {
+        const void* src = h_talker;
+        if (q == 1) {
+            TMOE_TRY(launch_embed_rows(w->c0_embedding, cfg->c0_vocab, c0, T, H, p.X, s));
+            src = p.X;
+        } else if (q >= 2) {
+            TMOE_TRY(launch_embed_rows(static_cast<const char*>(w->codec_embedding) + (q - 2) * table, K,
+                                       codes + (int64_t)(q - 1) * T, T, H, p.X, s));
+            src = p.X;
+        }
+        TMOE_TRY(launch_rmsnorm(MOE_BF16, src, w->layers[0].in_norm, eps, T, H, p.XN, s));
+        for (int l = 0; l < L; ++l) {
+            const moe_predictor_layer& ly = w->layers[l];
+            const int r = attn_run(&p.acfg, &ly.attn, p.ap, p.XN, T, p.pos + (int64_t)q * T * 3, p.len + (int64_t)q * T,
+                                   p.kc + l * p.cache_bytes, p.vc + l * p.cache_bytes, l == 0 ? src : p.X, p.Hh,
+                                   ly.post_norm, eps, p.HN, s);
+            if (r != MOE_OK) return r;
+            TMOE_TRY(launch_skinny_gemm(p.HN, ly.gate, p.pgu, T, 2 * I, H, p.ksgu, s, ly.up, I));
+            TMOE_TRY(launch_swiglu_partials(p.pgu, p.ksgu, T, I, p.h, s));
+            TMOE_TRY(launch_skinny_gemm(p.h, ly.down, p.pd, T, H, I, p.ksd, s));
+            const bool last = l + 1 == L;
+            const float* next = last ? w->final_norm : w->layers[l + 1].in_norm;
+            void* xn = last && xn_out ? static_cast<char*>(xn_out) + (int64_t)q * T * H * 2 : p.XN;
+            TMOE_TRY(launch_attn_out(p.pd, p.ksd, p.Hh, p.X, T, H, next, eps, xn, s));
+        }
+        if (q >= 1) {
+            const void* head = static_cast<const char*>(w->lm_head) + (q - 1) * table;
+            const void* xf = xn_out ? static_cast<const char*>(xn_out) + (int64_t)q * T * H * 2 : p.XN;
+            TMOE_TRY(launch_scores(MOE_BF16, xf, head, nullptr, T, H, K, p.sc, p.bd, s));
+            TMOE_TRY(launch_argmax(MOE_BF16, p.sc, p.bd, xf, head, T, H, K, codes + (int64_t)q * T, s));
+        }
     }
-    TMOE_TRY(launch_qk_rope_append(p.ksq ? p.pq : reinterpret_cast<const float*>(p.qkv), p.ksq, T, nq, nkv,
-                                   w->q_norm, w->k_norm, cfg->eps, pos, cache_len, cfg->max_len,
-                                   cfg->rope_sections[1], cfg->rope_sections[2], (double)cfg->rope_theta, p.q,
-                                   k_cache, v_cache, s));
-    TMOE_TRY(launch_attn_decode(p.q, k_cache, v_cache, cache_len, T, nq, nkv, cfg->max_len, p.pm, p.pl, p.pacc,
-                                p.o, s));
-    if (p.kso) {
-        TMOE_TRY(launch_skinny_gemm(p.o, w->w_o, p.po, T, H, nq * d, p.kso, s));
-        return hip_status(launch_attn_out(p.po, p.kso, residual, y, T, H, norm_gain, norm_eps, norm_out, s));
-    }
-    if (!residual && !norm_out) return run_dense(&p.co, p.go, p.o, w->w_o, y, T, s);
-    const int r = run_dense(&p.co, p.go, p.o, w->w_o, p.ao, T, s);
-    if (r != MOE_OK) return r;
-    if (norm_out)
-        return hip_status(launch_combine_norm(cfg->dtype, nullptr, 0, 0, p.ao, H, residual, y, T, H, norm_gain,
-                                              norm_eps, norm_out, s));
-    return hip_status(launch_combine(cfg->dtype, nullptr, nullptr, nullptr, 0, 0, p.ao, H, residual, y, T, H, s));
+    return MOE_OK;
 }
 
 int moe_codec_head_sample(const moe_config* cfg, const void* x, const void* w_head, int32_t V, int64_t T,

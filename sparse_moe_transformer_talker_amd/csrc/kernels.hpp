@@ -143,8 +143,11 @@ hipError_t launch_grouped_gemm_direct(int pass, const GemmArgs& args, hipStream_
 // s-th of KS equal runs of K; bf16 inputs, M <= 64, N % 16 == 0.  KS from
 // skinny_gemm_runs (0: the shape does not fit).
 int skinny_gemm_runs(int64_t M, int N, int K);
+// (W2, N1: output columns N1.. read rows of W2, so gate | up run as one product)
 hipError_t launch_skinny_gemm(const void* A, const void* W, float* P, int64_t M, int N, int K, int KS,
-                              hipStream_t st);
+                              hipStream_t st, const void* W2 = nullptr, int N1 = 0);
+// h [M, I] bf16 = SiLU(gate) * up from KS partials [KS][M][2 I] (gate columns first); I % 8 == 0
+hipError_t launch_swiglu_partials(const float* P, int KS, int64_t M, int I, void* h, hipStream_t st);
 // Portable path: one thread per output; rows of group 0 find their expert in offsets.
 hipError_t launch_gemm_generic(int dtype, int pass, const GemmGroup& g, const int32_t* offsets, int n_groups_rows,
                                int E, int64_t rows, hipStream_t st);
@@ -186,5 +189,12 @@ hipError_t launch_attn_decode(const void* q, const void* kc, const void* vc, con
 // (nullable), stored bf16; norm_out (nullable) = RMSNorm(y) * gain (nullable)
 hipError_t launch_attn_out(const float* part, int KS, const void* residual, void* y, int64_t T, int H,
                            const float* gain, float eps, void* norm_out, hipStream_t st);
+// out [n, H] = table[idx[i]] (bf16 rows, H % 8 == 0); indices outside [0, rows) give zero rows
+hipError_t launch_embed_rows(const void* table, int rows, const int32_t* idx, int64_t n, int H, void* out,
+                             hipStream_t st);
+// Frame set-up of the code predictor: pos [P][T][3] = p, len [P][T] = p, codes
+// row 0 = c0 (codes [num][T])
+hipError_t launch_frame_setup(int32_t* pos, int32_t* len, int P, int64_t T, const int32_t* c0, int32_t* codes,
+                              hipStream_t st);
 
 }  // namespace tmoe

@@ -220,3 +220,29 @@ def test_attention_config_and_argument_errors():
     for kw, want in ((dict(head_dim=64, rope_sections=(12, 10, 10)), -2), (dict(num_heads=48, num_kv_heads=2), -2),
                      (dict(num_heads=16, num_kv_heads=3), -1)):
         assert call(cfg=api.AttnConfig(**dict(dict(max_len=1024), **kw)).c()) == want, kw
+
+
+def test_predictor_config_and_argument_errors():
+    lib = api.load_library()
+    c = api.PredictorConfig().c()
+    n = lib.moe_predictor_workspace_size(ctypes.byref(c), 64)
+    assert n > 5 * 2 * 64 * 8 * 32 * 128 * 2     # the layers' frame caches live in the workspace
+    assert lib.moe_predictor_workspace_size(ctypes.byref(c), 65) == 0   # the skinny products take up to 64
+    assert lib.moe_predictor_workspace_size(ctypes.byref(api.PredictorConfig(intermediate_size=3080).c()), 8) == 0
+    assert lib.moe_predictor_workspace_size(ctypes.byref(api.PredictorConfig(num_codes=1).c()), 8) == 0
+    layer = api.moe_predictor_layer(api.moe_attn_weights(FAKE, FAKE, FAKE, FAKE), FAKE, FAKE, FAKE, FAKE, FAKE)
+    arr = (api.moe_predictor_layer * 5)(*([layer] * 5))
+    w = api.moe_predictor_weights(ctypes.cast(arr, ctypes.POINTER(api.moe_predictor_layer)), FAKE, FAKE, FAKE, FAKE)
+
+    def call(**kw):
+        return lib.moe_predictor_frame(ctypes.byref(c), kw.get("w", ctypes.byref(w)), kw.get("h", _p()),
+                                       _p(1 << 20), kw.get("T", 64), _p(1 << 24), None, _p(1 << 26), kw.get("ws", n),
+                                       None)
+
+    assert call(w=None) == -1
+    assert call(h=None) == -1
+    assert call(ws=n - 256) == -3
+    assert call(T=0) == 0
+    assert call(T=100) == -2
+    arr[3].down = None
+    assert call() == -1                          # every layer checked before launching

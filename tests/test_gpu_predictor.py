@@ -1,0 +1,124 @@
+"""The depth code predictor's frame through the C ABI against its oracle.
+
+One frame for T streams (5 layers, 16 query / 8 KV heads, MLP 3072, 16 codes of
+2048, c_0 vocabulary 3072).  The library returns the codes and the final-normed
+state at every position.  As for the stack, a code is an argmax over a bf16
+state, so the checks are:
+  * every code c_j (j >= 1) is the exact argmax (ties to the lowest code) of
+    head j - 1 on the library's own state at position j, computed by the oracle;
+  * teacher forcing: the oracle's frame fed the library's codes reproduces the
+    library's states at every position within the bf16 bars;
+  * the free-running oracle's codes are reported beside the library's.
+Cases: 64 streams and a ragged 5; c_0 outside the table (a zero embedding);
+the frame captured in a graph and replayed.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_ref as R
+from oracle import predictor_ref as P
+from sparse_moe_transformer_talker_amd import api
+from sparse_moe_transformer_talker_amd import inputs as INP
+from tests import gpu_helpers as G
+
+pytestmark = pytest.mark.gpu
+
+# The states are RMS-normalised (|x| up to about 5, where bf16 spacing is 1/32):
+# the max-abs bar is about 2.5 spacings there, 4x the layer outputs' (std 0.14);
+# the rel-L2 bar is the common one.
+STATE_MAX_ABS = 8e-2
+
+
+def _close(got, ref, what):
+    max_abs, rel = G.errors(got, ref)
+    print("%s: max_abs=%.3e rel_l2=%.3e" % (what, max_abs, rel), flush=True)
+    assert max_abs <= STATE_MAX_ABS and rel <= G.BF16_REL_L2, (what, max_abs, rel)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    api.load_library()
+
+
+@pytest.fixture(scope="module")
+def pred():
+    shape = INP.PREDICTOR
+    w = INP.predictor_weights(shape, 80)
+    dev = lambda a: G.dev(a, "bf16") if a.dtype == np.uint16 else torch.from_numpy(a).cuda()
+    wd = {k: dev(v) for k, v in w.items() if k != "layers"}
+    wd["layers"] = [{k: dev(v) for k, v in lw.items()} for lw in w["layers"]]
+    f64 = lambda a: INP.to_f64(a, "bf16") if a.dtype == np.uint16 else a.astype(np.float64)
+    w64 = {k: f64(v) for k, v in w.items() if k != "layers"}
+    w64["layers"] = [{k: f64(v) for k, v in lw.items()} for lw in w["layers"]]
+    return shape, wd, w64
+
+
+def _run(shape, wd, T, seed, c0=None):
+    h = INP.activations(T, shape.H, seed, "bf16")
+    if c0 is None:
+        c0 = np.random.default_rng(seed).integers(0, shape.c0_vocab, T).astype(np.int32)
+    xn = torch.empty((shape.num_codes, T, shape.H), dtype=torch.bfloat16, device="cuda")
+    codes = api.moe_predictor_frame(api.PredictorConfig(), wd, G.dev(h, "bf16"), torch.from_numpy(c0).cuda(),
+                                    xn_out=xn)
+    torch.cuda.synchronize()
+    return h, c0, codes.cpu().numpy().astype(np.int64), G.host64(xn.reshape(-1, shape.H)).reshape(
+        shape.num_codes, T, shape.H)
+
+
+@pytest.mark.parametrize("T", [64, 5])
+def test_predictor_frame(pred, T):
+    shape, wd, w64 = pred
+    h, c0, codes, xn = _run(shape, wd, T, 81 + T)
+    np.testing.assert_array_equal(codes[0], c0)
+    for j in range(1, shape.num_codes):
+        np.testing.assert_array_equal(codes[j], R.argmax_first(xn[j] @ w64["lm_head"][j - 1].T), err_msg="code %d" % j)
+    forced = P.predictor_frame(INP.to_f64(h, "bf16"), c0, w64, forced=codes)
+    for j in range(shape.num_codes):
+        _close(xn[j], forced["final"][j], "T=%d position %d" % (T, j))
+    free = P.predictor_frame(INP.to_f64(h, "bf16"), c0, w64)["codes"]
+    agree = float(np.mean(free[1:] == codes[1:]))
+    print("predictor T=%d: codes exact on the library's states; free-running oracle agreement %.3f" % (T, agree),
+          flush=True)
+
+
+def test_predictor_c0_outside_the_table(pred):
+    shape, wd, w64 = pred
+    c0 = np.array([-1, shape.c0_vocab, 7], np.int32)
+    h, _, codes, xn = _run(shape, wd, 3, 90, c0=c0)
+    np.testing.assert_array_equal(codes[0], c0)
+    for j in range(1, shape.num_codes):
+        np.testing.assert_array_equal(codes[j], R.argmax_first(xn[j] @ w64["lm_head"][j - 1].T))
+    # position 1 of streams 0 and 1 saw a zero embedding: the oracle with a zero row agrees
+    w0 = dict(w64, c0_embedding=np.vstack([w64["c0_embedding"], np.zeros((1, shape.H))]))
+    forced = P.predictor_frame(INP.to_f64(h, "bf16"), np.array([shape.c0_vocab, shape.c0_vocab, 7]), w0,
+                               forced=codes)
+    for j in range(shape.num_codes):
+        _close(xn[j], forced["final"][j], "outside position %d" % j)
+
+
+def test_predictor_graph_replay(pred):
+    shape, wd, _ = pred
+    T = 16
+    dev = torch.device("cuda", 0)
+    pc = api.PredictorConfig()
+    h = G.dev(INP.activations(T, shape.H, 95, "bf16"), "bf16")
+    c0 = torch.from_numpy(np.random.default_rng(95).integers(0, shape.c0_vocab, T).astype(np.int32)).cuda()
+    ws = api.workspace(api.moe_predictor_workspace_size(pc, T), dev)
+    wst = api.predictor_weights_struct(wd)
+    codes_e = api.moe_predictor_frame(pc, wst, h, c0, ws=ws).clone()
+    torch.cuda.synchronize()
+    codes_g = torch.empty_like(codes_e)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        api.moe_predictor_frame(pc, wst, h, c0, codes=codes_g, ws=ws)
+    h2 = G.dev(INP.activations(T, shape.H, 96, "bf16"), "bf16")
+    for rep in range(3):
+        api.moe_predictor_frame(pc, wst, h2, c0)  # eager work between replays
+        torch.cuda.synchronize()
+        codes_g.fill_(-7)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(codes_g, codes_e), "replay %d differs" % rep
