@@ -299,6 +299,60 @@ def measure_attention(api, torch, INP, T, L, steps, R=4):
             "timing": "HIP graph of %d layers' attention steps back to back" % R}
 
 
+def measure_talker_frame(api, torch, INP, shape, T, ctx, weight_sets, L, frames, vocab=3072):
+    """The Talker's decode step through L whole layers (attention over ctx cached positions, then the MoE) and
+    the codec head, as one graph.  Layer l uses MoE weight set l % R and attention weight set l % R; every layer
+    has its own caches (filled on the device with seeded normal values)."""
+    dev = torch.device("cuda", 0)
+    to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    ashape = INP.TALKER_ATTN
+    R = len(weight_sets)
+    attn_w = []
+    for r in range(R):
+        w = INP.attention_weights(ashape, 60 + r)
+        attn_w.append({"w_qkv": to_dev(w["w_qkv"]), "w_o": to_dev(w["w_o"]),
+                       "q_norm": torch.from_numpy(w["q_norm"]).to(dev), "k_norm": torch.from_numpy(w["k_norm"]).to(dev)})
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    max_len = ctx + 1
+    layers = []
+    for l in range(L):
+        kc = torch.randn((T, ashape.n_kv_heads, max_len, ashape.head_dim), generator=gen, device=dev,
+                         dtype=torch.float32).to(torch.bfloat16)
+        vc = (0.64 * torch.randn((T, ashape.n_kv_heads, ashape.head_dim, max_len), generator=gen, device=dev,
+                                 dtype=torch.float32)).to(torch.bfloat16)
+        layers.append({"moe": api.weights_struct(weight_sets[l % R]), "attn": attn_w[l % R], "k_cache": kc,
+                       "v_cache": vc})
+    arr = api.talker_layers_struct(layers)
+    cfg = api.Config(shape.H, shape.E, shape.k, shape.I, shape.Is, True, torch.bfloat16)
+    acfg = api.AttnConfig(max_len=max_len)
+    head = to_dev(INP.stack_weights(shape, 0, 30, 0.02, "bf16", vocab, 50)["codec_head"])
+    x = to_dev(INP.activations(T, shape.H, 30, "bf16"))
+    lens = torch.full((T,), ctx, dtype=torch.int32, device=dev)
+    pos = torch.from_numpy(INP.speech_positions(np.full(T, ctx, np.int32))).to(dev)
+    h, c0 = torch.empty_like(x), torch.empty(T, dtype=torch.int32, device=dev)
+    ws = api.workspace(api.moe_talker_decode_workspace_size(cfg, acfg, T, vocab), dev)
+    run = lambda: api.moe_talker_decode(cfg, acfg, arr, x, pos, lens, None, 1e-6, head, h_out=h, c0=c0, ws=ws)
+    run()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    g.replay()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(frames):
+        g.replay()
+    stop.record()
+    torch.cuda.synchronize()
+    us = start.elapsed_time(stop) * 1e3 / frames
+    return {"workload": "talker_decode_frame_%dlayers_T%d_ctx%d" % (L, T, max_len), "layers": L, "streams": T,
+            "positions": max_len, "frame_us": us, "per_layer_us": us / L, "tokens_per_s": T / (us * 1e-6),
+            "timing": "one HIP graph per frame: per layer attention (+ residual, post-attention norm) and MoE "
+                      "(+ residual, next norm), then the codec head argmax"}
+
+
 def measure_predictor(api, torch, INP, T, frames):
     """One frame of the depth code predictor (16 positions x 5 layers + 15 heads) for T streams, as one graph."""
     shape = INP.PREDICTOR
@@ -372,6 +426,7 @@ def main():
     ap.add_argument("--stack-frames", type=int, default=20)
     ap.add_argument("--no-attention", action="store_true")
     ap.add_argument("--no-predictor", action="store_true")
+    ap.add_argument("--no-talker-frame", action="store_true")
     ap.add_argument("--no-reports", action="store_true",
                     help="skip the report-only workloads (Zipf-skewed T=8192 layer, 20-layer stack at T=1024)")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
@@ -421,6 +476,11 @@ def main():
         log("attention decode: 64 streams x 1024 cached positions")
         attn = measure_attention(api, torch, INP, 64, 1023, args.steps)
         log("attention: %.2f us/step, %.1f%% of HBM peak" % (attn["us_per_step"], 100 * attn["hbm_frac"]))
+    tframe = None
+    if not args.no_talker_frame and not args.no_decode:
+        log("talker decode frame: 20 layers (attention + MoE) + codec head, 64 streams x 1024 positions")
+        tframe = measure_talker_frame(api, torch, INP, shape, 64, 1023, sets, 20, max(5, args.stack_frames // 2))
+        log("talker frame: %.1f us/frame, %.1f us/layer" % (tframe["frame_us"], tframe["per_layer_us"]))
     pred = None
     if not args.no_predictor and not args.no_decode:
         log("depth code predictor frame: 64 streams")
@@ -502,6 +562,8 @@ def main():
         line["attention"] = attn
     if pred is not None:
         line["predictor"] = pred
+    if tframe is not None:
+        line["talker_frame"] = tframe
     if pre is not None:
         gp = pre["gate_up"]
         line["prefill"] = {"workload": "talker_moe_layer_prefill_T4096", "tokens_per_s": pre["tokens_per_s"],

@@ -334,6 +334,46 @@ int moe_predictor_frame(const moe_predictor_config* cfg, const moe_predictor_wei
 size_t moe_predictor_workspace_size(const moe_predictor_config* cfg, int64_t T);
 
 /*
+ * The Talker's decode step through L whole decoder layers ("3C · Talker MoE (20
+ * lớp, 128 Experts Top-6) & Đầu ra mã ngữ nghĩa c_0" §1-§2: each of the 20
+ * layers runs GQA, then the Top-6-of-128 MoE with its shared expert; after the
+ * last, codec_head gives c_0), pre-norm as in the Qwen3-TTS module print:
+ *   a = h + Attn(RMSNorm_in(h));  h' = a + MoE(RMSNorm_post(a));
+ * then xn = RMSNorm_final(h_L) and c_0 = argmax codec_head(xn).
+ */
+typedef struct {
+    moe_weights moe;          /* the layer's MoE feed-forward */
+    moe_attn_weights attn;    /* the layer's attention */
+    const float* in_norm;     /* [hidden] input_layernorm gain, or NULL (1.0) */
+    const float* post_norm;   /* [hidden] post_attention_layernorm gain, or NULL (1.0) */
+    void* k_cache;            /* [T, num_kv_heads, max_len, head_dim], in/out (as moe_attention_decode) */
+    void* v_cache;            /* [T, num_kv_heads, head_dim, max_len], in/out */
+} moe_talker_layer;
+
+/*
+ * moe_talker_decode — one decode step of T streams through layers[0 .. L):
+ * each layer's attention adds its residual and writes the post-attention norm in
+ * its last launch, and its MoE combine adds its residual and writes the next
+ * layer's input norm (or the final norm) in one launch; results equal those of
+ * moe_rmsnorm, moe_attention_decode (with norm_out) and moe_layer_forward called
+ * layer by layer.
+ *   x          [dev] [T, hidden] the stack input;  h_out [dev] [T, hidden] out
+ *   pos, cache_len  as moe_attention_decode (shared by all layers; not advanced)
+ *   final_norm [dev] [hidden] or NULL (1.0);  eps: every RMSNorm's epsilon
+ *   codec_head [dev] [V, hidden] or NULL;  c0 [dev] [T] int32 out or NULL
+ *   xn_out     [dev] [T, hidden] out or NULL: the final-normed state
+ * Workspace: moe_talker_decode_workspace_size(cfg, acfg, T, V) (V = 0 without
+ * the head).  T <= 65535.
+ */
+int moe_talker_decode(const moe_config* cfg, const moe_attn_config* acfg, const moe_talker_layer* layers, int32_t L,
+                      const void* x, int64_t T, const int32_t* pos, const int32_t* cache_len,
+                      const float* final_norm, float eps, const void* codec_head, int32_t V, void* h_out,
+                      void* xn_out, int32_t* c0, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes for moe_talker_decode (0 for an invalid or unsupported case). Host only. */
+size_t moe_talker_decode_workspace_size(const moe_config* cfg, const moe_attn_config* acfg, int64_t T, int32_t V);
+
+/*
  * moe_codec_head_sample — c_0 drawn from the softmax of the codec head's logits
  * ("用 print(model) 认识 Qwen3-TTS", "Codec Head：语义码预测": the 3072 logits go
  * through a softmax and the next semantic code is sampled).  Inverse transform

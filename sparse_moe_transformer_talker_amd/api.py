@@ -27,7 +27,8 @@ EXPORTS = ("moe_status_string", "moe_check_config", "moe_workspace_size", "moe_r
            "moe_layer_forward_timed", "moe_rmsnorm",
            "moe_codec_head_argmax", "moe_codec_head_workspace_size", "moe_stack_forward",
            "moe_stack_workspace_size", "moe_codec_head_sample", "moe_attention_decode",
-           "moe_attention_workspace_size", "moe_predictor_frame", "moe_predictor_workspace_size")
+           "moe_attention_workspace_size", "moe_predictor_frame", "moe_predictor_workspace_size",
+           "moe_talker_decode", "moe_talker_decode_workspace_size")
 
 
 class MoeError(RuntimeError):
@@ -118,6 +119,11 @@ class moe_weights(ctypes.Structure):
                 ("shared_up", ctypes.c_void_p), ("shared_down", ctypes.c_void_p)]
 
 
+class moe_talker_layer(ctypes.Structure):
+    _fields_ = [("moe", moe_weights), ("attn", moe_attn_weights), ("in_norm", ctypes.c_void_p),
+                ("post_norm", ctypes.c_void_p), ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p)]
+
+
 @dataclasses.dataclass(frozen=True)
 class Config:
     """Layer configuration (field names as in the model configuration)."""
@@ -180,6 +186,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
                                                ctypes.POINTER(moe_predictor_weights), vp, vp, i64, vp, vp, vp, sz,
                                                vp]),
         "moe_predictor_workspace_size": (sz, [ctypes.POINTER(moe_predictor_config), i64]),
+        "moe_talker_decode": (ctypes.c_int, [cfgp, ctypes.POINTER(moe_attn_config), ctypes.POINTER(moe_talker_layer),
+                                             i32, vp, i64, vp, vp, vp, ctypes.c_float, vp, i32, vp, vp, vp, vp, sz,
+                                             vp]),
+        "moe_talker_decode_workspace_size": (sz, [cfgp, ctypes.POINTER(moe_attn_config), i64, i32]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -472,3 +482,40 @@ def moe_predictor_frame(pcfg: PredictorConfig, weights, h_talker: torch.Tensor, 
     _check("moe_predictor_frame", lib.moe_predictor_frame(ctypes.byref(c), ctypes.byref(w), _ptr(h_talker), _ptr(c0),
                                                           T, _ptr(codes), _ptr(xn_out), _ptr(buf), buf.numel(), st))
     return codes
+
+
+def moe_talker_decode_workspace_size(cfg: Config, acfg: AttnConfig, T: int, V: int = 0) -> int:
+    return int(load_library().moe_talker_decode_workspace_size(ctypes.byref(cfg.c()), ctypes.byref(acfg.c()), T, V))
+
+
+def talker_layers_struct(layers) -> ctypes.Array:
+    """A ctypes array of moe_talker_layer from dicts: "moe" (weight dict or moe_weights), "attn" (attention weight
+    dict or moe_attn_weights), "in_norm", "post_norm" (nullable), "k_cache", "v_cache"."""
+    mk = lambda w: w if isinstance(w, moe_weights) else weights_struct(w)
+    ma = lambda w: w if isinstance(w, moe_attn_weights) else attn_weights_struct(w)
+    return (moe_talker_layer * len(layers))(*[
+        moe_talker_layer(mk(l["moe"]), ma(l["attn"]), _ptr(l.get("in_norm")), _ptr(l.get("post_norm")),
+                         _ptr(l["k_cache"]), _ptr(l["v_cache"])) for l in layers])
+
+
+def moe_talker_decode(cfg: Config, acfg: AttnConfig, layers, x: torch.Tensor, pos: torch.Tensor,
+                      cache_len: torch.Tensor, final_norm: Optional[torch.Tensor] = None, eps: float = 1e-6,
+                      codec_head: Optional[torch.Tensor] = None, h_out=None, xn_out=None, c0=None,
+                      want_c0: bool = True, ws=None, stream=None):
+    """One decode step through the layers (caches updated in place).  ``layers``: list of dicts (see
+    talker_layers_struct) or a prebuilt array.  Returns (h_out, xn_out or None, c0 or None)."""
+    T, dev = x.shape[0], x.device
+    arr = layers if isinstance(layers, ctypes.Array) else talker_layers_struct(layers)
+    h_out = h_out if h_out is not None else torch.empty_like(x)
+    V = 0 if codec_head is None else codec_head.shape[0]
+    if c0 is None and want_c0 and codec_head is not None:
+        c0 = torch.empty(T, dtype=torch.int32, device=dev)
+    lib = load_library()
+    c, a = cfg.c(), acfg.c()
+    need = int(lib.moe_talker_decode_workspace_size(ctypes.byref(c), ctypes.byref(a), T, V if c0 is not None else 0))
+    buf = ws if ws is not None else workspace(need, dev)
+    st = stream if stream is not None else _stream(dev)
+    _check("moe_talker_decode", lib.moe_talker_decode(
+        ctypes.byref(c), ctypes.byref(a), arr, len(arr), _ptr(x), T, _ptr(pos), _ptr(cache_len), _ptr(final_norm),
+        eps, _ptr(codec_head), V, _ptr(h_out), _ptr(xn_out), _ptr(c0), _ptr(buf), buf.numel(), st))
+    return h_out, xn_out, c0

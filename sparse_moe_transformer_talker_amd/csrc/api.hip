@@ -754,6 +754,74 @@ int moe_stack_forward(const moe_config* cfg, const moe_weights* layers, int32_t 
                                  moe_codec_head_workspace_size(cfg, V, T), stream);
 }
 
+size_t moe_talker_decode_workspace_size(const moe_config* cfg, const moe_attn_config* acfg, int64_t T, int32_t V) {
+    if (check_cfg(cfg) != MOE_OK || check_T(cfg, T) != MOE_OK || check_attn_cfg(acfg) != MOE_OK || V < 0 ||
+        T > 65535 || acfg->hidden_size != cfg->hidden_size || acfg->dtype != cfg->dtype)
+        return 0;
+    const int H = cfg->hidden_size;
+    Carver cv(nullptr);
+    for (int i = 0; i < 3; ++i) cv.take<char>(T * H * (int64_t)esize(cfg->dtype));
+    AttnPlan ap;
+    plan_attn(acfg, T, cv, ap);
+    cv.take<char>(layer_ws(cfg, T));
+    if (V > 0) cv.take<char>(moe_codec_head_workspace_size(cfg, V, T));
+    return cv.size();
+}
+
+int moe_talker_decode(const moe_config* cfg, const moe_attn_config* acfg, const moe_talker_layer* layers, int32_t L,
+                      const void* x, int64_t T, const int32_t* pos, const int32_t* cache_len, const float* final_norm,
+                      float eps, const void* codec_head, int32_t V, void* h_out, void* xn_out, int32_t* c0, void* ws,
+                      size_t ws_bytes, void* stream) {
+    int st = check_cfg(cfg);
+    if (st != MOE_OK) return st;
+    if ((st = check_T(cfg, T)) != MOE_OK) return st;
+    if ((st = check_attn_cfg(acfg)) != MOE_OK) return st;
+    if (acfg->hidden_size != cfg->hidden_size || acfg->dtype != cfg->dtype) return MOE_ERR_INVALID;
+    if (L < 1 || L > kMaxStackLayers || !layers || !(eps >= 0.0f) || V < 0) return MOE_ERR_INVALID;
+    if (T > 65535 || V > (1 << 20)) return MOE_ERR_UNSUPPORTED;
+    if (T == 0) return MOE_OK;
+    if (!ok_ptr(x) || !ok_ptr(pos) || !ok_ptr(cache_len) || !ok_ptr(h_out) || !ok_opt(xn_out) || !ok_opt(final_norm) ||
+        !ok_opt(codec_head) || !ok_opt(c0) || !ok_ptr(ws))
+        return MOE_ERR_INVALID;
+    if (c0 && (!codec_head || V < 1)) return MOE_ERR_INVALID;
+    if (xn_out && (xn_out == x || xn_out == h_out)) return MOE_ERR_INVALID;
+    if (ws_bytes < moe_talker_decode_workspace_size(cfg, acfg, T, c0 ? V : 0)) return MOE_ERR_WORKSPACE;
+    const int H = cfg->hidden_size;
+    Carver cv(ws);
+    void* xa = cv.take<char>(T * H * (int64_t)esize(cfg->dtype));    // attention input (normalised)
+    void* hmid = cv.take<char>(T * H * (int64_t)esize(cfg->dtype));  // after the attention's residual add
+    void* xm = cv.take<char>(T * H * (int64_t)esize(cfg->dtype));    // MoE input (normalised)
+    AttnPlan ap;
+    plan_attn(acfg, T, cv, ap);
+    void* lws = cv.take<char>(layer_ws(cfg, T));
+    void* hws = c0 ? cv.take<char>(moe_codec_head_workspace_size(cfg, V, T)) : nullptr;
+    void* xf = xn_out ? xn_out : xa;
+    for (int l = 0; l < L; ++l) {
+        const moe_talker_layer& ly = layers[l];
+        if ((st = check_layer_args(cfg, &ly.moe, xm, hmid, h_out, lws)) != MOE_OK) return st;
+        if (!ok_ptr(ly.attn.w_qkv) || !ok_ptr(ly.attn.q_norm) || !ok_ptr(ly.attn.k_norm) || !ok_ptr(ly.attn.w_o) ||
+            !ok_opt(ly.in_norm) || !ok_opt(ly.post_norm) || !ok_ptr(ly.k_cache) || !ok_ptr(ly.v_cache))
+            return MOE_ERR_INVALID;
+    }
+    hipStream_t s = as_stream(stream);
+    TMOE_TRY(launch_rmsnorm(cfg->dtype, x, layers[0].in_norm, eps, T, H, xa, s));
+    for (int l = 0; l < L; ++l) {
+        const moe_talker_layer& ly = layers[l];
+        int r = attn_run(acfg, &ly.attn, ap, xa, T, pos, cache_len, ly.k_cache, ly.v_cache, l == 0 ? x : h_out, hmid,
+                         ly.post_norm, eps, xm, s);
+        if (r != MOE_OK) return r;
+        LayerEnd end;
+        end.gain = l + 1 < L ? layers[l + 1].in_norm : final_norm;
+        end.eps = eps;
+        end.norm_out = l + 1 < L ? xa : xf;
+        r = layer_run(cfg, &ly.moe, xm, hmid, T, h_out, nullptr, nullptr, nullptr, lws, s, nullptr, end);
+        if (r != MOE_OK) return r;
+    }
+    if (!c0) return MOE_OK;
+    return moe_codec_head_argmax(cfg, xf, codec_head, V, T, nullptr, c0, hws, moe_codec_head_workspace_size(cfg, V, T),
+                                 stream);
+}
+
 int moe_rmsnorm(const moe_config* cfg, const void* x, const float* gain, float eps, int64_t T, void* out,
                 void* stream) {
     int st = check_cfg(cfg);

@@ -246,3 +246,32 @@ def test_predictor_config_and_argument_errors():
     assert call(T=100) == -2
     arr[3].down = None
     assert call() == -1                          # every layer checked before launching
+
+
+def test_talker_decode_argument_errors():
+    lib = api.load_library()
+    c = _cfg()
+    a = api.AttnConfig(max_len=1024).c()
+    n = lib.moe_talker_decode_workspace_size(ctypes.byref(c), ctypes.byref(a), 64, 3072)
+    assert n > lib.moe_workspace_size(ctypes.byref(c), 64) + lib.moe_attention_workspace_size(ctypes.byref(a), 64)
+    bad = api.AttnConfig(max_len=1024, hidden_size=2048).c()
+    assert lib.moe_talker_decode_workspace_size(ctypes.byref(c), ctypes.byref(bad), 64, 0) == 0  # hidden sizes differ
+    lay = api.moe_talker_layer(api.moe_weights(FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE),
+                               api.moe_attn_weights(FAKE, FAKE, FAKE, FAKE), None, None, FAKE, FAKE)
+    arr = (api.moe_talker_layer * 2)(lay, lay)
+
+    def call(**kw):
+        return lib.moe_talker_decode(ctypes.byref(c), ctypes.byref(a), kw.get("layers", arr), kw.get("L", 2),
+                                     kw.get("x", _p()), kw.get("T", 64), _p(1 << 20), _p(1 << 21), None,
+                                     ctypes.c_float(1e-6), kw.get("head", _p(1 << 22)), 3072, _p(1 << 24),
+                                     kw.get("xn", None), _p(1 << 26), _p(1 << 28), kw.get("ws", n), None)
+
+    assert call(L=0) == -1
+    assert call(layers=None) == -1
+    assert call(x=None) == -1
+    assert call(head=None) == -1          # c0 needs the head
+    assert call(xn=_p(1 << 24)) == -1     # xn_out may not alias h_out
+    assert call(ws=n - 256) == -3
+    assert call(T=0) == 0
+    arr[1].v_cache = None
+    assert call() == -1                   # every layer checked before launching

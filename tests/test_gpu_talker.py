@@ -1,0 +1,120 @@
+"""The Talker's decode step through whole decoder layers (attention, then MoE)
+through the C ABI.
+
+moe_talker_decode fuses each seam (the attention's residual add with the
+post-attention RMSNorm, the MoE combine's residual add with the next input
+RMSNorm).  It must equal moe_rmsnorm + moe_attention_decode (with norm_out) +
+moe_layer_forward + moe_rmsnorm called layer by layer, bit for bit: the outputs,
+the final-normed state, c_0 and every layer's caches.  Each of those calls is
+checked against the oracle by its own tests; here c_0 is also checked as the
+exact argmax of the oracle's codec_head logits on the final state.  Then the
+step captured as one graph and replayed.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_ref as R
+from sparse_moe_transformer_talker_amd import api
+from sparse_moe_transformer_talker_amd import inputs as INP
+from tests import gpu_helpers as G
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    api.load_library()
+
+
+def _vt(v):
+    return np.ascontiguousarray(np.swapaxes(v, 2, 3))
+
+
+def _setup(T, L, max_len, seed=100):
+    shape, ashape = INP.TALKER, INP.TALKER_ATTN
+    rng = np.random.default_rng(seed)
+    lens = INP.cache_lengths(T, max_len, seed)
+    layers = []
+    for l in range(L):
+        aw = INP.attention_weights(ashape, seed + l)
+        kv = INP.kv_cache(T, ashape, max_len, seed + l)
+        layers.append({
+            "moe": G.weights_dev(INP.layer_weights(shape, 30 + l, 0.02, "bf16"), "bf16"),
+            "attn": {"w_qkv": G.dev(aw["w_qkv"], "bf16"), "w_o": G.dev(aw["w_o"], "bf16"),
+                     "q_norm": torch.from_numpy(aw["q_norm"]).cuda(), "k_norm": torch.from_numpy(aw["k_norm"]).cuda()},
+            "in_norm": torch.from_numpy((1 + 0.1 * rng.standard_normal(shape.H)).astype(np.float32)).cuda(),
+            "post_norm": torch.from_numpy((1 + 0.1 * rng.standard_normal(shape.H)).astype(np.float32)).cuda(),
+            "k_cache": G.dev(kv["k"], "bf16"), "v_cache": G.dev(_vt(kv["v"]), "bf16")})
+    final = torch.from_numpy((1 + 0.1 * rng.standard_normal(shape.H)).astype(np.float32)).cuda()
+    head_np = INP.stack_weights(shape, 0, 30, 0.02, "bf16", 3072, 50)["codec_head"]
+    x = G.dev(INP.activations(T, shape.H, seed, "bf16"), "bf16")
+    ld = torch.from_numpy(lens).cuda()
+    pd = torch.from_numpy(INP.speech_positions(lens)).cuda()
+    return shape, layers, final, head_np, x, ld, pd
+
+
+def _clone_caches(layers):
+    return [dict(l, k_cache=l["k_cache"].clone(), v_cache=l["v_cache"].clone()) for l in layers]
+
+
+@pytest.mark.parametrize("T,L,max_len", [(64, 3, 512), (96, 2, 256), (7, 2, 128)])
+def test_talker_decode_matches_layer_by_layer(T, L, max_len):
+    shape, layers, final, head_np, x, ld, pd = _setup(T, L, max_len)
+    cfg = G.config(shape, "bf16")
+    acfg = api.AttnConfig(max_len=max_len)
+    head = G.dev(head_np, "bf16")
+    eps = 1e-6
+    ref_layers = _clone_caches(layers)
+    h = x
+    xa = api.moe_rmsnorm(cfg, x, ref_layers[0]["in_norm"], eps)
+    for l, ly in enumerate(ref_layers):
+        xm = torch.empty_like(x)
+        a = api.moe_attention_decode(acfg, ly["attn"], xa, pd, ld, ly["k_cache"], ly["v_cache"], residual=h,
+                                     norm_gain=ly["post_norm"], norm_eps=eps, norm_out=xm)
+        h = api.moe_layer_forward(cfg, ly["moe"], xm, a)
+        nxt = ref_layers[l + 1]["in_norm"] if l + 1 < L else final
+        xa = api.moe_rmsnorm(cfg, h, nxt, eps)
+    c0_ref, _ = api.moe_codec_head_argmax(cfg, xa, head)
+    xn = torch.empty_like(x)
+    h_out, _, c0 = api.moe_talker_decode(cfg, acfg, layers, x, pd, ld, final, eps, head, xn_out=xn)
+    torch.cuda.synchronize()
+    assert torch.equal(h_out.view(torch.int16), h.view(torch.int16))
+    assert torch.equal(xn.view(torch.int16), xa.view(torch.int16))
+    assert torch.equal(c0, c0_ref)
+    for l in range(L):
+        assert torch.equal(layers[l]["k_cache"].view(torch.int16), ref_layers[l]["k_cache"].view(torch.int16))
+        assert torch.equal(layers[l]["v_cache"].view(torch.int16), ref_layers[l]["v_cache"].view(torch.int16))
+    want = R.argmax_first(R.codec_head_logits(G.host64(xn), INP.to_f64(head_np, "bf16")))
+    np.testing.assert_array_equal(c0.cpu().numpy(), want)
+    print("talker decode T=%d L=%d: equal to layer-by-layer; c0 exact" % (T, L), flush=True)
+
+
+def test_talker_decode_graph_replay():
+    T, L, max_len = 64, 2, 256
+    shape, layers, final, head_np, x, ld, pd = _setup(T, L, max_len, seed=110)
+    cfg, acfg = G.config(shape, "bf16"), api.AttnConfig(max_len=max_len)
+    head = G.dev(head_np, "bf16")
+    dev = torch.device("cuda", 0)
+    ws = api.workspace(api.moe_talker_decode_workspace_size(cfg, acfg, T, 3072), dev)
+    arr = api.talker_layers_struct(layers)
+    h_e, _, c0_e = api.moe_talker_decode(cfg, acfg, arr, x, pd, ld, final, 1e-6, head, ws=ws)
+    h_e, c0_e = h_e.clone(), c0_e.clone()
+    torch.cuda.synchronize()
+    h_g, c0_g = torch.empty_like(x), torch.empty(T, dtype=torch.int32, device=dev)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        api.moe_talker_decode(cfg, acfg, arr, x, pd, ld, final, 1e-6, head, h_out=h_g, c0=c0_g, ws=ws)
+    x2 = G.dev(INP.activations(T, shape.H, 111, "bf16"), "bf16")
+    other = _clone_caches(layers)
+    for rep in range(3):
+        api.moe_talker_decode(cfg, acfg, other, x2, pd, ld, final, 1e-6, head)  # eager work between replays
+        torch.cuda.synchronize()
+        h_g.zero_()
+        c0_g.fill_(-1)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(h_g.view(torch.int16), h_e.view(torch.int16)), "replay %d differs" % rep
+        assert torch.equal(c0_g, c0_e)
