@@ -347,7 +347,14 @@ def measure_talker_frame(api, torch, INP, shape, T, ctx, weight_sets, L, frames,
     stop.record()
     torch.cuda.synchronize()
     us = start.elapsed_time(stop) * 1e3 / frames
+    touched = 124  # experts a T=64 batch touches (the decode measurement's count for these weight sets)
+    moe_b = touched * 3 * shape.I * shape.H * 2 + 3 * shape.Is * shape.H * 2 + shape.E * shape.H * 2
+    attn_b = T * ashape.n_kv_heads * max_len * ashape.head_dim * 4 + (
+        (ashape.n_heads + 2 * ashape.n_kv_heads) * ashape.head_dim * shape.H + shape.H * ashape.n_heads *
+        ashape.head_dim) * 2
+    alg = L * (moe_b + attn_b) + vocab * shape.H * 2
     return {"workload": "talker_decode_frame_%dlayers_T%d_ctx%d" % (L, T, max_len), "layers": L, "streams": T,
+            "bytes_per_frame": alg, "hbm_frac": alg / (us * 1e-6) / (HBM_PEAK_GBS * 1e9),
             "positions": max_len, "frame_us": us, "per_layer_us": us / L, "tokens_per_s": T / (us * 1e-6),
             "timing": "one HIP graph per frame: per layer attention (+ residual, post-attention norm) and MoE "
                       "(+ residual, next norm), then the codec head argmax"}
@@ -383,19 +390,90 @@ def measure_predictor(api, torch, INP, T, frames):
     torch.cuda.synchronize()
     us = start.elapsed_time(stop) * 1e3 / frames
     layer_bytes = sum(v.numel() * v.element_size() for lw in wd["layers"] for v in lw.values())
+    head_bytes = (shape.num_codes - 1) * shape.codebook * shape.H * 2
+    alg = shape.num_codes * layer_bytes + head_bytes + shape.num_codes * T * shape.H * 2
     return {"workload": "depth_code_predictor_frame_T%d" % T, "streams": T, "positions": shape.num_codes,
+            "bytes_per_frame": alg, "hbm_frac": alg / (us * 1e-6) / (HBM_PEAK_GBS * 1e9),
+            "bytes_note": "every position reads every layer's weights once (the steps are sequential), each head once",
             "layers": shape.layers, "frame_us": us, "position_us": us / shape.num_codes,
             "codes_per_s": T * (shape.num_codes - 1) / (us * 1e-6), "layer_weight_bytes": layer_bytes,
             "timing": "one HIP graph per frame: 16 positions x 5 layers (attention + SwiGLU) and 15 heads"}
 
 
-def cpu_baseline(INP, shape, T, seconds):
-    from oracle import moe_ref as R
+def blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+        return max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
     except Exception:  # noqa: BLE001
-        threads = 1
+        return 1
+
+
+def oracle_rate(fn, units, unit, seconds, sample):
+    """Oracle baseline: fn() repeated for about `seconds` (the first call untimed); units per call."""
+    fn()
+    n, t0 = 0, time.perf_counter()
+    while True:
+        fn()
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": units * n / el, "unit": unit, "cores": blas_threads(), "kind": "oracle",
+            "sample": "%s; %d calls in %.1f s" % (sample, n, el)}
+
+
+def oracle_baselines(INP, shape, seconds):
+    """Bounded oracle timings beside the attention step, the Talker frame, the predictor and sampling."""
+    from oracle import attention_ref as A
+    from oracle import moe_ref as R
+    from oracle import predictor_ref as P
+    out = {}
+    ash = INP.TALKER_ATTN
+    aw = INP.attention_weights(ash, 60)
+    aw64 = {k: (INP.to_f64(v, "bf16") if v.dtype == np.uint16 else v.astype(np.float64)) for k, v in aw.items()}
+
+    def attn_inputs(T, ctx):
+        kv = INP.kv_cache(T, ash, ctx + 1, 61)
+        lens = np.full(T, ctx, np.int32)
+        return (INP.to_f64(INP.activations(T, ash.H, 62, "bf16"), "bf16"), INP.speech_positions(lens),
+                INP.to_f64(kv["k"], "bf16"), INP.to_f64(kv["v"], "bf16"), lens)
+
+    x, pos, kc, vc, lens = attn_inputs(64, 1023)
+    out["attention"] = oracle_rate(lambda: A.attention_decode(x, aw64, pos, kc, vc, lens, ash.n_heads, ash.n_kv_heads),
+                                   64, "tokens/s", seconds, "fp64 numpy oracle, one attention step, 64 streams x "
+                                   "1024 positions")
+    x8, pos8, kc8, vc8, lens8 = attn_inputs(8, 1023)
+    w = INP.layer_weights(shape, 30, 0.02, "bf16")
+    w64 = {k: INP.to_f64(v, "bf16") for k, v in w.items()}
+
+    def talker_layer():
+        a = A.attention_decode(R.rmsnorm(x8, np.ones(shape.H)), aw64, pos8, kc8, vc8, lens8,
+                               ash.n_heads, ash.n_kv_heads)["y"] + x8
+        return a + R.moe_layer(R.rmsnorm(a, np.ones(shape.H)), w64, shape.k)["y"]
+
+    out["talker_frame"] = oracle_rate(talker_layer, 8, "tokens x layers/s", seconds,
+                                      "fp64 numpy oracle, one Talker decoder layer (attention over 1024 positions, "
+                                      "then the MoE), 8 streams")
+    ps = INP.PREDICTOR
+    pw = INP.predictor_weights(ps, 80)
+    f64 = lambda a: INP.to_f64(a, "bf16") if a.dtype == np.uint16 else a.astype(np.float64)
+    pw64 = {k: f64(v) for k, v in pw.items() if k != "layers"}
+    pw64["layers"] = [{k: f64(v) for k, v in lw.items()} for lw in pw["layers"]]
+    h4 = INP.to_f64(INP.activations(4, ps.H, 81, "bf16"), "bf16")
+    c04 = np.arange(4) * 7
+    out["predictor"] = oracle_rate(lambda: P.predictor_frame(h4, c04, pw64), 4 * (ps.num_codes - 1), "codes/s",
+                                   seconds, "fp64 numpy oracle, one predictor frame, 4 streams")
+    head = INP.to_f64(INP.stack_weights(shape, 0, 30, 0.02, "bf16", 3072, 50)["codec_head"], "bf16")
+    xs = INP.to_f64(INP.activations(64, shape.H, 40, "bf16"), "bf16")
+    u = np.random.default_rng(41).random(64)
+    out["sampling"] = oracle_rate(lambda: R.sample_inverse_cdf(R.codec_head_logits(xs, head), u), 64, "tokens/s",
+                                  seconds, "fp64 numpy oracle, codec head + inverse-transform draw, 64 tokens")
+    return out
+
+
+def cpu_baseline(INP, shape, T, seconds):
+    from oracle import moe_ref as R
+    threads = blas_threads()
     w = INP.layer_weights(shape, 30, 0.02, "bf16")
     w64 = {k: INP.to_f64(v, "bf16") for k, v in w.items()}
     x64 = INP.to_f64(INP.activations(T, shape.H, 30, "bf16"), "bf16")
@@ -524,6 +602,12 @@ def main():
         log("cpu baseline (oracle, ~%.0f s)" % args.cpu_seconds)
         cpu = cpu_baseline(INP, shape, 64, args.cpu_seconds)
 
+    extra_cpu = None
+    if not args.no_cpu_baseline and (attn or tframe or pred):
+        log("oracle baselines for attention, the Talker frame, the predictor and sampling (~%.0f s each)"
+            % (args.cpu_seconds / 3))
+        extra_cpu = oracle_baselines(INP, shape, args.cpu_seconds / 3)
+
     g = dec["gate_up"]
     line = {
         "metric": METRIC,
@@ -564,6 +648,11 @@ def main():
         line["predictor"] = pred
     if tframe is not None:
         line["talker_frame"] = tframe
+    if extra_cpu is not None:
+        for key in ("attention", "predictor", "talker_frame"):
+            if key in line:
+                line[key]["cpu_baseline"] = extra_cpu[key]
+        line.setdefault("stack", {})["sampling_cpu_baseline"] = extra_cpu["sampling"]
     if pre is not None:
         gp = pre["gate_up"]
         line["prefill"] = {"workload": "talker_moe_layer_prefill_T4096", "tokens_per_s": pre["tokens_per_s"],
