@@ -324,8 +324,8 @@ int check_attn_cfg(const moe_attn_config* a) {
 struct PredPlan {
     moe_attn_config acfg;  // the layers' attention over the frame's positions
     AttnPlan ap;
-    int ksgu = 0, ksd = 0;
-    float *pgu, *pd, *sc, *bd;
+    int ksd = 0;
+    float *pd, *sc, *bd;
     void *h, *X, *Hh, *XN, *HN;
     char *kc, *vc;
     size_t cache_bytes;  // per layer, each of K and V
@@ -346,7 +346,7 @@ int check_pred_cfg(const moe_predictor_config* c, int64_t T) {
     if (st != MOE_OK) return st;
     const int H = a.hidden_size, I = c->intermediate_size;
     if (c->num_layers > 256 || c->num_codes > 256 || c->codebook_size > (1 << 20) || I % 16) return MOE_ERR_UNSUPPORTED;
-    if (T < 1 || T > 64 || !skinny_gemm_runs(T, 2 * I, H) || !skinny_gemm_runs(T, H, I) ||
+    if (T < 1 || T > 64 || !skinny_swiglu_ok(T, I, H) || !skinny_gemm_runs(T, H, I) ||
         !skinny_gemm_runs(T, (a.num_heads + 2 * a.num_kv_heads) * a.head_dim, H) ||
         !skinny_gemm_runs(T, H, a.num_heads * a.head_dim))
         return MOE_ERR_UNSUPPORTED;
@@ -356,9 +356,7 @@ void plan_pred(const moe_predictor_config* c, int64_t T, Carver& cv, PredPlan& p
     p.acfg = pred_attn_cfg(c);
     const int H = p.acfg.hidden_size, I = c->intermediate_size, K = c->codebook_size, P = c->num_codes;
     plan_attn(&p.acfg, T, cv, p.ap);
-    p.ksgu = skinny_gemm_runs(T, 2 * I, H);
     p.ksd = skinny_gemm_runs(T, H, I);
-    p.pgu = cv.take<float>((int64_t)p.ksgu * T * 2 * I);
     p.pd = cv.take<float>((int64_t)p.ksd * T * H);
     p.h = cv.take<char>(T * (int64_t)I * 2);
     p.X = cv.take<char>(T * (int64_t)H * 2);
@@ -939,8 +937,7 @@ int moe_predictor_frame(const moe_predictor_config* cfg, const moe_predictor_wei
                                    p.kc + l * p.cache_bytes, p.vc + l * p.cache_bytes, l == 0 ? src : p.X, p.Hh,
                                    ly.post_norm, eps, p.HN, s);
             if (r != MOE_OK) return r;
-            TMOE_TRY(launch_skinny_gemm(p.HN, ly.gate, p.pgu, T, 2 * I, H, p.ksgu, s, ly.up, I));
-            TMOE_TRY(launch_swiglu_partials(p.pgu, p.ksgu, T, I, p.h, s));
+            TMOE_TRY(launch_skinny_swiglu(p.HN, ly.gate, ly.up, p.h, T, I, H, s));
             TMOE_TRY(launch_skinny_gemm(p.h, ly.down, p.pd, T, H, I, p.ksd, s));
             const bool last = l + 1 == L;
             const float* next = last ? w->final_norm : w->layers[l + 1].in_norm;

@@ -163,7 +163,9 @@ __global__ __launch_bounds__(128) void attn_out_kernel(const float* __restrict__
 //   cache (8 consecutive positions of one dimension per lane; positions past
 //   the end are zeroed, so stale cache contents never reach the sum).
 // The waves' (max, sum, output) merge in LDS.  Writes the chunk's max m, sum l
-// and unnormalised output per head; an empty chunk writes m = -inf, l = 0.
+// and unnormalised output per head; an empty chunk writes m = -inf, l = 0.  When
+// the cache is a single chunk (nch == 1) the workgroup writes the normalised
+// output od [T, nq, 128] instead (zeros for a stream with no valid position).
 template <int G>
 __global__ __launch_bounds__(64 * kAttnWaves) void attn_partial_kernel(const bf16_t* __restrict__ q,
                                                                        const bf16_t* __restrict__ kc,
@@ -171,7 +173,8 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_partial_kernel(const bf1
                                                                        const int32_t* __restrict__ len, int nkv,
                                                                        int max_len, int nch, float* __restrict__ pm,
                                                                        float* __restrict__ pl,
-                                                                       float* __restrict__ pacc) {
+                                                                       float* __restrict__ pacc,
+                                                                       bf16_t* __restrict__ od) {
     __shared__ float red_m[kAttnWaves][16], red_l[kAttnWaves][16];
     __shared__ float red_acc[kAttnWaves][G][kHead];
     __shared__ __attribute__((aligned(16))) bf16_t pbuf[kAttnWaves][16][40];  // rows padded to 80 bytes
@@ -183,14 +186,16 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_partial_kernel(const bf1
     const int n = (nraw >= 0 && nraw < max_len) ? nraw + 1 : 0;
     const int64_t pidx = (t * nkv + g) * nch + c;
     const int k0 = c * kChunk;
+    const int nq = nkv * G;
     if (k0 >= n) {  // block-uniform
-        if (threadIdx.x < G) {
+        if (nch == 1) {
+            for (int i = threadIdx.x; i < G * kHead; i += 64 * kAttnWaves) od[(t * nq + g * G) * kHead + i] = 0;
+        } else if (threadIdx.x < G) {
             pm[pidx * G + threadIdx.x] = -INFINITY;
             pl[pidx * G + threadIdx.x] = 0.f;
         }
         return;
     }
-    const int nq = nkv * G;
     const int key0 = k0 + wave * kKeysPerWave;
     const f32x4 zero = {0, 0, 0, 0};
     float m_r[4], l_r[4];
@@ -305,6 +310,10 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_partial_kernel(const bf1
             const float f = red_m[w][j] == -INFINITY ? 0.f : __expf(red_m[w][j] - mx);
             a = fmaf(red_acc[w][j][dd], f, a);
             ls = fmaf(red_l[w][j], f, ls);
+        }
+        if (nch == 1) {  // the only chunk: the output itself
+            od[(t * nq + g * G + j) * kHead + dd] = f32_to_bf16(a / ls);
+            continue;
         }
         pacc[(pidx * G + j) * kHead + dd] = a;
         if (dd == 0) {
@@ -421,12 +430,13 @@ hipError_t launch_attn_decode(const void* q, const void* kc, const void* vc, con
     dim3 grid((unsigned)nch, (unsigned)nkv, (unsigned)T);
     const int G = nq / nkv;
     const bf16_t *qb = (const bf16_t*)q, *kb = (const bf16_t*)kc, *vb = (const bf16_t*)vc;
-    if (G == 8) attn_partial_kernel<8><<<grid, 64 * kAttnWaves, 0, st>>>(qb, kb, vb, len, nkv, max_len, nch, pm, pl, pacc);
-    else if (G == 4) attn_partial_kernel<4><<<grid, 64 * kAttnWaves, 0, st>>>(qb, kb, vb, len, nkv, max_len, nch, pm, pl, pacc);
-    else if (G == 2) attn_partial_kernel<2><<<grid, 64 * kAttnWaves, 0, st>>>(qb, kb, vb, len, nkv, max_len, nch, pm, pl, pacc);
-    else attn_partial_kernel<1><<<grid, 64 * kAttnWaves, 0, st>>>(qb, kb, vb, len, nkv, max_len, nch, pm, pl, pacc);
+    bf16_t* ob = (bf16_t*)o;
+    if (G == 8) attn_partial_kernel<8><<<grid, 64 * kAttnWaves, 0, st>>>(qb, kb, vb, len, nkv, max_len, nch, pm, pl, pacc, ob);
+    else if (G == 4) attn_partial_kernel<4><<<grid, 64 * kAttnWaves, 0, st>>>(qb, kb, vb, len, nkv, max_len, nch, pm, pl, pacc, ob);
+    else if (G == 2) attn_partial_kernel<2><<<grid, 64 * kAttnWaves, 0, st>>>(qb, kb, vb, len, nkv, max_len, nch, pm, pl, pacc, ob);
+    else attn_partial_kernel<1><<<grid, 64 * kAttnWaves, 0, st>>>(qb, kb, vb, len, nkv, max_len, nch, pm, pl, pacc, ob);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess || nch == 1) return e;  // a single chunk wrote the output itself
     attn_combine_kernel<<<dim3((unsigned)nq, (unsigned)T), kHead, 0, st>>>(pm, pl, pacc, len, nq, nkv, max_len, nch,
                                                                           (bf16_t*)o);
     return hipGetLastError();

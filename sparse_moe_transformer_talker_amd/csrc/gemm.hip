@@ -668,18 +668,22 @@ hipError_t launch_grouped_gemm_direct(int pass, const GemmArgs& args, hipStream_
 namespace {
 constexpr int kSkinnyRows = 64;
 constexpr int kSkinnyWaves = 4;
-template <int NW, int U>
+// SWIGLU: a workgroup's 16 columns are gate rows f .. f + 7 (of W) and up rows
+// f .. f + 7 (of W2) for the 8 features f = 8 blockIdx.x ..; with the whole K in
+// one run it stores h [M, N / 2] = SiLU(gate) * up in bf16 instead of partials.
+template <int NW, int U, bool SWIGLU>
 __global__ __launch_bounds__(64 * NW) void skinny_gemm_kernel(const bf16_t* __restrict__ A,
                                                               const bf16_t* __restrict__ W,
-                                                              const bf16_t* __restrict__ W2, int N1,
-                                                              float* __restrict__ P, int M, int N, int K, int KS) {
+                                                              const bf16_t* __restrict__ W2,
+                                                              float* __restrict__ P, bf16_t* __restrict__ h, int M,
+                                                              int N, int K, int KS) {
     __shared__ float part[NW][kSkinnyRows][17];
     const int wave = (int)(threadIdx.x >> 6), lane = lane_id();
     const int n0 = blockIdx.x * 16, run = blockIdx.y;
     const int r = lane & 15, kg = (lane >> 4) * 8;
     const int kw = K / KS / NW, kb = run * (K / KS) + wave * kw;
-    // output columns from N1 on take their rows from W2 (two matrices side by side)
-    const bf16_t* wp = (n0 < N1 ? W + (int64_t)(n0 + r) * K : W2 + (int64_t)(n0 - N1 + r) * K) + kb + kg;
+    const bf16_t* wp = (SWIGLU ? (r < 8 ? W + (int64_t)(n0 / 2 + r) * K : W2 + (int64_t)(n0 / 2 + r - 8) * K)
+                               : W + (int64_t)(n0 + r) * K) + kb + kg;
     const bf16_t* ap[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) ap[mt] = A + (int64_t)min(mt * 16 + r, M - 1) * K + kb + kg;
@@ -709,6 +713,20 @@ __global__ __launch_bounds__(64 * NW) void skinny_gemm_kernel(const bf16_t* __re
 #pragma unroll
         for (int i = 0; i < 4; ++i) part[wave][mt * 16 + 4 * (lane >> 4) + i][r] = acc[mt][i];
     __syncthreads();
+    if (SWIGLU) {
+        for (int idx = threadIdx.x; idx < kSkinnyRows * 8; idx += 64 * NW) {
+            const int row = idx >> 3, c = idx & 7;
+            if (row >= M) continue;
+            float gv = part[0][row][c], uv = part[0][row][c + 8];
+#pragma unroll
+            for (int w = 1; w < NW; ++w) {
+                gv += part[w][row][c];
+                uv += part[w][row][c + 8];
+            }
+            h[(int64_t)row * (N / 2) + n0 / 2 + c] = f32_to_bf16(silu(gv) * uv);
+        }
+        return;
+    }
     float* out = P + (int64_t)run * M * N;
     for (int idx = threadIdx.x; idx < kSkinnyRows * 16; idx += 64 * NW) {
         const int row = idx >> 4, col = idx & 15;
@@ -730,46 +748,21 @@ int skinny_gemm_runs(int64_t M, int N, int K) {
 }
 
 hipError_t launch_skinny_gemm(const void* A, const void* W, float* P, int64_t M, int N, int K, int KS,
-                              hipStream_t st, const void* W2, int N1) {
-    if (!W2) N1 = N;
+                              hipStream_t st) {
     dim3 grid((unsigned)(N / 16), (unsigned)KS);
-    skinny_gemm_kernel<kSkinnyWaves, 4><<<grid, 64 * kSkinnyWaves, 0, st>>>(
-        (const bf16_t*)A, (const bf16_t*)W, (const bf16_t*)W2, N1, P, (int)M, N, K, KS);
+    skinny_gemm_kernel<kSkinnyWaves, 4, false><<<grid, 64 * kSkinnyWaves, 0, st>>>(
+        (const bf16_t*)A, (const bf16_t*)W, nullptr, P, nullptr, (int)M, N, K, KS);
     return hipGetLastError();
 }
 
-// h [M, I] = SiLU(g) * u with g, u the sums (in run order) of the KS partial
-// rows [KS][M][2 I] of a gate | up product; 8 features per thread.
-__global__ __launch_bounds__(256) void swiglu_partials_kernel(const float* __restrict__ P, int KS, int M, int I,
-                                                              bf16_t* __restrict__ h) {
-    const int64_t i8 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
-    if (i8 >= (int64_t)M * I) return;
-    const int64_t row = i8 / I, c = i8 % I;
-    const int64_t ld = 2 * (int64_t)I;
-    float g[8], u[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) g[e] = u[e] = 0.f;
-    for (int s = 0; s < KS; ++s) {
-        const float* pr = P + ((int64_t)s * M + row) * ld + c;
-        const f32x4 g0 = *reinterpret_cast<const f32x4*>(pr), g1 = *reinterpret_cast<const f32x4*>(pr + 4);
-        const f32x4 u0 = *reinterpret_cast<const f32x4*>(pr + I), u1 = *reinterpret_cast<const f32x4*>(pr + I + 4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            g[e] += g0[e];
-            g[4 + e] += g1[e];
-            u[e] += u0[e];
-            u[4 + e] += u1[e];
-        }
-    }
-    u32x4 o;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(silu(g[2 * q]) * u[2 * q], silu(g[2 * q + 1]) * u[2 * q + 1]);
-    *reinterpret_cast<u32x4*>(h + row * I + c) = o;
+bool skinny_swiglu_ok(int64_t M, int I, int K) {
+    return M >= 1 && M <= kSkinnyRows && I >= 8 && I % 8 == 0 && K % (32 * kSkinnyWaves) == 0;
 }
 
-hipError_t launch_swiglu_partials(const float* P, int KS, int64_t M, int I, void* h, hipStream_t st) {
-    const int64_t n8 = M * I / 8;
-    swiglu_partials_kernel<<<(unsigned)((n8 + 255) / 256), 256, 0, st>>>(P, KS, (int)M, I, (bf16_t*)h);
+hipError_t launch_skinny_swiglu(const void* A, const void* Wg, const void* Wu, void* h, int64_t M, int I, int K,
+                                hipStream_t st) {
+    skinny_gemm_kernel<kSkinnyWaves, 4, true><<<(unsigned)(I / 8), 64 * kSkinnyWaves, 0, st>>>(
+        (const bf16_t*)A, (const bf16_t*)Wg, (const bf16_t*)Wu, nullptr, (bf16_t*)h, (int)M, 2 * I, K, 1);
     return hipGetLastError();
 }
 

@@ -143,11 +143,13 @@ hipError_t launch_grouped_gemm_direct(int pass, const GemmArgs& args, hipStream_
 // s-th of KS equal runs of K; bf16 inputs, M <= 64, N % 16 == 0.  KS from
 // skinny_gemm_runs (0: the shape does not fit).
 int skinny_gemm_runs(int64_t M, int N, int K);
-// (W2, N1: output columns N1.. read rows of W2, so gate | up run as one product)
 hipError_t launch_skinny_gemm(const void* A, const void* W, float* P, int64_t M, int N, int K, int KS,
-                              hipStream_t st, const void* W2 = nullptr, int N1 = 0);
-// h [M, I] bf16 = SiLU(gate) * up from KS partials [KS][M][2 I] (gate columns first); I % 8 == 0
-hipError_t launch_swiglu_partials(const float* P, int KS, int64_t M, int I, void* h, hipStream_t st);
+                              hipStream_t st);
+// h [M, I] bf16 = SiLU(A Wg^T) * (A Wu^T) for M <= 64 (Wg, Wu [I, K]; I % 8 == 0,
+// K % 128 == 0), in one launch without partials
+bool skinny_swiglu_ok(int64_t M, int I, int K);
+hipError_t launch_skinny_swiglu(const void* A, const void* Wg, const void* Wu, void* h, int64_t M, int I, int K,
+                                hipStream_t st);
 // Portable path: one thread per output; rows of group 0 find their expert in offsets.
 hipError_t launch_gemm_generic(int dtype, int pass, const GemmGroup& g, const int32_t* offsets, int n_groups_rows,
                                int E, int64_t rows, hipStream_t st);
