@@ -16,7 +16,17 @@ Draw recipe (ours; the pages fix no seeds beyond the lab's seed 30):
     order router [E,H], gate [E,I,H], up [E,I,H], down [E,H,I], shared gate [Is,H],
     shared up [Is,H], shared down [H,Is], each ``standard_normal(float32) * sigma``;
   * activations: ``default_rng(s + 10000)``, ``standard_normal(float32)`` of [T,H];
-  * bf16 tensors are the fp32 draw rounded to nearest even.
+  * bf16 tensors are the fp32 draw rounded to nearest even;
+  * attention ("3C" §1: 16 query / 2 KV heads of 128): ``default_rng(s + 20000)``
+    draws w_qkv [(16 + 4) 128, H] then w_o [H, 2048] (sigma 0.02), then the q_norm /
+    k_norm gains 1 + N(0, 0.1); caches ``default_rng(s + 30000)``: keys N(0, 1), values
+    N(0, 0.64) of [T, n_kv, max_len, 128]; cache lengths ``default_rng(s + 40000)``
+    uniform over [0, max_len); speech positions repeat the length on all three
+    TM-RoPE axes;
+  * code predictor ("用 print(model) 认识 Qwen3-TTS": 5 layers, 16 / 8 heads, SwiGLU
+    3072, 15 tables and heads of 2048): ``default_rng(s + 50000)`` draws, per layer,
+    the two norm gains, w_qkv, w_o, q/k gains, gate, up, down, then the final gain,
+    the c_0 table [3072, H] and the 15 tables (N(0, 1)), then the 15 heads (sigma 0.02).
 """
 from __future__ import annotations
 
