@@ -8,7 +8,7 @@ bf16 bars; every other cache entry must be unchanged bit for bit.  The value
 cache is transposed in the library ([T, nkv, head_dim, max_len]).  Cases: random
 lengths up to 1024 (T = 64), ragged chunks and lengths 0 / 1 / 127 / 128 / 129 /
 max_len - 1 (T = 37, max_len = 320), 3D positions with distinct T/H/W indices,
-long caches (max_len 4096), the 16/8 head split, the fused RMSNorm of y, a batch of 96
+long caches (max_len 4096 and 32768), the 16/8 head split, the fused RMSNorm of y, a batch of 96
 streams (the grouped GEMM path for the projections), streams
 whose length is out of range, and a captured graph replayed.
 """
@@ -167,3 +167,11 @@ def test_attention_decode_batch_above_64():
     T, L = 96, 256
     w, kv, x, res, lens, pos = _case(T, L, INP.cache_lengths(T, L, 69))
     _check(INP.TALKER_ATTN, L, w, kv, x, res, lens, pos, "T=96", norm=True)
+
+
+def test_attention_decode_very_long_cache():
+    # 32768-position caches (256 chunks per stream and KV head)
+    T, L = 3, 32768
+    lens = np.array([L - 1, 20000, 129], np.int32)
+    w, kv, x, res, lens, pos = _case(T, L, lens)
+    _check(INP.TALKER_ATTN, L, w, kv, x, res, lens, pos, "32k cache")

@@ -4,7 +4,9 @@ Bars: expert indices, per-expert counts and the grouping are bit-exact (ties go
 to the lower expert index); bf16 outputs within max-abs 2e-2 and relative L2
 1e-2; fp32 lab-scale outputs within 1e-5.  Inputs are the seeded synthetic
 workloads (decode T=64, prefill T=4096, Zipf-skewed T=8192, lab scale) plus odd
-shapes that take the portable kernels, ragged tails and degenerate cases.
+shapes that take the portable kernels, ragged tails and degenerate cases, and a
+262144-token batch checked on sampled tokens (the oracle's tokens are
+independent).
 """
 import numpy as np
 import pytest
@@ -265,3 +267,22 @@ def test_empty_batch(talker):
     idx, w, _ = api.moe_route(cfg, x, talker.wd["router"])
     torch.cuda.synchronize()
     assert y.shape == (0, 1024) and idx.shape == (0, 6)
+
+
+def test_layer_largest_batch_sampled(talker):
+    # 262144 tokens (1.57 M token-expert pairs): every token goes through the whole
+    # layer; the oracle (tokens are independent) checks routing bit for bit and the
+    # outputs within the bars on a sample, and the counts must account for every pair
+    T = 262144
+    shape = talker.shape
+    x_np = talker.x(T, seed=12)
+    cfg = G.config(shape, "bf16")
+    idx = torch.empty((T, shape.k), dtype=torch.int32, device="cuda")
+    counts = torch.empty(shape.E, dtype=torch.int32, device="cuda")
+    y = api.moe_layer_forward(cfg, talker.wd, G.dev(x_np, "bf16"), topk_idx=idx, counts=counts)
+    torch.cuda.synchronize()
+    assert int(counts.sum().item()) == T * shape.k and int(counts.min().item()) >= 0
+    sample = np.unique(np.concatenate([[0, T - 1], np.random.default_rng(13).choice(T, 126, replace=False)]))
+    ref = R.moe_layer(INP.to_f64(x_np[sample], "bf16"), talker.w64, shape.k)
+    np.testing.assert_array_equal(idx.cpu().numpy()[sample], ref["idx"])
+    G.assert_close(G.host64(y)[sample], ref["y"], "bf16", "T=%d sampled" % T)
