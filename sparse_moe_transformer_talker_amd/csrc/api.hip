@@ -224,8 +224,7 @@ int run_gemm_pass(const moe_config* c, const GemmPlan& plan, int pass, const Gem
 }
 
 GemmGroup group(const void* wa, const void* wb, int64_t estride, int N, int K, const void* a, int64_t a_ld,
-                const int32_t* a_rows, void* out, int64_t out_ld, const int32_t* out_rows, int mul, int add,
-                const float* scale) {
+                const int32_t* a_rows, void* out, int64_t out_ld, const int32_t* out_rows, int mul, int add) {
     GemmGroup g{};
     g.wa = wa;
     g.wb = wb;
@@ -241,7 +240,6 @@ GemmGroup group(const void* wa, const void* wb, int64_t estride, int N, int K, c
     g.out_rows = out_rows;
     g.out_mul = mul;
     g.out_add = add;
-    g.out_scale = scale;
     return g;
 }
 
@@ -269,7 +267,7 @@ void plan_dense(const moe_config* c, int64_t T, Carver& cv, GemmPlan& g) { plan_
 int run_dense(const moe_config* c, const GemmPlan& plan, const void* A, const void* W, void* C, int64_t T, hipStream_t s) {
     const int N = c->hidden_size, K = c->shared_expert_intermediate_size;
     if (plan.mfma) TMOE_TRY(launch_build_items(nullptr, 0, T, &plan.t[0], &plan.t[1], s));
-    const GemmGroup dn = group(W, nullptr, 0, N, K, A, K, nullptr, C, N, nullptr, 1, 0, nullptr);
+    const GemmGroup dn = group(W, nullptr, 0, N, K, A, K, nullptr, C, N, nullptr, 1, 0);
     return run_gemm_pass(c, plan, 1, no_group(), dn, nullptr, 0, T, s);
 }
 
@@ -398,8 +396,8 @@ int attn_run(const moe_attn_config* cfg, const moe_attn_weights* w, const AttnPl
     const int r = run_dense(&p.co, p.go, p.o, w->w_o, p.ao, T, s);
     if (r != MOE_OK) return r;
     if (norm_out)
-        return hip_status(launch_combine_norm(cfg->dtype, nullptr, 0, 0, p.ao, H, residual, y, T, H, norm_gain,
-                                              norm_eps, norm_out, s));
+        return hip_status(launch_combine_norm(cfg->dtype, nullptr, nullptr, 0, 0, p.ao, H, residual, y, T, H,
+                                              norm_gain, norm_eps, norm_out, s));
     return hip_status(launch_combine(cfg->dtype, nullptr, nullptr, nullptr, 0, 0, p.ao, H, residual, y, T, H, s));
 }
 
@@ -411,12 +409,16 @@ struct LayerEnd {
     void* norm_out = nullptr;     // null: plain combine
 };
 
-hipError_t finish_layer(int dtype, const void* ybuf, int k, int slots, const void* shared, int64_t sstride,
-                        const void* residual, void* y, int64_t T, int H, const LayerEnd& end, hipStream_t s) {
+// The layer's combine: slot j < k of token t (an unweighted expert output) times
+// w[t * k + j], the shared slot, the residual; then the next pre-norm when
+// end.norm_out is set.
+hipError_t finish_layer(int dtype, const void* ybuf, const float* w, int k, int slots, const void* shared,
+                        int64_t sstride, const void* residual, void* y, int64_t T, int H, const LayerEnd& end,
+                        hipStream_t s) {
     if (end.norm_out)
-        return launch_combine_norm(dtype, ybuf, k, slots, shared, sstride, residual, y, T, H, end.gain, end.eps,
+        return launch_combine_norm(dtype, ybuf, w, k, slots, shared, sstride, residual, y, T, H, end.gain, end.eps,
                                    end.norm_out, s);
-    return launch_combine(dtype, ybuf, nullptr, nullptr, k, slots, shared, sstride, residual, y, T, H, s);
+    return launch_combine(dtype, ybuf, nullptr, w, k, slots, shared, sstride, residual, y, T, H, s);
 }
 
 int check_layer_args(const moe_config* cfg, const moe_weights* w, const void* x, const void* residual,
@@ -468,9 +470,9 @@ int layer_run(const moe_config* cfg, const moe_weights* w, const void* x, const 
         a.direct_nb = (int)nb_of(T);
         a.direct_counts = counts;
         a.direct_T = (int)T;
-        a.g[0] = group(w->gate, w->up, (int64_t)I * H, I, H, x, H, nullptr, p.hd, I, nullptr, 1, 0, nullptr);
+        a.g[0] = group(w->gate, w->up, (int64_t)I * H, I, H, x, H, nullptr, p.hd, I, nullptr, 1, 0);
         a.g[0].a_div = k;
-        a.g[1] = Is > 0 ? group(w->shared_gate, w->shared_up, 0, Is, H, x, H, nullptr, p.hs, Is, nullptr, 1, 0, nullptr)
+        a.g[1] = Is > 0 ? group(w->shared_gate, w->shared_up, 0, Is, H, x, H, nullptr, p.hs, Is, nullptr, 1, 0)
                         : no_group();
         int bn = gemm_direct_tile(0, &bm);
         a.direct_nt[0] = I / bn;
@@ -479,11 +481,9 @@ int layer_run(const moe_config* cfg, const moe_weights* w, const void* x, const 
         TMOE_TRY(launch_grouped_gemm_direct(0, a, s, ev(6), ev(7)));
         TMOE_TRY(mark(3));
         a.direct_counts = nullptr;  // written by the gate/up pass
-        a.g[0] = group(w->down, nullptr, (int64_t)H * I, H, I, p.hd, I, nullptr, p.ybuf, H, nullptr, 1, 0, wt);
+        a.g[0] = group(w->down, nullptr, (int64_t)H * I, H, I, p.hd, I, nullptr, p.ybuf, H, nullptr, 1, 0);
         a.g[0].out_div = k;
-        a.g[0].scale_by_map = 1;
-        a.g[1] = Is > 0 ? group(w->shared_down, nullptr, 0, H, Is, p.hs, Is, nullptr, p.ybuf, H, nullptr, slots, k,
-                                nullptr)
+        a.g[1] = Is > 0 ? group(w->shared_down, nullptr, 0, H, Is, p.hs, Is, nullptr, p.ybuf, H, nullptr, slots, k)
                         : no_group();
         bn = gemm_direct_tile(1, &bm);
         a.direct_nt[0] = H / bn;
@@ -491,7 +491,7 @@ int layer_run(const moe_config* cfg, const moe_weights* w, const void* x, const 
         TMOE_TRY(launch_grouped_gemm_direct(1, a, s));
         TMOE_TRY(mark(4));
         const char* sb = Is > 0 ? static_cast<const char*>(p.ybuf) + (int64_t)k * H * esize(cfg->dtype) : nullptr;
-        TMOE_TRY(finish_layer(cfg->dtype, p.ybuf, k, slots, sb, (int64_t)slots * H, residual, y, T, H, end, s));
+        TMOE_TRY(finish_layer(cfg->dtype, p.ybuf, wt, k, slots, sb, (int64_t)slots * H, residual, y, T, H, end, s));
         TMOE_TRY(mark(5));
         return MOE_OK;
     }
@@ -517,25 +517,22 @@ int layer_run(const moe_config* cfg, const moe_weights* w, const void* x, const 
     }
     TMOE_TRY(mark(2));
 
-    GemmGroup gu_r = group(w->gate, w->up, (int64_t)I * H, I, H, x, H, p.row_token, p.hr, I, nullptr, 1, 0, nullptr);
-    GemmGroup gu_s = Is > 0 ? group(w->shared_gate, w->shared_up, 0, Is, H, x, H, nullptr, p.hs, Is, nullptr, 1, 0,
-                                    nullptr)
+    GemmGroup gu_r = group(w->gate, w->up, (int64_t)I * H, I, H, x, H, p.row_token, p.hr, I, nullptr, 1, 0);
+    GemmGroup gu_s = Is > 0 ? group(w->shared_gate, w->shared_up, 0, Is, H, x, H, nullptr, p.hs, Is, nullptr, 1, 0)
                             : no_group();
     int r = run_gemm_pass(cfg, p.gemm, 0, gu_r, gu_s, p.offsets, N, T, s, ev(6), ev(7));
     if (r != MOE_OK) return r;
     TMOE_TRY(mark(3));
-    // row_pair v = t * k + j goes to slot j of token t: row v + v / k of [T, k + 1, H], scaled by w[v]
-    GemmGroup dn_r = group(w->down, nullptr, (int64_t)H * I, H, I, p.hr, I, nullptr, p.ybuf, H, p.row_pair, 1, 0, wt);
+    // row_pair v = t * k + j goes to slot j of token t: row v + v / k of [T, k + 1, H]; the combine weights it
+    GemmGroup dn_r = group(w->down, nullptr, (int64_t)H * I, H, I, p.hr, I, nullptr, p.ybuf, H, p.row_pair, 1, 0);
     dn_r.out_div = k;
-    dn_r.scale_by_map = 1;
-    GemmGroup dn_s = Is > 0 ? group(w->shared_down, nullptr, 0, H, Is, p.hs, Is, nullptr, p.ybuf, H, nullptr, slots,
-                                    k, nullptr)
+    GemmGroup dn_s = Is > 0 ? group(w->shared_down, nullptr, 0, H, Is, p.hs, Is, nullptr, p.ybuf, H, nullptr, slots, k)
                             : no_group();
     r = run_gemm_pass(cfg, p.gemm, 1, dn_r, dn_s, p.offsets, N, T, s);
     if (r != MOE_OK) return r;
     TMOE_TRY(mark(4));
     const char* shared_base = Is > 0 ? static_cast<const char*>(p.ybuf) + (int64_t)k * H * esize(cfg->dtype) : nullptr;
-    TMOE_TRY(finish_layer(cfg->dtype, p.ybuf, k, slots, shared_base, (int64_t)slots * H, residual, y, T, H, end,
+    TMOE_TRY(finish_layer(cfg->dtype, p.ybuf, wt, k, slots, shared_base, (int64_t)slots * H, residual, y, T, H, end,
                           s));
     TMOE_TRY(mark(5));
     return MOE_OK;
@@ -638,10 +635,10 @@ int moe_grouped_swiglu(const moe_config* cfg, const void* x, const int32_t* row_
     grouped_ws(cfg, T, ws, &plan, &hr);
     hipStream_t s = as_stream(stream);
     if (plan.mfma) TMOE_TRY(launch_build_items(offsets, E, T, &plan.t[0], &plan.t[1], s));
-    GemmGroup gu = group(gate, up, (int64_t)I * H, I, H, x, H, row_token, hr, I, nullptr, 1, 0, nullptr);
+    GemmGroup gu = group(gate, up, (int64_t)I * H, I, H, x, H, row_token, hr, I, nullptr, 1, 0);
     int r = run_gemm_pass(cfg, plan, 0, gu, no_group(), offsets, N, 0, s);
     if (r != MOE_OK) return r;
-    GemmGroup dn = group(down, nullptr, (int64_t)H * I, H, I, hr, I, nullptr, y_perm, H, nullptr, 1, 0, nullptr);
+    GemmGroup dn = group(down, nullptr, (int64_t)H * I, H, I, hr, I, nullptr, y_perm, H, nullptr, 1, 0);
     return run_gemm_pass(cfg, plan, 1, dn, no_group(), offsets, N, 0, s);
 }
 
@@ -662,10 +659,10 @@ int moe_shared_swiglu(const moe_config* cfg, const void* x, int64_t T, const voi
     shared_ws(cfg, T, ws, &plan, &hs);
     hipStream_t s = as_stream(stream);
     if (plan.mfma) TMOE_TRY(launch_build_items(nullptr, 0, T, &plan.t[0], &plan.t[1], s));
-    GemmGroup gu = group(sg, su, 0, Is, H, x, H, nullptr, hs, Is, nullptr, 1, 0, nullptr);
+    GemmGroup gu = group(sg, su, 0, Is, H, x, H, nullptr, hs, Is, nullptr, 1, 0);
     int r = run_gemm_pass(cfg, plan, 0, no_group(), gu, nullptr, 0, T, s);
     if (r != MOE_OK) return r;
-    GemmGroup dn = group(sd, nullptr, 0, H, Is, hs, Is, nullptr, y_shared, H, nullptr, 1, 0, nullptr);
+    GemmGroup dn = group(sd, nullptr, 0, H, Is, hs, Is, nullptr, y_shared, H, nullptr, 1, 0);
     return run_gemm_pass(cfg, plan, 1, no_group(), dn, nullptr, 0, T, s);
 }
 

@@ -14,9 +14,9 @@
 namespace tmoe {
 
 // Source row of term j of token t.  Slot mode (rows == nullptr): expert
-// outputs are stored per token in `slots` consecutive rows with the weights
-// already applied.  The shared-expert term of token t is shared + t * sstride
-// (nullptr: no shared term).
+// outputs are stored per token in `slots` consecutive rows, weighted here by
+// w[t * k + j] (w null: weights already applied).  The shared-expert term of
+// token t is shared + t * sstride (nullptr: no shared term).
 template <typename T>
 __global__ __launch_bounds__(128) void combine_kernel(const T* __restrict__ ysrc, const int32_t* __restrict__ rows,
                                                       const float* __restrict__ w, int k, int slots,
@@ -32,7 +32,8 @@ __global__ __launch_bounds__(128) void combine_kernel(const T* __restrict__ ysrc
                 const int64_t r = rows[t * k + j];
                 acc += w[t * k + j] * Elem<T>::load(ysrc, r * H + h);
             } else {
-                acc += Elem<T>::load(ysrc, (t * slots + j) * (int64_t)H + h);
+                const float wj = w ? w[t * k + j] : 1.0f;
+                acc += wj * Elem<T>::load(ysrc, (t * slots + j) * (int64_t)H + h);
             }
         }
         if (residual) acc += Elem<T>::load(residual, t * H + h);
@@ -70,6 +71,7 @@ __global__ __launch_bounds__(128) void combine_bf16x8_kernel(const bf16_t* __res
                 wj = w[t * k + j];
             } else {
                 src = ysrc + (t * slots + j) * (int64_t)H;
+                if (w) wj = w[t * k + j];
             }
             u32x4 v = *reinterpret_cast<const u32x4*>(src + h);
 #pragma unroll
@@ -158,7 +160,8 @@ __global__ __launch_bounds__(128) void rmsnorm_bf16x8_kernel(const bf16_t* x, co
 // that stored row (the lab's [3C] step normalises the layer input; the final
 // norm before codec_head likewise), written to norm_out.
 template <int NCH>
-__global__ __launch_bounds__(128) void combine_norm_bf16x8_kernel(const bf16_t* __restrict__ ysrc, int k, int slots,
+__global__ __launch_bounds__(128) void combine_norm_bf16x8_kernel(const bf16_t* __restrict__ ysrc,
+                                                                  const float* __restrict__ w, int k, int slots,
                                                                   const bf16_t* __restrict__ shared, int64_t sstride,
                                                                   const bf16_t* residual, bf16_t* y, int64_t Ttok,
                                                                   int H, const float* __restrict__ gain, float eps,
@@ -187,11 +190,12 @@ __global__ __launch_bounds__(128) void combine_norm_bf16x8_kernel(const bf16_t* 
             for (int q = 0; q < 8; ++q) acc[q] = 0.f;
         }
         for (int j = 0; j < k; ++j) {
+            const float wj = w ? w[t * k + j] : 1.0f;
             const u32x4 v = *reinterpret_cast<const u32x4*>(ysrc + (t * slots + j) * (int64_t)H + h);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                acc[2 * q] += 1.0f * __uint_as_float(v[q] << 16);
-                acc[2 * q + 1] += 1.0f * __uint_as_float(v[q] & 0xFFFF0000u);
+                acc[2 * q] += wj * __uint_as_float(v[q] << 16);
+                acc[2 * q + 1] += wj * __uint_as_float(v[q] & 0xFFFF0000u);
             }
         }
         if (residual) {
@@ -296,18 +300,18 @@ hipError_t launch_rmsnorm(int dtype, const void* x, const float* gain, float eps
     return hipGetLastError();
 }
 
-hipError_t launch_combine_norm(int dtype, const void* ysrc, int k, int slots, const void* shared, int64_t sstride,
-                               const void* residual, void* y, int64_t Ttok, int H, const float* gain, float eps,
-                               void* norm_out, hipStream_t st) {
+hipError_t launch_combine_norm(int dtype, const void* ysrc, const float* w, int k, int slots, const void* shared,
+                               int64_t sstride, const void* residual, void* y, int64_t Ttok, int H, const float* gain,
+                               float eps, void* norm_out, hipStream_t st) {
     if (Ttok <= 0) return hipSuccess;
     const int nch = bf16x8_chunks(dtype, H);
     if (nch == 0) {  // the two steps apart, with the same kernels as the separate calls
-        hipError_t e = launch_combine(dtype, ysrc, nullptr, nullptr, k, slots, shared, sstride, residual, y, Ttok, H, st);
+        hipError_t e = launch_combine(dtype, ysrc, nullptr, w, k, slots, shared, sstride, residual, y, Ttok, H, st);
         if (e != hipSuccess) return e;
         return launch_rmsnorm(dtype, y, gain, eps, Ttok, H, norm_out, st);
     }
 #define TMOE_CN(N)                                                                                              \
-    combine_norm_bf16x8_kernel<N><<<(unsigned)Ttok, 128, 0, st>>>((const bf16_t*)ysrc, k, slots,               \
+    combine_norm_bf16x8_kernel<N><<<(unsigned)Ttok, 128, 0, st>>>((const bf16_t*)ysrc, w, k, slots,            \
                                                                  (const bf16_t*)shared, sstride,               \
                                                                  (const bf16_t*)residual, (bf16_t*)y, Ttok, H, \
                                                                  gain, eps, (bf16_t*)norm_out)

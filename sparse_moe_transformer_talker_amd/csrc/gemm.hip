@@ -5,7 +5,7 @@
 // horus-space, MLP section).
 //
 // pass 0 (gate/up):  h[r, n] = SiLU(x_r . gate[e, n]) * (x_r . up[e, n])
-// pass 1 (down):     y[dst(r), n] = scale(r) * (h_r . down[e, n])
+// pass 1 (down):     y[dst(r), n] = h_r . down[e, n]   (the combine applies the routing weights)
 //
 // Work arrives as a device-built list of tiles (expert, n0, m0, rows); the
 // launch is sized for the worst case and surplus workgroups exit at once.
@@ -183,16 +183,10 @@ __global__ __launch_bounds__(256, PASS == 1 ? 6 : 1) void grouped_gemm_kernel(Ge
                 const int64_t src = (int64_t)m0 + row;
                 const int64_t v = omap ? (int64_t)omap[row] : (g.out_rows ? (int64_t)g.out_rows[src] : src);
                 const int64_t dst = v * g.out_mul + g.out_add + (g.out_div > 0 ? v / g.out_div : 0);
-                const float sc = (PASS == 1 && g.out_scale) ? g.out_scale[g.scale_by_map ? v : src] : 1.0f;
 #pragma unroll
                 for (int b = 0; b < NS; ++b) {
                     const int col = n0 + wn * TN + b * 16 + li;
-                    float val;
-                    if (PASS == 0) {
-                        val = silu(acc[a][b][r]) * accu[a][b][r];
-                    } else {
-                        val = acc[a][b][r] * sc;
-                    }
+                    const float val = PASS == 0 ? silu(acc[a][b][r]) * accu[a][b][r] : acc[a][b][r];
                     out[dst * g.out_ld + col] = f32_to_bf16(val);
                 }
             }
@@ -382,24 +376,6 @@ __global__ __launch_bounds__(64 * lds_gemm::NWAVE) void grouped_gemm_lds_kernel(
         }
         pb[j] = w + (int64_t)e * g.w_estride + (int64_t)wrow * K + c * 8;
     }
-    // Destination row of every tile row (LDS, for the epilogue's row stores) and
-    // the scale of this lane's token in each of its MI token blocks, fetched now
-    // so the loads overlap the main loop.
-    __shared__ int32_t dst_rows[BM];
-    if (tid < BM) {
-        const int r = tid;
-        const int64_t src = (int64_t)m0 + (r < mrows ? r : 0);
-        const int32_t v = g.out_rows ? g.out_rows[src] : (int32_t)src;
-        dst_rows[r] = r < mrows ? v * g.out_mul + g.out_add + (g.out_div > 0 ? v / g.out_div : 0) : -1;
-    }
-    float row_sc[MI];
-#pragma unroll
-    for (int a = 0; a < MI; ++a) {
-        const int r = (wave >> 1) * WROWS + a * 32 + (lane & 31);
-        const int64_t src = (int64_t)m0 + (r < mrows ? r : 0);
-        const int32_t v = g.out_rows ? g.out_rows[src] : (int32_t)src;
-        row_sc[a] = (PASS == 1 && g.out_scale) ? g.out_scale[g.scale_by_map ? v : src] : 1.0f;
-    }
     typedef __attribute__((address_space(3))) void lds_void;
     auto issue = [&](int stage, char* base) {
         const int k0 = stage * BK;
@@ -464,6 +440,12 @@ __global__ __launch_bounds__(64 * lds_gemm::NWAVE) void grouped_gemm_lds_kernel(
     issue(0, buf0);
     issue(1, buf1);
     issue(2, buf2);
+    // The output row map is read behind the first stages and used only after
+    // the last wait, so no wait of the prologue waits on it (nothing else
+    // writes the register the load fills).
+    const bool mapped = g.out_rows != nullptr;
+    int32_t map_v = 0;
+    if (mapped && tid < BM) map_v = g.out_rows[m0 + (tid < mrows ? tid : 0)];
     // steady state: stage s waits for itself with two newer stages in flight,
     // then refills the buffer stage s - 1 used with stage s + 3
     for (int s = 0; s + 4 < nst; s += 4) {
@@ -496,6 +478,12 @@ __global__ __launch_bounds__(64 * lds_gemm::NWAVE) void grouped_gemm_lds_kernel(
         char* base = bsel == 0 ? buf0 : (bsel == 1 ? buf1 : (bsel == 2 ? buf2 : buf3));
         return base + (r % RPB) * ROWB;
     };
+    // destination row of every tile row, for the row stores below
+    __shared__ int32_t dst_rows[BM];
+    if (tid < BM) {
+        const int32_t v = mapped ? map_v : m0 + tid;
+        dst_rows[tid] = tid < mrows ? v * g.out_mul + g.out_add + (g.out_div > 0 ? v / g.out_div : 0) : -1;
+    }
     sync();  // every wave is done with the ring
 #pragma unroll
     for (int a = 0; a < MI; ++a) {
@@ -508,11 +496,7 @@ __global__ __launch_bounds__(64 * lds_gemm::NWAVE) void grouped_gemm_lds_kernel(
                 float v[4];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    if (PASS == 0) {
-                        v[q] = silu(acc[a][b][4 * j + q]) * acc[a][b + 2][4 * j + q];
-                    } else {
-                        v[q] = acc[a][b][4 * j + q] * row_sc[a];
-                    }
+                    v[q] = PASS == 0 ? silu(acc[a][b][4 * j + q]) * acc[a][b + 2][4 * j + q] : acc[a][b][4 * j + q];
                 }
                 uint2 pk;
                 pk.x = pack_bf16x2(v[0], v[1]);
@@ -566,7 +550,6 @@ __global__ __launch_bounds__(256) void gemm_generic_kernel(GemmGroup g, const in
         for (int kk = 0; kk < g.K; ++kk) s0 = fmaf(Elem<T>::load(a, kk), Elem<T>::load(wa, kk), s0);
     }
     const int64_t v = g.out_rows ? (int64_t)g.out_rows[r] : r;
-    if (PASS == 1 && g.out_scale) s0 *= g.out_scale[g.scale_by_map ? v : r];
     const int64_t dst = v * g.out_mul + g.out_add + (g.out_div > 0 ? v / g.out_div : 0);
     Elem<T>::store((T*)g.out, dst * g.out_ld + n, s0);
 }

@@ -99,8 +99,6 @@ struct GemmGroup {
     const int32_t* out_rows;  // row r -> v = out_rows[r], or nullptr (v = r)
     int out_mul, out_add;     // destination row = v * out_mul + out_add (+ v / out_div if out_div > 0)
     int out_div;
-    const float* out_scale;   // scale out_scale[r] (out_scale[v] if scale_by_map), or nullptr
-    int scale_by_map;
 };
 struct GemmArgs {
     GemmGroup g[2];  // [0] routed experts, [1] shared expert (expert index == E)
@@ -118,8 +116,8 @@ struct GemmArgs {
     // router's per-block pair lists (direct_bcnt / direct_blist of
     // launch_route_block, direct_nb blocks) into its m rows, which are rows
     // e * direct_T .. e * direct_T + m - 1 of its h buffer; in the gate/up pass
-    // the pair p gives A row p / a_div, in the down pass output row p (with the
-    // scale of p).  Tiles of column 0 write m to direct_counts[e] (nullable).
+    // the pair p gives A row p / a_div, in the down pass output row p.  Tiles
+    // of column 0 write m to direct_counts[e] (nullable).
     const int* direct_bcnt;
     const int* direct_blist;
     int direct_nb;
@@ -155,6 +153,9 @@ hipError_t launch_gemm_generic(int dtype, int pass, const GemmGroup& g, const in
                                int E, int64_t rows, hipStream_t st);
 
 // --- element-wise (elementwise.hip) ---
+// Term j < k of token t: row rows[t * k + j] of ysrc (rows not null) or slot j
+// of the token's `slots` consecutive rows (rows null), times w[t * k + j] (w
+// nullable in slot mode: the slots already carry their weights).
 hipError_t launch_combine(int dtype, const void* ysrc, const int32_t* rows, const float* w, int k, int slots,
                           const void* shared, int64_t sstride, const void* residual, void* y, int64_t T, int H,
                           hipStream_t st);
@@ -164,9 +165,9 @@ hipError_t launch_rmsnorm(int dtype, const void* x, const float* gain, float eps
 // Slot-mode combine (as launch_combine with rows == nullptr) followed by the
 // RMSNorm of the stored y into norm_out, fused for bf16 rows; same results as
 // the two launches.
-hipError_t launch_combine_norm(int dtype, const void* ysrc, int k, int slots, const void* shared, int64_t sstride,
-                               const void* residual, void* y, int64_t T, int H, const float* gain, float eps,
-                               void* norm_out, hipStream_t st);
+hipError_t launch_combine_norm(int dtype, const void* ysrc, const float* w, int k, int slots, const void* shared,
+                               int64_t sstride, const void* residual, void* y, int64_t T, int H, const float* gain,
+                               float eps, void* norm_out, hipStream_t st);
 hipError_t launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t st);
 hipError_t launch_gather_rows(int dtype, const void* x, const int32_t* rows, int64_t n, int H, void* out,
                               hipStream_t st);
