@@ -643,11 +643,14 @@ hipError_t launch_grouped_gemm_direct(int pass, const GemmArgs& args, hipStream_
 // ---------------------------------------------------------------------------
 // Skinny products for M <= 64 rows (a decode batch), split over K:
 // P[s] [M, N] = A [M, K_s] W_s^T in fp32, where K_s is the s-th of KS equal runs
-// of K.  One workgroup per (16 output columns, run) reads its 16 x K_s weight
-// block once; its four waves split the run again, each covering all 64 rows as
-// four 16-row matrix-core tiles (v_mfma_f32_16x16x32_bf16, four 32-wide K steps
-// with their loads in flight together).  The waves' partials are added in LDS
-// in wave order; the consumer adds the KS runs in run order (deterministic).
+// of K; the consumer adds the KS runs in run order (deterministic).  Two forms:
+// - 16 columns per workgroup (below): one workgroup per (16 output columns,
+//   run) reads its 16 x K_s weight block once; its four waves split the run
+//   again, each covering all 64 rows as four 16-row matrix-core tiles
+//   (v_mfma_f32_16x16x32_bf16, four 32-wide K steps with their loads in flight
+//   together), and their partials are added in LDS in wave order;
+// - 64 columns per workgroup with the run's token rows in LDS
+//   (skinny_lds_kernel), where the shape gives enough runs of 256.
 namespace {
 constexpr int kSkinnyRows = 64;
 constexpr int kSkinnyWaves = 4;
@@ -722,7 +725,138 @@ __global__ __launch_bounds__(64 * NW) void skinny_gemm_kernel(const bf16_t* __re
 }
 }  // namespace
 
+// Skinny products with the token rows in LDS.  A workgroup covers 64 output
+// columns (one 16-column tile per wave) over one K run of KR: it reads the
+// run's slice of all 64 token rows once into LDS and its waves read their
+// 16 x KR weight blocks straight into matrix-core operand registers, every
+// load of the run in flight at once.  Per workgroup the token bytes equal the
+// weight bytes (the 16-column form reads 64 rows per 16 columns).
+template <int KR>
+__global__ __launch_bounds__(256) void skinny_lds_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ W,
+                                                         float* __restrict__ P, int M, int N, int K) {
+    constexpr int LDA = KR + 8;                // bf16 per LDS row (16-byte pad against bank conflicts)
+    constexpr int CPR = KR / 8;                // 16-byte chunks per row of the slice
+    constexpr int AC = kSkinnyRows * CPR / 256;
+    constexpr int STEPS = KR / 32;
+    static_assert(AC * 256 == kSkinnyRows * CPR, "the slice divides over the block");
+    __shared__ __attribute__((aligned(16))) bf16_t As[kSkinnyRows * LDA];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int r = lane & 15, kg = (lane >> 4) * 8;
+    const int n0 = blockIdx.x * 64 + wave * 16;
+    const int64_t k0 = (int64_t)blockIdx.y * KR;
+    u32x4 b[STEPS];
+    const bf16_t* wp = W + (int64_t)(n0 + r) * K + k0 + kg;
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s) b[s] = *reinterpret_cast<const u32x4*>(wp + 32 * s);
+    u32x4 a[AC];
+#pragma unroll
+    for (int i = 0; i < AC; ++i) {  // rows past M repeat row M - 1 (computed, never stored)
+        const int c = tid + 256 * i, row = c / CPR;
+        a[i] = *reinterpret_cast<const u32x4*>(A + (int64_t)min(row, M - 1) * K + k0 + (c % CPR) * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < AC; ++i) {
+        const int c = tid + 256 * i;
+        *reinterpret_cast<u32x4*>(&As[(c / CPR) * LDA + (c % CPR) * 8]) = a[i];
+    }
+    __syncthreads();
+    const f32x4 zero = {0, 0, 0, 0};
+    f32x4 acc[4] = {zero, zero, zero, zero};
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                *reinterpret_cast<const bf16x8*>(&As[(mt * 16 + r) * LDA + 32 * s + kg]),
+                __builtin_bit_cast(bf16x8, b[s]), acc[mt], 0, 0, 0);
+    // D[row = 16 mt + 4 (lane / 16) + i][column n0 + lane % 16]
+    float* out = P + (int64_t)blockIdx.y * M * N;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = mt * 16 + 4 * (lane >> 4) + i;
+            if (row < M) out[(int64_t)row * N + n0 + r] = acc[mt][i];
+        }
+}
+
+// h [M, I] = SiLU(A Wg^T) * (A Wu^T) with all of K in one workgroup per 16
+// features: the 64 token rows (K <= 1024) sit in LDS; eight waves take the
+// gate or up tile over one K quarter each, and the quarters are added through
+// LDS in quarter order.
+template <int KQ>
+__global__ __launch_bounds__(512) void skinny_swiglu_lds_kernel(const bf16_t* __restrict__ A,
+                                                                const bf16_t* __restrict__ Wg,
+                                                                const bf16_t* __restrict__ Wu, bf16_t* __restrict__ h,
+                                                                int M, int I) {
+    constexpr int K = 4 * KQ, LDA = K + 8, CPR = K / 8;
+    constexpr int AC = kSkinnyRows * CPR / 512;
+    constexpr int STEPS = KQ / 32;
+    static_assert(AC * 512 == kSkinnyRows * CPR, "the rows divide over the block");
+    static_assert(2 * 4 * kSkinnyRows * 16 * 4 <= kSkinnyRows * LDA * 2, "the quarter sums fit in the row buffer");
+    __shared__ __attribute__((aligned(16))) bf16_t As[kSkinnyRows * LDA];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int r = lane & 15, kg = (lane >> 4) * 8;
+    const int tile = wave & 1, q = wave >> 1;  // tile 0: gate rows, 1: up rows
+    const int f0 = blockIdx.x * 16;
+    u32x4 b[STEPS];
+    const bf16_t* wp = (tile ? Wu : Wg) + (int64_t)(f0 + r) * K + q * KQ + kg;
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s) b[s] = *reinterpret_cast<const u32x4*>(wp + 32 * s);
+    u32x4 a[AC];
+#pragma unroll
+    for (int i = 0; i < AC; ++i) {
+        const int c = tid + 512 * i, row = c / CPR;
+        a[i] = *reinterpret_cast<const u32x4*>(A + (int64_t)min(row, M - 1) * K + (c % CPR) * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < AC; ++i) {
+        const int c = tid + 512 * i;
+        *reinterpret_cast<u32x4*>(&As[(c / CPR) * LDA + (c % CPR) * 8]) = a[i];
+    }
+    __syncthreads();
+    const f32x4 zero = {0, 0, 0, 0};
+    f32x4 acc[4] = {zero, zero, zero, zero};
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                *reinterpret_cast<const bf16x8*>(&As[(mt * 16 + r) * LDA + q * KQ + 32 * s + kg]),
+                __builtin_bit_cast(bf16x8, b[s]), acc[mt], 0, 0, 0);
+    __syncthreads();  // every wave is done with the token rows
+    float* red = reinterpret_cast<float*>(As);  // [tile][quarter][64 rows][16 features]
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            red[((tile * 4 + q) * kSkinnyRows + mt * 16 + 4 * (lane >> 4) + i) * 16 + r] = acc[mt][i];
+    __syncthreads();
+    for (int idx = tid; idx < kSkinnyRows * 16; idx += 512) {
+        const int row = idx >> 4, c = idx & 15;
+        if (row >= M) continue;
+        float g = 0.f, u = 0.f;
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+            g += red[(qq * kSkinnyRows + row) * 16 + c];
+            u += red[((4 + qq) * kSkinnyRows + row) * 16 + c];
+        }
+        h[(int64_t)row * I + f0 + c] = f32_to_bf16(silu(g) * u);
+    }
+}
+
+// Run length of the LDS form for a product (0: the 16-column form applies):
+// runs of 256, when they give at least 128 workgroups.  Shorter runs and fewer
+// workgroups measured slower than the 16-column form (more fp32 partials for
+// the consumer to add, or too few CUs reading weights).
+constexpr int kSkinnyRun = 256;
+int skinny_lds_run(int64_t M, int N, int K) {
+    if (M < 1 || M > kSkinnyRows || N < 64 || N % 64 || K % kSkinnyRun) return 0;
+    return (int64_t)(N / 64) * (K / kSkinnyRun) >= 128 ? kSkinnyRun : 0;
+}
+
 int skinny_gemm_runs(int64_t M, int N, int K) {
+    if (const int kr = skinny_lds_run(M, N, K)) return K / kr;
     if (M < 1 || M > kSkinnyRows || N < 16 || N % 16 || K % (32 * kSkinnyWaves)) return 0;
     // enough workgroups to fill the chip, each run at least 512 long
     int ks = 1;
@@ -732,6 +866,12 @@ int skinny_gemm_runs(int64_t M, int N, int K) {
 
 hipError_t launch_skinny_gemm(const void* A, const void* W, float* P, int64_t M, int N, int K, int KS,
                               hipStream_t st) {
+    const int kr = skinny_lds_run(M, N, K);
+    if (kr && KS == K / kr) {
+        skinny_lds_kernel<kSkinnyRun><<<dim3((unsigned)(N / 64), (unsigned)KS), 256, 0, st>>>(
+            (const bf16_t*)A, (const bf16_t*)W, P, (int)M, N, K);
+        return hipGetLastError();
+    }
     dim3 grid((unsigned)(N / 16), (unsigned)KS);
     skinny_gemm_kernel<kSkinnyWaves, 4, false><<<grid, 64 * kSkinnyWaves, 0, st>>>(
         (const bf16_t*)A, (const bf16_t*)W, nullptr, P, nullptr, (int)M, N, K, KS);
@@ -744,6 +884,11 @@ bool skinny_swiglu_ok(int64_t M, int I, int K) {
 
 hipError_t launch_skinny_swiglu(const void* A, const void* Wg, const void* Wu, void* h, int64_t M, int I, int K,
                                 hipStream_t st) {
+    if (K == 1024 && I % 16 == 0) {
+        skinny_swiglu_lds_kernel<256><<<(unsigned)(I / 16), 512, 0, st>>>(
+            (const bf16_t*)A, (const bf16_t*)Wg, (const bf16_t*)Wu, (bf16_t*)h, (int)M, I);
+        return hipGetLastError();
+    }
     skinny_gemm_kernel<kSkinnyWaves, 4, true><<<(unsigned)(I / 8), 64 * kSkinnyWaves, 0, st>>>(
         (const bf16_t*)A, (const bf16_t*)Wg, (const bf16_t*)Wu, nullptr, (bf16_t*)h, (int)M, 2 * I, K, 1);
     return hipGetLastError();
