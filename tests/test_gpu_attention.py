@@ -8,7 +8,8 @@ bf16 bars; every other cache entry must be unchanged bit for bit.  The value
 cache is transposed in the library ([T, nkv, head_dim, max_len]).  Cases: random
 lengths up to 1024 (T = 64), ragged chunks and lengths 0 / 1 / 127 / 128 / 129 /
 max_len - 1 (T = 37, max_len = 320), 3D positions with distinct T/H/W indices,
-long caches (max_len 4096 and 32768), the 16/8 head split, the fused RMSNorm of y, a batch of 96
+long caches (max_len 4096 and 32768), the 16/8 head split, hidden 512 (the
+16-column skinny products), the fused RMSNorm of y, a batch of 96
 streams (the grouped GEMM path for the projections), streams
 whose length is out of range, and a captured graph replayed.
 """
@@ -114,6 +115,15 @@ def test_attention_decode_long_cache():
     lens = np.array([4095, 4000, 3000, 2049, 2048, 1000, 17, 0], np.int32)
     w, kv, x, res, lens, pos = _case(T, L, lens)
     _check(INP.TALKER_ATTN, L, w, kv, x, res, lens, pos, "long")
+
+
+def test_attention_decode_small_hidden():
+    """Hidden 512, 8 query / 2 KV heads: the QKV (1536 x 512) and O (512 x 1024)
+    products take the 16-column skinny kernel."""
+    shape = INP.AttnShape(512, 8, 2, 128)
+    T, L = 20, 256
+    w, kv, x, res, lens, pos = _case(T, L, INP.cache_lengths(T, L, 68), shape=shape)
+    _check(shape, L, w, kv, x, res, lens, pos, "hidden 512", norm=True)
 
 
 def test_attention_decode_16q_8kv():

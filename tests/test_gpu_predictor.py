@@ -10,7 +10,9 @@ state, so the checks are:
     library's states at every position within the bf16 bars;
   * the free-running oracle's codes are reported beside the library's.
 Cases: 64 streams and a ragged 5; c_0 outside the table (a zero embedding);
-the frame captured in a graph and replayed.
+the frame captured in a graph and replayed; a smaller predictor (hidden 512,
+MLP 1536), whose products take the 16-column skinny forms (the production
+shape takes the forms with the token rows in LDS).
 """
 import numpy as np
 import pytest
@@ -122,3 +124,35 @@ def test_predictor_graph_replay(pred):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(codes_g, codes_e), "replay %d differs" % rep
+
+
+def test_predictor_frame_small_shape():
+    """Hidden 512, 8 query / 4 KV heads, MLP 1536, 2 layers, 4 codes of 256: the
+    SwiGLU product's K (512) and the other products' sizes select the 16-column
+    skinny kernels."""
+    shape = INP.PredictorShape(layers=2, H=512, n_heads=8, n_kv_heads=4, I=1536, num_codes=4, codebook=256,
+                               c0_vocab=300)
+    pc = api.PredictorConfig(num_layers=2, hidden_size=512, num_heads=8, num_kv_heads=4, intermediate_size=1536,
+                             num_codes=4, codebook_size=256, c0_vocab=300)
+    w = INP.predictor_weights(shape, 83)
+    dev = lambda a: G.dev(a, "bf16") if a.dtype == np.uint16 else torch.from_numpy(a).cuda()
+    wd = {k: dev(v) for k, v in w.items() if k != "layers"}
+    wd["layers"] = [{k: dev(v) for k, v in lw.items()} for lw in w["layers"]]
+    f64 = lambda a: INP.to_f64(a, "bf16") if a.dtype == np.uint16 else a.astype(np.float64)
+    w64 = {k: f64(v) for k, v in w.items() if k != "layers"}
+    w64["layers"] = [{k: f64(v) for k, v in lw.items()} for lw in w["layers"]]
+    T = 23
+    h = INP.activations(T, shape.H, 84, "bf16")
+    c0 = np.random.default_rng(84).integers(0, shape.c0_vocab, T).astype(np.int32)
+    xn = torch.empty((shape.num_codes, T, shape.H), dtype=torch.bfloat16, device="cuda")
+    codes = api.moe_predictor_frame(pc, wd, G.dev(h, "bf16"), torch.from_numpy(c0).cuda(), xn_out=xn)
+    torch.cuda.synchronize()
+    codes = codes.cpu().numpy().astype(np.int64)
+    xn = G.host64(xn.reshape(-1, shape.H)).reshape(shape.num_codes, T, shape.H)
+    np.testing.assert_array_equal(codes[0], c0)
+    for j in range(1, shape.num_codes):
+        np.testing.assert_array_equal(codes[j], R.argmax_first(xn[j] @ w64["lm_head"][j - 1].T), err_msg="code %d" % j)
+    forced = P.predictor_frame(INP.to_f64(h, "bf16"), c0, w64, n_heads=8, n_kv_heads=4, num_codes=4,
+                               forced=codes)
+    for j in range(shape.num_codes):
+        _close(xn[j], forced["final"][j], "small shape position %d" % j)
