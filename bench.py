@@ -32,11 +32,19 @@ def log(msg):
     print("[bench] " + msg, file=sys.stderr, flush=True)
 
 
+def shared_in_router_launch(shape, T):
+    """Whether the library computes the shared expert's gate/up product in the
+    router's launch (up to 64 tokens, H a multiple of 256, I_s of 8) rather
+    than in the grouped gate/up pass."""
+    return shape.Is > 0 and 1 <= T <= 64 and shape.Is % 8 == 0 and shape.H % 256 == 0
+
+
 def layer_costs(shape, T, touched):
     """Algorithmic bytes and flops of one layer step and of its gate/up pass.
 
     Weight bytes count each touched expert once (bf16); activations count the
     token rows read and written once; routing outputs 8 bytes per (token, slot).
+    The gate/up pass counts the shared expert's gate/up only when it runs there.
     """
     H, E, k, I, Is = shape.H, shape.E, shape.k, shape.I, shape.Is
     expert_b = 3 * I * H * 2
@@ -44,8 +52,11 @@ def layer_costs(shape, T, touched):
     router_b = E * H * 2
     layer_bytes = touched * expert_b + shared_b + router_b + 2 * T * H * 2 + T * k * 8
     layer_flops = T * (2 * H * E + 6 * H * I * k + 6 * H * Is)
-    gu_bytes = touched * 2 * I * H * 2 + 2 * Is * H * 2 + T * H * 2 + (T * k * I + T * Is) * 2
-    gu_flops = T * (4 * H * I * k + 4 * H * Is)
+    gu_bytes = touched * 2 * I * H * 2 + T * H * 2 + T * k * I * 2
+    gu_flops = T * 4 * H * I * k
+    if not shared_in_router_launch(shape, T):
+        gu_bytes += 2 * Is * H * 2 + T * Is * 2
+        gu_flops += T * 4 * H * Is
     return layer_bytes, layer_flops, gu_bytes, gu_flops
 
 
@@ -625,7 +636,10 @@ def main():
         "config": {"workload": "talker_moe_layer_decode_T64", "tokens": 64, "hidden": shape.H,
                    "experts": shape.E, "top_k": shape.k, "expert_intermediate": shape.I,
                    "shared_intermediate": shape.Is, "weight_sets_rotated": args.rotate},
-        "roofline": {"bound": "hbm", "kernel": "grouped gate/up SwiGLU pass (routed + shared)",
+        "roofline": {"bound": "hbm",
+                     "kernel": "grouped gate/up SwiGLU pass (routed experts; the shared expert's gate/up runs in "
+                               "the router's launch at this size)" if shared_in_router_launch(shape, 64)
+                               else "grouped gate/up SwiGLU pass (routed + shared)",
                      "achieved": g["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": g["gbs"] / HBM_PEAK_GBS, "traffic": measured_traffic(),
                      "bytes_per_launch": g["bytes"], "mean_us": g["mean_us"]},

@@ -458,8 +458,16 @@ int layer_run(const moe_config* cfg, const moe_weights* w, const void* x, const 
     TMOE_TRY(mark(0));
     auto ev = [&](int i) { return stage_events ? static_cast<hipEvent_t>(stage_events[i]) : nullptr; };
     if (p.direct) {
-        TMOE_TRY(launch_route_block(x, w->router, w->router_bias, T, H, E, k, cfg->norm_topk_prob, idx, wt, nullptr,
-                                    nullptr, nullptr, p.bcnt, p.blist, s));
+        // With at most 64 tokens the shared expert's gate/up runs in the router's
+        // launch, on the CUs the router leaves idle; the gate/up pass then holds
+        // the routed tiles alone.
+        const bool shared_early = Is > 0 && route_shared_ok(T, H, Is);
+        if (shared_early)
+            TMOE_TRY(launch_route_block_shared(x, w->router, w->router_bias, T, H, E, k, cfg->norm_topk_prob, idx, wt,
+                                               p.bcnt, p.blist, w->shared_gate, w->shared_up, Is, p.hs, s));
+        else
+            TMOE_TRY(launch_route_block(x, w->router, w->router_bias, T, H, E, k, cfg->norm_topk_prob, idx, wt,
+                                        nullptr, nullptr, nullptr, p.bcnt, p.blist, s));
         TMOE_TRY(mark(1));
         TMOE_TRY(mark(2));
         int bm;
@@ -472,11 +480,12 @@ int layer_run(const moe_config* cfg, const moe_weights* w, const void* x, const 
         a.direct_T = (int)T;
         a.g[0] = group(w->gate, w->up, (int64_t)I * H, I, H, x, H, nullptr, p.hd, I, nullptr, 1, 0);
         a.g[0].a_div = k;
-        a.g[1] = Is > 0 ? group(w->shared_gate, w->shared_up, 0, Is, H, x, H, nullptr, p.hs, Is, nullptr, 1, 0)
-                        : no_group();
+        a.g[1] = Is > 0 && !shared_early
+                     ? group(w->shared_gate, w->shared_up, 0, Is, H, x, H, nullptr, p.hs, Is, nullptr, 1, 0)
+                     : no_group();
         int bn = gemm_direct_tile(0, &bm);
         a.direct_nt[0] = I / bn;
-        a.direct_nt[1] = Is / bn;
+        a.direct_nt[1] = shared_early ? 0 : Is / bn;
         a.direct_mt1 = (int)((T + bm - 1) / bm);
         TMOE_TRY(launch_grouped_gemm_direct(0, a, s, ev(6), ev(7)));
         TMOE_TRY(mark(3));

@@ -18,6 +18,7 @@
 // conflicts) with a register prefetch of the next K block.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "skinny.hpp"
 
 #include <hip/hip_ext.h>
 
@@ -651,77 +652,17 @@ hipError_t launch_grouped_gemm_direct(int pass, const GemmArgs& args, hipStream_
 //   together), and their partials are added in LDS in wave order;
 // - 64 columns per workgroup with the run's token rows in LDS
 //   (skinny_lds_kernel), where the shape gives enough runs of 256.
-namespace {
-constexpr int kSkinnyRows = 64;
-constexpr int kSkinnyWaves = 4;
 // SWIGLU: a workgroup's 16 columns are gate rows f .. f + 7 (of W) and up rows
 // f .. f + 7 (of W2) for the 8 features f = 8 blockIdx.x ..; with the whole K in
 // one run it stores h [M, N / 2] = SiLU(gate) * up in bf16 instead of partials.
+namespace {
 template <int NW, int U, bool SWIGLU>
 __global__ __launch_bounds__(64 * NW) void skinny_gemm_kernel(const bf16_t* __restrict__ A,
                                                               const bf16_t* __restrict__ W,
                                                               const bf16_t* __restrict__ W2,
                                                               float* __restrict__ P, bf16_t* __restrict__ h, int M,
                                                               int N, int K, int KS) {
-    __shared__ float part[NW][kSkinnyRows][17];
-    const int wave = (int)(threadIdx.x >> 6), lane = lane_id();
-    const int n0 = blockIdx.x * 16, run = blockIdx.y;
-    const int r = lane & 15, kg = (lane >> 4) * 8;
-    const int kw = K / KS / NW, kb = run * (K / KS) + wave * kw;
-    const bf16_t* wp = (SWIGLU ? (r < 8 ? W + (int64_t)(n0 / 2 + r) * K : W2 + (int64_t)(n0 / 2 + r - 8) * K)
-                               : W + (int64_t)(n0 + r) * K) + kb + kg;
-    const bf16_t* ap[4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) ap[mt] = A + (int64_t)min(mt * 16 + r, M - 1) * K + kb + kg;
-    const f32x4 zero = {0, 0, 0, 0};
-    f32x4 acc[4] = {zero, zero, zero, zero};
-    for (int kk = 0; kk < kw; kk += 32 * U) {
-        u32x4 b[U], a[4][U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {  // branch-free: steps past the end repeat the last one, unused
-            const int k = min(kk + 32 * u, kw - 32);
-            b[u] = *reinterpret_cast<const u32x4*>(wp + k);
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) a[mt][u] = *reinterpret_cast<const u32x4*>(ap[mt] + k);
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            if (kk + 32 * u >= kw) continue;
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-                acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[mt][u]),
-                                                                  __builtin_bit_cast(bf16x8, b[u]), acc[mt], 0, 0, 0);
-        }
-    }
-    // D[row = 4 (lane / 16) + i][col = lane % 16] of each 16-row tile
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) part[wave][mt * 16 + 4 * (lane >> 4) + i][r] = acc[mt][i];
-    __syncthreads();
-    if (SWIGLU) {
-        for (int idx = threadIdx.x; idx < kSkinnyRows * 8; idx += 64 * NW) {
-            const int row = idx >> 3, c = idx & 7;
-            if (row >= M) continue;
-            float gv = part[0][row][c], uv = part[0][row][c + 8];
-#pragma unroll
-            for (int w = 1; w < NW; ++w) {
-                gv += part[w][row][c];
-                uv += part[w][row][c + 8];
-            }
-            h[(int64_t)row * (N / 2) + n0 / 2 + c] = f32_to_bf16(silu(gv) * uv);
-        }
-        return;
-    }
-    float* out = P + (int64_t)run * M * N;
-    for (int idx = threadIdx.x; idx < kSkinnyRows * 16; idx += 64 * NW) {
-        const int row = idx >> 4, col = idx & 15;
-        if (row >= M) continue;
-        float v = part[0][row][col];
-#pragma unroll
-        for (int w = 1; w < NW; ++w) v += part[w][row][col];
-        out[(int64_t)row * N + n0 + col] = v;
-    }
+    skinny_body<NW, U, SWIGLU>(A, W, W2, P, h, M, N, K, KS, (int)blockIdx.x, (int)blockIdx.y);
 }
 }  // namespace
 

@@ -47,6 +47,13 @@ bool route_block_ok(int dtype, int H, int E, int k);
 hipError_t launch_route_block(const void* x, const void* W, const float* bias, int64_t T, int H, int E, int k,
                               int norm, int32_t* idx, float* w, float* probs, uint16_t* masks, uint64_t* jmask,
                               int32_t* bcnt, int32_t* blist, hipStream_t st);
+// The same launch with the shared expert's gate/up product on further
+// workgroups (the CUs the router leaves idle): hs [T, Is] = SiLU(x sg^T) * (x su^T)
+// in bf16 (sg, su [Is, H]).  Needs route_shared_ok.
+bool route_shared_ok(int64_t T, int H, int Is);
+hipError_t launch_route_block_shared(const void* x, const void* W, const float* bias, int64_t T, int H, int E, int k,
+                                     int norm, int32_t* idx, float* w, int32_t* bcnt, int32_t* blist,
+                                     const void* sg, const void* su, int Is, void* hs, hipStream_t st);
 hipError_t launch_argmax(int dtype, const float* sc, const float* bd, const void* x, const void* W, int64_t T, int H,
                          int n, int32_t* out, hipStream_t st);
 // Draw per token from softmax(scores / tau) by inverse transform with the given

@@ -20,6 +20,7 @@
 // the tokens that chose the expert; grouping derives the stable per-expert
 // row order from these masks.
 #include "grouping.hpp"
+#include "skinny.hpp"
 
 namespace tmoe {
 
@@ -850,8 +851,9 @@ __device__ void route_exact_picks(const double* s, const double* cs, const int* 
     }
 }
 
+// The router of one block of 16 tokens (blockIdx.x): the body of route_block_kernel.
 template <int NS, int DEPTH>
-__global__ __launch_bounds__(kRouteThreads) void route_block_kernel(
+__device__ __forceinline__ void route_block_body(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ W, const float* __restrict__ bias, int64_t T, int H,
     int k, int norm, int32_t* __restrict__ out_idx, float* __restrict__ out_w, float* __restrict__ out_probs,
     uint16_t* __restrict__ masks, uint64_t* __restrict__ jmask, int mstride, int32_t* __restrict__ bcnt,
@@ -1093,6 +1095,34 @@ __global__ __launch_bounds__(kRouteThreads) void route_block_kernel(
         for (int e = tid; e < E; e += blockDim.x) cnt_b[e] = lcnt[e];
         for (int q = tid; q < E * 4; q += blockDim.x) list_b[q] = reinterpret_cast<const int4*>(llist)[q];
     }
+}
+
+template <int NS, int DEPTH>
+__global__ __launch_bounds__(kRouteThreads) void route_block_kernel(
+    const bf16_t* __restrict__ x, const bf16_t* __restrict__ W, const float* __restrict__ bias, int64_t T, int H,
+    int k, int norm, int32_t* __restrict__ out_idx, float* __restrict__ out_w, float* __restrict__ out_probs,
+    uint16_t* __restrict__ masks, uint64_t* __restrict__ jmask, int mstride, int32_t* __restrict__ bcnt,
+    int32_t* __restrict__ blist) {
+    route_block_body<NS, DEPTH>(x, W, bias, T, H, k, norm, out_idx, out_w, out_probs, masks, jmask, mstride, bcnt,
+                                blist);
+}
+
+// Blocks 0 .. ceil(T / 16) - 1 route (as route_block_kernel); the rest each
+// compute 8 features of the shared expert's gate/up product for all T <= 64
+// tokens (the 16-column skinny form over the whole K, one wave per K eighth).
+// The two kinds share no data; the router's blocks come first in dispatch.
+template <int NS, int DEPTH>
+__global__ __launch_bounds__(kRouteThreads) void route_shared_kernel(
+    const bf16_t* __restrict__ x, const bf16_t* __restrict__ W, const float* __restrict__ bias, int64_t T, int H,
+    int k, int norm, int32_t* __restrict__ out_idx, float* __restrict__ out_w, int mstride,
+    int32_t* __restrict__ bcnt, int32_t* __restrict__ blist, const bf16_t* __restrict__ sg,
+    const bf16_t* __restrict__ su, int Is, bf16_t* __restrict__ hs, int nroute) {
+    if ((int)blockIdx.x < nroute) {
+        route_block_body<NS, DEPTH>(x, W, bias, T, H, k, norm, out_idx, out_w, nullptr, nullptr, nullptr, mstride,
+                                    bcnt, blist);
+        return;
+    }
+    skinny_body<kRouteWaves, 4, true>(x, sg, su, nullptr, hs, (int)T, 2 * Is, H, 1, (int)blockIdx.x - nroute, 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -1682,6 +1712,37 @@ hipError_t launch_route_block(const void* x, const void* W, const float* bias, i
     else { TMOE_RB_E(1) }
 #undef TMOE_RB_E
 #undef TMOE_RB
+    return hipGetLastError();
+}
+
+bool route_shared_ok(int64_t T, int H, int Is) {
+    return T >= 1 && T <= kSkinnyRows && Is >= 8 && Is % 8 == 0 && H % (32 * kRouteWaves) == 0 &&
+           kRouteThreads == 64 * kRouteWaves;
+}
+
+hipError_t launch_route_block_shared(const void* x, const void* W, const float* bias, int64_t Ttok, int H, int E,
+                                     int k, int norm, int32_t* idx, float* w, int32_t* bcnt, int32_t* blist,
+                                     const void* sg, const void* su, int Is, void* hs, hipStream_t st) {
+    const int nroute = mask_words(Ttok);
+    const unsigned grid = (unsigned)(nroute + Is / 8);
+    const int mstride = mask_stride(Ttok);
+    const bf16_t* xb = (const bf16_t*)x;
+    const bf16_t* wb = (const bf16_t*)W;
+    const int nmine = H / (kRouteStageK * (kRouteWaves / (E / 16)));  // stages per wave
+#define TMOE_RS(NS, D)                                                                                             \
+    route_shared_kernel<NS, D><<<grid, kRouteThreads, 0, st>>>(xb, wb, bias, Ttok, H, k, norm, idx, w, mstride,     \
+                                                               bcnt, blist, (const bf16_t*)sg, (const bf16_t*)su, \
+                                                               Is, (bf16_t*)hs, nroute)
+#define TMOE_RS_E(D)                 \
+    if (E == 16) TMOE_RS(1, D);      \
+    else if (E == 32) TMOE_RS(2, D); \
+    else if (E == 64) TMOE_RS(4, D); \
+    else TMOE_RS(8, D);
+    if (nmine % 4 == 0) { TMOE_RS_E(4) }
+    else if (nmine % 2 == 0) { TMOE_RS_E(2) }
+    else { TMOE_RS_E(1) }
+#undef TMOE_RS_E
+#undef TMOE_RS
     return hipGetLastError();
 }
 
