@@ -17,9 +17,13 @@ namespace tmoe {
 namespace {
 
 constexpr int kHead = 128;                       // head width (64 pairs, one per lane)
-constexpr int kChunk = 128;                      // cached positions per partial
-constexpr int kAttnWaves = 4;
-constexpr int kKeysPerWave = kChunk / kAttnWaves;
+constexpr int kKeysPerWave = 32;  // cached positions per wave of the partial kernel
+// Waves per partial workgroup (a chunk is 32 positions per wave): 16 for long
+// caches, where fewer, longer chunks leave less to merge; 4 for short ones
+// (the predictor's 16-position frames), where idle waves would only cost.
+constexpr int kAttnWavesLong = 16, kAttnWavesShort = 4;
+__host__ __device__ constexpr int attn_waves(int max_len) { return max_len > 256 ? kAttnWavesLong : kAttnWavesShort; }
+__host__ __device__ constexpr int attn_chunk(int max_len) { return kKeysPerWave * attn_waves(max_len); }
 
 // One wave per (token, head of the fused q / k / v row), four heads per
 // workgroup; lane l owns pair l.  The row comes as KS fp32 partial products
@@ -166,7 +170,7 @@ __global__ __launch_bounds__(128) void attn_out_kernel(const float* __restrict__
 // and unnormalised output per head; an empty chunk writes m = -inf, l = 0.  When
 // the cache is a single chunk (nch == 1) the workgroup writes the normalised
 // output od [T, nq, 128] instead (zeros for a stream with no valid position).
-template <int G>
+template <int G, int kAttnWaves>
 __global__ __launch_bounds__(64 * kAttnWaves) void attn_partial_kernel(const bf16_t* __restrict__ q,
                                                                        const bf16_t* __restrict__ kc,
                                                                        const bf16_t* __restrict__ vt,
@@ -185,7 +189,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_partial_kernel(const bf1
     const int nraw = len[t];
     const int n = (nraw >= 0 && nraw < max_len) ? nraw + 1 : 0;
     const int64_t pidx = (t * nkv + g) * nch + c;
-    const int k0 = c * kChunk;
+    const int k0 = c * kKeysPerWave * kAttnWaves;
     const int nq = nkv * G;
     if (k0 >= n) {  // block-uniform
         if (nch == 1) {
@@ -337,7 +341,8 @@ __global__ __launch_bounds__(kHead) void attn_combine_kernel(const float* __rest
     const int dd = threadIdx.x;
     const int nraw = len[t];
     const int n = (nraw >= 0 && nraw < max_len) ? nraw + 1 : 0;
-    const int nc = (n + kChunk - 1) / kChunk;
+    const int chunk = attn_chunk(max_len);
+    const int nc = (n + chunk - 1) / chunk;
     const int64_t p0 = (t * nkv + g) * nch;
     float mx = -INFINITY;
     for (int c = 0; c < nc; ++c) mx = fmaxf(mx, pm[(p0 + c) * G + j]);
@@ -401,7 +406,7 @@ bool attn_decode_ok(int head_dim, int nq, int nkv, int max_len) {
     return G == 1 || G == 2 || G == 4 || G == 8;
 }
 
-int attn_chunks(int max_len) { return (max_len + kChunk - 1) / kChunk; }
+int attn_chunks(int max_len) { return (max_len + attn_chunk(max_len) - 1) / attn_chunk(max_len); }
 
 hipError_t launch_qk_rope_append(const float* qkv, int KS, int64_t T, int nq, int nkv, const float* q_gain,
                                  const float* k_gain, float eps, const int32_t* pos, const int32_t* len,
@@ -431,10 +436,17 @@ hipError_t launch_attn_decode(const void* q, const void* kc, const void* vc, con
     const int G = nq / nkv;
     const bf16_t *qb = (const bf16_t*)q, *kb = (const bf16_t*)kc, *vb = (const bf16_t*)vc;
     bf16_t* ob = (bf16_t*)o;
-    if (G == 8) attn_partial_kernel<8><<<grid, 64 * kAttnWaves, 0, st>>>(qb, kb, vb, len, nkv, max_len, nch, pm, pl, pacc, ob);
-    else if (G == 4) attn_partial_kernel<4><<<grid, 64 * kAttnWaves, 0, st>>>(qb, kb, vb, len, nkv, max_len, nch, pm, pl, pacc, ob);
-    else if (G == 2) attn_partial_kernel<2><<<grid, 64 * kAttnWaves, 0, st>>>(qb, kb, vb, len, nkv, max_len, nch, pm, pl, pacc, ob);
-    else attn_partial_kernel<1><<<grid, 64 * kAttnWaves, 0, st>>>(qb, kb, vb, len, nkv, max_len, nch, pm, pl, pacc, ob);
+#define TMOE_AP(GG, NW)                                                                                        \
+    attn_partial_kernel<GG, NW><<<grid, 64 * NW, 0, st>>>(qb, kb, vb, len, nkv, max_len, nch, pm, pl, pacc, ob)
+#define TMOE_AP_G(NW)                \
+    if (G == 8) TMOE_AP(8, NW);      \
+    else if (G == 4) TMOE_AP(4, NW); \
+    else if (G == 2) TMOE_AP(2, NW); \
+    else TMOE_AP(1, NW);
+    if (attn_waves(max_len) == kAttnWavesLong) { TMOE_AP_G(kAttnWavesLong) }
+    else { TMOE_AP_G(kAttnWavesShort) }
+#undef TMOE_AP_G
+#undef TMOE_AP
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || nch == 1) return e;  // a single chunk wrote the output itself
     attn_combine_kernel<<<dim3((unsigned)nq, (unsigned)T), kHead, 0, st>>>(pm, pl, pacc, len, nq, nkv, max_len, nch,

@@ -182,7 +182,7 @@ hipError_t launch_gather_rows(int dtype, const void* x, const int32_t* rows, int
 // --- decode-time attention (attention.hip) ---
 // head_dim 128, nq / nkv in {1, 2, 4, 8}, max_len a multiple of 32
 bool attn_decode_ok(int head_dim, int nq, int nkv, int max_len);
-int attn_chunks(int max_len);  // partials per (stream, KV head): 128 positions each
+int attn_chunks(int max_len);  // partials per (stream, KV head): 512 positions each (128 up to 256)
 // qkv: KS fp32 partials [KS][T][(nq + 2 nkv) 128] of the projection (summed in
 // order) -> q_out [T, nq, 128] (normalised, rotated), the new
 // key row at position len[t] of kc [T, nkv, max_len, 128] and the new value
