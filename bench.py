@@ -32,19 +32,23 @@ def log(msg):
     print("[bench] " + msg, file=sys.stderr, flush=True)
 
 
-def shared_in_router_launch(shape, T):
-    """Whether the library computes the shared expert's gate/up product in the
-    router's launch (up to 64 tokens, H a multiple of 256, I_s of 8) rather
-    than in the grouped gate/up pass."""
-    return shape.Is > 0 and 1 <= T <= 64 and shape.Is % 8 == 0 and shape.H % 256 == 0
+def decode_path(shape, T):
+    """Whether the library runs the decode-size layer (per-token router, one expert
+    launch over (expert, 64-wide slice) items, partial-row combine): at most 64
+    tokens, hidden 1024, E <= 128, k <= 8, I and I_s multiples of 64."""
+    return (1 <= T <= 64 and shape.H == 1024 and shape.E <= 128 and shape.k <= 8 and shape.I % 64 == 0
+            and shape.Is % 64 == 0)
 
 
 def layer_costs(shape, T, touched):
-    """Algorithmic bytes and flops of one layer step and of its gate/up pass.
+    """Algorithmic bytes and flops of one layer step and of its dominant kernel.
 
     Weight bytes count each touched expert once (bf16); activations count the
     token rows read and written once; routing outputs 8 bytes per (token, slot).
-    The gate/up pass counts the shared expert's gate/up only when it runs there.
+    At decode sizes the dominant kernel is the expert launch: every touched
+    expert's and the shared expert's weights plus the token rows it reads (its
+    partial output rows are design traffic, not counted).  Otherwise it is the
+    grouped gate/up pass.
     """
     H, E, k, I, Is = shape.H, shape.E, shape.k, shape.I, shape.Is
     expert_b = 3 * I * H * 2
@@ -52,33 +56,38 @@ def layer_costs(shape, T, touched):
     router_b = E * H * 2
     layer_bytes = touched * expert_b + shared_b + router_b + 2 * T * H * 2 + T * k * 8
     layer_flops = T * (2 * H * E + 6 * H * I * k + 6 * H * Is)
-    gu_bytes = touched * 2 * I * H * 2 + T * H * 2 + T * k * I * 2
-    gu_flops = T * 4 * H * I * k
-    if not shared_in_router_launch(shape, T):
-        gu_bytes += 2 * Is * H * 2 + T * Is * 2
-        gu_flops += T * 4 * H * Is
+    if decode_path(shape, T):
+        return layer_bytes, layer_flops, touched * expert_b + shared_b + T * H * 2, T * (6 * H * I * k + 6 * H * Is)
+    gu_bytes = touched * 2 * I * H * 2 + 2 * Is * H * 2 + T * H * 2 + T * k * I * 2 + T * Is * 2
+    gu_flops = T * (4 * H * I * k + 4 * H * Is)
     return layer_bytes, layer_flops, gu_bytes, gu_flops
 
 
+# Sources whose change invalidates the recorded HBM counters of the decode expert kernel.
+TRAFFIC_SOURCES = ("decode.hip", "common.hpp", "kernels.hpp", "api.hip")
+
+
 def measured_traffic():
-    """HBM bytes per launch of the decode gate/up kernel, from the rocprofv3
-    FETCH_SIZE / WRITE_SIZE summary in profiles/, scaled by the copy-kernel
-    calibration stated there; None when that summary is missing or the kernel
-    source has changed since the counters were taken."""
+    """HBM bytes per launch of the decode expert kernel from the rocprofv3
+    FETCH_SIZE / WRITE_SIZE summary in profiles/ (scaled by the copy-kernel
+    calibration stated there), with where they come from; (None, reason) when
+    the summary is missing or any source that shapes the kernel has changed
+    since the counters were taken."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "hbm_bytes_pmc.md")
     try:
         text = open(path).read()
         rec = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
     except (OSError, IndexError, ValueError):
-        return None
+        return None, "no counter record"
     h = hashlib.sha256()
-    for f in ("gemm.hip", "common.hpp"):
+    for f in TRAFFIC_SOURCES:
         with open(os.path.join(ROOT, "sparse_moe_transformer_talker_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     if h.hexdigest() != rec.get("source_sha256"):
-        return None
-    return float(rec["traffic_bytes_per_launch"])
+        return None, "the kernel's sources changed since the counters were taken"
+    return float(rec["traffic_bytes_per_launch"]), ("rocprofv3 FETCH_SIZE + WRITE_SIZE of this kernel source "
+                                                    "(profiles/hbm_bytes_pmc.md), not measured in this run")
 
 
 def pct(a, q):
@@ -155,8 +164,20 @@ def measure(api, torch, INP, shape, T, weight_sets, steps, warmup, bias=None):
     gpu_ms, wall = start.elapsed_time(stop), time.perf_counter() - t0
     eager_ms, _ = timed(lambda i: api.moe_layer_forward(cfg, structs[i % R], xs[i % R], y=ys[i % R], ws=ws))
 
+    # per-step times on the graph path: each layer's own graph replayed with an
+    # event recorded on the stream between consecutive replays
+    pev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    pev[0].record()
+    for i in range(steps):
+        graphs[i % R].replay()
+        pev[i + 1].record()
+    torch.cuda.synchronize()
+    graph_step_us = [pev[i].elapsed_time(pev[i + 1]) * 1e3 for i in range(steps)]
+
     # the same steps with HIP events at every stage boundary, on the library's stream
-    # (events 6 and 7 are timestamped by the gate/up kernel's own launch)
+    # (events 6 and 7 are timestamped by the dominant kernel's own launch: the
+    # decode expert kernel, or the gate/up pass at larger sizes)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(steps)]
     for row in evs:  # torch creates the HIP event on first record; the library re-records it
         for e in row:
@@ -165,7 +186,8 @@ def measure(api, torch, INP, shape, T, weight_sets, steps, warmup, bias=None):
     for i in range(steps):
         api.moe_layer_forward(cfg, structs[i % R], xs[i % R], y=ys[i % R], ws=ws, stage_events=evs[i])
     torch.cuda.synchronize()
-    names = ["route", "permute", "gate_up", "down", "combine"]
+    names = ["route", "permute", "experts" if decode_path(shape, T) else "gate_up",
+             "down" if not decode_path(shape, T) else "(none)", "combine"]
     stages = {n: [evs[i][j].elapsed_time(evs[i][j + 1]) * 1e3 for i in range(steps)] for j, n in enumerate(names)}
     step_us = [evs[i][0].elapsed_time(evs[i][5]) * 1e3 for i in range(steps)]
     gu_kernel_us = [evs[i][6].elapsed_time(evs[i][7]) * 1e3 for i in range(steps)]
@@ -181,9 +203,12 @@ def measure(api, torch, INP, shape, T, weight_sets, steps, warmup, bias=None):
         "tokens_per_s": T / s, "touched_experts": touched, "max_rows_per_expert": max_rows,
         "layer_bytes": lb, "layer_flops": lf, "layer_hbm_frac": lb / s / (HBM_PEAK_GBS * 1e9),
         "layer_mfma_frac": lf / s / (MFMA_BF16_PEAK_TFLOPS * 1e12),
-        "step_us": {"p50": pct(step_us, 50), "p95": pct(step_us, 95), "p99": pct(step_us, 99)},
-        "stages_us_mean": {n: float(np.mean(v)) for n, v in stages.items()},
-        "gate_up": {"bytes": gb, "flops": gf, "mean_us": gu_s * 1e6,
+        "step_us": {"p50": pct(graph_step_us, 50), "p95": pct(graph_step_us, 95), "p99": pct(graph_step_us, 99),
+                    "mean": float(np.mean(graph_step_us)),
+                    "timing": "per-replay events between single-layer graph replays (same rotation)"},
+        "eager_step_us": {"p50": pct(step_us, 50), "p95": pct(step_us, 95), "p99": pct(step_us, 99)},
+        "stages_us_mean": {n: float(np.mean(v)) for n, v in stages.items() if n != "(none)"},
+        "kernel": {"bytes": gb, "flops": gf, "mean_us": gu_s * 1e6,
                     "p50_us": pct(gu_kernel_us, 50), "p99_us": pct(gu_kernel_us, 99),
                     "timing": "kernel start/end timestamps of its own launch (hipExtLaunchKernel events)",
                     "gbs": gb / gu_s / 1e9, "tflops": gf / gu_s / 1e12},
@@ -482,22 +507,44 @@ def oracle_baselines(INP, shape, seconds):
     return out
 
 
-def cpu_baseline(INP, shape, T, seconds):
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(INP, shape, T, seconds, threads=None):
+    """The oracle (fp64 numpy, never tuned) timed for about `seconds` on one
+    Talker layer at T tokens; threads=1 limits BLAS to one thread."""
     from oracle import moe_ref as R
-    threads = blas_threads()
     w = INP.layer_weights(shape, 30, 0.02, "bf16")
     w64 = {k: INP.to_f64(v, "bf16") for k, v in w.items()}
     x64 = INP.to_f64(INP.activations(T, shape.H, 30, "bf16"), "bf16")
-    R.moe_layer(x64, w64, shape.k)  # first call outside the clock
-    n, t0 = 0, time.perf_counter()
-    while True:
-        R.moe_layer(x64, w64, shape.k)
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    return {"value": T * n / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": "fp64 numpy oracle, one Talker MoE layer at T=%d (seed 30), %d calls in %.1f s" % (T, n, el)}
+
+    def run():
+        R.moe_layer(x64, w64, shape.k)  # first call outside the clock
+        n, t0 = 0, time.perf_counter()
+        while True:
+            R.moe_layer(x64, w64, shape.k)
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                return n, el, blas_threads()
+
+    if threads is not None:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=threads, user_api="blas"):
+            n, el, used = run()
+    else:
+        n, el, used = run()
+    return {"value": T * n / el, "unit": "tokens/s", "cores": used, "kind": "oracle", "cpu_model": cpu_model(),
+            "host_cpus": os.cpu_count(),
+            "sample": "fp64 numpy oracle, one Talker MoE layer at T=%d (seed 30), %d calls in %.1f s with %d BLAS "
+                      "threads" % (T, n, el, used)}
 
 
 def main():
@@ -548,8 +595,8 @@ def main():
     if not args.no_decode:
         log("decode T=64")
         dec = measure(api, torch, INP, shape, 64, sets, args.steps, args.warmup)
-        log("decode: %.2f us/step, %.3f M tok/s, gate/up %.1f us" % (
-            dec["ms_per_step"] * 1e3, dec["tokens_per_s"] / 1e6, dec["gate_up"]["mean_us"]))
+        log("decode: %.2f us/step, %.3f M tok/s, expert kernel %.1f us" % (
+            dec["ms_per_step"] * 1e3, dec["tokens_per_s"] / 1e6, dec["kernel"]["mean_us"]))
     pre = None
     if not args.no_prefill:
         log("prefill T=4096")
@@ -608,10 +655,14 @@ def main():
     if dec is None:
         print(json.dumps({"prefill": pre}), flush=True)
         return
-    cpu = None
+    cpu = cpu_extra = None
     if not args.no_cpu_baseline:
-        log("cpu baseline (oracle, ~%.0f s)" % args.cpu_seconds)
-        cpu = cpu_baseline(INP, shape, 64, args.cpu_seconds)
+        log("cpu baseline (oracle): decode T=64 and prefill T=4096, all threads and one thread (~%.0f s)"
+            % (2 * args.cpu_seconds))
+        cpu = cpu_baseline(INP, shape, 64, args.cpu_seconds / 2)
+        cpu_extra = {"decode_T64_1thread": cpu_baseline(INP, shape, 64, args.cpu_seconds / 4, threads=1),
+                     "prefill_T4096": cpu_baseline(INP, shape, 4096, args.cpu_seconds / 2),
+                     "prefill_T4096_1thread": cpu_baseline(INP, shape, 4096, args.cpu_seconds / 4, threads=1)}
 
     extra_cpu = None
     if not args.no_cpu_baseline and (attn or tframe or pred):
@@ -619,7 +670,9 @@ def main():
             % (args.cpu_seconds / 3))
         extra_cpu = oracle_baselines(INP, shape, args.cpu_seconds / 3)
 
-    g = dec["gate_up"]
+    g = dec["kernel"]
+    traffic, traffic_source = measured_traffic()
+    layer_gbs = dec["layer_bytes"] / (dec["ms_per_step"] * 1e-3) / 1e9
     line = {
         "metric": METRIC,
         "value": dec["tokens_per_s"],
@@ -637,21 +690,27 @@ def main():
                    "experts": shape.E, "top_k": shape.k, "expert_intermediate": shape.I,
                    "shared_intermediate": shape.Is, "weight_sets_rotated": args.rotate},
         "roofline": {"bound": "hbm",
-                     "kernel": "grouped gate/up SwiGLU pass (routed experts; the shared expert's gate/up runs in "
-                               "the router's launch at this size)" if shared_in_router_launch(shape, 64)
-                               else "grouped gate/up SwiGLU pass (routed + shared)",
+                     "kernel": "decode expert kernel: every (expert, 64-wide slice) item of the touched routed "
+                               "experts and of the shared expert, gate/up + SwiGLU + partial down in one launch",
                      "achieved": g["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": g["gbs"] / HBM_PEAK_GBS, "traffic": measured_traffic(),
-                     "bytes_per_launch": g["bytes"], "mean_us": g["mean_us"]},
+                     "frac": g["gbs"] / HBM_PEAK_GBS, "traffic": traffic, "traffic_source": traffic_source,
+                     "bytes_per_launch": g["bytes"], "mean_us": g["mean_us"],
+                     "timing": g["timing"],
+                     "layer": {"achieved": layer_gbs, "frac": layer_gbs / HBM_PEAK_GBS,
+                               "bytes_per_step": dec["layer_bytes"], "us_per_step": dec["ms_per_step"] * 1e3,
+                               "timing": "the whole layer (route, experts, combine) per graph-timed step"}},
         "layer": {"hbm_frac": dec["layer_hbm_frac"], "mfma_frac": dec["layer_mfma_frac"],
                   "bytes_per_step": dec["layer_bytes"],
                   "timing": "HIP graph replay (the rotated layers back to back in one graph); "
                             "eager_ms_per_step without graphs",
                   "eager_ms_per_step": dec["eager_ms_per_step"],
-                  "step_us": dec["step_us"], "stages_us_mean": dec["stages_us_mean"],
+                  "step_us": dec["step_us"], "eager_step_us": dec["eager_step_us"],
+                  "stages_us_mean": dec["stages_us_mean"],
                   "touched_experts": dec["touched_experts"]},
         "cpu_baseline": cpu,
     }
+    if cpu_extra is not None:
+        line["cpu_baseline_more"] = cpu_extra
     if stack is not None:
         line["stack"] = stack
     if reports is not None:
@@ -668,7 +727,7 @@ def main():
                 line[key]["cpu_baseline"] = extra_cpu[key]
         line.setdefault("stack", {})["sampling_cpu_baseline"] = extra_cpu["sampling"]
     if pre is not None:
-        gp = pre["gate_up"]
+        gp = pre["kernel"]
         line["prefill"] = {"workload": "talker_moe_layer_prefill_T4096", "tokens_per_s": pre["tokens_per_s"],
                            "ms_per_step": pre["ms_per_step"], "eager_ms_per_step": pre["eager_ms_per_step"],
                            "mfma_frac": pre["layer_mfma_frac"],

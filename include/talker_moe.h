@@ -190,9 +190,12 @@ int moe_layer_forward(const moe_config* cfg, const moe_weights* w, const void* x
  * keep percentiles).  stage_events is NULL or an array of 8 hipEvent_t, each
  * NULL or created by the caller; events 0-5 are recorded on `stream`:
  *   0 before routing, 1 after routing, 2 after grouping, 3 after the gate/up
- *   pass of all experts, 4 after the down pass, 5 after the combine;
- * events 6 and 7 are timestamped by the gate/up kernel's own launch at its
- * start and end (hipExtLaunchKernel), so 6 -> 7 excludes dispatch latency.
+ *   pass of all experts, 4 after the down pass, 5 after the combine (at decode
+ *   sizes, T <= 64 of the Talker shape, there is no grouping launch and one
+ *   expert launch holds both passes: 1 = 2 and 3 = 4);
+ * events 6 and 7 are timestamped by the dominant kernel's own launch at its
+ * start and end (hipExtLaunchKernel): the expert launch at decode sizes, else
+ * the gate/up pass; so 6 -> 7 excludes dispatch latency.
  * Other arguments, results and errors are those of moe_layer_forward.
  */
 int moe_layer_forward_timed(const moe_config* cfg, const moe_weights* w, const void* x,

@@ -22,7 +22,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libtalker_moe.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 
-SOURCES = ["route.hip", "permute.hip", "gemm.hip", "elementwise.hip", "attention.hip", "api.hip"]
+SOURCES = ["route.hip", "permute.hip", "gemm.hip", "decode.hip", "elementwise.hip", "attention.hip", "api.hip"]
 HEADERS = ["common.hpp", "kernels.hpp"]
 
 ARCH = "gfx950"

@@ -118,6 +118,9 @@ struct LayerPlan {
     bool direct;
     int32_t *bcnt, *blist;
     void* hd;
+    // decode-size path (decode.hip): per-token router, one expert launch, partial rows
+    bool decode;
+    void* part;
 };
 // Small batches on the matrix-core path: the router writes per-block pair
 // lists and the expert products tile themselves from them (no grouping launch).
@@ -128,6 +131,10 @@ bool direct_ok(const moe_config* c, int64_t T, const GemmPlan& g) {
            route_block_ok(c->dtype, c->hidden_size, E, c->num_experts_per_tok) &&
            (int64_t)E * T * I * (int64_t)esize(c->dtype) <= (64ll << 20);
 }
+bool decode_ok(const moe_config* c, int64_t T) {
+    return decode_layer_ok(c->dtype, T, c->hidden_size, c->num_experts, c->num_experts_per_tok,
+                           c->moe_intermediate_size, c->shared_expert_intermediate_size);
+}
 void plan_layer(const moe_config* c, int64_t T, Carver& cv, LayerPlan& p) {
     const int E = c->num_experts, k = c->num_experts_per_tok, H = c->hidden_size;
     const int I = c->moe_intermediate_size, Is = c->shared_expert_intermediate_size;
@@ -135,6 +142,23 @@ void plan_layer(const moe_config* c, int64_t T, Carver& cv, LayerPlan& p) {
     const size_t es = esize(c->dtype);
     p.idx = cv.take<int32_t>(N);
     p.w = cv.take<float>(N);
+    p.decode = decode_ok(c, T);
+    if (p.decode) {
+        // everything else of the plan stays null: the decode path uses only these
+        p.route = RoutePlan{};
+        p.counts = cv.take<int32_t>(E);
+        p.part = cv.take<char>(T * decode_partial_rows(k, I, Is) * (int64_t)H * (int64_t)es);
+        p.hs = cv.take<char>(T * Is * (int64_t)es);
+        p.masks = nullptr;
+        p.jmask = nullptr;
+        p.prefix = p.offsets = p.row_token = p.row_of = p.row_pair = nullptr;
+        p.gemm = GemmPlan{};
+        p.hr = p.ybuf = p.hd = nullptr;
+        p.direct = false;
+        p.bcnt = p.blist = nullptr;
+        return;
+    }
+    p.part = nullptr;
     plan_route(c, T, cv, p.route);
     p.counts = cv.take<int32_t>(E);
     p.offsets = cv.take<int32_t>(E + 1);
@@ -457,6 +481,22 @@ int layer_run(const moe_config* cfg, const moe_weights* w, const void* x, const 
     const TileSpec* t2 = p.gemm.mfma ? &p.gemm.t[1] : nullptr;
     TMOE_TRY(mark(0));
     auto ev = [&](int i) { return stage_events ? static_cast<hipEvent_t>(stage_events[i]) : nullptr; };
+    if (p.decode) {
+        // route (one workgroup per token) -> every expert slice in one launch ->
+        // the partial rows summed per token with the routing weights
+        TMOE_TRY(launch_route_token(x, w->router, w->router_bias, T, H, E, k, cfg->norm_topk_prob, idx, wt,
+                                    Is > 0 ? w->shared_gate : nullptr, Is > 0 ? w->shared_up : nullptr, Is, p.hs, s));
+        TMOE_TRY(mark(1));
+        TMOE_TRY(mark(2));
+        TMOE_TRY(launch_decode_experts(x, idx, w->gate, w->up, w->down, p.hs, Is > 0 ? w->shared_down : nullptr,
+                                       p.part, counts, T, H, E, k, I, Is, s, ev(6), ev(7)));
+        TMOE_TRY(mark(3));
+        TMOE_TRY(mark(4));
+        TMOE_TRY(launch_combine_partials(p.part, I / 64, Is > 0 ? 1 : 0, k, wt, residual, y, T, H, end.gain, end.eps,
+                                         end.norm_out, s));
+        TMOE_TRY(mark(5));
+        return MOE_OK;
+    }
     if (p.direct) {
         // With at most 64 tokens the shared expert's gate/up runs in the router's
         // launch, on the CUs the router leaves idle; the gate/up pass then holds

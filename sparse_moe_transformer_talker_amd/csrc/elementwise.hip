@@ -214,6 +214,107 @@ __global__ __launch_bounds__(128) void combine_norm_bf16x8_kernel(const bf16_t* 
     rms_store_bf16x8<NCH>(yv, ok, inv, gain, norm_out + t * H);
 }
 
+// Partial-row combine of the decode layer.  Token t's partial rows are
+// part[t][0 .. NP) ([T, NP, H] bf16): rows j S .. j S + S - 1 add up to the
+// output of its j-th routed expert, rows k S .. NP - 1 to the shared expert's.
+//   y_t = sum_s part[t][k S + s] + sum_j w[t, j] (sum_s part[t][j S + s]) (+ residual_t)
+// summed in fp32 in exactly this order (bitwise reproducible), stored bf16;
+// norm_out (nullable) then receives RMSNorm(y_t) * gain with the same
+// reduction as rmsnorm_bf16x8_kernel, so the fused layer end and a separate
+// moe_rmsnorm call give the same bits.
+template <int NCH, int K, int S, int SSH>
+__global__ __launch_bounds__(128) void combine_partials_kernel(const bf16_t* __restrict__ part, int S_rt, int SSH_rt,
+                                                               int k_rt, const float* __restrict__ w,
+                                                               const bf16_t* residual, bf16_t* y, int64_t Ttok, int H,
+                                                               const float* __restrict__ gain, float eps,
+                                                               bf16_t* norm_out) {
+    const int64_t t = blockIdx.x;
+    if (t >= Ttok) return;
+    // K > 0: the sizes are compile-time, and every row of the token is loaded
+    // before the first add (one memory round trip)
+    const int k = K > 0 ? K : k_rt, s_n = K > 0 ? S : S_rt, ssh_n = K > 0 ? SSH : SSH_rt;
+    const int NP = k * s_n + ssh_n;
+    const bf16_t* prow = part + t * NP * (int64_t)H;
+    u32x4 yv[NCH];
+    bool ok[NCH];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int h = (threadIdx.x + 128 * c) * 8;
+        ok[c] = h < H;
+        yv[c] = u32x4{0, 0, 0, 0};
+        if (!ok[c]) continue;
+        float acc[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[q] = 0.f;
+        auto add = [&](float (&dst)[8], const u32x4& v) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                dst[2 * q] += __uint_as_float(v[q] << 16);
+                dst[2 * q + 1] += __uint_as_float(v[q] & 0xFFFF0000u);
+            }
+        };
+        auto row = [&](int r) { return *reinterpret_cast<const u32x4*>(prow + (int64_t)r * H + h); };
+        if (K > 0) {
+            constexpr int NPc = K * S + SSH;
+            u32x4 v[NPc > 0 ? NPc : 1];
+#pragma unroll
+            for (int r = 0; r < NPc; ++r) v[r] = row(r);
+            float wj[K > 0 ? K : 1];
+#pragma unroll
+            for (int j = 0; j < K; ++j) wj[j] = w[t * K + j];
+#pragma unroll
+            for (int r = 0; r < SSH; ++r) add(acc, v[K * S + r]);
+#pragma unroll
+            for (int j = 0; j < K; ++j) {
+                float e8[8];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) e8[q] = 0.f;
+#pragma unroll
+                for (int r = 0; r < S; ++r) add(e8, v[j * S + r]);
+#pragma unroll
+                for (int q = 0; q < 8; ++q) acc[q] = fmaf(wj[j], e8[q], acc[q]);
+            }
+        } else {
+            for (int r = 0; r < ssh_n; ++r) add(acc, row(k * s_n + r));
+            for (int j = 0; j < k; ++j) {
+                float e8[8];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) e8[q] = 0.f;
+                for (int r = 0; r < s_n; ++r) add(e8, row(j * s_n + r));
+                const float wj = w[t * k + j];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) acc[q] = fmaf(wj, e8[q], acc[q]);
+            }
+        }
+        if (residual) {
+            const u32x4 v = *reinterpret_cast<const u32x4*>(residual + t * H + h);
+            add(acc, v);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) yv[c][q] = pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
+        *reinterpret_cast<u32x4*>(y + t * H + h) = yv[c];
+    }
+    if (!norm_out) return;
+    const float inv = rms_inv_bf16x8<NCH>(yv, ok, H, eps);
+    rms_store_bf16x8<NCH>(yv, ok, inv, gain, norm_out + t * H);
+}
+
+hipError_t launch_combine_partials(const void* part, int S, int SSH, int k, const float* w, const void* residual,
+                                   void* y, int64_t Ttok, int H, const float* gain, float eps, void* norm_out,
+                                   hipStream_t st) {
+    if (Ttok <= 0) return hipSuccess;
+    if (H % 8 != 0 || H > 1024) return hipErrorInvalidValue;
+#define TMOE_CP(K_, S_, SSH_)                                                                               \
+    combine_partials_kernel<1, K_, S_, SSH_><<<(unsigned)Ttok, 128, 0, st>>>(                                  \
+        (const bf16_t*)part, S, SSH, k, w, (const bf16_t*)residual, (bf16_t*)y, Ttok, H, gain, eps,           \
+        (bf16_t*)norm_out)
+    if (k == 6 && S == 6 && SSH == 1) TMOE_CP(6, 6, 1);  // the Talker layer
+    else if (k == 6 && S == 6 && SSH == 0) TMOE_CP(6, 6, 0);
+    else TMOE_CP(0, 0, 0);
+#undef TMOE_CP
+    return hipGetLastError();
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const T* x, const float* __restrict__ gain, float eps,
                                                       int64_t Ttok, int H, T* out) {

@@ -179,6 +179,30 @@ hipError_t launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t st);
 hipError_t launch_gather_rows(int dtype, const void* x, const int32_t* rows, int64_t n, int H, void* out,
                               hipStream_t st);
 
+// Decode layer part of a partial-row combine (elementwise.hip): y [T, H] from the
+// partial rows [T, k S + SSH, H] of launch_decode_experts and the routing
+// weights w [T, k] (+ residual), then norm_out = RMSNorm(y) * gain when
+// norm_out is not null.  bf16, H % 8 == 0, H <= 1024.
+hipError_t launch_combine_partials(const void* part, int S, int SSH, int k, const float* w, const void* residual,
+                                   void* y, int64_t T, int H, const float* gain, float eps, void* norm_out,
+                                   hipStream_t st);
+
+// --- the decode-size layer (decode.hip) ---
+// bf16, 1 <= T <= 64, H == 1024, E <= 128, k <= 8, I a multiple of 64, Is a multiple of 128 (or 0).
+bool decode_layer_ok(int dtype, int64_t T, int H, int E, int k, int I, int Is);
+// partial rows per token: k I / 64 routed slots, then one slot for the shared expert (Is > 0)
+int decode_partial_rows(int k, int I, int Is);
+// idx [T, k], w [T, k]: top-k of the scores (certified, else fp64-rescored), ties
+// to the lower index; with Is > 0 also hs [T, Is] = SiLU(x sg^T) * (x su^T) in bf16
+hipError_t launch_route_token(const void* x, const void* W, const float* bias, int64_t T, int H, int E, int k,
+                              int norm, int32_t* idx, float* w, const void* sg, const void* su, int Is, void* hs,
+                              hipStream_t st);
+// part [T, decode_partial_rows, H] bf16 (see decode.hip), counts [E] (nullable)
+hipError_t launch_decode_experts(const void* x, const int32_t* idx, const void* gate, const void* up,
+                                 const void* down, const void* hs, const void* sdown, void* part, int32_t* counts,
+                                 int64_t T, int H, int E, int k, int I, int Is, hipStream_t st,
+                                 hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
+
 // --- decode-time attention (attention.hip) ---
 // head_dim 128, nq / nkv in {1, 2, 4, 8}, max_len a multiple of 32
 bool attn_decode_ok(int head_dim, int nq, int nkv, int max_len);
