@@ -61,6 +61,7 @@ extern "C" {
 #define MOE_ERR_UNSUPPORTED (-2) /* valid but outside the supported shapes / dtypes */
 #define MOE_ERR_WORKSPACE (-3)   /* ws_bytes below what the call needs */
 #define MOE_ERR_HIP (-4)         /* a HIP launch failed */
+#define MOE_ERR_SCRATCH (-5)     /* the call needs more than the static scratch (MOE_STATIC_SCRATCH_BYTES) */
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
@@ -202,6 +203,26 @@ int moe_layer_forward_timed(const moe_config* cfg, const moe_weights* w, const v
                             const void* residual, int64_t T, void* y, int32_t* topk_idx_out,
                             float* topk_w_out, int32_t* counts_out, void* ws, size_t ws_bytes,
                             void* stream, void* const* stage_events);
+
+/*
+ * moe_layer_forward_static — moe_layer_forward without a workspace argument,
+ * for callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  Its scratch is one
+ * file-scope device array of MOE_STATIC_SCRATCH_BYTES per GPU that the library
+ * is loaded on (held until the process ends); the call itself allocates
+ * nothing.  The decode-size layer (T <= 64 tokens of the Talker shape needs
+ * about 5 MB) fits; a call whose workspace would exceed the array returns
+ * MOE_ERR_SCRATCH before anything is enqueued.
+ *   The array of the current device is used (stream must belong to it); its
+ *   address is looked up on the first call on each device.  Every call on one
+ *   GPU shares that array, so calls that overlap on one GPU (two streams, two
+ *   host threads) race and must be serialised by the caller.  Arguments,
+ *   results and other errors are those of moe_layer_forward.
+ */
+#define MOE_STATIC_SCRATCH_BYTES ((size_t)8 << 20)
+int moe_layer_forward_static(const moe_config* cfg, const moe_weights* w, const void* x,
+                             const void* residual, int64_t T, void* y, int32_t* topk_idx_out,
+                             float* topk_w_out, int32_t* counts_out, void* stream);
 
 /*
  * moe_rmsnorm — out = x / sqrt(mean(x^2) + eps) * gain over each row of H

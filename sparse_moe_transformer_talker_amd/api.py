@@ -28,7 +28,7 @@ EXPORTS = ("moe_status_string", "moe_check_config", "moe_workspace_size", "moe_r
            "moe_codec_head_argmax", "moe_codec_head_workspace_size", "moe_stack_forward",
            "moe_stack_workspace_size", "moe_codec_head_sample", "moe_attention_decode",
            "moe_attention_workspace_size", "moe_predictor_frame", "moe_predictor_workspace_size",
-           "moe_talker_decode", "moe_talker_decode_workspace_size")
+           "moe_talker_decode", "moe_talker_decode_workspace_size", "moe_layer_forward_static")
 
 
 class MoeError(RuntimeError):
@@ -172,6 +172,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
                                              vp, sz, vp]),
         "moe_layer_forward_timed": (ctypes.c_int, [cfgp, ctypes.POINTER(moe_weights), vp, vp, i64, vp, vp, vp,
                                                    vp, vp, sz, vp, ctypes.POINTER(vp)]),
+        "moe_layer_forward_static": (ctypes.c_int, [cfgp, ctypes.POINTER(moe_weights), vp, vp, i64, vp, vp, vp,
+                                                    vp, vp]),
         "moe_rmsnorm": (ctypes.c_int, [cfgp, vp, vp, ctypes.c_float, i64, vp, vp]),
         "moe_codec_head_argmax": (ctypes.c_int, [cfgp, vp, vp, i32, i64, vp, vp, vp, sz, vp]),
         "moe_codec_head_workspace_size": (sz, [cfgp, i32, i64]),
@@ -350,6 +352,29 @@ def moe_layer_forward(cfg: Config, weights, x: torch.Tensor, residual: Optional[
             raise ValueError("at most 8 stage events")
         evs = (ctypes.c_void_p * 8)(*[None if e is None else e.cuda_event for e in stage_events])
         _check("moe_layer_forward_timed", lib.moe_layer_forward_timed(*args, evs))
+    return y
+
+
+# MOE_STATIC_SCRATCH_BYTES of include/talker_moe.h
+STATIC_SCRATCH_BYTES = 8 << 20
+MOE_ERR_SCRATCH = -5
+
+
+def moe_layer_forward_static(cfg: Config, weights, x: torch.Tensor, residual: Optional[torch.Tensor] = None,
+                             y=None, topk_idx=None, topk_w=None, counts=None, stream=None, check=True):
+    """moe_layer_forward on the library's static per-GPU scratch (no workspace
+    argument; the library allocates nothing).  Returns y, or the raw status when
+    check is False."""
+    T, dev = x.shape[0], x.device
+    y = y if y is not None else torch.empty_like(x)
+    ws_struct = weights if isinstance(weights, moe_weights) else weights_struct(weights)
+    st = stream if stream is not None else _stream(dev)
+    r = load_library().moe_layer_forward_static(ctypes.byref(cfg.c()), ctypes.byref(ws_struct), _ptr(x),
+                                                _ptr(residual), T, _ptr(y), _ptr(topk_idx), _ptr(topk_w),
+                                                _ptr(counts), st)
+    if not check:
+        return r
+    _check("moe_layer_forward_static", r)
     return y
 
 

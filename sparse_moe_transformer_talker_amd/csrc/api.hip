@@ -6,6 +6,8 @@
 
 #include <stdint.h>
 
+#include <mutex>
+
 #include "kernels.hpp"
 
 using namespace tmoe;
@@ -445,12 +447,13 @@ hipError_t finish_layer(int dtype, const void* ybuf, const float* w, int k, int 
     return launch_combine(dtype, ybuf, nullptr, w, k, slots, shared, sstride, residual, y, T, H, s);
 }
 
+// ws: the caller's workspace, or nullptr for the static scratch (not checked here)
 int check_layer_args(const moe_config* cfg, const moe_weights* w, const void* x, const void* residual,
-                     const void* y, const void* ws) {
+                     const void* y, const void* ws, bool static_scratch = false) {
     if (!w) return MOE_ERR_INVALID;
     const int Is = cfg->shared_expert_intermediate_size;
     if (!ok_ptr(x) || !ok_ptr(y) || !ok_opt(residual) || !ok_ptr(w->router) || !ok_opt(w->router_bias) ||
-        !ok_ptr(w->gate) || !ok_ptr(w->up) || !ok_ptr(w->down) || !ok_ptr(ws))
+        !ok_ptr(w->gate) || !ok_ptr(w->up) || !ok_ptr(w->down) || (!static_scratch && !ok_ptr(ws)))
         return MOE_ERR_INVALID;
     if (Is > 0 && (!ok_ptr(w->shared_gate) || !ok_ptr(w->shared_up) || !ok_ptr(w->shared_down)))
         return MOE_ERR_INVALID;
@@ -598,6 +601,7 @@ const char* moe_status_string(int status) {
         case MOE_ERR_UNSUPPORTED: return "unsupported shape or dtype";
         case MOE_ERR_WORKSPACE: return "workspace too small";
         case MOE_ERR_HIP: return "HIP launch failed";
+        case MOE_ERR_SCRATCH: return "the call needs more than the static scratch";
         default: return "unknown status";
     }
 }
@@ -747,6 +751,50 @@ int moe_layer_forward_timed(const moe_config* cfg, const moe_weights* w, const v
     if (ws_bytes < layer_ws(cfg, T)) return MOE_ERR_WORKSPACE;
     return layer_run(cfg, w, x, residual, T, y, topk_idx_out, topk_w_out, counts_out, ws, as_stream(stream),
                      stage_events, LayerEnd{});
+}
+
+}  // extern "C"
+
+namespace {
+// Scratch of moe_layer_forward_static: one array per GPU, for callers that
+// cannot allocate.  Host code never uses the array's name as an address: the
+// device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[MOE_STATIC_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int static_scratch(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return MOE_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int moe_layer_forward_static(const moe_config* cfg, const moe_weights* w, const void* x, const void* residual,
+                             int64_t T, void* y, int32_t* topk_idx_out, float* topk_w_out, int32_t* counts_out,
+                             void* stream) {
+    int st = check_cfg(cfg);
+    if (st != MOE_OK) return st;
+    if ((st = check_T(cfg, T)) != MOE_OK) return st;
+    if (T == 0) return MOE_OK;
+    if ((st = check_layer_args(cfg, w, x, residual, y, nullptr, true)) != MOE_OK) return st;
+    if (!ok_opt(topk_idx_out) || !ok_opt(topk_w_out) || !ok_opt(counts_out)) return MOE_ERR_INVALID;
+    if (layer_ws(cfg, T) > MOE_STATIC_SCRATCH_BYTES) return MOE_ERR_SCRATCH;
+    void* ws = nullptr;
+    if ((st = static_scratch(&ws)) != MOE_OK) return st;
+    return layer_run(cfg, w, x, residual, T, y, topk_idx_out, topk_w_out, counts_out, ws, as_stream(stream), nullptr,
+                     LayerEnd{});
 }
 
 size_t moe_stack_workspace_size(const moe_config* cfg, int64_t T, int32_t V) {

@@ -136,6 +136,25 @@ def test_layer_and_helper_argument_errors():
                                   None) == -1   # offsets required
 
 
+def test_static_scratch_entry_point_errors():
+    # moe_layer_forward_static checks everything on the host before its first HIP
+    # call: bad arguments, and workspaces beyond MOE_STATIC_SCRATCH_BYTES
+    lib = api.load_library()
+    c = _cfg()
+    w = api.moe_weights(FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    call = lambda T, **kw: lib.moe_layer_forward_static(
+        ctypes.byref(c), kw.get("w", ctypes.byref(w)), kw.get("x", _p()), None, T, kw.get("y", _p(4096)), None,
+        None, None, None)
+    assert call(64, x=None) == -1
+    assert call(64, y=_p()) == -1
+    assert call(-1) == -1
+    assert call(0) == 0
+    assert lib.moe_workspace_size(ctypes.byref(c), 64) <= api.STATIC_SCRATCH_BYTES  # the decode size fits
+    assert lib.moe_workspace_size(ctypes.byref(c), 4096) > api.STATIC_SCRATCH_BYTES
+    assert call(4096) == api.MOE_ERR_SCRATCH
+    assert api.status_string(api.MOE_ERR_SCRATCH) == "the call needs more than the static scratch"
+
+
 def test_stack_argument_errors():
     lib = api.load_library()
     c = _cfg()
