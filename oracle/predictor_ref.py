@@ -42,9 +42,11 @@ __all__ = ["decoder_layer", "predictor_frame"]
 
 def decoder_layer(x: np.ndarray, lw: Dict[str, np.ndarray], pos: np.ndarray, k_cache: np.ndarray,
                   v_cache: np.ndarray, cache_len: np.ndarray, n_heads: int, n_kv_heads: int, eps: float,
-                  theta: float, sections: Sequence[int]) -> np.ndarray:
+                  theta: float, sections: Sequence[int], parts=None) -> np.ndarray:
     """One pre-norm decoder layer for one new position per stream; appends its key and
-    value to the caches ([T, nkv, max_len, d], in place) at cache_len."""
+    value to the caches ([T, nkv, max_len, d], in place) at cache_len.  With ``parts``
+    (a list), appends (sub-layer output, residual state after it) for the attention
+    and then the MLP."""
     xa = R.rmsnorm(x, lw["in_norm"], eps)
     att = A.attention_decode(xa, lw, pos, k_cache, v_cache, cache_len, n_heads, n_kv_heads, theta, sections, eps)
     T = x.shape[0]
@@ -52,19 +54,27 @@ def decoder_layer(x: np.ndarray, lw: Dict[str, np.ndarray], pos: np.ndarray, k_c
         k_cache[t, :, int(cache_len[t])] = att["k_new"][t]
         v_cache[t, :, int(cache_len[t])] = att["v_new"][t]
     h = x + att["y"]
-    return h + R.swiglu(R.rmsnorm(h, lw["post_norm"], eps), lw["gate"], lw["up"], lw["down"])
+    m = R.swiglu(R.rmsnorm(h, lw["post_norm"], eps), lw["gate"], lw["up"], lw["down"])
+    if parts is not None:
+        parts += [(att["y"], h), (m, h + m)]
+    return h + m
 
 
 def predictor_frame(h_talker: np.ndarray, c0: np.ndarray, w: Dict, n_heads: int = 16, n_kv_heads: int = 8,
                     num_codes: int = 16, eps: float = 1e-6, theta: float = 1.0e6,
-                    sections: Sequence[int] = (24, 20, 20), forced=None) -> Dict[str, np.ndarray]:
+                    sections: Sequence[int] = (24, 20, 20), forced=None, trace: bool = False) -> Dict[str, np.ndarray]:
     """Codes c_0 .. c_{num_codes - 1} [num_codes, T] of one frame for T streams.
 
     w: "layers" (list of dicts: in_norm, post_norm, w_qkv, q_norm, k_norm, w_o, gate,
     up, down), "final_norm", "c0_embedding" [V0, H], "codec_embedding"
     [num_codes - 1, K, H], "lm_head" [num_codes - 1, K, H].  With ``forced`` [num_codes, T]
     (teacher forcing), position j + 1 embeds forced[j] instead of the code drawn at j;
-    the drawn codes are still returned.
+    the drawn codes are still returned.  With ``trace``, also per position: "sub_ms"
+    [num_codes, 2 L, T] the mean square over the hidden of every sub-layer's output
+    (attention, MLP, per layer), "resid_ms" [num_codes, 2 L, T] the mean square of
+    the residual state after each sub-layer, "resid_sq" [num_codes, T, H] the sum
+    over sub-layers of the squared residual state after each, and "h" [num_codes, T,
+    H] the state before the final norm.
     """
     h_talker = np.asarray(h_talker, np.float64)
     T, H = h_talker.shape
@@ -74,7 +84,7 @@ def predictor_frame(h_talker: np.ndarray, c0: np.ndarray, w: Dict, n_heads: int 
     vc = [np.zeros((T, n_kv_heads, num_codes, d)) for _ in range(L)]
     codes = np.zeros((num_codes, T), dtype=np.int64)
     codes[0] = np.asarray(c0)
-    finals = []
+    finals, sub_ms, resid_ms, resid_sq, pre = [], [], [], [], []
     for p in range(num_codes):
         if p == 0:
             x = h_talker
@@ -85,11 +95,21 @@ def predictor_frame(h_talker: np.ndarray, c0: np.ndarray, w: Dict, n_heads: int 
             x = np.asarray(w["codec_embedding"][p - 2], np.float64)[prev]
         pos = np.full((T, 3), p)
         lens = np.full(T, p)
+        parts = [] if trace else None
         for li, lw in enumerate(w["layers"]):
-            x = decoder_layer(x, lw, pos, kc[li], vc[li], lens, n_heads, n_kv_heads, eps, theta, sections)
+            x = decoder_layer(x, lw, pos, kc[li], vc[li], lens, n_heads, n_kv_heads, eps, theta, sections, parts)
         xf = R.rmsnorm(x, w["final_norm"], eps)
         finals.append(xf)
+        if trace:
+            sub_ms.append(np.stack([np.mean(o * o, axis=1) for o, _ in parts]))
+            resid_ms.append(np.stack([np.mean(r * r, axis=1) for _, r in parts]))
+            resid_sq.append(sum(r * r for _, r in parts))
+            pre.append(x)
         if p >= 1:
             logits = xf @ np.asarray(w["lm_head"][p - 1], np.float64).T
             codes[p] = R.argmax_first(logits)
-    return {"codes": codes, "final": np.stack(finals)}
+    out = {"codes": codes, "final": np.stack(finals)}
+    if trace:
+        out.update(sub_ms=np.stack(sub_ms), resid_ms=np.stack(resid_ms), resid_sq=np.stack(resid_sq),
+                   h=np.stack(pre))
+    return out

@@ -14,8 +14,11 @@
 * The stack entry point (each layer's combine, residual add and the next
   RMSNorm in one launch; T = 64, 333 and 4096, three layers, non-unit gains)
   against moe_rmsnorm + moe_layer_forward called layer by layer: bit for bit,
-  in place too; c_0 exact against the oracle's argmax of its final state; and
-  the whole stack with its head captured in one graph and replayed.
+  in place too; those calls against the oracle step by step (teacher forced,
+  with the same non-unit gains: every normalised input, every layer output and
+  its routing, the final norm); c_0 exact against the oracle's argmax of its
+  final state; and the whole stack with its head captured in one graph and
+  replayed.
 """
 import numpy as np
 import pytest
@@ -110,7 +113,7 @@ def test_layer_graph_replay(T):
     print("graph replay T=%d: 3 replays equal to eager" % T, flush=True)
 
 
-def _stack_inputs(T, L, dev):
+def _stack_inputs(T, L, dev, with_np=False):
     shape = INP.TALKER
     layers_np = [INP.layer_weights(shape, 30 + l, 0.02, "bf16") for l in range(L)]
     layers = [G.weights_dev(w, "bf16") for w in layers_np]
@@ -118,29 +121,52 @@ def _stack_inputs(T, L, dev):
     rng = np.random.default_rng(70)
     gains = torch.from_numpy((1.0 + 0.1 * rng.standard_normal((L + 1, shape.H))).astype(np.float32)).to(dev)
     x = G.dev(INP.activations(T, shape.H, 30, "bf16"), "bf16")
+    if with_np:
+        return shape, layers, G.dev(head_np, "bf16"), head_np, gains, x, layers_np
     return shape, layers, G.dev(head_np, "bf16"), head_np, gains, x
 
 
-def _layer_by_layer(cfg, layers, x, gains, eps, head):
+def _layer_by_layer(cfg, layers, x, gains, eps, head, layers_np=None, what=""):
+    """The stack as separate moe_rmsnorm + moe_layer_forward calls.  With layers_np,
+    every step is also checked against the oracle on the GPU's own input
+    (teacher forced): each normalised input with its non-unit gain, each layer's
+    output and routing."""
     h = x
+    k = cfg.num_experts_per_tok
+    T = x.shape[0]
+    idx = torch.empty((T, k), dtype=torch.int32, device=x.device)
     for l, wd in enumerate(layers):
         xn = api.moe_rmsnorm(cfg, h, gains[l], eps)
-        h = api.moe_layer_forward(cfg, wd, xn, h)
+        h_next = api.moe_layer_forward(cfg, wd, xn, h, topk_idx=idx)
+        if layers_np is not None:
+            torch.cuda.synchronize()
+            h64, xn64, g64 = G.host64(h), G.host64(xn), gains[l].double().cpu().numpy()
+            G.assert_close(xn64, R.rmsnorm(h64, g64, eps), "bf16", "%s layer %d input norm" % (what, l))
+            ref = R.moe_layer(xn64, G.weights_f64(layers_np[l], "bf16"), k, residual=h64)
+            np.testing.assert_array_equal(idx.cpu().numpy(), ref["idx"], err_msg="%s layer %d routing" % (what, l))
+            G.assert_close(G.host64(h_next), ref["y"], "bf16", "%s layer %d output" % (what, l))
+        h = h_next
     xf = api.moe_rmsnorm(cfg, h, gains[len(layers)], eps)
     c0, _ = api.moe_codec_head_argmax(cfg, xf, head)
+    if layers_np is not None:
+        torch.cuda.synchronize()
+        G.assert_close(G.host64(xf), R.rmsnorm(G.host64(h), gains[len(layers)].double().cpu().numpy(), eps),
+                       "bf16", "%s final norm" % what)
     return h, xf, c0
 
 
 @pytest.mark.parametrize("T", [64, 333, 4096])
 def test_stack_entry_point_matches_layer_by_layer(T):
     """moe_stack_forward (combine, residual and the next RMSNorm fused) equals
-    moe_rmsnorm + moe_layer_forward called layer by layer, bit for bit; its c_0 is
-    the exact argmax of the oracle's codec_head logits of its own final state."""
+    moe_rmsnorm + moe_layer_forward called layer by layer, bit for bit, and those
+    calls match the oracle step by step with the stack's non-unit gains (so the
+    fused path does too); its c_0 is the exact argmax of the oracle's codec_head
+    logits of its own final state."""
     dev = torch.device("cuda", 0)
     L, eps = 3, 1e-6
-    shape, layers, head, head_np, gains, x = _stack_inputs(T, L, dev)
+    shape, layers, head, head_np, gains, x, layers_np = _stack_inputs(T, L, dev, with_np=True)
     cfg = G.config(shape, "bf16")
-    h_ref, xf_ref, c0_ref = _layer_by_layer(cfg, layers, x, gains, eps, head)
+    h_ref, xf_ref, c0_ref = _layer_by_layer(cfg, layers, x, gains, eps, head, layers_np, "stack T=%d" % T)
     xn = torch.empty_like(x)
     h, _, c0 = api.moe_stack_forward(cfg, layers, x, gains, eps, head, xn_out=xn)
     torch.cuda.synchronize()

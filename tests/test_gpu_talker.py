@@ -5,15 +5,18 @@ moe_talker_decode fuses each seam (the attention's residual add with the
 post-attention RMSNorm, the MoE combine's residual add with the next input
 RMSNorm).  It must equal moe_rmsnorm + moe_attention_decode (with norm_out) +
 moe_layer_forward + moe_rmsnorm called layer by layer, bit for bit: the outputs,
-the final-normed state, c_0 and every layer's caches.  Each of those calls is
-checked against the oracle by its own tests; here c_0 is also checked as the
-exact argmax of the oracle's codec_head logits on the final state.  Then the
-step captured as one graph and replayed.
+the final-normed state, c_0 and every layer's caches.  Those calls are checked
+against the oracle step by step, teacher forced on the GPU's own state and with
+the layers' non-unit gains: every input norm, attention output, post-attention
+norm, MoE output and its routing.  c_0 is the exact argmax of the oracle's
+codec_head logits on the final state.  Then the step captured as one graph and
+replayed.
 """
 import numpy as np
 import pytest
 import torch
 
+from oracle import attention_ref as A
 from oracle import moe_ref as R
 from sparse_moe_transformer_talker_amd import api
 from sparse_moe_transformer_talker_amd import inputs as INP
@@ -68,15 +71,42 @@ def test_talker_decode_matches_layer_by_layer(T, L, max_len):
     head = G.dev(head_np, "bf16")
     eps = 1e-6
     ref_layers = _clone_caches(layers)
+    ashape = INP.TALKER_ATTN
+    lens, pos = ld.cpu().numpy(), pd.cpu().numpy()
+    g64 = lambda t: t.double().cpu().numpy()
+    idx = torch.empty((T, shape.k), dtype=torch.int32, device="cuda")
     h = x
     xa = api.moe_rmsnorm(cfg, x, ref_layers[0]["in_norm"], eps)
     for l, ly in enumerate(ref_layers):
+        # oracle inputs of this layer: the GPU's own state and the caches before the step
+        kc64 = G.host64(ly["k_cache"])
+        vc64 = np.ascontiguousarray(np.swapaxes(G.host64(ly["v_cache"]), 2, 3))
         xm = torch.empty_like(x)
         a = api.moe_attention_decode(acfg, ly["attn"], xa, pd, ld, ly["k_cache"], ly["v_cache"], residual=h,
                                      norm_gain=ly["post_norm"], norm_eps=eps, norm_out=xm)
-        h = api.moe_layer_forward(cfg, ly["moe"], xm, a)
+        h_next = api.moe_layer_forward(cfg, ly["moe"], xm, a, topk_idx=idx)
         nxt = ref_layers[l + 1]["in_norm"] if l + 1 < L else final
-        xa = api.moe_rmsnorm(cfg, h, nxt, eps)
+        xa_next = api.moe_rmsnorm(cfg, h_next, nxt, eps)
+        torch.cuda.synchronize()
+        # each call of the layer against the oracle, teacher forced, with the
+        # layer's non-unit gains (the fused decode step equals these calls bit
+        # for bit, below, so its norms are checked against the oracle too)
+        aw = INP.attention_weights(ashape, 100 + l)
+        aw64 = {"w_qkv": INP.to_f64(aw["w_qkv"], "bf16"), "w_o": INP.to_f64(aw["w_o"], "bf16"),
+                "q_norm": aw["q_norm"].astype(np.float64), "k_norm": aw["k_norm"].astype(np.float64)}
+        h64, xa64, a64, xm64 = G.host64(h), G.host64(xa), G.host64(a), G.host64(xm)
+        if l == 0:
+            G.assert_close(xa64, R.rmsnorm(h64, g64(ly["in_norm"]), eps), "bf16", "talker layer 0 input norm")
+        ra = A.attention_decode(xa64, aw64, pos, kc64, vc64, lens, ashape.n_heads, ashape.n_kv_heads, residual=h64)
+        G.assert_close(a64, ra["y"], "bf16", "talker layer %d attention" % l)
+        G.assert_close(xm64, R.rmsnorm(a64, g64(ly["post_norm"]), eps), "bf16", "talker layer %d post norm" % l)
+        rm = R.moe_layer(xm64, G.weights_f64(INP.layer_weights(shape, 30 + l, 0.02, "bf16"), "bf16"), shape.k,
+                         residual=a64)
+        np.testing.assert_array_equal(idx.cpu().numpy(), rm["idx"], err_msg="talker layer %d routing" % l)
+        G.assert_close(G.host64(h_next), rm["y"], "bf16", "talker layer %d moe" % l)
+        G.assert_close(G.host64(xa_next), R.rmsnorm(G.host64(h_next), g64(nxt), eps), "bf16",
+                       "talker layer %d next norm" % l)
+        h, xa = h_next, xa_next
     c0_ref, _ = api.moe_codec_head_argmax(cfg, xa, head)
     xn = torch.empty_like(x)
     h_out, _, c0 = api.moe_talker_decode(cfg, acfg, layers, x, pd, ld, final, eps, head, xn_out=xn)

@@ -41,7 +41,7 @@ def _from_scratch(h_talker, c0, w, nq, nkv, Q, eps=1e-6, theta=1.0e6, sections=(
     codes = np.zeros((Q, T), dtype=np.int64)
     codes[0] = c0
     inputs = [h_talker]
-    finals = []
+    finals, subs = [], []
     for p in range(Q):
         if p == 1:
             inputs.append(w["c0_embedding"][codes[0]])
@@ -62,21 +62,46 @@ def _from_scratch(h_talker, c0, w, nq, nkv, Q, eps=1e-6, theta=1.0e6, sections=(
             tk = torch.from_numpy(np.ascontiguousarray(k.transpose(0, 2, 1, 3))).repeat_interleave(nq // nkv, dim=1)
             tv = torch.from_numpy(np.ascontiguousarray(v.transpose(0, 2, 1, 3))).repeat_interleave(nq // nkv, dim=1)
             o = F.scaled_dot_product_attention(tq, tk, tv, is_causal=True).numpy().transpose(0, 2, 1, 3)
-            h = x + o.reshape(T, n, nq * d) @ lw["w_o"].T
-            x = h + R.swiglu(R.rmsnorm(h, lw["post_norm"], eps), lw["gate"], lw["up"], lw["down"])
+            a = o.reshape(T, n, nq * d) @ lw["w_o"].T
+            h = x + a
+            m = R.swiglu(R.rmsnorm(h, lw["post_norm"], eps), lw["gate"], lw["up"], lw["down"])
+            x = h + m
+            subs.append((p, a[:, -1], h[:, -1]))
+            subs.append((p, m[:, -1], x[:, -1]))
         xf = R.rmsnorm(x[:, -1], w["final_norm"], eps)
         finals.append(xf)
         if p >= 1:
             codes[p] = R.argmax_first(xf @ w["lm_head"][p - 1].T)
-    return codes, np.stack(finals)
+    return codes, np.stack(finals), subs
 
 
 def test_incremental_cache_equals_full_causal_recompute():
     w, h, c0 = _weights(1)
     got = P.predictor_frame(h, c0, w, n_heads=4, n_kv_heads=2, num_codes=6)
-    codes, finals = _from_scratch(h, c0, w, 4, 2, 6)
+    codes, finals, _ = _from_scratch(h, c0, w, 4, 2, 6)
     np.testing.assert_allclose(got["final"], finals, rtol=1e-10, atol=1e-10)
     np.testing.assert_array_equal(got["codes"], codes)
+
+
+def test_trace_matches_full_causal_recompute():
+    # the per-position sub-layer scales the parity bar is built from, against the
+    # recompute's own sub-layer outputs and residual states at the last position
+    w, h, c0 = _weights(4)
+    got = P.predictor_frame(h, c0, w, n_heads=4, n_kv_heads=2, num_codes=6, trace=True)
+    plain = P.predictor_frame(h, c0, w, n_heads=4, n_kv_heads=2, num_codes=6)
+    np.testing.assert_array_equal(got["final"], plain["final"])
+    _, finals, subs = _from_scratch(h, c0, w, 4, 2, 6)
+    L = len(w["layers"])
+    for p in range(6):
+        mine = [s for s in subs if s[0] == p]
+        assert len(mine) == 2 * L
+        np.testing.assert_allclose(got["sub_ms"][p], np.stack([np.mean(o * o, axis=1) for _, o, _ in mine]),
+                                   rtol=1e-9)
+        np.testing.assert_allclose(got["resid_ms"][p], np.stack([np.mean(r * r, axis=1) for _, _, r in mine]),
+                                   rtol=1e-9)
+        np.testing.assert_allclose(got["resid_sq"][p], sum(r * r for _, _, r in mine), rtol=1e-9)
+        np.testing.assert_allclose(got["h"][p], mine[-1][2], rtol=1e-9, atol=1e-12)
+        np.testing.assert_allclose(R.rmsnorm(got["h"][p], w["final_norm"]), finals[p], rtol=1e-9, atol=1e-12)
 
 
 def test_identity_layers_give_closed_form_codes():
