@@ -33,8 +33,9 @@ def log(msg):
 
 
 def decode_path(shape, T):
-    """Whether the library runs the decode-size layer (per-token router, one expert
-    launch over (expert, 64-wide slice) items, partial-row combine): at most 64
+    """Whether the library runs the decode-size layer (router scores and per-token
+    selection, one expert launch over (expert, 64-wide slice) items and the shared
+    expert's slices, partial-row combine): at most 64
     tokens, hidden 1024, E <= 128, k <= 8, I and I_s multiples of 64."""
     return (1 <= T <= 64 and shape.H == 1024 and shape.E <= 128 and shape.k <= 8 and shape.I % 64 == 0
             and shape.Is % 64 == 0)

@@ -120,9 +120,12 @@ struct LayerPlan {
     bool direct;
     int32_t *bcnt, *blist;
     void* hd;
-    // decode-size path (decode.hip): per-token router, one expert launch, partial rows
+    // decode-size path (decode.hip): spread router scores, per-token selection,
+    // one expert launch, partial rows
     bool decode;
     void* part;
+    double *sc, *dv;
+    uint32_t* mask;
 };
 // Small batches on the matrix-core path: the router writes per-block pair
 // lists and the expert products tile themselves from them (no grouping launch).
@@ -150,6 +153,9 @@ void plan_layer(const moe_config* c, int64_t T, Carver& cv, LayerPlan& p) {
         p.route = RoutePlan{};
         p.counts = cv.take<int32_t>(E);
         p.part = cv.take<char>(T * decode_partial_rows(k, I, Is) * (int64_t)H * (int64_t)es);
+        p.sc = cv.take<double>(T * E);
+        p.dv = cv.take<double>(T * E);
+        p.mask = cv.take<uint32_t>(4);
         p.hs = cv.take<char>(T * Is * (int64_t)es);
         p.masks = nullptr;
         p.jmask = nullptr;
@@ -161,6 +167,8 @@ void plan_layer(const moe_config* c, int64_t T, Carver& cv, LayerPlan& p) {
         return;
     }
     p.part = nullptr;
+    p.sc = p.dv = nullptr;
+    p.mask = nullptr;
     plan_route(c, T, cv, p.route);
     p.counts = cv.take<int32_t>(E);
     p.offsets = cv.take<int32_t>(E + 1);
@@ -485,14 +493,16 @@ int layer_run(const moe_config* cfg, const moe_weights* w, const void* x, const 
     TMOE_TRY(mark(0));
     auto ev = [&](int i) { return stage_events ? static_cast<hipEvent_t>(stage_events[i]) : nullptr; };
     if (p.decode) {
-        // route (one workgroup per token) -> every expert slice in one launch ->
-        // the partial rows summed per token with the routing weights
-        TMOE_TRY(launch_route_token(x, w->router, w->router_bias, T, H, E, k, cfg->norm_topk_prob, idx, wt,
-                                    Is > 0 ? w->shared_gate : nullptr, Is > 0 ? w->shared_up : nullptr, Is, p.hs, s));
+        // scores (and the shared gate/up) -> selection -> every expert slice and
+        // the shared down tiles in one launch -> the partial rows summed per
+        // token with the routing weights
+        TMOE_TRY(launch_route_decode(x, w->router, w->router_bias, T, H, E, k, cfg->norm_topk_prob, p.sc, p.dv, idx,
+                                     wt, Is > 0 ? w->shared_gate : nullptr, Is > 0 ? w->shared_up : nullptr, Is, p.hs,
+                                     p.mask, counts, s));
         TMOE_TRY(mark(1));
         TMOE_TRY(mark(2));
-        TMOE_TRY(launch_decode_experts(x, idx, w->gate, w->up, w->down, p.hs, Is > 0 ? w->shared_down : nullptr,
-                                       p.part, counts, T, H, E, k, I, Is, s, ev(6), ev(7)));
+        TMOE_TRY(launch_decode_experts(x, idx, p.mask, w->gate, w->up, w->down, p.hs,
+                                       Is > 0 ? w->shared_down : nullptr, p.part, T, H, E, k, I, Is, s, ev(6), ev(7)));
         TMOE_TRY(mark(3));
         TMOE_TRY(mark(4));
         TMOE_TRY(launch_combine_partials(p.part, I / 64, Is > 0 ? 1 : 0, k, wt, residual, y, T, H, end.gain, end.eps,

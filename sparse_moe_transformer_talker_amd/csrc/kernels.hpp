@@ -188,18 +188,21 @@ hipError_t launch_combine_partials(const void* part, int S, int SSH, int k, cons
                                    hipStream_t st);
 
 // --- the decode-size layer (decode.hip) ---
-// bf16, 1 <= T <= 64, H == 1024, E <= 128, k <= 8, I a multiple of 64, Is a multiple of 128 (or 0).
+// bf16, 1 <= T <= 64, H == 1024, k <= E <= 128, k <= 8, I a multiple of 64, Is a multiple of 128 (or 0).
 bool decode_layer_ok(int dtype, int64_t T, int H, int E, int k, int I, int Is);
 // partial rows per token: k I / 64 routed slots, then one slot for the shared expert (Is > 0)
 int decode_partial_rows(int k, int I, int Is);
 // idx [T, k], w [T, k]: top-k of the scores (certified, else fp64-rescored), ties
-// to the lower index; with Is > 0 also hs [T, Is] = SiLU(x sg^T) * (x su^T) in bf16
-hipError_t launch_route_token(const void* x, const void* W, const float* bias, int64_t T, int H, int E, int k,
-                              int norm, int32_t* idx, float* w, const void* sg, const void* su, int Is, void* hs,
-                              hipStream_t st);
-// part [T, decode_partial_rows, H] bf16 (see decode.hip), counts [E] (nullable)
-hipError_t launch_decode_experts(const void* x, const int32_t* idx, const void* gate, const void* up,
-                                 const void* down, const void* hs, const void* sdown, void* part, int32_t* counts,
+// to the lower index; sc, dv [T, E] fp64 scratch (the scores and their bounds);
+// mask [4] the touched experts, counts [E] the pairs per expert; with Is > 0
+// also hs [T, Is] = SiLU(x sg^T) * (x su^T) in bf16
+hipError_t launch_route_decode(const void* x, const void* W, const float* bias, int64_t T, int H, int E, int k,
+                               int norm, double* sc, double* dv, int32_t* idx, float* w, const void* sg,
+                               const void* su, int Is, void* hs, uint32_t* mask, int32_t* counts, hipStream_t st);
+// part [T, decode_partial_rows, H] bf16 (see decode.hip) from the routing (idx and
+// the mask of launch_route_decode)
+hipError_t launch_decode_experts(const void* x, const int32_t* idx, const uint32_t* mask, const void* gate,
+                                 const void* up, const void* down, const void* hs, const void* sdown, void* part,
                                  int64_t T, int H, int E, int k, int I, int Is, hipStream_t st,
                                  hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 

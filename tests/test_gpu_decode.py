@@ -1,6 +1,8 @@
 """Parity of the decode-size layer path (at most 64 tokens, hidden 1024): the
-per-token router, the expert kernel over (expert, 64-wide slice) items with its
-two forms (K-split up to 16 rows, M-split above), and the partial-row combine.
+router's score launch (with the shared expert's gate/up) and per-token
+selection, the expert kernel over (touched expert, 64-wide slice) items with its
+two forms (K-split up to 16 rows, M-split above) and the shared down tiles, and
+the partial-row combine.
 
 Bars as everywhere: indices and per-expert counts bit-exact against the fp64
 oracle (ties to the lower expert index); outputs within max-abs 2e-2 and
