@@ -398,6 +398,44 @@ int moe_talker_decode(const moe_config* cfg, const moe_attn_config* acfg, const 
 size_t moe_talker_decode_workspace_size(const moe_config* cfg, const moe_attn_config* acfg, int64_t T, int32_t V);
 
 /*
+ * moe_talker_frame — one 80 ms frame of T streams of the Dual-Track loop ("Bài
+ * Lab tổng hợp — Qwen3-Omni & Qwen3-TTS-12Hz Architecture", steps [3B] and
+ * [4A]; "3C · Talker MoE" §2, the pair [h_talker, c_0] handed to the code
+ * predictor):
+ *   x = prev_emb + cond (rounded to bf16);
+ *   the Talker step through layers[0 .. L) as moe_talker_decode (keys and values
+ *   appended at cache_len, queries at pos), its final-normed state xn and c_0;
+ *   codes = moe_predictor_frame(xn, c_0);
+ *   prev_emb = the mean of the frame's num_codes code embeddings (c_0 from the
+ *   predictor's c0_embedding, c_j from codec_embedding table j - 1; a code
+ *   outside its table is a zero row), summed in fp32 and rounded to bf16;
+ *   pos (all three indices) and cache_len advance by one.
+ * Every step runs on the stream from device data, so one captured graph replays
+ * frame after frame: between replays the caller only writes the next cond.
+ * Results equal moe_talker_decode on x, then moe_predictor_frame, bit for bit.
+ *   cond      [dev] [T, hidden] bf16: the frame's text condition (the trailing
+ *             text hidden state, or the pad embedding once the text has run out)
+ *   prev_emb  [dev] [T, hidden] bf16, in/out: the previous frame's audio embedding
+ *             (the codec BOS embedding before the first frame); the frame's own on return
+ *   pos       [dev] [T, 3] int32, in/out;  cache_len [dev] [T] int32, in/out
+ *   codes     [dev] [num_codes, T] int32 out (row 0 = c_0)
+ *   h_out, xn_out  [dev] [T, hidden] bf16 out or NULL: the Talker's last hidden
+ *             state and its final-normed state
+ *   codec_head [dev] [V, hidden] (V >= 1); final_norm as moe_talker_decode
+ * 1 <= T <= 64; bf16; the predictor's hidden size equals the Talker's.
+ * Workspace: moe_talker_frame_workspace_size(cfg, acfg, pcfg, T, V).
+ */
+int moe_talker_frame(const moe_config* cfg, const moe_attn_config* acfg, const moe_talker_layer* layers, int32_t L,
+                     const float* final_norm, float eps, const void* codec_head, int32_t V,
+                     const moe_predictor_config* pcfg, const moe_predictor_weights* pw, const void* cond, int64_t T,
+                     void* prev_emb, int32_t* pos, int32_t* cache_len, int32_t* codes, void* h_out, void* xn_out,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes for moe_talker_frame (0 for an invalid or unsupported case). Host only. */
+size_t moe_talker_frame_workspace_size(const moe_config* cfg, const moe_attn_config* acfg,
+                                       const moe_predictor_config* pcfg, int64_t T, int32_t V);
+
+/*
  * moe_codec_head_sample — c_0 drawn from the softmax of the codec head's logits
  * ("用 print(model) 认识 Qwen3-TTS", "Codec Head：语义码预测": the 3072 logits go
  * through a softmax and the next semantic code is sampled).  Inverse transform

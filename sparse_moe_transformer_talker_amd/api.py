@@ -28,7 +28,8 @@ EXPORTS = ("moe_status_string", "moe_check_config", "moe_workspace_size", "moe_r
            "moe_codec_head_argmax", "moe_codec_head_workspace_size", "moe_stack_forward",
            "moe_stack_workspace_size", "moe_codec_head_sample", "moe_attention_decode",
            "moe_attention_workspace_size", "moe_predictor_frame", "moe_predictor_workspace_size",
-           "moe_talker_decode", "moe_talker_decode_workspace_size", "moe_layer_forward_static")
+           "moe_talker_decode", "moe_talker_decode_workspace_size", "moe_layer_forward_static",
+           "moe_talker_frame", "moe_talker_frame_workspace_size")
 
 
 class MoeError(RuntimeError):
@@ -192,6 +193,12 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
                                              i32, vp, i64, vp, vp, vp, ctypes.c_float, vp, i32, vp, vp, vp, vp, sz,
                                              vp]),
         "moe_talker_decode_workspace_size": (sz, [cfgp, ctypes.POINTER(moe_attn_config), i64, i32]),
+        "moe_talker_frame": (ctypes.c_int, [cfgp, ctypes.POINTER(moe_attn_config), ctypes.POINTER(moe_talker_layer),
+                                            i32, vp, ctypes.c_float, vp, i32, ctypes.POINTER(moe_predictor_config),
+                                            ctypes.POINTER(moe_predictor_weights), vp, i64, vp, vp, vp, vp, vp, vp,
+                                            vp, sz, vp]),
+        "moe_talker_frame_workspace_size": (sz, [cfgp, ctypes.POINTER(moe_attn_config),
+                                                 ctypes.POINTER(moe_predictor_config), i64, i32]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -521,6 +528,34 @@ def talker_layers_struct(layers) -> ctypes.Array:
     return (moe_talker_layer * len(layers))(*[
         moe_talker_layer(mk(l["moe"]), ma(l["attn"]), _ptr(l.get("in_norm")), _ptr(l.get("post_norm")),
                          _ptr(l["k_cache"]), _ptr(l["v_cache"])) for l in layers])
+
+
+def moe_talker_frame_workspace_size(cfg: Config, acfg: AttnConfig, pcfg: PredictorConfig, T: int, V: int) -> int:
+    return int(load_library().moe_talker_frame_workspace_size(ctypes.byref(cfg.c()), ctypes.byref(acfg.c()),
+                                                              ctypes.byref(pcfg.c()), T, V))
+
+
+def moe_talker_frame(cfg: Config, acfg: AttnConfig, layers, final_norm, eps: float, codec_head: torch.Tensor,
+                     pcfg: PredictorConfig, pweights, cond: torch.Tensor, prev_emb: torch.Tensor, pos: torch.Tensor,
+                     cache_len: torch.Tensor, codes=None, h_out=None, xn_out=None, ws=None, stream=None):
+    """One frame of the Dual-Track loop (caches, prev_emb, pos and cache_len updated in place).  ``layers``: list
+    of dicts (see talker_layers_struct) or a prebuilt array; ``pweights``: predictor weight dict or struct.
+    Returns codes [num_codes, T] int32 (row 0 = c_0)."""
+    T, dev = cond.shape[0], cond.device
+    arr = layers if isinstance(layers, ctypes.Array) else talker_layers_struct(layers)
+    pw = pweights if isinstance(pweights, moe_predictor_weights) else predictor_weights_struct(pweights)
+    codes = codes if codes is not None else torch.empty((pcfg.num_codes, T), dtype=torch.int32, device=dev)
+    V = codec_head.shape[0]
+    lib = load_library()
+    c, a, p = cfg.c(), acfg.c(), pcfg.c()
+    buf = ws if ws is not None else workspace(
+        int(lib.moe_talker_frame_workspace_size(ctypes.byref(c), ctypes.byref(a), ctypes.byref(p), T, V)), dev)
+    st = stream if stream is not None else _stream(dev)
+    _check("moe_talker_frame", lib.moe_talker_frame(
+        ctypes.byref(c), ctypes.byref(a), arr, len(arr), _ptr(final_norm), eps, _ptr(codec_head), V, ctypes.byref(p),
+        ctypes.byref(pw), _ptr(cond), T, _ptr(prev_emb), _ptr(pos), _ptr(cache_len), _ptr(codes), _ptr(h_out),
+        _ptr(xn_out), _ptr(buf), buf.numel(), st))
+    return codes
 
 
 def moe_talker_decode(cfg: Config, acfg: AttnConfig, layers, x: torch.Tensor, pos: torch.Tensor,

@@ -368,6 +368,20 @@ moe_attn_config pred_attn_cfg(const moe_predictor_config* c) {
     a.max_len = (c->num_codes + 31) / 32 * 32;
     return a;
 }
+// Every weight pointer of the predictor present and 16-byte aligned.
+bool pred_weights_ok(const moe_predictor_config* c, const moe_predictor_weights* w) {
+    if (!w || !w->layers || !ok_ptr(w->final_norm) || !ok_ptr(w->c0_embedding) || !ok_ptr(w->codec_embedding) ||
+        !ok_ptr(w->lm_head))
+        return false;
+    for (int l = 0; l < c->num_layers; ++l) {
+        const moe_predictor_layer& L = w->layers[l];
+        if (!ok_ptr(L.attn.w_qkv) || !ok_ptr(L.attn.q_norm) || !ok_ptr(L.attn.k_norm) || !ok_ptr(L.attn.w_o) ||
+            !ok_ptr(L.in_norm) || !ok_ptr(L.post_norm) || !ok_ptr(L.gate) || !ok_ptr(L.up) || !ok_ptr(L.down))
+            return false;
+    }
+    return true;
+}
+
 int check_pred_cfg(const moe_predictor_config* c, int64_t T) {
     if (!c) return MOE_ERR_INVALID;
     const moe_attn_config a = pred_attn_cfg(c);
@@ -870,10 +884,15 @@ size_t moe_talker_decode_workspace_size(const moe_config* cfg, const moe_attn_co
     return cv.size();
 }
 
-int moe_talker_decode(const moe_config* cfg, const moe_attn_config* acfg, const moe_talker_layer* layers, int32_t L,
-                      const void* x, int64_t T, const int32_t* pos, const int32_t* cache_len, const float* final_norm,
-                      float eps, const void* codec_head, int32_t V, void* h_out, void* xn_out, int32_t* c0, void* ws,
-                      size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+// The Talker decode step; with x_add the input is x + x_add (rounded to bf16,
+// stored in xsum and used as layer 0's residual).
+int talker_run(const moe_config* cfg, const moe_attn_config* acfg, const moe_talker_layer* layers, int32_t L,
+               const void* x, const void* x_add, void* xsum, int64_t T, const int32_t* pos, const int32_t* cache_len,
+               const float* final_norm, float eps, const void* codec_head, int32_t V, void* h_out, void* xn_out,
+               int32_t* c0, void* ws, size_t ws_bytes, void* stream) {
     int st = check_cfg(cfg);
     if (st != MOE_OK) return st;
     if ((st = check_T(cfg, T)) != MOE_OK) return st;
@@ -906,7 +925,12 @@ int moe_talker_decode(const moe_config* cfg, const moe_attn_config* acfg, const 
             return MOE_ERR_INVALID;
     }
     hipStream_t s = as_stream(stream);
-    TMOE_TRY(launch_rmsnorm(cfg->dtype, x, layers[0].in_norm, eps, T, H, xa, s));
+    if (x_add) {
+        TMOE_TRY(launch_add_rmsnorm(x, x_add, xsum, layers[0].in_norm, eps, T, H, xa, s));
+        x = xsum;
+    } else {
+        TMOE_TRY(launch_rmsnorm(cfg->dtype, x, layers[0].in_norm, eps, T, H, xa, s));
+    }
     for (int l = 0; l < L; ++l) {
         const moe_talker_layer& ly = layers[l];
         int r = attn_run(acfg, &ly.attn, ap, xa, T, pos, cache_len, ly.k_cache, ly.v_cache, l == 0 ? x : h_out, hmid,
@@ -922,6 +946,75 @@ int moe_talker_decode(const moe_config* cfg, const moe_attn_config* acfg, const 
     if (!c0) return MOE_OK;
     return moe_codec_head_argmax(cfg, xf, codec_head, V, T, nullptr, c0, hws, moe_codec_head_workspace_size(cfg, V, T),
                                  stream);
+}
+}  // namespace
+
+extern "C" {
+
+int moe_talker_decode(const moe_config* cfg, const moe_attn_config* acfg, const moe_talker_layer* layers, int32_t L,
+                      const void* x, int64_t T, const int32_t* pos, const int32_t* cache_len, const float* final_norm,
+                      float eps, const void* codec_head, int32_t V, void* h_out, void* xn_out, int32_t* c0, void* ws,
+                      size_t ws_bytes, void* stream) {
+    return talker_run(cfg, acfg, layers, L, x, nullptr, nullptr, T, pos, cache_len, final_norm, eps, codec_head, V,
+                      h_out, xn_out, c0, ws, ws_bytes, stream);
+}
+
+size_t moe_talker_frame_workspace_size(const moe_config* cfg, const moe_attn_config* acfg,
+                                       const moe_predictor_config* pcfg, int64_t T, int32_t V) {
+    if (!pcfg || check_pred_cfg(pcfg, T) != MOE_OK || V < 1 || T < 1) return 0;
+    const size_t td = moe_talker_decode_workspace_size(cfg, acfg, T, V);
+    const size_t pd = moe_predictor_workspace_size(pcfg, T);
+    if (td == 0 || pd == 0) return 0;
+    const int H = cfg->hidden_size;
+    Carver cv(nullptr);
+    for (int i = 0; i < 3; ++i) cv.take<char>(T * H * (int64_t)esize(cfg->dtype));  // x, h, xn
+    cv.take<int32_t>(T);                                                            // c_0
+    cv.take<char>((int64_t)td);
+    cv.take<char>((int64_t)pd);
+    return cv.size();
+}
+
+int moe_talker_frame(const moe_config* cfg, const moe_attn_config* acfg, const moe_talker_layer* layers, int32_t L,
+                     const float* final_norm, float eps, const void* codec_head, int32_t V,
+                     const moe_predictor_config* pcfg, const moe_predictor_weights* pw, const void* cond, int64_t T,
+                     void* prev_emb, int32_t* pos, int32_t* cache_len, int32_t* codes, void* h_out, void* xn_out,
+                     void* ws, size_t ws_bytes, void* stream) {
+    int st = check_cfg(cfg);
+    if (st != MOE_OK) return st;
+    if (!pcfg || !pw) return MOE_ERR_INVALID;
+    if (T == 0) return MOE_OK;
+    if ((st = check_pred_cfg(pcfg, T)) != MOE_OK) return st;
+    if (cfg->dtype != MOE_BF16 || pcfg->attn.hidden_size != cfg->hidden_size) return MOE_ERR_UNSUPPORTED;
+    // everything the predictor and the frame's end read is checked here, before
+    // the Talker step is enqueued (the Talker step checks its own layers first)
+    if (!codec_head || V < 1 || !ok_ptr(cond) || !ok_ptr(prev_emb) || !ok_ptr(pos) || !ok_ptr(cache_len) ||
+        !ok_ptr(codes) || !ok_opt(h_out) || !ok_opt(xn_out) || !ok_ptr(ws) || !pred_weights_ok(pcfg, pw))
+        return MOE_ERR_INVALID;
+    if (h_out && xn_out && h_out == xn_out) return MOE_ERR_INVALID;
+    const size_t need = moe_talker_frame_workspace_size(cfg, acfg, pcfg, T, V);
+    if (need == 0) return MOE_ERR_INVALID;
+    if (ws_bytes < need) return MOE_ERR_WORKSPACE;
+    const int H = cfg->hidden_size;
+    const size_t td = moe_talker_decode_workspace_size(cfg, acfg, T, V);
+    const size_t pd = moe_predictor_workspace_size(pcfg, T);
+    Carver cv(ws);
+    void* x = cv.take<char>(T * H * (int64_t)esize(cfg->dtype));
+    void* h = cv.take<char>(T * H * (int64_t)esize(cfg->dtype));
+    void* xn = cv.take<char>(T * H * (int64_t)esize(cfg->dtype));
+    int32_t* c0 = cv.take<int32_t>(T);
+    void* tws = cv.take<char>((int64_t)td);
+    void* pws = cv.take<char>((int64_t)pd);
+    if (h_out) h = h_out;
+    if (xn_out) xn = xn_out;
+    // the Talker step on prev_emb + cond, then the predictor's frame on its
+    // final-normed state and c_0, then the next frame's input and positions
+    if ((st = talker_run(cfg, acfg, layers, L, prev_emb, cond, x, T, pos, cache_len, final_norm, eps, codec_head, V, h,
+                         xn, c0, tws, td, stream)) != MOE_OK)
+        return st;
+    if ((st = moe_predictor_frame(pcfg, pw, xn, c0, T, codes, nullptr, pws, pd, stream)) != MOE_OK) return st;
+    return hip_status(launch_frame_advance(codes, pcfg->num_codes, pw->c0_embedding, pcfg->c0_vocab,
+                                           pw->codec_embedding, pcfg->codebook_size, T, H, prev_emb, pos, cache_len,
+                                           as_stream(stream)));
 }
 
 int moe_rmsnorm(const moe_config* cfg, const void* x, const float* gain, float eps, int64_t T, void* out,
@@ -1004,16 +1097,9 @@ int moe_predictor_frame(const moe_predictor_config* cfg, const moe_predictor_wei
     if (T == 0 && cfg) return MOE_OK;
     int st = check_pred_cfg(cfg, T);
     if (st != MOE_OK) return st;
-    if (!w || !w->layers || !ok_ptr(w->final_norm) || !ok_ptr(w->c0_embedding) || !ok_ptr(w->codec_embedding) ||
-        !ok_ptr(w->lm_head) || !ok_ptr(h_talker) || !ok_ptr(c0) || !ok_ptr(codes) || !ok_opt(xn_out) ||
+    if (!pred_weights_ok(cfg, w) || !ok_ptr(h_talker) || !ok_ptr(c0) || !ok_ptr(codes) || !ok_opt(xn_out) ||
         !ok_ptr(ws))
         return MOE_ERR_INVALID;
-    for (int l = 0; l < cfg->num_layers; ++l) {
-        const moe_predictor_layer& L = w->layers[l];
-        if (!ok_ptr(L.attn.w_qkv) || !ok_ptr(L.attn.q_norm) || !ok_ptr(L.attn.k_norm) || !ok_ptr(L.attn.w_o) ||
-            !ok_ptr(L.in_norm) || !ok_ptr(L.post_norm) || !ok_ptr(L.gate) || !ok_ptr(L.up) || !ok_ptr(L.down))
-            return MOE_ERR_INVALID;
-    }
     if (ws_bytes < moe_predictor_workspace_size(cfg, T)) return MOE_ERR_WORKSPACE;
     Carver cv(ws);
     PredPlan p;

@@ -383,6 +383,100 @@ static int bf16x8_chunks(int dtype, int H) {
     return (H + 1023) / 1024;
 }
 
+// A frame's Talker input x = bf16(a + b) ("Bài Lab tổng hợp", step [3B]: the
+// previous frame's audio embedding plus the frame's text condition), stored,
+// then its RMSNorm: the same arithmetic as rmsnorm_bf16x8_kernel on the stored
+// row, so the result equals moe_rmsnorm of x bit for bit.
+template <int NCH>
+__global__ __launch_bounds__(128) void add_rmsnorm_bf16x8_kernel(const bf16_t* __restrict__ a,
+                                                                 const bf16_t* __restrict__ b, bf16_t* x,
+                                                                 const float* __restrict__ gain, float eps,
+                                                                 int64_t Ttok, int H, bf16_t* out) {
+    const int64_t t = blockIdx.x;
+    if (t >= Ttok) return;
+    u32x4 v[NCH];
+    bool ok[NCH];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int h = (threadIdx.x + 128 * c) * 8;
+        ok[c] = h < H;
+        v[c] = u32x4{0, 0, 0, 0};
+        if (!ok[c]) continue;
+        const u32x4 va = *reinterpret_cast<const u32x4*>(a + t * H + h);
+        const u32x4 vb = *reinterpret_cast<const u32x4*>(b + t * H + h);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            v[c][q] = pack_bf16x2(__uint_as_float(va[q] << 16) + __uint_as_float(vb[q] << 16),
+                                  __uint_as_float(va[q] & 0xFFFF0000u) + __uint_as_float(vb[q] & 0xFFFF0000u));
+        *reinterpret_cast<u32x4*>(x + t * H + h) = v[c];
+    }
+    const float inv = rms_inv_bf16x8<NCH>(v, ok, H, eps);
+    rms_store_bf16x8<NCH>(v, ok, inv, gain, out + t * H);
+}
+
+hipError_t launch_add_rmsnorm(const void* a, const void* b, void* x, const float* gain, float eps, int64_t Ttok,
+                              int H, void* out, hipStream_t st) {
+    if (Ttok <= 0) return hipSuccess;
+    const int nch = bf16x8_chunks(kBF16, H);
+#define TMOE_ARMS(N)                                                                                            \
+    add_rmsnorm_bf16x8_kernel<N><<<(unsigned)Ttok, 128, 0, st>>>((const bf16_t*)a, (const bf16_t*)b, (bf16_t*)x, \
+                                                                 gain, eps, Ttok, H, (bf16_t*)out)
+    if (nch == 1) TMOE_ARMS(1);
+    else if (nch == 2) TMOE_ARMS(2);
+    else if (nch == 3) TMOE_ARMS(3);
+    else if (nch == 4) TMOE_ARMS(4);
+    else return hipErrorInvalidValue;
+#undef TMOE_ARMS
+    return hipGetLastError();
+}
+
+// The end of a frame for stream t ("Bài Lab tổng hợp", step [3B]): the mean of
+// its Q code embeddings (c_0 from c0_table [V0, H], c_j from tables[j - 1]
+// [K, H]; a code outside its table is a zero row), summed in fp32 in code
+// order, divided by Q and rounded to bf16, becomes the next frame's audio
+// embedding; the stream's three TM-RoPE indices and its cache length advance
+// by one.
+__global__ __launch_bounds__(128) void frame_advance_kernel(const int32_t* __restrict__ codes, int Q,
+                                                            const bf16_t* __restrict__ c0_table, int V0,
+                                                            const bf16_t* __restrict__ tables, int K, int64_t Ttok,
+                                                            int H, bf16_t* __restrict__ prev, int32_t* pos,
+                                                            int32_t* len) {
+    const int64_t t = blockIdx.x;
+    if (t >= Ttok) return;
+    for (int h = threadIdx.x * 8; h < H; h += 128 * 8) {
+        float acc[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+        for (int j = 0; j < Q; ++j) {
+            const int c = codes[(int64_t)j * Ttok + t];
+            const int rows = j == 0 ? V0 : K;
+            if (c < 0 || c >= rows) continue;
+            const bf16_t* row = j == 0 ? c0_table + (int64_t)c * H : tables + ((int64_t)(j - 1) * K + c) * H;
+            const u32x4 v = *reinterpret_cast<const u32x4*>(row + h);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                acc[2 * q] += __uint_as_float(v[q] << 16);
+                acc[2 * q + 1] += __uint_as_float(v[q] & 0xFFFF0000u);
+            }
+        }
+        u32x4 o;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(acc[2 * q] / (float)Q, acc[2 * q + 1] / (float)Q);
+        *reinterpret_cast<u32x4*>(prev + t * H + h) = o;
+    }
+    if (threadIdx.x < 3) pos[t * 3 + threadIdx.x] += 1;
+    if (threadIdx.x == 3) len[t] += 1;
+}
+
+hipError_t launch_frame_advance(const int32_t* codes, int Q, const void* c0_table, int V0, const void* tables, int K,
+                                int64_t Ttok, int H, void* prev, int32_t* pos, int32_t* len, hipStream_t st) {
+    if (Ttok <= 0) return hipSuccess;
+    if (H % 8 != 0 || Q < 1) return hipErrorInvalidValue;
+    frame_advance_kernel<<<(unsigned)Ttok, 128, 0, st>>>(codes, Q, (const bf16_t*)c0_table, V0,
+                                                         (const bf16_t*)tables, K, Ttok, H, (bf16_t*)prev, pos, len);
+    return hipGetLastError();
+}
+
 hipError_t launch_rmsnorm(int dtype, const void* x, const float* gain, float eps, int64_t Ttok, int H, void* out,
                           hipStream_t st) {
     if (Ttok <= 0) return hipSuccess;

@@ -179,6 +179,15 @@ hipError_t launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t st);
 hipError_t launch_gather_rows(int dtype, const void* x, const int32_t* rows, int64_t n, int H, void* out,
                               hipStream_t st);
 
+// The frame loop (elementwise.hip): x = bf16(a + b) and out = RMSNorm(x) * gain
+// (bf16, H % 8 == 0, H <= 4096); then, after the frame, prev [T, H] = the mean
+// of the frame's code embeddings (codes [Q, T]: c_0 from c0_table [V0, H], c_j
+// from tables [Q - 1, K, H]) and pos [T, 3], len [T] advanced by one.
+hipError_t launch_add_rmsnorm(const void* a, const void* b, void* x, const float* gain, float eps, int64_t Ttok,
+                              int H, void* out, hipStream_t st);
+hipError_t launch_frame_advance(const int32_t* codes, int Q, const void* c0_table, int V0, const void* tables, int K,
+                                int64_t Ttok, int H, void* prev, int32_t* pos, int32_t* len, hipStream_t st);
+
 // Decode layer part of a partial-row combine (elementwise.hip): y [T, H] from the
 // partial rows [T, k S + SSH, H] of launch_decode_experts and the routing
 // weights w [T, k] (+ residual), then norm_out = RMSNorm(y) * gain when

@@ -294,3 +294,38 @@ def test_talker_decode_argument_errors():
     assert call(T=0) == 0
     arr[1].v_cache = None
     assert call() == -1                   # every layer checked before launching
+
+
+def test_talker_frame_argument_errors():
+    lib = api.load_library()
+    c = _cfg()
+    a = api.AttnConfig(max_len=1024).c()
+    p = api.PredictorConfig().c()
+    n = lib.moe_talker_frame_workspace_size(ctypes.byref(c), ctypes.byref(a), ctypes.byref(p), 64, 3072)
+    assert n > (lib.moe_talker_decode_workspace_size(ctypes.byref(c), ctypes.byref(a), 64, 3072) +
+                lib.moe_predictor_workspace_size(ctypes.byref(p), 64))
+    assert lib.moe_talker_frame_workspace_size(ctypes.byref(c), ctypes.byref(a), ctypes.byref(p), 65, 3072) == 0
+    assert lib.moe_talker_frame_workspace_size(ctypes.byref(c), ctypes.byref(a), ctypes.byref(p), 64, 0) == 0
+    lay = api.moe_talker_layer(api.moe_weights(FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE),
+                               api.moe_attn_weights(FAKE, FAKE, FAKE, FAKE), None, None, FAKE, FAKE)
+    arr = (api.moe_talker_layer * 2)(lay, lay)
+    player = api.moe_predictor_layer(api.moe_attn_weights(FAKE, FAKE, FAKE, FAKE), FAKE, FAKE, FAKE, FAKE, FAKE)
+    parr = (api.moe_predictor_layer * 5)(*([player] * 5))
+    pw = api.moe_predictor_weights(ctypes.cast(parr, ctypes.POINTER(api.moe_predictor_layer)), FAKE, FAKE, FAKE, FAKE)
+
+    def call(**kw):
+        return lib.moe_talker_frame(ctypes.byref(c), ctypes.byref(a), arr, 2, None, ctypes.c_float(1e-6),
+                                    kw.get("head", _p(1 << 22)), 3072, ctypes.byref(p), kw.get("pw", ctypes.byref(pw)),
+                                    kw.get("cond", _p()), kw.get("T", 64), _p(1 << 20), _p(1 << 21), _p(1 << 23),
+                                    _p(1 << 24), kw.get("h", None), kw.get("xn", None), _p(1 << 26), kw.get("ws", n),
+                                    None)
+
+    assert call(head=None) == -1
+    assert call(pw=None) == -1
+    assert call(cond=None) == -1
+    assert call(h=_p(1 << 25), xn=_p(1 << 25)) == -1   # h_out and xn_out may not alias
+    assert call(ws=n - 256) == -3
+    assert call(T=0) == 0
+    assert call(T=65) == -2                             # the predictor takes up to 64 streams
+    parr[2].gate = None
+    assert call() == -1                                 # the predictor's layers are checked before any launch
