@@ -337,12 +337,16 @@ def measure_attention(api, torch, INP, T, L, steps, R=4):
 
 
 def measure_talker_frame(api, torch, INP, shape, T, ctx, weight_sets, L, frames, vocab=3072):
-    """The Talker's decode step through L whole layers (attention over ctx cached positions, then the MoE) and
-    the codec head, as one graph.  Layer l uses MoE weight set l % R and attention weight set l % R; every layer
-    has its own caches (filled on the device with seeded normal values)."""
+    """Consecutive Dual-Track frames (moe_talker_frame): the frame input (previous frame's code-embedding mean +
+    text condition), the Talker's decode step through L whole layers (attention over the cached positions, then
+    the MoE) and the codec head, the depth predictor's frame and the frame's end (next input, positions and cache
+    lengths advanced on the device).  One frame is captured as a HIP graph and replayed `frames` times, the next
+    text condition copied in before each replay; the caches start at ctx positions and grow by one per frame.
+    Layer l uses MoE weight set l % R and attention weight set l % R; every layer has its own caches (filled on
+    the device with seeded normal values)."""
     dev = torch.device("cuda", 0)
     to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
-    ashape = INP.TALKER_ATTN
+    ashape, pshape = INP.TALKER_ATTN, INP.PREDICTOR
     R = len(weight_sets)
     attn_w = []
     for r in range(R):
@@ -351,7 +355,7 @@ def measure_talker_frame(api, torch, INP, shape, T, ctx, weight_sets, L, frames,
                        "q_norm": torch.from_numpy(w["q_norm"]).to(dev), "k_norm": torch.from_numpy(w["k_norm"]).to(dev)})
     gen = torch.Generator(device=dev)
     gen.manual_seed(7)
-    max_len = ctx + 1
+    max_len = (ctx + frames + 2 + 31) // 32 * 32
     layers = []
     for l in range(L):
         kc = torch.randn((T, ashape.n_kv_heads, max_len, ashape.head_dim), generator=gen, device=dev,
@@ -364,37 +368,57 @@ def measure_talker_frame(api, torch, INP, shape, T, ctx, weight_sets, L, frames,
     cfg = api.Config(shape.H, shape.E, shape.k, shape.I, shape.Is, True, torch.bfloat16)
     acfg = api.AttnConfig(max_len=max_len)
     head = to_dev(INP.stack_weights(shape, 0, 30, 0.02, "bf16", vocab, 50)["codec_head"])
-    x = to_dev(INP.activations(T, shape.H, 30, "bf16"))
+    pw = INP.predictor_weights(pshape, 80)
+    pdev = lambda a: to_dev(a) if a.dtype == np.uint16 else torch.from_numpy(a).to(dev)
+    pwd = {k: pdev(v) for k, v in pw.items() if k != "layers"}
+    pwd["layers"] = [{k: pdev(v) for k, v in lw.items()} for lw in pw["layers"]]
+    pst = api.predictor_weights_struct(pwd)
+    pc = api.PredictorConfig()
+    conds = torch.stack([to_dev(INP.activations(T, shape.H, 200 + f, "bf16")) for f in range(frames + 2)])
+    prev = to_dev(INP.activations(T, shape.H, 199, "bf16"))  # the codec BOS embedding
     lens = torch.full((T,), ctx, dtype=torch.int32, device=dev)
     pos = torch.from_numpy(INP.speech_positions(np.full(T, ctx, np.int32))).to(dev)
-    h, c0 = torch.empty_like(x), torch.empty(T, dtype=torch.int32, device=dev)
-    ws = api.workspace(api.moe_talker_decode_workspace_size(cfg, acfg, T, vocab), dev)
-    run = lambda: api.moe_talker_decode(cfg, acfg, arr, x, pos, lens, None, 1e-6, head, h_out=h, c0=c0, ws=ws)
-    run()
+    cond = torch.empty((T, shape.H), dtype=torch.bfloat16, device=dev)
+    codes = torch.empty((pc.num_codes, T), dtype=torch.int32, device=dev)
+    ws = api.workspace(api.moe_talker_frame_workspace_size(cfg, acfg, pc, T, vocab), dev)
+    run = lambda: api.moe_talker_frame(cfg, acfg, arr, None, 1e-6, head, pc, pst, cond, prev, pos, lens,
+                                       codes=codes, ws=ws)
+    cond.copy_(conds[0])
+    run()  # frame 0, eager
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         run()
-    g.replay()
+    cond.copy_(conds[1])
+    g.replay()  # frame 1
     torch.cuda.synchronize()
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
-    for _ in range(frames):
+    for f in range(frames):
+        cond.copy_(conds[2 + f])
         g.replay()
     stop.record()
     torch.cuda.synchronize()
     us = start.elapsed_time(stop) * 1e3 / frames
+    assert int(lens[0].item()) == ctx + frames + 2, "positions advanced on the device"
     touched = 124  # experts a T=64 batch touches (the decode measurement's count for these weight sets)
     moe_b = touched * 3 * shape.I * shape.H * 2 + 3 * shape.Is * shape.H * 2 + shape.E * shape.H * 2
-    attn_b = T * ashape.n_kv_heads * max_len * ashape.head_dim * 4 + (
+    mid = ctx + 2 + frames // 2  # mean cached positions over the timed frames
+    attn_b = T * ashape.n_kv_heads * (mid + 1) * ashape.head_dim * 4 + (
         (ashape.n_heads + 2 * ashape.n_kv_heads) * ashape.head_dim * shape.H + shape.H * ashape.n_heads *
         ashape.head_dim) * 2
-    alg = L * (moe_b + attn_b) + vocab * shape.H * 2
-    return {"workload": "talker_decode_frame_%dlayers_T%d_ctx%d" % (L, T, max_len), "layers": L, "streams": T,
-            "bytes_per_frame": alg, "hbm_frac": alg / (us * 1e-6) / (HBM_PEAK_GBS * 1e9),
-            "positions": max_len, "frame_us": us, "per_layer_us": us / L, "tokens_per_s": T / (us * 1e-6),
-            "timing": "one HIP graph per frame: per layer attention (+ residual, post-attention norm) and MoE "
-                      "(+ residual, next norm), then the codec head argmax"}
+    p_layer = sum(v.numel() * v.element_size() for lw in pwd["layers"] for v in lw.values())
+    pred_b = pshape.num_codes * p_layer + 2 * (pshape.num_codes - 1) * pshape.codebook * shape.H * 2
+    alg = L * (moe_b + attn_b) + vocab * shape.H * 2 + pred_b
+    return {"workload": "talker_frame_%dlayers_predictor_T%d_ctx%d" % (L, T, ctx), "layers": L, "streams": T,
+            "frames_timed": frames, "bytes_per_frame": alg, "hbm_frac": alg / (us * 1e-6) / (HBM_PEAK_GBS * 1e9),
+            "bytes_note": "touched experts, shared expert and router per layer; keys and values of the cached "
+                          "positions and the attention weights per layer; codec head; the predictor's layer "
+                          "weights once per position, its 15 heads and 15 tables once",
+            "positions_start": ctx, "frame_us": us, "per_layer_us": us / L, "tokens_per_s": T / (us * 1e-6),
+            "timing": "one HIP graph per frame (frame input, %d Talker layers, codec head, predictor frame, next "
+                      "input and positions on the device), replayed for consecutive frames with the next text "
+                      "condition copied in before each replay" % L}
 
 
 def measure_predictor(api, torch, INP, T, frames):
@@ -615,9 +639,10 @@ def main():
         log("attention: %.2f us/step, %.1f%% of HBM peak" % (attn["us_per_step"], 100 * attn["hbm_frac"]))
     tframe = None
     if not args.no_talker_frame and not args.no_decode:
-        log("talker decode frame: 20 layers (attention + MoE) + codec head, 64 streams x 1024 positions")
-        tframe = measure_talker_frame(api, torch, INP, shape, 64, 1023, sets, 20, max(5, args.stack_frames // 2))
-        log("talker frame: %.1f us/frame, %.1f us/layer" % (tframe["frame_us"], tframe["per_layer_us"]))
+        log("talker frames: input + 20 layers (attention + MoE) + codec head + predictor, 64 streams x ~1024 "
+            "positions, consecutive frames")
+        tframe = measure_talker_frame(api, torch, INP, shape, 64, 1000, sets, 20, max(5, args.stack_frames // 2))
+        log("talker frame: %.1f us/frame" % tframe["frame_us"])
     pred = None
     if not args.no_predictor and not args.no_decode:
         log("depth code predictor frame: 64 streams")
