@@ -47,9 +47,9 @@ def layer_costs(shape, T, touched):
     Weight bytes count each touched expert once (bf16); activations count the
     token rows read and written once; routing outputs 8 bytes per (token, slot).
     At decode sizes the dominant kernel is the expert launch: every touched
-    expert's and the shared expert's weights plus the token rows it reads (its
-    partial output rows are design traffic, not counted).  Otherwise it is the
-    grouped gate/up pass.
+    expert's weights, the shared expert's down weights and its gate/up output,
+    and the token rows it reads (its partial output rows are design traffic, not
+    counted).  Otherwise it is the grouped gate/up pass.
     """
     H, E, k, I, Is = shape.H, shape.E, shape.k, shape.I, shape.Is
     expert_b = 3 * I * H * 2
@@ -58,7 +58,11 @@ def layer_costs(shape, T, touched):
     layer_bytes = touched * expert_b + shared_b + router_b + 2 * T * H * 2 + T * k * 8
     layer_flops = T * (2 * H * E + 6 * H * I * k + 6 * H * Is)
     if decode_path(shape, T):
-        return layer_bytes, layer_flops, touched * expert_b + shared_b + T * H * 2, T * (6 * H * I * k + 6 * H * Is)
+        # the expert launch: routed experts' weights, the shared expert's down
+        # weights and gate/up output, the token rows (the shared gate/up runs in
+        # the router's launch)
+        return (layer_bytes, layer_flops, touched * expert_b + Is * H * 2 + T * Is * 2 + T * H * 2,
+                T * (6 * H * I * k + 2 * H * Is))
     gu_bytes = touched * 2 * I * H * 2 + 2 * Is * H * 2 + T * H * 2 + T * k * I * 2 + T * Is * 2
     gu_flops = T * (4 * H * I * k + 4 * H * Is)
     return layer_bytes, layer_flops, gu_bytes, gu_flops
@@ -717,7 +721,8 @@ def main():
                    "shared_intermediate": shape.Is, "weight_sets_rotated": args.rotate},
         "roofline": {"bound": "hbm",
                      "kernel": "decode expert kernel: every (expert, 64-wide slice) item of the touched routed "
-                               "experts and of the shared expert, gate/up + SwiGLU + partial down in one launch",
+                               "experts (gate/up + SwiGLU + partial down) and the shared expert's down tiles, "
+                               "in one launch",
                      "achieved": g["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": g["gbs"] / HBM_PEAK_GBS, "traffic": traffic, "traffic_source": traffic_source,
                      "bytes_per_launch": g["bytes"], "mean_us": g["mean_us"],

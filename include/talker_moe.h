@@ -33,11 +33,12 @@
  *     which reports a failed launch.  T == 0 is a successful no-op.
  *   - Device pointers must be 16-byte aligned; inputs must be finite (no NaN,
  *     Inf or subnormal values).
- *   - Expert selection is exact: the library's Top-k equals the Top-k of the
- *     exactly computed scores W_r x (+ bias), ties going to the lower expert
- *     index, listed by descending weight.  It scores in fp32 and recomputes in
- *     fp64 every token whose fp32 order is not certain under a rigorous
- *     rounding-error bound.
+ *   - Expert selection is fp64-rescored: the library's Top-k equals the Top-k
+ *     of the scores W_r x (+ bias) computed in fp64 from the exact bf16
+ *     products (so up to fp64 summation rounding), ties going to the lower
+ *     expert index, listed by descending weight.  It scores on the matrix cores
+ *     and rescores in fp64 every token whose order is not certain under a
+ *     rigorous rounding-error bound.
  *
  * Supported shapes: 1 <= k <= 32, k <= E <= 1024, 1 <= H, I <= 16384,
  * 0 <= Is <= 16384, T * k <= 2^22.  The bf16 matrix-core paths are taken when
@@ -236,7 +237,7 @@ int moe_rmsnorm(const moe_config* cfg, const void* x, const float* gain, float e
 /*
  * moe_codec_head_argmax — c_0 = argmax_v (W_c x)_v, the first codec code
  * (Talker MoE page §1: codec_head Linear 1024 -> 3072 after the last layer;
- * the lab picks the argmax).  Exact like the routing: ties go to the lowest v.
+ * the lab picks the argmax).  fp64-rescored like the routing: ties go to the lowest v.
  *   x [dev] [T, H];  w_head [dev] [V, H] (cfg->dtype, bias-free)
  *   logits [dev] [T, V] fp32 out, or NULL;  c0 [dev] [T] int32 out
  */
