@@ -501,7 +501,7 @@ int layer_run(const moe_config* cfg, const moe_weights* w, const void* x, const 
                                                  : hipSuccess;
     };
 
-    const int slots = k + 1;  // per token: k weighted expert rows, then the shared row
+    const int slots = k + 1;  // per token: k unweighted expert rows (the combine applies w), then the shared row
     const TileSpec* t1 = p.gemm.mfma ? &p.gemm.t[0] : nullptr;
     const TileSpec* t2 = p.gemm.mfma ? &p.gemm.t[1] : nullptr;
     TMOE_TRY(mark(0));

@@ -6,12 +6,15 @@ rope_theta 1e6): the output y = residual + o_proj(attention) and the cache rows
 written at each stream's length are compared with the float64 oracle under the
 bf16 bars; every other cache entry must be unchanged bit for bit.  The value
 cache is transposed in the library ([T, nkv, head_dim, max_len]).  Cases: random
-lengths up to 1024 (T = 64), ragged chunks and lengths 0 / 1 / 127 / 128 / 129 /
-max_len - 1 (T = 37, max_len = 320), 3D positions with distinct T/H/W indices,
-long caches (max_len 4096 and 32768), the 16/8 head split, hidden 512 (the
-16-column skinny products), the fused RMSNorm of y, a batch of 96
-streams (the grouped GEMM path for the projections), streams
-whose length is out of range, and a captured graph replayed.
+lengths up to 1024 (T = 64); ragged 128-position chunks with lengths 0 / 1 /
+126..129 / max_len - 1 (T = 37, max_len = 256: two chunks, the merge runs);
+512-position chunks with lengths 510..513 / 1022 / 1023 (max_len 1024); 3D
+positions with distinct T/H/W indices; long caches (max_len 4096 and 32768); the
+16/8 head split at 256 positions, and 16/8 and 8/2 at 1024 (the 16-wave chunk
+with 2 and 4 query heads per KV head); hidden 512 (the 16-column skinny
+products); the fused RMSNorm of y; a batch of 96 streams (the grouped GEMM path
+for the projections); streams whose length is out of range; and a captured graph
+replayed.
 """
 import numpy as np
 import pytest
@@ -95,11 +98,33 @@ def test_attention_decode_random_lengths():
 
 
 def test_attention_decode_ragged_chunks_and_edges():
-    T, L = 37, 320
+    # max_len 256: 128-position chunks (4 waves), two per stream, so lengths
+    # around 128 cross a chunk boundary and the chunk merge runs
+    T, L = 37, 256
     lens = INP.cache_lengths(T, L, 65)
-    lens[:8] = [0, 1, 127, 128, 129, 255, 256, L - 1]
+    lens[:8] = [0, 1, 126, 127, 128, 129, 254, L - 1]
     w, kv, x, res, lens, pos = _case(T, L, lens)
     _check(INP.TALKER_ATTN, L, w, kv, x, res, lens, pos, "ragged", norm=True)
+
+
+def test_attention_decode_long_chunk_boundaries():
+    # max_len 1024: 512-position chunks (16 waves); lengths around the chunk
+    # boundary and the cache's end
+    T, L = 9, 1024
+    lens = np.array([510, 511, 512, 513, 1022, 1023, 0, 255, 767], np.int32)
+    w, kv, x, res, lens, pos = _case(T, L, lens)
+    _check(INP.TALKER_ATTN, L, w, kv, x, res, lens, pos, "chunk boundaries")
+
+
+@pytest.mark.parametrize("heads", [(16, 8), (8, 2)])
+def test_attention_decode_other_groups_long_cache(heads):
+    # 2 and 4 query heads per KV head on the 16-wave (512-position chunk) kernel
+    shape = INP.AttnShape(1024, heads[0], heads[1], 128)
+    T, L = 12, 1024
+    lens = INP.cache_lengths(T, L, 70)
+    lens[:4] = [511, 512, 513, 1023]
+    w, kv, x, res, lens, pos = _case(T, L, lens, shape=shape)
+    _check(shape, L, w, kv, x, res, lens, pos, "%dq/%dkv L=1024" % heads)
 
 
 def test_attention_decode_3d_positions():
