@@ -7,12 +7,12 @@
 //
 // Four launches:
 //  1. route_scores_kernel: the E router scores of every token on the matrix
-//     cores with a rigorous error bound, spread over T / 8 x E / 16 workgroups;
-//     further workgroups of the launch compute the shared expert's gate/up.
+//     cores with a rigorous error bound, spread over T / 8 x E / 16 workgroups.
 //  2. route_select_kernel: one wave per token: the top-k (ties to the lower
 //     expert index) is certified from the bounds or settled by fp64 rescoring of
 //     the candidates, so it is the top-k of the scores computed in fp64, up to
-//     fp64 summation rounding; then the routing weights.
+//     fp64 summation rounding; then the routing weights.  Further workgroups of
+//     the launch compute the shared expert's gate/up, which needs no routing.
 //  3. decode_experts_kernel: one work item per (expert, 64-wide slice of the
 //     intermediate dimension) plus tiles of the shared expert's down product.
 //     A routed item runs its slice of gate/up and SwiGLU for its tokens, then
@@ -182,23 +182,9 @@ template <int H>
 __global__ __launch_bounds__(256) void route_scores_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ W,
                                                            const float* __restrict__ bias, int T, int E,
                                                            double* __restrict__ sc, double* __restrict__ dv,
-                                                           const bf16_t* __restrict__ sg,
-                                                           const bf16_t* __restrict__ su, int Is,
-                                                           bf16_t* __restrict__ hs, uint32_t* __restrict__ mask,
+                                                           uint32_t* __restrict__ mask,
                                                            int32_t* __restrict__ counts) {
     using namespace dec;
-    const int nsc = ((T + 7) / 8) * ((E + 15) / 16);
-    if ((int)blockIdx.x >= nsc) {
-        // the shared expert's gate/up: hs [T, Is] = SiLU(x sg^T) * (x su^T) in
-        // bf16, 8 features of 16 tokens per workgroup (the 16-column skinny form
-        // over all of K).  Workgroup tq * Is / 8 + f: the four token quarters of
-        // feature group f share an XCD (Is / 8 is a multiple of 8), so its
-        // weight rows come from HBM once.
-        const int nf = Is / 8, b = (int)blockIdx.x - nsc, tq = b / nf, f = b - tq * nf;
-        skinny_body<4, 4, true, 1>(x + (int64_t)16 * tq * H, sg, su, nullptr, hs + (int64_t)16 * tq * Is,
-                                   min(16, T - 16 * tq), 2 * Is, H, 1, f, 0);
-        return;
-    }
     // the selection launch ORs the touched experts into mask and counts the
     // routed pairs per expert: both start from zero here
     if (blockIdx.x == 0) {
@@ -289,7 +275,23 @@ __global__ __launch_bounds__(256) void route_select_kernel(const bf16_t* __restr
                                                            const double* __restrict__ dv, int T, int E, int k,
                                                            int norm, int32_t* __restrict__ idx_out,
                                                            float* __restrict__ w_out, uint32_t* __restrict__ mask,
-                                                           int32_t* __restrict__ counts) {
+                                                           int32_t* __restrict__ counts,
+                                                           const bf16_t* __restrict__ sg,
+                                                           const bf16_t* __restrict__ su, int Is,
+                                                           bf16_t* __restrict__ hs) {
+    const int nsel = (T + 3) / 4;
+    if ((int)blockIdx.x >= nsel) {
+        // the shared expert's gate/up beside the selection (it needs no
+        // routing): hs [T, Is] = SiLU(x sg^T) * (x su^T) in bf16, 8 features of
+        // 16 tokens per workgroup (the 16-column skinny form over all of K).
+        // Workgroup tq * Is / 8 + f: the four token quarters of feature group f
+        // share an XCD (Is / 8 is a multiple of 8), so its weight rows come from
+        // HBM once.
+        const int nf = Is / 8, b = (int)blockIdx.x - nsel, tq = b / nf, f = b - tq * nf;
+        skinny_body<4, 4, true, 1>(x + (int64_t)16 * tq * H, sg, su, nullptr, hs + (int64_t)16 * tq * Is,
+                                   min(16, T - 16 * tq), 2 * Is, H, 1, f, 0);
+        return;
+    }
     constexpr int NJ = H / 64;  // elements per lane of a rescored row
     __shared__ double s_sc[4][128];
     __shared__ double s_dv[4][128];
@@ -424,7 +426,7 @@ __global__ __launch_bounds__(256) void route_select_kernel(const bf16_t* __restr
 // Items, one per workgroup:
 //  - b < Nsd (= H / 64): tile b of the shared expert's down product,
 //    y_shared[:, 64 b .. 64 b + 63] = h_shared W_sd^T for all T tokens (h_shared
-//    [T, Is] from the router's scores launch), stored complete as partial slot
+//    [T, Is] from the selection launch), stored complete as partial slot
 //    k S.
 //  - b >= Nsd: routed item q = b - Nsd: slice s = q % S of the (q / S)-th
 //    touched expert e, in increasing index, from the 128-bit mask of touched
@@ -852,14 +854,15 @@ hipError_t launch_route_decode(const void* x, const void* W, const float* bias, 
         (Is > 0 && (!sg || !su || !hs)) || !mask || !counts)
         return hipErrorInvalidValue;
     const int nsc = (int)(((T + 7) / 8) * ((E + 15) / 16));
+    const int nsel = (int)((T + 3) / 4);
     const int nsk = (Is / 8) * (int)((T + 15) / 16);  // shared gate/up: feature groups x token quarters
-    route_scores_kernel<dec::kH><<<(unsigned)(nsc + nsk), 256, 0, st>>>(
-        (const bf16_t*)x, (const bf16_t*)W, bias, (int)T, E, sc, dv, (const bf16_t*)sg, (const bf16_t*)su, Is,
-        (bf16_t*)hs, mask, counts);
+    route_scores_kernel<dec::kH><<<(unsigned)nsc, 256, 0, st>>>((const bf16_t*)x, (const bf16_t*)W, bias, (int)T,
+                                                                E, sc, dv, mask, counts);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    route_select_kernel<dec::kH><<<(unsigned)((T + 3) / 4), 256, 0, st>>>(
-        (const bf16_t*)x, (const bf16_t*)W, bias, sc, dv, (int)T, E, k, norm, idx, w, mask, counts);
+    route_select_kernel<dec::kH><<<(unsigned)(nsel + nsk), 256, 0, st>>>(
+        (const bf16_t*)x, (const bf16_t*)W, bias, sc, dv, (int)T, E, k, norm, idx, w, mask, counts,
+        (const bf16_t*)sg, (const bf16_t*)su, Is, (bf16_t*)hs);
     return hipGetLastError();
 }
 

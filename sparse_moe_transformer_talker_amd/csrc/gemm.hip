@@ -333,7 +333,7 @@ template <int PASS, int BM>
 __global__ __launch_bounds__(64 * lds_gemm::NWAVE) void grouped_gemm_lds_kernel(GemmArgs args) {
     using namespace lds_gemm;
     constexpr int A_BYTES = Tile<BM>::A_BYTES, STAGE = Tile<BM>::STAGE, A_CALLS = Tile<BM>::A_CALLS;
-    constexpr int CALLS = Tile<BM>::CALLS, MI = Tile<BM>::MI, WROWS = Tile<BM>::WROWS;
+    constexpr int CALLS = Tile<BM>::CALLS, MI = Tile<BM>::MI;
     // one array per ring stage, so the compiler can tell which direct-to-LDS
     // load writes which buffer and waits only for the right one
     __shared__ __attribute__((aligned(1024))) char buf0[STAGE];
@@ -390,8 +390,15 @@ __global__ __launch_bounds__(64 * lds_gemm::NWAVE) void grouped_gemm_lds_kernel(
                                              (lds_void*)(base + A_BYTES + (wave * B_CALLS + j) * 1024), 16, 0, 0);
     };
 
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = __builtin_amdgcn_readfirstlane(wave >> 1), wn = wave & 1;
     const int lr = lane & 31, lh = lane >> 5;
+    // Token block a of wave row wm is 32-row block a * 4 + wm of the tile, so the
+    // blocks past the expert's last row fall on different waves; the waves of
+    // a SIMD (w and w + 4) then keep equal shares of the live blocks and skip
+    // the rest (a wave-uniform test).
+    bool live[MI];
+#pragma unroll
+    for (int a = 0; a < MI; ++a) live[a] = (a * (NWAVE / 2) + wm) * 32 < mrows;
     f32x16 acc[MI][4];
 #pragma unroll
     for (int a = 0; a < MI; ++a)
@@ -411,8 +418,8 @@ __global__ __launch_bounds__(64 * lds_gemm::NWAVE) void grouped_gemm_lds_kernel(
             bf16x8 af[MI], bfr[4];
 #pragma unroll
             for (int a = 0; a < MI; ++a) {
-                const int r = wm * WROWS + a * 32 + lr;
-                af[a] = *reinterpret_cast<const bf16x8*>(base + r * 64 + lds_chunk(r, c) * 16);
+                const int r = (a * (NWAVE / 2) + wm) * 32 + lr;
+                if (live[a]) af[a] = *reinterpret_cast<const bf16x8*>(base + r * 64 + lds_chunk(r, c) * 16);
             }
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
@@ -421,9 +428,10 @@ __global__ __launch_bounds__(64 * lds_gemm::NWAVE) void grouped_gemm_lds_kernel(
             }
 #pragma unroll
             for (int a = 0; a < MI; ++a)
+                if (live[a])
 #pragma unroll
-                for (int b = 0; b < 4; ++b)
-                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[b], af[a], acc[a][b], 0, 0, 0);
+                    for (int b = 0; b < 4; ++b)
+                        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[b], af[a], acc[a][b], 0, 0, 0);
         }
     };
     // stage s: wait until its loads (all waves') have landed, refill the buffer
@@ -488,7 +496,7 @@ __global__ __launch_bounds__(64 * lds_gemm::NWAVE) void grouped_gemm_lds_kernel(
     sync();  // every wave is done with the ring
 #pragma unroll
     for (int a = 0; a < MI; ++a) {
-        const int r = wm * WROWS + a * 32 + lr;
+        const int r = (a * (NWAVE / 2) + wm) * 32 + lr;
         char* rp = row_at(r);
 #pragma unroll
         for (int b = 0; b < (PASS == 0 ? 2 : 4); ++b)
