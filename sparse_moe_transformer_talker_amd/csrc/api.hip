@@ -1111,16 +1111,19 @@ int moe_predictor_frame(const moe_predictor_config* cfg, const moe_predictor_wei
     const int64_t table = (int64_t)K * H * 2;  // bytes per embedding table / head
     TMOE_TRY(launch_frame_setup(p.pos, p.len, P, T, c0, codes, s));
     for (int q = 0; q < P; ++q) {
+        // the position's input row (h_talker, or the embedding of the previous
+        // code) and its first pre-norm
         const void* src = h_talker;
-        if (q == 1) {
-            TMOE_TRY(launch_embed_rows(w->c0_embedding, cfg->c0_vocab, c0, T, H, p.X, s));
-            src = p.X;
-        } else if (q >= 2) {
-            TMOE_TRY(launch_embed_rows(static_cast<const char*>(w->codec_embedding) + (q - 2) * table, K,
-                                       codes + (int64_t)(q - 1) * T, T, H, p.X, s));
+        if (q == 0) {
+            TMOE_TRY(launch_rmsnorm(MOE_BF16, src, w->layers[0].in_norm, eps, T, H, p.XN, s));
+        } else {
+            const bool first = q == 1;
+            TMOE_TRY(launch_embed_norm(first ? w->c0_embedding
+                                             : static_cast<const char*>(w->codec_embedding) + (q - 2) * table,
+                                       first ? cfg->c0_vocab : K, first ? c0 : codes + (int64_t)(q - 1) * T, p.X,
+                                       w->layers[0].in_norm, eps, T, H, p.XN, s));
             src = p.X;
         }
-        TMOE_TRY(launch_rmsnorm(MOE_BF16, src, w->layers[0].in_norm, eps, T, H, p.XN, s));
         for (int l = 0; l < L; ++l) {
             const moe_predictor_layer& ly = w->layers[l];
             const int r = attn_run(&p.acfg, &ly.attn, p.ap, p.XN, T, p.pos + (int64_t)q * T * 3, p.len + (int64_t)q * T,

@@ -430,6 +430,49 @@ hipError_t launch_add_rmsnorm(const void* a, const void* b, void* x, const float
     return hipGetLastError();
 }
 
+// Row t of a code embedding table, gathered (a code outside [0, rows) gives a
+// zero row) and stored to x, then its RMSNorm times the gain stored to out:
+// the gather of embed_rows and rmsnorm_bf16x8_kernel in one launch, same bits.
+template <int NCH>
+__global__ __launch_bounds__(128) void embed_norm_bf16x8_kernel(const bf16_t* __restrict__ table, int rows,
+                                                                const int32_t* __restrict__ idx, bf16_t* x,
+                                                                const float* __restrict__ gain, float eps,
+                                                                int64_t Ttok, int H, bf16_t* out) {
+    const int64_t t = blockIdx.x;
+    if (t >= Ttok) return;
+    const int r = idx[t];
+    const bool in = r >= 0 && r < rows;
+    u32x4 v[NCH];
+    bool ok[NCH];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int h = (threadIdx.x + 128 * c) * 8;
+        ok[c] = h < H;
+        v[c] = u32x4{0, 0, 0, 0};
+        if (!ok[c]) continue;
+        if (in) v[c] = *reinterpret_cast<const u32x4*>(table + (int64_t)r * H + h);
+        *reinterpret_cast<u32x4*>(x + t * H + h) = v[c];
+    }
+    const float inv = rms_inv_bf16x8<NCH>(v, ok, H, eps);
+    rms_store_bf16x8<NCH>(v, ok, inv, gain, out + t * H);
+}
+
+hipError_t launch_embed_norm(const void* table, int rows, const int32_t* idx, void* x, const float* gain, float eps,
+                             int64_t Ttok, int H, void* out, hipStream_t st) {
+    if (Ttok <= 0) return hipSuccess;
+    const int nch = bf16x8_chunks(kBF16, H);
+#define TMOE_EN(N)                                                                                       \
+    embed_norm_bf16x8_kernel<N><<<(unsigned)Ttok, 128, 0, st>>>((const bf16_t*)table, rows, idx,        \
+                                                                (bf16_t*)x, gain, eps, Ttok, H, (bf16_t*)out)
+    if (nch == 1) TMOE_EN(1);
+    else if (nch == 2) TMOE_EN(2);
+    else if (nch == 3) TMOE_EN(3);
+    else if (nch == 4) TMOE_EN(4);
+    else return hipErrorInvalidValue;
+#undef TMOE_EN
+    return hipGetLastError();
+}
+
 // The end of a frame for stream t ("Bài Lab tổng hợp", step [3B]): the mean of
 // its Q code embeddings (c_0 from c0_table [V0, H], c_j from tables[j - 1]
 // [K, H]; a code outside its table is a zero row), summed in fp32 in code
