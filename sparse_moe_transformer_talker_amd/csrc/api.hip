@@ -430,12 +430,19 @@ int attn_run(const moe_attn_config* cfg, const moe_attn_weights* w, const AttnPl
         const int r = run_dense(&p.cq, p.gq, x, w->w_qkv, p.qkv, T, s);
         if (r != MOE_OK) return r;
     }
-    TMOE_TRY(launch_qk_rope_append(p.ksq ? p.pq : reinterpret_cast<const float*>(p.qkv), p.ksq, T, nq, nkv,
-                                   w->q_norm, w->k_norm, cfg->eps, pos, cache_len, cfg->max_len,
-                                   cfg->rope_sections[1], cfg->rope_sections[2], (double)cfg->rope_theta, p.q,
-                                   k_cache, v_cache, s));
-    TMOE_TRY(launch_attn_decode(p.q, k_cache, v_cache, cache_len, T, nq, nkv, cfg->max_len, p.pm, p.pl, p.pacc,
-                                p.o, s));
+    const float* qkv_rows = p.ksq ? p.pq : reinterpret_cast<const float*>(p.qkv);
+    if (attn_rope_fused_ok(nq, nkv, cfg->max_len)) {
+        // q / k norms, rotation and the cache append inside the attention launch
+        TMOE_TRY(launch_attn_rope_decode(qkv_rows, p.ksq, T, nq, nkv, w->q_norm, w->k_norm, cfg->eps, pos, cache_len,
+                                         cfg->max_len, cfg->rope_sections[1], cfg->rope_sections[2],
+                                         (double)cfg->rope_theta, k_cache, v_cache, p.pm, p.pl, p.pacc, p.o, s));
+    } else {
+        TMOE_TRY(launch_qk_rope_append(qkv_rows, p.ksq, T, nq, nkv, w->q_norm, w->k_norm, cfg->eps, pos, cache_len,
+                                       cfg->max_len, cfg->rope_sections[1], cfg->rope_sections[2],
+                                       (double)cfg->rope_theta, p.q, k_cache, v_cache, s));
+        TMOE_TRY(launch_attn_decode(p.q, k_cache, v_cache, cache_len, T, nq, nkv, cfg->max_len, p.pm, p.pl, p.pacc,
+                                    p.o, s));
+    }
     if (p.kso) {
         TMOE_TRY(launch_skinny_gemm(p.o, w->w_o, p.po, T, H, nq * d, p.kso, s));
         return hip_status(launch_attn_out(p.po, p.kso, residual, y, T, H, norm_gain, norm_eps, norm_out, s));

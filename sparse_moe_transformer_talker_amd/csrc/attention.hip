@@ -36,15 +36,18 @@ __host__ __device__ constexpr int attn_chunk(int max_len) { return kKeysPerWave 
 // [T, nkv, 128, max_len].  A stream whose len is outside [0, max_len) writes no
 // cache entry.
 constexpr int kRopeWaves = 4;
-__global__ __launch_bounds__(64 * kRopeWaves) void qk_rope_append_kernel(
-    const void* __restrict__ qkv, int KS, int64_t T, int nq, int nkv, const float* __restrict__ q_gain,
-    const float* __restrict__ k_gain, float eps, const int32_t* __restrict__ pos, const int32_t* __restrict__ len,
-    int max_len, int sec_h, int sec_w, double log_theta, bf16_t* __restrict__ q_out, bf16_t* __restrict__ kc,
-    bf16_t* __restrict__ vc) {
-    const int64_t t = blockIdx.x;
-    const int y = blockIdx.y * kRopeWaves + (int)(threadIdx.x >> 6);
+
+// Pair l (lane l) of row y (a query, key or value head of the fused q / k / v
+// row) of token t, as the bf16 pair the attention reads: the KS fp32 partials
+// summed in order (or the bf16 row when KS == 0); query and key heads then take
+// the RMSNorm over the head times the gain and the rotation (above).  Called by
+// one full wave.
+__device__ __forceinline__ uint32_t rope_pair(const void* __restrict__ qkv, int KS, int64_t T, int nq, int nkv,
+                                              int64_t t, int y, const float* __restrict__ q_gain,
+                                              const float* __restrict__ k_gain, float eps,
+                                              const int32_t* __restrict__ pos, int sec_h, int sec_w,
+                                              double log_theta) {
     const int l = lane_id();
-    if (y >= nq + 2 * nkv) return;  // wave-uniform
     const int64_t ld = (int64_t)(nq + 2 * nkv) * kHead;
     const int64_t e = t * ld + (int64_t)y * kHead + 2 * l;
     float x0, x1;
@@ -62,18 +65,7 @@ __global__ __launch_bounds__(64 * kRopeWaves) void qk_rope_append_kernel(
         x0 = __uint_as_float(raw << 16);
         x1 = __uint_as_float(raw & 0xFFFF0000u);
     }
-    const int n = len[t];
-    const bool ok = n >= 0 && n < max_len;
-    if (y >= nq + nkv) {  // values: dims are rows of the transposed cache
-        const int g = y - nq - nkv;
-        if (ok) {
-            const uint32_t packed = pack_bf16x2(x0, x1);
-            bf16_t* col = vc + ((t * nkv + g) * (int64_t)kHead + 2 * l) * max_len + n;
-            col[0] = (bf16_t)(packed & 0xFFFFu);
-            col[max_len] = (bf16_t)(packed >> 16);
-        }
-        return;
-    }
+    if (y >= nq + nkv) return pack_bf16x2(x0, x1);  // values: unchanged
     const float ss = wave_sum_dpp(fmaf(x0, x0, x1 * x1));
     const float inv = 1.0f / sqrtf(ss * (1.0f / kHead) + eps);
     const float* gain = y < nq ? q_gain : k_gain;
@@ -85,13 +77,45 @@ __global__ __launch_bounds__(64 * kRopeWaves) void qk_rope_append_kernel(
     const float red = (float)(ang - two_pi * rint(ang / two_pi));
     float s, c;
     sincosf(red, &s, &c);
-    const uint32_t packed = pack_bf16x2(x0 * c - x1 * s, x0 * s + x1 * c);
-    if (y < nq) {
-        *reinterpret_cast<uint32_t*>(q_out + (t * nq + y) * kHead + 2 * l) = packed;
-    } else if (ok) {
-        const int g = y - nq;
+    return pack_bf16x2(x0 * c - x1 * s, x0 * s + x1 * c);
+}
+
+// Pair `packed` of the new position's key (into the key cache [T, nkv, max_len,
+// 128]) or value (into the transposed value cache [T, nkv, 128, max_len]) of
+// KV head g at position n.
+__device__ __forceinline__ void append_pair(bool is_value, uint32_t packed, int64_t t, int g, int nkv, int n,
+                                            int max_len, bf16_t* __restrict__ kc, bf16_t* __restrict__ vc) {
+    const int l = lane_id();
+    if (is_value) {
+        bf16_t* col = vc + ((t * nkv + g) * (int64_t)kHead + 2 * l) * max_len + n;
+        col[0] = (bf16_t)(packed & 0xFFFFu);
+        col[max_len] = (bf16_t)(packed >> 16);
+    } else {
         *reinterpret_cast<uint32_t*>(kc + (((t * nkv + g) * (int64_t)max_len + n) * kHead + 2 * l)) = packed;
     }
+}
+
+// One wave per (token, head of the fused q / k / v row), four heads per
+// workgroup; lane l owns pair l.  Queries go to q_out [T, nq, 128]; keys and
+// values to position len[t] of the caches.  A stream whose len is outside
+// [0, max_len) writes no cache entry.
+__global__ __launch_bounds__(64 * kRopeWaves) void qk_rope_append_kernel(
+    const void* __restrict__ qkv, int KS, int64_t T, int nq, int nkv, const float* __restrict__ q_gain,
+    const float* __restrict__ k_gain, float eps, const int32_t* __restrict__ pos, const int32_t* __restrict__ len,
+    int max_len, int sec_h, int sec_w, double log_theta, bf16_t* __restrict__ q_out, bf16_t* __restrict__ kc,
+    bf16_t* __restrict__ vc) {
+    const int64_t t = blockIdx.x;
+    const int y = blockIdx.y * kRopeWaves + (int)(threadIdx.x >> 6);
+    const int l = lane_id();
+    if (y >= nq + 2 * nkv) return;  // wave-uniform
+    const uint32_t packed = rope_pair(qkv, KS, T, nq, nkv, t, y, q_gain, k_gain, eps, pos, sec_h, sec_w, log_theta);
+    if (y < nq) {
+        *reinterpret_cast<uint32_t*>(q_out + (t * nq + y) * kHead + 2 * l) = packed;
+        return;
+    }
+    const int n = len[t];
+    if (n >= 0 && n < max_len)
+        append_pair(y >= nq + nkv, packed, t, y >= nq + nkv ? y - nq - nkv : y - nq, nkv, n, max_len, kc, vc);
 }
 
 // y = sum of KS fp32 partial rows (in order) + residual, stored bf16; with
@@ -170,7 +194,25 @@ __global__ __launch_bounds__(128) void attn_out_kernel(const float* __restrict__
 // and unnormalised output per head; an empty chunk writes m = -inf, l = 0.  When
 // the cache is a single chunk (nch == 1) the workgroup writes the normalised
 // output od [T, nq, 128] instead (zeros for a stream with no valid position).
-template <int G, int kAttnWaves>
+//
+// FUSED: the workgroup also forms what qk_rope_append_kernel would (it then
+// needs no q): waves 0 .. G - 1 its G query heads, wave G the new key and wave
+// G + 1 the new value of KV head g (rope_pair), into LDS; the workgroup whose
+// chunk holds the new position appends them to the caches, and every
+// workgroup reads the new position's key and value from LDS rather than from
+// the caches (which the append may not have reached).
+struct RopeArgs {
+    const void* qkv;  // the fused q / k / v rows: KS fp32 partials, or bf16 when KS == 0
+    int KS;
+    const float *q_gain, *k_gain;
+    float eps;
+    const int32_t* pos;
+    int sec_h, sec_w;
+    double log_theta;
+    bf16_t *kc, *vc;  // the caches, written at len[t]
+};
+
+template <int G, int kAttnWaves, bool FUSED>
 __global__ __launch_bounds__(64 * kAttnWaves) void attn_partial_kernel(const bf16_t* __restrict__ q,
                                                                        const bf16_t* __restrict__ kc,
                                                                        const bf16_t* __restrict__ vt,
@@ -178,8 +220,11 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_partial_kernel(const bf1
                                                                        int max_len, int nch, float* __restrict__ pm,
                                                                        float* __restrict__ pl,
                                                                        float* __restrict__ pacc,
-                                                                       bf16_t* __restrict__ od) {
+                                                                       bf16_t* __restrict__ od, RopeArgs ra) {
+    static_assert(!FUSED || G + 2 <= kAttnWaves, "a wave per query head, the new key and the new value");
     __shared__ float red_m[kAttnWaves][16], red_l[kAttnWaves][16];
+    __shared__ __attribute__((aligned(16))) bf16_t qs[FUSED ? G : 1][kHead];  // FUSED: the query heads
+    __shared__ __attribute__((aligned(16))) bf16_t kvn[FUSED ? 2 : 1][kHead];  // FUSED: new key, new value
     __shared__ float red_acc[kAttnWaves][G][kHead];
     __shared__ __attribute__((aligned(16))) bf16_t pbuf[kAttnWaves][16][40];  // rows padded to 80 bytes
     const int c = blockIdx.x, g = blockIdx.y;
@@ -211,12 +256,10 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_partial_kernel(const bf1
     }
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) o[dt] = zero;
-    if (key0 < n) {  // wave-uniform
-        const u32x4 z4 = {0, 0, 0, 0};
-        u32x4 qa[4], kb[2][4], vb[8];
-        const bf16_t* qp = q + ((t * nq + g * G + min(col, G - 1)) * kHead + grp * 8);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) qa[s] = col < G ? *reinterpret_cast<const u32x4*>(qp + s * 32) : z4;
+    const bool act = key0 < n;  // wave-uniform
+    const u32x4 z4 = {0, 0, 0, 0};
+    u32x4 kb[2][4], vb[8];
+    auto load_kv = [&]() {
         const int64_t kvrow = (t * nkv + g) * (int64_t)max_len;
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {  // positions past the end load the last one (masked below)
@@ -229,6 +272,63 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_partial_kernel(const bf1
         const bf16_t* vp = vt + ((t * nkv + g) * (int64_t)kHead + col) * max_len + key0 + grp * 8;
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) vb[dt] = *reinterpret_cast<const u32x4*>(vp + (int64_t)dt * 16 * max_len);
+    };
+    // With the fused q / k / v step, a short workgroup (few waves, the
+    // predictor's frames) requests the cached keys and values before it, so
+    // their latency overlaps it; a long one requests them after (measured faster)
+    constexpr bool kv_first = !FUSED || kAttnWaves == kAttnWavesShort;
+    if (kv_first && act) load_kv();
+    if constexpr (FUSED) {
+        if (wave < G + 2) {  // wave-uniform
+            const int nq_ = nkv * G;
+            const int y = wave < G ? g * G + wave : (wave == G ? nq_ + g : nq_ + nkv + g);
+            const uint32_t packed = rope_pair(ra.qkv, ra.KS, (int64_t)gridDim.z, nq_, nkv, t, y, ra.q_gain, ra.k_gain,
+                                              ra.eps, ra.pos, ra.sec_h, ra.sec_w, ra.log_theta);
+            if (wave < G) {
+                *reinterpret_cast<uint32_t*>(&qs[wave][2 * lane]) = packed;
+            } else {
+                *reinterpret_cast<uint32_t*>(&kvn[wave - G][2 * lane]) = packed;
+                if (n > 0 && nraw / (kKeysPerWave * kAttnWaves) == c)  // this chunk holds the new position
+                    append_pair(wave == G + 1, packed, t, g, nkv, nraw, max_len, ra.kc, ra.vc);
+            }
+        }
+        __syncthreads();
+    }
+    if (!kv_first && act) load_kv();
+    if (act) {
+        u32x4 qa[4];
+        if constexpr (FUSED) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                qa[s] = col < G ? *reinterpret_cast<const u32x4*>(&qs[min(col, G - 1)][grp * 8 + s * 32]) : z4;
+            // the new position (n - 1) from LDS: its key for the lanes it falls
+            // on (the positions past the end load it too, masked below)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+                if (min(key0 + nt * 16 + col, n - 1) == nraw)
+#pragma unroll
+                    for (int s = 0; s < 4; ++s)
+                        kb[nt][s] = *reinterpret_cast<const u32x4*>(&kvn[0][grp * 8 + s * 32]);
+        } else {
+            const bf16_t* qp = q + ((t * nq + g * G + min(col, G - 1)) * kHead + grp * 8);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) qa[s] = col < G ? *reinterpret_cast<const u32x4*>(qp + s * 32) : z4;
+        }
+        if constexpr (FUSED) {
+            // the new position's value (dimension 16 dt + col) from LDS
+            const int j = nraw - (key0 + grp * 8);
+            if (j >= 0 && j < 8) {
+#pragma unroll
+                for (int dt = 0; dt < 8; ++dt) {
+                    const uint32_t nv = (uint32_t)kvn[1][16 * dt + col];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (e == (j >> 1))
+                            vb[dt][e] = (j & 1) ? ((vb[dt][e] & 0x0000FFFFu) | (nv << 16))
+                                                : ((vb[dt][e] & 0xFFFF0000u) | nv);
+                }
+            }
+        }
         f32x4 sacc[2] = {zero, zero};
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
@@ -437,7 +537,8 @@ hipError_t launch_attn_decode(const void* q, const void* kc, const void* vc, con
     const bf16_t *qb = (const bf16_t*)q, *kb = (const bf16_t*)kc, *vb = (const bf16_t*)vc;
     bf16_t* ob = (bf16_t*)o;
 #define TMOE_AP(GG, NW)                                                                                        \
-    attn_partial_kernel<GG, NW><<<grid, 64 * NW, 0, st>>>(qb, kb, vb, len, nkv, max_len, nch, pm, pl, pacc, ob)
+    attn_partial_kernel<GG, NW, false><<<grid, 64 * NW, 0, st>>>(qb, kb, vb, len, nkv, max_len, nch, pm, pl, pacc, \
+                                                                 ob, RopeArgs{})
 #define TMOE_AP_G(NW)                \
     if (G == 8) TMOE_AP(8, NW);      \
     else if (G == 4) TMOE_AP(4, NW); \
@@ -447,6 +548,41 @@ hipError_t launch_attn_decode(const void* q, const void* kc, const void* vc, con
     else { TMOE_AP_G(kAttnWavesShort) }
 #undef TMOE_AP_G
 #undef TMOE_AP
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || nch == 1) return e;  // a single chunk wrote the output itself
+    attn_combine_kernel<<<dim3((unsigned)nq, (unsigned)T), kHead, 0, st>>>(pm, pl, pacc, len, nq, nkv, max_len, nch,
+                                                                          (bf16_t*)o);
+    return hipGetLastError();
+}
+
+bool attn_rope_fused_ok(int nq, int nkv, int max_len) { return nq / nkv + 2 <= attn_waves(max_len); }
+
+hipError_t launch_attn_rope_decode(const float* qkv, int KS, int64_t T, int nq, int nkv, const float* q_gain,
+                                   const float* k_gain, float eps, const int32_t* pos, const int32_t* len,
+                                   int max_len, int sec_h, int sec_w, double theta, void* kc, void* vc, float* pm,
+                                   float* pl, float* pacc, void* o, hipStream_t st) {
+    if (T <= 0) return hipSuccess;
+    if (!attn_rope_fused_ok(nq, nkv, max_len)) return hipErrorInvalidValue;
+    const int nch = attn_chunks(max_len);
+    dim3 grid((unsigned)nch, (unsigned)nkv, (unsigned)T);
+    const int G = nq / nkv;
+    const RopeArgs ra{qkv, KS, q_gain, k_gain, eps, pos, sec_h, sec_w, log(theta), (bf16_t*)kc, (bf16_t*)vc};
+    const bf16_t *kb = (const bf16_t*)kc, *vb = (const bf16_t*)vc;
+    bf16_t* ob = (bf16_t*)o;
+#define TMOE_AF(GG, NW)                                                                                        \
+    attn_partial_kernel<GG, NW, true><<<grid, 64 * NW, 0, st>>>(nullptr, kb, vb, len, nkv, max_len, nch, pm, pl, \
+                                                                pacc, ob, ra)
+    if (attn_waves(max_len) == kAttnWavesLong) {
+        if (G == 8) TMOE_AF(8, kAttnWavesLong);
+        else if (G == 4) TMOE_AF(4, kAttnWavesLong);
+        else if (G == 2) TMOE_AF(2, kAttnWavesLong);
+        else TMOE_AF(1, kAttnWavesLong);
+    } else {
+        if (G == 2) TMOE_AF(2, kAttnWavesShort);
+        else if (G == 1) TMOE_AF(1, kAttnWavesShort);
+        else return hipErrorInvalidValue;
+    }
+#undef TMOE_AF
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || nch == 1) return e;  // a single chunk wrote the output itself
     attn_combine_kernel<<<dim3((unsigned)nq, (unsigned)T), kHead, 0, st>>>(pm, pl, pacc, len, nq, nkv, max_len, nch,

@@ -231,6 +231,14 @@ hipError_t launch_qk_rope_append(const float* qkv, int KS, int64_t T, int nq, in
 // cache; pm / pl [T nkv chunks (nq / nkv)], pacc [.. x 128] fp32 scratch
 hipError_t launch_attn_decode(const void* q, const void* kc, const void* vc, const int32_t* len, int64_t T, int nq,
                               int nkv, int max_len, float* pm, float* pl, float* pacc, void* o, hipStream_t st);
+// launch_qk_rope_append and launch_attn_decode in one launch (no q buffer):
+// each attention workgroup forms its query heads and the new key and value
+// itself; when attn_rope_fused_ok (nq / nkv + 2 waves fit the workgroup)
+bool attn_rope_fused_ok(int nq, int nkv, int max_len);
+hipError_t launch_attn_rope_decode(const float* qkv, int KS, int64_t T, int nq, int nkv, const float* q_gain,
+                                   const float* k_gain, float eps, const int32_t* pos, const int32_t* len,
+                                   int max_len, int sec_h, int sec_w, double theta, void* kc, void* vc, float* pm,
+                                   float* pl, float* pacc, void* o, hipStream_t st);
 // y [T, H] = sum of the KS fp32 partials [KS][T][H] (in order) + residual
 // (nullable), stored bf16; norm_out (nullable) = RMSNorm(y) * gain (nullable)
 hipError_t launch_attn_out(const float* part, int KS, const void* residual, void* y, int64_t T, int H,
