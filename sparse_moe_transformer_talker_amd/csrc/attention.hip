@@ -471,27 +471,6 @@ __global__ __launch_bounds__(256) void frame_setup_kernel(int32_t* __restrict__ 
     if (i < T) codes[i] = c0[i];
 }
 
-// out [n, H] = table[idx[i]] (bf16, H % 8 == 0); an index outside [0, rows)
-// gives a zero row.
-__global__ __launch_bounds__(128) void embed_rows_kernel(const bf16_t* __restrict__ table, int rows,
-                                                         const int32_t* __restrict__ idx, int H,
-                                                         bf16_t* __restrict__ out) {
-    const int64_t i = blockIdx.x;
-    const int r = idx[i];
-    const bool ok = r >= 0 && r < rows;
-    const u32x4 z = {0, 0, 0, 0};
-    for (int h = threadIdx.x * 8; h < H; h += 128 * 8)
-        *reinterpret_cast<u32x4*>(out + i * H + h) =
-            ok ? *reinterpret_cast<const u32x4*>(table + (int64_t)r * H + h) : z;
-}
-
-hipError_t launch_embed_rows(const void* table, int rows, const int32_t* idx, int64_t n, int H, void* out,
-                             hipStream_t st) {
-    if (n <= 0) return hipSuccess;
-    embed_rows_kernel<<<(unsigned)n, 128, 0, st>>>((const bf16_t*)table, rows, idx, H, (bf16_t*)out);
-    return hipGetLastError();
-}
-
 hipError_t launch_frame_setup(int32_t* pos, int32_t* len, int P, int64_t T, const int32_t* c0, int32_t* codes,
                               hipStream_t st) {
     const int64_t n = (int64_t)P * T;

@@ -243,10 +243,8 @@ hipError_t launch_attn_rope_decode(const float* qkv, int KS, int64_t T, int nq, 
 // (nullable), stored bf16; norm_out (nullable) = RMSNorm(y) * gain (nullable)
 hipError_t launch_attn_out(const float* part, int KS, const void* residual, void* y, int64_t T, int H,
                            const float* gain, float eps, void* norm_out, hipStream_t st);
-// out [n, H] = table[idx[i]] (bf16 rows, H % 8 == 0); indices outside [0, rows) give zero rows
-hipError_t launch_embed_rows(const void* table, int rows, const int32_t* idx, int64_t n, int H, void* out,
-                             hipStream_t st);
-// x [T, H] = table[idx[t]] as launch_embed_rows; out = RMSNorm(x) * gain (bf16, H % 8 == 0, H <= 4096)
+// x [T, H] = table[idx[t]] (bf16 rows, H % 8 == 0; indices outside [0, rows) give zero rows) and
+// out = RMSNorm(x) * gain (H <= 4096)
 hipError_t launch_embed_norm(const void* table, int rows, const int32_t* idx, void* x, const float* gain, float eps,
                              int64_t T, int H, void* out, hipStream_t st);
 // Frame set-up of the code predictor: pos [P][T][3] = p, len [P][T] = p, codes
