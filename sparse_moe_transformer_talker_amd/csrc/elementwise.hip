@@ -432,7 +432,7 @@ hipError_t launch_add_rmsnorm(const void* a, const void* b, void* x, const float
 
 // Row t of a code embedding table, gathered (a code outside [0, rows) gives a
 // zero row) and stored to x, then its RMSNorm times the gain stored to out:
-// the gather of embed_rows and rmsnorm_bf16x8_kernel in one launch, same bits.
+// a table gather followed by rmsnorm_bf16x8_kernel, in one launch and with the same bits.
 template <int NCH>
 __global__ __launch_bounds__(128) void embed_norm_bf16x8_kernel(const bf16_t* __restrict__ table, int rows,
                                                                 const int32_t* __restrict__ idx, bf16_t* x,
