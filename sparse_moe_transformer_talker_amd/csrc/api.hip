@@ -514,9 +514,9 @@ int layer_run(const moe_config* cfg, const moe_weights* w, const void* x, const 
     TMOE_TRY(mark(0));
     auto ev = [&](int i) { return stage_events ? static_cast<hipEvent_t>(stage_events[i]) : nullptr; };
     if (p.decode) {
-        // scores (and the shared gate/up) -> selection -> every expert slice and
-        // the shared down tiles in one launch -> the partial rows summed per
-        // token with the routing weights
+        // scores -> selection (beside it, the shared gate/up) -> every expert
+        // slice and the shared down tiles in one launch -> the partial rows
+        // summed per token with the routing weights
         TMOE_TRY(launch_route_decode(x, w->router, w->router_bias, T, H, E, k, cfg->norm_topk_prob, p.sc, p.dv, idx,
                                      wt, Is > 0 ? w->shared_gate : nullptr, Is > 0 ? w->shared_up : nullptr, Is, p.hs,
                                      p.mask, counts, s));
