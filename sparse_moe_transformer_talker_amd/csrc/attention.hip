@@ -120,7 +120,10 @@ __global__ __launch_bounds__(64 * kRopeWaves) void qk_rope_append_kernel(
 
 // y = sum of KS fp32 partial rows (in order) + residual, stored bf16; with
 // norm_out, also RMSNorm of the stored y times the gain.  One workgroup per
-// row, 8 contiguous features per thread per pass.
+// row, 8 contiguous features per thread per pass.  KSC > 0: KS == KSC, and
+// every partial row is requested before the first add (one memory round trip
+// instead of KS); the sums are the same, in the same order.
+template <int KSC>
 __global__ __launch_bounds__(128) void attn_out_kernel(const float* __restrict__ part, int KS, int64_t T, int H,
                                                        const bf16_t* residual, bf16_t* y,
                                                        const float* __restrict__ gain, float eps,
@@ -132,13 +135,27 @@ __global__ __launch_bounds__(128) void attn_out_kernel(const float* __restrict__
         float v[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) v[i] = 0.f;
-        for (int s = 0; s < KS; ++s) {
-            const float* p = part + (s * T + t) * (int64_t)H + h;
-            const f32x4 a = *reinterpret_cast<const f32x4*>(p), b = *reinterpret_cast<const f32x4*>(p + 4);
+        auto add = [&](const f32x4& a, const f32x4& b) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 v[i] += a[i];
                 v[4 + i] += b[i];
+            }
+        };
+        if (KSC > 0) {
+            f32x4 pa[KSC > 0 ? KSC : 1], pb[KSC > 0 ? KSC : 1];
+#pragma unroll
+            for (int s = 0; s < KSC; ++s) {
+                const float* p = part + (s * T + t) * (int64_t)H + h;
+                pa[s] = *reinterpret_cast<const f32x4*>(p);
+                pb[s] = *reinterpret_cast<const f32x4*>(p + 4);
+            }
+#pragma unroll
+            for (int s = 0; s < KSC; ++s) add(pa[s], pb[s]);
+        } else {
+            for (int s = 0; s < KS; ++s) {
+                const float* p = part + (s * T + t) * (int64_t)H + h;
+                add(*reinterpret_cast<const f32x4*>(p), *reinterpret_cast<const f32x4*>(p + 4));
             }
         }
         if (residual) {
@@ -166,13 +183,17 @@ __global__ __launch_bounds__(128) void attn_out_kernel(const float* __restrict__
     const float inv = 1.0f / sqrtf((wsum[0] + wsum[1]) / (float)H + eps);
     for (int h = threadIdx.x * 8; h < H; h += 128 * 8) {
         const u32x4 yv = *reinterpret_cast<const u32x4*>(y + t * H + h);
+        float g[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) g[i] = 1.f;
+        if (gain)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) g[i] = gain[h + i];
         u32x4 o;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const float g0 = gain ? gain[h + 2 * q] : 1.f, g1 = gain ? gain[h + 2 * q + 1] : 1.f;
-            o[q] = pack_bf16x2(__uint_as_float(yv[q] << 16) * inv * g0,
-                               __uint_as_float(yv[q] & 0xFFFF0000u) * inv * g1);
-        }
+        for (int q = 0; q < 4; ++q)
+            o[q] = pack_bf16x2(__uint_as_float(yv[q] << 16) * inv * g[2 * q],
+                               __uint_as_float(yv[q] & 0xFFFF0000u) * inv * g[2 * q + 1]);
         *reinterpret_cast<u32x4*>(norm_out + t * H + h) = o;
     }
 }
@@ -502,8 +523,19 @@ hipError_t launch_qk_rope_append(const float* qkv, int KS, int64_t T, int nq, in
 hipError_t launch_attn_out(const float* part, int KS, const void* residual, void* y, int64_t T, int H,
                            const float* gain, float eps, void* norm_out, hipStream_t st) {
     if (T <= 0) return hipSuccess;
-    attn_out_kernel<<<(unsigned)T, 128, 0, st>>>(part, KS, T, H, (const bf16_t*)residual, (bf16_t*)y, gain, eps,
-                                                (bf16_t*)norm_out);
+#define TMOE_AO(KSC)                                                                                        \
+    attn_out_kernel<KSC><<<(unsigned)T, 128, 0, st>>>(part, KS, T, H, (const bf16_t*)residual, (bf16_t*)y, gain, \
+                                                     eps, (bf16_t*)norm_out)
+    switch (KS) {
+        case 1: TMOE_AO(1); break;
+        case 2: TMOE_AO(2); break;
+        case 4: TMOE_AO(4); break;
+        case 8: TMOE_AO(8); break;
+        case 12: TMOE_AO(12); break;
+        case 16: TMOE_AO(16); break;
+        default: TMOE_AO(0); break;
+    }
+#undef TMOE_AO
     return hipGetLastError();
 }
 
