@@ -55,10 +55,18 @@ __device__ __forceinline__ uint32_t rope_pair(const void* __restrict__ qkv, int 
         const float* p = reinterpret_cast<const float*>(qkv);
         x0 = 0.f;
         x1 = 0.f;
-        for (int s = 0; s < KS; ++s) {
-            const f32x2_t v = *reinterpret_cast<const f32x2_t*>(p + s * T * ld + e);
-            x0 += v[0];
-            x1 += v[1];
+        // four partials requested at a time (the index clamped, the surplus
+        // dropped), then added in order
+        for (int s0 = 0; s0 < KS; s0 += 4) {
+            f32x2_t v[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                v[i] = *reinterpret_cast<const f32x2_t*>(p + min(s0 + i, KS - 1) * T * ld + e);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                x0 = s0 + i < KS ? x0 + v[i][0] : x0;
+                x1 = s0 + i < KS ? x1 + v[i][1] : x1;
+            }
         }
     } else {
         const uint32_t raw = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const bf16_t*>(qkv) + e);
