@@ -1056,7 +1056,7 @@ int moe_codec_head_argmax(const moe_config* cfg, const void* x, const void* w_he
     float* bd = cv.take<float>(T * V);
     if (logits) sc = logits;
     hipStream_t s = as_stream(stream);
-    TMOE_TRY(launch_scores(cfg->dtype, x, w_head, nullptr, T, cfg->hidden_size, V, sc, bd, s));
+    TMOE_TRY(launch_scores_argmax(cfg->dtype, x, w_head, T, cfg->hidden_size, V, sc, bd, s));
     return hip_status(launch_argmax(cfg->dtype, sc, bd, x, w_head, T, cfg->hidden_size, V, c0, s));
 }
 
@@ -1147,7 +1147,7 @@ int moe_predictor_frame(const moe_predictor_config* cfg, const moe_predictor_wei
         if (q >= 1) {
             const void* head = static_cast<const char*>(w->lm_head) + (q - 1) * table;
             const void* xf = xn_out ? static_cast<const char*>(xn_out) + (int64_t)q * T * H * 2 : p.XN;
-            TMOE_TRY(launch_scores(MOE_BF16, xf, head, nullptr, T, H, K, p.sc, p.bd, s));
+            TMOE_TRY(launch_scores_argmax(MOE_BF16, xf, head, T, H, K, p.sc, p.bd, s));
             TMOE_TRY(launch_argmax(MOE_BF16, p.sc, p.bd, xf, head, T, H, K, codes + (int64_t)q * T, s));
         }
     }

@@ -61,6 +61,11 @@ hipError_t launch_argmax(int dtype, const float* sc, const float* bd, const void
 // from fp64 logits recomputed from x and W.  n <= kSampleMaxN.
 constexpr int kSampleMaxN = 8192;
 bool sample_ok(int n);
+// Scores for an exact argmax (no bias): fp32 matrix-core partials added in fp64
+// for bf16 with H % 32 == 0 and T <= 256 (the argmax rescores the rare
+// near-ties in fp64); else launch_scores.
+hipError_t launch_scores_argmax(int dtype, const void* x, const void* W, int64_t T, int H, int n, float* sc,
+                                float* bd, hipStream_t st);
 // Scores with the tightest bounds available (fp64 sums of exact products for bf16
 // with H % 256 == 0, at any T; else launch_scores).
 hipError_t launch_scores_exact(int dtype, const void* x, const void* W, int64_t T, int H, int n, float* sc, float* bd,

@@ -1809,6 +1809,19 @@ hipError_t launch_argmax(int dtype, const float* sc, const float* bd, const void
 
 bool sample_ok(int n) { return n >= 1 && n <= kSampleMaxN; }
 
+hipError_t launch_scores_argmax(int dtype, const void* x, const void* W, int64_t Ttok, int H, int n, float* sc,
+                                float* bd, hipStream_t st) {
+    if (dtype == kBF16 && H % 32 == 0 && Ttok <= 256) {
+        // fp32 matrix-core partials into fp64: bounds near 5e-5 relative, ample
+        // for an argmax whose rare near-ties the argmax rescores exactly
+        dim3 grid((unsigned)((Ttok + 15) / 16), (unsigned)((n + 15) / 16));
+        scores_kernel<16><<<grid, 64 * kScoreWaves, 0, st>>>((const bf16_t*)x, (const bf16_t*)W, nullptr, Ttok, H, n,
+                                                             sc, bd);
+        return hipGetLastError();
+    }
+    return launch_scores(dtype, x, W, nullptr, Ttok, H, n, sc, bd, st);
+}
+
 hipError_t launch_scores_exact(int dtype, const void* x, const void* W, int64_t Ttok, int H, int n, float* sc,
                                float* bd, hipStream_t st) {
     if (dtype == kBF16 && H % 256 == 0) {
