@@ -8,7 +8,7 @@
 // Four launches:
 //  1. route_scores_kernel: the E router scores of every token on the matrix
 //     cores with a rigorous error bound, spread over T / 8 x E / 16 workgroups.
-//  2. route_select_kernel: one wave per token: the top-k (ties to the lower
+//  2. route_select_kernel: one workgroup per token: the top-k (ties to the lower
 //     expert index) is certified from the bounds or settled by fp64 rescoring of
 //     the candidates, so it is the top-k of the scores computed in fp64, up to
 //     fp64 summation rounding; then the routing weights.  Further workgroups of
@@ -105,13 +105,13 @@ __device__ __forceinline__ f32x4 mfma(const u32x4& a, const u32x4& b, const f32x
 // cores round or truncate, and the fp64 additions; plus 2^-52 |s_e| for the
 // bias add).  Scores and bounds go to two [T, E] fp64 arrays.
 //
-// route_select_kernel: one wave per token: the top k of s by (value, lower
-// index).  It is certified when the intervals [s - d, s + d] of consecutive
+// route_select_kernel: one workgroup per token, whose wave 0 picks the top k
+// of s by (value, lower index).  It is certified when the intervals [s - d, s + d] of consecutive
 // picks, and of the k-th pick against every other expert, are strictly
 // ordered.  Otherwise every expert whose upper bound reaches the lowest lower
-// bound of the picks is rescored in fp64 from exact products (four candidates
-// at a time, each lane summing elements l, l + 64, ... in order, then the wave),
-// which gives the top-k of the fp64 scores up to fp64 summation rounding;
+// bound of the picks is rescored in fp64 from exact products (the four waves
+// take eight candidates each at a time, each lane summing elements 8 l .. 8 l
+// + 7 of each 512-wide chunk in order, then the wave), which gives the top-k of the fp64 scores up to fp64 summation rounding;
 // experts not rescored lie strictly below every pick.  Weights: e^(s_i - s_max)
 // over their sum (norm_topk_prob) or over the sum of all E terms (the plain
 // softmax probabilities), in fp64.
@@ -133,49 +133,6 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppRowBcast15, 0xa, 0xf, false));
     v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppRowBcast31, 0xc, 0xf, false));
     return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
-}
-
-// Wave-wide best (key, index): larger key first, then lower index.  Returned to
-// every lane.
-__device__ __forceinline__ void wave_best_key_index(uint64_t& key, int& idx) {
-#define TMOE_BEST_STEP(CTRL, ROWS)                                                                      \
-    {                                                                                                   \
-        const uint32_t lo = __builtin_amdgcn_update_dpp(0u, (uint32_t)key, CTRL, ROWS, 0xf, false);     \
-        const uint32_t hi = __builtin_amdgcn_update_dpp(0u, (uint32_t)(key >> 32), CTRL, ROWS, 0xf, false); \
-        const int oi = __builtin_amdgcn_update_dpp(0x7fffffff, idx, CTRL, ROWS, 0xf, false);           \
-        const uint64_t ok = ((uint64_t)hi << 32) | lo;                                                  \
-        if (ok > key || (ok == key && oi < idx)) { key = ok; idx = oi; }                                \
-    }
-    TMOE_BEST_STEP(kDppRowShr1, 0xf)
-    TMOE_BEST_STEP(kDppRowShr2, 0xf)
-    TMOE_BEST_STEP(kDppRowShr4, 0xf)
-    TMOE_BEST_STEP(kDppRowShr8, 0xf)
-    TMOE_BEST_STEP(kDppRowBcast15, 0xa)
-    TMOE_BEST_STEP(kDppRowBcast31, 0xc)
-#undef TMOE_BEST_STEP
-    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)key, 63);
-    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(key >> 32), 63);
-    key = ((uint64_t)hi << 32) | lo;
-    idx = __builtin_amdgcn_readlane(idx, 63);
-}
-
-// k rounds of the wave-wide best over lane l's experts l and l + 64 (value v,
-// key 0 = none); sel / val receive the picks in order.
-__device__ __forceinline__ void wave_topk(double v0, double v1, bool ok0, bool ok1, int k, int (&sel)[8],
-                                          double (&val)[8]) {
-    const int lane = lane_id();
-    uint64_t k0 = ok0 ? double_order_key(v0) : 0, k1 = ok1 ? double_order_key(v1) : 0;
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-        if (r >= k) { sel[r] = 0; val[r] = 0.0; continue; }
-        uint64_t key = k0 >= k1 ? k0 : k1;
-        int ix = k0 >= k1 ? lane : lane + 64;
-        wave_best_key_index(key, ix);
-        sel[r] = ix;
-        val[r] = double_from_order_key(key);
-        if (ix == lane) k0 = 0;
-        if (ix == lane + 64) k1 = 0;
-    }
 }
 
 template <int H>
@@ -279,7 +236,7 @@ __global__ __launch_bounds__(256) void route_select_kernel(const bf16_t* __restr
                                                            const bf16_t* __restrict__ sg,
                                                            const bf16_t* __restrict__ su, int Is,
                                                            bf16_t* __restrict__ hs) {
-    const int nsel = (T + 3) / 4;
+    const int nsel = T;
     if ((int)blockIdx.x >= nsel) {
         // the shared expert's gate/up beside the selection (it needs no
         // routing): hs [T, Is] = SiLU(x sg^T) * (x su^T) in bf16, 8 features of
@@ -292,29 +249,29 @@ __global__ __launch_bounds__(256) void route_select_kernel(const bf16_t* __restr
                                    min(16, T - 16 * tq), 2 * Is, H, 1, f, 0);
         return;
     }
-    constexpr int NJ = H / 64;  // elements per lane of a rescored row
-    __shared__ double s_sc[4][128];
-    __shared__ double s_dv[4][128];
-    __shared__ double s_rs[4][128];
-    __shared__ int s_cand[4][128];
+    constexpr int NC8 = H / 512;  // 8-element chunks per lane of a rescored row
+    static_assert(H % 512 == 0, "hidden size");
+    // one token per workgroup: wave 0 selects; when the certificate fails the
+    // four waves share the candidates' rescoring
+    __shared__ double sct[128];
+    __shared__ double dvt[128];
+    __shared__ double rst[128];
+    __shared__ int cnd[128];
+    __shared__ int s_nc;
+    __shared__ int s_topi[8];
+    __shared__ double s_topv[8];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-    const int64_t t = 4 * (int64_t)blockIdx.x + wave;
-    if (t >= T) return;
-    double* const sct = s_sc[wave];
-    double* const dvt = s_dv[wave];
-    double* const rst = s_rs[wave];
-    int* const cnd = s_cand[wave];
+    const int64_t t = blockIdx.x;
     const bool ok0 = lane < E, ok1 = lane + 64 < E;
-    const double v0 = ok0 ? sc[t * E + lane] : 0.0, v1 = ok1 ? sc[t * E + lane + 64] : 0.0;
-    sct[lane] = v0;
-    sct[lane + 64] = v1;
-    dvt[lane] = ok0 ? dv[t * E + lane] : 0.0;
-    dvt[lane + 64] = ok1 ? dv[t * E + lane + 64] : 0.0;
-
     int sel[8];
     double val[8];
-    {
+    if (wave == 0) {
+        const double v0 = ok0 ? sc[t * E + lane] : 0.0, v1 = ok1 ? sc[t * E + lane + 64] : 0.0;
+        sct[lane] = v0;
+        sct[lane + 64] = v1;
+        dvt[lane] = ok0 ? dv[t * E + lane] : 0.0;
+        dvt[lane + 64] = ok1 ? dv[t * E + lane + 64] : 0.0;
         // the picks by a 32-bit key: the order-preserving image of the score's
         // fp32 rounding with its low 7 bits replaced by 127 - expert (larger
         // first, then the lower index).  The fp64 certificate below proves the
@@ -354,47 +311,94 @@ __global__ __launch_bounds__(256) void route_select_kernel(const bf16_t* __restr
         }
         const bool above = (!picked0 && hi0 >= kth_lo) || (!picked1 && hi1 >= kth_lo);
         cert = cert && !__any(above);
+        int nc = 0;
         if (!cert) {
             // every expert whose interval reaches the lowest pick's lower bound,
-            // listed in increasing index and rescored in fp64 from exact products
+            // listed in increasing index, for rescoring in fp64 from exact products
             const bool c0 = ok0 && hi0 >= lo_min, c1 = ok1 && hi1 >= lo_min;
             const uint64_t b0 = __ballot(c0), b1 = __ballot(c1);
-            const int n0 = __popcll(b0), nc = n0 + __popcll(b1);
+            const int n0 = __popcll(b0);
+            nc = n0 + __popcll(b1);
             if (c0) cnd[__popcll(b0 & lanemask_lt())] = lane;
             if (c1) cnd[n0 + __popcll(b1 & lanemask_lt())] = lane + 64;
-            double xh[NJ];
+        }
+        if (lane == 0) s_nc = nc;
+    }
+    __syncthreads();
+    const int nc = __builtin_amdgcn_readfirstlane(s_nc);  // 0: certified (uniform)
+    if (nc > 0) {
+        // wave w rescores candidates 8 w .. 8 w + 7, 8 w + 32 .., lane l holding
+        // elements 8 l .. 8 l + 7 of every 512-wide chunk of the token row and of
+        // each candidate row (16-byte loads), eight candidates' loads in flight
+        double xh[8 * NC8];
 #pragma unroll
-            for (int j = 0; j < NJ; ++j) xh[j] = (double)bf16_to_f32(x[t * H + lane + 64 * j]);
-            for (int c0i = 0; c0i < nc; c0i += 4) {
-                const bf16_t* wrow[4];
+        for (int c = 0; c < NC8; ++c) {
+            const u32x4 v = *reinterpret_cast<const u32x4*>(x + t * H + 512 * c + 8 * lane);
 #pragma unroll
-                for (int u = 0; u < 4; ++u) wrow[u] = W + (int64_t)cnd[min(c0i + u, nc - 1)] * H + lane;
-                double a4[4] = {0.0, 0.0, 0.0, 0.0};
+            for (int q = 0; q < 4; ++q) {
+                xh[8 * c + 2 * q] = (double)__uint_as_float(v[q] << 16);
+                xh[8 * c + 2 * q + 1] = (double)__uint_as_float(v[q] & 0xFFFF0000u);
+            }
+        }
+        for (int c0i = 8 * wave; c0i < nc; c0i += 32) {
+            u32x4 wv[8][NC8];
 #pragma unroll
-                for (int j = 0; j < NJ; ++j)
+            for (int u = 0; u < 8; ++u) {
+                const bf16_t* wr = W + (int64_t)cnd[min(c0i + u, nc - 1)] * H + 8 * lane;
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) a4[u] = fma(xh[j], (double)bf16_to_f32(wrow[u][64 * j]), a4[u]);
+                for (int c = 0; c < NC8; ++c) wv[u][c] = *reinterpret_cast<const u32x4*>(wr + 512 * c);
+            }
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const double sum = wave_sum_dpp_f64(a4[u]);
-                    if (lane == 0 && c0i + u < nc) {
-                        const int e = cnd[c0i + u];
-                        rst[c0i + u] = sum + (bias ? (double)bias[e] : 0.0);
+            for (int u = 0; u < 8; ++u) {
+                double acc = 0.0;
+#pragma unroll
+                for (int c = 0; c < NC8; ++c)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        acc = fma(xh[8 * c + 2 * q], (double)__uint_as_float(wv[u][c][q] << 16), acc);
+                        acc = fma(xh[8 * c + 2 * q + 1], (double)__uint_as_float(wv[u][c][q] & 0xFFFF0000u), acc);
+                    }
+                const double sum = wave_sum_dpp_f64(acc);
+                if (lane == 0 && c0i + u < nc) {
+                    const int e = cnd[c0i + u];
+                    rst[c0i + u] = sum + (bias ? (double)bias[e] : 0.0);
+                }
+            }
+        }
+        __syncthreads();
+        if (wave == 0) {
+            // the rescored values replace the matrix-core ones (the plain softmax
+            // sums over every expert), then the top k among the candidates by
+            // fp64 value (all others lie below them), ties to the lower index: a
+            // candidate's rank is the number before it in that order (the list
+            // is in increasing index), and ranks below k are the picks
+            if (lane < nc) sct[cnd[lane]] = rst[lane];
+            if (lane + 64 < nc) sct[cnd[lane + 64]] = rst[lane + 64];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int i = lane + 64 * h;
+                if (i < nc) {
+                    const double v = rst[i];
+                    int rank = 0;
+                    for (int j = 0; j < nc; ++j) {
+                        const double u = rst[j];
+                        rank += (u > v || (u == v && j < i)) ? 1 : 0;
+                    }
+                    if (rank < k) {
+                        s_topi[rank] = cnd[i];
+                        s_topv[rank] = v;
                     }
                 }
             }
-            // the rescored values replace the matrix-core ones (the plain softmax
-            // sums over every expert), then the top k among the candidates by
-            // fp64 value (all others lie below them); position order breaks ties
-            // by index
-            if (lane < nc) sct[cnd[lane]] = rst[lane];
-            if (lane + 64 < nc) sct[cnd[lane + 64]] = rst[lane + 64];
-            const double w0 = lane < nc ? rst[lane] : 0.0, w1 = lane + 64 < nc ? rst[lane + 64] : 0.0;
-            wave_topk(w0, w1, lane < nc, lane + 64 < nc, k, sel, val);
 #pragma unroll
-            for (int r = 0; r < 8; ++r) sel[r] = cnd[sel[r]];
+            for (int r = 0; r < 8; ++r) {
+                if (r >= k) break;
+                sel[r] = s_topi[r];
+                val[r] = s_topv[r];
+            }
         }
     }
+    if (wave != 0) return;
 
     // weights: lane r < k takes pick r; e^(s - s_max) over the picks' sum
     // (norm_topk_prob) or over all E terms
@@ -854,7 +858,7 @@ hipError_t launch_route_decode(const void* x, const void* W, const float* bias, 
         (Is > 0 && (!sg || !su || !hs)) || !mask || !counts)
         return hipErrorInvalidValue;
     const int nsc = (int)(((T + 7) / 8) * ((E + 15) / 16));
-    const int nsel = (int)((T + 3) / 4);
+    const int nsel = (int)T;                          // one selection workgroup per token
     const int nsk = (Is / 8) * (int)((T + 15) / 16);  // shared gate/up: feature groups x token quarters
     route_scores_kernel<dec::kH><<<(unsigned)nsc, 256, 0, st>>>((const bf16_t*)x, (const bf16_t*)W, bias, (int)T,
                                                                 E, sc, dv, mask, counts);
