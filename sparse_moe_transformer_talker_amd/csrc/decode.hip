@@ -106,15 +106,16 @@ __device__ __forceinline__ f32x4 mfma(const u32x4& a, const u32x4& b, const f32x
 // bias add).  Scores and bounds go to two [T, E] fp64 arrays.
 //
 // route_select_kernel: one workgroup per token, whose wave 0 picks the top k
-// of s by (value, lower index).  It is certified when the intervals [s - d, s + d] of consecutive
-// picks, and of the k-th pick against every other expert, are strictly
-// ordered.  Otherwise every expert whose upper bound reaches the lowest lower
-// bound of the picks is rescored in fp64 from exact products (the four waves
-// take eight candidates each at a time, each lane summing elements 8 l .. 8 l
-// + 7 of each 512-wide chunk in order, then the wave), which gives the top-k of the fp64 scores up to fp64 summation rounding;
-// experts not rescored lie strictly below every pick.  Weights: e^(s_i - s_max)
-// over their sum (norm_topk_prob) or over the sum of all E terms (the plain
-// softmax probabilities), in fp64.
+// of s by (value, lower index).  It is certified when the intervals
+// [s - d, s + d] of consecutive picks, and of the k-th pick against every other
+// expert, are strictly ordered.  Otherwise every expert whose upper bound
+// reaches the lowest lower bound of the picks is rescored in fp64 from exact
+// products (the four waves take eight candidates each at a time, each lane
+// summing elements 8 l .. 8 l + 7 of each 512-wide chunk in order, then the
+// wave), which gives the top-k of the fp64 scores up to fp64 summation
+// rounding; experts not rescored lie strictly below every pick.  Weights:
+// e^(s_i - s_max) over their sum (norm_topk_prob) or over the sum of all E
+// terms (the plain softmax probabilities), in fp64.
 
 // Order-preserving 32-bit key of a score (its fp32 rounding) with the expert
 // index in the low 7 bits: a larger key is a larger score, then a lower index.
