@@ -546,6 +546,37 @@ def cpu_model():
     return None
 
 
+def run_conditions(torch, steps, warmup, rotate):
+    """The conditions of the run: the GPU (name, architecture, compute units,
+    memory), its current shader and memory clocks as rocm-smi reports them
+    (None where the tool is missing or says nothing), the ROCm/HIP and torch
+    versions, the host CPU, the seeds of the synthetic inputs and the counts of
+    the timed loop."""
+    import subprocess
+    p = torch.cuda.get_device_properties(0)
+    cond = {"gpu": torch.cuda.get_device_name(0), "arch": getattr(p, "gcnArchName", None),
+            "compute_units": p.multi_processor_count, "hbm_gib": round(p.total_memory / 2 ** 30, 1),
+            "sclk": None, "mclk": None, "hip": torch.version.hip, "torch": torch.__version__,
+            "host_cpu": cpu_model(), "host_cpus": os.cpu_count(),
+            "seeds": {"weights": [30 + i for i in range(rotate)], "activations": "weight seed + 10000",
+                      "zipf_ranks": 20030},
+            "timed_steps": steps, "warmup_steps": warmup}
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], stdout=subprocess.PIPE,
+                           stderr=subprocess.DEVNULL, text=True, timeout=30)
+        clocks = json.loads(r.stdout) if r.returncode == 0 else {}
+        card = next(iter(clocks.values()), {}) if isinstance(clocks, dict) else {}
+        for key, val in card.items():
+            name = key.lower()
+            if name.startswith("sclk"):
+                cond["sclk"] = val
+            elif name.startswith("mclk"):
+                cond["mclk"] = val
+    except (OSError, ValueError, subprocess.SubprocessError):
+        pass
+    return cond
+
+
 def cpu_baseline(INP, shape, T, seconds, threads=None):
     """The oracle (fp64 numpy, never tuned) timed for about `seconds` on one
     Talker layer at T tokens; threads=1 limits BLAS to one thread."""
@@ -739,6 +770,7 @@ def main():
                   "stages_us_mean": dec["stages_us_mean"],
                   "touched_experts": dec["touched_experts"]},
         "cpu_baseline": cpu,
+        "conditions": run_conditions(torch, args.steps, args.warmup, args.rotate),
     }
     if cpu_extra is not None:
         line["cpu_baseline_more"] = cpu_extra
