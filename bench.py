@@ -548,11 +548,11 @@ def cpu_model():
 
 def run_conditions(torch, steps, warmup, rotate):
     """The conditions of the run: the GPU (name, architecture, compute units,
-    memory), its current shader and memory clocks as rocm-smi reports them
-    (None where the tool is missing or says nothing), the ROCm/HIP and torch
-    versions, the host CPU, the seeds of the synthetic inputs and the counts of
-    the timed loop."""
-    import subprocess
+    memory), its shader and memory clock levels as the driver's sysfs reports
+    them after the timed loops (None where they cannot be read), the HIP and
+    torch versions, the host CPU, the seeds of the synthetic inputs and the
+    counts of the timed loop.  Reads files only: no tool is started."""
+    import glob
     p = torch.cuda.get_device_properties(0)
     cond = {"gpu": torch.cuda.get_device_name(0), "arch": getattr(p, "gcnArchName", None),
             "compute_units": p.multi_processor_count, "hbm_gib": round(p.total_memory / 2 ** 30, 1),
@@ -561,19 +561,23 @@ def run_conditions(torch, steps, warmup, rotate):
             "seeds": {"weights": [30 + i for i in range(rotate)], "activations": "weight seed + 10000",
                       "zipf_ranks": 20030},
             "timed_steps": steps, "warmup_steps": warmup}
-    try:
-        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], stdout=subprocess.PIPE,
-                           stderr=subprocess.DEVNULL, text=True, timeout=30)
-        clocks = json.loads(r.stdout) if r.returncode == 0 else {}
-        card = next(iter(clocks.values()), {}) if isinstance(clocks, dict) else {}
-        for key, val in card.items():
-            name = key.lower()
-            if name.startswith("sclk"):
-                cond["sclk"] = val
-            elif name.startswith("mclk"):
-                cond["mclk"] = val
-    except (OSError, ValueError, subprocess.SubprocessError):
-        pass
+    dev_dir = None
+    bus = getattr(p, "pci_bus_id", None)
+    if bus is not None:
+        cand = "/sys/bus/pci/devices/%04x:%02x:%02x.0" % (getattr(p, "pci_domain_id", 0) or 0, bus,
+                                                         getattr(p, "pci_device_id", 0) or 0)
+        dev_dir = cand if os.path.exists(os.path.join(cand, "pp_dpm_sclk")) else None
+    if dev_dir is None:
+        found = glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")
+        dev_dir = os.path.dirname(found[0]) if len(found) == 1 else None
+    if dev_dir is not None:
+        for key, fname in (("sclk", "pp_dpm_sclk"), ("mclk", "pp_dpm_mclk")):
+            try:
+                for line in open(os.path.join(dev_dir, fname)):
+                    if line.rstrip().endswith("*"):  # the current level
+                        cond[key] = line.split(":", 1)[-1].strip(" *\n")
+            except OSError:
+                pass
     return cond
 
 
