@@ -549,9 +549,10 @@ def cpu_model():
 def run_conditions(torch, steps, warmup, rotate):
     """The conditions of the run: the GPU (name, architecture, compute units,
     memory), its shader and memory clock levels as the driver's sysfs reports
-    them after the timed loops (None where they cannot be read), the HIP and
-    torch versions, the host CPU, the seeds of the synthetic inputs and the
-    counts of the timed loop.  Reads files only: no tool is started."""
+    them under a matrix-product load after the timed loops (None where they
+    cannot be read), the HIP and torch versions, the host CPU, the seeds of the
+    synthetic inputs and the counts of the timed loop.  Reads files only: no
+    tool is started."""
     import glob
     p = torch.cuda.get_device_properties(0)
     cond = {"gpu": torch.cuda.get_device_name(0), "arch": getattr(p, "gcnArchName", None),
@@ -571,6 +572,13 @@ def run_conditions(torch, steps, warmup, rotate):
         found = glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")
         dev_dir = os.path.dirname(found[0]) if len(found) == 1 else None
     if dev_dir is not None:
+        # the levels read while a stream of large bf16 products keeps the GPU
+        # busy (the DPM level drops once it idles)
+        a = torch.ones(8192, 8192, dtype=torch.bfloat16, device="cuda")
+        torch.cuda.synchronize()
+        for _ in range(40):
+            b = a @ a
+        time.sleep(0.005)
         for key, fname in (("sclk", "pp_dpm_sclk"), ("mclk", "pp_dpm_mclk")):
             try:
                 for line in open(os.path.join(dev_dir, fname)):
@@ -578,6 +586,9 @@ def run_conditions(torch, steps, warmup, rotate):
                         cond[key] = line.split(":", 1)[-1].strip(" *\n")
             except OSError:
                 pass
+        torch.cuda.synchronize()
+        del a, b
+        cond["clocks_read"] = "during 40 back-to-back 8192^3 bf16 products, after the timed loops"
     return cond
 
 
