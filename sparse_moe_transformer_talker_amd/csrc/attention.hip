@@ -130,7 +130,10 @@ __global__ __launch_bounds__(64 * kRopeWaves) void qk_rope_append_kernel(
 // norm_out, also RMSNorm of the stored y times the gain.  One workgroup per
 // row, 8 contiguous features per thread per pass.  KSC > 0: KS == KSC, and
 // every partial row is requested before the first add (one memory round trip
-// instead of KS); the sums are the same, in the same order.
+// instead of KS); the sums are the same, in the same order.  The first kKeep
+// passes (H <= 2048) keep their stored values in registers and request their
+// gains at the start, so the norm after the barrier needs no memory round trip.
+constexpr int kKeep = 2;
 template <int KSC>
 __global__ __launch_bounds__(128) void attn_out_kernel(const float* __restrict__ part, int KS, int64_t T, int H,
                                                        const bf16_t* residual, bf16_t* y,
@@ -138,8 +141,26 @@ __global__ __launch_bounds__(128) void attn_out_kernel(const float* __restrict__
                                                        bf16_t* __restrict__ norm_out) {
     __shared__ float wsum[2];
     const int64_t t = blockIdx.x;
+    float gk[kKeep][8];
+#pragma unroll
+    for (int c = 0; c < kKeep; ++c) {
+        const int h = threadIdx.x * 8 + 128 * 8 * c;
+        if (norm_out && gain && h < H) {
+            const f32x4 a = *reinterpret_cast<const f32x4*>(gain + h);
+            const f32x4 b = *reinterpret_cast<const f32x4*>(gain + h + 4);
+#pragma unroll
+            for (int i2 = 0; i2 < 4; ++i2) {
+                gk[c][i2] = a[i2];
+                gk[c][4 + i2] = b[i2];
+            }
+        } else {
+#pragma unroll
+            for (int i2 = 0; i2 < 8; ++i2) gk[c][i2] = 1.f;
+        }
+    }
+    u32x4 yk[kKeep];
     float ss = 0.f;
-    for (int h = threadIdx.x * 8; h < H; h += 128 * 8) {
+    for (int h = threadIdx.x * 8, c = 0; h < H; h += 128 * 8, ++c) {
         float v[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) v[i] = 0.f;
@@ -183,20 +204,31 @@ __global__ __launch_bounds__(128) void attn_out_kernel(const float* __restrict__
             ss = fmaf(b, b, ss);
         }
         *reinterpret_cast<u32x4*>(y + t * H + h) = o;
+#pragma unroll
+        for (int c2 = 0; c2 < kKeep; ++c2)
+            if (c == c2) yk[c2] = o;
     }
     if (!norm_out) return;  // block-uniform
     ss = wave_sum_dpp(ss);
     if (lane_id() == 0) wsum[threadIdx.x >> 6] = ss;
     __syncthreads();
     const float inv = 1.0f / sqrtf((wsum[0] + wsum[1]) / (float)H + eps);
-    for (int h = threadIdx.x * 8; h < H; h += 128 * 8) {
-        const u32x4 yv = *reinterpret_cast<const u32x4*>(y + t * H + h);
+    for (int h = threadIdx.x * 8, c = 0; h < H; h += 128 * 8, ++c) {
+        u32x4 yv;
         float g[8];
+        if (c < kKeep) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) g[i] = 1.f;
-        if (gain)
+            for (int c2 = 0; c2 < kKeep; ++c2)
+                if (c == c2) {
+                    yv = yk[c2];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) g[i] = gain[h + i];
+                    for (int i = 0; i < 8; ++i) g[i] = gk[c2][i];
+                }
+        } else {  // rows wider than kKeep passes: the stored values and the gains from memory
+            yv = *reinterpret_cast<const u32x4*>(y + t * H + h);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) g[i] = gain ? gain[h + i] : 1.f;
+        }
         u32x4 o;
 #pragma unroll
         for (int q = 0; q < 4; ++q)

@@ -121,20 +121,40 @@ __device__ __forceinline__ float rms_inv_bf16x8(const u32x4 (&v)[NCH], bool (&ok
     const float ms = (part[0] + part[1]) / (float)H;
     return 1.0f / sqrtf(ms + eps);
 }
+// The gains of this thread's 8-element chunks (1.0 where gain is null or the
+// chunk lies past H), requested at a kernel's start so that they arrive with
+// its row data rather than after the sum-of-squares barrier.
+template <int NCH>
+__device__ __forceinline__ void load_gain_bf16x8(const float* __restrict__ gain, int H, float (&g)[NCH][8]) {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int h = (threadIdx.x + 128 * c) * 8;
+        if (gain && h < H) {
+            const f32x4 a = *reinterpret_cast<const f32x4*>(gain + h);
+            const f32x4 b = *reinterpret_cast<const f32x4*>(gain + h + 4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                g[c][i] = a[i];
+                g[c][4 + i] = b[i];
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) g[c][i] = 1.0f;
+        }
+    }
+}
 template <int NCH>
 __device__ __forceinline__ void rms_store_bf16x8(const u32x4 (&v)[NCH], bool (&ok)[NCH], float inv,
-                                                 const float* __restrict__ gain, bf16_t* out_row) {
+                                                 const float (&g)[NCH][8], bf16_t* out_row) {
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
         if (!ok[c]) continue;
         const int h = (threadIdx.x + 128 * c) * 8;
         u32x4 o;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const float g0 = gain ? gain[h + 2 * q] : 1.0f, g1 = gain ? gain[h + 2 * q + 1] : 1.0f;
-            o[q] = pack_bf16x2(__uint_as_float(v[c][q] << 16) * inv * g0,
-                               __uint_as_float(v[c][q] & 0xFFFF0000u) * inv * g1);
-        }
+        for (int q = 0; q < 4; ++q)
+            o[q] = pack_bf16x2(__uint_as_float(v[c][q] << 16) * inv * g[c][2 * q],
+                               __uint_as_float(v[c][q] & 0xFFFF0000u) * inv * g[c][2 * q + 1]);
         *reinterpret_cast<u32x4*>(out_row + h) = o;
     }
 }
@@ -143,6 +163,8 @@ __global__ __launch_bounds__(128) void rmsnorm_bf16x8_kernel(const bf16_t* x, co
                                                              float eps, int64_t Ttok, int H, bf16_t* out) {
     const int64_t t = blockIdx.x;
     if (t >= Ttok) return;
+    float gv[NCH][8];
+    load_gain_bf16x8<NCH>(gain, H, gv);
     u32x4 v[NCH];
     bool ok[NCH];
 #pragma unroll
@@ -152,7 +174,7 @@ __global__ __launch_bounds__(128) void rmsnorm_bf16x8_kernel(const bf16_t* x, co
         v[c] = ok[c] ? *reinterpret_cast<const u32x4*>(x + t * H + h) : u32x4{0, 0, 0, 0};
     }
     const float inv = rms_inv_bf16x8<NCH>(v, ok, H, eps);
-    rms_store_bf16x8<NCH>(v, ok, inv, gain, out + t * H);
+    rms_store_bf16x8<NCH>(v, ok, inv, gv, out + t * H);
 }
 
 // The end of a stacked layer: the combine above (shared, slots 0..k-1,
@@ -168,6 +190,8 @@ __global__ __launch_bounds__(128) void combine_norm_bf16x8_kernel(const bf16_t* 
                                                                   bf16_t* norm_out) {
     const int64_t t = blockIdx.x;
     if (t >= Ttok) return;
+    float gv[NCH][8];
+    load_gain_bf16x8<NCH>(norm_out ? gain : nullptr, H, gv);
     const bf16_t* shared_row = shared ? shared + t * sstride : nullptr;
     u32x4 yv[NCH];
     bool ok[NCH];
@@ -211,7 +235,7 @@ __global__ __launch_bounds__(128) void combine_norm_bf16x8_kernel(const bf16_t* 
         *reinterpret_cast<u32x4*>(y + t * H + h) = yv[c];
     }
     const float inv = rms_inv_bf16x8<NCH>(yv, ok, H, eps);
-    rms_store_bf16x8<NCH>(yv, ok, inv, gain, norm_out + t * H);
+    rms_store_bf16x8<NCH>(yv, ok, inv, gv, norm_out + t * H);
 }
 
 // Partial-row combine of the decode layer.  Token t's partial rows are
@@ -230,6 +254,8 @@ __global__ __launch_bounds__(128) void combine_partials_kernel(const bf16_t* __r
                                                                bf16_t* norm_out) {
     const int64_t t = blockIdx.x;
     if (t >= Ttok) return;
+    float gv[NCH][8];
+    load_gain_bf16x8<NCH>(norm_out ? gain : nullptr, H, gv);
     // K > 0: the sizes are compile-time, and every row of the token is loaded
     // before the first add (one memory round trip)
     const int k = K > 0 ? K : k_rt, s_n = K > 0 ? S : S_rt, ssh_n = K > 0 ? SSH : SSH_rt;
@@ -296,7 +322,7 @@ __global__ __launch_bounds__(128) void combine_partials_kernel(const bf16_t* __r
     }
     if (!norm_out) return;
     const float inv = rms_inv_bf16x8<NCH>(yv, ok, H, eps);
-    rms_store_bf16x8<NCH>(yv, ok, inv, gain, norm_out + t * H);
+    rms_store_bf16x8<NCH>(yv, ok, inv, gv, norm_out + t * H);
 }
 
 hipError_t launch_combine_partials(const void* part, int S, int SSH, int k, const float* w, const void* residual,
@@ -394,6 +420,8 @@ __global__ __launch_bounds__(128) void add_rmsnorm_bf16x8_kernel(const bf16_t* _
                                                                  int64_t Ttok, int H, bf16_t* out) {
     const int64_t t = blockIdx.x;
     if (t >= Ttok) return;
+    float gv[NCH][8];
+    load_gain_bf16x8<NCH>(gain, H, gv);
     u32x4 v[NCH];
     bool ok[NCH];
 #pragma unroll
@@ -411,7 +439,7 @@ __global__ __launch_bounds__(128) void add_rmsnorm_bf16x8_kernel(const bf16_t* _
         *reinterpret_cast<u32x4*>(x + t * H + h) = v[c];
     }
     const float inv = rms_inv_bf16x8<NCH>(v, ok, H, eps);
-    rms_store_bf16x8<NCH>(v, ok, inv, gain, out + t * H);
+    rms_store_bf16x8<NCH>(v, ok, inv, gv, out + t * H);
 }
 
 hipError_t launch_add_rmsnorm(const void* a, const void* b, void* x, const float* gain, float eps, int64_t Ttok,
@@ -440,6 +468,8 @@ __global__ __launch_bounds__(128) void embed_norm_bf16x8_kernel(const bf16_t* __
                                                                 int64_t Ttok, int H, bf16_t* out) {
     const int64_t t = blockIdx.x;
     if (t >= Ttok) return;
+    float gv[NCH][8];
+    load_gain_bf16x8<NCH>(gain, H, gv);
     const int r = idx[t];
     const bool in = r >= 0 && r < rows;
     u32x4 v[NCH];
@@ -454,7 +484,7 @@ __global__ __launch_bounds__(128) void embed_norm_bf16x8_kernel(const bf16_t* __
         *reinterpret_cast<u32x4*>(x + t * H + h) = v[c];
     }
     const float inv = rms_inv_bf16x8<NCH>(v, ok, H, eps);
-    rms_store_bf16x8<NCH>(v, ok, inv, gain, out + t * H);
+    rms_store_bf16x8<NCH>(v, ok, inv, gv, out + t * H);
 }
 
 hipError_t launch_embed_norm(const void* table, int rows, const int32_t* idx, void* x, const float* gain, float eps,
