@@ -557,7 +557,7 @@ def run_conditions(torch, steps, warmup, rotate):
     p = torch.cuda.get_device_properties(0)
     cond = {"gpu": torch.cuda.get_device_name(0), "arch": getattr(p, "gcnArchName", None),
             "compute_units": p.multi_processor_count, "hbm_gib": round(p.total_memory / 2 ** 30, 1),
-            "sclk": None, "mclk": None, "hip": torch.version.hip, "torch": torch.__version__,
+            "sclk_dpm_level": None, "mclk_dpm_level": None, "hip": torch.version.hip, "torch": torch.__version__,
             "host_cpu": cpu_model(), "host_cpus": os.cpu_count(),
             "seeds": {"weights": [30 + i for i in range(rotate)], "activations": "weight seed + 10000",
                       "zipf_ranks": 20030},
@@ -579,7 +579,7 @@ def run_conditions(torch, steps, warmup, rotate):
         for _ in range(40):
             b = a @ a
         time.sleep(0.005)
-        for key, fname in (("sclk", "pp_dpm_sclk"), ("mclk", "pp_dpm_mclk")):
+        for key, fname in (("sclk_dpm_level", "pp_dpm_sclk"), ("mclk_dpm_level", "pp_dpm_mclk")):
             try:
                 for line in open(os.path.join(dev_dir, fname)):
                     if line.rstrip().endswith("*"):  # the current level
@@ -588,7 +588,8 @@ def run_conditions(torch, steps, warmup, rotate):
                 pass
         torch.cuda.synchronize()
         del a, b
-        cond["clocks_read"] = "during 40 back-to-back 8192^3 bf16 products, after the timed loops"
+        cond["clocks_read"] = ("the DPM level sysfs marks current during 40 back-to-back 8192^3 bf16 products, "
+                               "after the timed loops: a coarse indicator, not a measured clock")
     return cond
 
 
