@@ -1357,9 +1357,31 @@ __global__ __launch_bounds__(kArgmaxThreads) void argmax_exact_kernel(const floa
     const float* s = sc + t * n;
     const float* d = bd + t * n;
     constexpr int U = 4;  // entries per thread with loads in flight together
+    // rows of at most R entries (R / 256 per thread: the code heads' 2048 and
+    // 3072): every entry requested at once and kept in registers for the
+    // candidate count, one memory round trip; longer rows loop U at a time
+    constexpr int RPT = 16, R = RPT * kArgmaxThreads;
+    const bool in_regs = n <= R;  // block-uniform
+    float sr[RPT], dr[RPT];
     uint64_t key = 0;
     double low = -1.0e300;
-    for (int e0 = (int)threadIdx.x; e0 < n; e0 += U * kArgmaxThreads) {
+    if (in_regs) {
+#pragma unroll
+        for (int u = 0; u < RPT; ++u) {  // entries past the end repeat the last one, unused
+            const int e = min((int)threadIdx.x + u * kArgmaxThreads, n - 1);
+            sr[u] = s[e];
+            dr[u] = d[e];
+        }
+#pragma unroll
+        for (int u = 0; u < RPT; ++u) {
+            const int e = (int)threadIdx.x + u * kArgmaxThreads;
+            if (e >= n) continue;
+            const uint64_t kk = rank_key(sr[u], e);
+            key = kk > key ? kk : key;
+            low = fmax(low, (double)sr[u] - (double)dr[u]);
+        }
+    }
+    for (int e0 = in_regs ? n : (int)threadIdx.x; e0 < n; e0 += U * kArgmaxThreads) {
         float sv[U], dv[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {  // branch-free: entries past the end repeat the last one, unused
@@ -1391,7 +1413,12 @@ __global__ __launch_bounds__(kArgmaxThreads) void argmax_exact_kernel(const floa
     }
     int bi = rank_key_index(key);
     int nc = 0;
-    for (int e0 = (int)threadIdx.x; e0 < n; e0 += U * kArgmaxThreads) {
+    if (in_regs) {
+#pragma unroll
+        for (int u = 0; u < RPT; ++u)
+            if ((int)threadIdx.x + u * kArgmaxThreads < n) nc += ((double)sr[u] + (double)dr[u] >= low) ? 1 : 0;
+    }
+    for (int e0 = in_regs ? n : (int)threadIdx.x; e0 < n; e0 += U * kArgmaxThreads) {
         float sv[U], dv[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
