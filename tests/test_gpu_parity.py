@@ -260,6 +260,32 @@ def test_rmsnorm_and_codec_head(talker):
     np.testing.assert_array_equal(c0d.cpu().numpy(), R.argmax_first(ref_logits[:64]))
 
 
+@pytest.mark.parametrize("V", [4096, 4097, 6000])
+def test_codec_head_argmax_row_lengths(talker, V):
+    """The exact argmax holds a row of up to 4096 scores in registers and loops
+    over longer ones: both forms, at and across the boundary, equal the oracle's
+    argmax (ties to the lowest code), including an exact tie placed on the
+    boundary's far side and at code 0."""
+    cfg = G.config(talker.shape, "bf16")
+    T = 64
+    xn = G.dev(INP.activations(T, 1024, 11, "bf16"), "bf16")
+    head_np = INP.stack_weights(INP.TALKER, 0, 30, 0.02, "bf16", V, 51)["codec_head"]
+    ref = R.codec_head_logits(G.host64(xn), INP.to_f64(head_np, "bf16"))
+    c0, _ = api.moe_codec_head_argmax(cfg, xn, G.dev(head_np, "bf16"))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(c0.cpu().numpy(), R.argmax_first(ref))
+    hd = head_np.copy()
+    top = int(R.argmax_first(ref)[0])
+    hd[V - 1] = hd[top]
+    c0b, _ = api.moe_codec_head_argmax(cfg, xn, G.dev(hd, "bf16"))
+    torch.cuda.synchronize()
+    assert int(c0b[0]) == min(top, V - 1)
+    hd[0] = hd[top]
+    c0c, _ = api.moe_codec_head_argmax(cfg, xn, G.dev(hd, "bf16"))
+    torch.cuda.synchronize()
+    assert int(c0c[0]) == 0
+
+
 def test_empty_batch(talker):
     cfg = G.config(talker.shape, "bf16")
     x = torch.empty((0, 1024), dtype=torch.bfloat16, device="cuda")
