@@ -8,7 +8,8 @@ bf16 bars; every other cache entry must be unchanged bit for bit.  The value
 cache is transposed in the library ([T, nkv, head_dim, max_len]).  Cases: random
 lengths up to 1024 (T = 64); ragged 128-position chunks with lengths 0 / 1 /
 126..129 / max_len - 1 (T = 37, max_len = 256: two chunks, the merge runs);
-512-position chunks with lengths 510..513 / 1022 / 1023 (max_len 1024); 3D
+512-position chunks with lengths 510..513 / 1022 / 1023 (max_len 1024); the chunk
+merge in both of its forms (four chunks at 2048 positions, five at 2560); 3D
 positions with distinct T/H/W indices; long caches (max_len 4096 and 32768); the
 16/8 head split at 256 positions, and 16/8 and 8/2 at 1024 (the 16-wave chunk
 with 2 and 4 query heads per KV head); hidden 512 (the 16-column skinny
@@ -114,6 +115,17 @@ def test_attention_decode_long_chunk_boundaries():
     lens = np.array([510, 511, 512, 513, 1022, 1023, 0, 255, 767], np.int32)
     w, kv, x, res, lens, pos = _case(T, L, lens)
     _check(INP.TALKER_ATTN, L, w, kv, x, res, lens, pos, "chunk boundaries")
+
+
+@pytest.mark.parametrize("L", [2048, 2560])
+def test_attention_decode_merge_forms(L):
+    # the chunk merge requests every chunk at once up to four chunks (2048
+    # positions) and loops above (2560: five chunks); streams holding 1 .. all
+    # of the chunks, lengths on the chunk boundaries and at the cache's end
+    lens = np.array([0, 1, 511, 512, 513, 1023, 1024, 1535, 1536, 2047, L - 2, L - 1], np.int32)
+    T = len(lens)
+    w, kv, x, res, lens, pos = _case(T, L, lens)
+    _check(INP.TALKER_ATTN, L, w, kv, x, res, lens, pos, "merge, %d positions" % L)
 
 
 @pytest.mark.parametrize("heads", [(16, 8), (8, 2)])
