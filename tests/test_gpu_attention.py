@@ -13,7 +13,8 @@ merge in both of its forms (four chunks at 2048 positions, five at 2560); 3D
 positions with distinct T/H/W indices; long caches (max_len 4096 and 32768); the
 16/8 head split at 256 positions, and 16/8 and 8/2 at 1024 (the 16-wave chunk
 with 2 and 4 query heads per KV head); hidden 512 (the 16-column skinny
-products); the fused RMSNorm of y; a batch of 96 streams (the grouped GEMM path
+products); hidden 2048 and 3072 with the fused norm (its register and memory
+forms); the fused RMSNorm of y; a batch of 96 streams (the grouped GEMM path
 for the projections); streams whose length is out of range; and a captured graph
 replayed.
 """
@@ -161,6 +162,17 @@ def test_attention_decode_small_hidden():
     T, L = 20, 256
     w, kv, x, res, lens, pos = _case(T, L, INP.cache_lengths(T, L, 68), shape=shape)
     _check(shape, L, w, kv, x, res, lens, pos, "hidden 512", norm=True)
+
+
+@pytest.mark.parametrize("H", [2048, 3072])
+def test_attention_decode_wide_hidden_norm(H):
+    """Hidden 2048 and 3072 with the fused RMSNorm of y: the output reduction
+    keeps its first two 1024-wide passes in registers and reads any further
+    pass back from memory (3072), so both forms of its norm run."""
+    shape = INP.AttnShape(H, 16, 2, 128)
+    T, L = 24, 256
+    w, kv, x, res, lens, pos = _case(T, L, INP.cache_lengths(T, L, 69), shape=shape)
+    _check(shape, L, w, kv, x, res, lens, pos, "hidden %d" % H, norm=True)
 
 
 def test_attention_decode_16q_8kv():
